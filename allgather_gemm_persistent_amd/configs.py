@@ -1,0 +1,143 @@
+"""The five workloads: one rank's share of AllGather+GEMM / GEMM+ReduceScatter on one GPU.
+
+Each entry states shapes, dtype, value distributions, chunk geometry, arrival order and seeds.
+Readings of points the workload statements leave open (output dtype, "N(0, 0.02)" as a standard
+deviation, seeds, delay magnitude, the ReduceScatter chunk size) are listed with the design notes.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+from . import inputs
+
+
+@dataclass(frozen=True)
+class AgConfig:
+    """AllGather+GEMM: C (W*Ms x N, bf16) = concat(shards) (W*Ms x K) @ B (K x N)."""
+    name: str
+    world: int
+    rank: int
+    m_shard: int
+    k: int
+    n: int
+    dtype: str                  # "bf16" or "fp8" (OCP e4m3fn)
+    chunk_rows: int
+    a_dist: dict
+    b_dist: dict
+    order_kind: str             # "seeded" or "ring"
+    seed: int
+    with_delays: bool = False   # seeded per-chunk host delays in correctness runs
+    op: str = field(default="ag")
+
+    @property
+    def m(self) -> int:
+        return self.world * self.m_shard
+
+    @property
+    def chunks_per_shard(self) -> int:
+        return self.m_shard // self.chunk_rows
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.m * self.n * self.k
+
+    def order(self) -> list:
+        if self.order_kind == "ring":
+            return inputs.ring_order(self.world, self.rank, self.chunks_per_shard)
+        return inputs.seeded_order(self.world, self.rank, self.chunks_per_shard, self.seed + 1)
+
+    def delays(self) -> list | None:
+        if not self.with_delays:
+            return None
+        n = (self.world - 1) * self.chunks_per_shard
+        return inputs.delays_us(n, self.seed + 2, 50)
+
+
+@dataclass(frozen=True)
+class RsConfig:
+    """GEMM+ReduceScatter: P = A (M x K) @ B (K x N) in fp32; this rank's block is reduced."""
+    name: str
+    world: int
+    rank: int
+    m: int
+    k: int
+    n: int
+    chunk_rows: int
+    a_dist: dict
+    b_dist: dict
+    peer_dist: dict
+    order_kind: str
+    seed: int
+    dtype: str = "bf16"
+    op: str = field(default="rs")
+
+    @property
+    def m_block(self) -> int:
+        return self.m // self.world
+
+    @property
+    def chunks_per_block(self) -> int:
+        return self.m_block // self.chunk_rows
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.m * self.n * self.k
+
+    def order(self) -> list:
+        if self.order_kind == "ring":
+            return inputs.ring_order(self.world, self.rank, self.chunks_per_block)
+        return inputs.seeded_order(self.world, self.rank, self.chunks_per_block, self.seed + 1)
+
+
+U11 = {"kind": "uniform", "lo": -1.0, "hi": 1.0}
+N1 = {"kind": "normal", "std": 1.0}
+N002 = {"kind": "normal", "std": 0.02}
+
+CONFIGS = {
+    # 1: tiny, latency-bound; oracle in milliseconds
+    "c1_ag_w2_tiny": AgConfig("c1_ag_w2_tiny", world=2, rank=0, m_shard=128, k=512, n=256,
+                              dtype="bf16", chunk_rows=64, a_dist=U11, b_dist=U11,
+                              order_kind="seeded", seed=1010),
+    # 2: the MFMA-bound bf16 workload (the headline)
+    "c2_ag_w8_bf16": AgConfig("c2_ag_w8_bf16", world=8, rank=0, m_shard=512, k=8192, n=3584,
+                              dtype="bf16", chunk_rows=128, a_dist=N1, b_dist=N002,
+                              order_kind="ring", seed=1020, with_delays=True),
+    # 3: GEMM + ReduceScatter, 7 incoming fp32 partial blocks
+    "c3_rs_w8_bf16": RsConfig("c3_rs_w8_bf16", world=8, rank=0, m=8192, k=3584, n=8192,
+                              chunk_rows=128, a_dist=N1, b_dist=N002, peer_dist=N1,
+                              order_kind="seeded", seed=1030),
+    # 4: decode-shaped, HBM-bound
+    "c4_ag_w8_decode": AgConfig("c4_ag_w8_decode", world=8, rank=0, m_shard=16, k=8192, n=3584,
+                                dtype="bf16", chunk_rows=16, a_dist=N1, b_dist=N002,
+                                order_kind="ring", seed=1040),
+    # 5: fp8 e4m3fn with per-tensor scales
+    "c5_ag_w8_fp8": AgConfig("c5_ag_w8_fp8", world=8, rank=0, m_shard=1024, k=8192, n=7168,
+                             dtype="fp8", chunk_rows=256, a_dist=N1, b_dist=N002,
+                             order_kind="seeded", seed=1050),
+}
+
+HEADLINE = "c2_ag_w8_bf16"
+
+
+def make_ag_data(cfg: AgConfig):
+    """Host tensors for an AllGather+GEMM workload.
+
+    Returns dict: shards (list of W CPU tensors Ms x K, bf16 or float8_e4m3fn), b (K x N, same
+    dtype), scale_a, scale_b (per-tensor fp8 scales; 1.0 for bf16). The W shards are drawn as one
+    M x K tensor (seed) and split, so the gathered matrix has one per-tensor scale.
+    """
+    a, sa = inputs.draw(cfg.a_dist, (cfg.m, cfg.k), cfg.dtype, cfg.seed)
+    b, sb = inputs.draw(cfg.b_dist, (cfg.k, cfg.n), cfg.dtype, cfg.seed + 3)
+    shards = [a[p * cfg.m_shard:(p + 1) * cfg.m_shard].contiguous() for p in range(cfg.world)]
+    return {"shards": shards, "b": b, "scale_a": sa, "scale_b": sb}
+
+
+def make_rs_data(cfg: RsConfig):
+    """Host tensors for a GEMM+ReduceScatter workload: a (M x K), b (K x N) bf16, and peers
+    (W x M/W x N fp32) where slot ``rank`` is zero and unused."""
+    a, _ = inputs.draw(cfg.a_dist, (cfg.m, cfg.k), cfg.dtype, cfg.seed)
+    b, _ = inputs.draw(cfg.b_dist, (cfg.k, cfg.n), cfg.dtype, cfg.seed + 3)
+    peers, _ = inputs.draw(cfg.peer_dist, (cfg.world, cfg.m_block, cfg.n), "f32", cfg.seed + 4)
+    peers[cfg.rank].zero_()
+    return {"a": a, "b": b, "peers": peers}

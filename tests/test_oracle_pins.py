@@ -1,0 +1,351 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+* number formats: exhaustive comparison with torch's independent casts, plus values fixed by
+  the format definitions;
+* the products: exact rational brute force (bf16 and e4m3fn values are dyadic rationals, so the
+  exact C is computable with fractions.Fraction) and hand-derived worked examples;
+* the chunk/tile bookkeeping: an event simulation of chunk arrivals, independent of the
+  oracle's "latest arrival position" formulation;
+* planted mistakes: plausible bugs (transposed operand, dropped peer, wrong sign, ignored
+  arrival order) planted in copies of the oracle must fail these pins.
+"""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import agg_oracle as O
+from allgather_gemm_persistent_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+def _bf16_bits(vals):
+    return inputs.raw_bits(torch.tensor(vals, dtype=torch.float64).to(torch.float32).to(torch.bfloat16))
+
+
+def _fp8_bits(vals):
+    return inputs.raw_bits(torch.tensor(vals, dtype=torch.float32).to(torch.float8_e4m3fn))
+
+
+def _bits(vals, dtype):
+    return _bf16_bits(vals) if dtype == "bf16" else _fp8_bits(vals)
+
+
+# ------------------------------------------------------------------ number formats
+
+def test_decode_bf16_exhaustive_vs_torch():
+    allb = np.arange(65536, dtype=np.uint16)
+    mine = O.decode_bf16(allb)
+    ref = torch.from_numpy(allb.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+
+
+def test_decode_e4m3fn_exhaustive_vs_torch():
+    allb = np.arange(256, dtype=np.uint8)
+    mine = O.decode_e4m3fn(allb)
+    ref = torch.from_numpy(allb).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+
+
+@pytest.mark.parametrize("bits,val", [
+    (0x3F80, 1.0), (0xC000, -2.0), (0x0001, 2.0 ** -133), (0x0080, 2.0 ** -126),
+    (0x7F7F, (2 - 2 ** -7) * 2.0 ** 127), (0x3E80, 0.25), (0x4049, 3.140625),
+])
+def test_decode_bf16_definition_values(bits, val):
+    assert O.decode_bf16(np.uint16(bits)) == val
+
+
+@pytest.mark.parametrize("bits,val", [
+    (0x38, 1.0), (0x7E, 448.0), (0x01, 2.0 ** -9), (0x08, 2.0 ** -6), (0x07, 7 * 2.0 ** -9),
+    (0xB8, -1.0), (0x30, 0.5), (0x77, 240.0),
+])
+def test_decode_e4m3fn_definition_values(bits, val):
+    assert O.decode_e4m3fn(np.uint8(bits)) == val
+
+
+def test_e4m3fn_nan_codes_and_no_inf():
+    d = O.decode_e4m3fn(np.arange(256, dtype=np.uint8))
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF])
+    assert np.isnan(d).sum() == 2 and not np.isinf(d).any()
+    assert np.nanmax(d) == 448.0
+
+
+def test_encode_bf16_vs_torch_on_float32():
+    """torch rounds binary32 -> bf16 to nearest even in one step: compare on float32 inputs."""
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-80, 80, 200000))).astype(np.float32)
+    # add every bf16 midpoint and its neighbours (the tie cases)
+    allb = np.arange(0, 0x7F80, dtype=np.uint32)
+    mids = ((allb << 16) | 0x8000).view(np.float32)
+    x = np.concatenate([x, mids, np.nextafter(mids, np.float32(np.inf)),
+                        np.nextafter(mids, np.float32(0)), -mids])
+    x = x[np.isfinite(x)]
+    mine = O.encode_bf16_rne(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+
+
+def test_encode_bf16_exact_on_float64():
+    """float64 inputs: the nearer neighbour by exact rational distance, even on a tie."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(3000) * np.exp(rng.uniform(-60, 60, 3000))
+    enc = O.encode_bf16_rne(x)
+    for xi, bi in zip(x, enc):
+        v = Fraction(float(xi))
+        got = Fraction(float(O.decode_bf16(bi)))
+        # neighbours of the chosen value
+        up = Fraction(float(O.decode_bf16(np.uint16(bi + 1))))
+        dn = Fraction(float(O.decode_bf16(np.uint16(bi - 1)))) if (bi & 0x7FFF) else -got
+        assert abs(v - got) <= abs(v - up) and abs(v - got) <= abs(v - dn)
+
+
+def test_encode_decode_roundtrip_all_finite_bf16():
+    allb = np.arange(65536, dtype=np.uint16)
+    d = O.decode_bf16(allb)
+    fin = np.isfinite(d)
+    back = O.encode_bf16_rne(d[fin])
+    assert np.array_equal(back, allb[fin])
+
+
+# ------------------------------------------------------------------ products: brute force
+
+def _exact_matmul(a_vals, b_vals):
+    """Exact rational product with pure-Python loops (tiny shapes only)."""
+    m, k = len(a_vals), len(a_vals[0])
+    n = len(b_vals[0])
+    return [[sum((a_vals[i][t] * b_vals[t][j] for t in range(k)), Fraction(0)) for j in range(n)]
+            for i in range(m)]
+
+
+def _frac_matrix(raw, dtype):
+    dec = O.decode_bf16 if dtype == "bf16" else O.decode_e4m3fn
+    vals = dec(raw)
+    return [[Fraction(float(v)) for v in row] for row in vals]
+
+
+def _random_raw(shape, dtype, rng):
+    if dtype == "bf16":
+        x = torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16)
+    else:
+        x = torch.from_numpy(rng.standard_normal(shape).astype(np.float32) * 30).to(torch.float8_e4m3fn)
+    return inputs.raw_bits(x)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("world,m_shard,k,n", [(1, 2, 16, 3), (2, 1, 32, 5), (3, 2, 48, 4),
+                                               (8, 1, 16, 2)])
+def test_ag_gemm_vs_exact_rational(dtype, world, m_shard, k, n):
+    rng = np.random.default_rng(world * 100 + k)
+    shards = [_random_raw((m_shard, k), dtype, rng) for _ in range(world)]
+    b = _random_raw((k, n), dtype, rng)
+    sa, sb = (0.75, 0.125) if dtype == "fp8" else (1.0, 1.0)
+    c = O.ag_gemm_ref(shards, b, dtype, sa, sb)
+    a_frac = sum((_frac_matrix(s, dtype) for s in shards), [])
+    exact = _exact_matmul(a_frac, _frac_matrix(b, dtype))
+    scale = Fraction(sa) * Fraction(sb) if dtype == "fp8" else Fraction(1)
+    for i in range(world * m_shard):
+        for j in range(n):
+            e = exact[i][j] * scale
+            assert abs(Fraction(float(c[i, j])) - e) <= abs(e) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 30)
+
+
+@pytest.mark.parametrize("world,rank", [(1, 0), (2, 1), (3, 0), (4, 2)])
+def test_gemm_rs_vs_exact_rational(world, rank):
+    rng = np.random.default_rng(world * 10 + rank)
+    mb, k, n = 2, 16, 3
+    a = _random_raw((world * mb, k), "bf16", rng)
+    b = _random_raw((k, n), "bf16", rng)
+    peers = rng.standard_normal((world, mb, n)).astype(np.float32)
+    send, out = O.gemm_rs_ref(a, b, peers, world, rank)
+    p = _exact_matmul(_frac_matrix(a, "bf16"), _frac_matrix(b, "bf16"))
+    others = [j for j in range(world) if j != rank]
+    assert send.shape == (world - 1, mb, n)
+    for s_i, j in enumerate(others):
+        for i in range(mb):
+            for c in range(n):
+                e = p[j * mb + i][c]
+                assert abs(Fraction(float(send[s_i, i, c])) - e) <= abs(e) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 30)
+    for i in range(mb):
+        for c in range(n):
+            e = p[rank * mb + i][c] + sum(Fraction(float(peers[q, i, c])) for q in others)
+            assert abs(Fraction(float(out[i, c])) - e) <= abs(e) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 30)
+
+
+def test_gather_places_rows_by_rank_not_arrival():
+    """Row-id encoded shards: gathered row i must carry id i (shard p holds ids p*Ms..)."""
+    world, ms, k = 5, 3, 4
+    shards = [_bf16_bits([[float(p * ms + i)] * k for i in range(ms)]) for p in range(world)]
+    g = O.decode_bf16(O.gather_ref(shards))
+    assert np.array_equal(g[:, 0], np.arange(world * ms, dtype=np.float64))
+
+
+# ------------------------------------------------------------------ worked examples
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", _golden()["ag"], ids=lambda c: c["name"])
+def test_ag_worked_examples(case):
+    dt = case["dtype"]
+    shards = [_bits(s, dt) for s in case["shards"]]
+    c = O.ag_gemm_ref(shards, _bits(case["b"], dt), dt, case["scale_a"], case["scale_b"])
+    assert np.array_equal(c, np.array(case["c"], dtype=np.float64))
+
+
+@pytest.mark.parametrize("case", _golden()["rs"], ids=lambda c: c["name"])
+def test_rs_worked_examples(case):
+    send, out = O.gemm_rs_ref(_bf16_bits(case["a"]), _bf16_bits(case["b"]),
+                              np.array(case["peers"], dtype=np.float32), case["world"], case["rank"])
+    assert np.array_equal(send, np.array(case["send"], dtype=np.float64))
+    assert np.array_equal(out, np.array(case["out"], dtype=np.float64))
+
+
+@pytest.mark.parametrize("case", _golden()["schedule"], ids=lambda c: c["name"])
+def test_schedule_worked_examples(case):
+    for key in case:
+        if key.startswith("bm") and key[2:].isdigit():
+            order, _ = O.ag_mtile_order(case["world"], case["rank"], case["m_shard"],
+                                        case["chunk_rows"], case["order"], int(key[2:]))
+            assert order == case[key], key
+
+
+# ------------------------------------------------------------------ bookkeeping: simulation
+
+def _simulate_ag(world, rank, ms, cr, order, bm):
+    """Deliver chunks one at a time; after each delivery, emit (ascending) every row tile whose
+    rows are all present and that was not emitted before."""
+    m = world * ms
+    present = np.zeros(m, dtype=bool)
+    present[rank * ms:(rank + 1) * ms] = True
+    n_tiles = -(-m // bm)
+    done, seq = set(), []
+
+    def sweep():
+        for t in range(n_tiles):
+            if t not in done and present[t * bm:min((t + 1) * bm, m)].all():
+                done.add(t)
+                seq.append(t)
+    sweep()
+    for c in order:
+        present[c * cr:(c + 1) * cr] = True
+        sweep()
+    return seq
+
+
+@pytest.mark.parametrize("world,rank,ms,cr,bm", [
+    (2, 0, 128, 64, 64), (2, 1, 128, 64, 128), (8, 0, 512, 128, 256), (8, 3, 16, 16, 128),
+    (8, 0, 1024, 256, 256), (3, 2, 10, 5, 4), (4, 1, 12, 3, 7), (8, 7, 8, 2, 3)])
+@pytest.mark.parametrize("order_seed", [0, 1, 2])
+def test_ag_mtile_order_vs_simulation(world, rank, ms, cr, bm, order_seed):
+    cps = ms // cr
+    order = inputs.seeded_order(world, rank, cps, order_seed) if order_seed else \
+        inputs.ring_order(world, rank, cps)
+    got, ready = O.ag_mtile_order(world, rank, ms, cr, order, bm)
+    assert got == _simulate_ag(world, rank, ms, cr, order, bm)
+    assert sorted(got) == list(range(-(-world * ms // bm)))
+
+
+@pytest.mark.parametrize("lo,hi,cr", [(0, 1, 1), (0, 128, 64), (5, 37, 8), (63, 65, 64),
+                                      (100, 356, 128), (7, 8, 3)])
+def test_covering_chunks_vs_per_row(lo, hi, cr):
+    assert O.covering_chunks(lo, hi, cr) == sorted({r // cr for r in range(lo, hi)})
+
+
+def _simulate_rs(world, rank, mb, cr, order, bm):
+    tpb = -(-mb // bm)
+    seq = [((rank + d) % world, i) for d in range(1, world) for i in range(tpb)]
+    cpb = mb // cr
+    present = {p: np.zeros(mb, dtype=bool) for p in range(world) if p != rank}
+    done = set()
+
+    def sweep():
+        for i in range(tpb):
+            lo, hi = i * bm, min((i + 1) * bm, mb)
+            if i not in done and all(present[p][lo:hi].all() for p in present):
+                done.add(i)
+                seq.append((rank, i))
+    sweep()
+    for c in order:
+        p, j = divmod(c, cpb)
+        present[p][j * cr:(j + 1) * cr] = True
+        sweep()
+    return seq
+
+
+@pytest.mark.parametrize("world,rank,mb,cr,bm", [(8, 0, 1024, 128, 256), (2, 1, 64, 16, 32),
+                                                  (4, 2, 30, 5, 8), (3, 0, 12, 12, 5)])
+def test_rs_mtile_order_vs_simulation(world, rank, mb, cr, bm):
+    order = inputs.seeded_order(world, rank, mb // cr, 99)
+    assert O.rs_mtile_order(world, rank, mb, cr, order, bm) == _simulate_rs(world, rank, mb, cr, order, bm)
+
+
+# ------------------------------------------------------------------ planted mistakes
+
+def _ag_transposed_b(shards, b, dtype="bf16", sa=1.0, sb=1.0):
+    a = O.decode_bf16(O.gather_ref(shards))
+    bb = O.decode_bf16(b)
+    return a @ bb.T.reshape(bb.shape) if bb.shape[0] == bb.shape[1] else a @ bb[::-1]
+
+
+def _ag_arrival_concat(shards, b, dtype="bf16", sa=1.0, sb=1.0):
+    a = O.decode_bf16(np.concatenate(shards[::-1], axis=0))
+    return a @ O.decode_bf16(b)
+
+
+def _rs_drop_last_peer(a, b, peers, world, rank, dtype="bf16"):
+    send, out = O.gemm_rs_ref(a, b, peers, world, rank)
+    last = max(q for q in range(world) if q != rank)
+    return send, out - np.asarray(peers, dtype=np.float64)[last]
+
+
+def _decode_e4m3_wrong_bias(bits):
+    return O.decode_e4m3fn(bits) * 2.0
+
+
+@pytest.mark.parametrize("mutant", ["transposed_b", "arrival_concat"])
+def test_planted_ag_mistakes_fail_the_pins(mutant):
+    fn = {"transposed_b": _ag_transposed_b, "arrival_concat": _ag_arrival_concat}[mutant]
+    failed = False
+    for case in _golden()["ag"]:
+        if case["dtype"] != "bf16":
+            continue
+        shards = [_bf16_bits(s) for s in case["shards"]]
+        c = fn(shards, _bf16_bits(case["b"]))
+        if c.shape != np.array(case["c"]).shape or not np.array_equal(c, np.array(case["c"], dtype=np.float64)):
+            failed = True
+    assert failed
+
+
+def test_planted_rs_mistake_fails_the_pin():
+    case = _golden()["rs"][0]
+    send, out = _rs_drop_last_peer(_bf16_bits(case["a"]), _bf16_bits(case["b"]),
+                                   np.array(case["peers"], dtype=np.float32), case["world"], case["rank"])
+    assert not np.array_equal(out, np.array(case["out"], dtype=np.float64))
+
+
+def test_planted_decoder_mistake_fails_the_pin():
+    allb = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(allb).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    bad = _decode_e4m3_wrong_bias(allb)
+    ok = ~np.isnan(ref)
+    assert not np.array_equal(bad[ok], ref[ok])
+
+
+def test_planted_schedule_mistake_fails_the_pin():
+    """A schedule that ignores arrival order (plain ascending tiles) fails the simulation."""
+    world, rank, ms, cr, bm = 8, 0, 512, 128, 256
+    order = inputs.ring_order(world, rank, ms // cr)[::-1]
+    naive = list(range(world * ms // bm))
+    assert naive != _simulate_ag(world, rank, ms, cr, order, bm)
