@@ -1,0 +1,281 @@
+"""ctypes binding of libagg (include/agg.h): the same entry points, argument marshalling only.
+
+Tensors are accepted wherever the C call takes a device pointer (their data_ptr() is passed),
+Python sequences wherever it takes a host array, and torch streams wherever it takes a stream.
+Every call returns None or raises AggError carrying the C status code and agg_last_error().
+All computation happens in the library; nothing here falls back to another implementation: a
+missing or unloadable library is an error.
+
+torch is imported before the library is loaded, so libagg binds to the HIP runtime torch already
+loaded (same soname) and torch's stream handles are valid for it.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch  # noqa: F401  (load order: torch's HIP runtime first)
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libagg.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "agg.h")
+
+AGG_OK, AGG_E_ARG, AGG_E_UNSUPPORTED, AGG_E_HIP, AGG_E_TIMEOUT, AGG_E_STATE = range(6)
+AGG_BF16, AGG_FP8_E4M3 = 0, 1
+AGG_OVERLAP, AGG_SERIAL, AGG_GEMM_ONLY, AGG_COPY_ONLY = range(4)
+MODES = {"overlap": AGG_OVERLAP, "serial": AGG_SERIAL, "gemm_only": AGG_GEMM_ONLY,
+         "copy_only": AGG_COPY_ONLY}
+DTYPES = {"bf16": AGG_BF16, "fp8": AGG_FP8_E4M3}
+MAX_ROW_TILES = 1024
+
+_c_int, _c_i64, _c_u32, _c_u64, _c_f32 = (ctypes.c_int, ctypes.c_int64, ctypes.c_uint32,
+                                          ctypes.c_uint64, ctypes.c_float)
+_vp, _sz = ctypes.c_void_p, ctypes.c_size_t
+_i32p, _u32p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_uint32)
+
+_SIGNATURES = {
+    "agg_ctx_create": [_c_int, ctypes.POINTER(_vp)],
+    "agg_ctx_destroy": [_vp],
+    "agg_ctx_reset": [_vp, _vp],
+    "agg_ctx_status": [_vp, _vp, _u32p, _i32p],
+    "agg_ctx_epoch": [_vp, _u32p],
+    "agg_ctx_set_epoch": [_vp, _c_u32],
+    "agg_ctx_set_timeout_us": [_vp, _c_u64],
+    "agg_ctx_set_tile": [_vp, _c_int, _c_int],
+    "agg_set_trace": [_vp, _vp, _sz],
+    "agg_put_signal": [_vp, _vp, _sz, _vp, _c_u32, _vp],
+    "agg_ctx_set_copy_streams": [_vp, _c_int],
+    "agg_ctx_set_reserved_cus": [_vp, _c_int],
+    "ag_gemm": [_vp, _c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_f32, _c_f32,
+                ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _i32p, _c_int, _u32p, _c_int, _vp, _vp],
+    "gemm_rs": [_vp, _c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp, _vp, _vp,
+                ctypes.POINTER(_vp), _vp, _vp, _vp, _i32p, _c_int, _u32p, _c_int, _vp, _vp],
+    "agg_transpose_kn_to_nk": [_vp, _vp, _c_i64, _c_i64, _c_int, _vp],
+    "agg_tile_shape": [_c_int, _c_int, _c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_int),
+                       ctypes.POINTER(_c_int)],
+    "agg_ag_row_tile_order": [_c_int, _c_int, _c_i64, _c_int, _i32p, _c_int, _c_int, _i32p,
+                              _c_int, ctypes.POINTER(_c_int)],
+    "agg_rs_row_tile_order": [_c_int, _c_int, _c_i64, _c_int, _i32p, _c_int, _c_int, _i32p,
+                              _c_int, ctypes.POINTER(_c_int)],
+    "agg_check_ag_args": [_c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_f32, _c_f32,
+                          ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _i32p, _c_int, _c_int, _vp, _vp],
+    "agg_check_rs_args": [_c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp, _vp, _vp,
+                          ctypes.POINTER(_vp), _vp, _vp, _vp, _i32p, _c_int, _c_int, _vp, _vp],
+}
+
+_lib = None
+
+
+class AggError(RuntimeError):
+    def __init__(self, code: int, where: str, text: str):
+        super().__init__(f"{where} failed with status {code}: {text}")
+        self.code = code
+
+
+def header_functions() -> list:
+    """Names of the functions include/agg.h declares."""
+    with open(HEADER) as f:
+        src = f.read()
+    return re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", src, flags=re.M)
+
+
+def load(path: str | None = None):
+    """Load libagg (building it first only if no built library exists) and declare signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        from . import build
+        build.build(verbose=False)
+    lib = ctypes.CDLL(p)
+    for name, args in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = _c_int
+    lib.agg_last_error.argtypes = []
+    lib.agg_last_error.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _call(name: str, *args) -> None:
+    lib = load()
+    rc = getattr(lib, name)(*args)
+    if rc != AGG_OK:
+        raise AggError(rc, name, lib.agg_last_error().decode())
+
+
+# ------------------------------------------------------------------------------ marshalling
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, torch.cuda.Stream):
+        return s.cuda_stream
+    return int(s)
+
+
+def _ptr_array(seq):
+    if seq is None:
+        return None
+    return (_vp * len(seq))(*[_ptr(x) for x in seq])
+
+
+def _i32_array(seq):
+    if seq is None:
+        return None, 0
+    return (ctypes.c_int32 * len(seq))(*[int(v) for v in seq]), len(seq)
+
+
+def _u32_array(seq):
+    if seq is None:
+        return None
+    return (ctypes.c_uint32 * len(seq))(*[int(v) for v in seq])
+
+
+def _mode(mode):
+    return MODES[mode] if isinstance(mode, str) else int(mode)
+
+
+def _dtype(dtype):
+    return DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+# ------------------------------------------------------------------------------ entry points
+
+def agg_ctx_create(device: int = 0) -> ctypes.c_void_p:
+    out = _vp()
+    _call("agg_ctx_create", device, ctypes.byref(out))
+    return out
+
+
+def agg_ctx_destroy(ctx) -> None:
+    _call("agg_ctx_destroy", ctx)
+
+
+def agg_ctx_reset(ctx, stream=None) -> None:
+    _call("agg_ctx_reset", ctx, _stream(stream))
+
+
+def agg_ctx_status(ctx, stream=None):
+    """Returns (status, failed_chunk); does not raise on a timeout status."""
+    lib = load()
+    st, fc = ctypes.c_uint32(), ctypes.c_int32()
+    rc = lib.agg_ctx_status(ctx, _stream(stream), ctypes.byref(st), ctypes.byref(fc))
+    if rc not in (AGG_OK, AGG_E_TIMEOUT):
+        raise AggError(rc, "agg_ctx_status", lib.agg_last_error().decode())
+    return st.value, fc.value
+
+
+def agg_ctx_epoch(ctx) -> int:
+    e = ctypes.c_uint32()
+    _call("agg_ctx_epoch", ctx, ctypes.byref(e))
+    return e.value
+
+
+def agg_ctx_set_epoch(ctx, epoch: int) -> None:
+    _call("agg_ctx_set_epoch", ctx, epoch)
+
+
+def agg_ctx_set_timeout_us(ctx, timeout_us: int) -> None:
+    _call("agg_ctx_set_timeout_us", ctx, timeout_us)
+
+
+def agg_ctx_set_tile(ctx, bm: int = 0, bn: int = 0) -> None:
+    _call("agg_ctx_set_tile", ctx, bm, bn)
+
+
+def agg_set_trace(ctx, buf=None, nbytes: int = 0) -> None:
+    _call("agg_set_trace", ctx, _ptr(buf), nbytes)
+
+
+def agg_put_signal(dst, src, nbytes: int, flag, value: int, copy_stream) -> None:
+    _call("agg_put_signal", _ptr(dst), _ptr(src), nbytes, _ptr(flag), value, _stream(copy_stream))
+
+
+def agg_ctx_set_copy_streams(ctx, n: int) -> None:
+    _call("agg_ctx_set_copy_streams", ctx, n)
+
+
+def agg_ctx_set_reserved_cus(ctx, n: int) -> None:
+    _call("agg_ctx_set_reserved_cus", ctx, n)
+
+
+def ag_gemm(ctx, world, rank, m_shard, n, k, chunk_rows, dtype, scale_a, scale_b, peer_src,
+            gather, flags, b, c, order=None, delay_us=None, mode="overlap", stream=None,
+            copy_stream=None) -> None:
+    ordr, n_order = _i32_array(order)
+    _call("ag_gemm", ctx, world, rank, m_shard, n, k, chunk_rows, _dtype(dtype), scale_a, scale_b,
+          _ptr_array(peer_src), _ptr(gather), _ptr(flags), _ptr(b), _ptr(c), ordr, n_order,
+          _u32_array(delay_us), _mode(mode), _stream(stream), _stream(copy_stream))
+
+
+def gemm_rs(ctx, world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_src, recv, flags,
+            out, order=None, delay_us=None, mode="overlap", stream=None, copy_stream=None) -> None:
+    ordr, n_order = _i32_array(order)
+    _call("gemm_rs", ctx, world, rank, m, n, k, chunk_rows, _ptr(a), _ptr(b), _ptr(send),
+          _ptr(send_flags), _ptr_array(peer_src), _ptr(recv), _ptr(flags), _ptr(out), ordr,
+          n_order, _u32_array(delay_us), _mode(mode), _stream(stream), _stream(copy_stream))
+
+
+def agg_transpose_kn_to_nk(src, dst, k: int, n: int, elem_bytes: int, stream=None) -> None:
+    _call("agg_transpose_kn_to_nk", _ptr(src), _ptr(dst), k, n, elem_bytes, _stream(stream))
+
+
+def agg_tile_shape(op: int, dtype, m: int, n: int, k: int):
+    bm, bn = _c_int(), _c_int()
+    _call("agg_tile_shape", op, _dtype(dtype), m, n, k, ctypes.byref(bm), ctypes.byref(bn))
+    return bm.value, bn.value
+
+
+def _tile_order(name, world, rank, size, chunk_rows, order, bm):
+    ordr, n_order = _i32_array(order)
+    cap = MAX_ROW_TILES * 64
+    out = (ctypes.c_int32 * cap)()
+    n = _c_int()
+    _call(name, world, rank, size, chunk_rows, ordr, n_order, bm, out, cap, ctypes.byref(n))
+    return list(out[:n.value])
+
+
+def agg_ag_row_tile_order(world, rank, m_shard, chunk_rows, order, bm) -> list:
+    return _tile_order("agg_ag_row_tile_order", world, rank, m_shard, chunk_rows, order, bm)
+
+
+def agg_rs_row_tile_order(world, rank, m, chunk_rows, order, bm) -> list:
+    return _tile_order("agg_rs_row_tile_order", world, rank, m, chunk_rows, order, bm)
+
+
+def agg_check_ag_args(world, rank, m_shard, n, k, chunk_rows, dtype, scale_a, scale_b, peer_src,
+                      gather, flags, b, c, order=None, mode="overlap", stream=None,
+                      copy_stream=None) -> int:
+    """Returns the status code (does not raise) so tests can check each error code."""
+    ordr, n_order = _i32_array(order)
+    return load().agg_check_ag_args(world, rank, m_shard, n, k, chunk_rows, _dtype(dtype), scale_a,
+                                    scale_b, _ptr_array(peer_src), _ptr(gather), _ptr(flags),
+                                    _ptr(b), _ptr(c), ordr, n_order, _mode(mode), _stream(stream),
+                                    _stream(copy_stream))
+
+
+def agg_check_rs_args(world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_src, recv,
+                      flags, out, order=None, mode="overlap", stream=None, copy_stream=None) -> int:
+    ordr, n_order = _i32_array(order)
+    return load().agg_check_rs_args(world, rank, m, n, k, chunk_rows, _ptr(a), _ptr(b), _ptr(send),
+                                    _ptr(send_flags), _ptr_array(peer_src), _ptr(recv), _ptr(flags),
+                                    _ptr(out), ordr, n_order, _mode(mode), _stream(stream),
+                                    _stream(copy_stream))
+
+
+def last_error() -> str:
+    return load().agg_last_error().decode()

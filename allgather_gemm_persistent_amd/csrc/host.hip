@@ -1,0 +1,597 @@
+// libagg host runtime: the ctx, the producer (put + signal without compute units) and the C entry
+// points ag_gemm / gemm_rs / agg_put_signal.
+//
+// Method: page "Triton-distributed is turning communication into compiler territory", section
+// "The first move was to expose the overlap": chunked transfers and computation proceed together
+// instead of one after the other; the primitives are symmetric memory, remote data access,
+// signaling and asynchronous tasks. Section "DITRON adds three levels of tiling": device-level
+// tiles are data movements mapped onto DMA engines; collectives are chunked and paired with
+// computation tiles with synchronization inserted.
+//
+// One chunk's "remote access" is a copy (hipMemcpyDeviceToDeviceNoCU) from the emulated peer's
+// memory into the symmetric gather buffer; its "signal" is hipStreamWriteValue32 of the call's
+// epoch into the chunk's flag word on the same stream, so stream order puts the flag after the
+// data.
+//
+// The producer needs a few free compute units. Measured under a grid that holds every wave slot
+// of every CU: in the HIP runtime that ships with torch, the stream write, memsets,
+// host-to-device copies and device-to-device copies below 64 KiB or from 1 MiB up all run as
+// runtime kernels and never start, so the consumer would wait for them forever (until its
+// timeout). In overlap mode the persistent grid therefore leaves `reserved_cus` CUs to the
+// producer (default 32, four per XCD: workgroups are dealt round-robin over the XCDs and one
+// fills a CU; 8 and 16 free CUs were measured to still starve it); every other mode uses all
+// CUs.
+//
+// Chunks are spread over several copy streams (chunk i of the arrival order on stream i mod S),
+// each stream feeding its own SDMA engine the way W-1 peers feed separate links; every stream
+// keeps the arrival order, so chunks land in that order in groups of S.
+//
+// Every stream the ctx launches work on (the consumer kernel's and the copy streams) is created
+// with a CU mask (all CUs), which gives it a hardware queue of its own. A shared queue deadlocks
+// the overlap: the runtime may hand a stream write that follows an SDMA copy to the hardware only
+// after the copy finishes, and if another stream has meanwhile put a barrier that waits for the
+// persistent kernel into the same queue (the caller joining the kernel, say), the late write
+// sits behind that barrier while the kernel waits for the write.
+//
+// Flags only grow within an epoch cycle (1 .. 0xFFFFFFFE); when the epoch would pass the end of
+// the cycle the ctx zero-fills every flags buffer bound to it and starts again at 1.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "kernels.h"
+#include "plan.h"
+
+using namespace agg;
+
+namespace {
+
+constexpr uint32_t kEpochLast = 0xFFFFFFFEu;   // 0xFFFFFFFF means "no flag" in traces
+constexpr int kMaxCopyStreams = 8;
+constexpr int kDefaultCopyStreams = 4;
+constexpr int kDefaultReservedCus = 32;
+
+enum FlagSlot { kFlagsAg = 0, kFlagsRsRecv = 1, kFlagsRsSend = 2, kFlagSlots = 3 };
+
+}  // namespace
+
+struct agg_ctx {
+  int device = 0;
+  int cus = 0;
+  int lists = 8;                    // claim lists: one per XCD of an MI355X
+  uint32_t* scratch = nullptr;      // kScrWords words
+  uint32_t epoch = 0;
+  uint64_t timeout_us = 2000000;
+  double ticks_per_us = 100.0;
+  int force_bm = 0, force_bn = 0;   // 0: automatic tile shape
+  int n_copy = kDefaultCopyStreams;
+  int reserved_cus = kDefaultReservedCus;   // CUs the overlapped grid leaves to the producer
+  hipStream_t ks = nullptr;                           // consumer kernel stream (own HW queue)
+  hipStream_t cstream[kMaxCopyStreams] = {};          // copy streams (own HW queues), lazily made
+  hipEvent_t ev_fork = nullptr, ev_kernel = nullptr, ev_user = nullptr;
+  hipEvent_t ev_copy[kMaxCopyStreams] = {};
+  uint32_t* trace = nullptr;
+  size_t trace_bytes = 0;
+  uint32_t* bound[kFlagSlots] = {nullptr, nullptr, nullptr};
+  size_t bound_words[kFlagSlots] = {0, 0, 0};
+};
+
+namespace {
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(AGG_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+int elem_bytes(int dtype) { return dtype == AGG_FP8_E4M3 ? 1 : 2; }
+
+hipStream_t S(agg_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+void busy_wait_us(uint32_t us) {
+  if (!us) return;
+  auto end = std::chrono::steady_clock::now() + std::chrono::microseconds(us);
+  while (std::chrono::steady_clock::now() < end) {
+  }
+}
+
+int bind_flags(agg_ctx* ctx, int slot, uint32_t* p, size_t words) {
+  if (!p || words == 0) return AGG_OK;
+  if (ctx->bound[slot] == nullptr) {
+    ctx->bound[slot] = p;
+    ctx->bound_words[slot] = words;
+    return AGG_OK;
+  }
+  if (ctx->bound[slot] != p)
+    return fail(AGG_E_STATE, "a different flags buffer is bound to this ctx; call agg_ctx_reset first");
+  ctx->bound_words[slot] = std::max(ctx->bound_words[slot], words);
+  return AGG_OK;
+}
+
+// Advance the epoch for a producing call; at the end of a cycle zero-fill the bound flags on
+// `stream` first (earlier producers were joined into `stream`, so this is ordered after them).
+int next_epoch(agg_ctx* ctx, hipStream_t stream, uint32_t* out) {
+  if (ctx->epoch >= kEpochLast) {
+    for (int s = 0; s < kFlagSlots; ++s)
+      if (ctx->bound[s]) HIP_TRY(launch_fill_u32(ctx->bound[s], ctx->bound_words[s], 0u, stream));
+    ctx->epoch = 0;
+  }
+  ctx->epoch += 1;
+  *out = ctx->epoch;
+  return AGG_OK;
+}
+
+int put_signal(void* dst, const void* src, size_t bytes, uint32_t* flag, uint32_t value, hipStream_t cs) {
+  if (bytes) HIP_TRY(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDeviceNoCU, cs));
+  HIP_TRY(hipStreamWriteValue32(cs, flag, value, 0));
+  return AGG_OK;
+}
+
+// Chunk q of peer p: rows [q*cr, (q+1)*cr) of peer p's block, landing at rows
+// p*slot_rows + q*cr of the symmetric buffer.
+struct ChunkCopy {
+  const uint8_t* const* src;   // [world] per-peer base
+  uint8_t* dst;                // symmetric buffer base
+  int64_t slot_rows, cr, row_bytes;
+  int cps;
+};
+
+hipError_t make_own_queue_stream(agg_ctx* ctx, hipStream_t* out) {
+  std::vector<uint32_t> mask(size_t((ctx->cus + 31) / 32), 0xFFFFFFFFu);
+  return hipExtStreamCreateWithCUMask(out, uint32_t(mask.size()), mask.data());
+}
+
+// The ctx copy streams a call uses (created on first use).
+int copy_streams(agg_ctx* ctx, size_t chunks, std::vector<hipStream_t>& out) {
+  const int n = int(std::max<size_t>(1, std::min<size_t>(size_t(ctx->n_copy), chunks)));
+  out.clear();
+  for (int i = 0; i < n; ++i) {
+    if (!ctx->cstream[i]) HIP_TRY(make_own_queue_stream(ctx, &ctx->cstream[i]));
+    out.push_back(ctx->cstream[i]);
+  }
+  return AGG_OK;
+}
+
+int produce(const ChunkCopy& cc, uint32_t* flags, const std::vector<int32_t>& order,
+            const uint32_t* delay_us, uint32_t epoch, const std::vector<hipStream_t>& streams) {
+  const size_t bytes = size_t(cc.cr * cc.row_bytes);
+  for (size_t i = 0; i < order.size(); ++i) {
+    const int c = order[i];
+    const int p = c / cc.cps, q = c % cc.cps;
+    if (delay_us) busy_wait_us(delay_us[i]);
+    const uint8_t* src = cc.src[p] + size_t(q) * bytes;
+    uint8_t* dst = cc.dst + size_t(p * cc.slot_rows + q * cc.cr) * size_t(cc.row_bytes);
+    if (int rc = put_signal(dst, src, bytes, flags + c, epoch, streams[i % streams.size()])) return rc;
+  }
+  return AGG_OK;
+}
+
+TileShape tile_for(agg_ctx* ctx, int op, int dtype, int64_t m, int64_t n, int64_t k) {
+  if (ctx->force_bm) return TileShape{ctx->force_bm, ctx->force_bn};
+  return choose_tile(op, dtype, m, n, k);
+}
+
+// Workgroups of the persistent grid: one per CU (a workgroup fills a CU), minus the CUs left to
+// the producer when chunks arrive while the kernel runs.
+int grid_for(agg_ctx* ctx, int64_t tiles, bool overlapped) {
+  int64_t units = ctx->cus - (overlapped ? ctx->reserved_cus : 0);
+  int64_t g = std::min<int64_t>(std::max<int64_t>(units, 1), tiles);
+  return int(std::max<int64_t>(g, 1));
+}
+
+// Stream choreography shared by ag_gemm and gemm_rs. `launch` enqueues the consumer kernel on
+// ctx->ks, `put_all` the producer's copies and flags on the copy streams.
+//   OVERLAP:   stream -> {ks, copy streams}; kernel and chunks run together; all -> stream
+//   SERIAL:    stream -> copy streams; all chunks; copy streams -> ks; kernel; ks -> stream
+//   GEMM_ONLY: stream -> ks; kernel; ks -> stream
+//   COPY_ONLY: stream -> copy streams; all chunks; copy streams -> stream
+// A non-NULL user copy stream `us` is joined too: the copies start after earlier work on it, and
+// later work on it starts after the copies.
+template <typename Launch, typename Put>
+int schedule(agg_ctx* ctx, int mode, hipStream_t s, hipStream_t us,
+             const std::vector<hipStream_t>& cstreams, bool kernel, Launch launch, bool chunks,
+             Put put_all) {
+  HIP_TRY(hipEventRecord(ctx->ev_fork, s));
+  if (chunks) {
+    if (us) HIP_TRY(hipEventRecord(ctx->ev_user, us));
+    for (hipStream_t c : cstreams) {
+      HIP_TRY(hipStreamWaitEvent(c, ctx->ev_fork, 0));
+      if (us) HIP_TRY(hipStreamWaitEvent(c, ctx->ev_user, 0));
+    }
+  }
+  auto join_copies = [&](hipStream_t into) -> int {
+    for (size_t j = 0; j < cstreams.size(); ++j) {
+      HIP_TRY(hipEventRecord(ctx->ev_copy[j], cstreams[j]));
+      HIP_TRY(hipStreamWaitEvent(into, ctx->ev_copy[j], 0));
+      if (us) HIP_TRY(hipStreamWaitEvent(us, ctx->ev_copy[j], 0));
+    }
+    return AGG_OK;
+  };
+  if (mode == AGG_OVERLAP) {
+    if (kernel) {
+      HIP_TRY(hipStreamWaitEvent(ctx->ks, ctx->ev_fork, 0));
+      if (int rc = launch()) return rc;
+    }
+    if (chunks) {
+      if (int rc = put_all()) return rc;
+      if (int rc = join_copies(s)) return rc;
+    }
+  } else {
+    if (chunks) {
+      if (int rc = put_all()) return rc;
+      if (int rc = join_copies(kernel ? ctx->ks : s)) return rc;
+    }
+    if (kernel) {
+      HIP_TRY(hipStreamWaitEvent(ctx->ks, ctx->ev_fork, 0));
+      if (int rc = launch()) return rc;
+    }
+  }
+  if (kernel) {
+    HIP_TRY(hipEventRecord(ctx->ev_kernel, ctx->ks));
+    HIP_TRY(hipStreamWaitEvent(s, ctx->ev_kernel, 0));
+  }
+  return AGG_OK;
+}
+
+void fill_common(agg_ctx* ctx, GemmArgs& g) {
+  g.scratch = ctx->scratch;
+  g.n_lists = std::min(ctx->lists, kMaxLists);
+  g.timeout_ticks = uint64_t(double(ctx->timeout_us) * ctx->ticks_per_us);
+}
+
+void attach_trace(agg_ctx* ctx, GemmArgs& g, int64_t tiles) {
+  if (ctx->trace && ctx->trace_bytes / 32 >= size_t(tiles)) {
+    g.trace = ctx->trace;
+    g.trace_tiles = uint32_t(tiles);
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------
+// ctx
+// ------------------------------------------------------------------------------------------
+
+extern "C" int agg_ctx_create(int device, agg_ctx** out) {
+  clear_error();
+  if (!out) return fail(AGG_E_ARG, "out is NULL");
+  *out = nullptr;
+  int count = 0;
+  HIP_TRY(hipGetDeviceCount(&count));
+  if (device < 0 || device >= count) return fail(AGG_E_ARG, "device %d not in [0, %d)", device, count);
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, device));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(AGG_E_UNSUPPORTED, "device %d is %s, libagg is built for gfx950 only", device, prop.gcnArchName);
+  int prev = 0;
+  HIP_TRY(hipGetDevice(&prev));
+  HIP_TRY(hipSetDevice(device));
+  agg_ctx* ctx = new agg_ctx;
+  ctx->device = device;
+  ctx->cus = prop.multiProcessorCount;
+  int rate_khz = 0;
+  if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && rate_khz > 0)
+    ctx->ticks_per_us = rate_khz / 1000.0;
+  int rc = AGG_OK;
+  auto step = [&](hipError_t e, const char* what) {
+    if (rc == AGG_OK && e != hipSuccess) rc = fail(AGG_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  };
+  step(hipMalloc(&ctx->scratch, kScrWords * sizeof(uint32_t)), "hipMalloc(scratch)");
+  if (rc == AGG_OK) {
+    std::vector<uint32_t> host(kScrWords, 0u);
+    host[kScrFailed] = 0xFFFFFFFFu;
+    step(hipMemcpy(ctx->scratch, host.data(), kScrWords * sizeof(uint32_t), hipMemcpyHostToDevice),
+         "hipMemcpy(scratch)");
+  }
+  step(hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming), "hipEventCreate");
+  step(hipEventCreateWithFlags(&ctx->ev_kernel, hipEventDisableTiming), "hipEventCreate");
+  step(hipEventCreateWithFlags(&ctx->ev_user, hipEventDisableTiming), "hipEventCreate");
+  for (int j = 0; j < kMaxCopyStreams; ++j)
+    step(hipEventCreateWithFlags(&ctx->ev_copy[j], hipEventDisableTiming), "hipEventCreate");
+  if (rc == AGG_OK) step(make_own_queue_stream(ctx, &ctx->ks), "hipExtStreamCreateWithCUMask");
+  step(hipSetDevice(prev), "hipSetDevice");
+  if (rc != AGG_OK) {
+    agg_ctx_destroy(ctx);
+    return rc;
+  }
+  *out = ctx;
+  return AGG_OK;
+}
+
+extern "C" int agg_ctx_destroy(agg_ctx* ctx) {
+  clear_error();
+  if (!ctx) return AGG_OK;
+  // best effort: release everything even if one call fails, report the first failure
+  int rc = AGG_OK;
+  auto step = [&](hipError_t e, const char* what) {
+    if (rc == AGG_OK && e != hipSuccess) rc = fail(AGG_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  };
+  int prev = 0;
+  step(hipGetDevice(&prev), "hipGetDevice");
+  step(hipSetDevice(ctx->device), "hipSetDevice");
+  step(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  if (ctx->scratch) step(hipFree(ctx->scratch), "hipFree(scratch)");
+  for (hipEvent_t e : {ctx->ev_fork, ctx->ev_kernel, ctx->ev_user})
+    if (e) step(hipEventDestroy(e), "hipEventDestroy");
+  for (int j = 0; j < kMaxCopyStreams; ++j) {
+    if (ctx->ev_copy[j]) step(hipEventDestroy(ctx->ev_copy[j]), "hipEventDestroy");
+    if (ctx->cstream[j]) step(hipStreamDestroy(ctx->cstream[j]), "hipStreamDestroy");
+  }
+  if (ctx->ks) step(hipStreamDestroy(ctx->ks), "hipStreamDestroy");
+  step(hipSetDevice(prev), "hipSetDevice");
+  delete ctx;
+  return rc;
+}
+
+extern "C" int agg_ctx_reset(agg_ctx* ctx, agg_stream stream) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  HIP_TRY(hipSetDevice(ctx->device));
+  HIP_TRY(hipDeviceSynchronize());
+  for (int s = 0; s < kFlagSlots; ++s) {
+    if (ctx->bound[s]) HIP_TRY(launch_fill_u32(ctx->bound[s], ctx->bound_words[s], 0u, S(stream)));
+    ctx->bound[s] = nullptr;
+    ctx->bound_words[s] = 0;
+  }
+  HIP_TRY(launch_fill_u32(ctx->scratch, kScrWords, 0u, S(stream)));
+  HIP_TRY(launch_fill_u32(ctx->scratch + kScrFailed, 1, 0xFFFFFFFFu, S(stream)));
+  HIP_TRY(hipStreamSynchronize(S(stream)));
+  ctx->epoch = 0;
+  return AGG_OK;
+}
+
+extern "C" int agg_ctx_status(agg_ctx* ctx, agg_stream stream, uint32_t* status, int32_t* failed_chunk) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  HIP_TRY(hipSetDevice(ctx->device));
+  HIP_TRY(hipStreamSynchronize(S(stream)));
+  uint32_t words[2] = {0, 0};
+  HIP_TRY(hipMemcpy(words, ctx->scratch + kScrStatus, sizeof words, hipMemcpyDeviceToHost));
+  if (status) *status = words[0];
+  if (failed_chunk) *failed_chunk = words[1] == 0xFFFFFFFFu ? -1 : int32_t(words[1]);
+  if (words[0]) return fail(AGG_E_TIMEOUT, "a chunk wait gave up (flag %d)", words[1] == 0xFFFFFFFFu ? -1 : int(words[1]));
+  return AGG_OK;
+}
+
+extern "C" int agg_ctx_epoch(agg_ctx* ctx, uint32_t* epoch) {
+  clear_error();
+  if (!ctx || !epoch) return fail(AGG_E_ARG, "NULL argument");
+  *epoch = ctx->epoch;
+  return AGG_OK;
+}
+
+extern "C" int agg_ctx_set_epoch(agg_ctx* ctx, uint32_t epoch) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (epoch > kEpochLast) return fail(AGG_E_ARG, "epoch %u beyond %u", epoch, kEpochLast);
+  for (int s = 0; s < kFlagSlots; ++s)
+    if (ctx->bound[s]) return fail(AGG_E_STATE, "flags are bound; call agg_ctx_reset first");
+  ctx->epoch = epoch;
+  return AGG_OK;
+}
+
+extern "C" int agg_ctx_set_timeout_us(agg_ctx* ctx, uint64_t timeout_us) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (timeout_us == 0 || timeout_us > 30000000ull) return fail(AGG_E_ARG, "timeout must be in (0, 30 s]");
+  ctx->timeout_us = timeout_us;
+  return AGG_OK;
+}
+
+extern "C" int agg_ctx_set_tile(agg_ctx* ctx, int bm, int bn) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (bm == 0 && bn == 0) {
+    ctx->force_bm = ctx->force_bn = 0;
+    return AGG_OK;
+  }
+  for (const TileShape& t : tile_shapes())
+    if (t.bm == bm && t.bn == bn) {
+      ctx->force_bm = bm;
+      ctx->force_bn = bn;
+      return AGG_OK;
+    }
+  return fail(AGG_E_ARG, "no kernel for a %dx%d tile", bm, bn);
+}
+
+extern "C" int agg_ctx_set_reserved_cus(agg_ctx* ctx, int n) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (n < 0 || n >= ctx->cus) return fail(AGG_E_ARG, "reserved CUs must be in [0, %d)", ctx->cus);
+  ctx->reserved_cus = n;
+  return AGG_OK;
+}
+
+extern "C" int agg_ctx_set_copy_streams(agg_ctx* ctx, int n) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (n < 1 || n > kMaxCopyStreams) return fail(AGG_E_ARG, "copy streams must be in [1, %d]", kMaxCopyStreams);
+  ctx->n_copy = n;
+  return AGG_OK;
+}
+
+extern "C" int agg_set_trace(agg_ctx* ctx, void* dev_buf, size_t bytes) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (dev_buf && (reinterpret_cast<uintptr_t>(dev_buf) & 3u)) return fail(AGG_E_ARG, "trace buffer not 4-byte aligned");
+  ctx->trace = bytes >= 32 ? static_cast<uint32_t*>(dev_buf) : nullptr;
+  ctx->trace_bytes = ctx->trace ? bytes : 0;
+  return AGG_OK;
+}
+
+extern "C" int agg_put_signal(void* dst, const void* src, size_t bytes, uint32_t* flag, uint32_t value,
+                              agg_stream copy_stream) {
+  clear_error();
+  if (!flag || (bytes && (!dst || !src))) return fail(AGG_E_ARG, "NULL argument");
+  if (reinterpret_cast<uintptr_t>(flag) & 3u) return fail(AGG_E_ARG, "flag not 4-byte aligned");
+  return put_signal(dst, src, bytes, flag, value, S(copy_stream));
+}
+
+extern "C" int agg_transpose_kn_to_nk(const void* src, void* dst, int64_t k, int64_t n, int elem_bytes_,
+                                      agg_stream stream) {
+  clear_error();
+  if (k < 0 || n < 0 || (elem_bytes_ != 1 && elem_bytes_ != 2)) return fail(AGG_E_ARG, "invalid sizes");
+  if (k && n && (!src || !dst)) return fail(AGG_E_ARG, "NULL pointer");
+  HIP_TRY(launch_transpose(src, dst, k, n, elem_bytes_, S(stream)));
+  return AGG_OK;
+}
+
+// ------------------------------------------------------------------------------------------
+// AllGather + GEMM
+// ------------------------------------------------------------------------------------------
+
+extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64_t k,
+                       int chunk_rows, int dtype, float scale_a, float scale_b,
+                       const void* const* peer_src, void* gather, uint32_t* flags, const void* b, void* c,
+                       const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
+                       agg_stream stream, agg_stream copy_stream) {
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (int rc = agg_check_ag_args(world, rank, m_shard, n, k, chunk_rows, dtype, scale_a, scale_b,
+                                 peer_src, gather, flags, b, c, order, n_order, mode, stream, copy_stream))
+    return rc;
+  const int64_t m = int64_t(world) * m_shard;
+  if (m == 0) return AGG_OK;
+  const TileShape ts = tile_for(ctx, 0, dtype, m, n, k);
+  if ((m + ts.bm - 1) / ts.bm > AGG_MAX_ROW_TILES)
+    return fail(AGG_E_UNSUPPORTED, "%lld row tiles exceed %d", (long long)((m + ts.bm - 1) / ts.bm), AGG_MAX_ROW_TILES);
+  HIP_TRY(hipSetDevice(ctx->device));
+  const int cps = int(m_shard / chunk_rows);
+  if (world > 1)
+    if (int rc = bind_flags(ctx, kFlagsAg, flags, size_t(world) * cps)) return rc;
+  const std::vector<int32_t> ord = order ? std::vector<int32_t>(order, order + n_order) : ring_order(world, rank, cps);
+  hipStream_t s = S(stream);
+  const bool kernel = (mode != AGG_COPY_ONLY) && n > 0;
+  const bool chunks = (mode != AGG_GEMM_ONLY) && world > 1;
+  std::vector<hipStream_t> cstreams;
+  if (chunks)
+    if (int rc = copy_streams(ctx, ord.size(), cstreams)) return rc;
+  uint32_t epoch = ctx->epoch;
+  if (chunks)
+    if (int rc = next_epoch(ctx, s, &epoch)) return rc;
+
+  ChunkCopy cc;
+  cc.src = reinterpret_cast<const uint8_t* const*>(peer_src);
+  cc.dst = static_cast<uint8_t*>(gather);
+  cc.slot_rows = m_shard;
+  cc.cr = chunk_rows;
+  cc.row_bytes = k * elem_bytes(dtype);
+  cc.cps = cps;
+
+  GemmArgs g;
+  std::memset(&g, 0, sizeof g);
+  int64_t tiles = 0;
+  if (kernel) {
+    const std::vector<int32_t> rows = ag_row_tile_order(world, rank, m_shard, chunk_rows, ord, ts.bm);
+    for (size_t i = 0; i < rows.size(); ++i) g.row_order[i] = uint16_t(rows[i]);
+    g.a = static_cast<const uint8_t*>(gather);
+    g.b = static_cast<const uint8_t*>(b);
+    g.c = static_cast<uint16_t*>(c);
+    g.flags = flags;
+    g.M = m;
+    g.N = n;
+    g.K = k;
+    g.world = world;
+    g.rank = rank;
+    g.chunk_rows = chunk_rows;
+    g.cps = cps;
+    g.n_row_tiles = int(rows.size());
+    g.n_col_tiles = int((n + ts.bn - 1) / ts.bn);
+    g.epoch = world > 1 ? epoch : 0;
+    g.scale = dtype == AGG_FP8_E4M3 ? scale_a * scale_b : 1.0f;
+    fill_common(ctx, g);
+    tiles = int64_t(g.n_row_tiles) * g.n_col_tiles;
+    attach_trace(ctx, g, tiles);
+  }
+  auto launch = [&]() -> int {
+    HIP_TRY(launch_gemm(g, ts.bm, ts.bn, dtype, kEpiAllGather, grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks), ctx->ks));
+    return AGG_OK;
+  };
+  return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
+                  [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams); });
+}
+
+// ------------------------------------------------------------------------------------------
+// GEMM + ReduceScatter
+// ------------------------------------------------------------------------------------------
+
+extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, int64_t k, int chunk_rows,
+                       const void* a, const void* b, float* send, uint32_t* send_flags,
+                       const float* const* peer_src, float* recv, uint32_t* flags, float* out,
+                       const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
+                       agg_stream stream, agg_stream copy_stream) {
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (int rc = agg_check_rs_args(world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_src,
+                                 recv, flags, out, order, n_order, mode, stream, copy_stream))
+    return rc;
+  const int64_t mb = m / world;
+  if (mb == 0 || n == 0) return AGG_OK;
+  const TileShape ts = tile_for(ctx, 1, AGG_BF16, m, n, k);
+  if (world * ((mb + ts.bm - 1) / ts.bm) > AGG_MAX_ROW_TILES)
+    return fail(AGG_E_UNSUPPORTED, "row tiles exceed %d", AGG_MAX_ROW_TILES);
+  HIP_TRY(hipSetDevice(ctx->device));
+  const int cpb = int(mb / chunk_rows);
+  if (world > 1) {
+    if (int rc = bind_flags(ctx, kFlagsRsRecv, flags, size_t(world) * cpb)) return rc;
+    if (int rc = bind_flags(ctx, kFlagsRsSend, send_flags, size_t(world) * cpb)) return rc;
+  }
+  const std::vector<int32_t> ord = order ? std::vector<int32_t>(order, order + n_order) : ring_order(world, rank, cpb);
+  hipStream_t s = S(stream);
+  const bool kernel = mode != AGG_COPY_ONLY;
+  const bool chunks = (mode != AGG_GEMM_ONLY) && world > 1;
+  std::vector<hipStream_t> cstreams;
+  if (chunks)
+    if (int rc = copy_streams(ctx, ord.size(), cstreams)) return rc;
+  uint32_t epoch = ctx->epoch;
+  if (chunks)
+    if (int rc = next_epoch(ctx, s, &epoch)) return rc;
+
+  ChunkCopy cc;
+  cc.src = reinterpret_cast<const uint8_t* const*>(peer_src);
+  cc.dst = reinterpret_cast<uint8_t*>(recv);
+  cc.slot_rows = mb;
+  cc.cr = chunk_rows;
+  cc.row_bytes = n * 4;
+  cc.cps = cpb;
+
+  GemmArgs g;
+  std::memset(&g, 0, sizeof g);
+  int64_t tiles = 0;
+  if (kernel) {
+    const std::vector<int32_t> rows = rs_row_tile_order(world, rank, m, chunk_rows, ord, ts.bm);
+    for (size_t i = 0; i < rows.size(); ++i) g.row_order[i] = uint16_t(rows[i]);
+    g.a = static_cast<const uint8_t*>(a);
+    g.b = static_cast<const uint8_t*>(b);
+    g.send = send;
+    g.out = out;
+    g.recv = recv;
+    g.flags = flags;
+    g.send_flags = send_flags;
+    g.M = m;
+    g.N = n;
+    g.K = k;
+    g.m_block = mb;
+    g.world = world;
+    g.rank = rank;
+    g.chunk_rows = chunk_rows;
+    g.cps = cpb;
+    g.tpb = int((mb + ts.bm - 1) / ts.bm);
+    g.n_row_tiles = int(rows.size());
+    g.n_col_tiles = int((n + ts.bn - 1) / ts.bn);
+    g.epoch = world > 1 ? epoch : 0;
+    g.scale = 1.0f;
+    fill_common(ctx, g);
+    tiles = int64_t(g.n_row_tiles) * g.n_col_tiles;
+    attach_trace(ctx, g, tiles);
+  }
+  auto launch = [&]() -> int {
+    HIP_TRY(launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiReduceScatter, grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks), ctx->ks));
+    return AGG_OK;
+  };
+  return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
+                  [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams); });
+}

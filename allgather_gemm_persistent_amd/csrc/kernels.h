@@ -1,0 +1,62 @@
+// Device-side interface of libagg: the argument block of the persistent GEMM kernel, the
+// layout of the ctx's device scratch, and the launch functions (defined in kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/agg.h"
+
+namespace agg {
+
+// ctx scratch, in uint32 words
+constexpr int kScrLists = 0;       // claim-list counters, one per XCD (<= 16)
+constexpr int kScrDone = 16;       // workgroups that finished the current launch
+constexpr int kScrStatus = 17;     // bit 0: a flag wait gave up
+constexpr int kScrFailed = 18;     // first flag index that timed out (0xFFFFFFFF = none)
+constexpr int kScrRsCount = 64;    // ReduceScatter per-send-chunk completion counters
+constexpr int kScrWords = kScrRsCount + AGG_MAX_CHUNKS;
+constexpr int kMaxLists = 16;
+
+enum Epilogue { kEpiAllGather = 0, kEpiReduceScatter = 1 };
+
+struct GemmArgs {
+  const uint8_t* a;         // AG: gather buffer M x K; RS: A, M x K
+  const uint8_t* b;         // N x K (K contiguous)
+  uint16_t* c;              // AG output, M x N bfloat16
+  float* send;              // RS: (world-1) x Mb x N
+  float* out;               // RS: Mb x N
+  const float* recv;        // RS: world x Mb x N
+  const uint32_t* flags;    // flags the tiles wait on (AG gather flags / RS receive flags)
+  uint32_t* send_flags;     // RS
+  uint32_t* scratch;        // ctx scratch (kScr*)
+  uint32_t* trace;          // optional per-tile trace, 8 words per tile
+  int64_t M, N, K;          // K in elements
+  int64_t m_block;          // RS: rows per block (Mb)
+  int world, rank;
+  int chunk_rows, cps;      // rows per chunk, chunks per shard (AG) / per block (RS)
+  int n_row_tiles;          // AG: ceil(M/BM); RS: world * tiles_per_block
+  int n_col_tiles;          // ceil(N/BN)
+  int tpb;                  // RS: row tiles per block
+  int n_lists;              // claim lists (one per XCD)
+  uint32_t epoch;           // flags >= epoch mean "arrived"
+  float scale;              // fp8: scale_a * scale_b; bf16: 1
+  uint64_t timeout_ticks;   // in wall-clock (s_memrealtime) ticks
+  uint32_t trace_tiles;     // capacity of `trace` in tiles (0 = off)
+  uint16_t row_order[AGG_MAX_ROW_TILES];  // row tiles in compute order
+};
+
+// Launch the persistent kernel instantiated for (bm, bn, dtype, epilogue) with `grid`
+// workgroups of 256 threads on `stream`. Returns hipErrorInvalidValue for a shape that has no
+// instantiation.
+hipError_t launch_gemm(const GemmArgs& args, int bm, int bn, int dtype, int epilogue, int grid,
+                       hipStream_t stream);
+
+// Fill `words` uint32 at `dst` with `value` (a kernel, not a memset node).
+hipError_t launch_fill_u32(uint32_t* dst, size_t words, uint32_t value, hipStream_t stream);
+
+// dst (n x k) = transpose(src (k x n)), elem_bytes in {1, 2}.
+hipError_t launch_transpose(const void* src, void* dst, int64_t k, int64_t n, int elem_bytes,
+                            hipStream_t stream);
+
+}  // namespace agg

@@ -1,0 +1,521 @@
+// Persistent MFMA GEMM for gfx950 (CDNA4) that consumes rows as their chunks arrive.
+//
+// The method: page "Triton-distributed is turning communication into compiler territory",
+// section "The first move was to expose the overlap" (compute on chunks that arrived while
+// others still move) and section "DITRON adds three levels of tiling" (core-level tiles in
+// registers / shared memory / matrix units; collectives cut into chunks paired with compute
+// tiles, with synchronization inserted).
+//
+// Design, per workgroup (256 threads = 4 wave64s in a 2 x 2 grid):
+//   loop:
+//     claim a tile from this XCD's list (atomic counter), stealing from other XCDs' lists when
+//       its own is exhausted; lists hold row tiles in arrival order, so early chunks are
+//       computed first; a workgroup never waits on another workgroup, only on chunk flags
+//     wave 0 polls the flags of the chunks the tile's rows overlap (relaxed system-scope
+//       loads, s_sleep back-off, bounded by a wall-clock limit), then an acquire fence
+//     K loop: 128-byte-wide K slices (64 bf16 or 128 fp8) of the A and B tiles go
+//       global -> registers -> LDS (XOR-swizzled 16-byte chunks, double buffered, one barrier
+//       per slice); MFMA 16x16x32 bf16 or 16x16x128 f8f6f4 accumulate in fp32
+//     epilogue: AllGather -> bf16 (round to nearest even) rows of C; ReduceScatter -> fp32
+//       partial rows to `send` (non-local blocks, then a per-chunk completion counter and a
+//       release store of the send flag) or, for the local block, the accumulator plus the
+//       incoming partials of every peer in ascending rank order.
+//   the last workgroup to finish resets the claim counters for the next launch.
+//
+// MFMA operand roles are swapped (the B tile feeds the instruction's first operand), so each
+// lane ends with 4 consecutive output columns of one row: 8-byte bf16 or 16-byte fp32 stores.
+#include "kernels.h"
+
+namespace agg {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kRowBytes = 128;  // bytes of one tile row in one K slice
+// word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle)
+constexpr int kBufferFlags = 0x00020000;
+// a buffer offset past every operand (operands are limited to 2^31 bytes)
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// hardware register XCC_ID (id 20), bits [3:0]: which accelerator die runs this wave
+__device__ inline int xcc_id() {
+  return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 0xF;
+}
+
+__device__ inline uint32_t wall_ticks() { return (uint32_t)wall_clock64(); }
+
+__device__ inline uint32_t load_flag(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// byte offset of 16-byte chunk `ch` (0..7) of tile row `row` in a swizzled LDS tile
+__device__ inline uint32_t lds_off(int row, int ch) {
+  return (uint32_t)(row * kRowBytes + ((ch ^ (row & 7)) << 4));
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays a quiet NaN)
+__device__ inline uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+struct Tile {
+  int row_tile;   // index into the row tiles (AG: m-tile; RS: block * tpb + tile)
+  int col_tile;
+  int list, pos;
+};
+
+// Claim the next tile: this XCD's list first, then the others in turn. List x holds, for every
+// row tile in compute order, the column tiles [x*nc/L, (x+1)*nc/L).
+__device__ inline bool claim(const GemmArgs& a, int home, Tile& t) {
+  const int L = a.n_lists;
+  for (int d = 0; d < L; ++d) {
+    int x = home + d;
+    if (x >= L) x -= L;
+    const int c_lo = (int)((int64_t)x * a.n_col_tiles / L);
+    const int c_hi = (int)((int64_t)(x + 1) * a.n_col_tiles / L);
+    const int nx = c_hi - c_lo;
+    if (nx <= 0) continue;
+    const uint32_t len = (uint32_t)a.n_row_tiles * (uint32_t)nx;
+    uint32_t* ctr = a.scratch + kScrLists + x;
+    if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
+    const uint32_t k = atomicAdd(ctr, 1u);
+    if (k < len) {
+      t.row_tile = a.row_order[k / nx];
+      t.col_tile = c_lo + (int)(k % nx);
+      t.list = x;
+      t.pos = (int)k;
+      return true;
+    }
+  }
+  return false;
+}
+
+// Rows of a row tile: [lo, hi) in the A operand, and (RS) the block it belongs to.
+template <int BM, int EPI>
+__device__ inline void tile_rows(const GemmArgs& a, int row_tile, int64_t& lo, int64_t& hi,
+                                 int& block, int& tile_in_block) {
+  if (EPI == kEpiAllGather) {
+    lo = (int64_t)row_tile * BM;
+    hi = lo + BM < a.M ? lo + BM : a.M;
+    block = 0;
+    tile_in_block = row_tile;
+  } else {
+    block = row_tile / a.tpb;
+    tile_in_block = row_tile - block * a.tpb;
+    const int64_t base = (int64_t)block * a.m_block;
+    lo = base + (int64_t)tile_in_block * BM;
+    const int64_t end = base + a.m_block;
+    hi = lo + BM < end ? lo + BM : end;
+  }
+}
+
+// Wave 0 waits until every flag the tile needs holds >= epoch. Returns false if the wait gave
+// up (its own limit, or another workgroup's). Reports the smallest flag value seen: on success
+// over all the tile's flags, on giving up the last value read of a flag still short of epoch.
+template <int EPI>
+__device__ bool wait_chunks(const GemmArgs& a, int64_t lo, int64_t hi, int block, uint32_t& min_seen) {
+  const int lane = threadIdx.x & 63;
+  int count, q_lo, nq;
+  if (EPI == kEpiAllGather) {
+    q_lo = (int)(lo / a.chunk_rows);
+    nq = (int)((hi - 1) / a.chunk_rows) - q_lo + 1;
+    count = nq;
+  } else {
+    if (block != a.rank) return true;
+    const int64_t base = (int64_t)block * a.m_block;
+    q_lo = (int)((lo - base) / a.chunk_rows);
+    nq = (int)((hi - 1 - base) / a.chunk_rows) - q_lo + 1;
+    count = (a.world - 1) * nq;
+  }
+  uint32_t seen = 0xFFFFFFFFu;
+  for (int base_i = 0; base_i < count; base_i += 64) {
+    const int i = base_i + lane;
+    int f = -1;
+    if (i < count) {
+      if (EPI == kEpiAllGather) {
+        const int c = q_lo + i;
+        if (c / a.cps != a.rank) f = c;
+      } else {
+        int p = i / nq;
+        if (p >= a.rank) ++p;
+        f = p * a.cps + q_lo + (i % nq);
+      }
+    }
+    const uint32_t t0 = wall_ticks();
+    uint32_t polls = 0;
+    for (;;) {
+      uint32_t v = 0xFFFFFFFFu;
+      if (f >= 0) v = load_flag(a.flags + f);
+      const bool ok = v >= a.epoch;
+      if (__all(ok)) {
+        seen = v < seen ? v : seen;
+        break;
+      }
+      ++polls;
+      const bool abort_seen = (polls & 15) == 0 &&
+          __hip_atomic_load(a.scratch + kScrStatus, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+      const bool expired = (uint64_t)(wall_ticks() - t0) > a.timeout_ticks;
+      if (abort_seen || expired) {
+        if (expired && !ok) {
+          atomicCAS(a.scratch + kScrFailed, 0xFFFFFFFFu, (uint32_t)f);
+          atomicOr(a.scratch + kScrStatus, 1u);
+        }
+        uint32_t short_v = ok ? 0xFFFFFFFFu : v;
+        for (int off = 32; off > 0; off >>= 1) {
+          uint32_t o = __shfl_xor(short_v, off);
+          short_v = o < short_v ? o : short_v;
+        }
+        min_seen = short_v;
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  // smallest value any lane saw
+  for (int off = 32; off > 0; off >>= 1) {
+    uint32_t o = __shfl_xor(seen, off);
+    seen = o < seen ? o : seen;
+  }
+  min_seen = seen;
+  return true;
+}
+
+template <int BM, int BN, int DT, int EPI>
+__global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
+  constexpr bool FP8 = (DT == AGG_FP8_E4M3);
+  constexpr int WTM = BM / 2, WTN = BN / 2;       // wave tile
+  constexpr int FM = WTM / 16, FN = WTN / 16;     // 16x16 MFMA blocks per wave
+  constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_LOADS = BM * 8 / kThreads, B_LOADS = BN * 8 / kThreads;
+  constexpr int KSTEPS = FP8 ? 1 : 2;             // MFMA K steps per 128-byte slice
+  constexpr int CPL = FP8 ? 2 : 1;                // 16-byte chunks per lane per step
+  static_assert(BM * 8 % kThreads == 0 && BN * 8 % kThreads == 0, "tile rows");
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ int s_tile[4];
+  __shared__ int s_ok;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int home = a.n_lists > 1 ? xcc_id() % a.n_lists : 0;
+  const int64_t kbytes = a.K * (FP8 ? 1 : 2);
+  const int nk = (int)((kbytes + kRowBytes - 1) / kRowBytes);
+
+  for (;;) {
+    if (tid == 0) {
+      Tile t;
+      if (claim(a, home, t)) {
+        s_tile[0] = t.row_tile; s_tile[1] = t.col_tile; s_tile[2] = t.list; s_tile[3] = t.pos;
+      } else {
+        s_tile[0] = -1;
+      }
+    }
+    __syncthreads();
+    const int row_tile = s_tile[0];
+    if (row_tile < 0) break;
+    const int col_tile = s_tile[1];
+    int64_t lo, hi;
+    int block, tib;
+    tile_rows<BM, EPI>(a, row_tile, lo, hi, block, tib);
+    const int64_t n0 = (int64_t)col_tile * BN;
+    uint32_t* trec = nullptr;
+    if (a.trace && (uint32_t)(row_tile * a.n_col_tiles + col_tile) < a.trace_tiles)
+      trec = a.trace + 8 * ((int64_t)row_tile * a.n_col_tiles + col_tile);
+    if (tid == 0 && trec) {
+      trec[0] = (uint32_t)s_tile[2]; trec[1] = (uint32_t)s_tile[3]; trec[2] = (uint32_t)xcc_id();
+      trec[5] = wall_ticks();
+    }
+
+    // ---- wait for the chunks this tile's rows need
+    if (wave == 0) {
+      uint32_t seen = 0xFFFFFFFFu;
+      const bool ok = wait_chunks<EPI>(a, lo, hi, block, seen);
+      if (lane == 0) {
+        s_ok = ok;
+        if (trec) { trec[3] = seen; trec[6] = wall_ticks(); }
+      }
+    }
+    __syncthreads();
+    if (!s_ok) {
+      __syncthreads();
+      continue;  // abandoned (timeout): the tile's output is left as it was
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+
+    // ---- K loop
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Operands are read through buffer resources: an offset at or past the resource's size
+    // reads as zero, which pads rows past the matrix end and the K tail without branches.
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.a), 0, (int)(a.M * kbytes), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.b), 0, (int)(a.N * kbytes), kBufferFlags);
+    u32x4 ra[A_LOADS], rb[B_LOADS];
+    auto gload = [&](int kt) {
+      const uint32_t kb = (uint32_t)kt * kRowBytes;
+#pragma unroll
+      for (int i = 0; i < A_LOADS; ++i) {
+        const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
+        const uint32_t kbyte = kb + ch * 16;
+        const uint32_t off = kbyte < (uint32_t)kbytes ? (uint32_t)(lo + row) * (uint32_t)kbytes + kbyte : kOutOfRange;
+        ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0));
+      }
+#pragma unroll
+      for (int i = 0; i < B_LOADS; ++i) {
+        const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
+        const uint32_t kbyte = kb + ch * 16;
+        const uint32_t off = kbyte < (uint32_t)kbytes ? (uint32_t)(n0 + row) * (uint32_t)kbytes + kbyte : kOutOfRange;
+        rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, off, 0, 0));
+      }
+    };
+    auto sstore = [&](int buf) {
+      uint8_t* As = smem + buf * STAGE;
+      uint8_t* Bs = As + A_BYTES;
+#pragma unroll
+      for (int i = 0; i < A_LOADS; ++i) {
+        const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
+        *reinterpret_cast<u32x4*>(As + lds_off(row, ch)) = ra[i];
+      }
+#pragma unroll
+      for (int i = 0; i < B_LOADS; ++i) {
+        const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
+        *reinterpret_cast<u32x4*>(Bs + lds_off(row, ch)) = rb[i];
+      }
+    };
+
+    if (nk > 0) {
+      gload(0);
+      sstore(0);
+      __syncthreads();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) gload(kt + 1);
+      const uint8_t* As = smem + buf * STAGE;
+      const uint8_t* Bs = As + A_BYTES;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        // all B fragments of this step stay in registers; A fragments stream one row block at
+        // a time, which keeps the live operand registers at (FN + 1) * CPL * 4
+        u32x4 fb[FN][CPL];
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const int ch = kk * 4 * CPL + (lane >> 4) * CPL + j;
+#pragma unroll
+          for (int i = 0; i < FN; ++i) {
+            const int row = wn * WTN + i * 16 + (lane & 15);
+            fb[i][j] = *reinterpret_cast<const u32x4*>(Bs + lds_off(row, ch));
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          u32x4 fa[CPL];
+          const int row = wm * WTM + i * 16 + (lane & 15);
+#pragma unroll
+          for (int j = 0; j < CPL; ++j)
+            fa[j] = *reinterpret_cast<const u32x4*>(As + lds_off(row, kk * 4 * CPL + (lane >> 4) * CPL + j));
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            if constexpr (FP8) {
+              i32x8 opa, opb;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                opa[e] = (int)fb[j][0][e]; opa[e + 4] = (int)fb[j][1][e];
+                opb[e] = (int)fa[0][e]; opb[e + 4] = (int)fa[1][e];
+              }
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  opa, opb, acc[i][j], 0, 0, 0, 127, 0, 127);
+            } else {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, fb[j][0]), __builtin_bit_cast(bf16x8, fa[0]),
+                  acc[i][j], 0, 0, 0);
+            }
+          }
+        }
+      }
+      if (kt + 1 < nk) sstore(buf ^ 1);
+      __syncthreads();
+    }
+
+    // ---- epilogue
+    const int mrow = lane & 15;          // row within a 16x16 block
+    const int ncol = (lane >> 4) * 4;    // first of 4 consecutive columns
+    if (EPI == kEpiAllGather) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int64_t m = lo + wm * WTM + i * 16 + mrow;
+        if (m >= hi) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t n = n0 + wn * WTN + j * 16 + ncol;
+          if (n >= a.N) continue;
+          f32x4 v = acc[i][j];
+          if (FP8) v *= a.scale;
+          u32x2 packed;
+          packed[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+          packed[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+          *reinterpret_cast<u32x2*>(a.c + m * a.N + n) = packed;
+        }
+      }
+    } else {
+      const int64_t base = (int64_t)block * a.m_block;
+      const bool local = (block == a.rank);
+      const int slot = block < a.rank ? block : block - 1;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int64_t m = lo + wm * WTM + i * 16 + mrow;
+        if (m >= hi) continue;
+        const int64_t r = m - base;       // row within the block
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t n = n0 + wn * WTN + j * 16 + ncol;
+          if (n >= a.N) continue;
+          f32x4 v = acc[i][j];
+          if (!local) {
+            *reinterpret_cast<f32x4*>(a.send + ((int64_t)slot * a.m_block + r) * a.N + n) = v;
+          } else {
+            for (int p = 0; p < a.world; ++p) {
+              if (p == a.rank) continue;
+              const f32x4 in = *reinterpret_cast<const f32x4*>(
+                  a.recv + ((int64_t)p * a.m_block + r) * a.N + n);
+              v += in;
+            }
+            *reinterpret_cast<f32x4*>(a.out + r * a.N + n) = v;
+          }
+        }
+      }
+      if (!local) {
+        // publish: this tile's rows of `send` are complete for its column range
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __syncthreads();
+        if (tid == 0) {
+          const int64_t rlo = lo - base, rhi = hi - base;
+          const int q_lo = (int)(rlo / a.chunk_rows), q_hi = (int)((rhi - 1) / a.chunk_rows);
+          for (int q = q_lo; q <= q_hi; ++q) {
+            // tiles overlapping chunk q of this block, times the column tiles
+            const int64_t clo = (int64_t)q * a.chunk_rows;
+            const int64_t chi = clo + a.chunk_rows;
+            const int t_first = (int)(clo / BM), t_last = (int)((chi - 1) / BM);
+            const uint32_t expect = (uint32_t)(t_last - t_first + 1) * (uint32_t)a.n_col_tiles;
+            const int c = block * a.cps + q;
+            const uint32_t prev = atomicAdd(a.scratch + kScrRsCount + c, 1u);
+            if (prev + 1 == expect) {
+              __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+              __hip_atomic_store(a.send_flags + c, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+          }
+        }
+      }
+    }
+    if (tid == 0 && trec) {
+      trec[7] = wall_ticks();
+      atomicAdd(trec + 4, 1u);
+    }
+    // s_tile / s_ok are rewritten by the next claim only after every thread passed here
+    __syncthreads();
+  }
+
+  // ---- the last workgroup resets the counters for the next launch
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t prev = atomicAdd(a.scratch + kScrDone, 1u);
+    s_ok = (prev == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (s_ok) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (tid < kMaxLists) __hip_atomic_store(a.scratch + kScrLists + tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (EPI == kEpiReduceScatter)
+      for (int i = tid; i < a.world * a.cps; i += kThreads)
+        __hip_atomic_store(a.scratch + kScrRsCount + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(a.scratch + kScrDone, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__global__ void fill_u32_kernel(uint32_t* dst, size_t words, uint32_t value) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = value;
+}
+
+// 64 x 64 element tiles through LDS: coalesced reads of src rows, coalesced writes of dst rows.
+template <typename T>
+__global__ void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst, int64_t k, int64_t n) {
+  __shared__ T tile[64][65];
+  const int64_t k0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+  for (int r = threadIdx.y; r < 64; r += blockDim.y) {
+    const int64_t kk = k0 + r, nn = n0 + threadIdx.x;
+    if (kk < k && nn < n) tile[r][threadIdx.x] = src[kk * n + nn];
+  }
+  __syncthreads();
+  for (int r = threadIdx.y; r < 64; r += blockDim.y) {
+    const int64_t nn = n0 + r, kk = k0 + threadIdx.x;
+    if (nn < n && kk < k) dst[nn * k + kk] = tile[threadIdx.x][r];
+  }
+}
+
+template <int BM, int BN, int DT, int EPI>
+static hipError_t launch_one(const GemmArgs& args, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, DT, EPI>), dim3(grid), dim3(kThreads), 0, stream, args);
+  return hipGetLastError();
+}
+
+template <int DT, int EPI>
+static hipError_t launch_shape(const GemmArgs& args, int bm, int bn, int grid, hipStream_t s) {
+  if (bm == 256 && bn == 256) return launch_one<256, 256, DT, EPI>(args, grid, s);
+  if (bm == 256 && bn == 224) return launch_one<256, 224, DT, EPI>(args, grid, s);
+  if (bm == 128 && bn == 128) return launch_one<128, 128, DT, EPI>(args, grid, s);
+  if (bm == 128 && bn == 64) return launch_one<128, 64, DT, EPI>(args, grid, s);
+  if (bm == 64 && bn == 64) return launch_one<64, 64, DT, EPI>(args, grid, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(const GemmArgs& args, int bm, int bn, int dtype, int epilogue, int grid,
+                       hipStream_t stream) {
+  if (epilogue == kEpiAllGather) {
+    if (dtype == AGG_BF16) return launch_shape<AGG_BF16, kEpiAllGather>(args, bm, bn, grid, stream);
+    if (dtype == AGG_FP8_E4M3) return launch_shape<AGG_FP8_E4M3, kEpiAllGather>(args, bm, bn, grid, stream);
+  } else if (epilogue == kEpiReduceScatter && dtype == AGG_BF16) {
+    return launch_shape<AGG_BF16, kEpiReduceScatter>(args, bm, bn, grid, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fill_u32(uint32_t* dst, size_t words, uint32_t value, hipStream_t stream) {
+  if (words == 0) return hipSuccess;
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, dst, words, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const void* src, void* dst, int64_t k, int64_t n, int elem_bytes,
+                            hipStream_t stream) {
+  if (k == 0 || n == 0) return hipSuccess;
+  dim3 grid((unsigned)((n + 63) / 64), (unsigned)((k + 63) / 64)), block(64, 4);
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, block, 0, stream,
+                       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), k, n);
+  else if (elem_bytes == 1)
+    hipLaunchKernelGGL(transpose_kernel<uint8_t>, grid, block, 0, stream,
+                       static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), k, n);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace agg

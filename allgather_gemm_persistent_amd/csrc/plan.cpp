@@ -1,0 +1,333 @@
+// Host-side planning: argument checks, tile shape choice and row-tile orders.
+//
+// The row-tile order is the chunk/tile pairing of the page "Triton-distributed is turning
+// communication into compiler territory", section "DITRON adds three levels of tiling"
+// (collectives broken into chunks that are paired with computation tiles), applied to the
+// overlap of section "The first move was to expose the overlap": tiles whose rows are all local
+// go first, then each tile as soon as the latest chunk it overlaps has arrived.
+#include "plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <numeric>
+
+#include "../../include/agg.h"
+
+namespace agg {
+
+namespace {
+thread_local std::string g_error;
+}
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+void clear_error() { g_error.clear(); }
+
+const std::vector<TileShape>& tile_shapes() {
+  static const std::vector<TileShape> shapes = {
+      {256, 256}, {256, 224}, {128, 128}, {128, 64}, {64, 64}};
+  return shapes;
+}
+
+TileShape choose_tile(int op, int dtype, int64_t m, int64_t n, int64_t k) {
+  (void)op;
+  (void)dtype;
+  (void)k;
+  // Relative MFMA efficiency of each shape (operand bytes per flop fall as the tile grows).
+  auto eff = [](const TileShape& s) {
+    if (s.bm == 256 && s.bn == 256) return 1.0;
+    if (s.bm == 256) return 0.98;
+    if (s.bm == 128 && s.bn == 128) return 0.7;
+    if (s.bm == 128) return 0.5;
+    return 0.35;
+  };
+  const int64_t kUnits = 256;  // compute units of one MI355X, one workgroup each
+  TileShape best = tile_shapes().back();
+  double best_cost = 1e300;
+  int64_t best_tiles = 0;
+  for (const TileShape& s : tile_shapes()) {
+    int64_t tiles = ((m + s.bm - 1) / s.bm) * ((n + s.bn - 1) / s.bn);
+    int64_t waves = std::max<int64_t>(1, (tiles + kUnits - 1) / kUnits);
+    double cost = double(waves) * s.bm * s.bn / eff(s);
+    if (cost < best_cost * (1 - 1e-9) || (std::fabs(cost - best_cost) <= 1e-9 * cost && tiles > best_tiles)) {
+      best = s;
+      best_cost = cost;
+      best_tiles = tiles;
+    }
+  }
+  return best;
+}
+
+std::vector<int32_t> ring_order(int world, int rank, int chunks_per_shard) {
+  std::vector<int32_t> out;
+  out.reserve(size_t(world - 1) * chunks_per_shard);
+  for (int d = 1; d < world; ++d) {
+    int p = (rank + d) % world;
+    for (int j = 0; j < chunks_per_shard; ++j) out.push_back(p * chunks_per_shard + j);
+  }
+  return out;
+}
+
+int check_order(int world, int rank, int chunks_per_shard, const int32_t* order, int n_order) {
+  const int64_t expect = int64_t(world - 1) * chunks_per_shard;
+  if (n_order != expect)
+    return fail(AGG_E_ARG, "order has %d entries, expected %lld remote chunks", n_order,
+                (long long)expect);
+  std::vector<char> seen(size_t(world) * chunks_per_shard, 0);
+  for (int i = 0; i < n_order; ++i) {
+    int32_t c = order[i];
+    if (c < 0 || c >= world * chunks_per_shard)
+      return fail(AGG_E_ARG, "order[%d] = %d is not a chunk id", i, c);
+    if (c / chunks_per_shard == rank)
+      return fail(AGG_E_ARG, "order[%d] = %d is a local chunk", i, c);
+    if (seen[c]) return fail(AGG_E_ARG, "order[%d] = %d repeats a chunk", i, c);
+    seen[c] = 1;
+  }
+  return AGG_OK;
+}
+
+std::vector<int32_t> ag_row_tile_order(int world, int rank, int64_t m_shard, int chunk_rows,
+                                       const std::vector<int32_t>& order, int bm) {
+  const int64_t m = int64_t(world) * m_shard;
+  const int64_t cps = m_shard / chunk_rows;
+  const int64_t n_chunks = int64_t(world) * cps;
+  std::vector<int64_t> pos(size_t(n_chunks), -1);
+  for (size_t i = 0; i < order.size(); ++i) pos[size_t(order[i])] = int64_t(i);
+  const int64_t tiles = (m + bm - 1) / bm;
+  std::vector<int64_t> ready(size_t(tiles), -1);
+  for (int64_t t = 0; t < tiles; ++t) {
+    int64_t lo = t * bm, hi = std::min(m, lo + bm);
+    for (int64_t c = lo / chunk_rows; c <= (hi - 1) / chunk_rows; ++c)
+      if (c / cps != rank) ready[size_t(t)] = std::max(ready[size_t(t)], pos[size_t(c)]);
+  }
+  std::vector<int32_t> idx(static_cast<size_t>(tiles));
+  std::iota(idx.begin(), idx.end(), 0);
+  std::stable_sort(idx.begin(), idx.end(),
+                   [&](int32_t a, int32_t b) { return ready[size_t(a)] < ready[size_t(b)]; });
+  return idx;
+}
+
+std::vector<int32_t> rs_row_tile_order(int world, int rank, int64_t m, int chunk_rows,
+                                       const std::vector<int32_t>& order, int bm) {
+  const int64_t mb = m / world;
+  const int64_t cpb = mb / chunk_rows;
+  const int64_t tpb = (mb + bm - 1) / bm;
+  std::vector<int32_t> seq;
+  seq.reserve(size_t(world * tpb));
+  for (int d = 1; d < world; ++d) {
+    int j = (rank + d) % world;
+    for (int64_t i = 0; i < tpb; ++i) seq.push_back(int32_t(j * tpb + i));
+  }
+  std::vector<int64_t> pos(size_t(world * cpb), -1);
+  for (size_t i = 0; i < order.size(); ++i) pos[size_t(order[i])] = int64_t(i);
+  std::vector<int64_t> ready(size_t(tpb), -1);
+  for (int64_t i = 0; i < tpb; ++i) {
+    int64_t lo = i * bm, hi = std::min(mb, lo + bm);
+    for (int p = 0; p < world; ++p) {
+      if (p == rank) continue;
+      for (int64_t q = lo / chunk_rows; q <= (hi - 1) / chunk_rows; ++q)
+        ready[size_t(i)] = std::max(ready[size_t(i)], pos[size_t(p * cpb + q)]);
+    }
+  }
+  std::vector<int32_t> local(static_cast<size_t>(tpb));
+  std::iota(local.begin(), local.end(), 0);
+  std::stable_sort(local.begin(), local.end(),
+                   [&](int32_t a, int32_t b) { return ready[size_t(a)] < ready[size_t(b)]; });
+  for (int32_t i : local) seq.push_back(int32_t(rank * tpb + i));
+  return seq;
+}
+
+}  // namespace agg
+
+// ------------------------------------------------------------------------------------------
+// C entry points that need no device
+// ------------------------------------------------------------------------------------------
+
+using namespace agg;
+
+namespace {
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int elem_bytes(int dtype) { return dtype == AGG_FP8_E4M3 ? 1 : 2; }
+
+bool uses_copy_stream(int mode) { return mode == AGG_OVERLAP || mode == AGG_SERIAL || mode == AGG_COPY_ONLY; }
+
+}  // namespace
+
+extern "C" const char* agg_last_error(void) { return g_error.c_str(); }
+
+extern "C" int agg_tile_shape(int op, int dtype, int64_t m, int64_t n, int64_t k, int* bm, int* bn) {
+  if (!bm || !bn) return fail(AGG_E_ARG, "agg_tile_shape: NULL output");
+  TileShape s = choose_tile(op, dtype, m, n, k);
+  *bm = s.bm;
+  *bn = s.bn;
+  return AGG_OK;
+}
+
+extern "C" int agg_check_ag_args(int world, int rank, int64_t m_shard, int64_t n, int64_t k,
+                                 int chunk_rows, int dtype, float scale_a, float scale_b,
+                                 const void* const* peer_src, const void* gather, const void* flags,
+                                 const void* b, const void* c, const int32_t* order, int n_order,
+                                 int mode, agg_stream stream, agg_stream copy_stream) {
+  clear_error();
+  if (world < 1 || world > AGG_MAX_WORLD) return fail(AGG_E_ARG, "world %d not in [1, %d]", world, AGG_MAX_WORLD);
+  if (rank < 0 || rank >= world) return fail(AGG_E_ARG, "rank %d not in [0, %d)", rank, world);
+  if (m_shard < 0 || n < 0 || k < 0) return fail(AGG_E_ARG, "negative size");
+  if (dtype != AGG_BF16 && dtype != AGG_FP8_E4M3) return fail(AGG_E_ARG, "unknown dtype %d", dtype);
+  if (mode < AGG_OVERLAP || mode > AGG_COPY_ONLY) return fail(AGG_E_ARG, "unknown mode %d", mode);
+  if (chunk_rows < 1) return fail(AGG_E_ARG, "chunk_rows %d < 1", chunk_rows);
+  if (m_shard % chunk_rows) return fail(AGG_E_ARG, "chunk_rows %d does not divide m_shard %lld", chunk_rows, (long long)m_shard);
+  const int64_t cps = m_shard / chunk_rows;
+  if (world * cps > AGG_MAX_CHUNKS) return fail(AGG_E_UNSUPPORTED, "%lld chunks exceed %d", (long long)(world * cps), AGG_MAX_CHUNKS);
+  const int eb = elem_bytes(dtype);
+  if ((k * eb) % 16) return fail(AGG_E_ARG, "k * %d bytes = %lld is not a multiple of 16", eb, (long long)(k * eb));
+  if ((n * 2) % 16) return fail(AGG_E_ARG, "n * 2 bytes = %lld is not a multiple of 16", (long long)(n * 2));
+  if (k > (int64_t(1) << 30) || n > (int64_t(1) << 30) || world * m_shard > (int64_t(1) << 30))
+    return fail(AGG_E_UNSUPPORTED, "dimension beyond 2^30");
+  if (world * m_shard * k * eb >= (int64_t(1) << 31) || n * k * eb >= (int64_t(1) << 31))
+    return fail(AGG_E_UNSUPPORTED, "an operand reaches 2 GiB (the kernel addresses operands with 31-bit offsets)");
+  if (dtype == AGG_FP8_E4M3 && !(std::isfinite(scale_a) && std::isfinite(scale_b) && scale_a > 0 && scale_b > 0))
+    return fail(AGG_E_ARG, "fp8 scales must be finite and > 0 (got %g, %g)", scale_a, scale_b);
+  if (uses_copy_stream(mode) && copy_stream && stream == copy_stream)
+    return fail(AGG_E_ARG, "stream and copy_stream must differ");
+  const int64_t m = world * m_shard;
+  const bool empty = (m == 0);
+  if (!empty) {
+    if (k > 0 && (!gather || misaligned(gather))) return fail(AGG_E_ARG, "gather is NULL or not 16-byte aligned");
+    if (world > 1 && (!flags || (reinterpret_cast<uintptr_t>(flags) & 3u))) return fail(AGG_E_ARG, "flags is NULL or not 4-byte aligned");
+    if (mode != AGG_COPY_ONLY && n > 0) {
+      if (k > 0 && (!b || misaligned(b))) return fail(AGG_E_ARG, "b is NULL or not 16-byte aligned");
+      if (!c || misaligned(c)) return fail(AGG_E_ARG, "c is NULL or not 16-byte aligned");
+    }
+    if (world > 1 && mode != AGG_GEMM_ONLY && k > 0) {
+      if (!peer_src) return fail(AGG_E_ARG, "peer_src is NULL");
+      for (int p = 0; p < world; ++p)
+        if (p != rank && (!peer_src[p] || misaligned(peer_src[p])))
+          return fail(AGG_E_ARG, "peer_src[%d] is NULL or not 16-byte aligned", p);
+    }
+  }
+  if (order == nullptr) {
+    if (n_order != 0) return fail(AGG_E_ARG, "order is NULL but n_order = %d", n_order);
+  } else if (int rc = check_order(world, rank, int(cps), order, n_order)) {
+    return rc;
+  }
+  if (!empty) {
+    TileShape s = choose_tile(0, dtype, m, n, k);
+    if ((m + s.bm - 1) / s.bm > AGG_MAX_ROW_TILES)
+      return fail(AGG_E_UNSUPPORTED, "%lld row tiles exceed %d", (long long)((m + s.bm - 1) / s.bm), AGG_MAX_ROW_TILES);
+  }
+  return AGG_OK;
+}
+
+extern "C" int agg_check_rs_args(int world, int rank, int64_t m, int64_t n, int64_t k, int chunk_rows,
+                                 const void* a, const void* b, const void* send, const void* send_flags,
+                                 const float* const* peer_src, const void* recv, const void* flags,
+                                 const void* out, const int32_t* order, int n_order, int mode,
+                                 agg_stream stream, agg_stream copy_stream) {
+  clear_error();
+  if (world < 1 || world > AGG_MAX_WORLD) return fail(AGG_E_ARG, "world %d not in [1, %d]", world, AGG_MAX_WORLD);
+  if (rank < 0 || rank >= world) return fail(AGG_E_ARG, "rank %d not in [0, %d)", rank, world);
+  if (m < 0 || n < 0 || k < 0) return fail(AGG_E_ARG, "negative size");
+  if (mode < AGG_OVERLAP || mode > AGG_COPY_ONLY) return fail(AGG_E_ARG, "unknown mode %d", mode);
+  if (m % world) return fail(AGG_E_ARG, "m %lld is not a multiple of world %d", (long long)m, world);
+  if (chunk_rows < 1) return fail(AGG_E_ARG, "chunk_rows %d < 1", chunk_rows);
+  const int64_t mb = m / world;
+  if (mb % chunk_rows) return fail(AGG_E_ARG, "chunk_rows %d does not divide m/world %lld", chunk_rows, (long long)mb);
+  const int64_t cpb = mb / chunk_rows;
+  if (world * cpb > AGG_MAX_CHUNKS) return fail(AGG_E_UNSUPPORTED, "%lld chunks exceed %d", (long long)(world * cpb), AGG_MAX_CHUNKS);
+  if ((k * 2) % 16) return fail(AGG_E_ARG, "k * 2 bytes = %lld is not a multiple of 16", (long long)(k * 2));
+  if ((n * 4) % 16) return fail(AGG_E_ARG, "n * 4 bytes = %lld is not a multiple of 16", (long long)(n * 4));
+  if (k > (int64_t(1) << 30) || n > (int64_t(1) << 30) || m > (int64_t(1) << 30))
+    return fail(AGG_E_UNSUPPORTED, "dimension beyond 2^30");
+  if (m * k * 2 >= (int64_t(1) << 31) || n * k * 2 >= (int64_t(1) << 31))
+    return fail(AGG_E_UNSUPPORTED, "an operand reaches 2 GiB (the kernel addresses operands with 31-bit offsets)");
+  if (uses_copy_stream(mode) && copy_stream && stream == copy_stream)
+    return fail(AGG_E_ARG, "stream and copy_stream must differ");
+  if (mb > 0 && n > 0) {
+    if (mode != AGG_COPY_ONLY) {
+      if (k > 0 && (!a || misaligned(a))) return fail(AGG_E_ARG, "a is NULL or not 16-byte aligned");
+      if (k > 0 && (!b || misaligned(b))) return fail(AGG_E_ARG, "b is NULL or not 16-byte aligned");
+      if (world > 1 && (!send || misaligned(send))) return fail(AGG_E_ARG, "send is NULL or not 16-byte aligned");
+      if (world > 1 && (!send_flags || (reinterpret_cast<uintptr_t>(send_flags) & 3u))) return fail(AGG_E_ARG, "send_flags is NULL or not 4-byte aligned");
+      if (!out || misaligned(out)) return fail(AGG_E_ARG, "out is NULL or not 16-byte aligned");
+    }
+    if (world > 1) {
+      if (!recv || misaligned(recv)) return fail(AGG_E_ARG, "recv is NULL or not 16-byte aligned");
+      if (!flags || (reinterpret_cast<uintptr_t>(flags) & 3u)) return fail(AGG_E_ARG, "flags is NULL or not 4-byte aligned");
+      if (mode != AGG_GEMM_ONLY) {
+        if (!peer_src) return fail(AGG_E_ARG, "peer_src is NULL");
+        for (int p = 0; p < world; ++p)
+          if (p != rank && (!peer_src[p] || misaligned(peer_src[p])))
+            return fail(AGG_E_ARG, "peer_src[%d] is NULL or not 16-byte aligned", p);
+      }
+    }
+  }
+  if (order == nullptr) {
+    if (n_order != 0) return fail(AGG_E_ARG, "order is NULL but n_order = %d", n_order);
+  } else if (int rc = check_order(world, rank, int(cpb), order, n_order)) {
+    return rc;
+  }
+  if (mb > 0) {
+    TileShape s = choose_tile(1, AGG_BF16, m, n, k);
+    if (world * ((mb + s.bm - 1) / s.bm) > AGG_MAX_ROW_TILES)
+      return fail(AGG_E_UNSUPPORTED, "row tiles exceed %d", AGG_MAX_ROW_TILES);
+  }
+  return AGG_OK;
+}
+
+extern "C" int agg_ag_row_tile_order(int world, int rank, int64_t m_shard, int chunk_rows,
+                                     const int32_t* order, int n_order, int bm, int32_t* out_tiles,
+                                     int max_tiles, int* n_tiles) {
+  clear_error();
+  if (world < 1 || world > AGG_MAX_WORLD || rank < 0 || rank >= world || m_shard < 0 ||
+      chunk_rows < 1 || m_shard % chunk_rows || bm < 1 || !n_tiles)
+    return fail(AGG_E_ARG, "agg_ag_row_tile_order: invalid geometry");
+  const int cps = int(m_shard / chunk_rows);
+  std::vector<int32_t> ord;
+  if (order) {
+    if (int rc = check_order(world, rank, cps, order, n_order)) return rc;
+    ord.assign(order, order + n_order);
+  } else {
+    ord = ring_order(world, rank, cps);
+  }
+  std::vector<int32_t> t = ag_row_tile_order(world, rank, m_shard, chunk_rows, ord, bm);
+  *n_tiles = int(t.size());
+  if (int(t.size()) > max_tiles || (!out_tiles && !t.empty()))
+    return fail(AGG_E_ARG, "agg_ag_row_tile_order: needs %d entries", int(t.size()));
+  std::copy(t.begin(), t.end(), out_tiles);
+  return AGG_OK;
+}
+
+extern "C" int agg_rs_row_tile_order(int world, int rank, int64_t m, int chunk_rows,
+                                     const int32_t* order, int n_order, int bm, int32_t* out_tiles,
+                                     int max_tiles, int* n_tiles) {
+  clear_error();
+  if (world < 1 || world > AGG_MAX_WORLD || rank < 0 || rank >= world || m < 0 || m % world ||
+      chunk_rows < 1 || (m / world) % chunk_rows || bm < 1 || !n_tiles)
+    return fail(AGG_E_ARG, "agg_rs_row_tile_order: invalid geometry");
+  const int cpb = int((m / world) / chunk_rows);
+  std::vector<int32_t> ord;
+  if (order) {
+    if (int rc = check_order(world, rank, cpb, order, n_order)) return rc;
+    ord.assign(order, order + n_order);
+  } else {
+    ord = ring_order(world, rank, cpb);
+  }
+  std::vector<int32_t> t = rs_row_tile_order(world, rank, m, chunk_rows, ord, bm);
+  *n_tiles = int(t.size());
+  if (int(t.size()) > max_tiles || (!out_tiles && !t.empty()))
+    return fail(AGG_E_ARG, "agg_rs_row_tile_order: needs %d entries", int(t.size()));
+  std::copy(t.begin(), t.end(), out_tiles);
+  return AGG_OK;
+}

@@ -1,0 +1,40 @@
+// Host-side planning shared by the C entry points: argument checks, tile shapes, row-tile
+// orders, and the thread-local error text. Plain C++17, no HIP: it also builds with g++ alone.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace agg {
+
+// Thread-local error text behind agg_last_error(); returns `code` for chaining.
+int fail(int code, const char* fmt, ...);
+void clear_error();
+
+struct TileShape {
+  int bm, bn;
+};
+
+// Output tile shape for one call. op: 0 = AllGather+GEMM, 1 = GEMM+ReduceScatter.
+TileShape choose_tile(int op, int dtype, int64_t m, int64_t n, int64_t k);
+
+// Every candidate tile shape the kernels are instantiated for.
+const std::vector<TileShape>& tile_shapes();
+
+// Row tiles of the AllGather+GEMM output in computable order (see agg.h).
+std::vector<int32_t> ag_row_tile_order(int world, int rank, int64_t m_shard, int chunk_rows,
+                                       const std::vector<int32_t>& order, int bm);
+
+// Row tiles (block * tiles_per_block + tile) of GEMM+ReduceScatter in compute order.
+std::vector<int32_t> rs_row_tile_order(int world, int rank, int64_t m, int chunk_rows,
+                                       const std::vector<int32_t>& order, int bm);
+
+// Ring arrival order of the remote chunks: peers rank+1, rank+2, ... (mod world), chunks
+// ascending within a peer.
+std::vector<int32_t> ring_order(int world, int rank, int chunks_per_shard);
+
+// Checks that `order` holds each remote chunk id exactly once. Returns AGG_OK or AGG_E_ARG.
+int check_order(int world, int rank, int chunks_per_shard, const int32_t* order, int n_order);
+
+}  // namespace agg

@@ -1,0 +1,116 @@
+"""Device buffers for one AllGather+GEMM or GEMM+ReduceScatter workload, and calls through the
+binding. PyTorch provides device memory and streams only; every step runs in libagg.
+
+The emulated peers are ordinary device allocations holding each remote rank's shard (or, for
+ReduceScatter, the partial block it contributes); the symmetric buffers (gather / receive) and
+the flag words are what a multi-GPU build would place in peer-visible memory.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class AgWorkload:
+    """One rank's share of AllGather+GEMM with W-1 emulated peers on one GPU.
+
+    shards: W CPU tensors (Ms x K, bf16 or float8_e4m3fn); b_kn: CPU tensor (K x N), the logical
+    weight, stored on the device as N x K (K contiguous).
+    """
+
+    def __init__(self, world, rank, shards, b_kn, chunk_rows, dtype="bf16", scale_a=1.0,
+                 scale_b=1.0, device="cuda", tile=None):
+        self.world, self.rank, self.chunk_rows, self.dtype = world, rank, chunk_rows, dtype
+        self.m_shard, self.k = shards[0].shape
+        self.n = b_kn.shape[1]
+        self.m = world * self.m_shard
+        self.scale_a, self.scale_b = float(scale_a), float(scale_b)
+        self.device = torch.device(device)
+        tdt = shards[0].dtype
+        self.peers = [s.to(self.device) if p != rank else None for p, s in enumerate(shards)]
+        self.local = shards[rank].to(self.device)
+        # zero-filled as bytes (every torch dtype, fp8 included, has a byte view)
+        esize = shards[0].element_size()
+        self.gather = torch.zeros(self.m, max(self.k, 1) * esize, dtype=torch.uint8,
+                                  device=self.device).view(tdt)[:, :self.k]
+        self.reset_local()
+        cps = self.m_shard // chunk_rows if chunk_rows else 0
+        self.flags = torch.zeros(max(world * cps, 1), dtype=torch.int32, device=self.device)
+        self.b = b_kn.t().contiguous().to(self.device)
+        self.c = torch.zeros(self.m, self.n, dtype=torch.bfloat16, device=self.device)
+        self.copy_stream = None     # the ctx runs the copies on its own streams
+        self.ctx = B.agg_ctx_create(self.device.index or 0)
+        if tile:
+            B.agg_ctx_set_tile(self.ctx, *tile)
+
+    def reset_local(self):
+        """Place the local shard in its slot of the gather buffer (the caller's job)."""
+        ms = self.m_shard
+        self.gather[self.rank * ms:(self.rank + 1) * ms].copy_(self.local)
+
+    def peer_ptrs(self):
+        return [p if p is not None else 0 for p in self.peers]
+
+    def run(self, mode="overlap", order=None, delay_us=None, stream=None):
+        stream = stream or torch.cuda.current_stream(self.device)
+        B.ag_gemm(self.ctx, self.world, self.rank, self.m_shard, self.n, self.k, self.chunk_rows,
+                  self.dtype, self.scale_a, self.scale_b, self.peer_ptrs(), self.gather,
+                  self.flags, self.b, self.c, order=order, delay_us=delay_us, mode=mode,
+                  stream=stream, copy_stream=self.copy_stream)
+
+    def status(self):
+        return B.agg_ctx_status(self.ctx, torch.cuda.current_stream(self.device))
+
+    def close(self):
+        if self.ctx is not None:
+            B.agg_ctx_destroy(self.ctx)
+            self.ctx = None
+
+
+class RsWorkload:
+    """One rank's share of GEMM+ReduceScatter with W-1 emulated peers on one GPU.
+
+    a: CPU (M x K) bf16; b_kn: CPU (K x N) bf16; peers: CPU (W x M/W x N) float32 (slot rank
+    unused).
+    """
+
+    def __init__(self, world, rank, a, b_kn, peers, chunk_rows, device="cuda", tile=None):
+        self.world, self.rank, self.chunk_rows = world, rank, chunk_rows
+        self.m, self.k = a.shape
+        self.n = b_kn.shape[1]
+        self.mb = self.m // world
+        self.device = torch.device(device)
+        self.a = a.to(self.device)
+        self.b = b_kn.t().contiguous().to(self.device)
+        self.peers = [peers[p].to(self.device) if p != rank else None for p in range(world)]
+        self.recv = torch.zeros(world, self.mb, self.n, dtype=torch.float32, device=self.device)
+        cpb = self.mb // chunk_rows if chunk_rows else 0
+        self.flags = torch.zeros(max(world * cpb, 1), dtype=torch.int32, device=self.device)
+        self.send_flags = torch.zeros(max(world * cpb, 1), dtype=torch.int32, device=self.device)
+        self.send = torch.zeros(max(world - 1, 1), self.mb, self.n, dtype=torch.float32,
+                                device=self.device)
+        self.out = torch.zeros(self.mb, self.n, dtype=torch.float32, device=self.device)
+        self.copy_stream = None     # the ctx runs the copies on its own streams
+        self.ctx = B.agg_ctx_create(self.device.index or 0)
+        if tile:
+            B.agg_ctx_set_tile(self.ctx, *tile)
+
+    def peer_ptrs(self):
+        return [p if p is not None else 0 for p in self.peers]
+
+    def run(self, mode="overlap", order=None, delay_us=None, stream=None):
+        stream = stream or torch.cuda.current_stream(self.device)
+        B.gemm_rs(self.ctx, self.world, self.rank, self.m, self.n, self.k, self.chunk_rows,
+                  self.a, self.b, self.send, self.send_flags, self.peer_ptrs(), self.recv,
+                  self.flags, self.out, order=order, delay_us=delay_us, mode=mode, stream=stream,
+                  copy_stream=self.copy_stream)
+
+    def status(self):
+        return B.agg_ctx_status(self.ctx, torch.cuda.current_stream(self.device))
+
+    def close(self):
+        if self.ctx is not None:
+            B.agg_ctx_destroy(self.ctx)
+            self.ctx = None

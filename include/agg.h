@@ -1,0 +1,251 @@
+/*
+ * agg.h — C ABI of libagg: one rank's share of an overlapped AllGather+GEMM and of a
+ * GEMM+ReduceScatter on one AMD Instinct MI355X (gfx950), peers emulated on the same GPU.
+ *
+ * Source of the method: the page "Triton-distributed is turning communication into compiler
+ * territory" (cronfeed.work), section "The first move was to expose the overlap": an AllGather
+ * moves shards into place and a GEMM consumes them; serialized, the transfer stays visible; cut
+ * into chunks, computation on arrived chunks proceeds while others still move; the building
+ * blocks are symmetric memory, remote data access, signaling and asynchronous tasks. Section
+ * "DITRON adds three levels of tiling": collectives are broken into chunks paired with
+ * computation tiles, with synchronization inserted; device-level tiles are data movements on
+ * DMA engines, core-level tiles live in registers, shared memory and matrix units.
+ *
+ * On one GPU the W-1 peers are "staging" regions in HBM. A producer on side streams copies them
+ * chunk by chunk into a symmetric gather buffer with the SDMA engines and after each chunk
+ * writes the call's epoch into that chunk's flag word with a stream write. A persistent MFMA
+ * GEMM kernel (on a ctx-owned stream with a hardware queue of its own) claims output tiles in
+ * the order their chunks arrive, waits on the flags each tile needs, and computes; while chunks
+ * are in flight it leaves a few CUs free for the producer (agg_ctx_set_reserved_cus).
+ *
+ * Conventions (every entry point):
+ *  - Returns AGG_OK (0) or an AGG_E_* code; agg_last_error() then holds a text for the
+ *    calling thread. No C++ exception crosses this boundary.
+ *  - Argument checks run before anything is enqueued: a call that returns AGG_E_ARG has
+ *    enqueued nothing.
+ *  - All device pointers are HIP device allocations of the ctx's device; they and the streams
+ *    stay owned by the caller and must outlive the enqueued work. Host arrays are read during
+ *    the call only.
+ *  - Streams are hipStream_t values passed as agg_stream (void*). Calls are asynchronous with
+ *    respect to the host, except that a non-NULL delay_us makes the calling thread wait between
+ *    chunk enqueues (a test device: it emulates late peers).
+ *  - A ctx serialises its calls: use one ctx from one host thread with one main stream.
+ *  - Matrix layouts are row-major. The weight operand B is stored N x K (K contiguous): row n
+ *    holds column n of the logical K x N matrix, the layout of a torch.nn.Linear weight.
+ *    agg_transpose_kn_to_nk converts a K x N (N contiguous) matrix once.
+ */
+#ifndef AGG_H
+#define AGG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* agg_stream;            /* a hipStream_t */
+typedef struct agg_ctx agg_ctx;
+
+enum agg_status {
+  AGG_OK = 0,
+  AGG_E_ARG = 1,          /* invalid argument; nothing was enqueued */
+  AGG_E_UNSUPPORTED = 2,  /* not a gfx950 device, or a size beyond a documented limit */
+  AGG_E_HIP = 3,          /* a HIP runtime call failed (its text is in agg_last_error) */
+  AGG_E_TIMEOUT = 4,      /* a device-side wait on a chunk flag gave up (agg_ctx_status) */
+  AGG_E_STATE = 5         /* the ctx is in the wrong state for the call (see each call) */
+};
+
+enum agg_dtype {
+  AGG_BF16 = 0,           /* bfloat16 operands */
+  AGG_FP8_E4M3 = 1        /* OCP float8 E4M3 ("fn": max 448, no inf) operands, per-tensor scales */
+};
+
+enum agg_mode {
+  AGG_OVERLAP = 0,        /* producer on copy_stream concurrent with the consumer kernel */
+  AGG_SERIAL = 1,         /* all chunks copied and flagged first, then the same kernel */
+  AGG_GEMM_ONLY = 2,      /* the kernel alone on already gathered data: no copy; tiles check
+                             their flags against the ctx's current epoch, which the last
+                             producing call left in them, so no wait lasts */
+  AGG_COPY_ONLY = 3       /* the producer alone (new epoch), no kernel */
+};
+
+/* Limits. */
+#define AGG_MAX_WORLD 8           /* emulated ranks */
+#define AGG_MAX_ROW_TILES 1024    /* row tiles of the output per call */
+#define AGG_MAX_CHUNKS 4096       /* world * chunks per shard (or per block) */
+
+/* ---- context -------------------------------------------------------------------------- */
+
+/* Create a ctx on HIP device `device`. Allocates the ctx's device scratch (tile counters,
+ * status word, ReduceScatter completion counters, 16.6 KiB) and creates its kernel stream.
+ * AGG_E_UNSUPPORTED unless the device's architecture is gfx950. */
+int agg_ctx_create(int device, agg_ctx** out);
+
+/* Free the ctx (synchronises the device first). NULL is accepted. */
+int agg_ctx_destroy(agg_ctx* ctx);
+
+/* After AGG_E_TIMEOUT, or before passing different flags buffers: synchronises the device,
+ * zero-fills the flags buffers bound to the ctx (they must still be allocated), unbinds them,
+ * clears counters and status, and restarts the epoch at 0. */
+int agg_ctx_reset(agg_ctx* ctx, agg_stream stream);
+
+/* Synchronise `stream` and read the ctx's device status: *status = 0 when no wait gave up,
+ * else bit 0 set; *failed_chunk = the first flag index whose wait gave up, or -1.
+ * Returns AGG_E_TIMEOUT when status != 0. Either output pointer may be NULL. */
+int agg_ctx_status(agg_ctx* ctx, agg_stream stream, uint32_t* status, int32_t* failed_chunk);
+
+/* Current epoch: the value the last producing call wrote into its flags (0 before any). */
+int agg_ctx_epoch(agg_ctx* ctx, uint32_t* epoch);
+
+/* Move the epoch (tests of the wrap-around): the next producing call uses epoch+1. Epochs run
+ * 1 .. 0xFFFFFFFE; past the end the ctx zero-fills its bound flags and restarts at 1.
+ * Requires no bound flags buffer (fresh ctx or after agg_ctx_reset); AGG_E_STATE otherwise. */
+int agg_ctx_set_epoch(agg_ctx* ctx, uint32_t epoch);
+
+/* Device-side wait limit in microseconds (default 2,000,000). A wait that runs past it sets
+ * the status word and abandons its tile; later waits of the same call give up at once. */
+int agg_ctx_set_timeout_us(agg_ctx* ctx, uint64_t timeout_us);
+
+/* Number of copy streams the producer spreads chunks over (1..8, default 4), all created by
+ * the ctx with hardware queues of their own. Chunk i of the arrival order goes to stream i mod n,
+ * so every stream keeps the arrival order and the SDMA engines work in parallel. */
+int agg_ctx_set_copy_streams(agg_ctx* ctx, int n);
+
+/* CUs the persistent grid leaves free in AGG_OVERLAP mode (default 32, four per XCD), where
+ * the producer's copies and flag writes must run beside it: in the HIP runtime shipped with
+ * torch several of them execute as runtime kernels and need a CU. 0..CUs-1. */
+int agg_ctx_set_reserved_cus(agg_ctx* ctx, int n);
+
+/* Force the output tile shape (bm x bn) of later calls; 0, 0 restores the automatic choice.
+ * Shapes: 256x256, 256x224, 128x128, 128x64, 64x64; anything else is AGG_E_ARG. */
+int agg_ctx_set_tile(agg_ctx* ctx, int bm, int bn);
+
+/* Optional per-tile trace (NULL or 0 bytes disables). The buffer is device memory of
+ * `bytes` >= 32 * tiles bytes; each computed tile (m-tile i, n-tile j) writes the 8 words
+ * agg_trace_rec at index i * n_tiles + j: claim list, position in that list, XCD id of the
+ * claiming workgroup, minimum flag value it observed (0xFFFFFFFF if it needed none), visit
+ * count (atomic increment), and the three 100 MHz timestamps: claimed, flags seen, done. */
+int agg_set_trace(agg_ctx* ctx, void* dev_buf, size_t bytes);
+
+typedef struct agg_trace_rec {
+  uint32_t list, pos, xcd, min_flag, visits, t_claim, t_ready, t_done;
+} agg_trace_rec;
+
+/* Thread-local text describing the last non-OK return of this thread. */
+const char* agg_last_error(void);
+
+/* ---- primitive: put with signal -------------------------------------------------------- */
+
+/* Enqueue on copy_stream: copy `bytes` from src to dst (hipMemcpyDeviceToDeviceNoCU), then
+ * write `value` into *flag (4-byte aligned) with a stream write, so that stream order places the
+ * flag after the data. This is the one-GPU form of the remote data access + signaling pair. */
+int agg_put_signal(void* dst, const void* src, size_t bytes, uint32_t* flag, uint32_t value,
+                   agg_stream copy_stream);
+
+/* ---- AllGather + GEMM ------------------------------------------------------------------ */
+
+/* C = concat(shard_0, ..., shard_{W-1}) @ B, one rank's share.
+ *   world, rank      1 <= world <= 8, 0 <= rank < world
+ *   m_shard          rows per shard (Ms >= 0); M = world * m_shard
+ *   n, k             output columns and contraction length (n, k >= 0)
+ *   chunk_rows       rows per chunk (>= 1, divides m_shard); chunk c (global id) covers gathered
+ *                    rows [c*cr, (c+1)*cr) and belongs to shard c / (m_shard/cr)
+ *   dtype            AGG_BF16 or AGG_FP8_E4M3; A and B share it
+ *   scale_a/scale_b  fp8 per-tensor dequantisation scales (finite, > 0); ignored for bf16
+ *   peer_src         HOST array of `world` device pointers: peer p's shard (m_shard x k), the
+ *                    emulated remote memory; entry `rank` is ignored
+ *   gather           device (M x k): the symmetric gather buffer; rows of shard `rank` must
+ *                    already hold the local shard; the producer fills the others
+ *   flags            device uint32[world * m_shard/cr], zero-filled once at allocation and then
+ *                    bound to this ctx (the first call binds it; another pointer gives
+ *                    AGG_E_STATE until agg_ctx_reset). Remote chunks' flags end at the epoch;
+ *                    the local shard's flags are not written
+ *   b                device (n x k), K contiguous, same dtype
+ *   c                device (M x n) bfloat16, row-major, rows in gathered (rank) order
+ *   order, n_order   HOST: the remote chunk ids in arrival order, a permutation of all
+ *                    (world-1)*m_shard/cr of them; NULL with n_order 0 = ring order (peers
+ *                    rank+1, rank+2, ... mod world; chunks ascending within a peer)
+ *   delay_us         HOST, NULL or n_order entries: wait this long before enqueueing each chunk
+ *   mode             AGG_OVERLAP / AGG_SERIAL / AGG_GEMM_ONLY / AGG_COPY_ONLY
+ *   stream           the caller's stream: the call is ordered after earlier work on it, and
+ *                    later work on it is ordered after the call (kernel and copies)
+ *   copy_stream      optional (NULL allowed, else != stream): the copies also start after
+ *                    earlier work on it, and later work on it starts after the copies. The
+ *                    copies themselves run on the ctx's own streams (agg_ctx_set_copy_streams)
+ * Alignment: k * elem and n * 2 bytes multiples of 16, device pointers 16-byte aligned. */
+int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64_t k,
+            int chunk_rows, int dtype, float scale_a, float scale_b,
+            const void* const* peer_src, void* gather, uint32_t* flags, const void* b, void* c,
+            const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
+            agg_stream stream, agg_stream copy_stream);
+
+/* ---- GEMM + ReduceScatter -------------------------------------------------------------- */
+
+/* P = A @ B in fp32 (bf16 operands); rows split into `world` blocks of Mb = m/world rows.
+ *   a                device (m x k) bf16; b: device (n x k) bf16, K contiguous
+ *   send             device fp32 (world-1) x Mb x n: the non-local blocks j != rank of P,
+ *                    ascending j (what this rank would push to rank j)
+ *   send_flags       device uint32[world * Mb/cr]: entry j*Mb/cr + q is set to the epoch
+ *                    when rows [q*cr, (q+1)*cr) of block j are complete in `send` (j != rank)
+ *   peer_src         HOST array of `world` device pointers to fp32 Mb x n blocks: the partial
+ *                    block each peer p contributes to this rank's block; entry `rank` ignored
+ *   recv             device fp32 world x Mb x n: symmetric receive buffer; the producer copies
+ *                    peer p's block into slot p chunk by chunk (slot `rank` unused)
+ *   flags            device uint32[world * Mb/cr]: the receive flags (chunk p*Mb/cr + q)
+ *   out              device fp32 Mb x n: P[block rank] + sum over p != rank, ascending p, of
+ *                    recv[p]; a fixed summation order, so the result does not depend on arrival
+ *   order/n_order, delay_us, mode, streams: as for ag_gemm, over the (world-1)*Mb/cr incoming
+ *   chunks. flags and send_flags are bound to the ctx like ag_gemm's flags.
+ * Alignment: k*2 and n*4 bytes multiples of 16; m a multiple of world; cr divides Mb. */
+int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, int64_t k, int chunk_rows,
+            const void* a, const void* b, float* send, uint32_t* send_flags,
+            const float* const* peer_src, float* recv, uint32_t* flags, float* out,
+            const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
+            agg_stream stream, agg_stream copy_stream);
+
+/* ---- layout helper ---------------------------------------------------------------------- */
+
+/* dst (n x k) = transpose of src (k x n), elements of `elem_bytes` (1 or 2), on `stream`.
+ * For callers holding the weight N-contiguous: done once, outside the per-call path. */
+int agg_transpose_kn_to_nk(const void* src, void* dst, int64_t k, int64_t n, int elem_bytes,
+                           agg_stream stream);
+
+/* ---- host-only planning (no device needed; used by the calls above) --------------------- */
+
+/* The tile shape the library uses for a call: *bm x *bn output tiles, *n_lists claim lists.
+ * op: 0 = ag_gemm, 1 = gemm_rs. m is M (ag: world*m_shard). */
+int agg_tile_shape(int op, int dtype, int64_t m, int64_t n, int64_t k, int* bm, int* bn);
+
+/* Row-tile order of ag_gemm: tiles of `bm` rows of C sorted by the arrival position of the
+ * latest remote chunk they overlap (-1 when none), ties by tile index. Writes
+ * ceil(world*m_shard/bm) entries to out_tiles (capacity max_tiles); *n_tiles = that count. */
+int agg_ag_row_tile_order(int world, int rank, int64_t m_shard, int chunk_rows,
+                          const int32_t* order, int n_order, int bm, int32_t* out_tiles,
+                          int max_tiles, int* n_tiles);
+
+/* Row-tile order of gemm_rs as (block, tile-in-block) pairs flattened to block*tpb + tile,
+ * tpb = ceil(Mb/bm): non-local blocks in send order rank+1, ..., rank+world-1 (mod world), each
+ * ascending; then the local block's tiles by the arrival position of the latest incoming
+ * chunk they need, ties by index. */
+int agg_rs_row_tile_order(int world, int rank, int64_t m, int chunk_rows, const int32_t* order,
+                          int n_order, int bm, int32_t* out_tiles, int max_tiles, int* n_tiles);
+
+/* The argument checks ag_gemm / gemm_rs run first (pointers are checked for NULL and 16-byte
+ * alignment only). AGG_OK or AGG_E_ARG / AGG_E_UNSUPPORTED with agg_last_error set. */
+int agg_check_ag_args(int world, int rank, int64_t m_shard, int64_t n, int64_t k, int chunk_rows,
+                      int dtype, float scale_a, float scale_b, const void* const* peer_src,
+                      const void* gather, const void* flags, const void* b, const void* c,
+                      const int32_t* order, int n_order, int mode, agg_stream stream,
+                      agg_stream copy_stream);
+int agg_check_rs_args(int world, int rank, int64_t m, int64_t n, int64_t k, int chunk_rows,
+                      const void* a, const void* b, const void* send, const void* send_flags,
+                      const float* const* peer_src, const void* recv, const void* flags,
+                      const void* out, const int32_t* order, int n_order, int mode,
+                      agg_stream stream, agg_stream copy_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AGG_H */

@@ -1,0 +1,120 @@
+"""The C ABI's host side, without a GPU: the library loads and exports every declared symbol,
+the argument checks return the documented codes, and the row-tile orders match the oracle."""
+
+import ctypes
+
+import pytest
+
+from allgather_gemm_persistent_amd import binding as B
+from allgather_gemm_persistent_amd import configs, inputs
+from oracle import agg_oracle as O
+
+FAKE = 1 << 20          # an aligned non-NULL address (never dereferenced by the checks)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = B.header_functions()
+    assert len(names) >= 19
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def _ag(**kw):
+    args = dict(world=2, rank=0, m_shard=128, n=256, k=512, chunk_rows=64, dtype="bf16",
+                scale_a=1.0, scale_b=1.0, peer_src=[FAKE, FAKE], gather=FAKE, flags=FAKE, b=FAKE,
+                c=FAKE, order=None, mode="overlap", stream=1, copy_stream=2)
+    args.update(kw)
+    return B.agg_check_ag_args(**args)
+
+
+def test_ag_args_ok(lib):
+    assert _ag() == B.AGG_OK
+    assert _ag(order=[3, 2]) == B.AGG_OK
+    assert _ag(mode="gemm_only", copy_stream=1) == B.AGG_OK
+    assert _ag(dtype="fp8", scale_a=0.5, scale_b=2.0) == B.AGG_OK
+    assert _ag(m_shard=0, gather=None, flags=None, order=None) == B.AGG_OK
+    assert _ag(world=1, peer_src=None, flags=None) == B.AGG_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(world=0), B.AGG_E_ARG), (dict(world=9), B.AGG_E_ARG), (dict(rank=2), B.AGG_E_ARG),
+    (dict(rank=-1), B.AGG_E_ARG), (dict(m_shard=-1), B.AGG_E_ARG), (dict(chunk_rows=0), B.AGG_E_ARG),
+    (dict(chunk_rows=48), B.AGG_E_ARG), (dict(k=500), B.AGG_E_ARG), (dict(n=252), B.AGG_E_ARG),
+    (dict(dtype=7), B.AGG_E_ARG), (dict(mode=9), B.AGG_E_ARG),
+    (dict(dtype="fp8", scale_a=0.0), B.AGG_E_ARG), (dict(dtype="fp8", scale_b=float("inf")), B.AGG_E_ARG),
+    (dict(copy_stream=1), B.AGG_E_ARG), (dict(gather=FAKE + 8), B.AGG_E_ARG),
+    (dict(b=None), B.AGG_E_ARG), (dict(c=FAKE + 2), B.AGG_E_ARG), (dict(flags=None), B.AGG_E_ARG),
+    (dict(peer_src=[FAKE, None]), B.AGG_E_ARG), (dict(peer_src=None), B.AGG_E_ARG),
+    (dict(order=[2]), B.AGG_E_ARG), (dict(order=[2, 2]), B.AGG_E_ARG), (dict(order=[0, 2]), B.AGG_E_ARG),
+    (dict(order=[2, 4]), B.AGG_E_ARG), (dict(order=[3, -1]), B.AGG_E_ARG),
+    (dict(m_shard=1 << 20, chunk_rows=1, k=8192), B.AGG_E_UNSUPPORTED),
+    (dict(m_shard=8192, chunk_rows=1), B.AGG_E_UNSUPPORTED),
+])
+def test_ag_args_rejected(lib, kw, code):
+    assert _ag(**kw) == code
+    assert B.last_error()
+
+
+def _rs(**kw):
+    args = dict(world=2, rank=1, m=256, n=256, k=512, chunk_rows=64, a=FAKE, b=FAKE, send=FAKE,
+                send_flags=FAKE, peer_src=[FAKE, FAKE], recv=FAKE, flags=FAKE, out=FAKE, order=None,
+                mode="overlap", stream=1, copy_stream=2)
+    args.update(kw)
+    return B.agg_check_rs_args(**args)
+
+
+def test_rs_args(lib):
+    assert _rs() == B.AGG_OK
+    assert _rs(order=[1, 0]) == B.AGG_OK
+    for kw in (dict(m=255), dict(chunk_rows=96), dict(n=250), dict(k=4), dict(out=None),
+               dict(send=FAKE + 4), dict(recv=None), dict(order=[2, 3]), dict(order=[0]),
+               dict(copy_stream=1), dict(world=0), dict(rank=2)):
+        assert _rs(**kw) == B.AGG_E_ARG, kw
+
+
+@pytest.mark.parametrize("world,rank,ms,cr,bm,seed", [
+    (2, 0, 128, 64, 64, 1), (8, 0, 512, 128, 256, 0), (8, 3, 16, 16, 64, 2), (3, 2, 10, 5, 64, 3),
+    (8, 0, 1024, 256, 256, 4), (5, 1, 60, 12, 128, 5), (1, 0, 100, 10, 64, 0)])
+def test_ag_row_tile_order_matches_oracle(lib, world, rank, ms, cr, bm, seed):
+    cps = ms // cr
+    order = inputs.ring_order(world, rank, cps) if seed == 0 else inputs.seeded_order(world, rank, cps, seed)
+    want, _ = O.ag_mtile_order(world, rank, ms, cr, order, bm)
+    assert B.agg_ag_row_tile_order(world, rank, ms, cr, order, bm) == want
+    if seed == 0:      # NULL order means ring order
+        assert B.agg_ag_row_tile_order(world, rank, ms, cr, None, bm) == want
+
+
+@pytest.mark.parametrize("world,rank,mb,cr,bm,seed", [
+    (8, 0, 1024, 128, 256, 1), (2, 1, 64, 16, 64, 2), (4, 2, 30, 5, 64, 3), (3, 0, 128, 128, 64, 0)])
+def test_rs_row_tile_order_matches_oracle(lib, world, rank, mb, cr, bm, seed):
+    cpb = mb // cr
+    order = inputs.ring_order(world, rank, cpb) if seed == 0 else inputs.seeded_order(world, rank, cpb, seed)
+    tpb = -(-mb // bm)
+    want = [blk * tpb + i for blk, i in O.rs_mtile_order(world, rank, mb, cr, order, bm)]
+    assert B.agg_rs_row_tile_order(world, rank, world * mb, cr, order, bm) == want
+
+
+def test_tile_shapes_for_the_workloads(lib):
+    """The shapes the library picks for the five workloads (whole waves of 256 tiles where the
+    sizes allow)."""
+    got = {}
+    for name, cfg in configs.CONFIGS.items():
+        op = 1 if cfg.op == "rs" else 0
+        got[name] = B.agg_tile_shape(op, cfg.dtype, cfg.m, cfg.n, cfg.k)
+    assert got["c2_ag_w8_bf16"] == (256, 224)     # 16 x 16 = 256 tiles
+    assert got["c3_rs_w8_bf16"] == (256, 256)     # 32 x 32 = 1024 tiles
+    assert got["c5_ag_w8_fp8"] == (256, 224)      # 32 x 32 = 1024 tiles
+
+
+def test_ctx_calls_reject_null(lib):
+    assert lib.agg_ctx_reset(None, None) == B.AGG_E_ARG
+    assert lib.agg_ctx_status(None, None, None, None) == B.AGG_E_ARG
+    assert lib.agg_ctx_destroy(None) == B.AGG_OK
+    e = ctypes.c_uint32()
+    assert lib.agg_ctx_epoch(None, ctypes.byref(e)) == B.AGG_E_ARG
+    assert lib.agg_transpose_kn_to_nk(None, None, -1, 2, 2, None) == B.AGG_E_ARG

@@ -1,0 +1,334 @@
+"""AllGather+GEMM on the GPU through the C ABI, compared with the CPU oracle.
+
+Parity bar: bf16 |C - ref| <= 1e-2 + 1e-2 |ref|, fp8 <= 2e-2 + 2e-2 |ref| (ref = oracle on the
+same dequantised values); bit-exact for the gather buffer, the flags, tile bookkeeping, and
+wherever the exact product is representable (integer inputs, identity weight).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from allgather_gemm_persistent_amd import binding as B
+from allgather_gemm_persistent_amd import configs, inputs
+from allgather_gemm_persistent_amd.workload import AgWorkload
+from oracle import agg_oracle as O
+
+from helpers import BF16_TOL, FP8_TOL, assert_close, bits_equal, raw, small_ag_data, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TILES = [(256, 256), (256, 224), (128, 128), (128, 64), (64, 64)]
+
+
+def _oracle_c(shards, b, dtype, sa, sb):
+    return O.ag_gemm_ref([raw(s) for s in shards], raw(b), dtype, sa, sb)
+
+
+def _tol(dtype):
+    return FP8_TOL if dtype == "fp8" else BF16_TOL
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("tile", TILES)
+def test_identity_weight_gives_gather_bitexact(gpu, dtype, tile):
+    """B = I (K = N): every output is one product with 1, so C equals the gathered A exactly
+    (fp8 values are exactly representable in bf16). Catches any row/column/layout mix-up."""
+    world, ms, k = 3, 96, 192
+    shards, _, _, _ = small_ag_data(world, ms, k, k, dtype, seed=5)
+    eye = torch.eye(k, dtype=torch.float32)
+    b = eye.to(torch.bfloat16) if dtype == "bf16" else eye.to(torch.float8_e4m3fn)
+    w = AgWorkload(world, 1, shards, b, chunk_rows=32, dtype=dtype, tile=tile)
+    try:
+        w.run("overlap", order=inputs.seeded_order(world, 1, 3, 11))
+        assert w.status() == (0, -1)
+        g = torch.cat([s.to(torch.float32) for s in shards]).to(torch.bfloat16)
+        assert bits_equal(w.c, g)
+    finally:
+        w.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("tile", TILES)
+def test_integer_inputs_bitexact(gpu, dtype, tile):
+    """Entries in {-2..2}: every fp32 partial sum is an exact integer (|sum| <= 4K < 2^24), so
+    the kernel's output must equal the round-to-nearest-even bf16 of the exact product, bit for
+    bit, whatever order the MFMA sums in."""
+    world, ms, k, n = 2, 160, (520 if dtype == "bf16" else 528), 200
+    shards, b, _, _ = small_ag_data(world, ms, k, n, dtype, seed=9, kind="int")
+    w = AgWorkload(world, 0, shards, b, chunk_rows=40, dtype=dtype, tile=tile)
+    try:
+        w.run("overlap")
+        assert w.status() == (0, -1)
+        exact = _oracle_c(shards, b, dtype, 1.0, 1.0)
+        want = O.encode_bf16_rne(exact)
+        assert np.array_equal(raw(w.c), want)
+    finally:
+        w.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("mode", ["overlap", "serial"])
+def test_ragged_shapes_vs_oracle(gpu, dtype, tile, mode):
+    """Sizes that are not multiples of any tile: ragged rows, columns and K tail."""
+    world, rank, ms, cr, k, n = 3, 1, 200, 40, 328, 264
+    if dtype == "fp8":
+        k = 336
+    shards, b, sa, sb = small_ag_data(world, ms, k, n, dtype, seed=21)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, dtype=dtype, scale_a=sa, scale_b=sb,
+                   tile=tile)
+    try:
+        w.run(mode, order=inputs.seeded_order(world, rank, ms // cr, 3))
+        assert w.status() == (0, -1)
+        assert_close(to_f64(w.c), _oracle_c(shards, b, dtype, sa, sb), _tol(dtype), "C")
+    finally:
+        w.close()
+
+
+def test_order_and_mode_invariance_bitexact(gpu):
+    """C is bit-identical for every arrival order and every mode (each tile's arithmetic does
+    not depend on when its rows arrived)."""
+    world, rank, ms, cr, k, n = 4, 2, 256, 64, 1024, 512
+    shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=33)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, tile=(128, 128))
+    try:
+        cps = ms // cr
+        orders = [None, inputs.ring_order(world, rank, cps)[::-1]] + \
+            [inputs.seeded_order(world, rank, cps, s) for s in (1, 2, 3)]
+        outs = []
+        for o in orders:
+            for mode in ("overlap", "serial", "gemm_only"):
+                w.c.zero_()
+                w.run(mode, order=o)
+                outs.append(w.c.clone())
+        assert w.status() == (0, -1)
+        for c in outs[1:]:
+            assert bits_equal(c, outs[0])
+        assert_close(to_f64(outs[0]), _oracle_c(shards, b, "bf16", 1, 1), BF16_TOL, "C")
+    finally:
+        w.close()
+
+
+def test_gather_and_flags_bitexact(gpu):
+    world, rank, ms, cr, k, n = 5, 3, 96, 16, 256, 128
+    shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=41)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr)
+    try:
+        for _ in range(3):
+            w.run("overlap", order=inputs.seeded_order(world, rank, ms // cr, 8))
+        assert w.status() == (0, -1)
+        e = B.agg_ctx_epoch(w.ctx)
+        assert e == 3
+        want_g = O.gather_ref([raw(s) for s in shards])
+        assert np.array_equal(raw(w.gather), want_g)
+        flags = w.flags.cpu().numpy().astype(np.uint32)
+        cps = ms // cr
+        for c in range(world * cps):
+            assert flags[c] == (0 if c // cps == rank else e), c
+    finally:
+        w.close()
+
+
+def test_trace_each_tile_once_and_flags_seen(gpu):
+    world, rank, ms, cr, k, n = 4, 0, 128, 32, 256, 256
+    shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=51)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, tile=(64, 64))
+    try:
+        tiles = (world * ms // 64) * (n // 64)
+        buf = torch.zeros(tiles * 8, dtype=torch.int32, device="cuda")
+        B.agg_set_trace(w.ctx, buf, buf.numel() * 4)
+        order = inputs.seeded_order(world, rank, ms // cr, 4)
+        w.run("overlap", order=order)
+        assert w.status() == (0, -1)
+        rec = buf.cpu().numpy().astype(np.uint32).reshape(-1, 8)
+        assert (rec[:, 4] == 1).all()                 # visited exactly once
+        e = B.agg_ctx_epoch(w.ctx)
+        row_order, _ = O.ag_mtile_order(world, rank, ms, cr, order, 64)
+        assert B.agg_ag_row_tile_order(world, rank, ms, cr, order, 64) == row_order
+        cps = ms // cr
+        for mt in range(world * ms // 64):
+            need_remote = any(c // cps != rank for c in O.covering_chunks(mt * 64, mt * 64 + 64, cr))
+            for nt in range(n // 64):
+                r = rec[mt * (n // 64) + nt]
+                if need_remote:
+                    assert r[3] >= e and r[3] != 0xFFFFFFFF
+                else:
+                    assert r[3] == 0xFFFFFFFF
+        # within each claim list, positions follow the row-tile order
+        for lst in np.unique(rec[:, 0]):
+            sel = rec[rec[:, 0] == lst]
+            assert len(np.unique(sel[:, 1])) == len(sel)
+    finally:
+        w.close()
+
+
+def test_withheld_chunks_time_out_then_recover(gpu):
+    """Flags that never reach the epoch make the waits give up (status, failed flag id) instead
+    of hanging; after agg_ctx_reset the next call is correct."""
+    world, rank, ms, cr, k, n = 2, 0, 128, 64, 256, 128
+    shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=61)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr)
+    try:
+        B.agg_ctx_set_timeout_us(w.ctx, 20000)
+        B.agg_ctx_set_epoch(w.ctx, 7)          # flags are 0 < 7: as if chunks never arrived
+        w.run("gemm_only")
+        status, failed = w.status()
+        assert status & 1 and failed in (2, 3)
+        B.agg_ctx_reset(w.ctx, torch.cuda.current_stream())
+        assert w.status() == (0, -1)
+        w.run("overlap")
+        assert w.status() == (0, -1)
+        assert_close(to_f64(w.c), _oracle_c(shards, b, "bf16", 1, 1), BF16_TOL, "C")
+    finally:
+        w.close()
+
+
+def test_stale_epoch_is_not_accepted(gpu):
+    """A flag holding the previous epoch does not satisfy the current call's wait."""
+    world, rank, ms, cr, k, n = 2, 1, 64, 64, 128, 128
+    shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=71)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr)
+    try:
+        w.run("copy_only")                      # flags = 1
+        B.agg_ctx_set_timeout_us(w.ctx, 20000)
+        B.agg_ctx_reset(w.ctx, torch.cuda.current_stream())
+        w.flags.fill_(4)                        # an older epoch than the next one
+        B.agg_ctx_set_epoch(w.ctx, 5)
+        w.run("gemm_only")                      # waits for >= 5
+        status, failed = w.status()
+        assert status & 1 and failed == 0
+    finally:
+        w.close()
+
+
+def test_epoch_wraps_and_stays_correct(gpu):
+    world, rank, ms, cr, k, n = 3, 0, 64, 32, 128, 64
+    shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=81)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr)
+    try:
+        B.agg_ctx_set_epoch(w.ctx, 0xFFFFFFFC)
+        ref = _oracle_c(shards, b, "bf16", 1, 1)
+        seen = []
+        for i in range(4):
+            w.c.zero_()
+            w.run("overlap", order=inputs.seeded_order(world, rank, ms // cr, i + 1))
+            assert w.status() == (0, -1)
+            assert_close(to_f64(w.c), ref, BF16_TOL, f"C call {i}")
+            seen.append(B.agg_ctx_epoch(w.ctx))
+        assert seen == [0xFFFFFFFD, 0xFFFFFFFE, 1, 2]
+        flags = w.flags.cpu().numpy()
+        assert (flags[ms // cr:] == 2).all() and (flags[:ms // cr] == 0).all()
+    finally:
+        w.close()
+
+
+def test_host_delays(gpu):
+    world, rank, ms, cr, k, n = 4, 0, 128, 32, 512, 256
+    shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=91)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr)
+    try:
+        nrem = (world - 1) * ms // cr
+        w.run("overlap", delay_us=inputs.delays_us(nrem, 5, 200))
+        assert w.status() == (0, -1)
+        assert_close(to_f64(w.c), _oracle_c(shards, b, "bf16", 1, 1), BF16_TOL, "C")
+    finally:
+        w.close()
+
+
+def test_degenerate_sizes(gpu):
+    # world 1: a plain GEMM, nothing to gather
+    shards, b, _, _ = small_ag_data(1, 100, 64, 72, "bf16", seed=3)
+    w = AgWorkload(1, 0, shards, b, chunk_rows=10)
+    try:
+        w.run("overlap")
+        assert w.status() == (0, -1)
+        assert_close(to_f64(w.c), _oracle_c(shards, b, "bf16", 1, 1), BF16_TOL, "C")
+    finally:
+        w.close()
+    # k = 0: C is zero
+    shards = [torch.zeros(16, 0, dtype=torch.bfloat16) for _ in range(2)]
+    b = torch.zeros(0, 32, dtype=torch.bfloat16)
+    w = AgWorkload(2, 0, shards, b, chunk_rows=8)
+    try:
+        w.c.fill_(1.0)
+        w.run("overlap")
+        assert w.status() == (0, -1)
+        assert (w.c.float() == 0).all()
+    finally:
+        w.close()
+    # m_shard = 0: nothing at all
+    ctx = B.agg_ctx_create(0)
+    try:
+        B.ag_gemm(ctx, 2, 0, 0, 64, 64, 1, "bf16", 1.0, 1.0, [0, 0], None, None, None, None)
+    finally:
+        B.agg_ctx_destroy(ctx)
+
+
+def test_put_signal_primitive(gpu):
+    src = torch.arange(1 << 16, dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    flag = torch.zeros(4, dtype=torch.int32, device="cuda")
+    cs = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    B.agg_put_signal(dst, src, src.numel() * 4, flag[2:], 1234, cs)
+    cs.synchronize()
+    assert torch.equal(dst, src) and flag.tolist() == [0, 0, 1234, 0]
+
+
+@pytest.mark.parametrize("streams", [1, 3, 8])
+def test_copy_stream_counts(gpu, streams):
+    world, rank, ms, cr, k, n = 8, 6, 64, 16, 256, 128
+    shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=95)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr)
+    try:
+        B.agg_ctx_set_copy_streams(w.ctx, streams)
+        w.run("overlap", order=inputs.seeded_order(world, rank, ms // cr, streams))
+        assert w.status() == (0, -1)
+        assert_close(to_f64(w.c), _oracle_c(shards, b, "bf16", 1, 1), BF16_TOL, "C")
+        assert np.array_equal(raw(w.gather), O.gather_ref([raw(s) for s in shards]))
+    finally:
+        w.close()
+
+
+@pytest.mark.parametrize("elem", [1, 2])
+def test_transpose_helper(gpu, elem):
+    k, n = 300, 136
+    src = torch.randint(0, 250, (k, n), dtype=torch.uint8 if elem == 1 else torch.int16,
+                        device="cuda")
+    dst = torch.empty(n, k, dtype=src.dtype, device="cuda")
+    B.agg_transpose_kn_to_nk(src, dst, k, n, elem)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.cpu(), src.cpu().t().contiguous())
+
+
+# ---------------------------------------------------------------------- the workload configs
+
+def _run_config(name, mode="overlap", with_delays=False):
+    cfg = configs.CONFIGS[name]
+    d = configs.make_ag_data(cfg)
+    w = AgWorkload(cfg.world, cfg.rank, d["shards"], d["b"], cfg.chunk_rows, cfg.dtype,
+                   d["scale_a"], d["scale_b"])
+    return cfg, d, w
+
+
+@pytest.mark.parametrize("name", ["c1_ag_w2_tiny", "c2_ag_w8_bf16", "c4_ag_w8_decode",
+                                  "c5_ag_w8_fp8"])
+def test_config_vs_oracle(gpu, name):
+    cfg, d, w = _run_config(name)
+    try:
+        print(f"config {name}", flush=True)
+        w.run("overlap", order=cfg.order(), delay_us=cfg.delays())
+        assert w.status() == (0, -1)
+        c_ovl = w.c.clone()
+        ref = _oracle_c(d["shards"], d["b"], cfg.dtype, d["scale_a"], d["scale_b"])
+        assert_close(to_f64(c_ovl), ref, _tol(cfg.dtype), name)
+        # the same kernels in the other modes give the same bits
+        for mode in ("serial", "gemm_only"):
+            w.c.zero_()
+            w.run(mode, order=cfg.order())
+            assert w.status() == (0, -1)
+            assert bits_equal(w.c, c_ovl), mode
+        assert np.array_equal(raw(w.gather), O.gather_ref([raw(s) for s in d["shards"]]))
+    finally:
+        w.close()

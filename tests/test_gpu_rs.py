@@ -1,0 +1,145 @@
+"""GEMM+ReduceScatter on the GPU through the C ABI, compared with the CPU oracle.
+
+Bar: |x - ref| <= 1e-2 + 1e-2 |ref| for `send` and `out` (fp32 results of bf16 products);
+bit-exact for the receive buffer, the flags, and for integer-valued inputs (every fp32 sum
+exact); `out` bit-identical for every arrival order (fixed summation order).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from allgather_gemm_persistent_amd import binding as B
+from allgather_gemm_persistent_amd import configs, inputs
+from allgather_gemm_persistent_amd.workload import RsWorkload
+from oracle import agg_oracle as O
+
+from helpers import BF16_TOL, assert_close, raw, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TILES = [(256, 256), (256, 224), (128, 128), (128, 64), (64, 64)]
+
+
+def _data(world, m, k, n, seed, kind="normal"):
+    if kind == "int":
+        d = {"kind": "int", "lo": -2, "hi": 2}
+        a, _ = inputs.draw(d, (m, k), "bf16", seed)
+        b, _ = inputs.draw(d, (k, n), "bf16", seed + 1)
+        peers, _ = inputs.draw({"kind": "int", "lo": -100, "hi": 100}, (world, m // world, n), "f32", seed + 2)
+    else:
+        a, _ = inputs.draw({"kind": "normal", "std": 1.0}, (m, k), "bf16", seed)
+        b, _ = inputs.draw({"kind": "normal", "std": 0.05}, (k, n), "bf16", seed + 1)
+        peers, _ = inputs.draw({"kind": "normal", "std": 1.0}, (world, m // world, n), "f32", seed + 2)
+    return a, b, peers
+
+
+def _ref(w, a, b, peers):
+    return O.gemm_rs_ref(raw(a), raw(b), peers.numpy(), w.world, w.rank)
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("mode", ["overlap", "serial"])
+def test_ragged_vs_oracle(gpu, tile, mode):
+    world, rank, m, k, n, cr = 3, 1, 3 * 200, 328, 264, 40
+    a, b, peers = _data(world, m, k, n, seed=7)
+    w = RsWorkload(world, rank, a, b, peers, cr, tile=tile)
+    try:
+        w.run(mode, order=inputs.seeded_order(world, rank, 200 // cr, 5))
+        assert w.status() == (0, -1)
+        send, out = _ref(w, a, b, peers)
+        assert_close(to_f64(w.send[:world - 1]), send, BF16_TOL, "send")
+        assert_close(to_f64(w.out), out, BF16_TOL, "out")
+    finally:
+        w.close()
+
+
+@pytest.mark.parametrize("tile", [(256, 256), (64, 64)])
+def test_integer_inputs_bitexact(gpu, tile):
+    world, rank, m, k, n, cr = 4, 2, 4 * 96, 512, 192, 32
+    a, b, peers = _data(world, m, k, n, seed=17, kind="int")
+    w = RsWorkload(world, rank, a, b, peers, cr, tile=tile)
+    try:
+        w.run("overlap")
+        assert w.status() == (0, -1)
+        send, out = _ref(w, a, b, peers)
+        assert np.array_equal(to_f64(w.send[:world - 1]), send)
+        assert np.array_equal(to_f64(w.out), out)
+    finally:
+        w.close()
+
+
+def test_order_invariance_and_bookkeeping(gpu):
+    world, rank, m, k, n, cr = 8, 5, 8 * 64, 256, 256, 16
+    a, b, peers = _data(world, m, k, n, seed=27)
+    w = RsWorkload(world, rank, a, b, peers, cr, tile=(64, 64))
+    try:
+        cpb = (m // world) // cr
+        outs, sends = [], []
+        for s in (None, 1, 2, 3):
+            order = None if s is None else inputs.seeded_order(world, rank, cpb, s)
+            for mode in ("overlap", "serial"):
+                w.out.zero_()
+                w.run(mode, order=order)
+                outs.append(w.out.clone())
+                sends.append(w.send.clone())
+        assert w.status() == (0, -1)
+        for o, s in zip(outs[1:], sends[1:]):
+            assert torch.equal(o, outs[0]) and torch.equal(s, sends[0])
+        send, out = _ref(w, a, b, peers)
+        assert_close(to_f64(outs[0]), out, BF16_TOL, "out")
+        e = B.agg_ctx_epoch(w.ctx)
+        rf = w.flags.cpu().numpy()
+        sf = w.send_flags.cpu().numpy()
+        for c in range(world * cpb):
+            local = c // cpb == rank
+            assert rf[c] == (0 if local else e)
+            assert sf[c] == (0 if local else e)
+        recv = w.recv.cpu()
+        for p in range(world):
+            if p != rank:
+                assert torch.equal(recv[p], peers[p])
+    finally:
+        w.close()
+
+
+def test_world_one_and_k_zero(gpu):
+    a, b, peers = _data(1, 96, 64, 32, seed=37)
+    w = RsWorkload(1, 0, a, b, peers, 32)
+    try:
+        w.run("overlap")
+        assert w.status() == (0, -1)
+        _, out = _ref(w, a, b, peers)
+        assert_close(to_f64(w.out), out, BF16_TOL, "out")
+    finally:
+        w.close()
+    a = torch.zeros(64, 0, dtype=torch.bfloat16)
+    b = torch.zeros(0, 32, dtype=torch.bfloat16)
+    peers = inputs.draw({"kind": "normal", "std": 1.0}, (2, 32, 32), "f32", 3)[0]
+    w = RsWorkload(2, 1, a, b, peers, 16)
+    try:
+        w.run("overlap")
+        assert w.status() == (0, -1)
+        assert torch.equal(w.out.cpu(), peers[0])
+    finally:
+        w.close()
+
+
+def test_config_c3_vs_oracle(gpu):
+    cfg = configs.CONFIGS["c3_rs_w8_bf16"]
+    d = configs.make_rs_data(cfg)
+    w = RsWorkload(cfg.world, cfg.rank, d["a"], d["b"], d["peers"], cfg.chunk_rows)
+    try:
+        print("config c3", flush=True)
+        w.run("overlap", order=cfg.order())
+        assert w.status() == (0, -1)
+        send, out = O.gemm_rs_ref(raw(d["a"]), raw(d["b"]), d["peers"].numpy(), cfg.world, cfg.rank)
+        assert_close(to_f64(w.send), send, BF16_TOL, "send")
+        assert_close(to_f64(w.out), out, BF16_TOL, "out")
+        o1 = w.out.clone()
+        w.out.zero_()
+        w.run("serial", order=cfg.order())
+        assert w.status() == (0, -1)
+        assert torch.equal(w.out, o1)
+    finally:
+        w.close()
