@@ -45,6 +45,8 @@ _SIGNATURES = {
     "agg_ctx_set_timeout_us": [_vp, _c_u64],
     "agg_ctx_set_tile": [_vp, _c_int, _c_int],
     "agg_set_trace": [_vp, _vp, _sz],
+    "agg_ctx_set_timing": [_vp, _c_int],
+    "agg_ctx_kernel_times": [_vp, ctypes.POINTER(ctypes.c_float), _c_int, ctypes.POINTER(_c_int)],
     "agg_put_signal": [_vp, _vp, _sz, _vp, _c_u32, _vp],
     "agg_ctx_set_copy_streams": [_vp, _c_int],
     "agg_ctx_set_reserved_cus": [_vp, _c_int],
@@ -195,6 +197,18 @@ def agg_ctx_set_timeout_us(ctx, timeout_us: int) -> None:
 
 def agg_ctx_set_tile(ctx, bm: int = 0, bn: int = 0) -> None:
     _call("agg_ctx_set_tile", ctx, bm, bn)
+
+
+def agg_ctx_set_timing(ctx, on: bool = True) -> None:
+    _call("agg_ctx_set_timing", ctx, 1 if on else 0)
+
+
+def agg_ctx_kernel_times(ctx, max_n: int = 256) -> list:
+    """Durations (ms) of the last launches' consumer kernels, oldest first."""
+    buf = (ctypes.c_float * max_n)()
+    n = _c_int()
+    _call("agg_ctx_kernel_times", ctx, buf, max_n, ctypes.byref(n))
+    return list(buf[:n.value])
 
 
 def agg_set_trace(ctx, buf=None, nbytes: int = 0) -> None:

@@ -55,6 +55,7 @@ constexpr uint32_t kEpochLast = 0xFFFFFFFEu;   // 0xFFFFFFFF means "no flag" in 
 constexpr int kMaxCopyStreams = 8;
 constexpr int kDefaultCopyStreams = 4;
 constexpr int kDefaultReservedCus = 32;
+constexpr int kTimingRing = 256;          // launches whose kernel duration is kept
 
 enum FlagSlot { kFlagsAg = 0, kFlagsRsRecv = 1, kFlagsRsSend = 2, kFlagSlots = 3 };
 
@@ -77,6 +78,9 @@ struct agg_ctx {
   hipEvent_t ev_copy[kMaxCopyStreams] = {};
   uint32_t* trace = nullptr;
   size_t trace_bytes = 0;
+  bool timing = false;                      // record a timing event pair around each launch
+  hipEvent_t ev_t0[kTimingRing] = {}, ev_t1[kTimingRing] = {};
+  uint64_t launches = 0;                    // launches recorded since timing was switched on
   uint32_t* bound[kFlagSlots] = {nullptr, nullptr, nullptr};
   size_t bound_words[kFlagSlots] = {0, 0, 0};
 };
@@ -238,6 +242,19 @@ int schedule(agg_ctx* ctx, int mode, hipStream_t s, hipStream_t us,
   return AGG_OK;
 }
 
+// Enqueue the consumer kernel on ctx->ks, bracketed by a timing event pair when timing is on.
+template <typename F>
+int timed_launch(agg_ctx* ctx, F launch) {
+  const int slot = int(ctx->launches % kTimingRing);
+  if (ctx->timing) HIP_TRY(hipEventRecord(ctx->ev_t0[slot], ctx->ks));
+  HIP_TRY(launch());
+  if (ctx->timing) {
+    HIP_TRY(hipEventRecord(ctx->ev_t1[slot], ctx->ks));
+    ++ctx->launches;
+  }
+  return AGG_OK;
+}
+
 void fill_common(agg_ctx* ctx, GemmArgs& g) {
   g.scratch = ctx->scratch;
   g.n_lists = std::min(ctx->lists, kMaxLists);
@@ -318,6 +335,10 @@ extern "C" int agg_ctx_destroy(agg_ctx* ctx) {
   if (ctx->scratch) step(hipFree(ctx->scratch), "hipFree(scratch)");
   for (hipEvent_t e : {ctx->ev_fork, ctx->ev_kernel, ctx->ev_user})
     if (e) step(hipEventDestroy(e), "hipEventDestroy");
+  for (int j = 0; j < kTimingRing; ++j) {
+    if (ctx->ev_t0[j]) step(hipEventDestroy(ctx->ev_t0[j]), "hipEventDestroy");
+    if (ctx->ev_t1[j]) step(hipEventDestroy(ctx->ev_t1[j]), "hipEventDestroy");
+  }
   for (int j = 0; j < kMaxCopyStreams; ++j) {
     if (ctx->ev_copy[j]) step(hipEventDestroy(ctx->ev_copy[j]), "hipEventDestroy");
     if (ctx->cstream[j]) step(hipStreamDestroy(ctx->cstream[j]), "hipStreamDestroy");
@@ -415,6 +436,37 @@ extern "C" int agg_ctx_set_copy_streams(agg_ctx* ctx, int n) {
   return AGG_OK;
 }
 
+extern "C" int agg_ctx_set_timing(agg_ctx* ctx, int on) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (on && !ctx->ev_t0[0]) {
+    HIP_TRY(hipSetDevice(ctx->device));
+    for (int j = 0; j < kTimingRing; ++j) {
+      HIP_TRY(hipEventCreate(&ctx->ev_t0[j]));
+      HIP_TRY(hipEventCreate(&ctx->ev_t1[j]));
+    }
+  }
+  ctx->timing = on != 0;
+  ctx->launches = 0;
+  return AGG_OK;
+}
+
+extern "C" int agg_ctx_kernel_times(agg_ctx* ctx, float* ms, int max, int* n) {
+  clear_error();
+  if (!ctx || !n || (max > 0 && !ms)) return fail(AGG_E_ARG, "NULL argument");
+  if (!ctx->timing) return fail(AGG_E_STATE, "timing is off (agg_ctx_set_timing)");
+  HIP_TRY(hipSetDevice(ctx->device));
+  const uint64_t have = std::min<uint64_t>(ctx->launches, kTimingRing);
+  const int count = int(std::min<uint64_t>(have, uint64_t(std::max(max, 0))));
+  for (int i = 0; i < count; ++i) {
+    const int slot = int((ctx->launches - uint64_t(count) + uint64_t(i)) % kTimingRing);
+    HIP_TRY(hipEventSynchronize(ctx->ev_t1[slot]));
+    HIP_TRY(hipEventElapsedTime(&ms[i], ctx->ev_t0[slot], ctx->ev_t1[slot]));
+  }
+  *n = count;
+  return AGG_OK;
+}
+
 extern "C" int agg_set_trace(agg_ctx* ctx, void* dev_buf, size_t bytes) {
   clear_error();
   if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
@@ -508,8 +560,9 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
     attach_trace(ctx, g, tiles);
   }
   auto launch = [&]() -> int {
-    HIP_TRY(launch_gemm(g, ts.bm, ts.bn, dtype, kEpiAllGather, grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks), ctx->ks));
-    return AGG_OK;
+    return timed_launch(ctx, [&]() {
+      return launch_gemm(g, ts.bm, ts.bn, dtype, kEpiAllGather, grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks), ctx->ks);
+    });
   };
   return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
                   [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams); });
@@ -589,8 +642,9 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
     attach_trace(ctx, g, tiles);
   }
   auto launch = [&]() -> int {
-    HIP_TRY(launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiReduceScatter, grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks), ctx->ks));
-    return AGG_OK;
+    return timed_launch(ctx, [&]() {
+      return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiReduceScatter, grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks), ctx->ks);
+    });
   };
   return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
                   [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams); });

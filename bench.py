@@ -1,0 +1,182 @@
+#!/usr/bin/env python3
+"""Benchmark: one rank's share of the overlapped AllGather+GEMM on one MI355X.
+
+One step is one ag_gemm call in overlap mode on the W=8 bf16 workload (A: 8 shards x 512 rows,
+4096 x 8192; W_local 8192 x 3584; 128-row chunks arriving in ring order): call setup, the
+producer's put + signal of the 28 remote chunks, tile claims in arrival order, flag waits, the
+MFMA main loop and the bf16 epilogue, and the join. Inputs are resident in HBM before timing.
+
+Printed (one JSON line): overlapped TFLOP/s (value), % of the bf16 MFMA peak, the overlap
+figures R = T_ovl / T_gemm and eta = (T_serial - T_ovl) / min(T_copy, T_gemm) from the same
+kernels in the other modes, the dominant kernel's roofline (its own duration from timing events
+on the stream it runs on), and the CPU oracle's rate on the same workload as a baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "overlapped AG+GEMM TFLOP/s on 1 MI355X (% MFMA peak) + overlap efficiency"
+PEAK_BF16_TFLOPS = 2516.6      # dense bf16 MFMA: 256 CUs x 4096 flop/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the W=8 bf16 one)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--modes", default="overlap,gemm_only,copy_only,serial",
+                    help="modes to time; the overlapped steps always run (profiling runs use"
+                         " 'overlap' alone so that every consumer-kernel launch is a timed step)")
+    return ap.parse_args()
+
+
+def time_mode(w, mode, order, steps, warmup):
+    """Mean wall time per call (us) of `steps` back-to-back calls, synchronised on both sides."""
+    import torch
+    for _ in range(warmup):
+        w.run(mode, order=order)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        w.run(mode, order=order)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps * 1e6
+    st = w.status()
+    if st[0]:
+        raise RuntimeError(f"{mode}: a chunk wait gave up (flag {st[1]})")
+    return dt
+
+
+def cpu_baseline(cfg, data):
+    """The CPU oracle on the whole workload (float64, numpy/BLAS threads)."""
+    from threadpoolctl import threadpool_info
+
+    from allgather_gemm_persistent_amd import inputs
+    from oracle import agg_oracle as O
+    shards = [inputs.raw_bits(s) for s in data["shards"]]
+    b = inputs.raw_bits(data["b"])
+    t0 = time.perf_counter()
+    O.ag_gemm_ref(shards, b, cfg.dtype, data["scale_a"], data["scale_b"])
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [os.cpu_count() or 1])
+    return {"value": round(cfg.flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole workload ({cfg.m}x{cfg.n}x{cfg.k}, {cfg.flops / 1e9:.1f} GFLOP):"
+                      f" exact decode + float64 matmul, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build runs one rank's share of the collective "
+              f"on one MI355X); --gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from allgather_gemm_persistent_amd import binding as B
+    from allgather_gemm_persistent_amd import configs
+    from allgather_gemm_persistent_amd.workload import AgWorkload
+
+    name = args.workload or configs.HEADLINE
+    cfg = configs.CONFIGS[name]
+    assert cfg.op == "ag", "the benchmark measures AllGather+GEMM workloads"
+    data = configs.make_ag_data(cfg)
+    w = AgWorkload(cfg.world, cfg.rank, data["shards"], data["b"], cfg.chunk_rows, cfg.dtype,
+                   data["scale_a"], data["scale_b"])
+    order = cfg.order()
+    peak = PEAK_FP8_TFLOPS if cfg.dtype == "fp8" else PEAK_BF16_TFLOPS
+    try:
+        B.agg_ctx_set_timing(w.ctx, True)
+        # the timed steps: overlapped calls
+        for _ in range(args.warmup):
+            w.run("overlap", order=order)
+        torch.cuda.synchronize()
+        B.agg_ctx_set_timing(w.ctx, True)          # clears the ring: only timed launches count
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            w.run("overlap", order=order)
+        torch.cuda.synchronize()
+        t_ovl = (time.perf_counter() - t0) / args.steps * 1e6
+        st = w.status()
+        if st[0]:
+            raise RuntimeError(f"overlap: a chunk wait gave up (flag {st[1]})")
+        kms = B.agg_ctx_kernel_times(w.ctx, args.steps)
+        k_ovl_us = statistics.mean(kms) * 1e3
+        # the same kernels in the other modes
+        modes = set(args.modes.split(","))
+        t_gemm = t_copy = t_serial = k_gemm_us = None
+        if "gemm_only" in modes:
+            B.agg_ctx_set_timing(w.ctx, True)
+            t_gemm = time_mode(w, "gemm_only", order, args.steps, args.warmup)
+            k_gemm_us = statistics.mean(B.agg_ctx_kernel_times(w.ctx, args.steps)) * 1e3
+        if "copy_only" in modes:
+            t_copy = time_mode(w, "copy_only", order, args.steps, args.warmup)
+        if "serial" in modes:
+            t_serial = time_mode(w, "serial", order, args.steps, args.warmup)
+    finally:
+        B.agg_ctx_set_timing(w.ctx, False)
+        w.close()
+
+    flops = cfg.flops
+    value = flops / (t_ovl * 1e-6) / 1e12
+    achieved = flops / (k_ovl_us * 1e-6) / 1e12
+
+    def rnd(x, d=1):
+        return None if x is None else round(x, d)
+    full = None not in (t_gemm, t_copy, t_serial)
+    eta = (t_serial - t_ovl) / min(t_copy, t_gemm) if full else None
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_ovl / 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": f"{name}: AllGather+GEMM one rank's share, W={cfg.world}, "
+                               f"A {cfg.m}x{cfg.k} ({cfg.world} shards x {cfg.m_shard} rows), "
+                               f"W_local {cfg.k}x{cfg.n}, chunk_rows={cfg.chunk_rows}, "
+                               f"{cfg.order_kind} arrival, {cfg.dtype}, fp32 accumulate, bf16 out",
+                   "m": cfg.m, "n": cfg.n, "k": cfg.k, "world": cfg.world,
+                   "chunk_rows": cfg.chunk_rows},
+        "pct_mfma_peak": round(100 * value / peak, 2),
+        "overlap": {"t_ovl_us": round(t_ovl, 1), "t_gemm_us": rnd(t_gemm),
+                    "t_copy_us": rnd(t_copy), "t_serial_us": rnd(t_serial),
+                    "R": rnd(t_ovl / t_gemm, 3) if t_gemm else None, "eta": rnd(eta, 3),
+                    "gemm_only_tflops": rnd(flops / (t_gemm * 1e-6) / 1e12) if t_gemm else None,
+                    "gemm_only_kernel_us": rnd(k_gemm_us)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "agg::gemm_kernel (overlap launch)",
+                     "kernel_us": round(k_ovl_us, 1),
+                     "gemm_only_frac": rnd(flops / (k_gemm_us * 1e-6) / 1e12 / peak, 4)
+                     if k_gemm_us else None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, data)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -121,6 +121,13 @@ int agg_ctx_set_reserved_cus(agg_ctx* ctx, int n);
  * Shapes: 256x256, 256x224, 128x128, 128x64, 64x64; anything else is AGG_E_ARG. */
 int agg_ctx_set_tile(agg_ctx* ctx, int bm, int bn);
 
+/* Kernel timing: with timing on, each call brackets its consumer kernel with a pair of timing
+ * events on the kernel's own stream (a ring of the last 256 launches; switching it on clears
+ * the ring). agg_ctx_kernel_times waits for and returns the durations in milliseconds of the
+ * last min(max, recorded) launches, oldest first, in ms[0..*n). */
+int agg_ctx_set_timing(agg_ctx* ctx, int on);
+int agg_ctx_kernel_times(agg_ctx* ctx, float* ms, int max, int* n);
+
 /* Optional per-tile trace (NULL or 0 bytes disables). The buffer is device memory of
  * `bytes` >= 32 * tiles bytes; each computed tile (m-tile i, n-tile j) writes the 8 words
  * agg_trace_rec at index i * n_tiles + j: claim list, position in that list, XCD id of the
