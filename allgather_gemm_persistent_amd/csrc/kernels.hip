@@ -57,6 +57,69 @@ __device__ inline uint32_t lds_off(int row, int ch) {
   return (uint32_t)(row * kRowBytes + ((ch ^ (row & 7)) << 4));
 }
 
+// ---- bf16 operand pipeline: 32-element (64-byte) K slices, four LDS stages filled by
+// direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds). One wave instruction writes 1 KiB of
+// LDS: 16 tile rows of 64 bytes, lane i landing at byte 16*i. Lane i therefore fetches row i/4
+// of its 16-row group and the 16-byte chunk that the swizzle below puts at position i%4.
+constexpr int kSliceBytes = 64;
+constexpr int kStages = 4;
+
+// byte offset of 16-byte chunk `g` (0..3) of LDS row `row` in a 64-byte-row stage: rows 2q and
+// 2q+1 share a 128-byte bank line, so chunks rotate with row/2; a ds_read_b128 of 16
+// consecutive rows at one chunk touches every bank once per 8 lanes
+__device__ inline uint32_t lds64_off(int row, int g) {
+  return (uint32_t)(row * kSliceBytes + ((g ^ ((row >> 1) & 3)) << 4));
+}
+
+// Wait until at most N of this wave's vector loads are in flight and its LDS reads are done,
+// then meet the other waves. One asm block, so that no compiler fence drains every load.
+template <int N>
+__device__ inline void stage_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+// acc += B fragment x A fragment, one 16x16x32 bf16 MFMA. The asm ties the accumulator to its
+// AGPRs: with the builtin's untied form the register allocator rotates the accumulators through
+// copies every K slice. volatile keeps the MFMAs in program order with the LDS reads and
+// barriers placed around them. The hardware does not interlock accumulator reads and writes by
+// other instructions against these MFMAs, so the caller brackets them with acc_settle().
+__device__ inline void mfma_bf16(f32x4& acc, const u32x4& b, const u32x4& a) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+}
+
+// 24 wait states: more than any MFMA result or operand hazard needs (19 for a 16-pass op).
+// Every accumulator then passes through an empty asm placed after the nops, so that nothing the
+// compiler emits touches an accumulator between the MFMAs and the nops.
+template <int FM, int FN>
+__device__ inline void acc_settle(f32x4 (&acc)[FM][FN]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Raw buffer descriptor (base, no stride, num_records bytes) in four scalar registers.
+__device__ inline u32x4 buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xFFFFu, bytes, (uint32_t)kBufferFlags};
+}
+
+// One direct-to-LDS load: 16 bytes per lane from desc + voff into LDS at lds_base + 16 * lane.
+// Issued as asm so that the compiler neither waits for it nor reorders LDS accesses around it:
+// the main loop accounts for these loads itself (stage_barrier / the final drain).
+__device__ inline void lds_dma_load(const u32x4& desc, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_base), "v"(voff), "s"(desc) : "memory", "m0");
+}
+
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)p);
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays a quiet NaN)
 __device__ inline uint32_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -195,12 +258,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int A_LOADS = BM * 8 / kThreads, B_LOADS = BN * 8 / kThreads;
-  constexpr int KSTEPS = FP8 ? 1 : 2;             // MFMA K steps per 128-byte slice
-  constexpr int CPL = FP8 ? 2 : 1;                // 16-byte chunks per lane per step
   static_assert(BM * 8 % kThreads == 0 && BN * 8 % kThreads == 0, "tile rows");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  // fp8 path: two 128-byte-slice stages staged through registers
+  __shared__ __attribute__((aligned(16))) uint8_t smem[FP8 ? 2 * STAGE : 16];
+  // bf16 path: four 64-byte-slice stages
+  constexpr int BNP = (BN + 63) / 64 * 64;                   // B rows held in LDS
+  constexpr int DSTAGE = FP8 ? 16 : (BM + BNP) * kSliceBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t stages[kStages * DSTAGE];
   __shared__ int s_tile[4];
   __shared__ int s_ok;
 
@@ -208,7 +274,6 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int home = a.n_lists > 1 ? xcc_id() % a.n_lists : 0;
   const int64_t kbytes = a.K * (FP8 ? 1 : 2);
-  const int nk = (int)((kbytes + kRowBytes - 1) / kRowBytes);
 
   for (;;) {
     if (tid == 0) {
@@ -264,57 +329,145 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         const_cast<uint8_t*>(a.a), 0, (int)(a.M * kbytes), kBufferFlags);
     const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(a.b), 0, (int)(a.N * kbytes), kBufferFlags);
-    u32x4 ra[A_LOADS], rb[B_LOADS];
-    auto gload = [&](int kt) {
-      const uint32_t kb = (uint32_t)kt * kRowBytes;
-#pragma unroll
-      for (int i = 0; i < A_LOADS; ++i) {
-        const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
-        const uint32_t kbyte = kb + ch * 16;
-        const uint32_t off = kbyte < (uint32_t)kbytes ? (uint32_t)(lo + row) * (uint32_t)kbytes + kbyte : kOutOfRange;
-        ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0));
-      }
-#pragma unroll
-      for (int i = 0; i < B_LOADS; ++i) {
-        const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
-        const uint32_t kbyte = kb + ch * 16;
-        const uint32_t off = kbyte < (uint32_t)kbytes ? (uint32_t)(n0 + row) * (uint32_t)kbytes + kbyte : kOutOfRange;
-        rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, off, 0, 0));
-      }
-    };
-    auto sstore = [&](int buf) {
-      uint8_t* As = smem + buf * STAGE;
-      uint8_t* Bs = As + A_BYTES;
-#pragma unroll
-      for (int i = 0; i < A_LOADS; ++i) {
-        const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
-        *reinterpret_cast<u32x4*>(As + lds_off(row, ch)) = ra[i];
-      }
-#pragma unroll
-      for (int i = 0; i < B_LOADS; ++i) {
-        const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
-        *reinterpret_cast<u32x4*>(Bs + lds_off(row, ch)) = rb[i];
-      }
-    };
 
-    if (nk > 0) {
-      gload(0);
-      sstore(0);
-      __syncthreads();
-    }
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) gload(kt + 1);
-      const uint8_t* As = smem + buf * STAGE;
-      const uint8_t* Bs = As + A_BYTES;
+    if constexpr (!FP8) {
+      // ---- bf16: 4-stage direct-to-LDS pipeline over 64-byte K slices
+      constexpr int NI = (BM + BNP) / 64;      // load instructions per wave per stage
+      constexpr int NA = BM / 64;              // the first NA of them fetch A rows
+      // lane's chunk: rows of a 16-row group are lane/4, chunk position lane%4
+      const uint32_t gk = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) << 4);
+      uint32_t base[NI];
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        // all B fragments of this step stay in registers; A fragments stream one row block at
-        // a time, which keeps the live operand registers at (FN + 1) * CPL * 4
-        u32x4 fb[FN][CPL];
+      for (int j = 0; j < NI; ++j) {
+        const int r = (j * 4 + wave) * 16 + (lane >> 2);   // LDS row
+        if (j < NA) {
+          const int64_t gr = lo + r;
+          base[j] = gr < a.M ? (uint32_t)gr * (uint32_t)kbytes + gk : kOutOfRange;
+        } else {
+          const int c = r - BM;
+          const int64_t gn = n0 + c;
+          base[j] = (c < BN && gn < a.N) ? (uint32_t)gn * (uint32_t)kbytes + gk : kOutOfRange;
+        }
+      }
+      const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+      const u32x4 da = buffer_desc(a.a, (uint32_t)(a.M * kbytes));
+      const u32x4 db = buffer_desc(a.b, (uint32_t)(a.N * kbytes));
+      const uint32_t lds0 = lds_addr(stages) + (uint32_t)wave_u * 1024u;
+      auto issue = [&](int t) {
+        const uint32_t tk = (uint32_t)t * kSliceBytes;
+        // past the K end: set the offset's top bit (out of range, reads zero) without a branch
+        const uint32_t oob = (uint32_t)((int)(tk + gk - (uint32_t)kbytes) >> 31) ^ 0xFFFFFFFFu;
+        const uint32_t kmask = oob & kOutOfRange;
+        const uint32_t st = lds0 + (uint32_t)(t & (kStages - 1)) * DSTAGE;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          const int ch = kk * 4 * CPL + (lane >> 4) * CPL + j;
+        for (int j = 0; j < NI; ++j)
+          lds_dma_load(j < NA ? da : db, st + j * 4096u, (base[j] + tk) | kmask);
+      };
+      auto load_b = [&](u32x4 (&fb)[FN], int t) {
+        const uint8_t* st = stages + (t & (kStages - 1)) * DSTAGE;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          fb[j] = *reinterpret_cast<const u32x4*>(
+              st + lds64_off(BM + wn * WTN + j * 16 + (lane & 15), lane >> 4));
+      };
+      auto load_a = [&](int t, int i) {
+        const uint8_t* st = stages + (t & (kStages - 1)) * DSTAGE;
+        return *reinterpret_cast<const u32x4*>(
+            st + lds64_off(wm * WTM + i * 16 + (lane & 15), lane >> 4));
+      };
+      // One K slice t, with its B fragments in fbc and its first A fragment in fa (both
+      // requested earlier). Each row's A fragment is requested one row ahead; before the last
+      // row the waves meet (slice t+1 has landed everywhere, slice t is fully read), slice
+      // t+1's fragments are requested into fbn / fa, and slice t+4 refills slice t's slot.
+      u32x4 fa;
+      auto slice = [&](u32x4 (&fbc)[FN], u32x4 (&fbn)[FN], int t) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          u32x4 fan;
+          if (i + 1 < FM) {
+            fan = load_a(t, i + 1);
+          } else {
+            stage_barrier<2 * NI>();
+            load_b(fbn, t + 1);
+            fan = load_a(t + 1, 0);
+          }
+#pragma unroll
+          for (int j = 0; j < FN; ++j) mfma_bf16(acc[i][j], fbc[j], fa);
+          if (i + 1 == FM) issue(t + 4);
+          fa = fan;
+        }
+      };
+      const int nk = (int)((kbytes + kSliceBytes - 1) / kSliceBytes);
+      if (nk > 0) {
+        u32x4 fb0[FN], fb1[FN];
+        acc_settle(acc);
+        issue(0);
+        issue(1);
+        issue(2);
+        issue(3);
+        stage_barrier<3 * NI>();
+        load_b(fb0, 0);
+        fa = load_a(0, 0);
+        // slices past the K end read zeros: an odd count runs one zero slice
+        for (int t = 0; t < nk; t += 2) {
+          slice(fb0, fb1, t);
+          slice(fb1, fb0, t + 1);
+        }
+        acc_settle(acc);
+        // loads issued past the end land (as zeros) and every wave is done with LDS before the
+        // next tile refills it
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+    } else {
+      // ---- fp8: 128-byte K slices staged through registers, two LDS stages
+      const int nk = (int)((kbytes + kRowBytes - 1) / kRowBytes);
+      u32x4 ra[A_LOADS], rb[B_LOADS];
+      auto gload = [&](int kt) {
+        const uint32_t kb = (uint32_t)kt * kRowBytes;
+#pragma unroll
+        for (int i = 0; i < A_LOADS; ++i) {
+          const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
+          const uint32_t kbyte = kb + ch * 16;
+          const uint32_t off = kbyte < (uint32_t)kbytes ? (uint32_t)(lo + row) * (uint32_t)kbytes + kbyte : kOutOfRange;
+          ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0));
+        }
+#pragma unroll
+        for (int i = 0; i < B_LOADS; ++i) {
+          const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
+          const uint32_t kbyte = kb + ch * 16;
+          const uint32_t off = kbyte < (uint32_t)kbytes ? (uint32_t)(n0 + row) * (uint32_t)kbytes + kbyte : kOutOfRange;
+          rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, off, 0, 0));
+        }
+      };
+      auto sstore = [&](int buf) {
+        uint8_t* As = smem + buf * STAGE;
+        uint8_t* Bs = As + A_BYTES;
+#pragma unroll
+        for (int i = 0; i < A_LOADS; ++i) {
+          const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
+          *reinterpret_cast<u32x4*>(As + lds_off(row, ch)) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < B_LOADS; ++i) {
+          const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
+          *reinterpret_cast<u32x4*>(Bs + lds_off(row, ch)) = rb[i];
+        }
+      };
+      if (nk > 0) {
+        gload(0);
+        sstore(0);
+        __syncthreads();
+      }
+      for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload(kt + 1);
+        const uint8_t* As = smem + buf * STAGE;
+        const uint8_t* Bs = As + A_BYTES;
+        // B fragments of the slice stay in registers; A fragments stream one row block at a time
+        u32x4 fb[FN][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int ch = (lane >> 4) * 2 + j;
 #pragma unroll
           for (int i = 0; i < FN; ++i) {
             const int row = wn * WTN + i * 16 + (lane & 15);
@@ -323,32 +476,26 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          u32x4 fa[CPL];
+          u32x4 fa[2];
           const int row = wm * WTM + i * 16 + (lane & 15);
 #pragma unroll
-          for (int j = 0; j < CPL; ++j)
-            fa[j] = *reinterpret_cast<const u32x4*>(As + lds_off(row, kk * 4 * CPL + (lane >> 4) * CPL + j));
+          for (int j = 0; j < 2; ++j)
+            fa[j] = *reinterpret_cast<const u32x4*>(As + lds_off(row, (lane >> 4) * 2 + j));
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            if constexpr (FP8) {
-              i32x8 opa, opb;
+            i32x8 opa, opb;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                opa[e] = (int)fb[j][0][e]; opa[e + 4] = (int)fb[j][1][e];
-                opb[e] = (int)fa[0][e]; opb[e + 4] = (int)fa[1][e];
-              }
-              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  opa, opb, acc[i][j], 0, 0, 0, 127, 0, 127);
-            } else {
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(bf16x8, fb[j][0]), __builtin_bit_cast(bf16x8, fa[0]),
-                  acc[i][j], 0, 0, 0);
+            for (int e = 0; e < 4; ++e) {
+              opa[e] = (int)fb[j][0][e]; opa[e + 4] = (int)fb[j][1][e];
+              opb[e] = (int)fa[0][e]; opb[e + 4] = (int)fa[1][e];
             }
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                opa, opb, acc[i][j], 0, 0, 0, 127, 0, 127);
           }
         }
+        if (kt + 1 < nk) sstore(buf ^ 1);
+        __syncthreads();
       }
-      if (kt + 1 < nk) sstore(buf ^ 1);
-      __syncthreads();
     }
 
     // ---- epilogue
