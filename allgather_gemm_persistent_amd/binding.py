@@ -44,6 +44,8 @@ _SIGNATURES = {
     "agg_ctx_set_epoch": [_vp, _c_u32],
     "agg_ctx_set_timeout_us": [_vp, _c_u64],
     "agg_ctx_set_tile": [_vp, _c_int, _c_int],
+    "agg_ctx_set_lists": [_vp, _c_int, _c_int],
+    "agg_ctx_set_producer": [_vp, _c_int, _c_int, _c_int],
     "agg_set_trace": [_vp, _vp, _sz],
     "agg_ctx_set_timing": [_vp, _c_int],
     "agg_ctx_kernel_times": [_vp, ctypes.POINTER(ctypes.c_float), _c_int, ctypes.POINTER(_c_int)],
@@ -221,6 +223,19 @@ def agg_put_signal(dst, src, nbytes: int, flag, value: int, copy_stream) -> None
 
 def agg_ctx_set_copy_streams(ctx, n: int) -> None:
     _call("agg_ctx_set_copy_streams", ctx, n)
+
+
+PRODUCERS = {"cu": 0, "sdma": 1}
+
+
+def agg_ctx_set_producer(ctx, kind="cu", copy_wgs: int = 0, piece_kib: int = 0) -> None:
+    """Producer of later calls: "cu" (copy jobs inside the persistent kernel) or "sdma"."""
+    _call("agg_ctx_set_producer", ctx, PRODUCERS[kind] if isinstance(kind, str) else int(kind),
+          copy_wgs, piece_kib)
+
+
+def agg_ctx_set_lists(ctx, lists: int = 8, list_cols: int = 0) -> None:
+    _call("agg_ctx_set_lists", ctx, lists, list_cols)
 
 
 def agg_ctx_set_reserved_cus(ctx, n: int) -> None:

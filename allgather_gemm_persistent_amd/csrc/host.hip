@@ -22,6 +22,11 @@
 // fills a CU; 8 and 16 free CUs were measured to still starve it); every other mode uses all
 // CUs.
 //
+// The CU producer needs none of that: copy workgroups inside the persistent kernel take the chunk
+// copies as jobs (arrival order, a chunk cut into pieces), the workgroup that completes a chunk
+// releases its flag, and copy workgroups turn to tiles when the jobs run out. Its arrival order
+// and delays sit in the ctx scratch, uploaded only when they change.
+//
 // Chunks are spread over several copy streams (chunk i of the arrival order on stream i mod S),
 // each stream feeding its own SDMA engine the way W-1 peers feed separate links; every stream
 // keeps the arrival order, so chunks land in that order in groups of S.
@@ -56,6 +61,7 @@ constexpr int kMaxCopyStreams = 8;
 constexpr int kDefaultCopyStreams = 4;
 constexpr int kDefaultReservedCus = 32;
 constexpr int kTimingRing = 256;          // launches whose kernel duration is kept
+constexpr int64_t kDefaultPieceBytes = 256 << 10;
 
 enum FlagSlot { kFlagsAg = 0, kFlagsRsRecv = 1, kFlagsRsSend = 2, kFlagSlots = 3 };
 
@@ -65,6 +71,7 @@ struct agg_ctx {
   int device = 0;
   int cus = 0;
   int lists = 8;                    // claim lists: one per XCD of an MI355X
+  int list_cols = 0;                // column blocks of the list grid (0: chosen per call)
   uint32_t* scratch = nullptr;      // kScrWords words
   uint32_t epoch = 0;
   uint64_t timeout_us = 2000000;
@@ -83,6 +90,14 @@ struct agg_ctx {
   uint64_t launches = 0;                    // launches recorded since timing was switched on
   uint32_t* bound[kFlagSlots] = {nullptr, nullptr, nullptr};
   size_t bound_words[kFlagSlots] = {0, 0, 0};
+  int producer = AGG_PRODUCER_CU;
+  int copy_wgs = 0;                          // 0: every workgroup takes copy jobs first
+  int64_t piece_bytes = kDefaultPieceBytes;
+  // arrival order + cumulative delays as uploaded to scratch (kScrOrder / kScrDelay)
+  std::vector<uint32_t> up_order, up_delay;
+  uint32_t* up_host = nullptr;               // pinned staging, 2 * AGG_MAX_CHUNKS words
+  hipEvent_t ev_upload = nullptr;
+  bool upload_pending = false;
 };
 
 namespace {
@@ -255,10 +270,66 @@ int timed_launch(agg_ctx* ctx, F launch) {
   return AGG_OK;
 }
 
-void fill_common(agg_ctx* ctx, GemmArgs& g) {
+void fill_common(agg_ctx* ctx, GemmArgs& g, TileShape ts, int grid) {
   g.scratch = ctx->scratch;
   g.n_lists = std::min(ctx->lists, kMaxLists);
+  g.list_cols = ctx->list_cols > 0 && g.n_lists % ctx->list_cols == 0
+                    ? ctx->list_cols
+                    : choose_list_cols(g.n_lists, g.n_row_tiles, g.n_col_tiles, ts.bm, ts.bn,
+                                       (grid + g.n_lists - 1) / g.n_lists);
   g.timeout_ticks = uint64_t(double(ctx->timeout_us) * ctx->ticks_per_us);
+}
+
+// Put the arrival order (and the cumulative delays, in wall-clock ticks) where the kernel's
+// producer reads them; skipped when they equal what is already there.
+int upload_schedule(agg_ctx* ctx, hipStream_t s, const std::vector<int32_t>& ord,
+                    const uint32_t* delay_us) {
+  std::vector<uint32_t> o(ord.begin(), ord.end()), d;
+  if (delay_us) {
+    d.resize(ord.size());
+    double sum = 0;
+    for (size_t i = 0; i < ord.size(); ++i) {
+      sum += double(delay_us[i]) * ctx->ticks_per_us;
+      d[i] = uint32_t(std::min(sum, 4.0e9));
+    }
+  }
+  const bool same_o = o == ctx->up_order;
+  const bool same_d = d.empty() || d == ctx->up_delay;
+  if (same_o && same_d) return AGG_OK;
+  if (!ctx->up_host) HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&ctx->up_host), 2 * AGG_MAX_CHUNKS * sizeof(uint32_t)));
+  if (ctx->upload_pending) HIP_TRY(hipEventSynchronize(ctx->ev_upload));   // staging still in use
+  if (!same_o) {
+    std::memcpy(ctx->up_host, o.data(), o.size() * sizeof(uint32_t));
+    HIP_TRY(hipMemcpyAsync(ctx->scratch + kScrOrder, ctx->up_host, o.size() * sizeof(uint32_t),
+                           hipMemcpyHostToDevice, s));
+    ctx->up_order = o;
+  }
+  if (!same_d) {
+    std::memcpy(ctx->up_host + AGG_MAX_CHUNKS, d.data(), d.size() * sizeof(uint32_t));
+    HIP_TRY(hipMemcpyAsync(ctx->scratch + kScrDelay, ctx->up_host + AGG_MAX_CHUNKS,
+                           d.size() * sizeof(uint32_t), hipMemcpyHostToDevice, s));
+    ctx->up_delay = d;
+  }
+  HIP_TRY(hipEventRecord(ctx->ev_upload, s));
+  ctx->upload_pending = true;
+  return AGG_OK;
+}
+
+// Copy-job fields of the kernel arguments for the CU producer.
+void fill_copies(agg_ctx* ctx, GemmArgs& g, const ChunkCopy& cc, uint32_t* flags, size_t n_order,
+                 bool delays, int world, int grid) {
+  for (int p = 0; p < world; ++p) g.peer[p] = cc.src[p];
+  g.sym = cc.dst;
+  g.put_flags = flags;
+  g.chunk_bytes = cc.cr * cc.row_bytes;
+  const int64_t piece = std::max<int64_t>(16, ctx->piece_bytes / 16 * 16);
+  g.piece_bytes = std::min<int64_t>(g.chunk_bytes, piece);
+  g.pieces = g.piece_bytes > 0 ? int((g.chunk_bytes + g.piece_bytes - 1) / g.piece_bytes) : 1;
+  if (g.piece_bytes == 0) g.piece_bytes = 16;   // empty chunks (k = 0): one empty piece each
+  g.copy_jobs = uint32_t(n_order) * uint32_t(g.pieces);
+  g.copy_cps = cc.cps;
+  g.copy_wgs = ctx->copy_wgs > 0 ? std::min(ctx->copy_wgs, grid) : grid;
+  g.copy_delays = delays ? 1 : 0;
 }
 
 void attach_trace(agg_ctx* ctx, GemmArgs& g, int64_t tiles) {
@@ -266,6 +337,69 @@ void attach_trace(agg_ctx* ctx, GemmArgs& g, int64_t tiles) {
     g.trace = ctx->trace;
     g.trace_tiles = uint32_t(tiles);
   }
+}
+
+// One launch of the persistent kernel under the CU producer: `copies` adds the copy jobs,
+// `tiles_on` keeps the GEMM tiles (without them: a copy-only grid of one workgroup per CU).
+int launch_cu(agg_ctx* ctx, const GemmArgs& g, TileShape ts, int dtype, int epi, int grid,
+              const ChunkCopy& cc, uint32_t* flags, size_t n_order, bool delays, int world,
+              uint32_t epoch, bool copies, bool tiles_on, bool timed) {
+  GemmArgs h = g;
+  int gr = grid;
+  if (!tiles_on) {
+    h.n_row_tiles = 0;
+    h.n_col_tiles = 0;
+    h.trace = nullptr;
+    h.trace_tiles = 0;
+    h.scratch = ctx->scratch;
+    h.n_lists = 1;
+    h.list_cols = 1;
+    h.epoch = epoch;
+    gr = ctx->cus;
+  }
+  if (copies) {
+    h.epoch = epoch;
+    fill_copies(ctx, h, cc, flags, n_order, delays, world, gr);
+  } else {
+    h.copy_jobs = 0;
+  }
+  auto go = [&]() { return launch_gemm(h, ts.bm, ts.bn, dtype, epi, gr, ctx->ks); };
+  if (timed) return timed_launch(ctx, go);
+  HIP_TRY(go());
+  return AGG_OK;
+}
+
+// Stream choreography under the CU producer, everything on ctx->ks:
+//   OVERLAP:   stream -> ks; one launch (copy jobs, then tiles); ks -> stream
+//   SERIAL:    stream -> ks; copy-only launch; GEMM launch; ks -> stream
+//   GEMM_ONLY: stream -> ks; GEMM launch; ks -> stream
+//   COPY_ONLY: stream -> ks; copy-only launch; ks -> stream
+// A non-NULL user copy stream is joined as in schedule(). `launch(copies, tiles, timed)`.
+template <typename Launch>
+int schedule_cu(agg_ctx* ctx, int mode, hipStream_t s, hipStream_t us, bool kernel, bool chunks,
+                Launch launch) {
+  HIP_TRY(hipEventRecord(ctx->ev_fork, s));
+  HIP_TRY(hipStreamWaitEvent(ctx->ks, ctx->ev_fork, 0));
+  if (chunks && us) {
+    HIP_TRY(hipEventRecord(ctx->ev_user, us));
+    HIP_TRY(hipStreamWaitEvent(ctx->ks, ctx->ev_user, 0));
+  }
+  int rc = AGG_OK;
+  if (mode == AGG_OVERLAP) {
+    if (kernel || chunks) rc = launch(chunks, kernel, true);
+  } else if (mode == AGG_SERIAL) {
+    if (chunks) rc = launch(true, false, !kernel);
+    if (rc == AGG_OK && kernel) rc = launch(false, true, true);
+  } else if (mode == AGG_GEMM_ONLY) {
+    if (kernel) rc = launch(false, true, true);
+  } else if (chunks) {
+    rc = launch(true, false, true);
+  }
+  if (rc != AGG_OK) return rc;
+  HIP_TRY(hipEventRecord(ctx->ev_kernel, ctx->ks));
+  HIP_TRY(hipStreamWaitEvent(s, ctx->ev_kernel, 0));
+  if (chunks && us) HIP_TRY(hipStreamWaitEvent(us, ctx->ev_kernel, 0));
+  return AGG_OK;
 }
 
 }  // namespace
@@ -308,6 +442,7 @@ extern "C" int agg_ctx_create(int device, agg_ctx** out) {
   step(hipEventCreateWithFlags(&ctx->ev_fork, hipEventDisableTiming), "hipEventCreate");
   step(hipEventCreateWithFlags(&ctx->ev_kernel, hipEventDisableTiming), "hipEventCreate");
   step(hipEventCreateWithFlags(&ctx->ev_user, hipEventDisableTiming), "hipEventCreate");
+  step(hipEventCreateWithFlags(&ctx->ev_upload, hipEventDisableTiming), "hipEventCreate");
   for (int j = 0; j < kMaxCopyStreams; ++j)
     step(hipEventCreateWithFlags(&ctx->ev_copy[j], hipEventDisableTiming), "hipEventCreate");
   if (rc == AGG_OK) step(make_own_queue_stream(ctx, &ctx->ks), "hipExtStreamCreateWithCUMask");
@@ -333,8 +468,9 @@ extern "C" int agg_ctx_destroy(agg_ctx* ctx) {
   step(hipSetDevice(ctx->device), "hipSetDevice");
   step(hipDeviceSynchronize(), "hipDeviceSynchronize");
   if (ctx->scratch) step(hipFree(ctx->scratch), "hipFree(scratch)");
-  for (hipEvent_t e : {ctx->ev_fork, ctx->ev_kernel, ctx->ev_user})
+  for (hipEvent_t e : {ctx->ev_fork, ctx->ev_kernel, ctx->ev_user, ctx->ev_upload})
     if (e) step(hipEventDestroy(e), "hipEventDestroy");
+  if (ctx->up_host) step(hipHostFree(ctx->up_host), "hipHostFree");
   for (int j = 0; j < kTimingRing; ++j) {
     if (ctx->ev_t0[j]) step(hipEventDestroy(ctx->ev_t0[j]), "hipEventDestroy");
     if (ctx->ev_t1[j]) step(hipEventDestroy(ctx->ev_t1[j]), "hipEventDestroy");
@@ -363,6 +499,8 @@ extern "C" int agg_ctx_reset(agg_ctx* ctx, agg_stream stream) {
   HIP_TRY(launch_fill_u32(ctx->scratch + kScrFailed, 1, 0xFFFFFFFFu, S(stream)));
   HIP_TRY(hipStreamSynchronize(S(stream)));
   ctx->epoch = 0;
+  ctx->up_order.clear();   // the scratch copy of the order and delays is gone too
+  ctx->up_delay.clear();
   return AGG_OK;
 }
 
@@ -418,6 +556,28 @@ extern "C" int agg_ctx_set_tile(agg_ctx* ctx, int bm, int bn) {
       return AGG_OK;
     }
   return fail(AGG_E_ARG, "no kernel for a %dx%d tile", bm, bn);
+}
+
+extern "C" int agg_ctx_set_producer(agg_ctx* ctx, int kind, int copy_wgs, int piece_kib) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (kind != AGG_PRODUCER_CU && kind != AGG_PRODUCER_SDMA) return fail(AGG_E_ARG, "unknown producer kind %d", kind);
+  if (copy_wgs < 0 || piece_kib < 0) return fail(AGG_E_ARG, "negative copy_wgs or piece_kib");
+  ctx->producer = kind;
+  ctx->copy_wgs = copy_wgs;
+  ctx->piece_bytes = piece_kib > 0 ? int64_t(piece_kib) << 10 : kDefaultPieceBytes;
+  return AGG_OK;
+}
+
+extern "C" int agg_ctx_set_lists(agg_ctx* ctx, int lists, int list_cols) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (lists < 1 || lists > kMaxLists) return fail(AGG_E_ARG, "lists must be in [1, %d]", kMaxLists);
+  if (list_cols < 0 || (list_cols > 0 && lists % list_cols != 0))
+    return fail(AGG_E_ARG, "list_cols (%d) must be 0 or divide lists (%d)", list_cols, lists);
+  ctx->lists = lists;
+  ctx->list_cols = list_cols;
+  return AGG_OK;
 }
 
 extern "C" int agg_ctx_set_reserved_cus(agg_ctx* ctx, int n) {
@@ -519,8 +679,9 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
   hipStream_t s = S(stream);
   const bool kernel = (mode != AGG_COPY_ONLY) && n > 0;
   const bool chunks = (mode != AGG_GEMM_ONLY) && world > 1;
+  const bool cu = ctx->producer == AGG_PRODUCER_CU;
   std::vector<hipStream_t> cstreams;
-  if (chunks)
+  if (chunks && !cu)
     if (int rc = copy_streams(ctx, ord.size(), cstreams)) return rc;
   uint32_t epoch = ctx->epoch;
   if (chunks)
@@ -537,6 +698,7 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
   GemmArgs g;
   std::memset(&g, 0, sizeof g);
   int64_t tiles = 0;
+  int grid = 1;
   if (kernel) {
     const std::vector<int32_t> rows = ag_row_tile_order(world, rank, m_shard, chunk_rows, ord, ts.bm);
     for (size_t i = 0; i < rows.size(); ++i) g.row_order[i] = uint16_t(rows[i]);
@@ -555,13 +717,23 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
     g.n_col_tiles = int((n + ts.bn - 1) / ts.bn);
     g.epoch = world > 1 ? epoch : 0;
     g.scale = dtype == AGG_FP8_E4M3 ? scale_a * scale_b : 1.0f;
-    fill_common(ctx, g);
     tiles = int64_t(g.n_row_tiles) * g.n_col_tiles;
+    grid = grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks && !cu);
+    fill_common(ctx, g, ts, grid);
     attach_trace(ctx, g, tiles);
+  }
+  if (cu) {
+    if (chunks)
+      if (int rc = upload_schedule(ctx, s, ord, delay_us)) return rc;
+    return schedule_cu(ctx, mode, s, S(copy_stream), kernel, chunks,
+                       [&](bool copies, bool tiles_on, bool timed) {
+                         return launch_cu(ctx, g, ts, dtype, kEpiAllGather, grid, cc, flags, ord.size(),
+                                          delay_us != nullptr, world, epoch, copies, tiles_on, timed);
+                       });
   }
   auto launch = [&]() -> int {
     return timed_launch(ctx, [&]() {
-      return launch_gemm(g, ts.bm, ts.bn, dtype, kEpiAllGather, grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks), ctx->ks);
+      return launch_gemm(g, ts.bm, ts.bn, dtype, kEpiAllGather, grid, ctx->ks);
     });
   };
   return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
@@ -596,8 +768,9 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
   hipStream_t s = S(stream);
   const bool kernel = mode != AGG_COPY_ONLY;
   const bool chunks = (mode != AGG_GEMM_ONLY) && world > 1;
+  const bool cu = ctx->producer == AGG_PRODUCER_CU;
   std::vector<hipStream_t> cstreams;
-  if (chunks)
+  if (chunks && !cu)
     if (int rc = copy_streams(ctx, ord.size(), cstreams)) return rc;
   uint32_t epoch = ctx->epoch;
   if (chunks)
@@ -614,6 +787,7 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
   GemmArgs g;
   std::memset(&g, 0, sizeof g);
   int64_t tiles = 0;
+  int grid = 1;
   if (kernel) {
     const std::vector<int32_t> rows = rs_row_tile_order(world, rank, m, chunk_rows, ord, ts.bm);
     for (size_t i = 0; i < rows.size(); ++i) g.row_order[i] = uint16_t(rows[i]);
@@ -637,13 +811,24 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
     g.n_col_tiles = int((n + ts.bn - 1) / ts.bn);
     g.epoch = world > 1 ? epoch : 0;
     g.scale = 1.0f;
-    fill_common(ctx, g);
     tiles = int64_t(g.n_row_tiles) * g.n_col_tiles;
+    grid = grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks && !cu);
+    fill_common(ctx, g, ts, grid);
     attach_trace(ctx, g, tiles);
+  }
+  if (cu) {
+    if (chunks)
+      if (int rc = upload_schedule(ctx, s, ord, delay_us)) return rc;
+    return schedule_cu(ctx, mode, s, S(copy_stream), kernel, chunks,
+                       [&](bool copies, bool tiles_on, bool timed) {
+                         return launch_cu(ctx, g, ts, AGG_BF16, kEpiReduceScatter, grid, cc, flags,
+                                          ord.size(), delay_us != nullptr, world, epoch, copies,
+                                          tiles_on, timed);
+                       });
   }
   auto launch = [&]() -> int {
     return timed_launch(ctx, [&]() {
-      return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiReduceScatter, grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks), ctx->ks);
+      return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiReduceScatter, grid, ctx->ks);
     });
   };
   return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,

@@ -14,8 +14,13 @@ constexpr int kScrLists = 0;       // claim-list counters, one per XCD (<= 16)
 constexpr int kScrDone = 16;       // workgroups that finished the current launch
 constexpr int kScrStatus = 17;     // bit 0: a flag wait gave up
 constexpr int kScrFailed = 18;     // first flag index that timed out (0xFFFFFFFF = none)
+constexpr int kScrCopyNext = 19;   // in-kernel producer: next copy job
+constexpr int kScrCopyT0 = 20;     // in-kernel producer: wall clock of the first job (delays)
 constexpr int kScrRsCount = 64;    // ReduceScatter per-send-chunk completion counters
-constexpr int kScrWords = kScrRsCount + AGG_MAX_CHUNKS;
+constexpr int kScrPieces = kScrRsCount + AGG_MAX_CHUNKS;   // per-chunk copied-piece counters
+constexpr int kScrOrder = kScrPieces + AGG_MAX_CHUNKS;     // arrival order (chunk ids)
+constexpr int kScrDelay = kScrOrder + AGG_MAX_CHUNKS;      // cumulative producer delays (ticks)
+constexpr int kScrWords = kScrDelay + AGG_MAX_CHUNKS;
 constexpr int kMaxLists = 16;
 
 enum Epilogue { kEpiAllGather = 0, kEpiReduceScatter = 1 };
@@ -39,10 +44,22 @@ struct GemmArgs {
   int n_col_tiles;          // ceil(N/BN)
   int tpb;                  // RS: row tiles per block
   int n_lists;              // claim lists (one per XCD)
+  int list_cols;            // lists split as (n_lists / list_cols) row groups x list_cols column blocks
   uint32_t epoch;           // flags >= epoch mean "arrived"
   float scale;              // fp8: scale_a * scale_b; bf16: 1
   uint64_t timeout_ticks;   // in wall-clock (s_memrealtime) ticks
   uint32_t trace_tiles;     // capacity of `trace` in tiles (0 = off)
+  // in-kernel producer: copy job i*pieces + q moves piece q of the i-th arriving chunk from its
+  // peer's block to the symmetric buffer; the job completing a chunk releases its flag
+  const uint8_t* peer[AGG_MAX_WORLD];   // per-peer source blocks (emulated peers)
+  uint8_t* sym;                         // symmetric buffer (AG gather / RS receive)
+  uint32_t* put_flags;                  // flags the producer releases
+  int64_t chunk_bytes, piece_bytes;
+  uint32_t copy_jobs;                   // 0: no copies in this launch
+  int pieces;                           // pieces per chunk
+  int copy_wgs;                         // workgroups that take copy jobs first (<= grid)
+  int copy_cps;                         // chunks per peer block
+  int copy_delays;                      // nonzero: honour the cumulative delays in scratch
   uint16_t row_order[AGG_MAX_ROW_TILES];  // row tiles in compute order
 };
 

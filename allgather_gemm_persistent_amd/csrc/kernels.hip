@@ -111,10 +111,16 @@ __device__ inline u32x4 buffer_desc(const void* base, uint32_t bytes) {
 // One direct-to-LDS load: 16 bytes per lane from desc + voff into LDS at lds_base + 16 * lane.
 // Issued as asm so that the compiler neither waits for it nor reorders LDS accesses around it:
 // the main loop accounts for these loads itself (stage_barrier / the final drain).
+// M0 is reserved by the compiler, which in these kernels never holds a value in it (checked on
+// the generated code), so the asm may set it; the s_nop is the wait state the hardware needs
+// between an M0 write and the LDS-destination load that reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ inline void lds_dma_load(const u32x4& desc, uint32_t lds_base, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds_base), "v"(voff), "s"(desc) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)p);
@@ -128,29 +134,106 @@ __device__ inline uint32_t bf16_rne(float f) {
   return u >> 16;
 }
 
+// Copy `bytes` (a multiple of 16) from src to dst with the whole workgroup: 16-byte vectors,
+// eight in flight per thread. The source (a peer's block) is read once, so its loads are
+// non-temporal; the destination stays cacheable because the GEMM reads it next.
+__device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __restrict__ src,
+                                  int64_t bytes, int tid) {
+  constexpr int U = 8;
+  const int64_t n16 = bytes >> 4;
+  const u32x4* s = reinterpret_cast<const u32x4*>(src);
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  int64_t i = tid;
+  for (; i + (U - 1) * kThreads < n16; i += U * kThreads) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(s + i + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[i + u * kThreads] = v[u];
+  }
+  for (; i < n16; i += kThreads) d[i] = __builtin_nontemporal_load(s + i);
+}
+
+// The in-kernel producer: take copy jobs until none are left. Job j*pieces + q copies piece q of
+// the chunk at arrival position j; the job that completes a chunk (all its pieces copied and
+// released) stores the epoch into the chunk's flag. Jobs are claimed in arrival order, so
+// chunks complete roughly in that order. With delays, job j*pieces + q starts no earlier than
+// the j-th cumulative delay after the first job was claimed.
+__device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job) {
+  const uint32_t* order = a.scratch + kScrOrder;
+  // every value that decides a branch around a barrier is made visibly uniform
+  // (readfirstlane): otherwise the compiler may treat the loop exit as divergent and lay the
+  // loop out so that the lanes of one wave run different iterations, which misaligns the
+  // barriers between the waves
+  const uint32_t jobs = __builtin_amdgcn_readfirstlane(a.copy_jobs);
+  const uint32_t pieces = __builtin_amdgcn_readfirstlane((uint32_t)a.pieces);
+  auto next_job = [&]() -> uint32_t {
+    if (tid == 0) s_job[0] = (int)atomicAdd(a.scratch + kScrCopyNext, 1u);
+    __syncthreads();
+    const uint32_t job = (uint32_t)__builtin_amdgcn_readfirstlane(s_job[0]);
+    __syncthreads();
+    return job;
+  };
+  uint32_t t0 = 0;
+  if (a.copy_delays && tid == 0) {
+    const uint32_t now = wall_ticks() | 1u;   // never 0, which marks "unset"
+    const uint32_t prev = atomicCAS(a.scratch + kScrCopyT0, 0u, now);
+    t0 = prev ? prev : now;
+  }
+  for (uint32_t job = next_job(); job < jobs; job = next_job()) {
+    const uint32_t j = job / pieces, q = job - j * pieces;
+    const int c = (int)__builtin_amdgcn_readfirstlane(order[j]);
+    const int p = c / a.copy_cps, jl = c - p * a.copy_cps;
+    if (a.copy_delays && tid == 0) {
+      const uint32_t due = a.scratch[kScrDelay + j];
+      while (wall_ticks() - t0 < due) __builtin_amdgcn_s_sleep(2);
+    }
+    __syncthreads();
+    const int64_t lo = (int64_t)q * a.piece_bytes;
+    const int64_t hi = lo + a.piece_bytes < a.chunk_bytes ? lo + a.piece_bytes : a.chunk_bytes;
+    const int64_t base = (int64_t)jl * a.chunk_bytes;
+    copy_piece(a.sym + ((int64_t)p * a.copy_cps) * a.chunk_bytes + base + lo,
+               a.peer[p] + base + lo, hi - lo, tid);
+    // every thread's stores, then one count per piece; the last piece publishes the chunk
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(a.scratch + kScrPieces + c, 1u, __ATOMIC_ACQ_REL,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      if (prev + 1 == pieces)
+        __hip_atomic_store(a.put_flags + c, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+  }
+}
+
 struct Tile {
   int row_tile;   // index into the row tiles (AG: m-tile; RS: block * tpb + tile)
   int col_tile;
   int list, pos;
 };
 
-// Claim the next tile: this XCD's list first, then the others in turn. List x holds, for every
-// row tile in compute order, the column tiles [x*nc/L, (x+1)*nc/L).
+// Claim the next tile: this XCD's list first, then the others in turn. The lists form a
+// (L / list_cols) x list_cols grid: list x holds the row tiles at compute positions
+// x / list_cols, + L / list_cols, ... (so every list follows the compute order) crossed with
+// column tiles [xc*nc/list_cols, (xc+1)*nc/list_cols), xc = x % list_cols.
 __device__ inline bool claim(const GemmArgs& a, int home, Tile& t) {
   const int L = a.n_lists;
+  const int Lc = a.list_cols, Lr = L / Lc;
   for (int d = 0; d < L; ++d) {
     int x = home + d;
     if (x >= L) x -= L;
-    const int c_lo = (int)((int64_t)x * a.n_col_tiles / L);
-    const int c_hi = (int)((int64_t)(x + 1) * a.n_col_tiles / L);
+    const int xr = x / Lc, xc = x - xr * Lc;
+    const int c_lo = (int)((int64_t)xc * a.n_col_tiles / Lc);
+    const int c_hi = (int)((int64_t)(xc + 1) * a.n_col_tiles / Lc);
     const int nx = c_hi - c_lo;
-    if (nx <= 0) continue;
-    const uint32_t len = (uint32_t)a.n_row_tiles * (uint32_t)nx;
+    const int ny = xr < a.n_row_tiles ? (a.n_row_tiles - xr + Lr - 1) / Lr : 0;
+    if (nx <= 0 || ny <= 0) continue;
+    const uint32_t len = (uint32_t)ny * (uint32_t)nx;
     uint32_t* ctr = a.scratch + kScrLists + x;
     if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
     const uint32_t k = atomicAdd(ctr, 1u);
     if (k < len) {
-      t.row_tile = a.row_order[k / nx];
+      t.row_tile = a.row_order[xr + (int)(k / nx) * Lr];
       t.col_tile = c_lo + (int)(k % nx);
       t.list = x;
       t.pos = (int)k;
@@ -275,6 +358,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   const int home = a.n_lists > 1 ? xcc_id() % a.n_lists : 0;
   const int64_t kbytes = a.K * (FP8 ? 1 : 2);
 
+  // ---- producer phase: the first copy_wgs workgroups move the remote chunks, then compute
+  if (a.copy_jobs && (int)blockIdx.x < a.copy_wgs) produce_chunks(a, tid, s_tile);
+
   for (;;) {
     if (tid == 0) {
       Tile t;
@@ -285,9 +371,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       }
     }
     __syncthreads();
-    const int row_tile = s_tile[0];
+    // uniform for the compiler too (see produce_chunks)
+    const int row_tile = __builtin_amdgcn_readfirstlane(s_tile[0]);
     if (row_tile < 0) break;
-    const int col_tile = s_tile[1];
+    const int col_tile = __builtin_amdgcn_readfirstlane(s_tile[1]);
     int64_t lo, hi;
     int block, tib;
     tile_rows<BM, EPI>(a, row_tile, lo, hi, block, tib);
@@ -310,7 +397,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       }
     }
     __syncthreads();
-    if (!s_ok) {
+    if (!__builtin_amdgcn_readfirstlane(s_ok)) {
       __syncthreads();
       continue;  // abandoned (timeout): the tile's output is left as it was
     }
@@ -583,9 +670,18 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     s_ok = (prev == gridDim.x - 1);
   }
   __syncthreads();
-  if (s_ok) {
+  if (__builtin_amdgcn_readfirstlane(s_ok)) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (tid < kMaxLists) __hip_atomic_store(a.scratch + kScrLists + tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.copy_jobs) {
+      if (tid == 0) {
+        __hip_atomic_store(a.scratch + kScrCopyNext, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.scratch + kScrCopyT0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      for (uint32_t i = tid; i * (uint32_t)a.pieces < a.copy_jobs; i += kThreads)
+        __hip_atomic_store(a.scratch + kScrPieces + a.scratch[kScrOrder + i], 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (EPI == kEpiReduceScatter)
       for (int i = tid; i < a.world * a.cps; i += kThreads)
         __hip_atomic_store(a.scratch + kScrRsCount + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

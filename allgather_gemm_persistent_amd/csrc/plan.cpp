@@ -39,6 +39,27 @@ const std::vector<TileShape>& tile_shapes() {
   return shapes;
 }
 
+int choose_list_cols(int lists, int n_row_tiles, int n_col_tiles, int bm, int bn, int workers) {
+  int best = 1;
+  int64_t best_rows = -1;
+  workers = std::max(workers, 1);
+  for (int lc = 1; lc <= lists; lc *= 2) {
+    if (lists % lc) continue;
+    const int lr = lists / lc;
+    if (lc > n_col_tiles || lr > std::max(n_row_tiles, 1)) continue;
+    const int64_t nx = (n_col_tiles + lc - 1) / lc;            // column tiles per list
+    const int64_t ny = (n_row_tiles + lr - 1) / lr;            // row tiles per list
+    const int64_t cols = std::min<int64_t>(nx, workers);
+    const int64_t rows = std::min<int64_t>((workers + nx - 1) / nx, ny);
+    const int64_t touched = rows * bm + cols * bn;
+    if (best_rows < 0 || touched < best_rows) {
+      best_rows = touched;
+      best = lc;
+    }
+  }
+  return best;
+}
+
 TileShape choose_tile(int op, int dtype, int64_t m, int64_t n, int64_t k) {
   (void)op;
   (void)dtype;

@@ -19,6 +19,12 @@ struct TileShape {
 // Output tile shape for one call. op: 0 = AllGather+GEMM, 1 = GEMM+ReduceScatter.
 TileShape choose_tile(int op, int dtype, int64_t m, int64_t n, int64_t k);
 
+// Split of the claim lists (one per XCD) into list_rows x list_cols: list x takes the row tiles
+// at compute positions x / list_cols, + list_rows, + 2 * list_rows, ... and the column tiles of
+// block x % list_cols. Picks the split whose first wave of tiles on one XCD (`workers` tiles in
+// flight) touches the fewest distinct A and B rows per K step, so the XCD's L2 holds them.
+int choose_list_cols(int lists, int n_row_tiles, int n_col_tiles, int bm, int bn, int workers);
+
 // Every candidate tile shape the kernels are instantiated for.
 const std::vector<TileShape>& tile_shapes();
 

@@ -21,7 +21,7 @@ class AgWorkload:
     """
 
     def __init__(self, world, rank, shards, b_kn, chunk_rows, dtype="bf16", scale_a=1.0,
-                 scale_b=1.0, device="cuda", tile=None):
+                 scale_b=1.0, device="cuda", tile=None, producer="cu"):
         self.world, self.rank, self.chunk_rows, self.dtype = world, rank, chunk_rows, dtype
         self.m_shard, self.k = shards[0].shape
         self.n = b_kn.shape[1]
@@ -42,6 +42,7 @@ class AgWorkload:
         self.c = torch.zeros(self.m, self.n, dtype=torch.bfloat16, device=self.device)
         self.copy_stream = None     # the ctx runs the copies on its own streams
         self.ctx = B.agg_ctx_create(self.device.index or 0)
+        B.agg_ctx_set_producer(self.ctx, producer)
         if tile:
             B.agg_ctx_set_tile(self.ctx, *tile)
 
@@ -76,7 +77,8 @@ class RsWorkload:
     unused).
     """
 
-    def __init__(self, world, rank, a, b_kn, peers, chunk_rows, device="cuda", tile=None):
+    def __init__(self, world, rank, a, b_kn, peers, chunk_rows, device="cuda", tile=None,
+                 producer="cu"):
         self.world, self.rank, self.chunk_rows = world, rank, chunk_rows
         self.m, self.k = a.shape
         self.n = b_kn.shape[1]
@@ -94,6 +96,7 @@ class RsWorkload:
         self.out = torch.zeros(self.mb, self.n, dtype=torch.float32, device=self.device)
         self.copy_stream = None     # the ctx runs the copies on its own streams
         self.ctx = B.agg_ctx_create(self.device.index or 0)
+        B.agg_ctx_set_producer(self.ctx, producer)
         if tile:
             B.agg_ctx_set_tile(self.ctx, *tile)
 

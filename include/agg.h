@@ -11,12 +11,17 @@
  * computation tiles, with synchronization inserted; device-level tiles are data movements on
  * DMA engines, core-level tiles live in registers, shared memory and matrix units.
  *
- * On one GPU the W-1 peers are "staging" regions in HBM. A producer on side streams copies them
- * chunk by chunk into a symmetric gather buffer with the SDMA engines and after each chunk
- * writes the call's epoch into that chunk's flag word with a stream write. A persistent MFMA
- * GEMM kernel (on a ctx-owned stream with a hardware queue of its own) claims output tiles in
- * the order their chunks arrive, waits on the flags each tile needs, and computes; while chunks
- * are in flight it leaves a few CUs free for the producer (agg_ctx_set_reserved_cus).
+ * On one GPU the W-1 peers are "staging" regions in HBM. A producer moves them chunk by chunk,
+ * in arrival order, into a symmetric gather buffer and after each chunk releases the call's
+ * epoch into that chunk's flag word. A persistent MFMA GEMM kernel (on a ctx-owned stream with a
+ * hardware queue of its own) claims output tiles in the order their chunks arrive, waits on the
+ * flags each tile needs, and computes. Two producers are built (agg_ctx_set_producer):
+ *  - AGG_PRODUCER_CU (default): copy workgroups inside the persistent kernel itself take the
+ *    chunk copies as jobs before they turn to tiles, the communication-by-compute-units form
+ *    (thread blocks dedicated to data movement) of the same overlap;
+ *  - AGG_PRODUCER_SDMA: the copy engines, one hipMemcpyAsync (no CU) plus one stream write per
+ *    chunk on side streams; while chunks are in flight the kernel leaves a few CUs free for the
+ *    runtime's own helper kernels (agg_ctx_set_reserved_cus).
  *
  * Conventions (every entry point):
  *  - Returns AGG_OK (0) or an AGG_E_* code; agg_last_error() then holds a text for the
@@ -112,6 +117,20 @@ int agg_ctx_set_timeout_us(agg_ctx* ctx, uint64_t timeout_us);
  * so every stream keeps the arrival order and the SDMA engines work in parallel. */
 int agg_ctx_set_copy_streams(agg_ctx* ctx, int n);
 
+/* Producer kinds. */
+enum {
+  AGG_PRODUCER_CU = 0,    /* copy jobs inside the persistent kernel (default) */
+  AGG_PRODUCER_SDMA = 1   /* hipMemcpyAsync (copy engines) + stream write per chunk */
+};
+
+/* Select the producer of later calls. For AGG_PRODUCER_CU, `copy_wgs` workgroups of the
+ * persistent grid (0: all of them) first take copy jobs, each moving `piece_kib` KiB of one chunk
+ * (0: 256; a chunk is cut into ceil(chunk bytes / piece) pieces), in arrival order, and only then
+ * claim tiles; the workgroup that completes a chunk's last piece releases its flag. The other
+ * arguments are ignored for AGG_PRODUCER_SDMA. AGG_E_ARG for an unknown kind or a negative
+ * count. */
+int agg_ctx_set_producer(agg_ctx* ctx, int kind, int copy_wgs, int piece_kib);
+
 /* CUs the persistent grid leaves free in AGG_OVERLAP mode (default 32, four per XCD), where
  * the producer's copies and flag writes must run beside it: in the HIP runtime shipped with
  * torch several of them execute as runtime kernels and need a CU. 0..CUs-1. */
@@ -120,6 +139,14 @@ int agg_ctx_set_reserved_cus(agg_ctx* ctx, int n);
 /* Force the output tile shape (bm x bn) of later calls; 0, 0 restores the automatic choice.
  * Shapes: 256x256, 256x224, 128x128, 128x64, 64x64; anything else is AGG_E_ARG. */
 int agg_ctx_set_tile(agg_ctx* ctx, int bm, int bn);
+
+/* Tile-claim lists of later calls. The persistent workgroups claim tiles from `lists` lists
+ * (1..16, default 8: one per XCD, a workgroup starting on the list of the XCD it runs on and
+ * stealing from the others when that is empty). The lists form a (lists / list_cols) x list_cols
+ * grid over the output: row tiles dealt round-robin in compute order to the grid rows, column
+ * tiles in list_cols contiguous blocks, so the tiles in flight on one XCD share A rows and B
+ * columns in its L2. list_cols must divide lists; 0 picks it per call from the tile counts. */
+int agg_ctx_set_lists(agg_ctx* ctx, int lists, int list_cols);
 
 /* Kernel timing: with timing on, each call brackets its consumer kernel with a pair of timing
  * events on the kernel's own stream (a ring of the last 256 launches; switching it on clears
@@ -173,13 +200,17 @@ int agg_put_signal(void* dst, const void* src, size_t bytes, uint32_t* flag, uin
  *   order, n_order   HOST: the remote chunk ids in arrival order, a permutation of all
  *                    (world-1)*m_shard/cr of them; NULL with n_order 0 = ring order (peers
  *                    rank+1, rank+2, ... mod world; chunks ascending within a peer)
- *   delay_us         HOST, NULL or n_order entries: wait this long before enqueueing each chunk
+ *   delay_us         HOST, NULL or n_order entries: emulated late peers. Chunk i of the arrival
+ *                    order starts no earlier than delay_us[0] + ... + delay_us[i] after the
+ *                    first chunk could (SDMA producer: the calling thread waits delay_us[i]
+ *                    before enqueueing chunk i; CU producer: the copy job waits on the GPU)
  *   mode             AGG_OVERLAP / AGG_SERIAL / AGG_GEMM_ONLY / AGG_COPY_ONLY
  *   stream           the caller's stream: the call is ordered after earlier work on it, and
  *                    later work on it is ordered after the call (kernel and copies)
  *   copy_stream      optional (NULL allowed, else != stream): the copies also start after
  *                    earlier work on it, and later work on it starts after the copies. The
  *                    copies themselves run on the ctx's own streams (agg_ctx_set_copy_streams)
+ *                    or inside the kernel (AGG_PRODUCER_CU)
  * Alignment: k * elem and n * 2 bytes multiples of 16, device pointers 16-byte aligned. */
 int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64_t k,
             int chunk_rows, int dtype, float scale_a, float scale_b,

@@ -19,6 +19,7 @@ from helpers import BF16_TOL, FP8_TOL, assert_close, bits_equal, raw, small_ag_d
 pytestmark = pytest.mark.gpu
 
 TILES = [(256, 256), (256, 224), (128, 128), (128, 64), (64, 64)]
+PRODUCERS = ["cu", "sdma"]
 
 
 def _oracle_c(shards, b, dtype, sa, sb):
@@ -70,14 +71,15 @@ def test_integer_inputs_bitexact(gpu, dtype, tile):
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("mode", ["overlap", "serial"])
-def test_ragged_shapes_vs_oracle(gpu, dtype, tile, mode):
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_ragged_shapes_vs_oracle(gpu, dtype, tile, mode, producer):
     """Sizes that are not multiples of any tile: ragged rows, columns and K tail."""
     world, rank, ms, cr, k, n = 3, 1, 200, 40, 328, 264
     if dtype == "fp8":
         k = 336
     shards, b, sa, sb = small_ag_data(world, ms, k, n, dtype, seed=21)
     w = AgWorkload(world, rank, shards, b, chunk_rows=cr, dtype=dtype, scale_a=sa, scale_b=sb,
-                   tile=tile)
+                   tile=tile, producer=producer)
     try:
         w.run(mode, order=inputs.seeded_order(world, rank, ms // cr, 3))
         assert w.status() == (0, -1)
@@ -86,12 +88,13 @@ def test_ragged_shapes_vs_oracle(gpu, dtype, tile, mode):
         w.close()
 
 
-def test_order_and_mode_invariance_bitexact(gpu):
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_order_and_mode_invariance_bitexact(gpu, producer):
     """C is bit-identical for every arrival order and every mode (each tile's arithmetic does
     not depend on when its rows arrived)."""
     world, rank, ms, cr, k, n = 4, 2, 256, 64, 1024, 512
     shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=33)
-    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, tile=(128, 128))
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, tile=(128, 128), producer=producer)
     try:
         cps = ms // cr
         orders = [None, inputs.ring_order(world, rank, cps)[::-1]] + \
@@ -110,10 +113,11 @@ def test_order_and_mode_invariance_bitexact(gpu):
         w.close()
 
 
-def test_gather_and_flags_bitexact(gpu):
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_gather_and_flags_bitexact(gpu, producer):
     world, rank, ms, cr, k, n = 5, 3, 96, 16, 256, 128
     shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=41)
-    w = AgWorkload(world, rank, shards, b, chunk_rows=cr)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, producer=producer)
     try:
         for _ in range(3):
             w.run("overlap", order=inputs.seeded_order(world, rank, ms // cr, 8))
@@ -130,10 +134,11 @@ def test_gather_and_flags_bitexact(gpu):
         w.close()
 
 
-def test_trace_each_tile_once_and_flags_seen(gpu):
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_trace_each_tile_once_and_flags_seen(gpu, producer):
     world, rank, ms, cr, k, n = 4, 0, 128, 32, 256, 256
     shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=51)
-    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, tile=(64, 64))
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, tile=(64, 64), producer=producer)
     try:
         tiles = (world * ms // 64) * (n // 64)
         buf = torch.zeros(tiles * 8, dtype=torch.int32, device="cuda")
@@ -184,11 +189,12 @@ def test_withheld_chunks_time_out_then_recover(gpu):
         w.close()
 
 
-def test_stale_epoch_is_not_accepted(gpu):
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_stale_epoch_is_not_accepted(gpu, producer):
     """A flag holding the previous epoch does not satisfy the current call's wait."""
     world, rank, ms, cr, k, n = 2, 1, 64, 64, 128, 128
     shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=71)
-    w = AgWorkload(world, rank, shards, b, chunk_rows=cr)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, producer=producer)
     try:
         w.run("copy_only")                      # flags = 1
         B.agg_ctx_set_timeout_us(w.ctx, 20000)
@@ -202,10 +208,11 @@ def test_stale_epoch_is_not_accepted(gpu):
         w.close()
 
 
-def test_epoch_wraps_and_stays_correct(gpu):
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_epoch_wraps_and_stays_correct(gpu, producer):
     world, rank, ms, cr, k, n = 3, 0, 64, 32, 128, 64
     shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=81)
-    w = AgWorkload(world, rank, shards, b, chunk_rows=cr)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, producer=producer)
     try:
         B.agg_ctx_set_epoch(w.ctx, 0xFFFFFFFC)
         ref = _oracle_c(shards, b, "bf16", 1, 1)
@@ -223,10 +230,11 @@ def test_epoch_wraps_and_stays_correct(gpu):
         w.close()
 
 
-def test_host_delays(gpu):
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_host_delays(gpu, producer):
     world, rank, ms, cr, k, n = 4, 0, 128, 32, 512, 256
     shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=91)
-    w = AgWorkload(world, rank, shards, b, chunk_rows=cr)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, producer=producer)
     try:
         nrem = (world - 1) * ms // cr
         w.run("overlap", delay_us=inputs.delays_us(nrem, 5, 200))
@@ -236,10 +244,11 @@ def test_host_delays(gpu):
         w.close()
 
 
-def test_degenerate_sizes(gpu):
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_degenerate_sizes(gpu, producer):
     # world 1: a plain GEMM, nothing to gather
     shards, b, _, _ = small_ag_data(1, 100, 64, 72, "bf16", seed=3)
-    w = AgWorkload(1, 0, shards, b, chunk_rows=10)
+    w = AgWorkload(1, 0, shards, b, chunk_rows=10, producer=producer)
     try:
         w.run("overlap")
         assert w.status() == (0, -1)
@@ -249,7 +258,7 @@ def test_degenerate_sizes(gpu):
     # k = 0: C is zero
     shards = [torch.zeros(16, 0, dtype=torch.bfloat16) for _ in range(2)]
     b = torch.zeros(0, 32, dtype=torch.bfloat16)
-    w = AgWorkload(2, 0, shards, b, chunk_rows=8)
+    w = AgWorkload(2, 0, shards, b, chunk_rows=8, producer=producer)
     try:
         w.c.fill_(1.0)
         w.run("overlap")
@@ -280,13 +289,40 @@ def test_put_signal_primitive(gpu):
 def test_copy_stream_counts(gpu, streams):
     world, rank, ms, cr, k, n = 8, 6, 64, 16, 256, 128
     shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=95)
-    w = AgWorkload(world, rank, shards, b, chunk_rows=cr)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, producer="sdma")
     try:
         B.agg_ctx_set_copy_streams(w.ctx, streams)
         w.run("overlap", order=inputs.seeded_order(world, rank, ms // cr, streams))
         assert w.status() == (0, -1)
         assert_close(to_f64(w.c), _oracle_c(shards, b, "bf16", 1, 1), BF16_TOL, "C")
         assert np.array_equal(raw(w.gather), O.gather_ref([raw(s) for s in shards]))
+    finally:
+        w.close()
+
+
+@pytest.mark.parametrize("copy_wgs,piece_kib", [(1, 1), (3, 2), (0, 3), (0, 1024)])
+@pytest.mark.parametrize("mode", ["overlap", "serial", "copy_only"])
+def test_cu_producer_pieces_and_workgroups(gpu, copy_wgs, piece_kib, mode):
+    """In-kernel producer: chunks cut into many pieces, copied by one, a few or every workgroup;
+    the gather buffer and flags are bit-exact and C matches the oracle."""
+    world, rank, ms, cr, k, n = 4, 1, 96, 24, 264, 136      # chunk = 24 x 528 B (not a piece multiple)
+    shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=97)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, tile=(64, 64), producer="cu")
+    try:
+        B.agg_ctx_set_producer(w.ctx, "cu", copy_wgs, piece_kib)
+        order = inputs.seeded_order(world, rank, ms // cr, 5)
+        for _ in range(2):
+            w.c.zero_()
+            w.run(mode, order=order)
+        assert w.status() == (0, -1)
+        e = B.agg_ctx_epoch(w.ctx)
+        assert np.array_equal(raw(w.gather), O.gather_ref([raw(s) for s in shards]))
+        flags = w.flags.cpu().numpy().astype(np.uint32)
+        cps = ms // cr
+        for c in range(world * cps):
+            assert flags[c] == (0 if c // cps == rank else e), c
+        if mode != "copy_only":
+            assert_close(to_f64(w.c), _oracle_c(shards, b, "bf16", 1, 1), BF16_TOL, "C")
     finally:
         w.close()
 

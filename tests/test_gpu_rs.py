@@ -19,6 +19,7 @@ from helpers import BF16_TOL, assert_close, raw, to_f64
 pytestmark = pytest.mark.gpu
 
 TILES = [(256, 256), (256, 224), (128, 128), (128, 64), (64, 64)]
+PRODUCERS = ["cu", "sdma"]
 
 
 def _data(world, m, k, n, seed, kind="normal"):
@@ -40,10 +41,11 @@ def _ref(w, a, b, peers):
 
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("mode", ["overlap", "serial"])
-def test_ragged_vs_oracle(gpu, tile, mode):
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_ragged_vs_oracle(gpu, tile, mode, producer):
     world, rank, m, k, n, cr = 3, 1, 3 * 200, 328, 264, 40
     a, b, peers = _data(world, m, k, n, seed=7)
-    w = RsWorkload(world, rank, a, b, peers, cr, tile=tile)
+    w = RsWorkload(world, rank, a, b, peers, cr, tile=tile, producer=producer)
     try:
         w.run(mode, order=inputs.seeded_order(world, rank, 200 // cr, 5))
         assert w.status() == (0, -1)
@@ -69,10 +71,11 @@ def test_integer_inputs_bitexact(gpu, tile):
         w.close()
 
 
-def test_order_invariance_and_bookkeeping(gpu):
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_order_invariance_and_bookkeeping(gpu, producer):
     world, rank, m, k, n, cr = 8, 5, 8 * 64, 256, 256, 16
     a, b, peers = _data(world, m, k, n, seed=27)
-    w = RsWorkload(world, rank, a, b, peers, cr, tile=(64, 64))
+    w = RsWorkload(world, rank, a, b, peers, cr, tile=(64, 64), producer=producer)
     try:
         cpb = (m // world) // cr
         outs, sends = [], []
@@ -103,9 +106,10 @@ def test_order_invariance_and_bookkeeping(gpu):
         w.close()
 
 
-def test_world_one_and_k_zero(gpu):
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_world_one_and_k_zero(gpu, producer):
     a, b, peers = _data(1, 96, 64, 32, seed=37)
-    w = RsWorkload(1, 0, a, b, peers, 32)
+    w = RsWorkload(1, 0, a, b, peers, 32, producer=producer)
     try:
         w.run("overlap")
         assert w.status() == (0, -1)
@@ -116,7 +120,7 @@ def test_world_one_and_k_zero(gpu):
     a = torch.zeros(64, 0, dtype=torch.bfloat16)
     b = torch.zeros(0, 32, dtype=torch.bfloat16)
     peers = inputs.draw({"kind": "normal", "std": 1.0}, (2, 32, 32), "f32", 3)[0]
-    w = RsWorkload(2, 1, a, b, peers, 16)
+    w = RsWorkload(2, 1, a, b, peers, 16, producer=producer)
     try:
         w.run("overlap")
         assert w.status() == (0, -1)
