@@ -91,7 +91,7 @@ struct agg_ctx {
   uint32_t* bound[kFlagSlots] = {nullptr, nullptr, nullptr};
   size_t bound_words[kFlagSlots] = {0, 0, 0};
   int producer = AGG_PRODUCER_CU;
-  int copy_wgs = 0;                          // 0: every workgroup takes copy jobs first
+  int copy_wgs = 0;                          // 0: half of the grid takes copy jobs first
   int64_t piece_bytes = kDefaultPieceBytes;
   // arrival order + cumulative delays as uploaded to scratch (kScrOrder / kScrDelay)
   std::vector<uint32_t> up_order, up_delay;
@@ -257,14 +257,16 @@ int schedule(agg_ctx* ctx, int mode, hipStream_t s, hipStream_t us,
   return AGG_OK;
 }
 
-// Enqueue the consumer kernel on ctx->ks, bracketed by a timing event pair when timing is on.
+// Enqueue the consumer kernel (on `ls`, ctx->ks unless given), bracketed by a timing event
+// pair on the same stream when timing is on.
 template <typename F>
-int timed_launch(agg_ctx* ctx, F launch) {
+int timed_launch(agg_ctx* ctx, F launch, hipStream_t ls = nullptr) {
+  if (!ls) ls = ctx->ks;
   const int slot = int(ctx->launches % kTimingRing);
-  if (ctx->timing) HIP_TRY(hipEventRecord(ctx->ev_t0[slot], ctx->ks));
+  if (ctx->timing) HIP_TRY(hipEventRecord(ctx->ev_t0[slot], ls));
   HIP_TRY(launch());
   if (ctx->timing) {
-    HIP_TRY(hipEventRecord(ctx->ev_t1[slot], ctx->ks));
+    HIP_TRY(hipEventRecord(ctx->ev_t1[slot], ls));
     ++ctx->launches;
   }
   return AGG_OK;
@@ -328,7 +330,8 @@ void fill_copies(agg_ctx* ctx, GemmArgs& g, const ChunkCopy& cc, uint32_t* flags
   if (g.piece_bytes == 0) g.piece_bytes = 16;   // empty chunks (k = 0): one empty piece each
   g.copy_jobs = uint32_t(n_order) * uint32_t(g.pieces);
   g.copy_cps = cc.cps;
-  g.copy_wgs = ctx->copy_wgs > 0 ? std::min(ctx->copy_wgs, grid) : grid;
+  // default: half of the grid copies, the other half starts on the local shard's tiles
+  g.copy_wgs = ctx->copy_wgs > 0 ? std::min(ctx->copy_wgs, grid) : std::max(1, grid / 2);
   g.copy_delays = delays ? 1 : 0;
 }
 
@@ -341,9 +344,9 @@ void attach_trace(agg_ctx* ctx, GemmArgs& g, int64_t tiles) {
 
 // One launch of the persistent kernel under the CU producer: `copies` adds the copy jobs,
 // `tiles_on` keeps the GEMM tiles (without them: a copy-only grid of one workgroup per CU).
-int launch_cu(agg_ctx* ctx, const GemmArgs& g, TileShape ts, int dtype, int epi, int grid,
-              const ChunkCopy& cc, uint32_t* flags, size_t n_order, bool delays, int world,
-              uint32_t epoch, bool copies, bool tiles_on, bool timed) {
+int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int dtype, int epi,
+              int grid, const ChunkCopy& cc, uint32_t* flags, size_t n_order, bool delays,
+              int world, uint32_t epoch, bool copies, bool tiles_on, bool timed) {
   GemmArgs h = g;
   int gr = grid;
   if (!tiles_on) {
@@ -363,26 +366,25 @@ int launch_cu(agg_ctx* ctx, const GemmArgs& g, TileShape ts, int dtype, int epi,
   } else {
     h.copy_jobs = 0;
   }
-  auto go = [&]() { return launch_gemm(h, ts.bm, ts.bn, dtype, epi, gr, ctx->ks); };
-  if (timed) return timed_launch(ctx, go);
+  auto go = [&]() { return launch_gemm(h, ts.bm, ts.bn, dtype, epi, gr, ls); };
+  if (timed) return timed_launch(ctx, go, ls);
   HIP_TRY(go());
   return AGG_OK;
 }
 
-// Stream choreography under the CU producer, everything on ctx->ks:
-//   OVERLAP:   stream -> ks; one launch (copy jobs, then tiles); ks -> stream
-//   SERIAL:    stream -> ks; copy-only launch; GEMM launch; ks -> stream
-//   GEMM_ONLY: stream -> ks; GEMM launch; ks -> stream
-//   COPY_ONLY: stream -> ks; copy-only launch; ks -> stream
-// A non-NULL user copy stream is joined as in schedule(). `launch(copies, tiles, timed)`.
+// Stream choreography under the CU producer. Nothing runs beside the kernel, so it goes on the
+// caller's stream itself (no fork, no join, no second hardware queue):
+//   OVERLAP:   one launch (copy jobs, then tiles)
+//   SERIAL:    copy-only launch; GEMM launch
+//   GEMM_ONLY: GEMM launch
+//   COPY_ONLY: copy-only launch
+// A non-NULL user copy stream is joined around the launches. `launch(copies, tiles, timed)`.
 template <typename Launch>
 int schedule_cu(agg_ctx* ctx, int mode, hipStream_t s, hipStream_t us, bool kernel, bool chunks,
                 Launch launch) {
-  HIP_TRY(hipEventRecord(ctx->ev_fork, s));
-  HIP_TRY(hipStreamWaitEvent(ctx->ks, ctx->ev_fork, 0));
   if (chunks && us) {
     HIP_TRY(hipEventRecord(ctx->ev_user, us));
-    HIP_TRY(hipStreamWaitEvent(ctx->ks, ctx->ev_user, 0));
+    HIP_TRY(hipStreamWaitEvent(s, ctx->ev_user, 0));
   }
   int rc = AGG_OK;
   if (mode == AGG_OVERLAP) {
@@ -396,9 +398,10 @@ int schedule_cu(agg_ctx* ctx, int mode, hipStream_t s, hipStream_t us, bool kern
     rc = launch(true, false, true);
   }
   if (rc != AGG_OK) return rc;
-  HIP_TRY(hipEventRecord(ctx->ev_kernel, ctx->ks));
-  HIP_TRY(hipStreamWaitEvent(s, ctx->ev_kernel, 0));
-  if (chunks && us) HIP_TRY(hipStreamWaitEvent(us, ctx->ev_kernel, 0));
+  if (chunks && us) {
+    HIP_TRY(hipEventRecord(ctx->ev_kernel, s));
+    HIP_TRY(hipStreamWaitEvent(us, ctx->ev_kernel, 0));
+  }
   return AGG_OK;
 }
 
@@ -727,8 +730,9 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
       if (int rc = upload_schedule(ctx, s, ord, delay_us)) return rc;
     return schedule_cu(ctx, mode, s, S(copy_stream), kernel, chunks,
                        [&](bool copies, bool tiles_on, bool timed) {
-                         return launch_cu(ctx, g, ts, dtype, kEpiAllGather, grid, cc, flags, ord.size(),
-                                          delay_us != nullptr, world, epoch, copies, tiles_on, timed);
+                         return launch_cu(ctx, s, g, ts, dtype, kEpiAllGather, grid, cc, flags,
+                                          ord.size(), delay_us != nullptr, world, epoch, copies,
+                                          tiles_on, timed);
                        });
   }
   auto launch = [&]() -> int {
@@ -821,9 +825,9 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
       if (int rc = upload_schedule(ctx, s, ord, delay_us)) return rc;
     return schedule_cu(ctx, mode, s, S(copy_stream), kernel, chunks,
                        [&](bool copies, bool tiles_on, bool timed) {
-                         return launch_cu(ctx, g, ts, AGG_BF16, kEpiReduceScatter, grid, cc, flags,
-                                          ord.size(), delay_us != nullptr, world, epoch, copies,
-                                          tiles_on, timed);
+                         return launch_cu(ctx, s, g, ts, AGG_BF16, kEpiReduceScatter, grid, cc,
+                                          flags, ord.size(), delay_us != nullptr, world, epoch,
+                                          copies, tiles_on, timed);
                        });
   }
   auto launch = [&]() -> int {

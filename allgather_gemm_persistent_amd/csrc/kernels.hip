@@ -134,12 +134,20 @@ __device__ inline uint32_t bf16_rne(float f) {
   return u >> 16;
 }
 
+// 16-byte store that writes through to memory (system-coherent: sc0 sc1), so that it is visible
+// to every XCD once it completes, without writing back this XCD's whole L2 afterwards.
+__device__ inline void store_through(u32x4* p, const u32x4& v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" :: "v"(p), "v"(v) : "memory");
+}
+
 // Copy `bytes` (a multiple of 16) from src to dst with the whole workgroup: 16-byte vectors,
-// eight in flight per thread. The source (a peer's block) is read once, so its loads are
-// non-temporal; the destination stays cacheable because the GEMM reads it next.
+// sixteen in flight per thread (64 KiB per workgroup, enough to cover HBM latency at the
+// workgroup's share of the bandwidth). The source (a peer's block) is read once, so its loads
+// are non-temporal; the stores write through (store_through). On return every store of the
+// calling thread has completed.
 __device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __restrict__ src,
                                   int64_t bytes, int tid) {
-  constexpr int U = 8;
+  constexpr int U = 16;
   const int64_t n16 = bytes >> 4;
   const u32x4* s = reinterpret_cast<const u32x4*>(src);
   u32x4* d = reinterpret_cast<u32x4*>(dst);
@@ -149,9 +157,10 @@ __device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __re
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(s + i + u * kThreads);
 #pragma unroll
-    for (int u = 0; u < U; ++u) d[i + u * kThreads] = v[u];
+    for (int u = 0; u < U; ++u) store_through(d + i + u * kThreads, v[u]);
   }
-  for (; i < n16; i += kThreads) d[i] = __builtin_nontemporal_load(s + i);
+  for (; i < n16; i += kThreads) store_through(d + i, __builtin_nontemporal_load(s + i));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // The in-kernel producer: take copy jobs until none are left. Job j*pieces + q copies piece q of
@@ -194,8 +203,8 @@ __device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job) {
     const int64_t base = (int64_t)jl * a.chunk_bytes;
     copy_piece(a.sym + ((int64_t)p * a.copy_cps) * a.chunk_bytes + base + lo,
                a.peer[p] + base + lo, hi - lo, tid);
-    // every thread's stores, then one count per piece; the last piece publishes the chunk
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // every thread's stores have reached memory (copy_piece); then one count per piece, and the
+    // last piece of a chunk publishes it
     __syncthreads();
     if (tid == 0) {
       const uint32_t prev = __hip_atomic_fetch_add(a.scratch + kScrPieces + c, 1u, __ATOMIC_ACQ_REL,

@@ -3,7 +3,8 @@
 
 One step is one ag_gemm call in overlap mode on the W=8 bf16 workload (A: 8 shards x 512 rows,
 4096 x 8192; W_local 8192 x 3584; 128-row chunks arriving in ring order): call setup, the
-producer's put + signal of the 28 remote chunks, tile claims in arrival order, flag waits, the
+producer's put + signal of the 28 remote chunks (by default copy jobs inside the persistent
+kernel; --producer sdma uses the copy engines), tile claims in arrival order, flag waits, the
 MFMA main loop and the bf16 epilogue, and the join. Inputs are resident in HBM before timing.
 
 Printed (one JSON line): overlapped TFLOP/s (value), % of the bf16 MFMA peak, the overlap
@@ -39,9 +40,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="workload name (default: the W=8 bf16 one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--modes", default="overlap,gemm_only,copy_only,serial",
+    ap.add_argument("--modes", default="overlap,gemm_only,copy_only,serial,sdma",
                     help="modes to time; the overlapped steps always run (profiling runs use"
-                         " 'overlap' alone so that every consumer-kernel launch is a timed step)")
+                         " 'overlap' alone so that every consumer-kernel launch is a timed step);"
+                         " 'sdma' also times the overlap with the copy-engine producer")
+    ap.add_argument("--producer", default="cu", choices=["cu", "sdma"],
+                    help="producer of the timed steps: copy jobs inside the kernel (cu) or the"
+                         " copy engines (sdma)")
     return ap.parse_args()
 
 
@@ -101,6 +106,7 @@ def main():
                    data["scale_a"], data["scale_b"])
     order = cfg.order()
     peak = PEAK_FP8_TFLOPS if cfg.dtype == "fp8" else PEAK_BF16_TFLOPS
+    B.agg_ctx_set_producer(w.ctx, args.producer)
     try:
         B.agg_ctx_set_timing(w.ctx, True)
         # the timed steps: overlapped calls
@@ -129,6 +135,12 @@ def main():
             t_copy = time_mode(w, "copy_only", order, args.steps, args.warmup)
         if "serial" in modes:
             t_serial = time_mode(w, "serial", order, args.steps, args.warmup)
+        other = {"cu": "sdma", "sdma": "cu"}[args.producer]
+        t_ovl_other = None
+        if other in modes:
+            B.agg_ctx_set_producer(w.ctx, other)
+            t_ovl_other = time_mode(w, "overlap", order, args.steps, args.warmup)
+            B.agg_ctx_set_producer(w.ctx, args.producer)
     finally:
         B.agg_ctx_set_timing(w.ctx, False)
         w.close()
@@ -165,7 +177,11 @@ def main():
                     "t_copy_us": rnd(t_copy), "t_serial_us": rnd(t_serial),
                     "R": rnd(t_ovl / t_gemm, 3) if t_gemm else None, "eta": rnd(eta, 3),
                     "gemm_only_tflops": rnd(flops / (t_gemm * 1e-6) / 1e12) if t_gemm else None,
-                    "gemm_only_kernel_us": rnd(k_gemm_us)},
+                    "gemm_only_kernel_us": rnd(k_gemm_us),
+                    "producer": args.producer,
+                    f"t_ovl_{other}_producer_us": rnd(t_ovl_other),
+                    f"R_{other}_producer": rnd(t_ovl_other / t_gemm, 3)
+                    if (t_ovl_other and t_gemm) else None},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
                      "kernel": "agg::gemm_kernel (overlap launch)",
