@@ -93,9 +93,10 @@ struct agg_ctx {
   int producer = AGG_PRODUCER_CU;
   int copy_wgs = 0;                          // 0: half of the grid takes copy jobs first
   int64_t piece_bytes = kDefaultPieceBytes;
-  // arrival order + cumulative delays as uploaded to scratch (kScrOrder / kScrDelay)
-  std::vector<uint32_t> up_order, up_delay;
-  uint32_t* up_host = nullptr;               // pinned staging, 2 * AGG_MAX_CHUNKS words
+  // tables the kernel reads from scratch, as last uploaded: row tiles in compute order, arrival
+  // order, cumulative delays (kScrRowOrder / kScrOrder / kScrDelay)
+  std::vector<uint32_t> up[3];
+  uint32_t* up_host = nullptr;               // pinned staging for the three tables
   hipEvent_t ev_upload = nullptr;
   bool upload_pending = false;
 };
@@ -282,39 +283,48 @@ void fill_common(agg_ctx* ctx, GemmArgs& g, TileShape ts, int grid) {
   g.timeout_ticks = uint64_t(double(ctx->timeout_us) * ctx->ticks_per_us);
 }
 
-// Put the arrival order (and the cumulative delays, in wall-clock ticks) where the kernel's
-// producer reads them; skipped when they equal what is already there.
-int upload_schedule(agg_ctx* ctx, hipStream_t s, const std::vector<int32_t>& ord,
-                    const uint32_t* delay_us) {
-  std::vector<uint32_t> o(ord.begin(), ord.end()), d;
-  if (delay_us) {
-    d.resize(ord.size());
-    double sum = 0;
-    for (size_t i = 0; i < ord.size(); ++i) {
-      sum += double(delay_us[i]) * ctx->ticks_per_us;
-      d[i] = uint32_t(std::min(sum, 4.0e9));
-    }
+// The tables the kernel reads from scratch: 0 = row tiles in compute order, 1 = arrival order of
+// the remote chunks, 2 = cumulative producer delays in wall-clock ticks.
+constexpr int kTabWords[3] = {AGG_MAX_ROW_TILES, AGG_MAX_CHUNKS, AGG_MAX_CHUNKS};
+constexpr int kTabScratch[3] = {kScrRowOrder, kScrOrder, kScrDelay};
+constexpr int kTabHost[3] = {0, AGG_MAX_ROW_TILES, AGG_MAX_ROW_TILES + AGG_MAX_CHUNKS};
+constexpr int kTabHostWords = AGG_MAX_ROW_TILES + 2 * AGG_MAX_CHUNKS;
+
+// Copy table `t` into scratch on stream `s`, unless scratch already holds exactly `v`. The
+// pinned staging area is reused only after the previous upload has been consumed.
+int upload_table(agg_ctx* ctx, hipStream_t s, int t, const std::vector<uint32_t>& v) {
+  if (v.empty() || v == ctx->up[t]) return AGG_OK;
+  if (v.size() > size_t(kTabWords[t])) return fail(AGG_E_UNSUPPORTED, "table %d: %zu entries exceed %d", t, v.size(), kTabWords[t]);
+  if (!ctx->up_host) HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&ctx->up_host), kTabHostWords * sizeof(uint32_t)));
+  if (ctx->upload_pending) {
+    HIP_TRY(hipEventSynchronize(ctx->ev_upload));
+    ctx->upload_pending = false;
   }
-  const bool same_o = o == ctx->up_order;
-  const bool same_d = d.empty() || d == ctx->up_delay;
-  if (same_o && same_d) return AGG_OK;
-  if (!ctx->up_host) HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&ctx->up_host), 2 * AGG_MAX_CHUNKS * sizeof(uint32_t)));
-  if (ctx->upload_pending) HIP_TRY(hipEventSynchronize(ctx->ev_upload));   // staging still in use
-  if (!same_o) {
-    std::memcpy(ctx->up_host, o.data(), o.size() * sizeof(uint32_t));
-    HIP_TRY(hipMemcpyAsync(ctx->scratch + kScrOrder, ctx->up_host, o.size() * sizeof(uint32_t),
-                           hipMemcpyHostToDevice, s));
-    ctx->up_order = o;
-  }
-  if (!same_d) {
-    std::memcpy(ctx->up_host + AGG_MAX_CHUNKS, d.data(), d.size() * sizeof(uint32_t));
-    HIP_TRY(hipMemcpyAsync(ctx->scratch + kScrDelay, ctx->up_host + AGG_MAX_CHUNKS,
-                           d.size() * sizeof(uint32_t), hipMemcpyHostToDevice, s));
-    ctx->up_delay = d;
-  }
+  std::memcpy(ctx->up_host + kTabHost[t], v.data(), v.size() * sizeof(uint32_t));
+  HIP_TRY(hipMemcpyAsync(ctx->scratch + kTabScratch[t], ctx->up_host + kTabHost[t],
+                         v.size() * sizeof(uint32_t), hipMemcpyHostToDevice, s));
   HIP_TRY(hipEventRecord(ctx->ev_upload, s));
   ctx->upload_pending = true;
+  ctx->up[t] = v;
   return AGG_OK;
+}
+
+int upload_rows(agg_ctx* ctx, hipStream_t s, const std::vector<int32_t>& rows) {
+  return upload_table(ctx, s, 0, std::vector<uint32_t>(rows.begin(), rows.end()));
+}
+
+// Arrival order and cumulative delays (wall-clock ticks) for the CU producer.
+int upload_schedule(agg_ctx* ctx, hipStream_t s, const std::vector<int32_t>& ord,
+                    const uint32_t* delay_us) {
+  if (int rc = upload_table(ctx, s, 1, std::vector<uint32_t>(ord.begin(), ord.end()))) return rc;
+  if (!delay_us) return AGG_OK;
+  std::vector<uint32_t> d(ord.size());
+  double sum = 0;
+  for (size_t i = 0; i < ord.size(); ++i) {
+    sum += double(delay_us[i]) * ctx->ticks_per_us;
+    d[i] = uint32_t(std::min(sum, 4.0e9));
+  }
+  return upload_table(ctx, s, 2, d);
 }
 
 // Copy-job fields of the kernel arguments for the CU producer.
@@ -502,8 +512,7 @@ extern "C" int agg_ctx_reset(agg_ctx* ctx, agg_stream stream) {
   HIP_TRY(launch_fill_u32(ctx->scratch + kScrFailed, 1, 0xFFFFFFFFu, S(stream)));
   HIP_TRY(hipStreamSynchronize(S(stream)));
   ctx->epoch = 0;
-  ctx->up_order.clear();   // the scratch copy of the order and delays is gone too
-  ctx->up_delay.clear();
+  for (auto& t : ctx->up) t.clear();   // the scratch copies of the tables are gone too
   return AGG_OK;
 }
 
@@ -704,7 +713,7 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
   int grid = 1;
   if (kernel) {
     const std::vector<int32_t> rows = ag_row_tile_order(world, rank, m_shard, chunk_rows, ord, ts.bm);
-    for (size_t i = 0; i < rows.size(); ++i) g.row_order[i] = uint16_t(rows[i]);
+    if (int rc = upload_rows(ctx, s, rows)) return rc;
     g.a = static_cast<const uint8_t*>(gather);
     g.b = static_cast<const uint8_t*>(b);
     g.c = static_cast<uint16_t*>(c);
@@ -794,7 +803,7 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
   int grid = 1;
   if (kernel) {
     const std::vector<int32_t> rows = rs_row_tile_order(world, rank, m, chunk_rows, ord, ts.bm);
-    for (size_t i = 0; i < rows.size(); ++i) g.row_order[i] = uint16_t(rows[i]);
+    if (int rc = upload_rows(ctx, s, rows)) return rc;
     g.a = static_cast<const uint8_t*>(a);
     g.b = static_cast<const uint8_t*>(b);
     g.send = send;

@@ -20,7 +20,8 @@ constexpr int kScrRsCount = 64;    // ReduceScatter per-send-chunk completion co
 constexpr int kScrPieces = kScrRsCount + AGG_MAX_CHUNKS;   // per-chunk copied-piece counters
 constexpr int kScrOrder = kScrPieces + AGG_MAX_CHUNKS;     // arrival order (chunk ids)
 constexpr int kScrDelay = kScrOrder + AGG_MAX_CHUNKS;      // cumulative producer delays (ticks)
-constexpr int kScrWords = kScrDelay + AGG_MAX_CHUNKS;
+constexpr int kScrRowOrder = kScrDelay + AGG_MAX_CHUNKS;   // row tiles in compute order
+constexpr int kScrWords = kScrRowOrder + AGG_MAX_ROW_TILES;
 constexpr int kMaxLists = 16;
 
 enum Epilogue { kEpiAllGather = 0, kEpiReduceScatter = 1 };
@@ -49,6 +50,7 @@ struct GemmArgs {
   float scale;              // fp8: scale_a * scale_b; bf16: 1
   uint64_t timeout_ticks;   // in wall-clock (s_memrealtime) ticks
   uint32_t trace_tiles;     // capacity of `trace` in tiles (0 = off)
+  // (the row tiles in compute order are in scratch, kScrRowOrder)
   // in-kernel producer: copy job i*pieces + q moves piece q of the i-th arriving chunk from its
   // peer's block to the symmetric buffer; the job completing a chunk releases its flag
   const uint8_t* peer[AGG_MAX_WORLD];   // per-peer source blocks (emulated peers)
@@ -60,7 +62,6 @@ struct GemmArgs {
   int copy_wgs;                         // workgroups that take copy jobs first (<= grid)
   int copy_cps;                         // chunks per peer block
   int copy_delays;                      // nonzero: honour the cumulative delays in scratch
-  uint16_t row_order[AGG_MAX_ROW_TILES];  // row tiles in compute order
 };
 
 // Launch the persistent kernel instantiated for (bm, bn, dtype, epilogue) with `grid`

@@ -242,7 +242,7 @@ __device__ inline bool claim(const GemmArgs& a, int home, Tile& t) {
     if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
     const uint32_t k = atomicAdd(ctr, 1u);
     if (k < len) {
-      t.row_tile = a.row_order[xr + (int)(k / nx) * Lr];
+      t.row_tile = (int)a.scratch[kScrRowOrder + xr + (int)(k / nx) * Lr];
       t.col_tile = c_lo + (int)(k % nx);
       t.list = x;
       t.pos = (int)k;
