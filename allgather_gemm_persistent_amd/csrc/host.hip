@@ -91,7 +91,7 @@ struct agg_ctx {
   uint32_t* bound[kFlagSlots] = {nullptr, nullptr, nullptr};
   size_t bound_words[kFlagSlots] = {0, 0, 0};
   int producer = AGG_PRODUCER_CU;
-  int copy_wgs = 0;                          // 0: half of the grid takes copy jobs first
+  int copy_wgs = 0;                          // 0: every workgroup takes copy jobs first
   int64_t piece_bytes = kDefaultPieceBytes;
   // tables the kernel reads from scratch, as last uploaded: row tiles in compute order, arrival
   // order, cumulative delays (kScrRowOrder / kScrOrder / kScrDelay)
@@ -340,8 +340,9 @@ void fill_copies(agg_ctx* ctx, GemmArgs& g, const ChunkCopy& cc, uint32_t* flags
   if (g.piece_bytes == 0) g.piece_bytes = 16;   // empty chunks (k = 0): one empty piece each
   g.copy_jobs = uint32_t(n_order) * uint32_t(g.pieces);
   g.copy_cps = cc.cps;
-  // default: half of the grid copies, the other half starts on the local shard's tiles
-  g.copy_wgs = ctx->copy_wgs > 0 ? std::min(ctx->copy_wgs, grid) : std::max(1, grid / 2);
+  // default: every workgroup copies first. A grid of one tile per workgroup finishes at the last
+  // tile's start plus one tile time, and the copy ends soonest with every workgroup on it.
+  g.copy_wgs = ctx->copy_wgs > 0 ? std::min(ctx->copy_wgs, grid) : grid;
   g.copy_delays = delays ? 1 : 0;
 }
 

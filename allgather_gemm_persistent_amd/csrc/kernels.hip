@@ -134,32 +134,60 @@ __device__ inline uint32_t bf16_rne(float f) {
   return u >> 16;
 }
 
-// 16-byte store that writes through to memory (system-coherent: sc0 sc1), so that it is visible
-// to every XCD once it completes, without writing back this XCD's whole L2 afterwards.
-__device__ inline void store_through(u32x4* p, const u32x4& v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" :: "v"(p), "v"(v) : "memory");
-}
+// Cache-policy bits of a buffer store on gfx950: sc0 | sc1 = system coherent, i.e. the store
+// writes through to memory and is visible to every XCD once it completes, without writing back
+// this XCD's whole L2 afterwards.
+constexpr int kStoreSystemCoherent = 1 | 16;
 
-// Copy `bytes` (a multiple of 16) from src to dst with the whole workgroup: 16-byte vectors,
-// sixteen in flight per thread (64 KiB per workgroup, enough to cover HBM latency at the
-// workgroup's share of the bandwidth). The source (a peer's block) is read once, so its loads
-// are non-temporal; the stores write through (store_through). On return every store of the
-// calling thread has completed.
+// Copy `bytes` (a multiple of 16, < 2 GiB) from src to dst with the whole workgroup: 16-byte
+// vectors in groups of sixteen per thread, software-pipelined over two register sets so that
+// the loads of group g+1 are issued before the stores of group g (one counter tracks loads and
+// stores in issue order, so a load wait never waits for the stores issued after it). The
+// source (a peer's block) is read once: non-temporal loads; the stores write through. On return
+// every store of the calling thread has completed.
 __device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __restrict__ src,
                                   int64_t bytes, int tid) {
   constexpr int U = 16;
+  constexpr int64_t kStep = (int64_t)U * kThreads;
   const int64_t n16 = bytes >> 4;
   const u32x4* s = reinterpret_cast<const u32x4*>(src);
-  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, 0, (int)bytes, kBufferFlags);
+  auto put = [&](int64_t e, const u32x4& v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, rd, (int)(e * 16), 0, kStoreSystemCoherent);
+  };
+  auto load = [&](u32x4 (&v)[U], int64_t g) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(s + g + u * kThreads);
+  };
+  auto store = [&](const u32x4 (&v)[U], int64_t g) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) put(g + u * kThreads, v[u]);
+  };
+  // G full groups (the same count for every thread), then a per-vector tail
+  const int64_t G = n16 / kStep;
   int64_t i = tid;
-  for (; i + (U - 1) * kThreads < n16; i += U * kThreads) {
-    u32x4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(s + i + u * kThreads);
-#pragma unroll
-    for (int u = 0; u < U; ++u) store_through(d + i + u * kThreads, v[u]);
+  if (G > 0) {
+    u32x4 va[U], vb[U];
+    load(va, i);
+    int64_t g = 1;
+    for (; g + 1 < G; g += 2) {          // two groups per trip: loads run one group ahead
+      load(vb, i + kStep);
+      store(va, i);
+      load(va, i + 2 * kStep);
+      store(vb, i + kStep);
+      i += 2 * kStep;
+    }
+    if (g < G) {                         // an even count: one more pair, without a look-ahead
+      load(vb, i + kStep);
+      store(va, i);
+      store(vb, i + kStep);
+      i += 2 * kStep;
+    } else {
+      store(va, i);
+      i += kStep;
+    }
   }
-  for (; i < n16; i += kThreads) store_through(d + i, __builtin_nontemporal_load(s + i));
+  for (; i < n16; i += kThreads) put(i, __builtin_nontemporal_load(s + i));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -449,48 +477,71 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       const u32x4 da = buffer_desc(a.a, (uint32_t)(a.M * kbytes));
       const u32x4 db = buffer_desc(a.b, (uint32_t)(a.N * kbytes));
       const uint32_t lds0 = lds_addr(stages) + (uint32_t)wave_u * 1024u;
-      auto issue = [&](int t) {
+      // load j of slice t (j < NI): A rows for j < NA, else B rows
+      auto issue_one = [&](int t, int j) {
         const uint32_t tk = (uint32_t)t * kSliceBytes;
         // past the K end: set the offset's top bit (out of range, reads zero) without a branch
         const uint32_t oob = (uint32_t)((int)(tk + gk - (uint32_t)kbytes) >> 31) ^ 0xFFFFFFFFu;
         const uint32_t kmask = oob & kOutOfRange;
         const uint32_t st = lds0 + (uint32_t)(t & (kStages - 1)) * DSTAGE;
+        lds_dma_load(j < NA ? da : db, st + j * 4096u, (base[j] + tk) | kmask);
+      };
+      auto issue = [&](int t) {
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
-          lds_dma_load(j < NA ? da : db, st + j * 4096u, (base[j] + tk) | kmask);
+        for (int j = 0; j < NI; ++j) issue_one(t, j);
+      };
+      auto load_b1 = [&](int t, int j) {
+        const uint8_t* st = stages + (t & (kStages - 1)) * DSTAGE;
+        return *reinterpret_cast<const u32x4*>(
+            st + lds64_off(BM + wn * WTN + j * 16 + (lane & 15), lane >> 4));
       };
       auto load_b = [&](u32x4 (&fb)[FN], int t) {
-        const uint8_t* st = stages + (t & (kStages - 1)) * DSTAGE;
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          fb[j] = *reinterpret_cast<const u32x4*>(
-              st + lds64_off(BM + wn * WTN + j * 16 + (lane & 15), lane >> 4));
+        for (int j = 0; j < FN; ++j) fb[j] = load_b1(t, j);
       };
       auto load_a = [&](int t, int i) {
         const uint8_t* st = stages + (t & (kStages - 1)) * DSTAGE;
         return *reinterpret_cast<const u32x4*>(
             st + lds64_off(wm * WTM + i * 16 + (lane & 15), lane >> 4));
       };
-      // One K slice t, with its B fragments in fbc and its first A fragment in fa (both
-      // requested earlier). Each row's A fragment is requested one row ahead; before the last
-      // row the waves meet (slice t+1 has landed everywhere, slice t is fully read), slice
-      // t+1's fragments are requested into fbn / fa, and slice t+4 refills slice t's slot.
+      // One K slice t, its B fragments in fbc and its first A fragment in fa (requested during
+      // the previous slice). The first RB rows of MFMAs run while the remaining A fragments of
+      // slice t are requested; then the waves meet (slice t+1 has landed everywhere and every
+      // wave has read all of slice t), and the last FM-RB rows run with the E requests for
+      // later slices spread between their MFMAs: first slice t+1's FN B fragments and its first
+      // A fragment, then the NI loads that refill slice t's slot with slice t+4. Spreading them
+      // keeps the LDS port, the load path and the MFMA pipe busy at the same time instead of
+      // in turn.
+      constexpr int RB = FM / 2;                 // rows before the barrier (FM >= 2)
+      constexpr int S2 = (FM - RB) * FN;         // MFMAs after it
+      constexpr int E = FN + 1 + NI;             // requests spread over them
+      static_assert(FM - RB - 1 <= RB, "the A fragments after the barrier are loaded before it");
       u32x4 fa;
       auto slice = [&](u32x4 (&fbc)[FN], u32x4 (&fbn)[FN], int t) {
+        u32x4 far[FM];
+        far[0] = fa;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          u32x4 fan;
-          if (i + 1 < FM) {
-            fan = load_a(t, i + 1);
-          } else {
-            stage_barrier<2 * NI>();
-            load_b(fbn, t + 1);
-            fan = load_a(t + 1, 0);
+        for (int i = 0; i < RB; ++i) {
+          far[i + 1] = load_a(t, i + 1);
+          if (RB + 1 + i < FM) far[RB + 1 + i] = load_a(t, RB + 1 + i);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) mfma_bf16(acc[i][j], fbc[j], far[i]);
+        }
+        stage_barrier<2 * NI>();
+#pragma unroll
+        for (int i = RB; i < FM; ++i) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            mfma_bf16(acc[i][j], fbc[j], far[i]);
+            const int q = (i - RB) * FN + j;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              if (e * S2 / E != q) continue;          // request e goes after MFMA slot e*S2/E
+              if (e < FN) fbn[e] = load_b1(t + 1, e);
+              else if (e == FN) fa = load_a(t + 1, 0);
+              else issue_one(t + 4, e - FN - 1);
+            }
           }
-#pragma unroll
-          for (int j = 0; j < FN; ++j) mfma_bf16(acc[i][j], fbc[j], fa);
-          if (i + 1 == FM) issue(t + 4);
-          fa = fan;
         }
       };
       const int nk = (int)((kbytes + kSliceBytes - 1) / kSliceBytes);

@@ -124,7 +124,7 @@ enum {
 };
 
 /* Select the producer of later calls. For AGG_PRODUCER_CU, `copy_wgs` workgroups of the
- * persistent grid (0: half of them) first take copy jobs, each moving `piece_kib` KiB of one chunk
+ * persistent grid (0: all of them) first take copy jobs, each moving `piece_kib` KiB of one chunk
  * (0: 256; a chunk is cut into ceil(chunk bytes / piece) pieces), in arrival order, and only then
  * claim tiles; the workgroup that completes a chunk's last piece releases its flag. The other
  * arguments are ignored for AGG_PRODUCER_SDMA. AGG_E_ARG for an unknown kind or a negative
