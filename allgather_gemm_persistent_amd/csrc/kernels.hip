@@ -505,16 +505,18 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
             st + lds64_off(wm * WTM + i * 16 + (lane & 15), lane >> 4));
       };
       // One K slice t, its B fragments in fbc and its first A fragment in fa (requested during
-      // the previous slice). The first RB rows of MFMAs run while the remaining A fragments of
-      // slice t are requested; then the waves meet (slice t+1 has landed everywhere and every
-      // wave has read all of slice t), and the last FM-RB rows run with the E requests for
-      // later slices spread between their MFMAs: first slice t+1's FN B fragments and its first
-      // A fragment, then the NI loads that refill slice t's slot with slice t+4. Spreading them
-      // keeps the LDS port, the load path and the MFMA pipe busy at the same time instead of
-      // in turn.
+      // the previous slice). Slot t%4 is refilled with slice t+4 by NI direct-to-LDS loads, the
+      // first NH of them in the second half of slice t and the rest in the first half of slice
+      // t+1, so that every half slice carries about NI/2 loads between its MFMAs and the load
+      // path never takes a burst. First half of slice t: the remaining A fragments of slice t
+      // are requested row by row, and the loads NH..NI-1 of slice t+3 go between the MFMAs.
+      // Then the waves meet (slice t+1 has landed everywhere; every wave has read all of slice
+      // t), and the second half spreads slice t+1's B fragments and first A fragment, then the
+      // loads 0..NH-1 of slice t+4, between its MFMAs.
       constexpr int RB = FM / 2;                 // rows before the barrier (FM >= 2)
-      constexpr int S2 = (FM - RB) * FN;         // MFMAs after it
-      constexpr int E = FN + 1 + NI;             // requests spread over them
+      constexpr int NH = NI / 2;                 // loads of a slice issued in the earlier half
+      constexpr int S1 = RB * FN, S2 = (FM - RB) * FN;
+      constexpr int E1 = NI - NH, E2 = FN + 1 + NH;
       static_assert(FM - RB - 1 <= RB, "the A fragments after the barrier are loaded before it");
       u32x4 fa;
       auto slice = [&](u32x4 (&fbc)[FN], u32x4 (&fbn)[FN], int t) {
@@ -525,7 +527,13 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
           far[i + 1] = load_a(t, i + 1);
           if (RB + 1 + i < FM) far[RB + 1 + i] = load_a(t, RB + 1 + i);
 #pragma unroll
-          for (int j = 0; j < FN; ++j) mfma_bf16(acc[i][j], fbc[j], far[i]);
+          for (int j = 0; j < FN; ++j) {
+            mfma_bf16(acc[i][j], fbc[j], far[i]);
+            const int q = i * FN + j;
+#pragma unroll
+            for (int e = 0; e < E1; ++e)
+              if (e * S1 / E1 == q) issue_one(t + 3, NH + e);
+          }
         }
         stage_barrier<2 * NI>();
 #pragma unroll
@@ -535,8 +543,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
             mfma_bf16(acc[i][j], fbc[j], far[i]);
             const int q = (i - RB) * FN + j;
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-              if (e * S2 / E != q) continue;          // request e goes after MFMA slot e*S2/E
+            for (int e = 0; e < E2; ++e) {
+              if (e * S2 / E2 != q) continue;         // request e goes after MFMA slot e*S2/E2
               if (e < FN) fbn[e] = load_b1(t + 1, e);
               else if (e == FN) fa = load_a(t + 1, 0);
               else issue_one(t + 4, e - FN - 1);
@@ -551,8 +559,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         issue(0);
         issue(1);
         issue(2);
-        issue(3);
-        stage_barrier<3 * NI>();
+#pragma unroll
+        for (int j = 0; j < NH; ++j) issue_one(3, j);   // slice 0 issues the rest of slice 3
+        stage_barrier<2 * NI + NH>();
         load_b(fb0, 0);
         fa = load_a(0, 0);
         // slices past the K end read zeros: an odd count runs one zero slice
