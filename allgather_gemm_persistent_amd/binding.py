@@ -45,6 +45,7 @@ _SIGNATURES = {
     "agg_ctx_set_timeout_us": [_vp, _c_u64],
     "agg_ctx_set_tile": [_vp, _c_int, _c_int],
     "agg_ctx_set_lists": [_vp, _c_int, _c_int],
+    "agg_ctx_set_split": [_vp, _c_int],
     "agg_ctx_set_producer": [_vp, _c_int, _c_int, _c_int],
     "agg_set_trace": [_vp, _vp, _sz],
     "agg_ctx_set_timing": [_vp, _c_int],
@@ -232,6 +233,10 @@ def agg_ctx_set_producer(ctx, kind="cu", copy_wgs: int = 0, piece_kib: int = 0) 
     """Producer of later calls: "cu" (copy jobs inside the persistent kernel) or "sdma"."""
     _call("agg_ctx_set_producer", ctx, PRODUCERS[kind] if isinstance(kind, str) else int(kind),
           copy_wgs, piece_kib)
+
+
+def agg_ctx_set_split(ctx, ksplit: int = 0) -> None:
+    _call("agg_ctx_set_split", ctx, ksplit)
 
 
 def agg_ctx_set_lists(ctx, lists: int = 8, list_cols: int = 0) -> None:

@@ -61,7 +61,6 @@ constexpr int kMaxCopyStreams = 8;
 constexpr int kDefaultCopyStreams = 4;
 constexpr int kDefaultReservedCus = 32;
 constexpr int kTimingRing = 256;          // launches whose kernel duration is kept
-constexpr int64_t kDefaultPieceBytes = 256 << 10;
 
 enum FlagSlot { kFlagsAg = 0, kFlagsRsRecv = 1, kFlagsRsSend = 2, kFlagSlots = 3 };
 
@@ -90,9 +89,12 @@ struct agg_ctx {
   uint64_t launches = 0;                    // launches recorded since timing was switched on
   uint32_t* bound[kFlagSlots] = {nullptr, nullptr, nullptr};
   size_t bound_words[kFlagSlots] = {0, 0, 0};
+  int force_split = 0;                       // 0: split-K chosen per call
+  float* ws = nullptr;                       // split-K partials (grown on demand)
+  size_t ws_bytes = 0;
   int producer = AGG_PRODUCER_CU;
   int copy_wgs = 0;                          // 0: every workgroup takes copy jobs first
-  int64_t piece_bytes = kDefaultPieceBytes;
+  int64_t piece_bytes = 0;                   // 0: chosen per call
   // tables the kernel reads from scratch, as last uploaded: row tiles in compute order, arrival
   // order, cumulative delays (kScrRowOrder / kScrOrder / kScrDelay)
   std::vector<uint32_t> up[3];
@@ -273,6 +275,38 @@ int timed_launch(agg_ctx* ctx, F launch, hipStream_t ls = nullptr) {
   return AGG_OK;
 }
 
+// The split-K partial buffer, grown to `bytes` when needed (a synchronising reallocation: the
+// previous buffer may still be read by enqueued work).
+int ensure_ws(agg_ctx* ctx, size_t bytes) {
+  if (bytes <= ctx->ws_bytes) return AGG_OK;
+  if (ctx->ws) {
+    HIP_TRY(hipDeviceSynchronize());
+    HIP_TRY(hipFree(ctx->ws));
+    ctx->ws = nullptr;
+    ctx->ws_bytes = 0;
+  }
+  HIP_TRY(hipMalloc(reinterpret_cast<void**>(&ctx->ws), bytes));
+  ctx->ws_bytes = bytes;
+  return AGG_OK;
+}
+
+// K split of one AllGather+GEMM call (the ctx may force one; tiles above 128 x 128 never split).
+KSplit ksplit_for(agg_ctx* ctx, TileShape ts, int dtype, int64_t tiles, int64_t k) {
+  KSplit ks = choose_ksplit(0, dtype, tiles, k, ctx->cus);
+  if (ts.bm * ts.bn > kMaxSplitTileArea) {
+    ks.ksplit = 1;
+    const int64_t kb = k * (dtype == AGG_FP8_E4M3 ? 1 : 2);
+    ks.kps = int(std::max<int64_t>(1, (kb + slice_bytes(dtype) - 1) / slice_bytes(dtype)));
+  } else if (ctx->force_split > 0) {
+    const int64_t kb = k * (dtype == AGG_FP8_E4M3 ? 1 : 2);
+    const int64_t nk = std::max<int64_t>(1, (kb + slice_bytes(dtype) - 1) / slice_bytes(dtype));
+    const int64_t s = std::min<int64_t>(ctx->force_split, nk);
+    ks.kps = int((nk + s - 1) / s);
+    ks.ksplit = int((nk + ks.kps - 1) / ks.kps);
+  }
+  return ks;
+}
+
 void fill_common(agg_ctx* ctx, GemmArgs& g, TileShape ts, int grid) {
   g.scratch = ctx->scratch;
   g.n_lists = std::min(ctx->lists, kMaxLists);
@@ -334,7 +368,12 @@ void fill_copies(agg_ctx* ctx, GemmArgs& g, const ChunkCopy& cc, uint32_t* flags
   g.sym = cc.dst;
   g.put_flags = flags;
   g.chunk_bytes = cc.cr * cc.row_bytes;
-  const int64_t piece = std::max<int64_t>(16, ctx->piece_bytes / 16 * 16);
+  // automatic piece size: the remote bytes spread over the copying workgroups, 16 KiB .. 1 MiB
+  const int copiers = ctx->copy_wgs > 0 ? std::min(ctx->copy_wgs, grid) : grid;
+  const int64_t total = g.chunk_bytes * int64_t(n_order);
+  const int64_t autop = std::min<int64_t>(std::max<int64_t>((total / std::max(copiers, 1) + 16383) / 16384 * 16384,
+                                                            16384), 1 << 20);
+  const int64_t piece = std::max<int64_t>(16, (ctx->piece_bytes > 0 ? ctx->piece_bytes : autop) / 16 * 16);
   g.piece_bytes = std::min<int64_t>(g.chunk_bytes, piece);
   g.pieces = g.piece_bytes > 0 ? int((g.chunk_bytes + g.piece_bytes - 1) / g.piece_bytes) : 1;
   if (g.piece_bytes == 0) g.piece_bytes = 16;   // empty chunks (k = 0): one empty piece each
@@ -368,6 +407,7 @@ int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int
     h.scratch = ctx->scratch;
     h.n_lists = 1;
     h.list_cols = 1;
+    h.ksplit = 1;
     h.epoch = epoch;
     gr = ctx->cus;
   }
@@ -485,6 +525,7 @@ extern "C" int agg_ctx_destroy(agg_ctx* ctx) {
   for (hipEvent_t e : {ctx->ev_fork, ctx->ev_kernel, ctx->ev_user, ctx->ev_upload})
     if (e) step(hipEventDestroy(e), "hipEventDestroy");
   if (ctx->up_host) step(hipHostFree(ctx->up_host), "hipHostFree");
+  if (ctx->ws) step(hipFree(ctx->ws), "hipFree(ws)");
   for (int j = 0; j < kTimingRing; ++j) {
     if (ctx->ev_t0[j]) step(hipEventDestroy(ctx->ev_t0[j]), "hipEventDestroy");
     if (ctx->ev_t1[j]) step(hipEventDestroy(ctx->ev_t1[j]), "hipEventDestroy");
@@ -578,7 +619,15 @@ extern "C" int agg_ctx_set_producer(agg_ctx* ctx, int kind, int copy_wgs, int pi
   if (copy_wgs < 0 || piece_kib < 0) return fail(AGG_E_ARG, "negative copy_wgs or piece_kib");
   ctx->producer = kind;
   ctx->copy_wgs = copy_wgs;
-  ctx->piece_bytes = piece_kib > 0 ? int64_t(piece_kib) << 10 : kDefaultPieceBytes;
+  ctx->piece_bytes = piece_kib > 0 ? int64_t(piece_kib) << 10 : 0;
+  return AGG_OK;
+}
+
+extern "C" int agg_ctx_set_split(agg_ctx* ctx, int ksplit) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (ksplit < 0 || ksplit > kMaxKSplit) return fail(AGG_E_ARG, "ksplit must be in [0, %d]", kMaxKSplit);
+  ctx->force_split = ksplit;
   return AGG_OK;
 }
 
@@ -728,6 +777,18 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
     g.cps = cps;
     g.n_row_tiles = int(rows.size());
     g.n_col_tiles = int((n + ts.bn - 1) / ts.bn);
+    const KSplit ks = ksplit_for(ctx, ts, dtype, int64_t(g.n_row_tiles) * g.n_col_tiles, k);
+    if (ks.ksplit > 1) {
+      if (int64_t(g.n_row_tiles) * g.n_col_tiles > kMaxSplitTiles)
+        return fail(AGG_E_UNSUPPORTED, "split-K over more than %d tiles", kMaxSplitTiles);
+      const size_t ws_bytes = size_t(ks.ksplit) * size_t(m) * size_t(n) * sizeof(float);
+      if (ws_bytes >= (size_t(1) << 31)) return fail(AGG_E_UNSUPPORTED, "split-K partials exceed 2 GiB");
+      if (int rc = ensure_ws(ctx, ws_bytes)) return rc;
+      g.ws = ctx->ws;
+    }
+    g.ksplit = ks.ksplit;
+    g.kps = ks.kps;
+    g.n_col_tiles *= ks.ksplit;
     g.epoch = world > 1 ? epoch : 0;
     g.scale = dtype == AGG_FP8_E4M3 ? scale_a * scale_b : 1.0f;
     tiles = int64_t(g.n_row_tiles) * g.n_col_tiles;
@@ -823,6 +884,8 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
     g.tpb = int((mb + ts.bm - 1) / ts.bm);
     g.n_row_tiles = int(rows.size());
     g.n_col_tiles = int((n + ts.bn - 1) / ts.bn);
+    g.ksplit = 1;
+    g.kps = int(std::max<int64_t>(1, (k * 2 + slice_bytes(AGG_BF16) - 1) / slice_bytes(AGG_BF16)));
     g.epoch = world > 1 ? epoch : 0;
     g.scale = 1.0f;
     tiles = int64_t(g.n_row_tiles) * g.n_col_tiles;

@@ -21,7 +21,8 @@ constexpr int kScrPieces = kScrRsCount + AGG_MAX_CHUNKS;   // per-chunk copied-p
 constexpr int kScrOrder = kScrPieces + AGG_MAX_CHUNKS;     // arrival order (chunk ids)
 constexpr int kScrDelay = kScrOrder + AGG_MAX_CHUNKS;      // cumulative producer delays (ticks)
 constexpr int kScrRowOrder = kScrDelay + AGG_MAX_CHUNKS;   // row tiles in compute order
-constexpr int kScrWords = kScrRowOrder + AGG_MAX_ROW_TILES;
+constexpr int kScrSplit = kScrRowOrder + AGG_MAX_ROW_TILES; // split-K: parts done per tile
+constexpr int kScrWords = kScrSplit + 1024;
 constexpr int kMaxLists = 16;
 
 enum Epilogue { kEpiAllGather = 0, kEpiReduceScatter = 1 };
@@ -42,7 +43,10 @@ struct GemmArgs {
   int world, rank;
   int chunk_rows, cps;      // rows per chunk, chunks per shard (AG) / per block (RS)
   int n_row_tiles;          // AG: ceil(M/BM); RS: world * tiles_per_block
-  int n_col_tiles;          // ceil(N/BN)
+  int n_col_tiles;          // ceil(N/BN) * ksplit: claimable columns (each tile's K parts)
+  int ksplit;               // K parts per tile (1: no split); part p covers K slices
+  int kps;                  //   [p*kps, min((p+1)*kps, slices)) of the main loop's slices
+  float* ws;                // split-K partial products, ksplit x M x N fp32
   int tpb;                  // RS: row tiles per block
   int n_lists;              // claim lists (one per XCD)
   int list_cols;            // lists split as (n_lists / list_cols) row groups x list_cols column blocks

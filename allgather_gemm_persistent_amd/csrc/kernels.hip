@@ -231,14 +231,15 @@ __device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job) {
     const int64_t base = (int64_t)jl * a.chunk_bytes;
     copy_piece(a.sym + ((int64_t)p * a.copy_cps) * a.chunk_bytes + base + lo,
                a.peer[p] + base + lo, hi - lo, tid);
-    // every thread's stores have reached memory (copy_piece); then one count per piece, and the
-    // last piece of a chunk publishes it
+    // every thread's write-through stores have completed in memory (copy_piece waited for
+    // them), so the count and the flag need no cache maintenance: a relaxed count per piece,
+    // and the piece that completes the chunk writes its flag (a system-coherent store)
     __syncthreads();
     if (tid == 0) {
-      const uint32_t prev = __hip_atomic_fetch_add(a.scratch + kScrPieces + c, 1u, __ATOMIC_ACQ_REL,
+      const uint32_t prev = __hip_atomic_fetch_add(a.scratch + kScrPieces + c, 1u, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
       if (prev + 1 == pieces)
-        __hip_atomic_store(a.put_flags + c, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(a.put_flags + c, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
 }
@@ -373,6 +374,7 @@ __device__ bool wait_chunks(const GemmArgs& a, int64_t lo, int64_t hi, int block
 template <int BM, int BN, int DT, int EPI>
 __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   constexpr bool FP8 = (DT == AGG_FP8_E4M3);
+  constexpr bool kSplitTiles = BM * BN <= 128 * 128;
   constexpr int WTM = BM / 2, WTN = BN / 2;       // wave tile
   constexpr int FM = WTM / 16, FN = WTN / 16;     // 16x16 MFMA blocks per wave
   constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
@@ -411,14 +413,21 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     // uniform for the compiler too (see produce_chunks)
     const int row_tile = __builtin_amdgcn_readfirstlane(s_tile[0]);
     if (row_tile < 0) break;
-    const int col_tile = __builtin_amdgcn_readfirstlane(s_tile[1]);
+    const int vcol = __builtin_amdgcn_readfirstlane(s_tile[1]);
+    const int col_tile = vcol / a.ksplit, part = vcol - col_tile * a.ksplit;
     int64_t lo, hi;
     int block, tib;
     tile_rows<BM, EPI>(a, row_tile, lo, hi, block, tib);
     const int64_t n0 = (int64_t)col_tile * BN;
+    // this part's K slices [t_lo, t_hi) and the K byte where its loads stop (zeros past it)
+    constexpr int kSlice = FP8 ? kRowBytes : kSliceBytes;
+    const int nk_all = (int)((kbytes + kSlice - 1) / kSlice);
+    const int t_lo = part * a.kps;
+    const int t_hi = t_lo + a.kps < nk_all ? t_lo + a.kps : nk_all;
+    const uint32_t kend = (uint32_t)((int64_t)t_hi * kSlice < kbytes ? (int64_t)t_hi * kSlice : kbytes);
     uint32_t* trec = nullptr;
-    if (a.trace && (uint32_t)(row_tile * a.n_col_tiles + col_tile) < a.trace_tiles)
-      trec = a.trace + 8 * ((int64_t)row_tile * a.n_col_tiles + col_tile);
+    if (a.trace && (uint32_t)(row_tile * a.n_col_tiles + vcol) < a.trace_tiles)
+      trec = a.trace + 8 * ((int64_t)row_tile * a.n_col_tiles + vcol);
     if (tid == 0 && trec) {
       trec[0] = (uint32_t)s_tile[2]; trec[1] = (uint32_t)s_tile[3]; trec[2] = (uint32_t)xcc_id();
       trec[5] = wall_ticks();
@@ -481,7 +490,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       auto issue_one = [&](int t, int j) {
         const uint32_t tk = (uint32_t)t * kSliceBytes;
         // past the K end: set the offset's top bit (out of range, reads zero) without a branch
-        const uint32_t oob = (uint32_t)((int)(tk + gk - (uint32_t)kbytes) >> 31) ^ 0xFFFFFFFFu;
+        const uint32_t oob = (uint32_t)((int)(tk + gk - kend) >> 31) ^ 0xFFFFFFFFu;
         const uint32_t kmask = oob & kOutOfRange;
         const uint32_t st = lds0 + (uint32_t)(t & (kStages - 1)) * DSTAGE;
         lds_dma_load(j < NA ? da : db, st + j * 4096u, (base[j] + tk) | kmask);
@@ -552,20 +561,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
           }
         }
       };
-      const int nk = (int)((kbytes + kSliceBytes - 1) / kSliceBytes);
-      if (nk > 0) {
+      if (t_hi > t_lo) {
         u32x4 fb0[FN], fb1[FN];
         acc_settle(acc);
-        issue(0);
-        issue(1);
-        issue(2);
+        issue(t_lo);
+        issue(t_lo + 1);
+        issue(t_lo + 2);
 #pragma unroll
-        for (int j = 0; j < NH; ++j) issue_one(3, j);   // slice 0 issues the rest of slice 3
+        for (int j = 0; j < NH; ++j) issue_one(t_lo + 3, j);   // the first slice issues the rest
         stage_barrier<2 * NI + NH>();
-        load_b(fb0, 0);
-        fa = load_a(0, 0);
-        // slices past the K end read zeros: an odd count runs one zero slice
-        for (int t = 0; t < nk; t += 2) {
+        load_b(fb0, t_lo);
+        fa = load_a(t_lo, 0);
+        // slices past the part's end read zeros: an odd count runs one zero slice
+        for (int t = t_lo; t < t_hi; t += 2) {
           slice(fb0, fb1, t);
           slice(fb1, fb0, t + 1);
         }
@@ -576,7 +584,6 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       }
     } else {
       // ---- fp8: 128-byte K slices staged through registers, two LDS stages
-      const int nk = (int)((kbytes + kRowBytes - 1) / kRowBytes);
       u32x4 ra[A_LOADS], rb[B_LOADS];
       auto gload = [&](int kt) {
         const uint32_t kb = (uint32_t)kt * kRowBytes;
@@ -584,14 +591,14 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         for (int i = 0; i < A_LOADS; ++i) {
           const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
           const uint32_t kbyte = kb + ch * 16;
-          const uint32_t off = kbyte < (uint32_t)kbytes ? (uint32_t)(lo + row) * (uint32_t)kbytes + kbyte : kOutOfRange;
+          const uint32_t off = kbyte < kend ? (uint32_t)(lo + row) * (uint32_t)kbytes + kbyte : kOutOfRange;
           ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0));
         }
 #pragma unroll
         for (int i = 0; i < B_LOADS; ++i) {
           const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
           const uint32_t kbyte = kb + ch * 16;
-          const uint32_t off = kbyte < (uint32_t)kbytes ? (uint32_t)(n0 + row) * (uint32_t)kbytes + kbyte : kOutOfRange;
+          const uint32_t off = kbyte < kend ? (uint32_t)(n0 + row) * (uint32_t)kbytes + kbyte : kOutOfRange;
           rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, off, 0, 0));
         }
       };
@@ -609,14 +616,14 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
           *reinterpret_cast<u32x4*>(Bs + lds_off(row, ch)) = rb[i];
         }
       };
-      if (nk > 0) {
-        gload(0);
+      if (t_hi > t_lo) {
+        gload(t_lo);
         sstore(0);
         __syncthreads();
       }
-      for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
+      for (int kt = t_lo; kt < t_hi; ++kt) {
+        const int buf = (kt - t_lo) & 1;
+        if (kt + 1 < t_hi) gload(kt + 1);
         const uint8_t* As = smem + buf * STAGE;
         const uint8_t* Bs = As + A_BYTES;
         // B fragments of the slice stay in registers; A fragments stream one row block at a time
@@ -649,7 +656,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
                 opa, opb, acc[i][j], 0, 0, 0, 127, 0, 127);
           }
         }
-        if (kt + 1 < nk) sstore(buf ^ 1);
+        if (kt + 1 < t_hi) sstore(buf ^ 1);
         __syncthreads();
       }
     }
@@ -658,20 +665,76 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     const int mrow = lane & 15;          // row within a 16x16 block
     const int ncol = (lane >> 4) * 4;    // first of 4 consecutive columns
     if (EPI == kEpiAllGather) {
+      bool finish = true;
+      // split-K exists for tiles up to 128 x 128 only (the host never splits a larger one): the
+      // partial and reduction code would cost the big tiles registers in their main loop
+      if (kSplitTiles && a.ksplit > 1) {
+        // split-K: every part writes its fp32 partial (write-through) and counts itself in; the
+        // part that arrives last reads all parts back and sums them in part order (so the sum
+        // does not depend on which part is last), then converts and stores the tile. The
+        // partial loads are system-coherent: a stale line of an earlier launch must not be read.
+        const int64_t plane = a.M * a.N;
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            a.ws, 0, (int)(a.ksplit * plane * 4), kBufferFlags);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int64_t m = lo + wm * WTM + i * 16 + mrow;
-        if (m >= hi) continue;
+        for (int i = 0; i < FM; ++i) {
+          const int64_t m = lo + wm * WTM + i * 16 + mrow;
+          if (m >= hi) continue;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int64_t n = n0 + wn * WTN + j * 16 + ncol;
-          if (n >= a.N) continue;
-          f32x4 v = acc[i][j];
-          if (FP8) v *= a.scale;
-          u32x2 packed;
-          packed[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-          packed[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-          *reinterpret_cast<u32x2*>(a.c + m * a.N + n) = packed;
+          for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + wn * WTN + j * 16 + ncol;
+            if (n >= a.N) continue;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rw,
+                                                   (int)(((int64_t)part * plane + m * a.N + n) * 4),
+                                                   0, kStoreSystemCoherent);
+          }
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const int tile_id = row_tile * (a.n_col_tiles / a.ksplit) + col_tile;
+        if (tid == 0)
+          s_ok = (__hip_atomic_fetch_add(a.scratch + kScrSplit + tile_id, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)a.ksplit - 1);
+        __syncthreads();
+        finish = __builtin_amdgcn_readfirstlane(s_ok) != 0;
+        if (finish) {
+          // one part at a time, every (i, j) of the part in flight together
+          for (int q = 0; q < a.ksplit; ++q) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+              const int64_t m = lo + wm * WTM + i * 16 + mrow;
+#pragma unroll
+              for (int j = 0; j < FN; ++j) {
+                const int64_t n = n0 + wn * WTN + j * 16 + ncol;
+                // rows / columns past the end read zeros (offset past the buffer)
+                const int off = (m < hi && n < a.N) ? (int)(((int64_t)q * plane + m * a.N + n) * 4)
+                                                     : (int)kOutOfRange;
+                const f32x4 v = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kStoreSystemCoherent));
+                acc[i][j] = q == 0 ? v : acc[i][j] + v;
+              }
+            }
+          }
+          if (tid == 0)
+            __hip_atomic_store(a.scratch + kScrSplit + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      if (finish) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int64_t m = lo + wm * WTM + i * 16 + mrow;
+          if (m >= hi) continue;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + wn * WTN + j * 16 + ncol;
+            if (n >= a.N) continue;
+            f32x4 v = acc[i][j];
+            if (FP8) v *= a.scale;
+            u32x2 packed;
+            packed[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+            packed[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+            *reinterpret_cast<u32x2*>(a.c + m * a.N + n) = packed;
+          }
         }
       }
     } else {

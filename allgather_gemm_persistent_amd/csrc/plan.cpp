@@ -60,10 +60,25 @@ int choose_list_cols(int lists, int n_row_tiles, int n_col_tiles, int bm, int bn
   return best;
 }
 
+int slice_bytes(int dtype) { return dtype == AGG_FP8_E4M3 ? 128 : 64; }
+
+KSplit choose_ksplit(int op, int dtype, int64_t tiles, int64_t k, int units) {
+  KSplit r{1, 0};
+  const int64_t kbytes = k * (dtype == AGG_FP8_E4M3 ? 1 : 2);
+  const int64_t nk = (kbytes + slice_bytes(dtype) - 1) / slice_bytes(dtype);
+  r.kps = int(std::max<int64_t>(nk, 1));
+  // split only an AllGather+GEMM whose tiles leave more than half the units idle, and only so
+  // far that every part keeps at least 16 slices
+  if (op != 0 || tiles <= 0 || tiles * 2 > units || tiles > kMaxSplitTiles) return r;
+  int64_t s = std::min<int64_t>({int64_t(units) / tiles, nk / 16, int64_t(kAutoKSplit)});
+  if (s < 2) return r;
+  const int64_t kps = (nk + s - 1) / s;
+  r.kps = int(kps);
+  r.ksplit = int((nk + kps - 1) / kps);   // no empty part
+  return r;
+}
+
 TileShape choose_tile(int op, int dtype, int64_t m, int64_t n, int64_t k) {
-  (void)op;
-  (void)dtype;
-  (void)k;
   // Relative MFMA efficiency of each shape (operand bytes per flop fall as the tile grows).
   auto eff = [](const TileShape& s) {
     if (s.bm == 256 && s.bn == 256) return 1.0;
@@ -78,8 +93,12 @@ TileShape choose_tile(int op, int dtype, int64_t m, int64_t n, int64_t k) {
   int64_t best_tiles = 0;
   for (const TileShape& s : tile_shapes()) {
     int64_t tiles = ((m + s.bm - 1) / s.bm) * ((n + s.bn - 1) / s.bn);
-    int64_t waves = std::max<int64_t>(1, (tiles + kUnits - 1) / kUnits);
-    double cost = double(waves) * s.bm * s.bn / eff(s);
+    // a split-K call spreads each tile's K over ksplit workgroups (plus a reduction)
+    const KSplit ks = s.bm * s.bn <= kMaxSplitTileArea ? choose_ksplit(op, dtype, tiles, k, int(kUnits))
+                                                       : KSplit{1, 0};
+    int64_t items = tiles * ks.ksplit;
+    int64_t waves = std::max<int64_t>(1, (items + kUnits - 1) / kUnits);
+    double cost = double(waves) * s.bm * s.bn / eff(s) / ks.ksplit * (ks.ksplit > 1 ? 1.1 : 1.0);
     if (cost < best_cost * (1 - 1e-9) || (std::fabs(cost - best_cost) <= 1e-9 * cost && tiles > best_tiles)) {
       best = s;
       best_cost = cost;

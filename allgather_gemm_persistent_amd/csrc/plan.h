@@ -19,6 +19,22 @@ struct TileShape {
 // Output tile shape for one call. op: 0 = AllGather+GEMM, 1 = GEMM+ReduceScatter.
 TileShape choose_tile(int op, int dtype, int64_t m, int64_t n, int64_t k);
 
+// K slice of the kernel's main loop in bytes: 64 for bf16, 128 for fp8.
+int slice_bytes(int dtype);
+
+// Split-K: with fewer output tiles than half the compute units and a long K, each tile's K
+// range is cut into `ksplit` parts computed by different workgroups (AllGather+GEMM only). The
+// parts hold `kps` K slices each (the last one may hold fewer); every part is non-empty.
+struct KSplit {
+  int ksplit, kps;
+};
+KSplit choose_ksplit(int op, int dtype, int64_t tiles, int64_t k, int units);
+// split-K exists for tiles of at most this many elements (128 x 128)
+constexpr int kMaxSplitTileArea = 128 * 128;
+constexpr int kMaxKSplit = 16;      // parts a caller may force
+constexpr int kAutoKSplit = 4;      // parts chosen automatically (the reduction costs a pass per part)
+constexpr int kMaxSplitTiles = 1024;   // tiles of a split-K call (one arrival counter each)
+
 // Split of the claim lists (one per XCD) into list_rows x list_cols: list x takes the row tiles
 // at compute positions x / list_cols, + list_rows, + 2 * list_rows, ... and the column tiles of
 // block x % list_cols. Picks the split whose first wave of tiles on one XCD (`workers` tiles in

@@ -125,7 +125,8 @@ enum {
 
 /* Select the producer of later calls. For AGG_PRODUCER_CU, `copy_wgs` workgroups of the
  * persistent grid (0: all of them) first take copy jobs, each moving `piece_kib` KiB of one chunk
- * (0: 256; a chunk is cut into ceil(chunk bytes / piece) pieces), in arrival order, and only then
+ * (0: the remote bytes divided by the copying workgroups, rounded up to 16 KiB, at most
+ * 1 MiB; a chunk is cut into ceil(chunk bytes / piece) pieces), in arrival order, and only then
  * claim tiles; the workgroup that completes a chunk's last piece releases its flag. The other
  * arguments are ignored for AGG_PRODUCER_SDMA. AGG_E_ARG for an unknown kind or a negative
  * count. */
@@ -139,6 +140,16 @@ int agg_ctx_set_reserved_cus(agg_ctx* ctx, int n);
 /* Force the output tile shape (bm x bn) of later calls; 0, 0 restores the automatic choice.
  * Shapes: 256x256, 256x224, 128x128, 128x64, 64x64; anything else is AGG_E_ARG. */
 int agg_ctx_set_tile(agg_ctx* ctx, int bm, int bn);
+
+/* Split-K of later AllGather+GEMM calls. With few output tiles (fewer than half the CUs) and a
+ * long K, the library cuts each tile's K range into parts computed by different workgroups;
+ * every part writes an fp32 partial into a ctx-owned buffer (ksplit x M x N floats, allocated
+ * and grown by the ctx) and the last part to finish sums the parts in part order, so C does not
+ * depend on which part finishes last. `ksplit` 1..16 forces that many parts (at most one per K
+ * slice) for tiles of up to 128 x 128 (larger tiles are never split), 0 restores the automatic
+ * choice. A chunk wait that times out leaves split-K tile
+ * counters behind: call agg_ctx_reset before the next call. */
+int agg_ctx_set_split(agg_ctx* ctx, int ksplit);
 
 /* Tile-claim lists of later calls. The persistent workgroups claim tiles from `lists` lists
  * (1..16, default 8: one per XCD, a workgroup starting on the list of the XCD it runs on and

@@ -327,6 +327,43 @@ def test_cu_producer_pieces_and_workgroups(gpu, copy_wgs, piece_kib, mode):
         w.close()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("tile", [(128, 128), (128, 64), (64, 64), (256, 224)])
+@pytest.mark.parametrize("ksplit", [2, 3, 16])
+def test_split_k_vs_oracle(gpu, dtype, tile, ksplit):
+    """Split-K: every part's K range (the last one shorter), partials summed in part order;
+    C within tolerance, bit-identical on a second call, and bit-exact on integer inputs. (A
+    256 x 224 tile is never split: the request is ignored and the result must not change.)"""
+    world, rank, ms, cr, n = 2, 1, 96, 32, 200
+    k = 1000 if dtype == "bf16" else 1040          # 32 bf16 slices (last partial) / 9 fp8 slices
+    shards, b, sa, sb = small_ag_data(world, ms, k, n, dtype, seed=101)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, dtype=dtype, scale_a=sa, scale_b=sb,
+                   tile=tile)
+    try:
+        B.agg_ctx_set_split(w.ctx, ksplit)
+        order = inputs.seeded_order(world, rank, ms // cr, 7)
+        w.run("overlap", order=order)
+        first = w.c.clone()
+        w.c.zero_()
+        w.run("overlap", order=order)
+        assert w.status() == (0, -1)
+        assert bits_equal(w.c, first)
+        assert_close(to_f64(w.c), _oracle_c(shards, b, dtype, sa, sb), _tol(dtype), "C")
+    finally:
+        w.close()
+    # integer inputs: every partial and every sum is exact, so the split changes no bit
+    shards, b, _, _ = small_ag_data(world, ms, k, n, dtype, seed=103, kind="int")
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, dtype=dtype, tile=tile)
+    try:
+        B.agg_ctx_set_split(w.ctx, ksplit)
+        w.run("overlap")
+        assert w.status() == (0, -1)
+        want = O.encode_bf16_rne(_oracle_c(shards, b, dtype, 1.0, 1.0))
+        assert np.array_equal(raw(w.c), want)
+    finally:
+        w.close()
+
+
 @pytest.mark.parametrize("elem", [1, 2])
 def test_transpose_helper(gpu, elem):
     k, n = 300, 136
