@@ -741,32 +741,74 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       const int64_t base = (int64_t)block * a.m_block;
       const bool local = (block == a.rank);
       const int slot = block < a.rank ? block : block - 1;
+      const int64_t blk = a.m_block * a.N;    // floats per block
+      if (!local) {
+        // a non-local block's partial goes to `send` with write-through stores, so it is visible
+        // everywhere once they complete (no L2 writeback before the flag)
+        const __amdgpu_buffer_rsrc_t rsend = __builtin_amdgcn_make_buffer_rsrc(
+            a.send, 0, (int)((a.world - 1) * blk * 4), kBufferFlags);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int64_t m = lo + wm * WTM + i * 16 + mrow;
-        if (m >= hi) continue;
-        const int64_t r = m - base;       // row within the block
+        for (int i = 0; i < FM; ++i) {
+          const int64_t m = lo + wm * WTM + i * 16 + mrow;
+          if (m >= hi) continue;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int64_t n = n0 + wn * WTN + j * 16 + ncol;
-          if (n >= a.N) continue;
-          f32x4 v = acc[i][j];
-          if (!local) {
-            *reinterpret_cast<f32x4*>(a.send + ((int64_t)slot * a.m_block + r) * a.N + n) = v;
-          } else {
-            for (int p = 0; p < a.world; ++p) {
-              if (p == a.rank) continue;
-              const f32x4 in = *reinterpret_cast<const f32x4*>(
-                  a.recv + ((int64_t)p * a.m_block + r) * a.N + n);
-              v += in;
+          for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + wn * WTN + j * 16 + ncol;
+            if (n >= a.N) continue;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4, acc[i][j]), rsend,
+                (int)(((int64_t)slot * blk + (m - base) * a.N + n) * 4), 0, kStoreSystemCoherent);
+          }
+        }
+      } else {
+        // the local block: acc + the incoming partials of the peers in ascending rank order,
+        // one peer at a time with half the tile's loads in flight together (rows and columns
+        // past the end read zeros through the buffer's range check)
+        const __amdgpu_buffer_rsrc_t rrecv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(a.recv), 0, (int)(a.world * blk * 4), kBufferFlags);
+        constexpr int FH = FM > 1 ? FM / 2 : 1;
+        for (int p = 0; p < a.world; ++p) {
+          if (p == a.rank) continue;
+#pragma unroll
+          for (int h = 0; h < FM; h += FH) {
+            f32x4 in[FH][FN];
+#pragma unroll
+            for (int i = 0; i < FH; ++i) {
+              const int64_t m = lo + wm * WTM + (h + i) * 16 + mrow;
+#pragma unroll
+              for (int j = 0; j < FN; ++j) {
+                const int64_t n = n0 + wn * WTN + j * 16 + ncol;
+                const int off = (m < hi && n < a.N) ? (int)(((int64_t)p * blk + (m - base) * a.N + n) * 4)
+                                                     : (int)kOutOfRange;
+                in[i][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrecv, off, 0, 0));
+              }
             }
-            *reinterpret_cast<f32x4*>(a.out + r * a.N + n) = v;
+            // keep the loads together: the scheduler would otherwise move each next to its add
+            // and wait for them one at a time
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < FH; ++i)
+#pragma unroll
+              for (int j = 0; j < FN; ++j) acc[h + i][j] += in[i][j];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int64_t m = lo + wm * WTM + i * 16 + mrow;
+          if (m >= hi) continue;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + wn * WTN + j * 16 + ncol;
+            if (n >= a.N) continue;
+            *reinterpret_cast<f32x4*>(a.out + (m - base) * a.N + n) = acc[i][j];
           }
         }
       }
       if (!local) {
-        // publish: this tile's rows of `send` are complete for its column range
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // publish: once every thread's write-through stores have completed, this tile's rows of
+        // `send` are final for its column range; the tile that completes a send chunk raises
+        // its flag (a system-coherent store)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tid == 0) {
           const int64_t rlo = lo - base, rhi = hi - base;
@@ -778,11 +820,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
             const int t_first = (int)(clo / BM), t_last = (int)((chi - 1) / BM);
             const uint32_t expect = (uint32_t)(t_last - t_first + 1) * (uint32_t)a.n_col_tiles;
             const int c = block * a.cps + q;
-            const uint32_t prev = atomicAdd(a.scratch + kScrRsCount + c, 1u);
-            if (prev + 1 == expect) {
-              __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-              __hip_atomic_store(a.send_flags + c, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-            }
+            const uint32_t prev = __hip_atomic_fetch_add(a.scratch + kScrRsCount + c, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            if (prev + 1 == expect)
+              __hip_atomic_store(a.send_flags + c, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
           }
         }
       }

@@ -292,6 +292,8 @@ extern "C" int agg_check_rs_args(int world, int rank, int64_t m, int64_t n, int6
     return fail(AGG_E_UNSUPPORTED, "dimension beyond 2^30");
   if (m * k * 2 >= (int64_t(1) << 31) || n * k * 2 >= (int64_t(1) << 31))
     return fail(AGG_E_UNSUPPORTED, "an operand reaches 2 GiB (the kernel addresses operands with 31-bit offsets)");
+  if (m * n * 4 >= (int64_t(1) << 31))
+    return fail(AGG_E_UNSUPPORTED, "the receive buffer reaches 2 GiB (31-bit offsets)");
   if (uses_copy_stream(mode) && copy_stream && stream == copy_stream)
     return fail(AGG_E_ARG, "stream and copy_stream must differ");
   if (mb > 0 && n > 0) {
