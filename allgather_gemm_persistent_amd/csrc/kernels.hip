@@ -6,16 +6,18 @@
 // registers / shared memory / matrix units; collectives cut into chunks paired with compute
 // tiles, with synchronization inserted).
 //
-// Design, per workgroup (256 threads = 4 wave64s in a 2 x 2 grid):
+// Design, per workgroup (256 threads = 4 wave64s, 2 x 2 over the tile; 4 x 1 for fp8 tiles
+// whose half width is not a multiple of 32):
 //   loop:
 //     claim a tile from this XCD's list (atomic counter), stealing from other XCDs' lists when
 //       its own is exhausted; lists hold row tiles in arrival order, so early chunks are
 //       computed first; a workgroup never waits on another workgroup, only on chunk flags
 //     wave 0 polls the flags of the chunks the tile's rows overlap (relaxed system-scope
 //       loads, s_sleep back-off, bounded by a wall-clock limit), then an acquire fence
-//     K loop: 128-byte-wide K slices (64 bf16 or 128 fp8) of the A and B tiles go
-//       global -> registers -> LDS (XOR-swizzled 16-byte chunks, double buffered, one barrier
-//       per slice); MFMA 16x16x32 bf16 or 16x16x128 f8f6f4 accumulate in fp32
+//     K loop: 64-byte-wide K slices (32 bf16 or 64 fp8) of the A and B tiles go straight from
+//       global memory to LDS (direct-to-LDS buffer loads, swizzled 16-byte chunks, four
+//       stages, one barrier per slice); MFMA 16x16x32 bf16 or 32x32x64 f8f6f4 blocks
+//       accumulate in fp32
 //     epilogue: AllGather -> bf16 (round to nearest even) rows of C; ReduceScatter -> fp32
 //       partial rows to `send` (non-local blocks, then a per-chunk completion counter and a
 //       release store of the send flag) or, for the local block, the accumulator plus the
@@ -23,7 +25,8 @@
 //   the last workgroup to finish resets the claim counters for the next launch.
 //
 // MFMA operand roles are swapped (the B tile feeds the instruction's first operand), so each
-// lane ends with 4 consecutive output columns of one row: 8-byte bf16 or 16-byte fp32 stores.
+// lane ends with quads of 4 consecutive output columns of one row: 8-byte bf16 or 16-byte fp32
+// stores.
 #include "kernels.h"
 
 namespace agg {
@@ -31,11 +34,11 @@ namespace agg {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int kRowBytes = 128;  // bytes of one tile row in one K slice
 // word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle)
 constexpr int kBufferFlags = 0x00020000;
 // a buffer offset past every operand (operands are limited to 2^31 bytes)
@@ -52,12 +55,7 @@ __device__ inline uint32_t load_flag(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// byte offset of 16-byte chunk `ch` (0..7) of tile row `row` in a swizzled LDS tile
-__device__ inline uint32_t lds_off(int row, int ch) {
-  return (uint32_t)(row * kRowBytes + ((ch ^ (row & 7)) << 4));
-}
-
-// ---- bf16 operand pipeline: 32-element (64-byte) K slices, four LDS stages filled by
+// ---- operand pipeline: 64-byte K slices (32 bf16 or 64 fp8 elements), four LDS stages filled by
 // direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds). One wave instruction writes 1 KiB of
 // LDS: 16 tile rows of 64 bytes, lane i landing at byte 16*i. Lane i therefore fetches row i/4
 // of its 16-row group and the 16-byte chunk that the swizzle below puts at position i%4.
@@ -88,12 +86,19 @@ __device__ inline void mfma_bf16(f32x4& acc, const u32x4& b, const u32x4& a) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
 }
 
-// 24 wait states: more than any MFMA result or operand hazard needs (19 for a 16-pass op).
+// acc += B fragment x A fragment, one 32x32x64 MFMA on e4m3 operands (the instruction's
+// default operand formats) with unit block scales (exponent 127 = 2^0); same rules as mfma_bf16.
+__device__ inline void mfma_fp8(f32x16& acc, const i32x8& b, const i32x8& a) {
+  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+               : "+a"(acc) : "v"(b), "v"(a), "v"(127));
+}
+
+// 32 wait states: more than any MFMA result or operand hazard needs (about 20 for a 16-pass op).
 // Every accumulator then passes through an empty asm placed after the nops, so that nothing the
 // compiler emits touches an accumulator between the MFMAs and the nops.
-template <int FM, int FN>
-__device__ inline void acc_settle(f32x4 (&acc)[FM][FN]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+template <typename V, int FM, int FN>
+__device__ inline void acc_settle(V (&acc)[FM][FN]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -375,25 +380,27 @@ template <int BM, int BN, int DT, int EPI>
 __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   constexpr bool FP8 = (DT == AGG_FP8_E4M3);
   constexpr bool kSplitTiles = BM * BN <= 128 * 128;
-  constexpr int WTM = BM / 2, WTN = BN / 2;       // wave tile
-  constexpr int FM = WTM / 16, FN = WTN / 16;     // 16x16 MFMA blocks per wave
-  constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int A_LOADS = BM * 8 / kThreads, B_LOADS = BN * 8 / kThreads;
-  static_assert(BM * 8 % kThreads == 0 && BN * 8 % kThreads == 0, "tile rows");
-  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
+  // 2 x 2 waves over 16x16x32 bf16 or 32x32x64 fp8 MFMA blocks (fp8: 4 x 1 when half the
+  // tile's columns are not whole 32-column blocks)
+  constexpr int WMW = (!FP8 || (BN / 2) % 32 == 0) ? 2 : 4;   // waves along M
+  constexpr int WNW = 4 / WMW;
+  constexpr int WTM = BM / WMW, WTN = BN / WNW;        // wave tile
+  constexpr int BLK = FP8 ? 32 : 16;                   // MFMA output block edge
+  static_assert(WTM % BLK == 0 && WTN % BLK == 0, "wave tile");
+  constexpr int F8M = WTM / 32 > 0 ? WTM / 32 : 1, F8N = WTN / 32 > 0 ? WTN / 32 : 1;
+  // output quads (4 consecutive columns of one row per lane) of a wave: acc[FM][FN]; an fp8
+  // 32x32 block holds 4 of them per lane
+  constexpr int FM = WTM / BLK, FN = (WTN / BLK) * (FP8 ? 4 : 1);
 
-  // fp8 path: two 128-byte-slice stages staged through registers
-  __shared__ __attribute__((aligned(16))) uint8_t smem[FP8 ? 2 * STAGE : 16];
-  // bf16 path: four 64-byte-slice stages
+  // four stages of 64-byte K slices filled by direct-to-LDS loads
   constexpr int BNP = (BN + 63) / 64 * 64;                   // B rows held in LDS
-  constexpr int DSTAGE = FP8 ? 16 : (BM + BNP) * kSliceBytes;
+  constexpr int DSTAGE = (BM + BNP) * kSliceBytes;
   __shared__ __attribute__((aligned(1024))) uint8_t stages[kStages * DSTAGE];
   __shared__ int s_tile[4];
   __shared__ int s_ok;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
   const int home = a.n_lists > 1 ? xcc_id() % a.n_lists : 0;
   const int64_t kbytes = a.K * (FP8 ? 1 : 2);
 
@@ -420,7 +427,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     tile_rows<BM, EPI>(a, row_tile, lo, hi, block, tib);
     const int64_t n0 = (int64_t)col_tile * BN;
     // this part's K slices [t_lo, t_hi) and the K byte where its loads stop (zeros past it)
-    constexpr int kSlice = FP8 ? kRowBytes : kSliceBytes;
+    constexpr int kSlice = kSliceBytes;
     const int nk_all = (int)((kbytes + kSlice - 1) / kSlice);
     const int t_lo = part * a.kps;
     const int t_hi = t_lo + a.kps < nk_all ? t_lo + a.kps : nk_all;
@@ -449,56 +456,50 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
 
-    // ---- K loop
+    // ---- K loop: four LDS stages of 64-byte K slices, filled by direct-to-LDS buffer loads
+    // (out-of-range rows and the K tail read zeros through the buffer descriptor's range check)
     f32x4 acc[FM][FN];
+    constexpr int NI = (BM + BNP) / 64;      // load instructions per wave per stage
+    constexpr int NA = BM / 64;              // the first NA of them fetch A rows
+    // lane's chunk: rows of a 16-row group are lane/4, chunk position lane%4
+    const uint32_t gk = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) << 4);
+    uint32_t base[NI];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // Operands are read through buffer resources: an offset at or past the resource's size
-    // reads as zero, which pads rows past the matrix end and the K tail without branches.
-    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(a.a), 0, (int)(a.M * kbytes), kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(a.b), 0, (int)(a.N * kbytes), kBufferFlags);
-
-    if constexpr (!FP8) {
-      // ---- bf16: 4-stage direct-to-LDS pipeline over 64-byte K slices
-      constexpr int NI = (BM + BNP) / 64;      // load instructions per wave per stage
-      constexpr int NA = BM / 64;              // the first NA of them fetch A rows
-      // lane's chunk: rows of a 16-row group are lane/4, chunk position lane%4
-      const uint32_t gk = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) << 4);
-      uint32_t base[NI];
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int r = (j * 4 + wave) * 16 + (lane >> 2);   // LDS row
-        if (j < NA) {
-          const int64_t gr = lo + r;
-          base[j] = gr < a.M ? (uint32_t)gr * (uint32_t)kbytes + gk : kOutOfRange;
-        } else {
-          const int c = r - BM;
-          const int64_t gn = n0 + c;
-          base[j] = (c < BN && gn < a.N) ? (uint32_t)gn * (uint32_t)kbytes + gk : kOutOfRange;
-        }
+    for (int j = 0; j < NI; ++j) {
+      const int r = (j * 4 + wave) * 16 + (lane >> 2);   // LDS row
+      if (j < NA) {
+        const int64_t gr = lo + r;
+        base[j] = gr < a.M ? (uint32_t)gr * (uint32_t)kbytes + gk : kOutOfRange;
+      } else {
+        const int c = r - BM;
+        const int64_t gn = n0 + c;
+        base[j] = (c < BN && gn < a.N) ? (uint32_t)gn * (uint32_t)kbytes + gk : kOutOfRange;
       }
-      const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-      const u32x4 da = buffer_desc(a.a, (uint32_t)(a.M * kbytes));
-      const u32x4 db = buffer_desc(a.b, (uint32_t)(a.N * kbytes));
-      const uint32_t lds0 = lds_addr(stages) + (uint32_t)wave_u * 1024u;
-      // load j of slice t (j < NI): A rows for j < NA, else B rows
-      auto issue_one = [&](int t, int j) {
-        const uint32_t tk = (uint32_t)t * kSliceBytes;
-        // past the K end: set the offset's top bit (out of range, reads zero) without a branch
-        const uint32_t oob = (uint32_t)((int)(tk + gk - kend) >> 31) ^ 0xFFFFFFFFu;
-        const uint32_t kmask = oob & kOutOfRange;
-        const uint32_t st = lds0 + (uint32_t)(t & (kStages - 1)) * DSTAGE;
-        lds_dma_load(j < NA ? da : db, st + j * 4096u, (base[j] + tk) | kmask);
-      };
-      auto issue = [&](int t) {
+    }
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const u32x4 da = buffer_desc(a.a, (uint32_t)(a.M * kbytes));
+    const u32x4 db = buffer_desc(a.b, (uint32_t)(a.N * kbytes));
+    const uint32_t lds0 = lds_addr(stages) + (uint32_t)wave_u * 1024u;
+    // load j of slice t (j < NI): A rows for j < NA, else B rows
+    auto issue_one = [&](int t, int j) {
+      const uint32_t tk = (uint32_t)t * kSliceBytes;
+      // past the K end: set the offset's top bit (out of range, reads zero) without a branch
+      const uint32_t oob = (uint32_t)((int)(tk + gk - kend) >> 31) ^ 0xFFFFFFFFu;
+      const uint32_t kmask = oob & kOutOfRange;
+      const uint32_t st = lds0 + (uint32_t)(t & (kStages - 1)) * DSTAGE;
+      lds_dma_load(j < NA ? da : db, st + j * 4096u, (base[j] + tk) | kmask);
+    };
+    auto issue = [&](int t) {
 #pragma unroll
-        for (int j = 0; j < NI; ++j) issue_one(t, j);
-      };
+      for (int j = 0; j < NI; ++j) issue_one(t, j);
+    };
+    constexpr int NH = NI / 2;                 // loads of a slice issued in the earlier half
+    if constexpr (!FP8) {
+      // ---- bf16: 16x16x32 MFMA blocks, one 16-byte fragment per lane
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       auto load_b1 = [&](int t, int j) {
         const uint8_t* st = stages + (t & (kStages - 1)) * DSTAGE;
         return *reinterpret_cast<const u32x4*>(
@@ -523,7 +524,6 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       // t), and the second half spreads slice t+1's B fragments and first A fragment, then the
       // loads 0..NH-1 of slice t+4, between its MFMAs.
       constexpr int RB = FM / 2;                 // rows before the barrier (FM >= 2)
-      constexpr int NH = NI / 2;                 // loads of a slice issued in the earlier half
       constexpr int S1 = RB * FN, S2 = (FM - RB) * FN;
       constexpr int E1 = NI - NH, E2 = FN + 1 + NH;
       static_assert(FM - RB - 1 <= RB, "the A fragments after the barrier are loaded before it");
@@ -583,87 +583,124 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
     } else {
-      // ---- fp8: 128-byte K slices staged through registers, two LDS stages
-      u32x4 ra[A_LOADS], rb[B_LOADS];
-      auto gload = [&](int kt) {
-        const uint32_t kb = (uint32_t)kt * kRowBytes;
+      // ---- fp8 (e4m3): 32x32x64 MFMA blocks with unit block scales, one 32-byte fragment per
+      // lane; the per-tensor scales are applied in the epilogue
+      f32x16 acc8[F8M][F8N];
 #pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) {
-          const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
-          const uint32_t kbyte = kb + ch * 16;
-          const uint32_t off = kbyte < kend ? (uint32_t)(lo + row) * (uint32_t)kbytes + kbyte : kOutOfRange;
-          ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsa, off, 0, 0));
-        }
+      for (int i = 0; i < F8M; ++i)
 #pragma unroll
-        for (int i = 0; i < B_LOADS; ++i) {
-          const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
-          const uint32_t kbyte = kb + ch * 16;
-          const uint32_t off = kbyte < kend ? (uint32_t)(n0 + row) * (uint32_t)kbytes + kbyte : kOutOfRange;
-          rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, off, 0, 0));
-        }
+        for (int j = 0; j < F8N; ++j) acc8[i][j] = f32x16{};
+      // a 32-row fp8 fragment: row r + (lane & 31), K bytes 32*(lane/32) .. +31 of the slice
+      auto frag8 = [&](int t, int r) {
+        const uint8_t* st = stages + (t & (kStages - 1)) * DSTAGE;
+        const int row = r + (lane & 31), g = (lane >> 5) * 2;
+        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(st + lds64_off(row, g));
+        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(st + lds64_off(row, g + 1));
+        return i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                     (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
       };
-      auto sstore = [&](int buf) {
-        uint8_t* As = smem + buf * STAGE;
-        uint8_t* Bs = As + A_BYTES;
+      auto load_b1 = [&](int t, int j) { return frag8(t, BM + wn * WTN + j * 32); };
+      auto load_b = [&](i32x8 (&fb)[F8N], int t) {
 #pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) {
-          const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
-          *reinterpret_cast<u32x4*>(As + lds_off(row, ch)) = ra[i];
+        for (int j = 0; j < F8N; ++j) fb[j] = load_b1(t, j);
+      };
+      auto load_a = [&](int t, int i) { return frag8(t, wm * WTM + i * 32); };
+      // One K slice t, its B fragments in fbc and its first A fragment in fa (requested during
+      // the previous slice). Slot t%4 is refilled with slice t+4 by NI direct-to-LDS loads, the
+      // first NH of them in the second half of slice t and the rest in the first half of slice
+      // t+1, so that every half slice carries about NI/2 loads between its MFMAs and the load
+      // path never takes a burst. First half of slice t: the remaining A fragments of slice t
+      // are requested row by row, and the loads NH..NI-1 of slice t+3 go between the MFMAs.
+      // Then the waves meet (slice t+1 has landed everywhere; every wave has read all of slice
+      // t), and the second half spreads slice t+1's B fragments and first A fragment, then the
+      // loads 0..NH-1 of slice t+4, between its MFMAs.
+      constexpr int RB = F8M / 2;                // rows before the barrier
+      constexpr int S1 = RB * F8N, S2 = (F8M - RB) * F8N;
+      constexpr int E1 = NI - NH, E2 = F8N + 1 + NH;
+      static_assert(F8M - RB - 1 <= RB, "the A fragments after the barrier are loaded before it");
+      // a wave with a single 32x32 block reuses its accumulator in the next slice's first
+      // MFMA: give the previous one time to write it back
+      constexpr bool kLoneBlock = F8M * F8N < 3;
+      i32x8 fa;
+      auto slice = [&](i32x8 (&fbc)[F8N], i32x8 (&fbn)[F8N], int t) {
+        i32x8 far[F8M];
+        far[0] = fa;
+        if (S1 == 0) {                            // no MFMA before the barrier: issue plainly
+#pragma unroll
+          for (int e = 0; e < E1; ++e) issue_one(t + 3, NH + e);
         }
 #pragma unroll
-        for (int i = 0; i < B_LOADS; ++i) {
-          const int idx = i * kThreads + tid, row = idx >> 3, ch = idx & 7;
-          *reinterpret_cast<u32x4*>(Bs + lds_off(row, ch)) = rb[i];
+        for (int i = 0; i < RB; ++i) {
+          far[i + 1] = load_a(t, i + 1);
+          if (RB + 1 + i < F8M) far[RB + 1 + i] = load_a(t, RB + 1 + i);
+#pragma unroll
+          for (int j = 0; j < F8N; ++j) {
+            mfma_fp8(acc8[i][j], fbc[j], far[i]);
+            const int q = i * F8N + j;
+#pragma unroll
+            for (int e = 0; e < E1; ++e)
+              if (S1 > 0 && e * S1 / E1 == q) issue_one(t + 3, NH + e);
+          }
+        }
+        stage_barrier<2 * NI>();
+#pragma unroll
+        for (int i = RB; i < F8M; ++i) {
+#pragma unroll
+          for (int j = 0; j < F8N; ++j) {
+            if (kLoneBlock) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+            mfma_fp8(acc8[i][j], fbc[j], far[i]);
+            const int q = (i - RB) * F8N + j;
+#pragma unroll
+            for (int e = 0; e < E2; ++e) {
+              if (e * S2 / E2 != q) continue;         // request e goes after MFMA slot e*S2/E2
+              if (e < F8N) fbn[e] = load_b1(t + 1, e);
+              else if (e == F8N) fa = load_a(t + 1, 0);
+              else issue_one(t + 4, e - F8N - 1);
+            }
+          }
         }
       };
       if (t_hi > t_lo) {
-        gload(t_lo);
-        sstore(0);
-        __syncthreads();
-      }
-      for (int kt = t_lo; kt < t_hi; ++kt) {
-        const int buf = (kt - t_lo) & 1;
-        if (kt + 1 < t_hi) gload(kt + 1);
-        const uint8_t* As = smem + buf * STAGE;
-        const uint8_t* Bs = As + A_BYTES;
-        // B fragments of the slice stay in registers; A fragments stream one row block at a time
-        u32x4 fb[FN][2];
+        i32x8 fb0[F8N], fb1[F8N];
+        acc_settle(acc8);
+        issue(t_lo);
+        issue(t_lo + 1);
+        issue(t_lo + 2);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int ch = (lane >> 4) * 2 + j;
-#pragma unroll
-          for (int i = 0; i < FN; ++i) {
-            const int row = wn * WTN + i * 16 + (lane & 15);
-            fb[i][j] = *reinterpret_cast<const u32x4*>(Bs + lds_off(row, ch));
-          }
+        for (int j = 0; j < NH; ++j) issue_one(t_lo + 3, j);   // the first slice issues the rest
+        stage_barrier<2 * NI + NH>();
+        load_b(fb0, t_lo);
+        fa = load_a(t_lo, 0);
+        // slices past the part's end read zeros: an odd count runs one zero slice
+        for (int t = t_lo; t < t_hi; t += 2) {
+          slice(fb0, fb1, t);
+          slice(fb1, fb0, t + 1);
         }
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          u32x4 fa[2];
-          const int row = wm * WTM + i * 16 + (lane & 15);
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            fa[j] = *reinterpret_cast<const u32x4*>(As + lds_off(row, (lane >> 4) * 2 + j));
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            i32x8 opa, opb;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              opa[e] = (int)fb[j][0][e]; opa[e + 4] = (int)fb[j][1][e];
-              opb[e] = (int)fa[0][e]; opb[e + 4] = (int)fa[1][e];
-            }
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                opa, opb, acc[i][j], 0, 0, 0, 127, 0, 127);
-          }
-        }
-        if (kt + 1 < t_hi) sstore(buf ^ 1);
-        __syncthreads();
+        acc_settle(acc8);
+        // loads issued past the end land (as zeros) and every wave is done with LDS before the
+        // next tile refills it
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
+      // the epilogue's view: quad q of block (i, j) is acc[i][4j + q]
+#pragma unroll
+      for (int i = 0; i < F8M; ++i)
+#pragma unroll
+        for (int j = 0; j < F8N; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[i][4 * j + q] = f32x4{acc8[i][j][4 * q], acc8[i][j][4 * q + 1], acc8[i][j][4 * q + 2],
+                                      acc8[i][j][4 * q + 3]};
     }
 
     // ---- epilogue
-    const int mrow = lane & 15;          // row within a 16x16 block
-    const int ncol = (lane >> 4) * 4;    // first of 4 consecutive columns
+    // quad (i, j) of this lane: row qrow(i), columns qcol(j) .. qcol(j)+3 of the tile
+    auto qrow = [&](int i) {
+      return FP8 ? wm * WTM + i * 32 + (lane & 31) : wm * WTM + i * 16 + (lane & 15);
+    };
+    auto qcol = [&](int j) {
+      return FP8 ? wn * WTN + (j >> 2) * 32 + (j & 3) * 8 + (lane >> 5) * 4
+                 : wn * WTN + j * 16 + (lane >> 4) * 4;
+    };
     if (EPI == kEpiAllGather) {
       bool finish = true;
       // split-K exists for tiles up to 128 x 128 only (the host never splits a larger one): the
@@ -678,11 +715,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
             a.ws, 0, (int)(a.ksplit * plane * 4), kBufferFlags);
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          const int64_t m = lo + wm * WTM + i * 16 + mrow;
+          const int64_t m = lo + qrow(i);
           if (m >= hi) continue;
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + wn * WTN + j * 16 + ncol;
+            const int64_t n = n0 + qcol(j);
             if (n >= a.N) continue;
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rw,
                                                    (int)(((int64_t)part * plane + m * a.N + n) * 4),
@@ -702,10 +739,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
           for (int q = 0; q < a.ksplit; ++q) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-              const int64_t m = lo + wm * WTM + i * 16 + mrow;
+              const int64_t m = lo + qrow(i);
 #pragma unroll
               for (int j = 0; j < FN; ++j) {
-                const int64_t n = n0 + wn * WTN + j * 16 + ncol;
+                const int64_t n = n0 + qcol(j);
                 // rows / columns past the end read zeros (offset past the buffer)
                 const int off = (m < hi && n < a.N) ? (int)(((int64_t)q * plane + m * a.N + n) * 4)
                                                      : (int)kOutOfRange;
@@ -722,11 +759,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       if (finish) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          const int64_t m = lo + wm * WTM + i * 16 + mrow;
+          const int64_t m = lo + qrow(i);
           if (m >= hi) continue;
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + wn * WTN + j * 16 + ncol;
+            const int64_t n = n0 + qcol(j);
             if (n >= a.N) continue;
             f32x4 v = acc[i][j];
             if (FP8) v *= a.scale;
@@ -749,11 +786,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
             a.send, 0, (int)((a.world - 1) * blk * 4), kBufferFlags);
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          const int64_t m = lo + wm * WTM + i * 16 + mrow;
+          const int64_t m = lo + qrow(i);
           if (m >= hi) continue;
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + wn * WTN + j * 16 + ncol;
+            const int64_t n = n0 + qcol(j);
             if (n >= a.N) continue;
             __builtin_amdgcn_raw_buffer_store_b128(
                 __builtin_bit_cast(u32x4, acc[i][j]), rsend,
@@ -774,10 +811,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
             f32x4 in[FH][FN];
 #pragma unroll
             for (int i = 0; i < FH; ++i) {
-              const int64_t m = lo + wm * WTM + (h + i) * 16 + mrow;
+              const int64_t m = lo + qrow(h + i);
 #pragma unroll
               for (int j = 0; j < FN; ++j) {
-                const int64_t n = n0 + wn * WTN + j * 16 + ncol;
+                const int64_t n = n0 + qcol(j);
                 const int off = (m < hi && n < a.N) ? (int)(((int64_t)p * blk + (m - base) * a.N + n) * 4)
                                                      : (int)kOutOfRange;
                 in[i][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrecv, off, 0, 0));
@@ -794,11 +831,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          const int64_t m = lo + wm * WTM + i * 16 + mrow;
+          const int64_t m = lo + qrow(i);
           if (m >= hi) continue;
 #pragma unroll
           for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + wn * WTN + j * 16 + ncol;
+            const int64_t n = n0 + qcol(j);
             if (n >= a.N) continue;
             *reinterpret_cast<f32x4*>(a.out + (m - base) * a.N + n) = acc[i][j];
           }

@@ -60,7 +60,7 @@ int choose_list_cols(int lists, int n_row_tiles, int n_col_tiles, int bm, int bn
   return best;
 }
 
-int slice_bytes(int dtype) { return dtype == AGG_FP8_E4M3 ? 128 : 64; }
+int slice_bytes(int) { return 64; }
 
 KSplit choose_ksplit(int op, int dtype, int64_t tiles, int64_t k, int units) {
   KSplit r{1, 0};

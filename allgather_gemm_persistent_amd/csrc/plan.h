@@ -19,7 +19,7 @@ struct TileShape {
 // Output tile shape for one call. op: 0 = AllGather+GEMM, 1 = GEMM+ReduceScatter.
 TileShape choose_tile(int op, int dtype, int64_t m, int64_t n, int64_t k);
 
-// K slice of the kernel's main loop in bytes: 64 for bf16, 128 for fp8.
+// K slice of the kernel's main loop in bytes (64 for both operand types).
 int slice_bytes(int dtype);
 
 // Split-K: with fewer output tiles than half the compute units and a long K, each tile's K
