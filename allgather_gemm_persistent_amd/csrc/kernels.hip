@@ -259,31 +259,48 @@ struct Tile {
 // (L / list_cols) x list_cols grid: list x holds the row tiles at compute positions
 // x / list_cols, + L / list_cols, ... (so every list follows the compute order) crossed with
 // column tiles [xc*nc/list_cols, (xc+1)*nc/list_cols), xc = x % list_cols.
+// Run by all lanes of one wave: lane d reads the counter of the d-th list in search order, so
+// one round trip finds the first list with tiles left (and, at the end, that none has any); the
+// lane owning that list takes a tile with an atomic add, retrying if another workgroup emptied
+// the list in between. Returns, on every lane, whether a tile was claimed (then in t).
 __device__ inline bool claim(const GemmArgs& a, int home, Tile& t) {
   const int L = a.n_lists;
   const int Lc = a.list_cols, Lr = L / Lc;
-  for (int d = 0; d < L; ++d) {
-    int x = home + d;
-    if (x >= L) x -= L;
-    const int xr = x / Lc, xc = x - xr * Lc;
-    const int c_lo = (int)((int64_t)xc * a.n_col_tiles / Lc);
-    const int c_hi = (int)((int64_t)(xc + 1) * a.n_col_tiles / Lc);
-    const int nx = c_hi - c_lo;
-    const int ny = xr < a.n_row_tiles ? (a.n_row_tiles - xr + Lr - 1) / Lr : 0;
-    if (nx <= 0 || ny <= 0) continue;
-    const uint32_t len = (uint32_t)ny * (uint32_t)nx;
-    uint32_t* ctr = a.scratch + kScrLists + x;
-    if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= len) continue;
-    const uint32_t k = atomicAdd(ctr, 1u);
-    if (k < len) {
-      t.row_tile = (int)a.scratch[kScrRowOrder + xr + (int)(k / nx) * Lr];
-      t.col_tile = c_lo + (int)(k % nx);
-      t.list = x;
-      t.pos = (int)k;
+  const int lane = threadIdx.x & 63;
+  int x = home + lane;
+  if (x >= L) x -= L;
+  // recomputed per call: hoisted out of the tile loop, these would hold registers through the
+  // main loop
+  asm volatile("" : "+v"(x));
+  const int xr = x / Lc, xc = x - xr * Lc;
+  const int c_lo = (int)((int64_t)xc * a.n_col_tiles / Lc);
+  const int c_hi = (int)((int64_t)(xc + 1) * a.n_col_tiles / Lc);
+  const int nx = c_hi - c_lo;
+  const int ny = xr < a.n_row_tiles ? (a.n_row_tiles - xr + Lr - 1) / Lr : 0;
+  const uint32_t len = (lane < L && nx > 0 && ny > 0) ? (uint32_t)ny * (uint32_t)nx : 0u;
+  uint32_t* ctr = a.scratch + kScrLists + x;
+  for (;;) {
+    const bool open = len > 0 && __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < len;
+    const uint64_t m = __ballot(open);
+    if (m == 0) return false;
+    const int d = (int)__builtin_ctzll(m);
+    uint32_t k = 0;
+    if (lane == d) k = atomicAdd(ctr, 1u);
+    k = (uint32_t)__shfl((int)k, d);
+    if (k < (uint32_t)__shfl((int)len, d)) {
+      if (lane == d) {
+        t.row_tile = (int)a.scratch[kScrRowOrder + xr + (int)(k / nx) * Lr];
+        t.col_tile = c_lo + (int)(k % nx);
+        t.list = x;
+        t.pos = (int)k;
+      }
+      t.row_tile = __shfl(t.row_tile, d);
+      t.col_tile = __shfl(t.col_tile, d);
+      t.list = __shfl(t.list, d);
+      t.pos = __shfl(t.pos, d);
       return true;
     }
   }
-  return false;
 }
 
 // Rows of a row tile: [lo, hi) in the A operand, and (RS) the block it belongs to.
@@ -408,12 +425,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   if (a.copy_jobs && (int)blockIdx.x < a.copy_wgs) produce_chunks(a, tid, s_tile);
 
   for (;;) {
-    if (tid == 0) {
-      Tile t;
-      if (claim(a, home, t)) {
-        s_tile[0] = t.row_tile; s_tile[1] = t.col_tile; s_tile[2] = t.list; s_tile[3] = t.pos;
-      } else {
-        s_tile[0] = -1;
+    if (wave == 0) {
+      Tile t{};
+      const bool got = claim(a, home, t);
+      if (lane == 0) {
+        s_tile[0] = got ? t.row_tile : -1;
+        s_tile[1] = t.col_tile; s_tile[2] = t.list; s_tile[3] = t.pos;
       }
     }
     __syncthreads();
@@ -873,15 +890,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     __syncthreads();
   }
 
-  // ---- the last workgroup resets the counters for the next launch
+  // ---- the last workgroup resets the counters for the next launch. No fence: every counter
+  // reset here was last touched by the other workgroups through atomics whose returned values
+  // they used, i.e. that had completed, before they counted themselves done.
   if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t prev = atomicAdd(a.scratch + kScrDone, 1u);
     s_ok = (prev == gridDim.x - 1);
   }
   __syncthreads();
   if (__builtin_amdgcn_readfirstlane(s_ok)) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (tid < kMaxLists) __hip_atomic_store(a.scratch + kScrLists + tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (a.copy_jobs) {
       if (tid == 0) {
@@ -896,7 +913,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       for (int i = tid; i < a.world * a.cps; i += kThreads)
         __hip_atomic_store(a.scratch + kScrRsCount + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (tid == 0) __hip_atomic_store(a.scratch + kScrDone, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(a.scratch + kScrDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
