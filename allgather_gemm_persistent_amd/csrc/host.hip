@@ -368,11 +368,13 @@ void fill_copies(agg_ctx* ctx, GemmArgs& g, const ChunkCopy& cc, uint32_t* flags
   g.sym = cc.dst;
   g.put_flags = flags;
   g.chunk_bytes = cc.cr * cc.row_bytes;
-  // automatic piece size: the remote bytes spread over the copying workgroups, 16 KiB .. 1 MiB
+  // automatic piece size: as many pieces per chunk as keep every job in one round of the
+  // copying workgroups (so no workgroup copies twice while others idle), in whole 4 KiB pages,
+  // at least 16 KiB
   const int copiers = ctx->copy_wgs > 0 ? std::min(ctx->copy_wgs, grid) : grid;
-  const int64_t total = g.chunk_bytes * int64_t(n_order);
-  const int64_t autop = std::min<int64_t>(std::max<int64_t>((total / std::max(copiers, 1) + 16383) / 16384 * 16384,
-                                                            16384), 1 << 20);
+  const int64_t per_chunk = std::max<int64_t>(1, int64_t(copiers) / std::max<int64_t>(int64_t(n_order), 1));
+  const int64_t autop =
+      std::max<int64_t>(((g.chunk_bytes + per_chunk - 1) / per_chunk + 4095) / 4096 * 4096, 16384);
   const int64_t piece = std::max<int64_t>(16, (ctx->piece_bytes > 0 ? ctx->piece_bytes : autop) / 16 * 16);
   g.piece_bytes = std::min<int64_t>(g.chunk_bytes, piece);
   g.pieces = g.piece_bytes > 0 ? int((g.chunk_bytes + g.piece_bytes - 1) / g.piece_bytes) : 1;

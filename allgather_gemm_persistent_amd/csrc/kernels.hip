@@ -196,12 +196,13 @@ __device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __re
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// The in-kernel producer: take copy jobs until none are left. Job j*pieces + q copies piece q of
-// the chunk at arrival position j; the job that completes a chunk (all its pieces copied and
-// released) stores the epoch into the chunk's flag. Jobs are claimed in arrival order, so
-// chunks complete roughly in that order. With delays, job j*pieces + q starts no earlier than
-// the j-th cumulative delay after the first job was claimed.
-__device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job) {
+// The in-kernel producer. Job j*pieces + q copies piece q of the chunk at arrival position j;
+// the job that completes a chunk (all its pieces copied and released) stores the epoch into the
+// chunk's flag. Copying workgroup w takes jobs w, w + copy_wgs, w + 2*copy_wgs, ...: a static
+// round robin in arrival order, so no job counter is contended and chunks complete roughly in
+// arrival order. With delays, job j*pieces + q starts no earlier than the j-th cumulative delay
+// after the first copying workgroup started.
+__device__ inline void produce_chunks(const GemmArgs& a, int tid) {
   const uint32_t* order = a.scratch + kScrOrder;
   // every value that decides a branch around a barrier is made visibly uniform
   // (readfirstlane): otherwise the compiler may treat the loop exit as divergent and lay the
@@ -209,20 +210,14 @@ __device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job) {
   // barriers between the waves
   const uint32_t jobs = __builtin_amdgcn_readfirstlane(a.copy_jobs);
   const uint32_t pieces = __builtin_amdgcn_readfirstlane((uint32_t)a.pieces);
-  auto next_job = [&]() -> uint32_t {
-    if (tid == 0) s_job[0] = (int)atomicAdd(a.scratch + kScrCopyNext, 1u);
-    __syncthreads();
-    const uint32_t job = (uint32_t)__builtin_amdgcn_readfirstlane(s_job[0]);
-    __syncthreads();
-    return job;
-  };
+  const uint32_t stride = __builtin_amdgcn_readfirstlane((uint32_t)a.copy_wgs);
   uint32_t t0 = 0;
   if (a.copy_delays && tid == 0) {
     const uint32_t now = wall_ticks() | 1u;   // never 0, which marks "unset"
     const uint32_t prev = atomicCAS(a.scratch + kScrCopyT0, 0u, now);
     t0 = prev ? prev : now;
   }
-  for (uint32_t job = next_job(); job < jobs; job = next_job()) {
+  for (uint32_t job = blockIdx.x; job < jobs; job += stride) {
     const uint32_t j = job / pieces, q = job - j * pieces;
     const int c = (int)__builtin_amdgcn_readfirstlane(order[j]);
     const int p = c / a.copy_cps, jl = c - p * a.copy_cps;
@@ -421,10 +416,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   const int home = a.n_lists > 1 ? xcc_id() % a.n_lists : 0;
   const int64_t kbytes = a.K * (FP8 ? 1 : 2);
 
-  // ---- producer phase: the first copy_wgs workgroups move the remote chunks, then compute
-  if (a.copy_jobs && (int)blockIdx.x < a.copy_wgs) produce_chunks(a, tid, s_tile);
-
-  for (;;) {
+  auto claim_tile = [&]() {
     if (wave == 0) {
       Tile t{};
       const bool got = claim(a, home, t);
@@ -434,6 +426,16 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       }
     }
     __syncthreads();
+  };
+
+  // ---- the first tile is claimed at once, while the counters are quiet; then the first
+  // copy_wgs workgroups move the remote chunks (so the claim is off the path from the end of
+  // the copy to the first tile), and every workgroup computes tiles, claiming the next one after
+  // each
+  claim_tile();
+  if (a.copy_jobs && (int)blockIdx.x < a.copy_wgs) produce_chunks(a, tid);
+
+  for (;; claim_tile()) {   // (an abandoned tile's `continue` claims the next one too)
     // uniform for the compiler too (see produce_chunks)
     const int row_tile = __builtin_amdgcn_readfirstlane(s_tile[0]);
     if (row_tile < 0) break;
@@ -901,10 +903,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   if (__builtin_amdgcn_readfirstlane(s_ok)) {
     if (tid < kMaxLists) __hip_atomic_store(a.scratch + kScrLists + tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (a.copy_jobs) {
-      if (tid == 0) {
-        __hip_atomic_store(a.scratch + kScrCopyNext, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0)
         __hip_atomic_store(a.scratch + kScrCopyT0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
       for (uint32_t i = tid; i * (uint32_t)a.pieces < a.copy_jobs; i += kThreads)
         __hip_atomic_store(a.scratch + kScrPieces + a.scratch[kScrOrder + i], 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);

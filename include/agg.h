@@ -125,8 +125,9 @@ enum {
 
 /* Select the producer of later calls. For AGG_PRODUCER_CU, `copy_wgs` workgroups of the
  * persistent grid (0: all of them) first take copy jobs, each moving `piece_kib` KiB of one chunk
- * (0: the remote bytes divided by the copying workgroups, rounded up to 16 KiB, at most
- * 1 MiB; a chunk is cut into ceil(chunk bytes / piece) pieces), in arrival order, and only then
+ * (0: a chunk is cut into floor(copying workgroups / remote chunks) pieces, at least one, each
+ * rounded up to whole 4 KiB and at least 16 KiB, so that every job fits in one round of the
+ * copying workgroups; a chunk is cut into ceil(chunk bytes / piece) pieces), in arrival order, and only then
  * claim tiles; the workgroup that completes a chunk's last piece releases its flag. The other
  * arguments are ignored for AGG_PRODUCER_SDMA. AGG_E_ARG for an unknown kind or a negative
  * count. */
