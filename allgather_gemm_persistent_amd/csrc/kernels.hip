@@ -754,22 +754,38 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         __syncthreads();
         finish = __builtin_amdgcn_readfirstlane(s_ok) != 0;
         if (finish) {
-          // one part at a time, every (i, j) of the part in flight together
-          for (int q = 0; q < a.ksplit; ++q) {
+          // parts in order, software-pipelined: the loads of part q+1 are in flight while part
+          // q is added (past the last part they read zeros, so every step issues the same
+          // loads and the wait for part q leaves part q+1's loads outstanding)
+          auto load_part = [&](f32x4 (&v)[FM][FN], int q) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
               const int64_t m = lo + qrow(i);
 #pragma unroll
               for (int j = 0; j < FN; ++j) {
                 const int64_t n = n0 + qcol(j);
-                // rows / columns past the end read zeros (offset past the buffer)
-                const int off = (m < hi && n < a.N) ? (int)(((int64_t)q * plane + m * a.N + n) * 4)
-                                                     : (int)kOutOfRange;
-                const f32x4 v = __builtin_bit_cast(
+                // rows / columns past the end, and parts past the last, read zeros (offset past
+                // the buffer)
+                const int off = (q < a.ksplit && m < hi && n < a.N)
+                                    ? (int)(((int64_t)q * plane + m * a.N + n) * 4)
+                                    : (int)kOutOfRange;
+                v[i][j] = __builtin_bit_cast(
                     f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kStoreSystemCoherent));
-                acc[i][j] = q == 0 ? v : acc[i][j] + v;
               }
             }
+          };
+          f32x4 cur[FM][FN], nxt[FM][FN];
+          load_part(cur, 0);
+          for (int q = 0; q < a.ksplit; ++q) {
+            load_part(nxt, q + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+              for (int j = 0; j < FN; ++j) {
+                acc[i][j] = q == 0 ? cur[i][j] : acc[i][j] + cur[i][j];
+                cur[i][j] = nxt[i][j];
+              }
           }
           if (tid == 0)
             __hip_atomic_store(a.scratch + kScrSplit + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
