@@ -46,6 +46,7 @@ _SIGNATURES = {
     "agg_ctx_set_tile": [_vp, _c_int, _c_int],
     "agg_ctx_set_lists": [_vp, _c_int, _c_int],
     "agg_ctx_set_split": [_vp, _c_int],
+    "agg_ctx_set_pull": [_vp, _c_int],
     "agg_ctx_set_producer": [_vp, _c_int, _c_int, _c_int],
     "agg_set_trace": [_vp, _vp, _sz],
     "agg_ctx_set_timing": [_vp, _c_int],
@@ -233,6 +234,13 @@ def agg_ctx_set_producer(ctx, kind="cu", copy_wgs: int = 0, piece_kib: int = 0) 
     """Producer of later calls: "cu" (copy jobs inside the persistent kernel) or "sdma"."""
     _call("agg_ctx_set_producer", ctx, PRODUCERS[kind] if isinstance(kind, str) else int(kind),
           copy_wgs, piece_kib)
+
+
+PULL_MODES = {"auto": 0, "off": 1, "on": 2}
+
+
+def agg_ctx_set_pull(ctx, pull: str = "auto") -> None:
+    _call("agg_ctx_set_pull", ctx, PULL_MODES[pull])
 
 
 def agg_ctx_set_split(ctx, ksplit: int = 0) -> None:

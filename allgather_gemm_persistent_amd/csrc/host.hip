@@ -60,6 +60,8 @@ constexpr uint32_t kEpochLast = 0xFFFFFFFEu;   // 0xFFFFFFFF means "no flag" in 
 constexpr int kMaxCopyStreams = 8;
 constexpr int kDefaultCopyStreams = 4;
 constexpr int kDefaultReservedCus = 32;
+// AGG_PULL_AUTO pulls gathers of at most this many remote bytes (latency-bound transfers)
+constexpr int64_t kPullMaxBytes = int64_t(4) << 20;
 constexpr int kTimingRing = 256;          // launches whose kernel duration is kept
 
 enum FlagSlot { kFlagsAg = 0, kFlagsRsRecv = 1, kFlagsRsSend = 2, kFlagSlots = 3 };
@@ -94,6 +96,7 @@ struct agg_ctx {
   size_t ws_bytes = 0;
   int producer = AGG_PRODUCER_CU;
   int copy_wgs = 0;                          // 0: every workgroup takes copy jobs first
+  int pull = AGG_PULL_AUTO;                  // AllGather+GEMM pull mode (overlapped CU calls)
   int64_t piece_bytes = 0;                   // 0: chosen per call
   // tables the kernel reads from scratch, as last uploaded: row tiles in compute order, arrival
   // order, cumulative delays (kScrRowOrder / kScrOrder / kScrDelay)
@@ -363,7 +366,7 @@ int upload_schedule(agg_ctx* ctx, hipStream_t s, const std::vector<int32_t>& ord
 
 // Copy-job fields of the kernel arguments for the CU producer.
 void fill_copies(agg_ctx* ctx, GemmArgs& g, const ChunkCopy& cc, uint32_t* flags, size_t n_order,
-                 bool delays, int world, int grid) {
+                 bool delays, int world, int grid, int pull_copiers) {
   for (int p = 0; p < world; ++p) g.peer[p] = cc.src[p];
   g.sym = cc.dst;
   g.put_flags = flags;
@@ -371,7 +374,8 @@ void fill_copies(agg_ctx* ctx, GemmArgs& g, const ChunkCopy& cc, uint32_t* flags
   // automatic piece size: as many pieces per chunk as keep every job in one round of the
   // copying workgroups (so no workgroup copies twice while others idle), in whole 4 KiB pages,
   // at least 16 KiB
-  const int copiers = ctx->copy_wgs > 0 ? std::min(ctx->copy_wgs, grid) : grid;
+  const int copiers = pull_copiers > 0 ? pull_copiers
+                      : ctx->copy_wgs > 0 ? std::min(ctx->copy_wgs, grid) : grid;
   const int64_t per_chunk = std::max<int64_t>(1, int64_t(copiers) / std::max<int64_t>(int64_t(n_order), 1));
   const int64_t autop =
       std::max<int64_t>(((g.chunk_bytes + per_chunk - 1) / per_chunk + 4095) / 4096 * 4096, 16384);
@@ -383,7 +387,7 @@ void fill_copies(agg_ctx* ctx, GemmArgs& g, const ChunkCopy& cc, uint32_t* flags
   g.copy_cps = cc.cps;
   // default: every workgroup copies first. A grid of one tile per workgroup finishes at the last
   // tile's start plus one tile time, and the copy ends soonest with every workgroup on it.
-  g.copy_wgs = ctx->copy_wgs > 0 ? std::min(ctx->copy_wgs, grid) : grid;
+  g.copy_wgs = copiers;
   g.copy_delays = delays ? 1 : 0;
 }
 
@@ -398,9 +402,13 @@ void attach_trace(agg_ctx* ctx, GemmArgs& g, int64_t tiles) {
 // `tiles_on` keeps the GEMM tiles (without them: a copy-only grid of one workgroup per CU).
 int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int dtype, int epi,
               int grid, const ChunkCopy& cc, uint32_t* flags, size_t n_order, bool delays,
-              int world, uint32_t epoch, bool copies, bool tiles_on, bool timed) {
+              int world, uint32_t epoch, bool copies, bool tiles_on, bool timed, int pull_copiers = 0) {
   GemmArgs h = g;
   int gr = grid;
+  // pull only where tiles and copies share the launch: the grid gains the copiers
+  const bool pull = pull_copiers > 0 && copies && tiles_on;
+  h.pull = pull ? 1 : 0;
+  if (pull) gr = grid + pull_copiers;
   if (!tiles_on) {
     h.n_row_tiles = 0;
     h.n_col_tiles = 0;
@@ -415,7 +423,7 @@ int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int
   }
   if (copies) {
     h.epoch = epoch;
-    fill_copies(ctx, h, cc, flags, n_order, delays, world, gr);
+    fill_copies(ctx, h, cc, flags, n_order, delays, world, gr, pull ? pull_copiers : 0);
   } else {
     h.copy_jobs = 0;
   }
@@ -625,6 +633,14 @@ extern "C" int agg_ctx_set_producer(agg_ctx* ctx, int kind, int copy_wgs, int pi
   return AGG_OK;
 }
 
+extern "C" int agg_ctx_set_pull(agg_ctx* ctx, int pull) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (pull < AGG_PULL_AUTO || pull > AGG_PULL_ON) return fail(AGG_E_ARG, "unknown pull mode %d", pull);
+  ctx->pull = pull;
+  return AGG_OK;
+}
+
 extern "C" int agg_ctx_set_split(agg_ctx* ctx, int ksplit) {
   clear_error();
   if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
@@ -801,11 +817,22 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
   if (cu) {
     if (chunks)
       if (int rc = upload_schedule(ctx, s, ord, delay_us)) return rc;
+    // pull: an overlapped call whose row tiles each lie inside one shard, with compute units to
+    // spare for the copiers, reads the remote rows straight from the peers' blocks (automatic
+    // for small gathers, where the chunk copy's latency would otherwise be exposed)
+    int pull_copiers = 0;
+    if (kernel && chunks && mode == AGG_OVERLAP && ctx->pull != AGG_PULL_OFF && delay_us == nullptr &&
+        m_shard % ts.bm == 0) {
+      const int64_t remote = int64_t(world - 1) * m_shard * cc.row_bytes;
+      const int64_t spare = int64_t(ctx->cus) - grid;
+      if (spare >= 1 && (ctx->pull == AGG_PULL_ON || remote <= kPullMaxBytes))
+        pull_copiers = int(std::min<int64_t>(spare, std::max<int64_t>(1, (remote + 16383) / 16384)));
+    }
     return schedule_cu(ctx, mode, s, S(copy_stream), kernel, chunks,
                        [&](bool copies, bool tiles_on, bool timed) {
                          return launch_cu(ctx, s, g, ts, dtype, kEpiAllGather, grid, cc, flags,
                                           ord.size(), delay_us != nullptr, world, epoch, copies,
-                                          tiles_on, timed);
+                                          tiles_on, timed, pull_copiers);
                        });
   }
   auto launch = [&]() -> int {

@@ -66,6 +66,10 @@ struct GemmArgs {
   int copy_wgs;                         // workgroups that take copy jobs first (<= grid)
   int copy_cps;                         // chunks per peer block
   int copy_delays;                      // nonzero: honour the cumulative delays in scratch
+  // AG pull: tiles read remote rows straight from the peers' blocks (no chunk wait); the copy
+  // jobs (which still fill the gather buffer and release the flags) go to the last copy_wgs
+  // workgroups, which claim tiles only after copying
+  int pull;
 };
 
 // Launch the persistent kernel instantiated for (bm, bn, dtype, epilogue) with `grid`

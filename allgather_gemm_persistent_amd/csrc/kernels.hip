@@ -198,11 +198,12 @@ __device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __re
 
 // The in-kernel producer. Job j*pieces + q copies piece q of the chunk at arrival position j;
 // the job that completes a chunk (all its pieces copied and released) stores the epoch into the
-// chunk's flag. Copying workgroup w takes jobs w, w + copy_wgs, w + 2*copy_wgs, ...: a static
+// chunk's flag. Copying workgroup w (0-based among the copiers) takes jobs w, w + copy_wgs,
+// w + 2*copy_wgs, ...: a static
 // round robin in arrival order, so no job counter is contended and chunks complete roughly in
 // arrival order. With delays, job j*pieces + q starts no earlier than the j-th cumulative delay
 // after the first copying workgroup started.
-__device__ inline void produce_chunks(const GemmArgs& a, int tid) {
+__device__ inline void produce_chunks(const GemmArgs& a, int tid, uint32_t first_job) {
   const uint32_t* order = a.scratch + kScrOrder;
   // every value that decides a branch around a barrier is made visibly uniform
   // (readfirstlane): otherwise the compiler may treat the loop exit as divergent and lay the
@@ -217,7 +218,7 @@ __device__ inline void produce_chunks(const GemmArgs& a, int tid) {
     const uint32_t prev = atomicCAS(a.scratch + kScrCopyT0, 0u, now);
     t0 = prev ? prev : now;
   }
-  for (uint32_t job = blockIdx.x; job < jobs; job += stride) {
+  for (uint32_t job = first_job; job < jobs; job += stride) {
     const uint32_t j = job / pieces, q = job - j * pieces;
     const int c = (int)__builtin_amdgcn_readfirstlane(order[j]);
     const int p = c / a.copy_cps, jl = c - p * a.copy_cps;
@@ -432,8 +433,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   // copy_wgs workgroups move the remote chunks (so the claim is off the path from the end of
   // the copy to the first tile), and every workgroup computes tiles, claiming the next one after
   // each
-  claim_tile();
-  if (a.copy_jobs && (int)blockIdx.x < a.copy_wgs) produce_chunks(a, tid);
+  // (pull: the copiers are the last copy_wgs workgroups and take no tile before copying, so the
+  // tiles start at once on the others)
+  const bool pull = EPI == kEpiAllGather && a.pull;
+  const int first_copier = pull ? (int)gridDim.x - a.copy_wgs : 0;
+  const bool copier = a.copy_jobs && (int)blockIdx.x >= first_copier &&
+                      (int)blockIdx.x < first_copier + a.copy_wgs;
+  if (!(pull && copier)) claim_tile();
+  if (copier) produce_chunks(a, tid, blockIdx.x - first_copier);
+  if (pull && copier) claim_tile();
 
   for (;; claim_tile()) {   // (an abandoned tile's `continue` claims the next one too)
     // uniform for the compiler too (see produce_chunks)
@@ -462,7 +470,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     // ---- wait for the chunks this tile's rows need
     if (wave == 0) {
       uint32_t seen = 0xFFFFFFFFu;
-      const bool ok = wait_chunks<EPI>(a, lo, hi, block, seen);
+      const bool ok = pull || wait_chunks<EPI>(a, lo, hi, block, seen);
       if (lane == 0) {
         s_ok = ok;
         if (trec) { trec[3] = seen; trec[6] = wall_ticks(); }
@@ -496,7 +504,20 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       }
     }
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const u32x4 da = buffer_desc(a.a, (uint32_t)(a.M * kbytes));
+    u32x4 da = buffer_desc(a.a, (uint32_t)(a.M * kbytes));
+    if (pull) {
+      // a remote row tile (never spanning two shards) reads its peer's block: rebase the A
+      // offsets from gather-buffer rows to block rows
+      const int64_t ms = (int64_t)a.chunk_rows * a.cps;
+      const int p = (int)(lo / ms);
+      if (p != a.rank) {
+        da = buffer_desc(a.peer[p], (uint32_t)(ms * kbytes));
+        const uint32_t shift = (uint32_t)((int64_t)p * ms * kbytes);
+#pragma unroll
+        for (int j = 0; j < NA; ++j)
+          if (base[j] != kOutOfRange) base[j] -= shift;
+      }
+    }
     const u32x4 db = buffer_desc(a.b, (uint32_t)(a.N * kbytes));
     const uint32_t lds0 = lds_addr(stages) + (uint32_t)wave_u * 1024u;
     // load j of slice t (j < NI): A rows for j < NA, else B rows

@@ -133,6 +133,24 @@ enum {
  * count. */
 int agg_ctx_set_producer(agg_ctx* ctx, int kind, int copy_wgs, int piece_kib);
 
+/* Pull modes of ag_gemm (AGG_OVERLAP calls under AGG_PRODUCER_CU without delays). */
+enum {
+  AGG_PULL_AUTO = 0,   /* pull when the remote rows total at most 4 MiB (default) */
+  AGG_PULL_OFF = 1,    /* always push: tiles wait for their chunks' flags */
+  AGG_PULL_ON = 2      /* pull whenever it applies */
+};
+
+/* Select the pull mode of later ag_gemm calls. In a pulled call the tiles read remote rows
+ * straight from the peers' blocks (peer_src; in a multi-GPU setting, loads over the GPU links)
+ * instead of waiting for their chunks to reach the gather buffer; the same launch still copies
+ * every remote chunk into `gather` and releases its flag, on extra workgroups that take no tile
+ * before they finish copying. It applies when every row tile lies inside one shard (m_shard a
+ * multiple of the tile height) and fewer tiles than compute units leave room for the copiers;
+ * otherwise the call pushes. Results are identical either way. The pages' overlap puts a
+ * chunk's transfer before its tiles; pulling takes that transfer off the tiles' path for small
+ * gathers, whose cost is latency rather than bandwidth. AGG_E_ARG for an unknown mode. */
+int agg_ctx_set_pull(agg_ctx* ctx, int pull);
+
 /* CUs the persistent grid leaves free in AGG_OVERLAP mode (default 32, four per XCD), where
  * the producer's copies and flag writes must run beside it: in the HIP runtime shipped with
  * torch several of them execute as runtime kernels and need a CU. 0..CUs-1. */

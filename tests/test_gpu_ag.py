@@ -140,6 +140,8 @@ def test_trace_each_tile_once_and_flags_seen(gpu, producer):
     shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=51)
     w = AgWorkload(world, rank, shards, b, chunk_rows=cr, tile=(64, 64), producer=producer)
     try:
+        if producer == "cu":
+            B.agg_ctx_set_pull(w.ctx, "off")        # the flag waits are what this test traces
         tiles = (world * ms // 64) * (n // 64)
         buf = torch.zeros(tiles * 8, dtype=torch.int32, device="cuda")
         B.agg_set_trace(w.ctx, buf, buf.numel() * 4)
@@ -164,6 +166,42 @@ def test_trace_each_tile_once_and_flags_seen(gpu, producer):
         for lst in np.unique(rec[:, 0]):
             sel = rec[rec[:, 0] == lst]
             assert len(np.unique(sel[:, 1])) == len(sel)
+    finally:
+        w.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("tile", [(64, 64), (128, 64), (128, 128), (256, 224)])
+@pytest.mark.parametrize("rank", [0, 2])
+def test_pull_matches_push_bitexact(gpu, dtype, tile, rank):
+    """Pulled calls (tiles read remote rows from the peers' blocks while extra workgroups fill
+    the gather buffer) give the same bits as pushed and serialized calls, the same gather
+    buffer and the same flags, and match the oracle."""
+    world, cr, k, n = 3, 64, (320 if dtype == "bf16" else 384), 200
+    ms = tile[0] * 2
+    shards, b, sa, sb = small_ag_data(world, ms, k, n, dtype, seed=91)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, dtype=dtype, scale_a=sa, scale_b=sb,
+                   tile=tile)
+    try:
+        order = inputs.seeded_order(world, rank, ms // cr, 5)
+        outs = {}
+        for pull, mode in (("on", "overlap"), ("off", "overlap"), ("on", "serial")):
+            B.agg_ctx_set_pull(w.ctx, pull)
+            w.c.zero_()
+            w.gather[[r for r in range(world * ms) if r // ms != rank]] = 0
+            w.run(mode, order=order)
+            assert w.status() == (0, -1)
+            outs[(pull, mode)] = w.c.clone()
+            assert np.array_equal(raw(w.gather), O.gather_ref([raw(s) for s in shards])), (pull, mode)
+            flags = w.flags.cpu().numpy().astype(np.uint32)
+            e = B.agg_ctx_epoch(w.ctx)
+            cps = ms // cr
+            for c in range(world * cps):
+                assert flags[c] == (0 if c // cps == rank else e), (pull, mode, c)
+        ref = outs[("on", "overlap")]
+        for key, c in outs.items():
+            assert bits_equal(c, ref), key
+        assert_close(to_f64(ref), _oracle_c(shards, b, dtype, sa, sb), _tol(dtype), "C")
     finally:
         w.close()
 
