@@ -822,7 +822,7 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
     // for small gathers, where the chunk copy's latency would otherwise be exposed)
     int pull_copiers = 0;
     if (kernel && chunks && mode == AGG_OVERLAP && ctx->pull != AGG_PULL_OFF && delay_us == nullptr &&
-        m_shard % ts.bm == 0) {
+        (m_shard % ts.bm == 0 || (ts.bm <= 128 && m_shard % 16 == 0))) {
       const int64_t remote = int64_t(world - 1) * m_shard * cc.row_bytes;
       const int64_t spare = int64_t(ctx->cus) - grid;
       if (spare >= 1 && (ctx->pull == AGG_PULL_ON || remote <= kPullMaxBytes))

@@ -504,18 +504,37 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       }
     }
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    // A operand: one descriptor for the tile, or (pull, tiles of up to 128 rows) one per A load,
+    // whose 16-row group lies in one shard when shards are multiples of 16 rows
+    constexpr bool kGroupPull = NA <= 2;
     u32x4 da = buffer_desc(a.a, (uint32_t)(a.M * kbytes));
-    if (pull) {
-      // a remote row tile (never spanning two shards) reads its peer's block: rebase the A
-      // offsets from gather-buffer rows to block rows
-      const int64_t ms = (int64_t)a.chunk_rows * a.cps;
-      const int p = (int)(lo / ms);
-      if (p != a.rank) {
-        da = buffer_desc(a.peer[p], (uint32_t)(ms * kbytes));
-        const uint32_t shift = (uint32_t)((int64_t)p * ms * kbytes);
+    u32x4 dag[kGroupPull ? NA : 1];
 #pragma unroll
-        for (int j = 0; j < NA; ++j)
-          if (base[j] != kOutOfRange) base[j] -= shift;
+    for (int j = 0; j < (kGroupPull ? NA : 1); ++j) dag[j] = da;
+    if (pull) {
+      // remote rows are read from the peer's block: rebase those A offsets from gather-buffer
+      // rows to block rows
+      const int64_t ms = (int64_t)a.chunk_rows * a.cps;
+      if constexpr (kGroupPull) {
+#pragma unroll
+        for (int j = 0; j < NA; ++j) {
+          const int64_t g0 = lo + (int64_t)(j * 4 + wave_u) * 16;   // first row of the group
+          const int p = (int)(g0 / ms);
+          if (g0 < a.M && p != a.rank) {
+            dag[j] = buffer_desc(a.peer[p], (uint32_t)(ms * kbytes));
+            if (base[j] != kOutOfRange) base[j] -= (uint32_t)((int64_t)p * ms * kbytes);
+          }
+        }
+      } else {
+        // (a tile of more than 128 rows is pulled only when it lies inside one shard)
+        const int p = (int)(lo / ms);
+        if (p != a.rank) {
+          da = buffer_desc(a.peer[p], (uint32_t)(ms * kbytes));
+          const uint32_t shift = (uint32_t)((int64_t)p * ms * kbytes);
+#pragma unroll
+          for (int j = 0; j < NA; ++j)
+            if (base[j] != kOutOfRange) base[j] -= shift;
+        }
       }
     }
     const u32x4 db = buffer_desc(a.b, (uint32_t)(a.N * kbytes));
@@ -527,7 +546,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       const uint32_t oob = (uint32_t)((int)(tk + gk - kend) >> 31) ^ 0xFFFFFFFFu;
       const uint32_t kmask = oob & kOutOfRange;
       const uint32_t st = lds0 + (uint32_t)(t & (kStages - 1)) * DSTAGE;
-      lds_dma_load(j < NA ? da : db, st + j * 4096u, (base[j] + tk) | kmask);
+      lds_dma_load(j < NA ? (kGroupPull ? dag[j < NA ? j : 0] : da) : db, st + j * 4096u,
+                   (base[j] + tk) | kmask);
     };
     auto issue = [&](int t) {
 #pragma unroll

@@ -144,8 +144,9 @@ enum {
  * straight from the peers' blocks (peer_src; in a multi-GPU setting, loads over the GPU links)
  * instead of waiting for their chunks to reach the gather buffer; the same launch still copies
  * every remote chunk into `gather` and releases its flag, on extra workgroups that take no tile
- * before they finish copying. It applies when every row tile lies inside one shard (m_shard a
- * multiple of the tile height) and fewer tiles than compute units leave room for the copiers;
+ * before they finish copying. It applies when the tile's rows can be read shard by shard (m_shard
+ * a multiple of the tile height, or, for tiles of up to 128 rows, of 16 rows) and fewer tiles
+ * than compute units leave room for the copiers;
  * otherwise the call pushes. Results are identical either way. The pages' overlap puts a
  * chunk's transfer before its tiles; pulling takes that transfer off the tiles' path for small
  * gathers, whose cost is latency rather than bandwidth. AGG_E_ARG for an unknown mode. */

@@ -206,6 +206,39 @@ def test_pull_matches_push_bitexact(gpu, dtype, tile, rank):
         w.close()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("tile", [(64, 64), (128, 64), (128, 128)])
+@pytest.mark.parametrize("world,ms,rank", [(8, 16, 0), (8, 16, 5), (3, 48, 1)])
+def test_pull_by_row_groups_matches_push_bitexact(gpu, dtype, tile, world, ms, rank):
+    """Shards of a multiple of 16 rows inside taller tiles (the decode shape): each 16-row load
+    group of a pulled tile reads its own shard's block. Same bits, gather buffer and flags as a
+    pushed call, and the oracle."""
+    cr, k, n = 16, (512 if dtype == "bf16" else 1024), 200
+    shards, b, sa, sb = small_ag_data(world, ms, k, n, dtype, seed=93)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, dtype=dtype, scale_a=sa, scale_b=sb,
+                   tile=tile)
+    try:
+        order = inputs.seeded_order(world, rank, ms // cr, 7)
+        outs = []
+        for pull in ("on", "off"):
+            B.agg_ctx_set_pull(w.ctx, pull)
+            w.c.zero_()
+            w.gather[[r for r in range(world * ms) if r // ms != rank]] = 0
+            w.run("overlap", order=order)
+            assert w.status() == (0, -1)
+            outs.append(w.c.clone())
+            assert np.array_equal(raw(w.gather), O.gather_ref([raw(s) for s in shards])), pull
+            flags = w.flags.cpu().numpy().astype(np.uint32)
+            e = B.agg_ctx_epoch(w.ctx)
+            cps = ms // cr
+            for c in range(world * cps):
+                assert flags[c] == (0 if c // cps == rank else e), (pull, c)
+        assert bits_equal(outs[0], outs[1])
+        assert_close(to_f64(outs[0]), _oracle_c(shards, b, dtype, sa, sb), _tol(dtype), "C")
+    finally:
+        w.close()
+
+
 def test_withheld_chunks_time_out_then_recover(gpu):
     """Flags that never reach the epoch make the waits give up (status, failed flag id) instead
     of hanging; after agg_ctx_reset the next call is correct."""
