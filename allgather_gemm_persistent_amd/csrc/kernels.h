@@ -14,7 +14,7 @@ constexpr int kScrLists = 0;       // claim-list counters, one per XCD (<= 16)
 constexpr int kScrDone = 16;       // workgroups that finished the current launch
 constexpr int kScrStatus = 17;     // bit 0: a flag wait gave up
 constexpr int kScrFailed = 18;     // first flag index that timed out (0xFFFFFFFF = none)
-// (word 19 is unused)
+constexpr int kScrCopyNext = 19;   // in-kernel producer: next copy job
 constexpr int kScrCopyT0 = 20;     // in-kernel producer: wall clock of the first job (delays)
 constexpr int kScrRsCount = 64;    // ReduceScatter per-send-chunk completion counters
 constexpr int kScrPieces = kScrRsCount + AGG_MAX_CHUNKS;   // per-chunk copied-piece counters

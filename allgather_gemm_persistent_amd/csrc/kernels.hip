@@ -198,12 +198,11 @@ __device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __re
 
 // The in-kernel producer. Job j*pieces + q copies piece q of the chunk at arrival position j;
 // the job that completes a chunk (all its pieces copied and released) stores the epoch into the
-// chunk's flag. Copying workgroup w (0-based among the copiers) takes jobs w, w + copy_wgs,
-// w + 2*copy_wgs, ...: a static
-// round robin in arrival order, so no job counter is contended and chunks complete roughly in
-// arrival order. With delays, job j*pieces + q starts no earlier than the j-th cumulative delay
-// after the first copying workgroup started.
-__device__ inline void produce_chunks(const GemmArgs& a, int tid, uint32_t first_job) {
+// chunk's flag. Jobs are taken from a shared counter in arrival order, so chunks complete
+// roughly in arrival order and the jobs go to whichever workgroups are running (one that has not
+// started yet holds none back). With delays, job j*pieces + q starts no earlier than the j-th
+// cumulative delay after the first copying workgroup started.
+__device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job) {
   const uint32_t* order = a.scratch + kScrOrder;
   // every value that decides a branch around a barrier is made visibly uniform
   // (readfirstlane): otherwise the compiler may treat the loop exit as divergent and lay the
@@ -211,14 +210,27 @@ __device__ inline void produce_chunks(const GemmArgs& a, int tid, uint32_t first
   // barriers between the waves
   const uint32_t jobs = __builtin_amdgcn_readfirstlane(a.copy_jobs);
   const uint32_t pieces = __builtin_amdgcn_readfirstlane((uint32_t)a.pieces);
-  const uint32_t stride = __builtin_amdgcn_readfirstlane((uint32_t)a.copy_wgs);
+  // the next job comes from a shared counter; once it is past the last job a plain load says so
+  // (one uncontended read per workgroup at the end of the copy instead of an atomic add)
+  auto next_job = [&]() -> uint32_t {
+    if (tid == 0) {
+      uint32_t j = jobs;
+      if (__hip_atomic_load(a.scratch + kScrCopyNext, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < jobs)
+        j = atomicAdd(a.scratch + kScrCopyNext, 1u);
+      s_job[0] = (int)j;
+    }
+    __syncthreads();
+    const uint32_t job = (uint32_t)__builtin_amdgcn_readfirstlane(s_job[0]);
+    __syncthreads();
+    return job;
+  };
   uint32_t t0 = 0;
   if (a.copy_delays && tid == 0) {
     const uint32_t now = wall_ticks() | 1u;   // never 0, which marks "unset"
     const uint32_t prev = atomicCAS(a.scratch + kScrCopyT0, 0u, now);
     t0 = prev ? prev : now;
   }
-  for (uint32_t job = first_job; job < jobs; job += stride) {
+  for (uint32_t job = next_job(); job < jobs; job = next_job()) {
     const uint32_t j = job / pieces, q = job - j * pieces;
     const int c = (int)__builtin_amdgcn_readfirstlane(order[j]);
     const int p = c / a.copy_cps, jl = c - p * a.copy_cps;
@@ -411,6 +423,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t stages[kStages * DSTAGE];
   __shared__ int s_tile[4];
   __shared__ int s_ok;
+  __shared__ int s_job;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WNW, wn = wave % WNW;
@@ -440,7 +453,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   const bool copier = a.copy_jobs && (int)blockIdx.x >= first_copier &&
                       (int)blockIdx.x < first_copier + a.copy_wgs;
   if (!(pull && copier)) claim_tile();
-  if (copier) produce_chunks(a, tid, blockIdx.x - first_copier);
+  if (copier) produce_chunks(a, tid, &s_job);
   if (pull && copier) claim_tile();
 
   for (;; claim_tile()) {   // (an abandoned tile's `continue` claims the next one too)
@@ -960,8 +973,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   if (__builtin_amdgcn_readfirstlane(s_ok)) {
     if (tid < kMaxLists) __hip_atomic_store(a.scratch + kScrLists + tid, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (a.copy_jobs) {
-      if (tid == 0)
+      if (tid == 0) {
+        __hip_atomic_store(a.scratch + kScrCopyNext, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(a.scratch + kScrCopyT0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       for (uint32_t i = tid; i * (uint32_t)a.pieces < a.copy_jobs; i += kThreads)
         __hip_atomic_store(a.scratch + kScrPieces + a.scratch[kScrOrder + i], 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
