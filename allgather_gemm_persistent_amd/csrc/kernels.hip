@@ -29,6 +29,8 @@
 // stores.
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace agg {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -38,7 +40,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
+constexpr int kWaveLanes = 64;
 // word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle)
 constexpr int kBufferFlags = 0x00020000;
 // a buffer offset past every operand (operands are limited to 2^31 bytes)
@@ -92,6 +94,27 @@ __device__ inline void mfma_fp8(f32x16& acc, const i32x8& b, const i32x8& a) {
   asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
                : "+a"(acc) : "v"(b), "v"(a), "v"(127));
 }
+
+// The two above followed by one direct-to-LDS load (as lds_dma_load below), in one asm statement
+// so that the MFMA sits between the M0 write and the load: the wait state the load needs after
+// an M0 write, without an s_nop.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void mfma_bf16_dma(f32x4& acc, const u32x4& b, const u32x4& a, const u32x4& desc,
+                                     uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %3\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\t"
+               "buffer_load_dwordx4 %4, %5, 0 offen lds"
+               : "+a"(acc) : "v"(b), "v"(a), "s"(lds_base), "v"(voff), "s"(desc) : "memory", "m0");
+}
+
+__device__ inline void mfma_fp8_dma(f32x16& acc, const i32x8& b, const i32x8& a, const u32x4& desc,
+                                    uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %3\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %6, %6 op_sel_hi:[0,0,0]\n\t"
+               "buffer_load_dwordx4 %4, %5, 0 offen lds"
+               : "+a"(acc) : "v"(b), "v"(a), "s"(lds_base), "v"(voff), "s"(desc), "v"(127)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // 32 wait states: more than any MFMA result or operand hazard needs (about 20 for a 16-pass op).
 // Every accumulator then passes through an empty asm placed after the nops, so that nothing the
@@ -150,10 +173,11 @@ constexpr int kStoreSystemCoherent = 1 | 16;
 // stores in issue order, so a load wait never waits for the stores issued after it). The
 // source (a peer's block) is read once: non-temporal loads; the stores write through. On return
 // every store of the calling thread has completed.
+template <int NT>
 __device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __restrict__ src,
                                   int64_t bytes, int tid) {
   constexpr int U = 16;
-  constexpr int64_t kStep = (int64_t)U * kThreads;
+  constexpr int64_t kStep = (int64_t)U * NT;
   const int64_t n16 = bytes >> 4;
   const u32x4* s = reinterpret_cast<const u32x4*>(src);
   const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, 0, (int)bytes, kBufferFlags);
@@ -162,11 +186,11 @@ __device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __re
   };
   auto load = [&](u32x4 (&v)[U], int64_t g) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(s + g + u * kThreads);
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(s + g + u * NT);
   };
   auto store = [&](const u32x4 (&v)[U], int64_t g) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) put(g + u * kThreads, v[u]);
+    for (int u = 0; u < U; ++u) put(g + u * NT, v[u]);
   };
   // G full groups (the same count for every thread), then a per-vector tail
   const int64_t G = n16 / kStep;
@@ -192,7 +216,7 @@ __device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __re
       i += kStep;
     }
   }
-  for (; i < n16; i += kThreads) put(i, __builtin_nontemporal_load(s + i));
+  for (; i < n16; i += NT) put(i, __builtin_nontemporal_load(s + i));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -202,6 +226,7 @@ __device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __re
 // roughly in arrival order and the jobs go to whichever workgroups are running (one that has not
 // started yet holds none back). With delays, job j*pieces + q starts no earlier than the j-th
 // cumulative delay after the first copying workgroup started.
+template <int NT>
 __device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job) {
   const uint32_t* order = a.scratch + kScrOrder;
   // every value that decides a branch around a barrier is made visibly uniform
@@ -242,7 +267,7 @@ __device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job) {
     const int64_t lo = (int64_t)q * a.piece_bytes;
     const int64_t hi = lo + a.piece_bytes < a.chunk_bytes ? lo + a.piece_bytes : a.chunk_bytes;
     const int64_t base = (int64_t)jl * a.chunk_bytes;
-    copy_piece(a.sym + ((int64_t)p * a.copy_cps) * a.chunk_bytes + base + lo,
+    copy_piece<NT>(a.sym + ((int64_t)p * a.copy_cps) * a.chunk_bytes + base + lo,
                a.peer[p] + base + lo, hi - lo, tid);
     // every thread's write-through stores have completed in memory (copy_piece waited for
     // them), so the count and the flag need no cache maintenance: a relaxed count per piece,
@@ -401,14 +426,18 @@ __device__ bool wait_chunks(const GemmArgs& a, int64_t lo, int64_t hi, int block
   return true;
 }
 
-template <int BM, int BN, int DT, int EPI>
-__global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
+// NW waves per workgroup: 4 (one per SIMD, 2 x 2 over the tile) or 8 (two per SIMD, 4 x 2, so
+// that each SIMD's MFMA pipe has a second wave to issue from while one waits on LDS or memory).
+template <int BM, int BN, int DT, int EPI, int NW>
+__global__ void __launch_bounds__(NW * kWaveLanes, 1) gemm_kernel(const GemmArgs a) {
+  constexpr int NT = NW * kWaveLanes;
   constexpr bool FP8 = (DT == AGG_FP8_E4M3);
   constexpr bool kSplitTiles = BM * BN <= 128 * 128;
-  // 2 x 2 waves over 16x16x32 bf16 or 32x32x64 fp8 MFMA blocks (fp8: 4 x 1 when half the
-  // tile's columns are not whole 32-column blocks)
-  constexpr int WMW = (!FP8 || (BN / 2) % 32 == 0) ? 2 : 4;   // waves along M
-  constexpr int WNW = 4 / WMW;
+  static_assert(NW == 4 || (NW == 8 && !FP8 && BM == 256 && BN >= 224), "8 waves: big bf16 tiles");
+  // 2 x 2 (4 x 2 with 8) waves over 16x16x32 bf16 or 32x32x64 fp8 MFMA blocks (fp8: 4 x 1 when
+  // half the tile's columns are not whole 32-column blocks)
+  constexpr int WMW = NW == 8 ? 4 : (!FP8 || (BN / 2) % 32 == 0) ? 2 : 4;   // waves along M
+  constexpr int WNW = NW / WMW;
   constexpr int WTM = BM / WMW, WTN = BN / WNW;        // wave tile
   constexpr int BLK = FP8 ? 32 : 16;                   // MFMA output block edge
   static_assert(WTM % BLK == 0 && WTN % BLK == 0, "wave tile");
@@ -453,7 +482,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   const bool copier = a.copy_jobs && (int)blockIdx.x >= first_copier &&
                       (int)blockIdx.x < first_copier + a.copy_wgs;
   if (!(pull && copier)) claim_tile();
-  if (copier) produce_chunks(a, tid, &s_job);
+  if (copier) produce_chunks<NT>(a, tid, &s_job);
   if (pull && copier) claim_tile();
 
   for (;; claim_tile()) {   // (an abandoned tile's `continue` claims the next one too)
@@ -499,14 +528,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     // ---- K loop: four LDS stages of 64-byte K slices, filled by direct-to-LDS buffer loads
     // (out-of-range rows and the K tail read zeros through the buffer descriptor's range check)
     f32x4 acc[FM][FN];
-    constexpr int NI = (BM + BNP) / 64;      // load instructions per wave per stage
-    constexpr int NA = BM / 64;              // the first NA of them fetch A rows
+    constexpr int NI = (BM + BNP) / (16 * NW);   // load instructions per wave per stage
+    constexpr int NA = BM / (16 * NW);           // the first NA of them fetch A rows
+    static_assert(BM % (16 * NW) == 0 && BNP % (16 * NW) == 0, "whole 16-row groups per wave");
     // lane's chunk: rows of a 16-row group are lane/4, chunk position lane%4
     const uint32_t gk = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) << 4);
     uint32_t base[NI];
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const int r = (j * 4 + wave) * 16 + (lane >> 2);   // LDS row
+      const int r = (j * NW + wave) * 16 + (lane >> 2);  // LDS row
       if (j < NA) {
         const int64_t gr = lo + r;
         base[j] = gr < a.M ? (uint32_t)gr * (uint32_t)kbytes + gk : kOutOfRange;
@@ -519,7 +549,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     // A operand: one descriptor for the tile, or (pull, tiles of up to 128 rows) one per A load,
     // whose 16-row group lies in one shard when shards are multiples of 16 rows
-    constexpr bool kGroupPull = NA <= 2;
+    constexpr bool kGroupPull = BM <= 128;
     u32x4 da = buffer_desc(a.a, (uint32_t)(a.M * kbytes));
     u32x4 dag[kGroupPull ? NA : 1];
 #pragma unroll
@@ -531,7 +561,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       if constexpr (kGroupPull) {
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
-          const int64_t g0 = lo + (int64_t)(j * 4 + wave_u) * 16;   // first row of the group
+          const int64_t g0 = lo + (int64_t)(j * NW + wave_u) * 16;  // first row of the group
           const int p = (int)(g0 / ms);
           if (g0 < a.M && p != a.rank) {
             dag[j] = buffer_desc(a.peer[p], (uint32_t)(ms * kbytes));
@@ -552,109 +582,166 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     }
     const u32x4 db = buffer_desc(a.b, (uint32_t)(a.N * kbytes));
     const uint32_t lds0 = lds_addr(stages) + (uint32_t)wave_u * 1024u;
-    // load j of slice t (j < NI): A rows for j < NA, else B rows
-    auto issue_one = [&](int t, int j) {
-      const uint32_t tk = (uint32_t)t * kSliceBytes;
-      // past the K end: set the offset's top bit (out of range, reads zero) without a branch
-      const uint32_t oob = (uint32_t)((int)(tk + gk - kend) >> 31) ^ 0xFFFFFFFFu;
-      const uint32_t kmask = oob & kOutOfRange;
-      const uint32_t st = lds0 + (uint32_t)(t & (kStages - 1)) * DSTAGE;
-      lds_dma_load(j < NA ? (kGroupPull ? dag[j < NA ? j : 0] : da) : db, st + j * 4096u,
-                   (base[j] + tk) | kmask);
+    // Load j of a slice (j < NI): A rows for j < NA, else B rows. The LDS stage of slice t is
+    // (t - t_lo) % 4; the main loop runs four slices per trip, so every stage is a constant.
+    auto desc_of = [&](int j) -> const u32x4& {
+      return j < NA ? (kGroupPull ? dag[j < NA ? j : 0] : da) : db;
     };
-    auto issue = [&](int t) {
-#pragma unroll
-      for (int j = 0; j < NI; ++j) issue_one(t, j);
+    auto m0_of = [&](int sg, int j) { return lds0 + (uint32_t)sg * DSTAGE + (uint32_t)j * (NW * 1024u); };
+    // K byte offset of load j of slice t. Slices below t_safe lie wholly inside the part's K
+    // range: a plain offset. Otherwise (`masked`) the offset's top bit is set past the K end
+    // (out of range: reads zero), lane by lane, since a slice may straddle the end.
+    const int t_safe = (int)(kend / kSlice);
+    auto voff_of = [&](auto masked, int t, int j) -> uint32_t {
+      const uint32_t tk = (uint32_t)t * kSliceBytes;
+      if constexpr (decltype(masked)::value) {
+        const uint32_t oob = (uint32_t)((int)(tk + gk - kend) >> 31) ^ 0xFFFFFFFFu;
+        return (base[j] + tk) | (oob & kOutOfRange);
+      } else {
+        return base[j] + tk;
+      }
+    };
+    auto issue_one = [&](auto masked, int t, int sg, int j) {
+      lds_dma_load(desc_of(j), m0_of(sg, j), voff_of(masked, t, j));
     };
     constexpr int NH = NI / 2;                 // loads of a slice issued in the earlier half
+    // The slice schedule, for both dtypes: RM x CN MFMA blocks per wave and slice, operand
+    // fragments of type F read from LDS by lda(stage, block row) / ldb(stage, block column).
+    // One K slice t in stage U, its B fragments in fbc and its first A fragment in fa (requested
+    // during the previous slice). Stage U is refilled with slice t+4 by NI direct-to-LDS loads,
+    // the first NH of them in the second half of slice t and the rest in the first half of slice
+    // t+1, so that every half slice carries about NI/2 loads between its MFMAs and the load path
+    // never takes a burst. First half of slice t: the remaining A fragments of slice t are
+    // requested row by row, and the loads NH..NI-1 of slice t+3 go between the MFMAs. Then the
+    // waves meet (slice t+1 has landed everywhere; every wave has read all of slice t), and the
+    // second half spreads slice t+1's B fragments and first A fragment, then the loads 0..NH-1
+    // of slice t+4, between its MFMAs. A load that follows an MFMA shares its asm statement
+    // (mma_dma), so the MFMA is the wait state between the M0 write and the load.
+    auto run_slices = [&](auto& accs, auto fa, auto lda, auto ldb, auto mma, auto mma_dma,
+                          auto rm_, auto cn_, auto lone_) {
+      constexpr int RM = decltype(rm_)::value, CN = decltype(cn_)::value;
+      constexpr bool kLone = decltype(lone_)::value;
+      using F = decltype(fa);
+      constexpr int RB = RM / 2;                 // block rows before the barrier
+      constexpr int S1 = RB * CN, S2 = (RM - RB) * CN;
+      constexpr int E1 = NI - NH, E2 = CN + 1 + NH;
+      static_assert(RM - RB - 1 <= RB, "the A fragments after the barrier are loaded before it");
+      auto slice = [&](auto u_, auto masked, F (&fbc)[CN], F (&fbn)[CN], int t) {
+        constexpr int U = decltype(u_)::value;
+        constexpr int U1 = (U + 1) & 3, U3 = (U + 3) & 3;
+        F far[RM];
+        far[0] = fa;
+        if (S1 == 0) {                            // no MFMA before the barrier: issue plainly
+#pragma unroll
+          for (int e = 0; e < E1; ++e) issue_one(masked, t + 3, U3, NH + e);
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          far[i + 1] = lda(U, i + 1);
+          if (RB + 1 + i < RM) far[RB + 1 + i] = lda(U, RB + 1 + i);
+#pragma unroll
+          for (int j = 0; j < CN; ++j) {
+            const int q = i * CN + j;
+            bool fused = false;
+#pragma unroll
+            for (int e = 0; e < E1; ++e) {
+              if (S1 == 0 || e * S1 / E1 != q) continue;
+              const int jj = NH + e;
+              if (!fused) {
+                mma_dma(accs[i][j], fbc[j], far[i], desc_of(jj), m0_of(U3, jj), voff_of(masked, t + 3, jj));
+                fused = true;
+              } else {
+                issue_one(masked, t + 3, U3, jj);
+              }
+            }
+            if (!fused) mma(accs[i][j], fbc[j], far[i]);
+          }
+        }
+        stage_barrier<2 * NI>();
+#pragma unroll
+        for (int i = RB; i < RM; ++i) {
+#pragma unroll
+          for (int j = 0; j < CN; ++j) {
+            const int q = (i - RB) * CN + j;
+            if (kLone) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+            // the first load of slice t+4 scheduled after this MFMA is fused with it
+            int fuse_e = -1;
+#pragma unroll
+            for (int e = CN + 1; e < E2; ++e)
+              if (fuse_e < 0 && e * S2 / E2 == q) fuse_e = e;
+            if (fuse_e >= 0) {
+              const int jj = fuse_e - CN - 1;
+              mma_dma(accs[i][j], fbc[j], far[i], desc_of(jj), m0_of(U, jj), voff_of(masked, t + 4, jj));
+            } else {
+              mma(accs[i][j], fbc[j], far[i]);
+            }
+#pragma unroll
+            for (int e = 0; e < E2; ++e) {
+              if (e * S2 / E2 != q || e == fuse_e) continue;   // request e goes after MFMA slot e*S2/E2
+              if (e < CN) fbn[e] = ldb(U1, e);
+              else if (e == CN) fa = lda(U1, 0);
+              else issue_one(masked, t + 4, U, e - CN - 1);
+            }
+          }
+        }
+      };
+      if (t_hi > t_lo) {
+        F fb0[CN], fb1[CN];
+        acc_settle(accs);
+        constexpr auto kPlain = std::integral_constant<bool, false>{};
+        constexpr auto kMasked = std::integral_constant<bool, true>{};
+#pragma unroll
+        for (int s = 0; s < 3; ++s)
+#pragma unroll
+          for (int j = 0; j < NI; ++j) issue_one(kMasked, t_lo + s, s, j);
+#pragma unroll
+        for (int j = 0; j < NH; ++j) issue_one(kMasked, t_lo + 3, 3, j);   // the first slice issues the rest
+        stage_barrier<2 * NI + NH>();
+#pragma unroll
+        for (int j = 0; j < CN; ++j) fb0[j] = ldb(0, j);
+        fa = lda(0, 0);
+        // four slices per trip (slices past the part's end read zeros); a trip whose loads
+        // (up to slice t+7) stay below t_safe needs no K-end masks
+        int t = t_lo;
+        for (; t + 7 < t_safe; t += 4) {
+          slice(std::integral_constant<int, 0>{}, kPlain, fb0, fb1, t);
+          slice(std::integral_constant<int, 1>{}, kPlain, fb1, fb0, t + 1);
+          slice(std::integral_constant<int, 2>{}, kPlain, fb0, fb1, t + 2);
+          slice(std::integral_constant<int, 3>{}, kPlain, fb1, fb0, t + 3);
+        }
+        for (; t < t_hi; t += 4) {
+          slice(std::integral_constant<int, 0>{}, kMasked, fb0, fb1, t);
+          slice(std::integral_constant<int, 1>{}, kMasked, fb1, fb0, t + 1);
+          slice(std::integral_constant<int, 2>{}, kMasked, fb0, fb1, t + 2);
+          slice(std::integral_constant<int, 3>{}, kMasked, fb1, fb0, t + 3);
+        }
+        acc_settle(accs);
+        // loads issued past the end land (as zeros) and every wave is done with LDS before the
+        // next tile refills it
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+    };
     if constexpr (!FP8) {
       // ---- bf16: 16x16x32 MFMA blocks, one 16-byte fragment per lane
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      auto load_b1 = [&](int t, int j) {
-        const uint8_t* st = stages + (t & (kStages - 1)) * DSTAGE;
+      auto ldb = [&](int sg, int j) {
         return *reinterpret_cast<const u32x4*>(
-            st + lds64_off(BM + wn * WTN + j * 16 + (lane & 15), lane >> 4));
+            stages + sg * DSTAGE + lds64_off(BM + wn * WTN + j * 16 + (lane & 15), lane >> 4));
       };
-      auto load_b = [&](u32x4 (&fb)[FN], int t) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[j] = load_b1(t, j);
-      };
-      auto load_a = [&](int t, int i) {
-        const uint8_t* st = stages + (t & (kStages - 1)) * DSTAGE;
+      auto lda = [&](int sg, int i) {
         return *reinterpret_cast<const u32x4*>(
-            st + lds64_off(wm * WTM + i * 16 + (lane & 15), lane >> 4));
+            stages + sg * DSTAGE + lds64_off(wm * WTM + i * 16 + (lane & 15), lane >> 4));
       };
-      // One K slice t, its B fragments in fbc and its first A fragment in fa (requested during
-      // the previous slice). Slot t%4 is refilled with slice t+4 by NI direct-to-LDS loads, the
-      // first NH of them in the second half of slice t and the rest in the first half of slice
-      // t+1, so that every half slice carries about NI/2 loads between its MFMAs and the load
-      // path never takes a burst. First half of slice t: the remaining A fragments of slice t
-      // are requested row by row, and the loads NH..NI-1 of slice t+3 go between the MFMAs.
-      // Then the waves meet (slice t+1 has landed everywhere; every wave has read all of slice
-      // t), and the second half spreads slice t+1's B fragments and first A fragment, then the
-      // loads 0..NH-1 of slice t+4, between its MFMAs.
-      constexpr int RB = FM / 2;                 // rows before the barrier (FM >= 2)
-      constexpr int S1 = RB * FN, S2 = (FM - RB) * FN;
-      constexpr int E1 = NI - NH, E2 = FN + 1 + NH;
-      static_assert(FM - RB - 1 <= RB, "the A fragments after the barrier are loaded before it");
-      u32x4 fa;
-      auto slice = [&](u32x4 (&fbc)[FN], u32x4 (&fbn)[FN], int t) {
-        u32x4 far[FM];
-        far[0] = fa;
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          far[i + 1] = load_a(t, i + 1);
-          if (RB + 1 + i < FM) far[RB + 1 + i] = load_a(t, RB + 1 + i);
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            mfma_bf16(acc[i][j], fbc[j], far[i]);
-            const int q = i * FN + j;
-#pragma unroll
-            for (int e = 0; e < E1; ++e)
-              if (e * S1 / E1 == q) issue_one(t + 3, NH + e);
-          }
-        }
-        stage_barrier<2 * NI>();
-#pragma unroll
-        for (int i = RB; i < FM; ++i) {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            mfma_bf16(acc[i][j], fbc[j], far[i]);
-            const int q = (i - RB) * FN + j;
-#pragma unroll
-            for (int e = 0; e < E2; ++e) {
-              if (e * S2 / E2 != q) continue;         // request e goes after MFMA slot e*S2/E2
-              if (e < FN) fbn[e] = load_b1(t + 1, e);
-              else if (e == FN) fa = load_a(t + 1, 0);
-              else issue_one(t + 4, e - FN - 1);
-            }
-          }
-        }
-      };
-      if (t_hi > t_lo) {
-        u32x4 fb0[FN], fb1[FN];
-        acc_settle(acc);
-        issue(t_lo);
-        issue(t_lo + 1);
-        issue(t_lo + 2);
-#pragma unroll
-        for (int j = 0; j < NH; ++j) issue_one(t_lo + 3, j);   // the first slice issues the rest
-        stage_barrier<2 * NI + NH>();
-        load_b(fb0, t_lo);
-        fa = load_a(t_lo, 0);
-        // slices past the part's end read zeros: an odd count runs one zero slice
-        for (int t = t_lo; t < t_hi; t += 2) {
-          slice(fb0, fb1, t);
-          slice(fb1, fb0, t + 1);
-        }
-        acc_settle(acc);
-        // loads issued past the end land (as zeros) and every wave is done with LDS before the
-        // next tile refills it
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      }
+      run_slices(acc, u32x4{}, lda, ldb,
+                 [](f32x4& c, const u32x4& b, const u32x4& x) { mfma_bf16(c, b, x); },
+                 [](f32x4& c, const u32x4& b, const u32x4& x, const u32x4& d, uint32_t m0v, uint32_t vo) {
+                   mfma_bf16_dma(c, b, x, d, m0v, vo);
+                 },
+                 std::integral_constant<int, FM>{}, std::integral_constant<int, FN>{},
+                 std::integral_constant<bool, false>{});
     } else {
       // ---- fp8 (e4m3): 32x32x64 MFMA blocks with unit block scales, one 32-byte fragment per
       // lane; the per-tensor scales are applied in the epilogue
@@ -664,96 +751,25 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < F8N; ++j) acc8[i][j] = f32x16{};
       // a 32-row fp8 fragment: row r + (lane & 31), K bytes 32*(lane/32) .. +31 of the slice
-      auto frag8 = [&](int t, int r) {
-        const uint8_t* st = stages + (t & (kStages - 1)) * DSTAGE;
+      auto frag8 = [&](int sg, int r) {
+        const uint8_t* st = stages + sg * DSTAGE;
         const int row = r + (lane & 31), g = (lane >> 5) * 2;
         const u32x4 lo4 = *reinterpret_cast<const u32x4*>(st + lds64_off(row, g));
         const u32x4 hi4 = *reinterpret_cast<const u32x4*>(st + lds64_off(row, g + 1));
         return i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
                      (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
       };
-      auto load_b1 = [&](int t, int j) { return frag8(t, BM + wn * WTN + j * 32); };
-      auto load_b = [&](i32x8 (&fb)[F8N], int t) {
-#pragma unroll
-        for (int j = 0; j < F8N; ++j) fb[j] = load_b1(t, j);
-      };
-      auto load_a = [&](int t, int i) { return frag8(t, wm * WTM + i * 32); };
-      // One K slice t, its B fragments in fbc and its first A fragment in fa (requested during
-      // the previous slice). Slot t%4 is refilled with slice t+4 by NI direct-to-LDS loads, the
-      // first NH of them in the second half of slice t and the rest in the first half of slice
-      // t+1, so that every half slice carries about NI/2 loads between its MFMAs and the load
-      // path never takes a burst. First half of slice t: the remaining A fragments of slice t
-      // are requested row by row, and the loads NH..NI-1 of slice t+3 go between the MFMAs.
-      // Then the waves meet (slice t+1 has landed everywhere; every wave has read all of slice
-      // t), and the second half spreads slice t+1's B fragments and first A fragment, then the
-      // loads 0..NH-1 of slice t+4, between its MFMAs.
-      constexpr int RB = F8M / 2;                // rows before the barrier
-      constexpr int S1 = RB * F8N, S2 = (F8M - RB) * F8N;
-      constexpr int E1 = NI - NH, E2 = F8N + 1 + NH;
-      static_assert(F8M - RB - 1 <= RB, "the A fragments after the barrier are loaded before it");
+      auto ldb = [&](int sg, int j) { return frag8(sg, BM + wn * WTN + j * 32); };
+      auto lda = [&](int sg, int i) { return frag8(sg, wm * WTM + i * 32); };
       // a wave with a single 32x32 block reuses its accumulator in the next slice's first
       // MFMA: give the previous one time to write it back
-      constexpr bool kLoneBlock = F8M * F8N < 3;
-      i32x8 fa;
-      auto slice = [&](i32x8 (&fbc)[F8N], i32x8 (&fbn)[F8N], int t) {
-        i32x8 far[F8M];
-        far[0] = fa;
-        if (S1 == 0) {                            // no MFMA before the barrier: issue plainly
-#pragma unroll
-          for (int e = 0; e < E1; ++e) issue_one(t + 3, NH + e);
-        }
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          far[i + 1] = load_a(t, i + 1);
-          if (RB + 1 + i < F8M) far[RB + 1 + i] = load_a(t, RB + 1 + i);
-#pragma unroll
-          for (int j = 0; j < F8N; ++j) {
-            mfma_fp8(acc8[i][j], fbc[j], far[i]);
-            const int q = i * F8N + j;
-#pragma unroll
-            for (int e = 0; e < E1; ++e)
-              if (S1 > 0 && e * S1 / E1 == q) issue_one(t + 3, NH + e);
-          }
-        }
-        stage_barrier<2 * NI>();
-#pragma unroll
-        for (int i = RB; i < F8M; ++i) {
-#pragma unroll
-          for (int j = 0; j < F8N; ++j) {
-            if (kLoneBlock) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-            mfma_fp8(acc8[i][j], fbc[j], far[i]);
-            const int q = (i - RB) * F8N + j;
-#pragma unroll
-            for (int e = 0; e < E2; ++e) {
-              if (e * S2 / E2 != q) continue;         // request e goes after MFMA slot e*S2/E2
-              if (e < F8N) fbn[e] = load_b1(t + 1, e);
-              else if (e == F8N) fa = load_a(t + 1, 0);
-              else issue_one(t + 4, e - F8N - 1);
-            }
-          }
-        }
-      };
-      if (t_hi > t_lo) {
-        i32x8 fb0[F8N], fb1[F8N];
-        acc_settle(acc8);
-        issue(t_lo);
-        issue(t_lo + 1);
-        issue(t_lo + 2);
-#pragma unroll
-        for (int j = 0; j < NH; ++j) issue_one(t_lo + 3, j);   // the first slice issues the rest
-        stage_barrier<2 * NI + NH>();
-        load_b(fb0, t_lo);
-        fa = load_a(t_lo, 0);
-        // slices past the part's end read zeros: an odd count runs one zero slice
-        for (int t = t_lo; t < t_hi; t += 2) {
-          slice(fb0, fb1, t);
-          slice(fb1, fb0, t + 1);
-        }
-        acc_settle(acc8);
-        // loads issued past the end land (as zeros) and every wave is done with LDS before the
-        // next tile refills it
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      }
+      run_slices(acc8, i32x8{}, lda, ldb,
+                 [](f32x16& c, const i32x8& b, const i32x8& x) { mfma_fp8(c, b, x); },
+                 [](f32x16& c, const i32x8& b, const i32x8& x, const u32x4& d, uint32_t m0v, uint32_t vo) {
+                   mfma_fp8_dma(c, b, x, d, m0v, vo);
+                 },
+                 std::integral_constant<int, F8M>{}, std::integral_constant<int, F8N>{},
+                 std::integral_constant<bool, (F8M * F8N < 3)>{});
       // the epilogue's view: quad q of block (i, j) is acc[i][4j + q]
 #pragma unroll
       for (int i = 0; i < F8M; ++i)
@@ -977,12 +993,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         __hip_atomic_store(a.scratch + kScrCopyNext, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(a.scratch + kScrCopyT0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      for (uint32_t i = tid; i * (uint32_t)a.pieces < a.copy_jobs; i += kThreads)
+      for (uint32_t i = tid; i * (uint32_t)a.pieces < a.copy_jobs; i += NT)
         __hip_atomic_store(a.scratch + kScrPieces + a.scratch[kScrOrder + i], 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
     if (EPI == kEpiReduceScatter)
-      for (int i = tid; i < a.world * a.cps; i += kThreads)
+      for (int i = tid; i < a.world * a.cps; i += NT)
         __hip_atomic_store(a.scratch + kScrRsCount + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (tid == 0) __hip_atomic_store(a.scratch + kScrDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1010,14 +1026,21 @@ __global__ void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst,
   }
 }
 
-template <int BM, int BN, int DT, int EPI>
+template <int BM, int BN, int DT, int EPI, int NW = 4>
 static hipError_t launch_one(const GemmArgs& args, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, DT, EPI>), dim3(grid), dim3(kThreads), 0, stream, args);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, DT, EPI, NW>), dim3(grid), dim3(NW * kWaveLanes), 0, stream,
+                     args);
   return hipGetLastError();
 }
 
 template <int DT, int EPI>
-static hipError_t launch_shape(const GemmArgs& args, int bm, int bn, int grid, hipStream_t s) {
+static hipError_t launch_shape(const GemmArgs& args, int bm, int bn, int waves, int grid,
+                               hipStream_t s) {
+  if constexpr (DT == AGG_BF16) {
+    if (waves == 8 && bm == 256 && bn == 256) return launch_one<256, 256, DT, EPI, 8>(args, grid, s);
+    if (waves == 8 && bm == 256 && bn == 224) return launch_one<256, 224, DT, EPI, 8>(args, grid, s);
+  }
+  if (waves != 4) return hipErrorInvalidValue;
   if (bm == 256 && bn == 256) return launch_one<256, 256, DT, EPI>(args, grid, s);
   if (bm == 256 && bn == 224) return launch_one<256, 224, DT, EPI>(args, grid, s);
   if (bm == 128 && bn == 128) return launch_one<128, 128, DT, EPI>(args, grid, s);
@@ -1026,13 +1049,15 @@ static hipError_t launch_shape(const GemmArgs& args, int bm, int bn, int grid, h
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm(const GemmArgs& args, int bm, int bn, int dtype, int epilogue, int grid,
-                       hipStream_t stream) {
+hipError_t launch_gemm(const GemmArgs& args, int bm, int bn, int dtype, int epilogue, int waves,
+                       int grid, hipStream_t stream) {
   if (epilogue == kEpiAllGather) {
-    if (dtype == AGG_BF16) return launch_shape<AGG_BF16, kEpiAllGather>(args, bm, bn, grid, stream);
-    if (dtype == AGG_FP8_E4M3) return launch_shape<AGG_FP8_E4M3, kEpiAllGather>(args, bm, bn, grid, stream);
+    if (dtype == AGG_BF16)
+      return launch_shape<AGG_BF16, kEpiAllGather>(args, bm, bn, waves, grid, stream);
+    if (dtype == AGG_FP8_E4M3)
+      return launch_shape<AGG_FP8_E4M3, kEpiAllGather>(args, bm, bn, waves, grid, stream);
   } else if (epilogue == kEpiReduceScatter && dtype == AGG_BF16) {
-    return launch_shape<AGG_BF16, kEpiReduceScatter>(args, bm, bn, grid, stream);
+    return launch_shape<AGG_BF16, kEpiReduceScatter>(args, bm, bn, waves, grid, stream);
   }
   return hipErrorInvalidValue;
 }
