@@ -46,7 +46,6 @@ _SIGNATURES = {
     "agg_ctx_set_tile": [_vp, _c_int, _c_int],
     "agg_ctx_set_lists": [_vp, _c_int, _c_int],
     "agg_ctx_set_split": [_vp, _c_int],
-    "agg_ctx_set_waves": [_vp, _c_int],
     "agg_ctx_set_pull": [_vp, _c_int],
     "agg_ctx_set_producer": [_vp, _c_int, _c_int, _c_int],
     "agg_set_trace": [_vp, _vp, _sz],
@@ -246,10 +245,6 @@ def agg_ctx_set_pull(ctx, pull: str = "auto") -> None:
 
 def agg_ctx_set_split(ctx, ksplit: int = 0) -> None:
     _call("agg_ctx_set_split", ctx, ksplit)
-
-
-def agg_ctx_set_waves(ctx, waves: int = 0) -> None:
-    _call("agg_ctx_set_waves", ctx, waves)
 
 
 def agg_ctx_set_lists(ctx, lists: int = 8, list_cols: int = 0) -> None:

@@ -78,7 +78,6 @@ struct agg_ctx {
   uint64_t timeout_us = 2000000;
   double ticks_per_us = 100.0;
   int force_bm = 0, force_bn = 0;   // 0: automatic tile shape
-  int waves = 0;                    // waves per workgroup of the big bf16 tiles (0: automatic)
   int n_copy = kDefaultCopyStreams;
   int reserved_cus = kDefaultReservedCus;   // CUs the overlapped grid leaves to the producer
   hipStream_t ks = nullptr;                           // consumer kernel stream (own HW queue)
@@ -295,13 +294,6 @@ int ensure_ws(agg_ctx* ctx, size_t bytes) {
 }
 
 // K split of one AllGather+GEMM call (the ctx may force one; tiles above 128 x 128 never split).
-// Waves per workgroup: 8 (two per SIMD) only for the bf16 256 x 224 and 256 x 256 tiles and only
-// when asked for; every other launch runs 4.
-int waves_for(const agg_ctx* ctx, TileShape ts, int dtype) {
-  const bool big_bf16 = dtype == AGG_BF16 && ts.bm == 256 && ts.bn >= 224;
-  return (big_bf16 && ctx->waves == 8) ? 8 : 4;
-}
-
 KSplit ksplit_for(agg_ctx* ctx, TileShape ts, int dtype, int64_t tiles, int64_t k) {
   KSplit ks = choose_ksplit(0, dtype, tiles, k, ctx->cus);
   if (ts.bm * ts.bn > kMaxSplitTileArea) {
@@ -435,7 +427,7 @@ int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int
   } else {
     h.copy_jobs = 0;
   }
-  auto go = [&]() { return launch_gemm(h, ts.bm, ts.bn, dtype, epi, waves_for(ctx, ts, dtype), gr, ls); };
+  auto go = [&]() { return launch_gemm(h, ts.bm, ts.bn, dtype, epi, gr, ls); };
   if (timed) return timed_launch(ctx, go, ls);
   HIP_TRY(go());
   return AGG_OK;
@@ -628,14 +620,6 @@ extern "C" int agg_ctx_set_tile(agg_ctx* ctx, int bm, int bn) {
       return AGG_OK;
     }
   return fail(AGG_E_ARG, "no kernel for a %dx%d tile", bm, bn);
-}
-
-extern "C" int agg_ctx_set_waves(agg_ctx* ctx, int waves) {
-  clear_error();
-  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
-  if (waves != 0 && waves != 4 && waves != 8) return fail(AGG_E_ARG, "waves must be 0, 4 or 8");
-  ctx->waves = waves;
-  return AGG_OK;
 }
 
 extern "C" int agg_ctx_set_producer(agg_ctx* ctx, int kind, int copy_wgs, int piece_kib) {
@@ -853,8 +837,7 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
   }
   auto launch = [&]() -> int {
     return timed_launch(ctx, [&]() {
-      return launch_gemm(g, ts.bm, ts.bn, dtype, kEpiAllGather, waves_for(ctx, ts, dtype), grid,
-                         ctx->ks);
+      return launch_gemm(g, ts.bm, ts.bn, dtype, kEpiAllGather, grid, ctx->ks);
     });
   };
   return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
@@ -951,8 +934,7 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
   }
   auto launch = [&]() -> int {
     return timed_launch(ctx, [&]() {
-      return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiReduceScatter, waves_for(ctx, ts, AGG_BF16),
-                         grid, ctx->ks);
+      return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiReduceScatter, grid, ctx->ks);
     });
   };
   return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,

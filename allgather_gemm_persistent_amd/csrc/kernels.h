@@ -73,10 +73,10 @@ struct GemmArgs {
 };
 
 // Launch the persistent kernel instantiated for (bm, bn, dtype, epilogue) with `grid`
-// workgroups of `waves` x 64 threads on `stream` (waves: 4, or 8 for the bf16 256 x 224 and
-// 256 x 256 tiles). Returns hipErrorInvalidValue for a combination that has no instantiation.
-hipError_t launch_gemm(const GemmArgs& args, int bm, int bn, int dtype, int epilogue, int waves,
-                       int grid, hipStream_t stream);
+// workgroups of 256 threads on `stream`. Returns hipErrorInvalidValue for a shape that has no
+// instantiation.
+hipError_t launch_gemm(const GemmArgs& args, int bm, int bn, int dtype, int epilogue, int grid,
+                       hipStream_t stream);
 
 // Fill `words` uint32 at `dst` with `value` (a kernel, not a memset node).
 hipError_t launch_fill_u32(uint32_t* dst, size_t words, uint32_t value, hipStream_t stream);

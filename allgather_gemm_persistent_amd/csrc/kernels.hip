@@ -41,6 +41,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaveLanes = 64;
+constexpr int kThreads = 256;
 // word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle)
 constexpr int kBufferFlags = 0x00020000;
 // a buffer offset past every operand (operands are limited to 2^31 bytes)
@@ -426,17 +427,14 @@ __device__ bool wait_chunks(const GemmArgs& a, int64_t lo, int64_t hi, int block
   return true;
 }
 
-// NW waves per workgroup: 4 (one per SIMD, 2 x 2 over the tile) or 8 (two per SIMD, 4 x 2, so
-// that each SIMD's MFMA pipe has a second wave to issue from while one waits on LDS or memory).
-template <int BM, int BN, int DT, int EPI, int NW>
-__global__ void __launch_bounds__(NW * kWaveLanes, 1) gemm_kernel(const GemmArgs a) {
-  constexpr int NT = NW * kWaveLanes;
+template <int BM, int BN, int DT, int EPI>
+__global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
+  constexpr int NW = kThreads / kWaveLanes, NT = kThreads;   // one wave per SIMD
   constexpr bool FP8 = (DT == AGG_FP8_E4M3);
   constexpr bool kSplitTiles = BM * BN <= 128 * 128;
-  static_assert(NW == 4 || (NW == 8 && !FP8 && BM == 256 && BN >= 224), "8 waves: big bf16 tiles");
-  // 2 x 2 (4 x 2 with 8) waves over 16x16x32 bf16 or 32x32x64 fp8 MFMA blocks (fp8: 4 x 1 when
-  // half the tile's columns are not whole 32-column blocks)
-  constexpr int WMW = NW == 8 ? 4 : (!FP8 || (BN / 2) % 32 == 0) ? 2 : 4;   // waves along M
+  // 2 x 2 waves over 16x16x32 bf16 or 32x32x64 fp8 MFMA blocks (fp8: 4 x 1 when half the
+  // tile's columns are not whole 32-column blocks)
+  constexpr int WMW = (!FP8 || (BN / 2) % 32 == 0) ? 2 : 4;   // waves along M
   constexpr int WNW = NW / WMW;
   constexpr int WTM = BM / WMW, WTN = BN / WNW;        // wave tile
   constexpr int BLK = FP8 ? 32 : 16;                   // MFMA output block edge
@@ -824,9 +822,9 @@ __global__ void __launch_bounds__(NW * kWaveLanes, 1) gemm_kernel(const GemmArgs
         __syncthreads();
         finish = __builtin_amdgcn_readfirstlane(s_ok) != 0;
         if (finish) {
-          // parts in order, software-pipelined: the loads of part q+1 are in flight while part
-          // q is added (past the last part they read zeros, so every step issues the same
-          // loads and the wait for part q leaves part q+1's loads outstanding)
+          // parts in order, G at a time: the loads of G parts are in flight together (one round
+          // trip per group instead of per part), then they are added one after another in part
+          // order, so the sum does not depend on the grouping
           auto load_part = [&](f32x4 (&v)[FM][FN], int q) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
@@ -844,18 +842,21 @@ __global__ void __launch_bounds__(NW * kWaveLanes, 1) gemm_kernel(const GemmArgs
               }
             }
           };
-          f32x4 cur[FM][FN], nxt[FM][FN];
-          load_part(cur, 0);
-          for (int q = 0; q < a.ksplit; ++q) {
-            load_part(nxt, q + 1);
+          constexpr int G = FM * FN >= 32 ? 1 : (32 / (FM * FN) > 8 ? 8 : 32 / (FM * FN));
+          const int ks = __builtin_amdgcn_readfirstlane(a.ksplit);
+          for (int q0 = 0; q0 < ks; q0 += G) {
+            f32x4 v[G][FM][FN];
+#pragma unroll
+            for (int g = 0; g < G; ++g) load_part(v[g], q0 + g);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int g = 0; g < G; ++g) {
+              if (q0 + g >= ks) break;
 #pragma unroll
-              for (int j = 0; j < FN; ++j) {
-                acc[i][j] = q == 0 ? cur[i][j] : acc[i][j] + cur[i][j];
-                cur[i][j] = nxt[i][j];
-              }
+              for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = (q0 + g == 0) ? v[g][i][j] : acc[i][j] + v[g][i][j];
+            }
           }
           if (tid == 0)
             __hip_atomic_store(a.scratch + kScrSplit + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1026,21 +1027,14 @@ __global__ void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst,
   }
 }
 
-template <int BM, int BN, int DT, int EPI, int NW = 4>
+template <int BM, int BN, int DT, int EPI>
 static hipError_t launch_one(const GemmArgs& args, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, DT, EPI, NW>), dim3(grid), dim3(NW * kWaveLanes), 0, stream,
-                     args);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, DT, EPI>), dim3(grid), dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 
 template <int DT, int EPI>
-static hipError_t launch_shape(const GemmArgs& args, int bm, int bn, int waves, int grid,
-                               hipStream_t s) {
-  if constexpr (DT == AGG_BF16) {
-    if (waves == 8 && bm == 256 && bn == 256) return launch_one<256, 256, DT, EPI, 8>(args, grid, s);
-    if (waves == 8 && bm == 256 && bn == 224) return launch_one<256, 224, DT, EPI, 8>(args, grid, s);
-  }
-  if (waves != 4) return hipErrorInvalidValue;
+static hipError_t launch_shape(const GemmArgs& args, int bm, int bn, int grid, hipStream_t s) {
   if (bm == 256 && bn == 256) return launch_one<256, 256, DT, EPI>(args, grid, s);
   if (bm == 256 && bn == 224) return launch_one<256, 224, DT, EPI>(args, grid, s);
   if (bm == 128 && bn == 128) return launch_one<128, 128, DT, EPI>(args, grid, s);
@@ -1049,15 +1043,13 @@ static hipError_t launch_shape(const GemmArgs& args, int bm, int bn, int waves, 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm(const GemmArgs& args, int bm, int bn, int dtype, int epilogue, int waves,
-                       int grid, hipStream_t stream) {
+hipError_t launch_gemm(const GemmArgs& args, int bm, int bn, int dtype, int epilogue, int grid,
+                       hipStream_t stream) {
   if (epilogue == kEpiAllGather) {
-    if (dtype == AGG_BF16)
-      return launch_shape<AGG_BF16, kEpiAllGather>(args, bm, bn, waves, grid, stream);
-    if (dtype == AGG_FP8_E4M3)
-      return launch_shape<AGG_FP8_E4M3, kEpiAllGather>(args, bm, bn, waves, grid, stream);
+    if (dtype == AGG_BF16) return launch_shape<AGG_BF16, kEpiAllGather>(args, bm, bn, grid, stream);
+    if (dtype == AGG_FP8_E4M3) return launch_shape<AGG_FP8_E4M3, kEpiAllGather>(args, bm, bn, grid, stream);
   } else if (epilogue == kEpiReduceScatter && dtype == AGG_BF16) {
-    return launch_shape<AGG_BF16, kEpiReduceScatter>(args, bm, bn, waves, grid, stream);
+    return launch_shape<AGG_BF16, kEpiReduceScatter>(args, bm, bn, grid, stream);
   }
   return hipErrorInvalidValue;
 }

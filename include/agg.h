@@ -161,15 +161,6 @@ int agg_ctx_set_reserved_cus(agg_ctx* ctx, int n);
  * Shapes: 256x256, 256x224, 128x128, 128x64, 64x64; anything else is AGG_E_ARG. */
 int agg_ctx_set_tile(agg_ctx* ctx, int bm, int bn);
 
-/* Waves per workgroup of the bf16 256 x 256 and 256 x 224 tiles in later calls: 4 (one wave per
- * SIMD, each computing a 128-row quarter of the tile), 8 (two waves per SIMD, each an 64-row
- * eighth: while one waits for LDS or memory the other issues MFMAs), or 0 for the automatic
- * choice. Other tiles and fp8 always run 4. Results are bit-identical either way (the same
- * per-element MFMA chain over K). AGG_E_ARG for any other value. (MFMA-shaped core tiles in
- * registers and shared memory: "DITRON adds three levels of tiling", page "Triton-distributed
- * is turning communication into compiler territory".) */
-int agg_ctx_set_waves(agg_ctx* ctx, int waves);
-
 /* Split-K of later AllGather+GEMM calls. With few output tiles (fewer than half the CUs) and a
  * long K, the library cuts each tile's K range into parts computed by different workgroups;
  * every part writes an fp32 partial into a ctx-owned buffer (ksplit x M x N floats, allocated
