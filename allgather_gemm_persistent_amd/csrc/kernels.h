@@ -16,13 +16,15 @@ constexpr int kScrStatus = 17;     // bit 0: a flag wait gave up
 constexpr int kScrFailed = 18;     // first flag index that timed out (0xFFFFFFFF = none)
 constexpr int kScrCopyNext = 19;   // in-kernel producer: next copy job
 constexpr int kScrCopyT0 = 20;     // in-kernel producer: wall clock of the first job (delays)
+constexpr int kScrRedNext = 21;    // ReduceScatter: next row group of the local block to reduce
 constexpr int kScrRsCount = 64;    // ReduceScatter per-send-chunk completion counters
 constexpr int kScrPieces = kScrRsCount + AGG_MAX_CHUNKS;   // per-chunk copied-piece counters
 constexpr int kScrOrder = kScrPieces + AGG_MAX_CHUNKS;     // arrival order (chunk ids)
 constexpr int kScrDelay = kScrOrder + AGG_MAX_CHUNKS;      // cumulative producer delays (ticks)
 constexpr int kScrRowOrder = kScrDelay + AGG_MAX_CHUNKS;   // row tiles in compute order
 constexpr int kScrSplit = kScrRowOrder + AGG_MAX_ROW_TILES; // split-K: parts done per tile
-constexpr int kScrWords = kScrSplit + 1024;
+constexpr int kScrLocal = kScrSplit + 1024;  // RS: local tiles stored, per row tile of the block
+constexpr int kScrWords = kScrLocal + AGG_MAX_ROW_TILES;
 constexpr int kMaxLists = 16;
 
 enum Epilogue { kEpiAllGather = 0, kEpiReduceScatter = 1 };

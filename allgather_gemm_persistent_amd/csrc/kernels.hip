@@ -427,6 +427,104 @@ __device__ bool wait_chunks(const GemmArgs& a, int64_t lo, int64_t hi, int block
   return true;
 }
 
+// Wave-uniform bounded wait until *ctr >= expect: relaxed agent-scope polls with s_sleep, giving
+// up like the chunk waits (past the ctx limit, which sets the status word, or once another wait
+// has given up). Returns false if it gave up.
+__device__ bool wait_count(const GemmArgs& a, const uint32_t* ctr, uint32_t expect) {
+  const uint32_t t0 = wall_ticks();
+  for (uint32_t polls = 0;; ++polls) {
+    if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= expect) return true;
+    const bool abort_seen = (polls & 15) == 15 &&
+        __hip_atomic_load(a.scratch + kScrStatus, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    const bool expired = (uint64_t)(wall_ticks() - t0) > a.timeout_ticks;
+    if (abort_seen || expired) {
+      if (expired && (threadIdx.x & 63) == 0) atomicOr(a.scratch + kScrStatus, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// The local block of a ReduceScatter ("reduce partial results"): out = out + the incoming
+// partial of every peer in ascending rank order, where `out` already holds this rank's own
+// partial (stored by the local tiles). Run by every workgroup once no tile is left, over groups
+// of kRedRows rows claimed from a shared counter, so the reduction is spread over the whole grid
+// instead of the few workgroups holding local tiles. A group waits (wave 0, bounded) until the
+// local tiles of its row tile have all stored their partials and until every peer's chunk of
+// its rows has arrived; an abandoned group leaves its rows at the local partial. The sums are
+// elementwise over 16-byte vectors, consecutive threads on consecutive addresses; `out` is read
+// system-coherent (written through by other workgroups of this launch), the received blocks after
+// an acquire fence, as the tiles read the gather buffer.
+template <int BM>
+__device__ void reduce_local(const GemmArgs& a, int tid, int* s_item, int* s_ok) {
+  constexpr int kRedRows = 4;              // divides every tile height: a group is in one row tile
+  constexpr int U = 4;                     // vectors per thread in flight per peer
+  const int64_t mb = a.m_block, N = a.N;
+  if (mb == 0 || N == 0) return;
+  const uint32_t items = (uint32_t)((mb + kRedRows - 1) / kRedRows);
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t blk = mb * N;              // floats per block
+  const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, (int)(blk * 4), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rrecv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.recv), 0, (int)(a.world * blk * 4), kBufferFlags);
+  const int world = __builtin_amdgcn_readfirstlane(a.world), rank = __builtin_amdgcn_readfirstlane(a.rank);
+  for (;;) {
+    if (tid == 0) {
+      uint32_t it = items;
+      if (__hip_atomic_load(a.scratch + kScrRedNext, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < items)
+        it = atomicAdd(a.scratch + kScrRedNext, 1u);
+      s_item[0] = (int)it;
+    }
+    __syncthreads();
+    const uint32_t it = (uint32_t)__builtin_amdgcn_readfirstlane(s_item[0]);
+    __syncthreads();
+    if (it >= items) break;
+    const int64_t r0 = (int64_t)it * kRedRows;
+    const int64_t r1 = r0 + kRedRows < mb ? r0 + kRedRows : mb;
+    if (wave == 0) {
+      uint32_t seen = 0;
+      const int64_t base = (int64_t)rank * mb;
+      const bool ok = wait_count(a, a.scratch + kScrLocal + (int)(r0 / BM), (uint32_t)a.n_col_tiles) &&
+                      wait_chunks<kEpiReduceScatter>(a, base + r0, base + r1, rank, seen);
+      if (lane == 0) *s_ok = ok;
+    }
+    __syncthreads();
+    if (!__builtin_amdgcn_readfirstlane(*s_ok)) {
+      __syncthreads();
+      continue;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+    const int64_t v0 = r0 * N / 4, nv = (r1 - r0) * N / 4;   // the group's 16-byte vectors
+    for (int64_t e0 = tid; e0 < nv; e0 += (int64_t)kThreads * U) {
+      f32x4 v[U], in[U][AGG_MAX_WORLD - 1];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t e = e0 + (int64_t)u * kThreads;
+        const bool live = e < nv;
+        v[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                   rout, live ? (int)((v0 + e) * 16) : (int)kOutOfRange, 0, kStoreSystemCoherent));
+#pragma unroll
+        for (int q = 0; q < AGG_MAX_WORLD - 1; ++q) {
+          const int p = q < rank ? q : q + 1;     // peers in ascending rank order
+          const int off = (live && p < world) ? (int)((int64_t)p * blk * 4 + (v0 + e) * 16) : (int)kOutOfRange;
+          in[u][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrecv, off, 0, 0));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t e = e0 + (int64_t)u * kThreads;
+        if (e >= nv) continue;
+#pragma unroll
+        for (int q = 0; q < AGG_MAX_WORLD - 1; ++q)
+          if (q + 1 < world) v[u] += in[u][q];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[u]), rout, (int)((v0 + e) * 16), 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <int BM, int BN, int DT, int EPI>
 __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   constexpr int NW = kThreads / kWaveLanes, NT = kThreads;   // one wave per SIMD
@@ -510,7 +608,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     // ---- wait for the chunks this tile's rows need
     if (wave == 0) {
       uint32_t seen = 0xFFFFFFFFu;
-      const bool ok = pull || wait_chunks<EPI>(a, lo, hi, block, seen);
+      // (ReduceScatter tiles need no chunk: the received partials are added by reduce_local)
+      const bool ok = pull || EPI == kEpiReduceScatter || wait_chunks<EPI>(a, lo, hi, block, seen);
       if (lane == 0) {
         s_ok = ok;
         if (trec) { trec[3] = seen; trec[6] = wall_ticks(); }
@@ -904,37 +1003,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
           }
         }
       } else {
-        // the local block: acc + the incoming partials of the peers in ascending rank order,
-        // one peer at a time with half the tile's loads in flight together (rows and columns
-        // past the end read zeros through the buffer's range check)
-        const __amdgpu_buffer_rsrc_t rrecv = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(a.recv), 0, (int)(a.world * blk * 4), kBufferFlags);
-        constexpr int FH = FM > 1 ? FM / 2 : 1;
-        for (int p = 0; p < a.world; ++p) {
-          if (p == a.rank) continue;
-#pragma unroll
-          for (int h = 0; h < FM; h += FH) {
-            f32x4 in[FH][FN];
-#pragma unroll
-            for (int i = 0; i < FH; ++i) {
-              const int64_t m = lo + qrow(h + i);
-#pragma unroll
-              for (int j = 0; j < FN; ++j) {
-                const int64_t n = n0 + qcol(j);
-                const int off = (m < hi && n < a.N) ? (int)(((int64_t)p * blk + (m - base) * a.N + n) * 4)
-                                                     : (int)kOutOfRange;
-                in[i][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrecv, off, 0, 0));
-              }
-            }
-            // keep the loads together: the scheduler would otherwise move each next to its add
-            // and wait for them one at a time
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < FH; ++i)
-#pragma unroll
-              for (int j = 0; j < FN; ++j) acc[h + i][j] += in[i][j];
-          }
-        }
+        // the local block: the tile's partial goes to `out` (write-through, like `send`); the
+        // peers' partials are added after the last tile by reduce_local
+        const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(
+            a.out, 0, (int)(blk * 4), kBufferFlags);
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const int64_t m = lo + qrow(i);
@@ -943,9 +1015,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
           for (int j = 0; j < FN; ++j) {
             const int64_t n = n0 + qcol(j);
             if (n >= a.N) continue;
-            *reinterpret_cast<f32x4*>(a.out + (m - base) * a.N + n) = acc[i][j];
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rout,
+                                                   (int)(((m - base) * a.N + n) * 4), 0, kStoreSystemCoherent);
           }
         }
+        // once the stores have completed, count the tile in its row tile
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0)
+          __hip_atomic_fetch_add(a.scratch + kScrLocal + tib, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (!local) {
         // publish: once every thread's write-through stores have completed, this tile's rows of
@@ -979,9 +1057,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     __syncthreads();
   }
 
+  if (EPI == kEpiReduceScatter) reduce_local<BM>(a, tid, &s_job, &s_ok);
+
   // ---- the last workgroup resets the counters for the next launch. No fence: every counter
   // reset here was last touched by the other workgroups through atomics whose returned values
-  // they used, i.e. that had completed, before they counted themselves done.
+  // they used, i.e. that had completed, before they counted themselves done (the local row-tile
+  // counts were read to their final values by the reduction's waits).
   if (tid == 0) {
     const uint32_t prev = atomicAdd(a.scratch + kScrDone, 1u);
     s_ok = (prev == gridDim.x - 1);
@@ -998,9 +1079,13 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         __hip_atomic_store(a.scratch + kScrPieces + a.scratch[kScrOrder + i], 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (EPI == kEpiReduceScatter)
+    if (EPI == kEpiReduceScatter) {
       for (int i = tid; i < a.world * a.cps; i += NT)
         __hip_atomic_store(a.scratch + kScrRsCount + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = tid; i < a.tpb; i += NT)
+        __hip_atomic_store(a.scratch + kScrLocal + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_store(a.scratch + kScrRedNext, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
     if (tid == 0) __hip_atomic_store(a.scratch + kScrDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
