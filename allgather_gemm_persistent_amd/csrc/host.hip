@@ -811,6 +811,9 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
     g.scale = dtype == AGG_FP8_E4M3 ? scale_a * scale_b : 1.0f;
     tiles = int64_t(g.n_row_tiles) * g.n_col_tiles;
     grid = grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks && !cu);
+    // every split part claims its workgroup at launch (no more parts than workgroups): the parts
+    // of a tile can wait for each other and sum the tile together
+    g.split_together = (g.ksplit > 1 && tiles <= grid) ? 1 : 0;
     fill_common(ctx, g, ts, grid);
     attach_trace(ctx, g, tiles);
   }

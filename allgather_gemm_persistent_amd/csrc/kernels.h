@@ -49,6 +49,8 @@ struct GemmArgs {
   int ksplit;               // K parts per tile (1: no split); part p covers K slices
   int kps;                  //   [p*kps, min((p+1)*kps, slices)) of the main loop's slices
   float* ws;                // split-K partial products, ksplit x M x N fp32
+  int split_together;       // split-K with every part of every tile in its own workgroup at
+                            //   once: the parts sum the tile together, a row range each
   int tpb;                  // RS: row tiles per block
   int n_lists;              // claim lists (one per XCD)
   int list_cols;            // lists split as (n_lists / list_cols) row groups x list_cols column blocks

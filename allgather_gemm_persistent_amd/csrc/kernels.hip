@@ -155,12 +155,12 @@ __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)p);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays a quiet NaN)
-__device__ inline uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 -> a packed bf16 pair (first value in the low half), rounded to nearest even: one
+// gfx950 v_cvt_pk_bf16_f32 (finite inputs; a NaN stays a NaN)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // Cache-policy bits of a buffer store on gfx950: sc0 | sc1 = system coherent, i.e. the store
@@ -289,29 +289,72 @@ struct Tile {
   int list, pos;
 };
 
-// Claim the next tile: this XCD's list first, then the others in turn. The lists form a
-// (L / list_cols) x list_cols grid: list x holds the row tiles at compute positions
-// x / list_cols, + L / list_cols, ... (so every list follows the compute order) crossed with
-// column tiles [xc*nc/list_cols, (xc+1)*nc/list_cols), xc = x % list_cols.
-// Run by all lanes of one wave: lane d reads the counter of the d-th list in search order, so
-// one round trip finds the first list with tiles left (and, at the end, that none has any); the
-// lane owning that list takes a tile with an atomic add, retrying if another workgroup emptied
-// the list in between. Returns, on every lane, whether a tile was claimed (then in t).
-__device__ inline bool claim(const GemmArgs& a, int home, Tile& t) {
+// Claim lists. The lists form a (L / list_cols) x list_cols grid: list x holds the row tiles at
+// compute positions x / list_cols, + L / list_cols, ... (so every list follows the compute order)
+// crossed with column tiles [xc*nc/list_cols, (xc+1)*nc/list_cols), xc = x % list_cols.
+// Position k of list x is row tile (k / nx) of the list and column c_lo + k % nx.
+struct ListGeom {
+  int xr, c_lo, nx;
+  uint32_t len;
+};
+
+__device__ inline ListGeom list_geom(const GemmArgs& a, int x) {
+  const int L = a.n_lists, Lc = a.list_cols, Lr = L / Lc;
+  ListGeom g;
+  g.xr = x / Lc;
+  const int xc = x - g.xr * Lc;
+  g.c_lo = (int)((int64_t)xc * a.n_col_tiles / Lc);
+  g.nx = (int)((int64_t)(xc + 1) * a.n_col_tiles / Lc) - g.c_lo;
+  const int ny = g.xr < a.n_row_tiles ? (a.n_row_tiles - g.xr + Lr - 1) / Lr : 0;
+  g.len = (x < L && g.nx > 0 && ny > 0) ? (uint32_t)ny * (uint32_t)g.nx : 0u;
+  return g;
+}
+
+// The first `nstat` workgroups take their first tile without an atomic: workgroup b takes
+// position b / L of list b % L (workgroups are dealt to the XCDs round robin, so that is its own
+// XCD's list), if the list is that long. The counters then count only the later claims, which
+// start past these positions.
+__device__ inline uint32_t static_taken(const GemmArgs& a, int x, int nstat, uint32_t len) {
   const int L = a.n_lists;
-  const int Lc = a.list_cols, Lr = L / Lc;
+  const uint32_t n = nstat > x ? (uint32_t)((nstat - 1 - x) / L + 1) : 0u;
+  return n < len ? n : len;
+}
+
+__device__ inline void list_tile(const GemmArgs& a, int x, const ListGeom& g, uint32_t k, Tile& t) {
+  const int Lr = a.n_lists / a.list_cols;
+  t.row_tile = (int)a.scratch[kScrRowOrder + g.xr + (int)(k / (uint32_t)g.nx) * Lr];
+  t.col_tile = g.c_lo + (int)(k % (uint32_t)g.nx);
+  t.list = x;
+  t.pos = (int)k;
+}
+
+// First tile of workgroup b < nstat (uniform on every lane); false if its list is too short.
+__device__ inline bool claim_static(const GemmArgs& a, Tile& t) {
+  const int L = a.n_lists, b = (int)blockIdx.x;
+  const int x = b % L;
+  const uint32_t k = (uint32_t)(b / L);
+  const ListGeom g = list_geom(a, x);
+  if (k >= g.len) return false;
+  list_tile(a, x, g, k, t);
+  return true;
+}
+
+// Claim the next tile: this XCD's list first, then the others in turn. Run by all lanes of one
+// wave: lane d reads the counter of the d-th list in search order, so one round trip finds the
+// first list with tiles left (and, at the end, that none has any); the lane owning that list
+// takes a tile with an atomic add, retrying if another workgroup emptied the list in between.
+// Returns, on every lane, whether a tile was claimed (then in t).
+__device__ inline bool claim(const GemmArgs& a, int home, int nstat, Tile& t) {
+  const int L = a.n_lists;
   const int lane = threadIdx.x & 63;
   int x = home + lane;
   if (x >= L) x -= L;
   // recomputed per call: hoisted out of the tile loop, these would hold registers through the
   // main loop
   asm volatile("" : "+v"(x));
-  const int xr = x / Lc, xc = x - xr * Lc;
-  const int c_lo = (int)((int64_t)xc * a.n_col_tiles / Lc);
-  const int c_hi = (int)((int64_t)(xc + 1) * a.n_col_tiles / Lc);
-  const int nx = c_hi - c_lo;
-  const int ny = xr < a.n_row_tiles ? (a.n_row_tiles - xr + Lr - 1) / Lr : 0;
-  const uint32_t len = (lane < L && nx > 0 && ny > 0) ? (uint32_t)ny * (uint32_t)nx : 0u;
+  const ListGeom g = list_geom(a, lane < L ? x : L);
+  const uint32_t skip = static_taken(a, x, nstat, g.len);
+  const uint32_t len = g.len - skip;
   uint32_t* ctr = a.scratch + kScrLists + x;
   for (;;) {
     const bool open = len > 0 && __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < len;
@@ -322,12 +365,7 @@ __device__ inline bool claim(const GemmArgs& a, int home, Tile& t) {
     if (lane == d) k = atomicAdd(ctr, 1u);
     k = (uint32_t)__shfl((int)k, d);
     if (k < (uint32_t)__shfl((int)len, d)) {
-      if (lane == d) {
-        t.row_tile = (int)a.scratch[kScrRowOrder + xr + (int)(k / nx) * Lr];
-        t.col_tile = c_lo + (int)(k % nx);
-        t.list = x;
-        t.pos = (int)k;
-      }
+      if (lane == d) list_tile(a, x, g, skip + k, t);
       t.row_tile = __shfl(t.row_tile, d);
       t.col_tile = __shfl(t.col_tile, d);
       t.list = __shfl(t.list, d);
@@ -525,6 +563,47 @@ __device__ void reduce_local(const GemmArgs& a, int tid, int* s_item, int* s_ok)
   }
 }
 
+// Split-K, every part of the tile running at once: part `part` of `ks` sums rows
+// [part*BM/ks, (part+1)*BM/ks) of the tile over all parts' fp32 partials, in part order (the
+// same sum, bit for bit, as one workgroup adding every part), scales (fp8), and stores bf16.
+// Coalesced: consecutive threads take consecutive 16-byte column quads of a row. The partial
+// loads are system-coherent, like the partial stores.
+template <int BM, int BN, bool FP8>
+__device__ void sum_split_rows(const GemmArgs& a, int tid, int64_t lo, int64_t hi, int64_t n0, int part) {
+  constexpr int Q = BN / 4;                       // column quads per tile row
+  constexpr int G = 8;                            // partial loads in flight per quad
+  const int ks = __builtin_amdgcn_readfirstlane(a.ksplit);
+  const int r0 = part * BM / ks, r1 = (part + 1) * BM / ks;
+  const int64_t plane = a.M * a.N;
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(a.ws, 0, (int)(ks * plane * 4), kBufferFlags);
+  for (int e = tid; e < (r1 - r0) * Q; e += kThreads) {
+    const int64_t m = lo + r0 + e / Q;
+    const int64_t n = n0 + 4 * (e % Q);
+    if (m >= hi || n >= a.N) continue;
+    const int64_t off = (m * a.N + n) * 4;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int q0 = 0; q0 < ks; q0 += G) {
+      f32x4 v[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int o = q0 + g < ks ? (int)((q0 + g) * plane * 4 + off) : (int)kOutOfRange;
+        v[g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, o, 0, kStoreSystemCoherent));
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (q0 + g >= ks) break;
+        sum = (q0 + g == 0) ? v[g] : sum + v[g];
+      }
+    }
+    if (FP8) sum *= a.scale;
+    u32x2 packed;
+    packed[0] = bf16x2_rne(sum[0], sum[1]);
+    packed[1] = bf16x2_rne(sum[2], sum[3]);
+    *reinterpret_cast<u32x2*>(a.c + m * a.N + n) = packed;
+  }
+}
+
 template <int BM, int BN, int DT, int EPI>
 __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   constexpr int NW = kThreads / kWaveLanes, NT = kThreads;   // one wave per SIMD
@@ -552,13 +631,18 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WNW, wn = wave % WNW;
-  const int home = a.n_lists > 1 ? xcc_id() % a.n_lists : 0;
+  // the list searched first: the one that gives this workgroup its static first tile. The
+  // workgroups of one list share an XCD (they are dealt to the XCDs round robin), so its
+  // tiles' operand rows stay in that XCD's L2.
+  const int home = (int)blockIdx.x % a.n_lists;
   const int64_t kbytes = a.K * (FP8 ? 1 : 2);
 
-  auto claim_tile = [&]() {
+  // workgroups whose first tile is taken statically (pull: all but the copiers at the end)
+  const int nstat = (EPI == kEpiAllGather && a.pull) ? (int)gridDim.x - a.copy_wgs : (int)gridDim.x;
+  auto claim_tile = [&](bool first) {
     if (wave == 0) {
       Tile t{};
-      const bool got = claim(a, home, t);
+      const bool got = (first && (int)blockIdx.x < nstat && claim_static(a, t)) || claim(a, home, nstat, t);
       if (lane == 0) {
         s_tile[0] = got ? t.row_tile : -1;
         s_tile[1] = t.col_tile; s_tile[2] = t.list; s_tile[3] = t.pos;
@@ -577,11 +661,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   const int first_copier = pull ? (int)gridDim.x - a.copy_wgs : 0;
   const bool copier = a.copy_jobs && (int)blockIdx.x >= first_copier &&
                       (int)blockIdx.x < first_copier + a.copy_wgs;
-  if (!(pull && copier)) claim_tile();
+  if (!(pull && copier)) claim_tile(true);
   if (copier) produce_chunks<NT>(a, tid, &s_job);
-  if (pull && copier) claim_tile();
+  if (pull && copier) claim_tile(false);
 
-  for (;; claim_tile()) {   // (an abandoned tile's `continue` claims the next one too)
+  for (;; claim_tile(false)) {   // (an abandoned tile's `continue` claims the next one too)
     // uniform for the compiler too (see produce_chunks)
     const int row_tile = __builtin_amdgcn_readfirstlane(s_tile[0]);
     if (row_tile < 0) break;
@@ -915,50 +999,68 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         const int tile_id = row_tile * (a.n_col_tiles / a.ksplit) + col_tile;
-        if (tid == 0)
-          s_ok = (__hip_atomic_fetch_add(a.scratch + kScrSplit + tile_id, 1u, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)a.ksplit - 1);
-        __syncthreads();
-        finish = __builtin_amdgcn_readfirstlane(s_ok) != 0;
-        if (finish) {
-          // parts in order, G at a time: the loads of G parts are in flight together (one round
-          // trip per group instead of per part), then they are added one after another in part
-          // order, so the sum does not depend on the grouping
-          auto load_part = [&](f32x4 (&v)[FM][FN], int q) {
+        uint32_t* split_ctr = a.scratch + kScrSplit + tile_id;
+        if (a.split_together) {
+          // every part has its own workgroup in this launch: once all parts have stored, each
+          // sums a row range of the tile; the counter counts every part in twice (stored, then
+          // summed) and the last arrival resets it
+          const uint32_t ks = (uint32_t)a.ksplit;
+          if (tid == 0) __hip_atomic_fetch_add(split_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (wave == 0) {
+            const bool ok = wait_count(a, split_ctr, ks);
+            if (lane == 0) s_ok = ok;
+          }
+          __syncthreads();
+          if (__builtin_amdgcn_readfirstlane(s_ok)) sum_split_rows<BM, BN, FP8>(a, tid, lo, hi, n0, part);
+          __syncthreads();
+          if (tid == 0 && __hip_atomic_fetch_add(split_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 2 * ks - 1)
+            __hip_atomic_store(split_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          finish = false;
+        } else {
+          if (tid == 0)
+            s_ok = (__hip_atomic_fetch_add(split_ctr, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)a.ksplit - 1);
+          __syncthreads();
+          finish = __builtin_amdgcn_readfirstlane(s_ok) != 0;
+          if (finish) {
+            // parts in order, G at a time: the loads of G parts are in flight together (one round
+            // trip per group instead of per part), then they are added one after another in part
+            // order, so the sum does not depend on the grouping
+            auto load_part = [&](f32x4 (&v)[FM][FN], int q) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-              const int64_t m = lo + qrow(i);
+              for (int i = 0; i < FM; ++i) {
+                const int64_t m = lo + qrow(i);
 #pragma unroll
-              for (int j = 0; j < FN; ++j) {
-                const int64_t n = n0 + qcol(j);
-                // rows / columns past the end, and parts past the last, read zeros (offset past
-                // the buffer)
-                const int off = (q < a.ksplit && m < hi && n < a.N)
-                                    ? (int)(((int64_t)q * plane + m * a.N + n) * 4)
-                                    : (int)kOutOfRange;
-                v[i][j] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kStoreSystemCoherent));
+                for (int j = 0; j < FN; ++j) {
+                  const int64_t n = n0 + qcol(j);
+                  // rows / columns past the end, and parts past the last, read zeros (offset past
+                  // the buffer)
+                  const int off = (q < a.ksplit && m < hi && n < a.N)
+                                      ? (int)(((int64_t)q * plane + m * a.N + n) * 4)
+                                      : (int)kOutOfRange;
+                  v[i][j] = __builtin_bit_cast(
+                      f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kStoreSystemCoherent));
+                }
+              }
+            };
+            constexpr int G = FM * FN >= 32 ? 1 : (32 / (FM * FN) > 8 ? 8 : 32 / (FM * FN));
+            const int ks = __builtin_amdgcn_readfirstlane(a.ksplit);
+            for (int q0 = 0; q0 < ks; q0 += G) {
+              f32x4 v[G][FM][FN];
+#pragma unroll
+              for (int g = 0; g < G; ++g) load_part(v[g], q0 + g);
+              __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+              for (int g = 0; g < G; ++g) {
+                if (q0 + g >= ks) break;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                  for (int j = 0; j < FN; ++j) acc[i][j] = (q0 + g == 0) ? v[g][i][j] : acc[i][j] + v[g][i][j];
               }
             }
-          };
-          constexpr int G = FM * FN >= 32 ? 1 : (32 / (FM * FN) > 8 ? 8 : 32 / (FM * FN));
-          const int ks = __builtin_amdgcn_readfirstlane(a.ksplit);
-          for (int q0 = 0; q0 < ks; q0 += G) {
-            f32x4 v[G][FM][FN];
-#pragma unroll
-            for (int g = 0; g < G; ++g) load_part(v[g], q0 + g);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-              if (q0 + g >= ks) break;
-#pragma unroll
-              for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = (q0 + g == 0) ? v[g][i][j] : acc[i][j] + v[g][i][j];
-            }
+            if (tid == 0) __hip_atomic_store(split_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
-          if (tid == 0)
-            __hip_atomic_store(a.scratch + kScrSplit + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
       if (finish) {
@@ -973,8 +1075,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
             f32x4 v = acc[i][j];
             if (FP8) v *= a.scale;
             u32x2 packed;
-            packed[0] = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-            packed[1] = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+            packed[0] = bf16x2_rne(v[0], v[1]);
+            packed[1] = bf16x2_rne(v[2], v[3]);
             *reinterpret_cast<u32x2*>(a.c + m * a.N + n) = packed;
           }
         }

@@ -435,6 +435,34 @@ def test_split_k_vs_oracle(gpu, dtype, tile, ksplit):
         w.close()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_split_k_more_parts_than_workgroups(gpu, dtype):
+    """Split-K with more parts than workgroups (1024 parts of 64 x 64 tiles): the parts cannot
+    all run at once, so the last part of each tile sums it alone. Same bar as above."""
+    world, rank, ms, cr, n = 2, 0, 512, 128, 200
+    k = 1000 if dtype == "bf16" else 1040
+    shards, b, sa, sb = small_ag_data(world, ms, k, n, dtype, seed=107)
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, dtype=dtype, scale_a=sa, scale_b=sb,
+                   tile=(64, 64))
+    try:
+        B.agg_ctx_set_split(w.ctx, 16)
+        w.run("overlap")
+        assert w.status() == (0, -1)
+        assert_close(to_f64(w.c), _oracle_c(shards, b, dtype, sa, sb), _tol(dtype), "C")
+    finally:
+        w.close()
+    shards, b, _, _ = small_ag_data(world, ms, k, n, dtype, seed=109, kind="int")
+    w = AgWorkload(world, rank, shards, b, chunk_rows=cr, dtype=dtype, tile=(64, 64))
+    try:
+        B.agg_ctx_set_split(w.ctx, 16)
+        w.run("serial")
+        assert w.status() == (0, -1)
+        want = O.encode_bf16_rne(_oracle_c(shards, b, dtype, 1.0, 1.0))
+        assert np.array_equal(raw(w.c), want)
+    finally:
+        w.close()
+
+
 @pytest.mark.parametrize("elem", [1, 2])
 def test_transpose_helper(gpu, elem):
     k, n = 300, 136
