@@ -228,7 +228,7 @@ __device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __re
 // started yet holds none back). With delays, job j*pieces + q starts no earlier than the j-th
 // cumulative delay after the first copying workgroup started.
 template <int NT>
-__device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job) {
+__device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job, int static_rank) {
   const uint32_t* order = a.scratch + kScrOrder;
   // every value that decides a branch around a barrier is made visibly uniform
   // (readfirstlane): otherwise the compiler may treat the loop exit as divergent and lay the
@@ -238,7 +238,15 @@ __device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job) {
   const uint32_t pieces = __builtin_amdgcn_readfirstlane((uint32_t)a.pieces);
   // the next job comes from a shared counter; once it is past the last job a plain load says so
   // (one uncontended read per workgroup at the end of the copy instead of an atomic add)
+  // (static_rank >= 0: this is copier static_rank of a.copy_wgs, which takes jobs static_rank,
+  // + copy_wgs, ... without a counter; only where no tile waits for a copy)
+  uint32_t fixed = static_rank >= 0 ? (uint32_t)static_rank : 0u;
   auto next_job = [&]() -> uint32_t {
+    if (static_rank >= 0) {
+      const uint32_t job = fixed;
+      fixed += (uint32_t)a.copy_wgs;
+      return job;
+    }
     if (tid == 0) {
       uint32_t j = jobs;
       if (__hip_atomic_load(a.scratch + kScrCopyNext, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < jobs)
@@ -355,6 +363,8 @@ __device__ inline bool claim(const GemmArgs& a, int home, int nstat, Tile& t) {
   const ListGeom g = list_geom(a, lane < L ? x : L);
   const uint32_t skip = static_taken(a, x, nstat, g.len);
   const uint32_t len = g.len - skip;
+  // no list has tiles past its static positions: nothing to claim, no counter to read
+  if (__ballot(len > 0) == 0) return false;
   uint32_t* ctr = a.scratch + kScrLists + x;
   for (;;) {
     const bool open = len > 0 && __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < len;
@@ -662,7 +672,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   const bool copier = a.copy_jobs && (int)blockIdx.x >= first_copier &&
                       (int)blockIdx.x < first_copier + a.copy_wgs;
   if (!(pull && copier)) claim_tile(true);
-  if (copier) produce_chunks<NT>(a, tid, &s_job);
+  // (pulled: no tile waits for a copy, so the copiers may deal the jobs among themselves)
+  if (copier) produce_chunks<NT>(a, tid, &s_job, pull ? (int)blockIdx.x - first_copier : -1);
   if (pull && copier) claim_tile(false);
 
   for (;; claim_tile(false)) {   // (an abandoned tile's `continue` claims the next one too)
