@@ -72,6 +72,14 @@ __device__ inline uint32_t lds64_off(int row, int g) {
   return (uint32_t)(row * kSliceBytes + ((g ^ ((row >> 1) & 3)) << 4));
 }
 
+// byte offset of 16-byte chunk `g` (0..7) of LDS row `row` in a 128-byte-row stage pair (two
+// consecutive 64-byte K slices of one tile row side by side): rows 2q and 2q+1 share a 256-byte
+// bank line, so chunks rotate with row/2; a ds_read_b128 of 16 consecutive rows at one chunk
+// touches every bank once
+__device__ inline uint32_t lds128_off(int row, int g) {
+  return (uint32_t)(row * (2 * kSliceBytes) + ((g ^ ((row >> 1) & 7)) << 4));
+}
+
 // Wait until at most N of this wave's vector loads are in flight and its LDS reads are done,
 // then meet the other waves. One asm block, so that no compiler fence drains every load.
 template <int N>
@@ -634,6 +642,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   // four stages of 64-byte K slices filled by direct-to-LDS loads
   constexpr int BNP = (BN + 63) / 64 * 64;                   // B rows held in LDS
   constexpr int DSTAGE = (BM + BNP) * kSliceBytes;
+  // Tiles above 128 x 128 (never split, so their K loop starts at slice 0) load K slices in
+  // pairs: an LDS row holds two consecutive 64-byte slices of a tile row, so that each load
+  // instruction fetches whole 128-byte lines (8 lanes per row) and the L1 sends half as many
+  // requests for the same bytes. The two pair regions (2 x DSTAGE each) replace the four stages;
+  // slice stage sg lies in region sg / 2, half sg % 2.
+  constexpr bool kPairs = !kSplitTiles;
   __shared__ __attribute__((aligned(1024))) uint8_t stages[kStages * DSTAGE];
   __shared__ int s_tile[4];
   __shared__ int s_ok;
@@ -723,19 +737,27 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     constexpr int NI = (BM + BNP) / (16 * NW);   // load instructions per wave per stage
     constexpr int NA = BM / (16 * NW);           // the first NA of them fetch A rows
     static_assert(BM % (16 * NW) == 0 && BNP % (16 * NW) == 0, "whole 16-row groups per wave");
-    // lane's chunk: rows of a 16-row group are lane/4, chunk position lane%4
+    // pairs: NL load instructions per wave per slice pair, 8 rows x 128 bytes each, the first NAL
+    // of them fetching A rows
+    constexpr int NL = kPairs ? 2 * NI : NI;
+    constexpr int NAL = kPairs ? 2 * NA : NA;
+    // lane's chunk: rows of a 16-row group are lane/4, chunk position lane%4 (pairs: rows of an
+    // 8-row group are lane/8, chunk position lane%8)
     const uint32_t gk = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) << 4);
-    uint32_t base[NI];
+    auto pair_row = [&](int j) { return (j * NW + wave) * 8 + (lane >> 3); };
+    auto pair_gk = [&](int r) { return (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) << 4); };
+    uint32_t base[NL];
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const int r = (j * NW + wave) * 16 + (lane >> 2);  // LDS row
-      if (j < NA) {
+    for (int j = 0; j < NL; ++j) {
+      const int r = kPairs ? pair_row(j) : (j * NW + wave) * 16 + (lane >> 2);  // LDS row
+      const uint32_t g = kPairs ? pair_gk(r) : gk;
+      if (j < NAL) {
         const int64_t gr = lo + r;
-        base[j] = gr < a.M ? (uint32_t)gr * (uint32_t)kbytes + gk : kOutOfRange;
+        base[j] = gr < a.M ? (uint32_t)gr * (uint32_t)kbytes + g : kOutOfRange;
       } else {
         const int c = r - BM;
         const int64_t gn = n0 + c;
-        base[j] = (c < BN && gn < a.N) ? (uint32_t)gn * (uint32_t)kbytes + gk : kOutOfRange;
+        base[j] = (c < BN && gn < a.N) ? (uint32_t)gn * (uint32_t)kbytes + g : kOutOfRange;
       }
     }
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -767,7 +789,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
           da = buffer_desc(a.peer[p], (uint32_t)(ms * kbytes));
           const uint32_t shift = (uint32_t)((int64_t)p * ms * kbytes);
 #pragma unroll
-          for (int j = 0; j < NA; ++j)
+          for (int j = 0; j < NAL; ++j)
             if (base[j] != kOutOfRange) base[j] -= shift;
         }
       }
@@ -777,9 +799,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     // Load j of a slice (j < NI): A rows for j < NA, else B rows. The LDS stage of slice t is
     // (t - t_lo) % 4; the main loop runs four slices per trip, so every stage is a constant.
     auto desc_of = [&](int j) -> const u32x4& {
-      return j < NA ? (kGroupPull ? dag[j < NA ? j : 0] : da) : db;
+      return j < NAL ? (kGroupPull ? dag[j < NA ? j : 0] : da) : db;
     };
     auto m0_of = [&](int sg, int j) { return lds0 + (uint32_t)sg * DSTAGE + (uint32_t)j * (NW * 1024u); };
+    // pairs: LDS address of load j into pair region rg
+    auto m0p = [&](int rg, int j) { return lds0 + (uint32_t)rg * (2 * DSTAGE) + (uint32_t)j * (NW * 1024u); };
     // K byte offset of load j of slice t. Slices below t_safe lie wholly inside the part's K
     // range: a plain offset. Otherwise (`masked`) the offset's top bit is set past the K end
     // (out of range: reads zero), lane by lane, since a slice may straddle the end.
@@ -793,8 +817,40 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         return base[j] + tk;
       }
     };
+    // pairs: K byte offset of load j of slice pair pr (slices 2pr and 2pr+1), masked as above
+    auto voffp = [&](auto masked, int pr, int j) -> uint32_t {
+      const uint32_t pk = (uint32_t)pr * (2 * kSliceBytes);
+      if constexpr (decltype(masked)::value) {
+        const uint32_t oob = (uint32_t)((int)(pk + pair_gk(pair_row(j)) - kend) >> 31) ^ 0xFFFFFFFFu;
+        return (base[j] + pk) | (oob & kOutOfRange);
+      } else {
+        return base[j] + pk;
+      }
+    };
     auto issue_one = [&](auto masked, int t, int sg, int j) {
       lds_dma_load(desc_of(j), m0_of(sg, j), voff_of(masked, t, j));
+    };
+    // The loads a slice issues, as (load index, LDS address, offset). Four stages: in the first
+    // half of slice t, loads NH.. of slice t+3 into stage (t+3)%4; in the second half, loads
+    // 0..NH-1 of slice t+4 into stage t%4. Pairs: an even slice t issues, in its first half, the
+    // second half of the loads of pair t/2+1 into the other region; an odd slice t, in its second
+    // half, the first half of the loads of pair (t+1)/2+1 into its own region (whose pair every
+    // wave has finished at the odd slice's barrier).
+    struct Ld { int j; uint32_t m0, vo; };
+    auto ld_first = [&](auto masked, auto u_, int t, int e) -> Ld {
+      constexpr int U = decltype(u_)::value;
+      if constexpr (kPairs) {
+        const int j = NL / 2 + e;
+        return Ld{j, m0p((U >> 1) ^ 1, j), voffp(masked, t / 2 + 1, j)};
+      } else {
+        const int j = NI / 2 + e;
+        return Ld{j, m0_of((U + 3) & 3, j), voff_of(masked, t + 3, j)};
+      }
+    };
+    auto ld_second = [&](auto masked, auto u_, int t, int k) -> Ld {
+      constexpr int U = decltype(u_)::value;
+      if constexpr (kPairs) return Ld{k, m0p(U >> 1, k), voffp(masked, (t + 1) / 2 + 1, k)};
+      else return Ld{k, m0_of(U, k), voff_of(masked, t + 4, k)};
     };
     constexpr int NH = NI / 2;                 // loads of a slice issued in the earlier half
     // The slice schedule, for both dtypes: RM x CN MFMA blocks per wave and slice, operand
@@ -816,16 +872,22 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       using F = decltype(fa);
       constexpr int RB = RM / 2;                 // block rows before the barrier
       constexpr int S1 = RB * CN, S2 = (RM - RB) * CN;
-      constexpr int E1 = NI - NH, E2 = CN + 1 + NH;
       static_assert(RM - RB - 1 <= RB, "the A fragments after the barrier are loaded before it");
       auto slice = [&](auto u_, auto masked, F (&fbc)[CN], F (&fbn)[CN], int t) {
         constexpr int U = decltype(u_)::value;
-        constexpr int U1 = (U + 1) & 3, U3 = (U + 3) & 3;
+        constexpr int U1 = (U + 1) & 3;
+        // loads issued in the first half (E1) and in the second half (ND) of this slice
+        constexpr int E1 = kPairs ? ((U & 1) ? 0 : NL / 2) : NI - NH;
+        constexpr int ND = kPairs ? ((U & 1) ? NL / 2 : 0) : NH;
+        constexpr int E2 = CN + 1 + ND;
         F far[RM];
         far[0] = fa;
         if (S1 == 0) {                            // no MFMA before the barrier: issue plainly
 #pragma unroll
-          for (int e = 0; e < E1; ++e) issue_one(masked, t + 3, U3, NH + e);
+          for (int e = 0; e < E1; ++e) {
+            const Ld l = ld_first(masked, u_, t, e);
+            lds_dma_load(desc_of(l.j), l.m0, l.vo);
+          }
         }
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
@@ -837,19 +899,21 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
             bool fused = false;
 #pragma unroll
             for (int e = 0; e < E1; ++e) {
-              if (S1 == 0 || e * S1 / E1 != q) continue;
-              const int jj = NH + e;
+              if (S1 == 0 || e * S1 / (E1 > 0 ? E1 : 1) != q) continue;
+              const Ld l = ld_first(masked, u_, t, e);
               if (!fused) {
-                mma_dma(accs[i][j], fbc[j], far[i], desc_of(jj), m0_of(U3, jj), voff_of(masked, t + 3, jj));
+                mma_dma(accs[i][j], fbc[j], far[i], desc_of(l.j), l.m0, l.vo);
                 fused = true;
               } else {
-                issue_one(masked, t + 3, U3, jj);
+                lds_dma_load(desc_of(l.j), l.m0, l.vo);
               }
             }
             if (!fused) mma(accs[i][j], fbc[j], far[i]);
           }
         }
-        stage_barrier<2 * NI>();
+        // slice t+1 has landed (four stages: all but the 2*NI loads issued since; pairs, odd t:
+        // all of pair (t+1)/2, the last loads issued; even t: all but the NL of pair t/2+1)
+        stage_barrier<kPairs ? ((U & 1) ? 0 : NL) : 2 * NI>();
 #pragma unroll
         for (int i = RB; i < RM; ++i) {
 #pragma unroll
@@ -862,8 +926,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
             for (int e = CN + 1; e < E2; ++e)
               if (fuse_e < 0 && e * S2 / E2 == q) fuse_e = e;
             if (fuse_e >= 0) {
-              const int jj = fuse_e - CN - 1;
-              mma_dma(accs[i][j], fbc[j], far[i], desc_of(jj), m0_of(U, jj), voff_of(masked, t + 4, jj));
+              const Ld l = ld_second(masked, u_, t, fuse_e - CN - 1);
+              mma_dma(accs[i][j], fbc[j], far[i], desc_of(l.j), l.m0, l.vo);
             } else {
               mma(accs[i][j], fbc[j], far[i]);
             }
@@ -872,7 +936,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
               if (e * S2 / E2 != q || e == fuse_e) continue;   // request e goes after MFMA slot e*S2/E2
               if (e < CN) fbn[e] = ldb(U1, e);
               else if (e == CN) fa = lda(U1, 0);
-              else issue_one(masked, t + 4, U, e - CN - 1);
+              else {
+                const Ld l = ld_second(masked, u_, t, e - CN - 1);
+                lds_dma_load(desc_of(l.j), l.m0, l.vo);
+              }
             }
           }
         }
@@ -882,13 +949,22 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         acc_settle(accs);
         constexpr auto kPlain = std::integral_constant<bool, false>{};
         constexpr auto kMasked = std::integral_constant<bool, true>{};
+        if constexpr (kPairs) {
+          // pair 0 whole and the first half of pair 1 (the first slice issues the rest)
 #pragma unroll
-        for (int s = 0; s < 3; ++s)
+          for (int j = 0; j < NL; ++j) lds_dma_load(desc_of(j), m0p(0, j), voffp(kMasked, t_lo / 2, j));
 #pragma unroll
-          for (int j = 0; j < NI; ++j) issue_one(kMasked, t_lo + s, s, j);
+          for (int j = 0; j < NL / 2; ++j) lds_dma_load(desc_of(j), m0p(1, j), voffp(kMasked, t_lo / 2 + 1, j));
+          stage_barrier<NL / 2>();
+        } else {
 #pragma unroll
-        for (int j = 0; j < NH; ++j) issue_one(kMasked, t_lo + 3, 3, j);   // the first slice issues the rest
-        stage_barrier<2 * NI + NH>();
+          for (int s = 0; s < 3; ++s)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) issue_one(kMasked, t_lo + s, s, j);
+#pragma unroll
+          for (int j = 0; j < NH; ++j) issue_one(kMasked, t_lo + 3, 3, j);   // the first slice issues the rest
+          stage_barrier<2 * NI + NH>();
+        }
 #pragma unroll
         for (int j = 0; j < CN; ++j) fb0[j] = ldb(0, j);
         fa = lda(0, 0);
@@ -913,6 +989,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
     };
+    // LDS byte offset of 16-byte chunk g (0..3) of row `row` of slice stage sg
+    auto frag_off = [&](int sg, int row, int g) -> uint32_t {
+      if constexpr (kPairs) return (uint32_t)((sg >> 1) * (2 * DSTAGE)) + lds128_off(row, (sg & 1) * 4 + g);
+      else return (uint32_t)(sg * DSTAGE) + lds64_off(row, g);
+    };
     if constexpr (!FP8) {
       // ---- bf16: 16x16x32 MFMA blocks, one 16-byte fragment per lane
 #pragma unroll
@@ -921,11 +1002,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       auto ldb = [&](int sg, int j) {
         return *reinterpret_cast<const u32x4*>(
-            stages + sg * DSTAGE + lds64_off(BM + wn * WTN + j * 16 + (lane & 15), lane >> 4));
+            stages + frag_off(sg, BM + wn * WTN + j * 16 + (lane & 15), lane >> 4));
       };
       auto lda = [&](int sg, int i) {
         return *reinterpret_cast<const u32x4*>(
-            stages + sg * DSTAGE + lds64_off(wm * WTM + i * 16 + (lane & 15), lane >> 4));
+            stages + frag_off(sg, wm * WTM + i * 16 + (lane & 15), lane >> 4));
       };
       run_slices(acc, u32x4{}, lda, ldb,
                  [](f32x4& c, const u32x4& b, const u32x4& x) { mfma_bf16(c, b, x); },
@@ -944,10 +1025,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         for (int j = 0; j < F8N; ++j) acc8[i][j] = f32x16{};
       // a 32-row fp8 fragment: row r + (lane & 31), K bytes 32*(lane/32) .. +31 of the slice
       auto frag8 = [&](int sg, int r) {
-        const uint8_t* st = stages + sg * DSTAGE;
         const int row = r + (lane & 31), g = (lane >> 5) * 2;
-        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(st + lds64_off(row, g));
-        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(st + lds64_off(row, g + 1));
+        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(stages + frag_off(sg, row, g));
+        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(stages + frag_off(sg, row, g + 1));
         return i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
                      (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
       };
