@@ -305,6 +305,7 @@ KSplit ksplit_for(agg_ctx* ctx, TileShape ts, int dtype, int64_t tiles, int64_t 
     const int64_t nk = std::max<int64_t>(1, (kb + slice_bytes(dtype) - 1) / slice_bytes(dtype));
     const int64_t s = std::min<int64_t>(ctx->force_split, nk);
     ks.kps = int((nk + s - 1) / s);
+    ks.kps += ks.kps & 1;                   // parts start on whole slice pairs
     ks.ksplit = int((nk + ks.kps - 1) / ks.kps);
   }
   return ks;

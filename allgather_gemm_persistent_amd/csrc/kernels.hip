@@ -642,13 +642,16 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   // four stages of 64-byte K slices filled by direct-to-LDS loads
   constexpr int BNP = (BN + 63) / 64 * 64;                   // B rows held in LDS
   constexpr int DSTAGE = (BM + BNP) * kSliceBytes;
-  // Tiles above 128 x 128 (never split, so their K loop starts at slice 0) load K slices in
-  // pairs: an LDS row holds two consecutive 64-byte slices of a tile row, so that each load
-  // instruction fetches whole 128-byte lines (8 lanes per row) and the L1 sends half as many
-  // requests for the same bytes. The two pair regions (2 x DSTAGE each) replace the four stages;
-  // slice stage sg lies in region sg / 2, half sg % 2.
-  constexpr bool kPairs = !kSplitTiles;
-  __shared__ __attribute__((aligned(1024))) uint8_t stages[kStages * DSTAGE];
+  // Tiles of 128 x 64 and larger load K slices in pairs: an LDS row holds two consecutive 64-byte
+  // slices of a tile row, so that each load instruction fetches whole 128-byte lines (8 lanes per
+  // row) and the L1 sends half as many requests for the same bytes. kRegions pair regions of
+  // 2 x DSTAGE bytes each replace the four stages; slice stage sg lies in region sg / 2, half
+  // sg % 2. The big tiles have room for two regions; the split-K tiles take four (a longer lead
+  // for their latency-bound loads; split parts start on whole pairs). 64 x 64 tiles, whose short
+  // K loops measured faster with the four 64-byte stages, keep those.
+  constexpr bool kPairs = BM * BN >= 128 * 64;
+  constexpr int kRegions = kSplitTiles ? 4 : 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t stages[kPairs ? kRegions * 2 * DSTAGE : kStages * DSTAGE];
   __shared__ int s_tile[4];
   __shared__ int s_ok;
   __shared__ int s_job;
@@ -741,6 +744,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     // of them fetching A rows
     constexpr int NL = kPairs ? 2 * NI : NI;
     constexpr int NAL = kPairs ? 2 * NA : NA;
+    static_assert(!kPairs || (kRegions - 1) * NL < 64, "loads in flight within the vmcnt range");
     // lane's chunk: rows of a 16-row group are lane/4, chunk position lane%4 (pairs: rows of an
     // 8-row group are lane/8, chunk position lane%8)
     const uint32_t gk = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) << 4);
@@ -765,17 +769,17 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     // whose 16-row group lies in one shard when shards are multiples of 16 rows
     constexpr bool kGroupPull = BM <= 128;
     u32x4 da = buffer_desc(a.a, (uint32_t)(a.M * kbytes));
-    u32x4 dag[kGroupPull ? NA : 1];
+    u32x4 dag[kGroupPull ? NAL : 1];
 #pragma unroll
-    for (int j = 0; j < (kGroupPull ? NA : 1); ++j) dag[j] = da;
+    for (int j = 0; j < (kGroupPull ? NAL : 1); ++j) dag[j] = da;
     if (pull) {
       // remote rows are read from the peer's block: rebase those A offsets from gather-buffer
       // rows to block rows
       const int64_t ms = (int64_t)a.chunk_rows * a.cps;
       if constexpr (kGroupPull) {
 #pragma unroll
-        for (int j = 0; j < NA; ++j) {
-          const int64_t g0 = lo + (int64_t)(j * NW + wave_u) * 16;  // first row of the group
+        for (int j = 0; j < NAL; ++j) {
+          const int64_t g0 = lo + (int64_t)(j * NW + wave_u) * (kPairs ? 8 : 16);  // first row of the group
           const int p = (int)(g0 / ms);
           if (g0 < a.M && p != a.rank) {
             dag[j] = buffer_desc(a.peer[p], (uint32_t)(ms * kbytes));
@@ -799,7 +803,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     // Load j of a slice (j < NI): A rows for j < NA, else B rows. The LDS stage of slice t is
     // (t - t_lo) % 4; the main loop runs four slices per trip, so every stage is a constant.
     auto desc_of = [&](int j) -> const u32x4& {
-      return j < NAL ? (kGroupPull ? dag[j < NA ? j : 0] : da) : db;
+      return j < NAL ? (kGroupPull ? dag[j < NAL ? j : 0] : da) : db;
     };
     auto m0_of = [&](int sg, int j) { return lds0 + (uint32_t)sg * DSTAGE + (uint32_t)j * (NW * 1024u); };
     // pairs: LDS address of load j into pair region rg
@@ -841,7 +845,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       constexpr int U = decltype(u_)::value;
       if constexpr (kPairs) {
         const int j = NL / 2 + e;
-        return Ld{j, m0p((U >> 1) ^ 1, j), voffp(masked, t / 2 + 1, j)};
+        return Ld{j, m0p(((U >> 1) + kRegions - 1) % kRegions, j), voffp(masked, t / 2 + kRegions - 1, j)};
       } else {
         const int j = NI / 2 + e;
         return Ld{j, m0_of((U + 3) & 3, j), voff_of(masked, t + 3, j)};
@@ -849,7 +853,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     };
     auto ld_second = [&](auto masked, auto u_, int t, int k) -> Ld {
       constexpr int U = decltype(u_)::value;
-      if constexpr (kPairs) return Ld{k, m0p(U >> 1, k), voffp(masked, (t + 1) / 2 + 1, k)};
+      if constexpr (kPairs) return Ld{k, m0p(U >> 1, k), voffp(masked, (t + 1) / 2 + kRegions - 1, k)};
       else return Ld{k, m0_of(U, k), voff_of(masked, t + 4, k)};
     };
     constexpr int NH = NI / 2;                 // loads of a slice issued in the earlier half
@@ -875,7 +879,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       static_assert(RM - RB - 1 <= RB, "the A fragments after the barrier are loaded before it");
       auto slice = [&](auto u_, auto masked, F (&fbc)[CN], F (&fbn)[CN], int t) {
         constexpr int U = decltype(u_)::value;
-        constexpr int U1 = (U + 1) & 3;
+        constexpr int U1 = (U + 1) % (kPairs ? 2 * kRegions : 4);
         // loads issued in the first half (E1) and in the second half (ND) of this slice
         constexpr int E1 = kPairs ? ((U & 1) ? 0 : NL / 2) : NI - NH;
         constexpr int ND = kPairs ? ((U & 1) ? NL / 2 : 0) : NH;
@@ -913,7 +917,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         }
         // slice t+1 has landed (four stages: all but the 2*NI loads issued since; pairs, odd t:
         // all of pair (t+1)/2, the last loads issued; even t: all but the NL of pair t/2+1)
-        stage_barrier<kPairs ? ((U & 1) ? 0 : NL) : 2 * NI>();
+        stage_barrier<kPairs ? ((U & 1) ? (kRegions - 2) * NL : (kRegions - 1) * NL) : 2 * NI>();
 #pragma unroll
         for (int i = RB; i < RM; ++i) {
 #pragma unroll
@@ -950,12 +954,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         constexpr auto kPlain = std::integral_constant<bool, false>{};
         constexpr auto kMasked = std::integral_constant<bool, true>{};
         if constexpr (kPairs) {
-          // pair 0 whole and the first half of pair 1 (the first slice issues the rest)
+          // pairs 0 .. R-2 whole and the first half of pair R-1 (the first slice issues the rest)
 #pragma unroll
-          for (int j = 0; j < NL; ++j) lds_dma_load(desc_of(j), m0p(0, j), voffp(kMasked, t_lo / 2, j));
+          for (int q = 0; q + 1 < kRegions; ++q)
 #pragma unroll
-          for (int j = 0; j < NL / 2; ++j) lds_dma_load(desc_of(j), m0p(1, j), voffp(kMasked, t_lo / 2 + 1, j));
-          stage_barrier<NL / 2>();
+            for (int j = 0; j < NL; ++j) lds_dma_load(desc_of(j), m0p(q, j), voffp(kMasked, t_lo / 2 + q, j));
+#pragma unroll
+          for (int j = 0; j < NL / 2; ++j)
+            lds_dma_load(desc_of(j), m0p(kRegions - 1, j), voffp(kMasked, t_lo / 2 + kRegions - 1, j));
+          stage_barrier<(kRegions - 2) * NL + NL / 2>();
         } else {
 #pragma unroll
           for (int s = 0; s < 3; ++s)
@@ -970,19 +977,23 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         fa = lda(0, 0);
         // four slices per trip (slices past the part's end read zeros); a trip whose loads
         // (up to slice t+7) stay below t_safe needs no K-end masks
+        // (pairs: 2R slices per trip, whose loads reach slice t + 4R - 1)
+        constexpr int TRIP = kPairs ? 2 * kRegions : 4;
+        auto trip = [&](auto masked, int t) {
+          slice(std::integral_constant<int, 0>{}, masked, fb0, fb1, t);
+          slice(std::integral_constant<int, 1>{}, masked, fb1, fb0, t + 1);
+          slice(std::integral_constant<int, 2>{}, masked, fb0, fb1, t + 2);
+          slice(std::integral_constant<int, 3>{}, masked, fb1, fb0, t + 3);
+          if constexpr (TRIP == 8) {
+            slice(std::integral_constant<int, 4>{}, masked, fb0, fb1, t + 4);
+            slice(std::integral_constant<int, 5>{}, masked, fb1, fb0, t + 5);
+            slice(std::integral_constant<int, 6>{}, masked, fb0, fb1, t + 6);
+            slice(std::integral_constant<int, 7>{}, masked, fb1, fb0, t + 7);
+          }
+        };
         int t = t_lo;
-        for (; t + 7 < t_safe; t += 4) {
-          slice(std::integral_constant<int, 0>{}, kPlain, fb0, fb1, t);
-          slice(std::integral_constant<int, 1>{}, kPlain, fb1, fb0, t + 1);
-          slice(std::integral_constant<int, 2>{}, kPlain, fb0, fb1, t + 2);
-          slice(std::integral_constant<int, 3>{}, kPlain, fb1, fb0, t + 3);
-        }
-        for (; t < t_hi; t += 4) {
-          slice(std::integral_constant<int, 0>{}, kMasked, fb0, fb1, t);
-          slice(std::integral_constant<int, 1>{}, kMasked, fb1, fb0, t + 1);
-          slice(std::integral_constant<int, 2>{}, kMasked, fb0, fb1, t + 2);
-          slice(std::integral_constant<int, 3>{}, kMasked, fb1, fb0, t + 3);
-        }
+        for (; t + (kPairs ? 4 * kRegions : 8) - 1 < t_safe; t += TRIP) trip(kPlain, t);
+        for (; t < t_hi; t += TRIP) trip(kMasked, t);
         acc_settle(accs);
         // loads issued past the end land (as zeros) and every wave is done with LDS before the
         // next tile refills it

@@ -72,7 +72,8 @@ KSplit choose_ksplit(int op, int dtype, int64_t tiles, int64_t k, int units) {
   if (op != 0 || tiles <= 0 || tiles * 2 > units || tiles > kMaxSplitTiles) return r;
   int64_t s = std::min<int64_t>({int64_t(units) / tiles, nk / 16, int64_t(kAutoKSplit)});
   if (s < 2) return r;
-  const int64_t kps = (nk + s - 1) / s;
+  int64_t kps = (nk + s - 1) / s;
+  kps += kps & 1;                         // parts start on whole slice pairs
   r.kps = int(kps);
   r.ksplit = int((nk + kps - 1) / kps);   // no empty part
   return r;
