@@ -164,11 +164,13 @@ int agg_ctx_set_tile(agg_ctx* ctx, int bm, int bn);
 /* Split-K of later AllGather+GEMM calls. With few output tiles (fewer than half the CUs) and a
  * long K, the library cuts each tile's K range into parts computed by different workgroups;
  * every part writes an fp32 partial into a ctx-owned buffer (ksplit x M x N floats, allocated
- * and grown by the ctx) and the last part to finish sums the parts in part order, so C does not
- * depend on which part finishes last. `ksplit` 1..16 forces that many parts (at most one per K
- * slice) for tiles of up to 128 x 128 (larger tiles are never split), 0 restores the automatic
- * choice. A chunk wait that times out leaves split-K tile
- * counters behind: call agg_ctx_reset before the next call. */
+ * and grown by the ctx) and the parts are summed in part order (by the last part to finish, or,
+ * when every part has a workgroup of its own, by all parts together, a row range each), so C
+ * does not depend on which part finishes last. `ksplit` 1..16 asks for that many parts for
+ * tiles of up to 128 x 128 (larger tiles are never split); parts span a whole number of 64-byte
+ * K slice pairs, so fewer parts may result (at most one per pair). 0 restores the automatic
+ * choice. A chunk wait that times out leaves split-K tile counters behind: call agg_ctx_reset
+ * before the next call. */
 int agg_ctx_set_split(agg_ctx* ctx, int ksplit);
 
 /* Tile-claim lists of later calls. The persistent workgroups claim tiles from `lists` lists
