@@ -58,8 +58,9 @@ __device__ inline uint32_t load_flag(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// ---- operand pipeline: 64-byte K slices (32 bf16 or 64 fp8 elements), four LDS stages filled by
-// direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds). One wave instruction writes 1 KiB of
+// ---- operand pipeline: 64-byte K slices (32 bf16 or 64 fp8 elements) in LDS, filled by
+// direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): four 64-byte stages, or (tiles of
+// 128 x 64 and up) regions of slice pairs with 128-byte rows. One wave instruction writes 1 KiB of
 // LDS: 16 tile rows of 64 bytes, lane i landing at byte 16*i. Lane i therefore fetches row i/4
 // of its 16-row group and the 16-byte chunk that the swizzle below puts at position i%4.
 constexpr int kSliceBytes = 64;
@@ -639,7 +640,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   // 32x32 block holds 4 of them per lane
   constexpr int FM = WTM / BLK, FN = (WTN / BLK) * (FP8 ? 4 : 1);
 
-  // four stages of 64-byte K slices filled by direct-to-LDS loads
+  // 64-byte K slices filled by direct-to-LDS loads, in four stages or in regions of slice pairs
   constexpr int BNP = (BN + 63) / 64 * 64;                   // B rows held in LDS
   constexpr int DSTAGE = (BM + BNP) * kSliceBytes;
   // Tiles of 128 x 64 and larger load K slices in pairs: an LDS row holds two consecutive 64-byte
@@ -734,7 +735,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
 
-    // ---- K loop: four LDS stages of 64-byte K slices, filled by direct-to-LDS buffer loads
+    // ---- K loop: 64-byte K slices in LDS stages or pair regions, filled by direct-to-LDS loads
     // (out-of-range rows and the K tail read zeros through the buffer descriptor's range check)
     f32x4 acc[FM][FN];
     constexpr int NI = (BM + BNP) / (16 * NW);   // load instructions per wave per stage
@@ -800,8 +801,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     }
     const u32x4 db = buffer_desc(a.b, (uint32_t)(a.N * kbytes));
     const uint32_t lds0 = lds_addr(stages) + (uint32_t)wave_u * 1024u;
-    // Load j of a slice (j < NI): A rows for j < NA, else B rows. The LDS stage of slice t is
-    // (t - t_lo) % 4; the main loop runs four slices per trip, so every stage is a constant.
+    // Load j of a slice (j < NI; pairs: of a slice pair, j < NL): A rows for j < NA (NAL), else B
+    // rows. The LDS stage of slice t is (t - t_lo) % 4 (pairs: region ((t - t_lo) / 2) % R); the
+    // main loop runs four (pairs: 2R) slices per trip, so every stage and region is a constant.
     auto desc_of = [&](int j) -> const u32x4& {
       return j < NAL ? (kGroupPull ? dag[j < NAL ? j : 0] : da) : db;
     };
@@ -867,7 +869,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     // requested row by row, and the loads NH..NI-1 of slice t+3 go between the MFMAs. Then the
     // waves meet (slice t+1 has landed everywhere; every wave has read all of slice t), and the
     // second half spreads slice t+1's B fragments and first A fragment, then the loads 0..NH-1
-    // of slice t+4, between its MFMAs. A load that follows an MFMA shares its asm statement
+    // of slice t+4, between its MFMAs. (Pairs: the same two halves carry the pair loads that
+    // ld_first / ld_second describe.) A load that follows an MFMA shares its asm statement
     // (mma_dma), so the MFMA is the wait state between the M0 write and the load.
     auto run_slices = [&](auto& accs, auto fa, auto lda, auto ldb, auto mma, auto mma_dma,
                           auto rm_, auto cn_, auto lone_) {
@@ -924,7 +927,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
           for (int j = 0; j < CN; ++j) {
             const int q = (i - RB) * CN + j;
             if (kLone) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-            // the first load of slice t+4 scheduled after this MFMA is fused with it
+            // the first second-half load scheduled after this MFMA is fused with it
             int fuse_e = -1;
 #pragma unroll
             for (int e = CN + 1; e < E2; ++e)
@@ -1079,9 +1082,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       // partial and reduction code would cost the big tiles registers in their main loop
       if (kSplitTiles && a.ksplit > 1) {
         // split-K: every part writes its fp32 partial (write-through) and counts itself in; the
-        // part that arrives last reads all parts back and sums them in part order (so the sum
-        // does not depend on which part is last), then converts and stores the tile. The
-        // partial loads are system-coherent: a stale line of an earlier launch must not be read.
+        // parts are summed in part order (so the sum does not depend on which part is last),
+        // by all parts together or by the part that arrives last, then converted and stored.
+        // The partial loads are system-coherent: a stale line of an earlier launch must not be
+        // read.
         const int64_t plane = a.M * a.N;
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
             a.ws, 0, (int)(a.ksplit * plane * 4), kBufferFlags);
