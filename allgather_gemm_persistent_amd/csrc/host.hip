@@ -798,6 +798,8 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
     g.n_col_tiles = int((n + ts.bn - 1) / ts.bn);
     const KSplit ks = ksplit_for(ctx, ts, dtype, int64_t(g.n_row_tiles) * g.n_col_tiles, k);
     if (ks.ksplit > 1) {
+      // the kernel's slice-pair pipeline starts every part on a whole pair
+      if (ks.kps & 1) return fail(AGG_E_STATE, "split-K part of %d slices (must be even)", ks.kps);
       if (int64_t(g.n_row_tiles) * g.n_col_tiles > kMaxSplitTiles)
         return fail(AGG_E_UNSUPPORTED, "split-K over more than %d tiles", kMaxSplitTiles);
       const size_t ws_bytes = size_t(ks.ksplit) * size_t(m) * size_t(n) * sizeof(float);
