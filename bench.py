@@ -9,8 +9,10 @@ MFMA main loop and the bf16 epilogue, and the join. Inputs are resident in HBM b
 
 Printed (one JSON line): overlapped TFLOP/s (value), % of the bf16 MFMA peak, the overlap
 figures R = T_ovl / T_gemm and eta = (T_serial - T_ovl) / min(T_copy, T_gemm) from the same
-kernels in the other modes, the dominant kernel's roofline (its own duration from timing events
-on the stream it runs on), and the CPU oracle's rate on the same workload as a baseline.
+kernels in the other modes (per-call stream times with the modes interleaved call by call; the
+t_*_us fields are the modes timed one after another, which the board's clock drift skews), the
+dominant kernel's roofline (its own duration from timing events on the stream it runs on), and
+the CPU oracle's rate on the same workload as a baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -166,20 +168,30 @@ def main():
             t_copy = time_mode(w, "copy_only", order, args.steps, args.warmup)
         if "serial" in modes:
             t_serial = time_mode(w, "serial", order, args.steps, args.warmup)
-        # overlapped and bare launches interleaved call by call, so that both see the same clock
-        # and temperature (the clock drops as the board heats within a run)
-        k_int = None
+        # every mode again, interleaved call by call, so that all see the same clock and
+        # temperature (the clock drops as the board heats within a run, so modes timed one after
+        # another are not comparable): per-call stream time from events around each call, and
+        # the consumer kernels' own durations
+        k_int = s_int = None
+        inter = [m for m in ("overlap", "gemm_only", "copy_only", "serial") if m == "overlap" or m in modes]
         if "gemm_only" in modes:
             B.agg_ctx_set_timing(w.ctx, True)
-            seq = []
+            seq, ev = [], []
             for _ in range(args.steps):
-                for m in ("overlap", "gemm_only"):
+                for m in inter:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(bench_stream)
                     w.run(m, order=order)
-                    seq.append(m)
+                    e1.record(bench_stream)
+                    ev.append((m, e0, e1))
+                    seq.append(m)          # every mode times one consumer launch per call
             torch.cuda.synchronize()
             ks = B.agg_ctx_kernel_times(w.ctx, len(seq))
             k_int = {m: statistics.median([k * 1e3 for k, q in zip(ks, seq) if q == m])
                      for m in ("overlap", "gemm_only")}
+            s_int = {m: statistics.median([a.elapsed_time(b) * 1e3 for q, a, b in ev if q == m])
+                     for m in inter}
         other = {"cu": "sdma", "sdma": "cu"}[args.producer]
         t_ovl_other = None
         if other in modes:
@@ -196,8 +208,12 @@ def main():
 
     def rnd(x, d=1):
         return None if x is None else round(x, d)
-    full = None not in (t_gemm, t_copy, t_serial)
-    eta = (t_serial - t_ovl) / min(t_copy, t_gemm) if full else None
+    # R and eta from the interleaved per-call times (same clock for every mode)
+    R = eta = None
+    if s_int and "gemm_only" in s_int:
+        R = s_int["overlap"] / s_int["gemm_only"]
+        if "copy_only" in s_int and "serial" in s_int:
+            eta = (s_int["serial"] - s_int["overlap"]) / min(s_int["copy_only"], s_int["gemm_only"])
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -220,7 +236,8 @@ def main():
         "pct_mfma_peak": round(100 * value / peak, 2),
         "overlap": {"t_ovl_us": round(t_ovl, 1), "t_gemm_us": rnd(t_gemm),
                     "t_copy_us": rnd(t_copy), "t_serial_us": rnd(t_serial),
-                    "R": rnd(t_ovl / t_gemm, 3) if t_gemm else None, "eta": rnd(eta, 3),
+                    "R": rnd(R, 3), "eta": rnd(eta, 3),
+                    "interleaved_call_us": ({m: rnd(v) for m, v in s_int.items()} if s_int else None),
                     "interleaved_kernel_us": ({"overlap": rnd(k_int["overlap"]),
                                                "gemm_only": rnd(k_int["gemm_only"]),
                                                "R": rnd(k_int["overlap"] / k_int["gemm_only"], 3)}
