@@ -111,8 +111,8 @@ def cpu_baseline(cfg, data):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build runs one rank's share of the collective "
-              f"on one MI355X); --gpus {args.gpus} is not supported.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (one rank's share of the collective on one MI355X); "
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
     import torch
 
