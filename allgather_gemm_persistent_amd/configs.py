@@ -95,29 +95,29 @@ N1 = {"kind": "normal", "std": 1.0}
 N002 = {"kind": "normal", "std": 0.02}
 
 CONFIGS = {
-    # 1: tiny, latency-bound; oracle in milliseconds
-    "c1_ag_w2_tiny": AgConfig("c1_ag_w2_tiny", world=2, rank=0, m_shard=128, k=512, n=256,
-                              dtype="bf16", chunk_rows=64, a_dist=U11, b_dist=U11,
-                              order_kind="seeded", seed=1010),
-    # 2: the MFMA-bound bf16 workload (the headline)
-    "c2_ag_w8_bf16": AgConfig("c2_ag_w8_bf16", world=8, rank=0, m_shard=512, k=8192, n=3584,
-                              dtype="bf16", chunk_rows=128, a_dist=N1, b_dist=N002,
-                              order_kind="ring", seed=1020, with_delays=True),
-    # 3: GEMM + ReduceScatter, 7 incoming fp32 partial blocks
-    "c3_rs_w8_bf16": RsConfig("c3_rs_w8_bf16", world=8, rank=0, m=8192, k=3584, n=8192,
-                              chunk_rows=128, a_dist=N1, b_dist=N002, peer_dist=N1,
-                              order_kind="seeded", seed=1030),
-    # 4: decode-shaped, HBM-bound
-    "c4_ag_w8_decode": AgConfig("c4_ag_w8_decode", world=8, rank=0, m_shard=16, k=8192, n=3584,
-                                dtype="bf16", chunk_rows=16, a_dist=N1, b_dist=N002,
-                                order_kind="ring", seed=1040),
-    # 5: fp8 e4m3fn with per-tensor scales
-    "c5_ag_w8_fp8": AgConfig("c5_ag_w8_fp8", world=8, rank=0, m_shard=1024, k=8192, n=7168,
-                             dtype="fp8", chunk_rows=256, a_dist=N1, b_dist=N002,
-                             order_kind="seeded", seed=1050),
+    # tiny, latency-bound; the oracle takes milliseconds
+    "ag_w2_256x256x512_bf16": AgConfig(
+        "ag_w2_256x256x512_bf16", world=2, rank=0, m_shard=128, k=512, n=256, dtype="bf16",
+        chunk_rows=64, a_dist=U11, b_dist=U11, order_kind="seeded", seed=1010),
+    # the MFMA-bound bf16 workload (the benchmark's)
+    "ag_w8_4096x3584x8192_bf16": AgConfig(
+        "ag_w8_4096x3584x8192_bf16", world=8, rank=0, m_shard=512, k=8192, n=3584, dtype="bf16",
+        chunk_rows=128, a_dist=N1, b_dist=N002, order_kind="ring", seed=1020, with_delays=True),
+    # GEMM + ReduceScatter, 7 incoming fp32 partial blocks
+    "rs_w8_8192x8192x3584_bf16": RsConfig(
+        "rs_w8_8192x8192x3584_bf16", world=8, rank=0, m=8192, k=3584, n=8192, chunk_rows=128,
+        a_dist=N1, b_dist=N002, peer_dist=N1, order_kind="seeded", seed=1030),
+    # decode-shaped, HBM-bound
+    "ag_w8_128x3584x8192_bf16_decode": AgConfig(
+        "ag_w8_128x3584x8192_bf16_decode", world=8, rank=0, m_shard=16, k=8192, n=3584,
+        dtype="bf16", chunk_rows=16, a_dist=N1, b_dist=N002, order_kind="ring", seed=1040),
+    # fp8 e4m3fn with per-tensor scales
+    "ag_w8_8192x7168x8192_fp8": AgConfig(
+        "ag_w8_8192x7168x8192_fp8", world=8, rank=0, m_shard=1024, k=8192, n=7168, dtype="fp8",
+        chunk_rows=256, a_dist=N1, b_dist=N002, order_kind="seeded", seed=1050),
 }
 
-HEADLINE = "c2_ag_w8_bf16"
+HEADLINE = "ag_w8_4096x3584x8192_bf16"
 
 
 def make_ag_data(cfg: AgConfig):

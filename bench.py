@@ -34,7 +34,7 @@ PEAK_BF16_TFLOPS = 2516.6      # dense bf16 MFMA: 256 CUs x 4096 flop/clk x 2.4 
 PEAK_FP8_TFLOPS = 5033.2
 PEAK_HBM_GBS = 8000.0
 # counter records (profiles/traffic_<record>.txt) of each workload's overlapped launch
-TRAFFIC_RECORDS = {"c2_ag_w8_bf16": "gemm_kernel_256x224_bf16_c2_overlap"}
+TRAFFIC_RECORDS = {"ag_w8_4096x3584x8192_bf16": "gemm_kernel_256x224_bf16_ag_w8_4096x3584x8192_overlap"}
 
 
 def parse():

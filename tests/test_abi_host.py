@@ -106,9 +106,9 @@ def test_tile_shapes_for_the_workloads(lib):
     for name, cfg in configs.CONFIGS.items():
         op = 1 if cfg.op == "rs" else 0
         got[name] = B.agg_tile_shape(op, cfg.dtype, cfg.m, cfg.n, cfg.k)
-    assert got["c2_ag_w8_bf16"] == (256, 224)     # 16 x 16 = 256 tiles
-    assert got["c3_rs_w8_bf16"] == (256, 256)     # 32 x 32 = 1024 tiles
-    assert got["c5_ag_w8_fp8"] == (256, 224)      # 32 x 32 = 1024 tiles
+    assert got["ag_w8_4096x3584x8192_bf16"] == (256, 224)     # 16 x 16 = 256 tiles
+    assert got["rs_w8_8192x8192x3584_bf16"] == (256, 256)     # 32 x 32 = 1024 tiles
+    assert got["ag_w8_8192x7168x8192_fp8"] == (256, 224)      # 32 x 32 = 1024 tiles
 
 
 def test_ctx_calls_reject_null(lib):

@@ -484,8 +484,8 @@ def _run_config(name, mode="overlap", with_delays=False):
     return cfg, d, w
 
 
-@pytest.mark.parametrize("name", ["c1_ag_w2_tiny", "c2_ag_w8_bf16", "c4_ag_w8_decode",
-                                  "c5_ag_w8_fp8"])
+@pytest.mark.parametrize("name", ["ag_w2_256x256x512_bf16", "ag_w8_4096x3584x8192_bf16", "ag_w8_128x3584x8192_bf16_decode",
+                                  "ag_w8_8192x7168x8192_fp8"])
 def test_config_vs_oracle(gpu, name):
     cfg, d, w = _run_config(name)
     try:

@@ -130,7 +130,7 @@ def test_world_one_and_k_zero(gpu, producer):
 
 
 def test_config_c3_vs_oracle(gpu):
-    cfg = configs.CONFIGS["c3_rs_w8_bf16"]
+    cfg = configs.CONFIGS["rs_w8_8192x8192x3584_bf16"]
     d = configs.make_rs_data(cfg)
     w = RsWorkload(cfg.world, cfg.rank, d["a"], d["b"], d["peers"], cfg.chunk_rows)
     try:
