@@ -126,6 +126,42 @@ __device__ inline void mfma_fp8_dma(f32x16& acc, const i32x8& b, const i32x8& a,
 }
 #pragma clang diagnostic pop
 
+// Mixed pipeline (big tiles): A rows in two regions of 128-byte slice pairs, B rows in four
+// 64-byte slice stages. Issue order per wave: prologue A pair 0, first part of A pair 1, B slices
+// 0..2, first part of B slice 3; then slice s issues, before its barrier, the second part of A
+// pair s/2+1 (even s) and the second part of B slice s+3, and after its barrier the first part of
+// A pair (s+1)/2+1 (odd s) and the first part of B slice s+4 (first parts: NLA/2, NHB loads).
+// Returns how many loads follow the later of the last load of A pair (t+1)/2 and of B slice t+1
+// when the barrier of slice t is reached (t = -1: the prologue's barrier, A pair 0 and B slice 0).
+constexpr int mixed_loads_after(int t, int NLA, int NIB, int NHB) {
+  const int pa_need = t < 0 ? 0 : (t + 1) / 2;
+  const int sb_need = t + 1;
+  int n = 0, last = 0;
+  auto mark = [&](bool hit) { if (hit && n > last) last = n; };
+  n += NLA; mark(pa_need == 0);
+  n += NLA / 2; mark(pa_need == 1 && NLA / 2 == NLA);
+  for (int q = 0; q < 3; ++q) { n += NIB; mark(sb_need == q); }
+  n += NHB; mark(false);
+  for (int s = 0; s <= t; ++s) {
+    if (s % 2 == 0) { n += NLA - NLA / 2; mark(pa_need == s / 2 + 1); }
+    n += NIB - NHB; mark(sb_need == s + 3);
+    if (s < t) {
+      if (s % 2 == 1) { n += NLA / 2; mark(pa_need == (s + 1) / 2 + 1 && NLA / 2 == NLA); }
+      n += NHB; mark(sb_need == s + 4 && NHB == NIB);
+    }
+  }
+  return n - last;
+}
+
+constexpr int mixed_barrier_count(int u, int NLA, int NIB, int NHB) {
+  int m = mixed_loads_after(u, NLA, NIB, NHB);
+  for (int k = 1; k < 4; ++k) {
+    const int v = mixed_loads_after(u + 4 * k, NLA, NIB, NHB);
+    m = v < m ? v : m;
+  }
+  return m;
+}
+
 // 32 wait states: more than any MFMA result or operand hazard needs (about 20 for a 16-pass op).
 // Every accumulator then passes through an empty asm placed after the nops, so that nothing the
 // compiler emits touches an accumulator between the MFMAs and the nops.
@@ -647,12 +683,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   // slices of a tile row, so that each load instruction fetches whole 128-byte lines (8 lanes per
   // row) and the L1 sends half as many requests for the same bytes. kRegions pair regions of
   // 2 x DSTAGE bytes each replace the four stages; slice stage sg lies in region sg / 2, half
-  // sg % 2. The big tiles have room for two regions; the split-K tiles take four (a longer lead
-  // for their latency-bound loads; split parts start on whole pairs). 64 x 64 tiles, whose short
+  // sg % 2. The split-K tiles take four regions (a longer lead for their latency-bound loads;
+  // split parts start on whole pairs); the big fp8 tiles two. The big bf16 tiles (kMixed) load
+  // only their A rows in pairs (two regions) and keep their B rows in the four 64-byte stages,
+  // whose longer lead the B rows need (the XCD's L2 reuses them less); more regions do not fit
+  // the 128 KiB that direct-to-LDS loads were seen to fill correctly. 64 x 64 tiles, whose short
   // K loops measured faster with the four 64-byte stages, keep those.
-  constexpr bool kPairs = BM * BN >= 128 * 64;
+  constexpr bool kMixed = !kSplitTiles && !FP8;
+  constexpr bool kPairs = BM * BN >= 128 * 64 && !kMixed;
   constexpr int kRegions = kSplitTiles ? 4 : 2;
-  __shared__ __attribute__((aligned(1024))) uint8_t stages[kPairs ? kRegions * 2 * DSTAGE : kStages * DSTAGE];
+  constexpr int AREG = BM * 2 * kSliceBytes;                 // mixed: one A pair region
+  constexpr int BSTAGE = BNP * kSliceBytes;                  // mixed: one B slice stage
+  __shared__ __attribute__((aligned(1024))) uint8_t stages[kMixed ? 2 * AREG + 4 * BSTAGE
+                                                           : kPairs ? kRegions * 2 * DSTAGE : kStages * DSTAGE];
   __shared__ int s_tile[4];
   __shared__ int s_ok;
   __shared__ int s_job;
@@ -743,8 +786,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     static_assert(BM % (16 * NW) == 0 && BNP % (16 * NW) == 0, "whole 16-row groups per wave");
     // pairs: NL load instructions per wave per slice pair, 8 rows x 128 bytes each, the first NAL
     // of them fetching A rows
-    constexpr int NL = kPairs ? 2 * NI : NI;
-    constexpr int NAL = kPairs ? 2 * NA : NA;
+    // mixed: NLA A loads per wave per pair (8 rows x 128 bytes), then NIB B loads per wave per
+    // slice (16 rows x 64 bytes)
+    constexpr int NLA = BM / (8 * NW), NIB = BNP / (16 * NW), NHB = NIB / 2;
+    constexpr int NL = kMixed ? NLA + NIB : kPairs ? 2 * NI : NI;
+    constexpr int NAL = kMixed ? NLA : kPairs ? 2 * NA : NA;
     static_assert(!kPairs || (kRegions - 1) * NL < 64, "loads in flight within the vmcnt range");
     // lane's chunk: rows of a 16-row group are lane/4, chunk position lane%4 (pairs: rows of an
     // 8-row group are lane/8, chunk position lane%8)
@@ -754,8 +800,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     uint32_t base[NL];
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      const int r = kPairs ? pair_row(j) : (j * NW + wave) * 16 + (lane >> 2);  // LDS row
-      const uint32_t g = kPairs ? pair_gk(r) : gk;
+      const int r = (kPairs || (kMixed && j < NLA)) ? pair_row(j)
+                    : kMixed ? BM + ((j - NLA) * NW + wave) * 16 + (lane >> 2)
+                             : (j * NW + wave) * 16 + (lane >> 2);  // tile row
+      const uint32_t g = (kPairs || (kMixed && j < NLA)) ? pair_gk(r) : gk;
       if (j < NAL) {
         const int64_t gr = lo + r;
         base[j] = gr < a.M ? (uint32_t)gr * (uint32_t)kbytes + g : kOutOfRange;
@@ -833,6 +881,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         return base[j] + pk;
       }
     };
+    // mixed: A load j into A region rg; B load j (>= NLA) into B stage sg
+    auto m0ma = [&](int rg, int j) { return lds0 + (uint32_t)rg * AREG + (uint32_t)j * (NW * 1024u); };
+    auto m0mb = [&](int sg, int j) {
+      return lds0 + (uint32_t)(2 * AREG + sg * BSTAGE) + (uint32_t)(j - NLA) * (NW * 1024u);
+    };
     auto issue_one = [&](auto masked, int t, int sg, int j) {
       lds_dma_load(desc_of(j), m0_of(sg, j), voff_of(masked, t, j));
     };
@@ -845,7 +898,17 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     struct Ld { int j; uint32_t m0, vo; };
     auto ld_first = [&](auto masked, auto u_, int t, int e) -> Ld {
       constexpr int U = decltype(u_)::value;
-      if constexpr (kPairs) {
+      if constexpr (kMixed) {
+        // even slices: the second part of A pair t/2+1, then (all slices) the second part of B
+        // slice t+3
+        constexpr int EA = (U & 1) ? 0 : NLA - NLA / 2;
+        if (e < EA) {
+          const int j = NLA / 2 + e;
+          return Ld{j, m0ma(((U >> 1) + 1) & 1, j), voffp(masked, t / 2 + 1, j)};
+        }
+        const int j = NLA + NHB + (e - EA);
+        return Ld{j, m0mb((U + 3) & 3, j), voff_of(masked, t + 3, j)};
+      } else if constexpr (kPairs) {
         const int j = NL / 2 + e;
         return Ld{j, m0p(((U >> 1) + kRegions - 1) % kRegions, j), voffp(masked, t / 2 + kRegions - 1, j)};
       } else {
@@ -855,6 +918,14 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     };
     auto ld_second = [&](auto masked, auto u_, int t, int k) -> Ld {
       constexpr int U = decltype(u_)::value;
+      if constexpr (kMixed) {
+        // odd slices: the first part of A pair (t+1)/2+1, then (all slices) the first part of B
+        // slice t+4
+        constexpr int KA = (U & 1) ? NLA / 2 : 0;
+        if (k < KA) return Ld{k, m0ma(U >> 1, k), voffp(masked, (t + 1) / 2 + 1, k)};
+        const int j = NLA + (k - KA);
+        return Ld{j, m0mb(U, j), voff_of(masked, t + 4, j)};
+      }
       if constexpr (kPairs) return Ld{k, m0p(U >> 1, k), voffp(masked, (t + 1) / 2 + kRegions - 1, k)};
       else return Ld{k, m0_of(U, k), voff_of(masked, t + 4, k)};
     };
@@ -884,8 +955,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         constexpr int U = decltype(u_)::value;
         constexpr int U1 = (U + 1) % (kPairs ? 2 * kRegions : 4);
         // loads issued in the first half (E1) and in the second half (ND) of this slice
-        constexpr int E1 = kPairs ? ((U & 1) ? 0 : NL / 2) : NI - NH;
-        constexpr int ND = kPairs ? ((U & 1) ? NL / 2 : 0) : NH;
+        constexpr int E1 = kMixed ? ((U & 1) ? 0 : NLA - NLA / 2) + (NIB - NHB)
+                           : kPairs ? ((U & 1) ? 0 : NL / 2) : NI - NH;
+        constexpr int ND = kMixed ? ((U & 1) ? NLA / 2 : 0) + NHB : kPairs ? ((U & 1) ? NL / 2 : 0) : NH;
         constexpr int E2 = CN + 1 + ND;
         F far[RM];
         far[0] = fa;
@@ -920,7 +992,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         }
         // slice t+1 has landed (four stages: all but the 2*NI loads issued since; pairs, odd t:
         // all of pair (t+1)/2, the last loads issued; even t: all but the NL of pair t/2+1)
-        stage_barrier<kPairs ? ((U & 1) ? (kRegions - 2) * NL : (kRegions - 1) * NL) : 2 * NI>();
+        stage_barrier<kMixed ? mixed_barrier_count(U, NLA, NIB, NHB)
+                      : kPairs ? ((U & 1) ? (kRegions - 2) * NL : (kRegions - 1) * NL) : 2 * NI>();
 #pragma unroll
         for (int i = RB; i < RM; ++i) {
 #pragma unroll
@@ -956,7 +1029,21 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         acc_settle(accs);
         constexpr auto kPlain = std::integral_constant<bool, false>{};
         constexpr auto kMasked = std::integral_constant<bool, true>{};
-        if constexpr (kPairs) {
+        if constexpr (kMixed) {
+          // A pair 0 whole and the first part of A pair 1; B slices 0..2 whole and the first part
+          // of B slice 3 (the first slices issue the rest)
+#pragma unroll
+          for (int j = 0; j < NLA; ++j) lds_dma_load(desc_of(j), m0ma(0, j), voffp(kMasked, t_lo / 2, j));
+#pragma unroll
+          for (int j = 0; j < NLA / 2; ++j) lds_dma_load(desc_of(j), m0ma(1, j), voffp(kMasked, t_lo / 2 + 1, j));
+#pragma unroll
+          for (int q = 0; q < 3; ++q)
+#pragma unroll
+            for (int j = NLA; j < NLA + NIB; ++j) lds_dma_load(desc_of(j), m0mb(q, j), voff_of(kMasked, t_lo + q, j));
+#pragma unroll
+          for (int j = NLA; j < NLA + NHB; ++j) lds_dma_load(desc_of(j), m0mb(3, j), voff_of(kMasked, t_lo + 3, j));
+          stage_barrier<mixed_loads_after(-1, NLA, NIB, NHB)>();
+        } else if constexpr (kPairs) {
           // pairs 0 .. R-2 whole and the first half of pair R-1 (the first slice issues the rest)
 #pragma unroll
           for (int q = 0; q + 1 < kRegions; ++q)
@@ -1004,9 +1091,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       }
     };
     // LDS byte offset of 16-byte chunk g (0..3) of row `row` of slice stage sg
-    auto frag_off = [&](int sg, int row, int g) -> uint32_t {
-      if constexpr (kPairs) return (uint32_t)((sg >> 1) * (2 * DSTAGE)) + lds128_off(row, (sg & 1) * 4 + g);
-      else return (uint32_t)(sg * DSTAGE) + lds64_off(row, g);
+    auto frag_off = [&](auto b_rows, int sg, int row, int g) -> uint32_t {
+      if constexpr (kMixed) {
+        // A rows: pair region (sg/2) % 2, half sg % 2; B rows: stage sg (rows counted from BM,
+        // a multiple of 16, so the swizzle is unchanged)
+        if constexpr (!decltype(b_rows)::value)
+          return (uint32_t)(((sg >> 1) & 1) * AREG) + lds128_off(row, (sg & 1) * 4 + g);
+        else
+          return (uint32_t)(2 * AREG + sg * BSTAGE) + lds64_off(row - BM, g);
+      } else if constexpr (kPairs) {
+        return (uint32_t)((sg >> 1) * (2 * DSTAGE)) + lds128_off(row, (sg & 1) * 4 + g);
+      } else {
+        return (uint32_t)(sg * DSTAGE) + lds64_off(row, g);
+      }
     };
     if constexpr (!FP8) {
       // ---- bf16: 16x16x32 MFMA blocks, one 16-byte fragment per lane
@@ -1016,11 +1113,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       auto ldb = [&](int sg, int j) {
         return *reinterpret_cast<const u32x4*>(
-            stages + frag_off(sg, BM + wn * WTN + j * 16 + (lane & 15), lane >> 4));
+            stages + frag_off(std::true_type{}, sg, BM + wn * WTN + j * 16 + (lane & 15), lane >> 4));
       };
       auto lda = [&](int sg, int i) {
         return *reinterpret_cast<const u32x4*>(
-            stages + frag_off(sg, wm * WTM + i * 16 + (lane & 15), lane >> 4));
+            stages + frag_off(std::false_type{}, sg, wm * WTM + i * 16 + (lane & 15), lane >> 4));
       };
       run_slices(acc, u32x4{}, lda, ldb,
                  [](f32x4& c, const u32x4& b, const u32x4& x) { mfma_bf16(c, b, x); },
@@ -1038,15 +1135,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < F8N; ++j) acc8[i][j] = f32x16{};
       // a 32-row fp8 fragment: row r + (lane & 31), K bytes 32*(lane/32) .. +31 of the slice
-      auto frag8 = [&](int sg, int r) {
+      auto frag8 = [&](auto b_rows, int sg, int r) {
         const int row = r + (lane & 31), g = (lane >> 5) * 2;
-        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(stages + frag_off(sg, row, g));
-        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(stages + frag_off(sg, row, g + 1));
+        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(stages + frag_off(b_rows, sg, row, g));
+        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(stages + frag_off(b_rows, sg, row, g + 1));
         return i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
                      (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
       };
-      auto ldb = [&](int sg, int j) { return frag8(sg, BM + wn * WTN + j * 32); };
-      auto lda = [&](int sg, int i) { return frag8(sg, wm * WTM + i * 32); };
+      auto ldb = [&](int sg, int j) { return frag8(std::true_type{}, sg, BM + wn * WTN + j * 32); };
+      auto lda = [&](int sg, int i) { return frag8(std::false_type{}, sg, wm * WTM + i * 32); };
       // a wave with a single 32x32 block reuses its accumulator in the next slice's first
       // MFMA: give the previous one time to write it back
       run_slices(acc8, i32x8{}, lda, ldb,
