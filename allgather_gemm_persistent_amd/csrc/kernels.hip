@@ -28,6 +28,7 @@
 // lane ends with quads of 4 consecutive output columns of one row: 8-byte bf16 or 16-byte fp32
 // stores.
 #include "kernels.h"
+#include "pipeline.h"
 
 #include <type_traits>
 
@@ -125,42 +126,6 @@ __device__ inline void mfma_fp8_dma(f32x16& acc, const i32x8& b, const i32x8& a,
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
-
-// Mixed pipeline (big tiles): A rows in two regions of 128-byte slice pairs, B rows in four
-// 64-byte slice stages. Issue order per wave: prologue A pair 0, first part of A pair 1, B slices
-// 0..2, first part of B slice 3; then slice s issues, before its barrier, the second part of A
-// pair s/2+1 (even s) and the second part of B slice s+3, and after its barrier the first part of
-// A pair (s+1)/2+1 (odd s) and the first part of B slice s+4 (first parts: NLA/2, NHB loads).
-// Returns how many loads follow the later of the last load of A pair (t+1)/2 and of B slice t+1
-// when the barrier of slice t is reached (t = -1: the prologue's barrier, A pair 0 and B slice 0).
-constexpr int mixed_loads_after(int t, int NLA, int NIB, int NHB) {
-  const int pa_need = t < 0 ? 0 : (t + 1) / 2;
-  const int sb_need = t + 1;
-  int n = 0, last = 0;
-  auto mark = [&](bool hit) { if (hit && n > last) last = n; };
-  n += NLA; mark(pa_need == 0);
-  n += NLA / 2; mark(pa_need == 1 && NLA / 2 == NLA);
-  for (int q = 0; q < 3; ++q) { n += NIB; mark(sb_need == q); }
-  n += NHB; mark(false);
-  for (int s = 0; s <= t; ++s) {
-    if (s % 2 == 0) { n += NLA - NLA / 2; mark(pa_need == s / 2 + 1); }
-    n += NIB - NHB; mark(sb_need == s + 3);
-    if (s < t) {
-      if (s % 2 == 1) { n += NLA / 2; mark(pa_need == (s + 1) / 2 + 1 && NLA / 2 == NLA); }
-      n += NHB; mark(sb_need == s + 4 && NHB == NIB);
-    }
-  }
-  return n - last;
-}
-
-constexpr int mixed_barrier_count(int u, int NLA, int NIB, int NHB) {
-  int m = mixed_loads_after(u, NLA, NIB, NHB);
-  for (int k = 1; k < 4; ++k) {
-    const int v = mixed_loads_after(u + 4 * k, NLA, NIB, NHB);
-    m = v < m ? v : m;
-  }
-  return m;
-}
 
 // 32 wait states: more than any MFMA result or operand hazard needs (about 20 for a 16-pass op).
 // Every accumulator then passes through an empty asm placed after the nops, so that nothing the
@@ -993,7 +958,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         // slice t+1 has landed (four stages: all but the 2*NI loads issued since; pairs, odd t:
         // all of pair (t+1)/2, the last loads issued; even t: all but the NL of pair t/2+1)
         stage_barrier<kMixed ? mixed_barrier_count(U, NLA, NIB, NHB)
-                      : kPairs ? ((U & 1) ? (kRegions - 2) * NL : (kRegions - 1) * NL) : 2 * NI>();
+                      : kPairs ? pair_barrier_count(U, kRegions, NL) : stage_barrier_count(NI)>();
 #pragma unroll
         for (int i = RB; i < RM; ++i) {
 #pragma unroll
@@ -1042,7 +1007,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
             for (int j = NLA; j < NLA + NIB; ++j) lds_dma_load(desc_of(j), m0mb(q, j), voff_of(kMasked, t_lo + q, j));
 #pragma unroll
           for (int j = NLA; j < NLA + NHB; ++j) lds_dma_load(desc_of(j), m0mb(3, j), voff_of(kMasked, t_lo + 3, j));
-          stage_barrier<mixed_loads_after(-1, NLA, NIB, NHB)>();
+          stage_barrier<mixed_prologue_count(NLA, NIB, NHB)>();
         } else if constexpr (kPairs) {
           // pairs 0 .. R-2 whole and the first half of pair R-1 (the first slice issues the rest)
 #pragma unroll
@@ -1052,7 +1017,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
 #pragma unroll
           for (int j = 0; j < NL / 2; ++j)
             lds_dma_load(desc_of(j), m0p(kRegions - 1, j), voffp(kMasked, t_lo / 2 + kRegions - 1, j));
-          stage_barrier<(kRegions - 2) * NL + NL / 2>();
+          stage_barrier<pair_prologue_count(kRegions, NL)>();
         } else {
 #pragma unroll
           for (int s = 0; s < 3; ++s)
@@ -1060,7 +1025,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
             for (int j = 0; j < NI; ++j) issue_one(kMasked, t_lo + s, s, j);
 #pragma unroll
           for (int j = 0; j < NH; ++j) issue_one(kMasked, t_lo + 3, 3, j);   // the first slice issues the rest
-          stage_barrier<2 * NI + NH>();
+          stage_barrier<stage_prologue_count(NI)>();
         }
 #pragma unroll
         for (int j = 0; j < CN; ++j) fb0[j] = ldb(0, j);

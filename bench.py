@@ -83,7 +83,7 @@ def measured_traffic(name):
         return None
     kv = dict(line.strip().split("=", 1) for line in open(rec) if "=" in line and not line.startswith("#"))
     src = b"".join(open(os.path.join(ROOT, "allgather_gemm_persistent_amd", "csrc", f), "rb").read()
-                   for f in ("kernels.hip", "kernels.h"))
+                   for f in ("kernels.hip", "kernels.h", "pipeline.h"))
     if hashlib.sha256(src).hexdigest() != kv.get("kernel_source_sha256"):
         return None
     return int(kv["traffic_bytes"])
