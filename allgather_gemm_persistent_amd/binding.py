@@ -125,6 +125,27 @@ def _ptr(x):
     return int(x)
 
 
+def _checked(items):
+    """Device pointers of `items` = [(x, nbytes, what), ...] for a call that touches `nbytes`
+    bytes of each x.
+
+    A tensor must be contiguous, hold at least `nbytes` bytes and live on the GPU (every tensor
+    is checked for the first two before any for the third); anything else (an int address,
+    None) is passed through unchanged and is the caller's responsibility.
+    """
+    for x, nbytes, what in items:
+        if isinstance(x, torch.Tensor):
+            if not x.is_contiguous():
+                raise AggError(AGG_E_ARG, what, "must be contiguous (the library reads it row-major)")
+            have = x.numel() * x.element_size()
+            if have < nbytes:
+                raise AggError(AGG_E_ARG, what, f"holds {have} bytes, the call touches {nbytes}")
+    for x, _, what in items:
+        if isinstance(x, torch.Tensor) and x.device.type != "cuda":
+            raise AggError(AGG_E_ARG, what, f"must be a device tensor, got {x.device}")
+    return [_ptr(x) for x, _, _ in items]
+
+
 def _stream(s):
     if s is None:
         return None
@@ -255,21 +276,53 @@ def agg_ctx_set_reserved_cus(ctx, n: int) -> None:
     _call("agg_ctx_set_reserved_cus", ctx, n)
 
 
+def _ag_ptrs(world, rank, m_shard, n, k, chunk_rows, dtype, peer_src, gather, flags, b, c):
+    """Checked device pointers of an ag_gemm call (sizes as include/agg.h states them)."""
+    el = 1 if _dtype(dtype) == AGG_FP8_E4M3 else 2
+    m = world * m_shard
+    cps = m_shard // chunk_rows if chunk_rows > 0 else 0
+    items = [(gather, m * k * el, "gather"), (flags, world * cps * 4, "flags"), (b, k * n * el, "b"),
+             (c, m * n * 2, "c")]
+    if peer_src is not None:
+        items += [(p, m_shard * k * el if i != rank else 0, f"peer_src[{i}]")
+                  for i, p in enumerate(peer_src)]
+    ptrs = _checked(items)
+    peers = (_vp * len(peer_src))(*ptrs[4:]) if peer_src is not None else None
+    return (peers, *ptrs[:4])
+
+
 def ag_gemm(ctx, world, rank, m_shard, n, k, chunk_rows, dtype, scale_a, scale_b, peer_src,
             gather, flags, b, c, order=None, delay_us=None, mode="overlap", stream=None,
             copy_stream=None) -> None:
     ordr, n_order = _i32_array(order)
+    peers, g, f, bp, cp = _ag_ptrs(world, rank, m_shard, n, k, chunk_rows, dtype, peer_src,
+                                   gather, flags, b, c)
     _call("ag_gemm", ctx, world, rank, m_shard, n, k, chunk_rows, _dtype(dtype), scale_a, scale_b,
-          _ptr_array(peer_src), _ptr(gather), _ptr(flags), _ptr(b), _ptr(c), ordr, n_order,
-          _u32_array(delay_us), _mode(mode), _stream(stream), _stream(copy_stream))
+          peers, g, f, bp, cp, ordr, n_order, _u32_array(delay_us), _mode(mode), _stream(stream),
+          _stream(copy_stream))
+
+
+def _rs_ptrs(world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_src, recv, flags, out):
+    """Checked device pointers of a gemm_rs call, in its argument order."""
+    mb = m // world if world > 0 else 0
+    cpb = mb // chunk_rows if chunk_rows > 0 else 0
+    items = [(a, m * k * 2, "a"), (b, k * n * 2, "b"), (send, max(world - 1, 0) * mb * n * 4, "send"),
+             (send_flags, world * cpb * 4, "send_flags"), (recv, world * mb * n * 4, "recv"),
+             (flags, world * cpb * 4, "flags"), (out, mb * n * 4, "out")]
+    if peer_src is not None:
+        items += [(p, mb * n * 4 if i != rank else 0, f"peer_src[{i}]") for i, p in enumerate(peer_src)]
+    ptrs = _checked(items)
+    peers = (_vp * len(peer_src))(*ptrs[7:]) if peer_src is not None else None
+    return (*ptrs[:4], peers, *ptrs[4:7])
 
 
 def gemm_rs(ctx, world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_src, recv, flags,
             out, order=None, delay_us=None, mode="overlap", stream=None, copy_stream=None) -> None:
     ordr, n_order = _i32_array(order)
-    _call("gemm_rs", ctx, world, rank, m, n, k, chunk_rows, _ptr(a), _ptr(b), _ptr(send),
-          _ptr(send_flags), _ptr_array(peer_src), _ptr(recv), _ptr(flags), _ptr(out), ordr,
-          n_order, _u32_array(delay_us), _mode(mode), _stream(stream), _stream(copy_stream))
+    ptrs = _rs_ptrs(world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_src, recv,
+                    flags, out)
+    _call("gemm_rs", ctx, world, rank, m, n, k, chunk_rows, *ptrs, ordr, n_order,
+          _u32_array(delay_us), _mode(mode), _stream(stream), _stream(copy_stream))
 
 
 def agg_transpose_kn_to_nk(src, dst, k: int, n: int, elem_bytes: int, stream=None) -> None:

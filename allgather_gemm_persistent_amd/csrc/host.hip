@@ -183,8 +183,12 @@ int copy_streams(agg_ctx* ctx, size_t chunks, std::vector<hipStream_t>& out) {
 }
 
 int produce(const ChunkCopy& cc, uint32_t* flags, const std::vector<int32_t>& order,
-            const uint32_t* delay_us, uint32_t epoch, const std::vector<hipStream_t>& streams) {
+            const uint32_t* delay_us, uint32_t epoch, const std::vector<hipStream_t>& streams,
+            int rank) {
   const size_t bytes = size_t(cc.cr * cc.row_bytes);
+  // the local shard's chunks are in place from the start: their flags are raised first
+  for (int q = 0; q < cc.cps; ++q)
+    HIP_TRY(hipStreamWriteValue32(streams[0], flags + size_t(rank) * cc.cps + q, epoch, 0));
   for (size_t i = 0; i < order.size(); ++i) {
     const int c = order[i];
     const int p = c / cc.cps, q = c % cc.cps;
@@ -401,10 +405,29 @@ void attach_trace(agg_ctx* ctx, GemmArgs& g, int64_t tiles) {
 
 // One launch of the persistent kernel under the CU producer: `copies` adds the copy jobs,
 // `tiles_on` keeps the GEMM tiles (without them: a copy-only grid of one workgroup per CU).
+// Flags a launch raises to the epoch at its start: the local slot of the flags the producer
+// releases (a launch with copy jobs) and, ReduceScatter, the local slot of the send flags (a
+// launch with tiles).
+struct Marks {
+  uint32_t* copy_flags = nullptr;
+  uint32_t* tile_flags = nullptr;
+  int count = 0;
+};
+
 int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int dtype, int epi,
               int grid, const ChunkCopy& cc, uint32_t* flags, size_t n_order, bool delays,
-              int world, uint32_t epoch, bool copies, bool tiles_on, bool timed, int pull_copiers = 0) {
+              int world, uint32_t epoch, bool copies, bool tiles_on, bool timed, const Marks& marks,
+              int pull_copiers = 0) {
   GemmArgs h = g;
+  h.mark_count[0] = h.mark_count[1] = 0;
+  if (copies && marks.copy_flags) {
+    h.mark_flags[0] = marks.copy_flags;
+    h.mark_count[0] = marks.count;
+  }
+  if (tiles_on && marks.tile_flags) {
+    h.mark_flags[1] = marks.tile_flags;
+    h.mark_count[1] = marks.count;
+  }
   int gr = grid;
   // pull only where tiles and copies share the launch: the grid gains the copiers
   const bool pull = pull_copiers > 0 && copies && tiles_on;
@@ -816,7 +839,11 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
     grid = grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks && !cu);
     // every split part claims its workgroup at launch (no more parts than workgroups): the parts
     // of a tile can wait for each other and sum the tile together
-    g.split_together = (g.ksplit > 1 && tiles <= grid) ? 1 : 0;
+    // (and only when the whole grid fits on the GPU at once, so that no part waits for a sibling
+    // that has no CU)
+    g.split_together = (g.ksplit > 1 && tiles <= grid &&
+                        int64_t(max_blocks_per_cu(ts.bm, ts.bn, dtype, kEpiAllGather)) * ctx->cus >= grid)
+                           ? 1 : 0;
     fill_common(ctx, g, ts, grid);
     attach_trace(ctx, g, tiles);
   }
@@ -834,11 +861,16 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
       if (spare >= 1 && (ctx->pull == AGG_PULL_ON || remote <= kPullMaxBytes))
         pull_copiers = int(std::min<int64_t>(spare, std::max<int64_t>(1, (remote + 16383) / 16384)));
     }
+    Marks marks;
+    if (world > 1) {
+      marks.copy_flags = flags + size_t(rank) * cps;
+      marks.count = cps;
+    }
     return schedule_cu(ctx, mode, s, S(copy_stream), kernel, chunks,
                        [&](bool copies, bool tiles_on, bool timed) {
                          return launch_cu(ctx, s, g, ts, dtype, kEpiAllGather, grid, cc, flags,
                                           ord.size(), delay_us != nullptr, world, epoch, copies,
-                                          tiles_on, timed, pull_copiers);
+                                          tiles_on, timed, marks, pull_copiers);
                        });
   }
   auto launch = [&]() -> int {
@@ -847,7 +879,7 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
     });
   };
   return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
-                  [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams); });
+                  [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams, rank); });
 }
 
 // ------------------------------------------------------------------------------------------
@@ -927,15 +959,26 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
     grid = grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks && !cu);
     fill_common(ctx, g, ts, grid);
     attach_trace(ctx, g, tiles);
+    if (world > 1) {
+      // nothing is sent for the local block: its send flags are raised with the others' epoch
+      g.mark_flags[1] = send_flags + size_t(rank) * cpb;
+      g.mark_count[1] = cpb;
+    }
   }
   if (cu) {
     if (chunks)
       if (int rc = upload_schedule(ctx, s, ord, delay_us)) return rc;
+    Marks marks;
+    if (world > 1) {
+      marks.copy_flags = flags + size_t(rank) * cpb;
+      marks.tile_flags = send_flags + size_t(rank) * cpb;
+      marks.count = cpb;
+    }
     return schedule_cu(ctx, mode, s, S(copy_stream), kernel, chunks,
                        [&](bool copies, bool tiles_on, bool timed) {
                          return launch_cu(ctx, s, g, ts, AGG_BF16, kEpiReduceScatter, grid, cc,
                                           flags, ord.size(), delay_us != nullptr, world, epoch,
-                                          copies, tiles_on, timed);
+                                          copies, tiles_on, timed, marks);
                        });
   }
   auto launch = [&]() -> int {
@@ -944,5 +987,5 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
     });
   };
   return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
-                  [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams); });
+                  [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams, rank); });
 }

@@ -74,6 +74,11 @@ struct GemmArgs {
   // jobs (which still fill the gather buffer and release the flags) go to the last copy_wgs
   // workgroups, which claim tiles only after copying
   int pull;
+  // flags this launch sets to the epoch at its start (workgroup 0): the local shard's chunks
+  // (present from the call's start; a launch that carries the copy jobs marks them) and, for
+  // ReduceScatter tile launches, the local block's send flags (nothing is sent for that block)
+  uint32_t* mark_flags[2];
+  int mark_count[2];
 };
 
 // Launch the persistent kernel instantiated for (bm, bn, dtype, epilogue) with `grid`
@@ -81,6 +86,10 @@ struct GemmArgs {
 // instantiation.
 hipError_t launch_gemm(const GemmArgs& args, int bm, int bn, int dtype, int epilogue, int grid,
                        hipStream_t stream);
+
+// Workgroups of the (bm, bn, dtype, epilogue) kernel that fit on one CU at once (0 for a shape
+// without an instantiation).
+int max_blocks_per_cu(int bm, int bn, int dtype, int epilogue);
 
 // Fill `words` uint32 at `dst` with `value` (a kernel, not a memset node).
 hipError_t launch_fill_u32(uint32_t* dst, size_t words, uint32_t value, hipStream_t stream);

@@ -659,14 +659,33 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   constexpr int kRegions = kSplitTiles ? 4 : 2;
   constexpr int AREG = BM * 2 * kSliceBytes;                 // mixed: one A pair region
   constexpr int BSTAGE = BNP * kSliceBytes;                  // mixed: one B slice stage
-  __shared__ __attribute__((aligned(1024))) uint8_t stages[kMixed ? 2 * AREG + 4 * BSTAGE
-                                                           : kPairs ? kRegions * 2 * DSTAGE : kStages * DSTAGE];
-  __shared__ int s_tile[4];
-  __shared__ int s_ok;
-  __shared__ int s_job;
+  constexpr int kStageBytes = kMixed ? 2 * AREG + 4 * BSTAGE : kPairs ? kRegions * 2 * DSTAGE : kStages * DSTAGE;
+  // Direct-to-LDS loads take their LDS address from M0. Layouts whose destinations reached past
+  // 128 KiB gave wrong results (and a copy staged there faulted), consistent with that address
+  // wrapping at 128 KiB, so every destination stays below it: the operand stages come first in
+  // the kernel's one LDS block, at offset 0, and end at or below 128 KiB.
+  struct Smem {
+    uint8_t stages[kStageBytes];
+    int tile[4];
+    int ok;
+    int job;
+  };
+  static_assert(kStageBytes <= kLdsDmaLimit, "direct-to-LDS destinations must stay below 128 KiB");
+  static_assert(__builtin_offsetof(Smem, stages) == 0, "the operand stages start the LDS block");
+  __shared__ __attribute__((aligned(1024))) Smem sm;
+  auto& stages = sm.stages;
+  auto& s_tile = sm.tile;
+  auto& s_ok = sm.ok;
+  auto& s_job = sm.job;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WNW, wn = wave % WNW;
+  if (blockIdx.x == 0) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      for (int i = tid; i < a.mark_count[f]; i += NT)
+        __hip_atomic_store(a.mark_flags[f] + i, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
   // the list searched first: the one that gives this workgroup its static first tile. The
   // workgroups of one list share an XCD (they are dealt to the XCDs round robin), so its
   // tiles' operand rows stay in that XCD's L2.
@@ -1386,6 +1405,34 @@ template <int BM, int BN, int DT, int EPI>
 static hipError_t launch_one(const GemmArgs& args, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_kernel<BM, BN, DT, EPI>), dim3(grid), dim3(kThreads), 0, stream, args);
   return hipGetLastError();
+}
+
+template <int BM, int BN, int DT, int EPI>
+static int occupancy_one() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel<BM, BN, DT, EPI>, kThreads, 0) != hipSuccess)
+    return 0;
+  return n;
+}
+
+template <int DT, int EPI>
+static int occupancy_shape(int bm, int bn) {
+  if (bm == 256 && bn == 256) return occupancy_one<256, 256, DT, EPI>();
+  if (bm == 256 && bn == 224) return occupancy_one<256, 224, DT, EPI>();
+  if (bm == 128 && bn == 128) return occupancy_one<128, 128, DT, EPI>();
+  if (bm == 128 && bn == 64) return occupancy_one<128, 64, DT, EPI>();
+  if (bm == 64 && bn == 64) return occupancy_one<64, 64, DT, EPI>();
+  return 0;
+}
+
+int max_blocks_per_cu(int bm, int bn, int dtype, int epilogue) {
+  if (epilogue == kEpiAllGather) {
+    if (dtype == AGG_BF16) return occupancy_shape<AGG_BF16, kEpiAllGather>(bm, bn);
+    if (dtype == AGG_FP8_E4M3) return occupancy_shape<AGG_FP8_E4M3, kEpiAllGather>(bm, bn);
+  } else if (epilogue == kEpiReduceScatter && dtype == AGG_BF16) {
+    return occupancy_shape<AGG_BF16, kEpiReduceScatter>(bm, bn);
+  }
+  return 0;
 }
 
 template <int DT, int EPI>

@@ -6,6 +6,11 @@
 
 namespace agg {
 
+// Bytes of LDS that direct-to-LDS loads may fill: their LDS address (M0) is taken to wrap at
+// 128 KiB on gfx950 (layouts that reached past it gave wrong results), so every operand stage of
+// the GEMM kernel lies below this bound.
+constexpr int kLdsDmaLimit = 128 * 1024;
+
 // Four 64-byte stages, NI loads per wave per slice: slice t issues, before its barrier, loads
 // NI/2.. of slice t+3 and, after it, loads 0..NI/2-1 of slice t+4; the prologue issues slices 0..2
 // and the first half of slice 3.
@@ -63,5 +68,60 @@ constexpr int mixed_barrier_count(int u, int NLA, int NIB, int NHB) {
 }
 
 constexpr int mixed_prologue_count(int NLA, int NIB, int NHB) { return mixed_loads_after(-1, NLA, NIB, NHB); }
+
+}  // namespace agg
+
+namespace agg {
+
+// ---- the B operand (K x N, N contiguous) in LDS
+//
+// One 64-byte K slice of a tile's B columns is a block of 64/elem K rows, each BNP*elem bytes (BNP
+// = the tile's columns rounded up to 64), i.e. P = BNP*elem/16 chunks of 16 bytes per row and
+// 4*BNP chunks in all. Chunk c of row k sits at chunk position k*P + (c ^ b_swizzle(k, P, elem)),
+// so direct-to-LDS load lanes that fill consecutive positions fetch whole row segments (every
+// request a full line for rows of 128 bytes and more).
+//
+// The MFMA operand needs K-packed fragments (a lane holds consecutive K of one column); gfx950's
+// transposing LDS reads build them from N-contiguous rows. Within each 16-lane group g of the
+// wave, ds_read_b64_tr_b16 gives lane l element e = element l%4 of the 8 bytes read by lane
+// 16g + (l%16)/4 + 4e, and ds_read_b64_tr_b8 gives lane l byte e = byte l%8 of the 8 bytes read by
+// lane 16g + (l%16)/8 + 2e (both measured on the GPU with every lane reading a distinct address).
+// So for the bf16 16x16x32 fragment (lane l: column l%16, K 8*(l/16) .. +7), read r of two has lane
+// s fetch K row 8*(s/16) + 4r + (s%16)/4, columns 4*(s%4) .. +3; for the fp8 32x32x64 fragment
+// (lane l: column l%32, K 32*(l/32) .. +31), read r of four has lane s fetch K row
+// 32*(s/32) + 8r + (s%16)/2, columns 16*((s/16)%2) + 8*(s%2) .. +7. A half wave then reads 8 rows
+// x 32 bytes; the swizzle puts those rows on distinct 32-byte bank groups of the 256-byte bank
+// line (64 banks of 4 bytes).
+constexpr int b_swizzle(int k, int P, int elem) {
+  if (elem == 2) {      // half wave: rows 4r + a and 8 + 4r + a, a = 0..3
+    if (P >= 16) return 2 * ((k & 3) | (((k >> 3) & 1) << 2));
+    return 2 * (((k >> 1) & 1) | (((k >> 3) & 1) << 1));    // P == 8: two rows per bank line
+  }
+  // fp8, half wave: rows 8r .. 8r + 7
+  if (P >= 16) return 2 * (k & 7);
+  if (P == 8) return 2 * ((k >> 1) & 3);
+  return 2 * ((k >> 2) & 1);                               // P == 4: four rows per bank line
+}
+
+// The B load that fills chunk position q of a slice's block: its K row and its column chunk.
+constexpr int b_load_row(int q, int P) { return q / P; }
+constexpr int b_load_chunk(int q, int P, int elem) { return (q % P) ^ b_swizzle(q / P, P, elem); }
+
+// Transposing reads of a B fragment: lane `lane`'s K row for read r (0..1 bf16, 0..3 fp8), the
+// chunk it reads relative to the fragment's first chunk (0 or 1), the 8-byte half, and the
+// swizzle of its rows (the same for every r).
+constexpr int b_read_row(int lane, int r, int elem) {
+  return elem == 2 ? 8 * (lane >> 4) + 4 * r + ((lane & 15) >> 2)
+                   : 32 * (lane >> 5) + 8 * r + ((lane & 15) >> 1);
+}
+constexpr int b_read_chunk(int lane, int elem) { return elem == 2 ? (lane & 3) >> 1 : (lane >> 4) & 1; }
+constexpr int b_read_half(int lane, int elem) { return elem == 2 ? lane & 1 : lane & 1; }
+constexpr int b_read_swizzle(int lane, int P, int elem) { return b_swizzle(b_read_row(lane, 0, elem), P, elem); }
+// LDS byte offset, inside the slice's B block, of read r of lane `lane` for the fragment whose
+// columns start at chunk `c0` (even)
+constexpr int b_read_offset(int lane, int r, int c0, int P, int elem) {
+  return 16 * (b_read_row(lane, r, elem) * P + ((c0 + b_read_chunk(lane, elem)) ^ b_read_swizzle(lane, P, elem))) +
+         8 * b_read_half(lane, elem);
+}
 
 }  // namespace agg

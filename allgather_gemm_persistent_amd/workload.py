@@ -38,13 +38,17 @@ class AgWorkload:
         self.reset_local()
         cps = self.m_shard // chunk_rows if chunk_rows else 0
         self.flags = torch.zeros(max(world * cps, 1), dtype=torch.int32, device=self.device)
-        self.b = b_kn.t().contiguous().to(self.device)
+        self.b = self.device_weight(b_kn)
         self.c = torch.zeros(self.m, self.n, dtype=torch.bfloat16, device=self.device)
         self.copy_stream = None     # the ctx runs the copies on its own streams
         self.ctx = B.agg_ctx_create(self.device.index or 0)
         B.agg_ctx_set_producer(self.ctx, producer)
         if tile:
             B.agg_ctx_set_tile(self.ctx, *tile)
+
+    def device_weight(self, b_kn):
+        """The weight as the library takes it, on the device."""
+        return b_kn.t().contiguous().to(self.device)
 
     def reset_local(self):
         """Place the local shard in its slot of the gather buffer (the caller's job)."""

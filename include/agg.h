@@ -226,8 +226,9 @@ int agg_put_signal(void* dst, const void* src, size_t bytes, uint32_t* flag, uin
  *                    already hold the local shard; the producer fills the others
  *   flags            device uint32[world * m_shard/cr], zero-filled once at allocation and then
  *                    bound to this ctx (the first call binds it; another pointer gives
- *                    AGG_E_STATE until agg_ctx_reset). Remote chunks' flags end at the epoch;
- *                    the local shard's flags are not written
+ *                    AGG_E_STATE until agg_ctx_reset). Every flag ends at the call's epoch: the
+ *                    local shard's chunks are raised first (their rows are in place at the call),
+ *                    each remote chunk's once its rows have landed
  *   b                device (n x k), K contiguous, same dtype
  *   c                device (M x n) bfloat16, row-major, rows in gathered (rank) order
  *   order, n_order   HOST: the remote chunk ids in arrival order, a permutation of all
@@ -267,7 +268,8 @@ int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64
  *   out              device fp32 Mb x n: P[block rank] + sum over p != rank, ascending p, of
  *                    recv[p]; a fixed summation order, so the result does not depend on arrival
  *   order/n_order, delay_us, mode, streams: as for ag_gemm, over the (world-1)*Mb/cr incoming
- *   chunks. flags and send_flags are bound to the ctx like ag_gemm's flags.
+ *   chunks. flags and send_flags are bound to the ctx like ag_gemm's flags; both end at the
+ *   epoch everywhere, the local block's entries included (nothing arrives or leaves for them).
  * Alignment: k*2 and n*4 bytes multiples of 16; m a multiple of world; cr divides Mb. */
 int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, int64_t k, int chunk_rows,
             const void* a, const void* b, float* send, uint32_t* send_flags,

@@ -118,3 +118,40 @@ def test_ctx_calls_reject_null(lib):
     e = ctypes.c_uint32()
     assert lib.agg_ctx_epoch(None, ctypes.byref(e)) == B.AGG_E_ARG
     assert lib.agg_transpose_kn_to_nk(None, None, -1, 2, 2, None) == B.AGG_E_ARG
+
+
+def _ag_call_args(**kw):
+    import torch
+    ms, k, n, world = 8, 16, 16, 2
+    args = dict(ctx=None, world=world, rank=0, m_shard=ms, n=n, k=k, chunk_rows=8, dtype="bf16",
+                scale_a=1.0, scale_b=1.0,
+                peer_src=[None, torch.zeros(ms, k, dtype=torch.bfloat16)],
+                gather=torch.zeros(world * ms, k, dtype=torch.bfloat16),
+                flags=torch.zeros(world, dtype=torch.int32),
+                b=torch.zeros(k, n, dtype=torch.bfloat16),
+                c=torch.zeros(world * ms, n, dtype=torch.bfloat16))
+    args.update(kw)
+    return args
+
+
+@pytest.mark.parametrize("bad,text", [
+    ("b_transposed_view", "contiguous"), ("c_short", "bytes"), ("gather_short", "bytes"),
+    ("flags_short", "bytes"), ("peer_short", "bytes"), ("host_tensor", "device tensor")])
+def test_binding_rejects_bad_tensors_before_the_call(lib, bad, text):
+    """The binding refuses non-contiguous, undersized or host tensors before anything reaches the
+    library (no GPU needed: the checks run first)."""
+    import torch
+    a = _ag_call_args()
+    if bad == "b_transposed_view":
+        a["b"] = torch.zeros(a["n"], a["k"], dtype=torch.bfloat16).t()
+    elif bad == "c_short":
+        a["c"] = a["c"][:-1]
+    elif bad == "gather_short":
+        a["gather"] = torch.zeros(3, a["k"], dtype=torch.bfloat16)
+    elif bad == "flags_short":
+        a["flags"] = torch.zeros(1, dtype=torch.int32)
+    elif bad == "peer_short":
+        a["peer_src"] = [None, torch.zeros(1, a["k"], dtype=torch.bfloat16)]
+    with pytest.raises(B.AggError) as e:
+        B.ag_gemm(**a)
+    assert text in str(e.value) and e.value.code == B.AGG_E_ARG

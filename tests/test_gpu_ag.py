@@ -128,8 +128,7 @@ def test_gather_and_flags_bitexact(gpu, producer):
         assert np.array_equal(raw(w.gather), want_g)
         flags = w.flags.cpu().numpy().astype(np.uint32)
         cps = ms // cr
-        for c in range(world * cps):
-            assert flags[c] == (0 if c // cps == rank else e), c
+        assert (flags == e).all(), flags      # the local shard's flags too
     finally:
         w.close()
 
@@ -196,8 +195,7 @@ def test_pull_matches_push_bitexact(gpu, dtype, tile, rank):
             flags = w.flags.cpu().numpy().astype(np.uint32)
             e = B.agg_ctx_epoch(w.ctx)
             cps = ms // cr
-            for c in range(world * cps):
-                assert flags[c] == (0 if c // cps == rank else e), (pull, mode, c)
+            assert (flags == e).all(), (pull, mode, flags)
         ref = outs[("on", "overlap")]
         for key, c in outs.items():
             assert bits_equal(c, ref), key
@@ -231,8 +229,7 @@ def test_pull_by_row_groups_matches_push_bitexact(gpu, dtype, tile, world, ms, r
             flags = w.flags.cpu().numpy().astype(np.uint32)
             e = B.agg_ctx_epoch(w.ctx)
             cps = ms // cr
-            for c in range(world * cps):
-                assert flags[c] == (0 if c // cps == rank else e), (pull, c)
+            assert (flags == e).all(), (pull, flags)
         assert bits_equal(outs[0], outs[1])
         assert_close(to_f64(outs[0]), _oracle_c(shards, b, dtype, sa, sb), _tol(dtype), "C")
     finally:
@@ -296,7 +293,7 @@ def test_epoch_wraps_and_stays_correct(gpu, producer):
             seen.append(B.agg_ctx_epoch(w.ctx))
         assert seen == [0xFFFFFFFD, 0xFFFFFFFE, 1, 2]
         flags = w.flags.cpu().numpy()
-        assert (flags[ms // cr:] == 2).all() and (flags[:ms // cr] == 0).all()
+        assert (flags == 2).all(), flags
     finally:
         w.close()
 
@@ -390,8 +387,7 @@ def test_cu_producer_pieces_and_workgroups(gpu, copy_wgs, piece_kib, mode):
         assert np.array_equal(raw(w.gather), O.gather_ref([raw(s) for s in shards]))
         flags = w.flags.cpu().numpy().astype(np.uint32)
         cps = ms // cr
-        for c in range(world * cps):
-            assert flags[c] == (0 if c // cps == rank else e), c
+        assert (flags == e).all(), flags      # the local shard's flags too
         if mode != "copy_only":
             assert_close(to_f64(w.c), _oracle_c(shards, b, "bf16", 1, 1), BF16_TOL, "C")
     finally:
@@ -476,31 +472,107 @@ def test_transpose_helper(gpu, elem):
 
 # ---------------------------------------------------------------------- the workload configs
 
-def _run_config(name, mode="overlap", with_delays=False):
+AG_CONFIGS = ["ag_w2_256x256x512_bf16", "ag_w8_4096x3584x8192_bf16",
+              "ag_w8_128x3584x8192_bf16_decode", "ag_w8_8192x7168x8192_fp8"]
+_REFS = {}
+
+
+def _config_ref(name, d):
+    if name not in _REFS:
+        cfg = configs.CONFIGS[name]
+        _REFS[name] = _oracle_c(d["shards"], d["b"], cfg.dtype, d["scale_a"], d["scale_b"])
+    return _REFS[name]
+
+
+def _remote_rows(w):
+    ms = w.m_shard
+    return [r for r in range(w.world * ms) if r // ms != w.rank]
+
+
+def _check_gather_and_flags(w, d, what):
+    assert np.array_equal(raw(w.gather), O.gather_ref([raw(s) for s in d["shards"]])), what
+    e = B.agg_ctx_epoch(w.ctx)
+    flags = w.flags.cpu().numpy().astype(np.uint32)
+    assert (flags == e).all(), (what, e, flags)
+
+
+@pytest.mark.parametrize("name", AG_CONFIGS)
+def test_config_vs_oracle(gpu, name):
+    """Each AllGather+GEMM workload at full size: the overlapped call (its automatic choices),
+    then every other path of the same call, each after clearing C and the remote rows of the
+    gather buffer: serialized, bare GEMM, the flag-gated push (pull off: every remote tile waits
+    on its chunks' flags) and both producers. C matches the oracle and every run gives the same
+    bits; the gather buffer is the rank-order concatenation and every flag holds the epoch."""
     cfg = configs.CONFIGS[name]
     d = configs.make_ag_data(cfg)
     w = AgWorkload(cfg.world, cfg.rank, d["shards"], d["b"], cfg.chunk_rows, cfg.dtype,
                    d["scale_a"], d["scale_b"])
-    return cfg, d, w
-
-
-@pytest.mark.parametrize("name", ["ag_w2_256x256x512_bf16", "ag_w8_4096x3584x8192_bf16", "ag_w8_128x3584x8192_bf16_decode",
-                                  "ag_w8_8192x7168x8192_fp8"])
-def test_config_vs_oracle(gpu, name):
-    cfg, d, w = _run_config(name)
+    rows = _remote_rows(w)
     try:
-        print(f"config {name}", flush=True)
+        print(f"config {name}: overlap", flush=True)
         w.run("overlap", order=cfg.order(), delay_us=cfg.delays())
         assert w.status() == (0, -1)
         c_ovl = w.c.clone()
-        ref = _oracle_c(d["shards"], d["b"], cfg.dtype, d["scale_a"], d["scale_b"])
-        assert_close(to_f64(c_ovl), ref, _tol(cfg.dtype), name)
-        # the same kernels in the other modes give the same bits
-        for mode in ("serial", "gemm_only"):
+        assert_close(to_f64(c_ovl), _config_ref(name, d), _tol(cfg.dtype), name)
+        _check_gather_and_flags(w, d, "overlap")
+        runs = [("cu", "auto", "serial"), ("cu", "auto", "gemm_only"), ("cu", "off", "overlap"),
+                ("sdma", "auto", "overlap"), ("sdma", "auto", "serial")]
+        for producer, pull, mode in runs:
+            print(f"config {name}: {producer} pull={pull} {mode}", flush=True)
+            B.agg_ctx_set_producer(w.ctx, producer)
+            B.agg_ctx_set_pull(w.ctx, pull)
             w.c.zero_()
+            if mode != "gemm_only":
+                w.gather[rows] = 0
             w.run(mode, order=cfg.order())
-            assert w.status() == (0, -1)
-            assert bits_equal(w.c, c_ovl), mode
-        assert np.array_equal(raw(w.gather), O.gather_ref([raw(s) for s in d["shards"]]))
+            assert w.status() == (0, -1), (producer, pull, mode)
+            assert bits_equal(w.c, c_ovl), (producer, pull, mode)
+            _check_gather_and_flags(w, d, (producer, pull, mode))
+    finally:
+        w.close()
+
+
+def _alt_data(cfg, seed_shift):
+    import dataclasses
+    return configs.make_ag_data(dataclasses.replace(cfg, seed=cfg.seed + seed_shift))
+
+
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_stale_data_reuse_full_size(gpu, producer):
+    """Fifty overlapped calls at the W=8 4096 x 3584 x 8192 bf16 size alternate two seeded
+    datasets (different peer blocks, local shard and weight) over the same gather buffer, flags
+    and C, none of them cleared between calls. A tile that read a row before its chunk landed,
+    or skipped its wait, would reproduce the other dataset's rows. The first call of each dataset
+    is compared with the oracle; every later one must repeat its bits exactly."""
+    cfg = configs.CONFIGS["ag_w8_4096x3584x8192_bf16"]
+    data = [configs.make_ag_data(cfg), _alt_data(cfg, 100)]
+    dev = torch.device("cuda")
+    peers = [[s.to(dev) if p != cfg.rank else 0 for p, s in enumerate(d["shards"])] for d in data]
+    local = [d["shards"][cfg.rank].to(dev) for d in data]
+    w = AgWorkload(cfg.world, cfg.rank, data[0]["shards"], data[0]["b"], cfg.chunk_rows, cfg.dtype,
+                   producer=producer)
+    bs = [w.device_weight(d["b"]) for d in data]
+    ms = cfg.m_shard
+    first = [None, None]
+    try:
+        order = cfg.order()
+        for i in range(50):
+            j = i % 2
+            w.gather[cfg.rank * ms:(cfg.rank + 1) * ms].copy_(local[j])   # the caller's shard
+            B.ag_gemm(w.ctx, cfg.world, cfg.rank, ms, cfg.n, cfg.k, cfg.chunk_rows, "bf16", 1.0,
+                      1.0, peers[j], w.gather, w.flags, bs[j], w.c, order=order, mode="overlap",
+                      stream=torch.cuda.current_stream())
+            if first[j] is None:
+                assert w.status() == (0, -1)
+                print(f"stale-data {producer}: dataset {j} against the oracle", flush=True)
+                ref = _oracle_c(data[j]["shards"], data[j]["b"], "bf16", 1.0, 1.0)
+                assert_close(to_f64(w.c), ref, BF16_TOL, f"dataset {j}")
+                first[j] = w.c.clone()
+            else:
+                assert torch.equal(w.c, first[j]), f"call {i} (dataset {j}) differs from its first result"
+        assert w.status() == (0, -1)
+        flags = w.flags.cpu().numpy().astype(np.uint32)
+        assert (flags == B.agg_ctx_epoch(w.ctx)).all()
+        assert np.array_equal(raw(w.gather), O.gather_ref([raw(s) for s in data[1]["shards"]]))
     finally:
         w.close()

@@ -94,10 +94,7 @@ def test_order_invariance_and_bookkeeping(gpu, producer):
         e = B.agg_ctx_epoch(w.ctx)
         rf = w.flags.cpu().numpy()
         sf = w.send_flags.cpu().numpy()
-        for c in range(world * cpb):
-            local = c // cpb == rank
-            assert rf[c] == (0 if local else e)
-            assert sf[c] == (0 if local else e)
+        assert (rf == e).all() and (sf == e).all(), (rf, sf)   # the local block's flags too
         recv = w.recv.cpu()
         for p in range(world):
             if p != rank:
@@ -130,20 +127,40 @@ def test_world_one_and_k_zero(gpu, producer):
 
 
 def test_config_c3_vs_oracle(gpu):
+    """The W=8 8192 x 8192 x 3584 GEMM+ReduceScatter at full size, overlapped, against the oracle;
+    then serialized and with the copy-engine producer (receive buffer cleared first): the same
+    bits in `send` and `out`, the receive buffer holding every peer's block, all flags at the
+    epoch."""
     cfg = configs.CONFIGS["rs_w8_8192x8192x3584_bf16"]
     d = configs.make_rs_data(cfg)
     w = RsWorkload(cfg.world, cfg.rank, d["a"], d["b"], d["peers"], cfg.chunk_rows)
+
+    def bookkeeping(what):
+        e = B.agg_ctx_epoch(w.ctx)
+        assert (w.flags.cpu().numpy() == e).all(), what
+        assert (w.send_flags.cpu().numpy() == e).all(), what
+        recv = w.recv.cpu()
+        for p in range(cfg.world):
+            if p != cfg.rank:
+                assert torch.equal(recv[p], d["peers"][p]), (what, p)
     try:
-        print("config c3", flush=True)
+        print("config c3: overlap", flush=True)
         w.run("overlap", order=cfg.order())
         assert w.status() == (0, -1)
         send, out = O.gemm_rs_ref(raw(d["a"]), raw(d["b"]), d["peers"].numpy(), cfg.world, cfg.rank)
         assert_close(to_f64(w.send), send, BF16_TOL, "send")
         assert_close(to_f64(w.out), out, BF16_TOL, "out")
-        o1 = w.out.clone()
-        w.out.zero_()
-        w.run("serial", order=cfg.order())
-        assert w.status() == (0, -1)
-        assert torch.equal(w.out, o1)
+        bookkeeping("overlap")
+        o1, s1 = w.out.clone(), w.send.clone()
+        for producer, mode in (("cu", "serial"), ("sdma", "overlap")):
+            print(f"config c3: {producer} {mode}", flush=True)
+            B.agg_ctx_set_producer(w.ctx, producer)
+            w.out.zero_()
+            w.send.zero_()
+            w.recv.zero_()
+            w.run(mode, order=cfg.order())
+            assert w.status() == (0, -1), (producer, mode)
+            assert torch.equal(w.out, o1) and torch.equal(w.send, s1), (producer, mode)
+            bookkeeping((producer, mode))
     finally:
         w.close()
