@@ -58,7 +58,6 @@ _SIGNATURES = {
                 ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _i32p, _c_int, _u32p, _c_int, _vp, _vp],
     "gemm_rs": [_vp, _c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp, _vp, _vp,
                 ctypes.POINTER(_vp), _vp, _vp, _vp, _i32p, _c_int, _u32p, _c_int, _vp, _vp],
-    "agg_transpose_kn_to_nk": [_vp, _vp, _c_i64, _c_i64, _c_int, _vp],
     "agg_tile_shape": [_c_int, _c_int, _c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_int),
                        ctypes.POINTER(_c_int)],
     "agg_ag_row_tile_order": [_c_int, _c_int, _c_i64, _c_int, _i32p, _c_int, _c_int, _i32p,
@@ -323,10 +322,6 @@ def gemm_rs(ctx, world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_
                     flags, out)
     _call("gemm_rs", ctx, world, rank, m, n, k, chunk_rows, *ptrs, ordr, n_order,
           _u32_array(delay_us), _mode(mode), _stream(stream), _stream(copy_stream))
-
-
-def agg_transpose_kn_to_nk(src, dst, k: int, n: int, elem_bytes: int, stream=None) -> None:
-    _call("agg_transpose_kn_to_nk", _ptr(src), _ptr(dst), k, n, elem_bytes, _stream(stream))
 
 
 def agg_tile_shape(op: int, dtype, m: int, n: int, k: int):

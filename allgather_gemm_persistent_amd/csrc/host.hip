@@ -748,15 +748,6 @@ extern "C" int agg_put_signal(void* dst, const void* src, size_t bytes, uint32_t
   return put_signal(dst, src, bytes, flag, value, S(copy_stream));
 }
 
-extern "C" int agg_transpose_kn_to_nk(const void* src, void* dst, int64_t k, int64_t n, int elem_bytes_,
-                                      agg_stream stream) {
-  clear_error();
-  if (k < 0 || n < 0 || (elem_bytes_ != 1 && elem_bytes_ != 2)) return fail(AGG_E_ARG, "invalid sizes");
-  if (k && n && (!src || !dst)) return fail(AGG_E_ARG, "NULL pointer");
-  HIP_TRY(launch_transpose(src, dst, k, n, elem_bytes_, S(stream)));
-  return AGG_OK;
-}
-
 // ------------------------------------------------------------------------------------------
 // AllGather + GEMM
 // ------------------------------------------------------------------------------------------

@@ -31,7 +31,7 @@ enum Epilogue { kEpiAllGather = 0, kEpiReduceScatter = 1 };
 
 struct GemmArgs {
   const uint8_t* a;         // AG: gather buffer M x K; RS: A, M x K
-  const uint8_t* b;         // N x K (K contiguous)
+  const uint8_t* b;         // K x N (N contiguous)
   uint16_t* c;              // AG output, M x N bfloat16
   float* send;              // RS: (world-1) x Mb x N
   float* out;               // RS: Mb x N
@@ -93,9 +93,5 @@ int max_blocks_per_cu(int bm, int bn, int dtype, int epilogue);
 
 // Fill `words` uint32 at `dst` with `value` (a kernel, not a memset node).
 hipError_t launch_fill_u32(uint32_t* dst, size_t words, uint32_t value, hipStream_t stream);
-
-// dst (n x k) = transpose(src (k x n)), elem_bytes in {1, 2}.
-hipError_t launch_transpose(const void* src, void* dst, int64_t k, int64_t n, int elem_bytes,
-                            hipStream_t stream);
 
 }  // namespace agg

@@ -140,6 +140,22 @@ __device__ inline void acc_settle(V (&acc)[FM][FN]) {
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// Transposing LDS reads of 8 bytes per lane (gfx950 ds_read_b64_tr_b16 / _b8) at byte offset
+// `off` of the LDS block starting at `base`; the lane permutation is described with the B
+// layout (b_swizzle).
+__device__ inline u32x2 lds_read_tr16(const uint8_t* base, uint32_t off) {
+  typedef __attribute__((address_space(3))) i16x4* p_t;
+  typedef __attribute__((address_space(3))) uint8_t* b_t;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((p_t)((b_t)base + off)));
+}
+__device__ inline u32x2 lds_read_tr8(const uint8_t* base, uint32_t off) {
+  typedef __attribute__((address_space(3))) i32x2* p_t;
+  typedef __attribute__((address_space(3))) uint8_t* b_t;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((p_t)((b_t)base + off)));
+}
 
 // Raw buffer descriptor (base, no stride, num_records bytes) in four scalar registers.
 __device__ inline u32x4 buffer_desc(const void* base, uint32_t bytes) {
@@ -775,26 +791,38 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     constexpr int NLA = BM / (8 * NW), NIB = BNP / (16 * NW), NHB = NIB / 2;
     constexpr int NL = kMixed ? NLA + NIB : kPairs ? 2 * NI : NI;
     constexpr int NAL = kMixed ? NLA : kPairs ? 2 * NA : NA;
+    constexpr int EL = FP8 ? 1 : 2;
+    constexpr int kRowsB = kSliceBytes / EL;              // K rows of B per slice
+    constexpr int kChunksB = BNP * EL / 16;               // 16-byte chunks per B row
+    constexpr int NBS = BNP / (16 * NW);                  // B loads per wave per slice
+    static_assert(NL - NAL == (kPairs ? 2 : 1) * NBS, "B loads per slice");
     static_assert(!kPairs || (kRegions - 1) * NL < 64, "loads in flight within the vmcnt range");
     // lane's chunk: rows of a 16-row group are lane/4, chunk position lane%4 (pairs: rows of an
     // 8-row group are lane/8, chunk position lane%8)
     const uint32_t gk = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) << 4);
     auto pair_row = [&](int j) { return (j * NW + wave) * 8 + (lane >> 3); };
     auto pair_gk = [&](int r) { return (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) << 4); };
+    // B (K x N, N contiguous): a slice's B block holds kRowsB K rows of kChunksB 16-byte chunks;
+    // B load jb of a slice (NBS per wave) fills chunk positions (jb*NW + wave)*64 + lane, i.e. K row
+    // b_load_row and column chunk b_load_chunk of the slice (whole rows per instruction, 2..16 of
+    // them, so each request is a whole line for rows of 128 bytes and more). Pair tiles load two
+    // slices of B per pair: B loads jb and jb + NBS fill the same positions of consecutive slices.
+    auto b_pos = [&](int j) { return (((j - NAL) % NBS) * NW + wave) * 64 + lane; };
     uint32_t base[NL];
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      const int r = (kPairs || (kMixed && j < NLA)) ? pair_row(j)
-                    : kMixed ? BM + ((j - NLA) * NW + wave) * 16 + (lane >> 2)
-                             : (j * NW + wave) * 16 + (lane >> 2);  // tile row
-      const uint32_t g = (kPairs || (kMixed && j < NLA)) ? pair_gk(r) : gk;
       if (j < NAL) {
+        const int r = (kPairs || kMixed) ? pair_row(j) : (j * NW + wave) * 16 + (lane >> 2);  // tile row
+        const uint32_t g = (kPairs || kMixed) ? pair_gk(r) : gk;
         const int64_t gr = lo + r;
         base[j] = gr < a.M ? (uint32_t)gr * (uint32_t)kbytes + g : kOutOfRange;
       } else {
-        const int c = r - BM;
-        const int64_t gn = n0 + c;
-        base[j] = (c < BN && gn < a.N) ? (uint32_t)gn * (uint32_t)kbytes + g : kOutOfRange;
+        const int q = b_pos(j);
+        const int ncol = b_load_chunk(q, kChunksB, EL) * (16 / EL);
+        const int64_t gn = n0 + ncol;
+        base[j] = (ncol < BN && gn < a.N)
+                      ? (uint32_t)b_load_row(q, kChunksB) * (uint32_t)(a.N * EL) + (uint32_t)gn * EL
+                      : kOutOfRange;
       }
     }
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -846,7 +874,20 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     // range: a plain offset. Otherwise (`masked`) the offset's top bit is set past the K end
     // (out of range: reads zero), lane by lane, since a slice may straddle the end.
     const int t_safe = (int)(kend / kSlice);
+    // B load j of slice t: row b_load_row of the slice's K rows, which start at K row t*kRowsB
+    // (64 * N bytes per slice); masked: rows at or past the part's K end read zeros
+    const uint32_t kend_rows = kend / EL;
+    auto voff_b = [&](auto masked, int t, int j) -> uint32_t {
+      const uint32_t tb = (uint32_t)t * (uint32_t)(kSliceBytes * a.N);
+      if constexpr (decltype(masked)::value) {
+        const uint32_t row = (uint32_t)(t * kRowsB + b_load_row(b_pos(j), kChunksB));
+        return (base[j] + tb) | (row >= kend_rows ? kOutOfRange : 0u);
+      } else {
+        return base[j] + tb;
+      }
+    };
     auto voff_of = [&](auto masked, int t, int j) -> uint32_t {
+      if (j >= NAL) return voff_b(masked, t, j);
       const uint32_t tk = (uint32_t)t * kSliceBytes;
       if constexpr (decltype(masked)::value) {
         const uint32_t oob = (uint32_t)((int)(tk + gk - kend) >> 31) ^ 0xFFFFFFFFu;
@@ -857,6 +898,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     };
     // pairs: K byte offset of load j of slice pair pr (slices 2pr and 2pr+1), masked as above
     auto voffp = [&](auto masked, int pr, int j) -> uint32_t {
+      if (j >= NAL) return voff_b(masked, 2 * pr + (j - NAL) / NBS, j);
       const uint32_t pk = (uint32_t)pr * (2 * kSliceBytes);
       if constexpr (decltype(masked)::value) {
         const uint32_t oob = (uint32_t)((int)(pk + pair_gk(pair_row(j)) - kend) >> 31) ^ 0xFFFFFFFFu;
@@ -1074,34 +1116,48 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
     };
-    // LDS byte offset of 16-byte chunk g (0..3) of row `row` of slice stage sg
-    auto frag_off = [&](auto b_rows, int sg, int row, int g) -> uint32_t {
+    // LDS byte offset of 16-byte chunk g (0..3) of A row `row` of slice stage sg
+    auto frag_off = [&](int sg, int row, int g) -> uint32_t {
       if constexpr (kMixed) {
-        // A rows: pair region (sg/2) % 2, half sg % 2; B rows: stage sg (rows counted from BM,
-        // a multiple of 16, so the swizzle is unchanged)
-        if constexpr (!decltype(b_rows)::value)
-          return (uint32_t)(((sg >> 1) & 1) * AREG) + lds128_off(row, (sg & 1) * 4 + g);
-        else
-          return (uint32_t)(2 * AREG + sg * BSTAGE) + lds64_off(row - BM, g);
+        // A rows: pair region (sg/2) % 2, half sg % 2
+        return (uint32_t)(((sg >> 1) & 1) * AREG) + lds128_off(row, (sg & 1) * 4 + g);
       } else if constexpr (kPairs) {
         return (uint32_t)((sg >> 1) * (2 * DSTAGE)) + lds128_off(row, (sg & 1) * 4 + g);
       } else {
         return (uint32_t)(sg * DSTAGE) + lds64_off(row, g);
       }
     };
+    // LDS byte offset of the B block of slice stage sg (after the A rows of its stage or pair
+    // region; mixed: the B stages after the two A regions)
+    auto bblk = [&](int sg) -> uint32_t {
+      if constexpr (kMixed) return (uint32_t)(2 * AREG + sg * BSTAGE);
+      else if constexpr (kPairs)
+        return (uint32_t)((sg >> 1) * (2 * DSTAGE) + BM * 2 * kSliceBytes + (sg & 1) * (BNP * kSliceBytes));
+      else return (uint32_t)(sg * DSTAGE + BM * kSliceBytes);
+    };
+    // this lane's transposing B reads: byte offset of read 0 inside a B block for the fragment
+    // whose first chunk is 0, and its rows' swizzle (read r adds r times 4 rows (bf16) or 8 rows
+    // (fp8); the fragment's first chunk c0 (even) enters as (c0 ^ swizzle))
+    const uint32_t boff0 = (uint32_t)b_read_base(lane, kChunksB, EL);
+    const uint32_t bswz = (uint32_t)b_read_swizzle(lane, kChunksB, EL);
+    constexpr uint32_t kReadRowStep = (uint32_t)b_read_step(kChunksB, EL);
     if constexpr (!FP8) {
       // ---- bf16: 16x16x32 MFMA blocks, one 16-byte fragment per lane
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // B fragment: 16 columns starting at chunk c0, K rows 8*(lane/16) .. +7 from two
+      // transposing reads (rows +0..3 and +4..7)
       auto ldb = [&](int sg, int j) {
-        return *reinterpret_cast<const u32x4*>(
-            stages + frag_off(std::true_type{}, sg, BM + wn * WTN + j * 16 + (lane & 15), lane >> 4));
+        const uint32_t c0 = (uint32_t)((wn * WTN + j * 16) >> 3);
+        const uint32_t off = bblk(sg) + boff0 + 16u * (c0 ^ bswz);
+        const u32x2 r0 = lds_read_tr16(stages, off);
+        const u32x2 r1 = lds_read_tr16(stages, off + kReadRowStep);
+        return u32x4{r0[0], r0[1], r1[0], r1[1]};
       };
       auto lda = [&](int sg, int i) {
-        return *reinterpret_cast<const u32x4*>(
-            stages + frag_off(std::false_type{}, sg, wm * WTM + i * 16 + (lane & 15), lane >> 4));
+        return *reinterpret_cast<const u32x4*>(stages + frag_off(sg, wm * WTM + i * 16 + (lane & 15), lane >> 4));
       };
       run_slices(acc, u32x4{}, lda, ldb,
                  [](f32x4& c, const u32x4& b, const u32x4& x) { mfma_bf16(c, b, x); },
@@ -1118,16 +1174,26 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       for (int i = 0; i < F8M; ++i)
 #pragma unroll
         for (int j = 0; j < F8N; ++j) acc8[i][j] = f32x16{};
-      // a 32-row fp8 fragment: row r + (lane & 31), K bytes 32*(lane/32) .. +31 of the slice
-      auto frag8 = [&](auto b_rows, int sg, int r) {
-        const int row = r + (lane & 31), g = (lane >> 5) * 2;
-        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(stages + frag_off(b_rows, sg, row, g));
-        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(stages + frag_off(b_rows, sg, row, g + 1));
+      // a 32-row fp8 A fragment: row r + (lane & 31), K bytes 32*(lane/32) .. +31 of the slice
+      auto lda = [&](int sg, int i) {
+        const int row = wm * WTM + i * 32 + (lane & 31), g = (lane >> 5) * 2;
+        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(stages + frag_off(sg, row, g));
+        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(stages + frag_off(sg, row, g + 1));
         return i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
                      (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
       };
-      auto ldb = [&](int sg, int j) { return frag8(std::true_type{}, sg, BM + wn * WTN + j * 32); };
-      auto lda = [&](int sg, int i) { return frag8(std::false_type{}, sg, wm * WTM + i * 32); };
+      // B fragment: 32 columns starting at chunk c0, K rows 32*(lane/32) .. +31 from four
+      // transposing reads of 8 rows each
+      auto ldb = [&](int sg, int j) {
+        const uint32_t c0 = (uint32_t)((wn * WTN + j * 32) >> 4);
+        const uint32_t off = bblk(sg) + boff0 + 16u * (c0 ^ bswz);
+        const u32x2 r0 = lds_read_tr8(stages, off);
+        const u32x2 r1 = lds_read_tr8(stages, off + kReadRowStep);
+        const u32x2 r2 = lds_read_tr8(stages, off + 2 * kReadRowStep);
+        const u32x2 r3 = lds_read_tr8(stages, off + 3 * kReadRowStep);
+        return i32x8{(int)r0[0], (int)r0[1], (int)r1[0], (int)r1[1],
+                     (int)r2[0], (int)r2[1], (int)r3[0], (int)r3[1]};
+      };
       // a wave with a single 32x32 block reuses its accumulator in the next slice's first
       // MFMA: give the previous one time to write it back
       run_slices(acc8, i32x8{}, lda, ldb,
@@ -1385,22 +1451,6 @@ __global__ void fill_u32_kernel(uint32_t* dst, size_t words, uint32_t value) {
     dst[i] = value;
 }
 
-// 64 x 64 element tiles through LDS: coalesced reads of src rows, coalesced writes of dst rows.
-template <typename T>
-__global__ void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst, int64_t k, int64_t n) {
-  __shared__ T tile[64][65];
-  const int64_t k0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
-  for (int r = threadIdx.y; r < 64; r += blockDim.y) {
-    const int64_t kk = k0 + r, nn = n0 + threadIdx.x;
-    if (kk < k && nn < n) tile[r][threadIdx.x] = src[kk * n + nn];
-  }
-  __syncthreads();
-  for (int r = threadIdx.y; r < 64; r += blockDim.y) {
-    const int64_t nn = n0 + r, kk = k0 + threadIdx.x;
-    if (nn < n && kk < k) dst[nn * k + kk] = tile[threadIdx.x][r];
-  }
-}
-
 template <int BM, int BN, int DT, int EPI>
 static hipError_t launch_one(const GemmArgs& args, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_kernel<BM, BN, DT, EPI>), dim3(grid), dim3(kThreads), 0, stream, args);
@@ -1461,21 +1511,6 @@ hipError_t launch_fill_u32(uint32_t* dst, size_t words, uint32_t value, hipStrea
   size_t blocks = (words + 255) / 256;
   if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, dst, words, value);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose(const void* src, void* dst, int64_t k, int64_t n, int elem_bytes,
-                            hipStream_t stream) {
-  if (k == 0 || n == 0) return hipSuccess;
-  dim3 grid((unsigned)((n + 63) / 64), (unsigned)((k + 63) / 64)), block(64, 4);
-  if (elem_bytes == 2)
-    hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, block, 0, stream,
-                       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), k, n);
-  else if (elem_bytes == 1)
-    hipLaunchKernelGGL(transpose_kernel<uint8_t>, grid, block, 0, stream,
-                       static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), k, n);
-  else
-    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

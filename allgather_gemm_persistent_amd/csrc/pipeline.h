@@ -117,6 +117,13 @@ constexpr int b_read_row(int lane, int r, int elem) {
 constexpr int b_read_chunk(int lane, int elem) { return elem == 2 ? (lane & 3) >> 1 : (lane >> 4) & 1; }
 constexpr int b_read_half(int lane, int elem) { return elem == 2 ? lane & 1 : lane & 1; }
 constexpr int b_read_swizzle(int lane, int P, int elem) { return b_swizzle(b_read_row(lane, 0, elem), P, elem); }
+// What the kernel computes once per lane: the offset of read 0 for a fragment at chunk 0 before
+// the swizzle, and the step from read r to read r + 1 (4 rows bf16, 8 rows fp8). For an even c0
+// the offset of read r is b_read_base + r * b_read_step + 16 * (c0 ^ b_read_swizzle).
+constexpr int b_read_base(int lane, int P, int elem) {
+  return 16 * (b_read_row(lane, 0, elem) * P + b_read_chunk(lane, elem)) + 8 * b_read_half(lane, elem);
+}
+constexpr int b_read_step(int P, int elem) { return 16 * (elem == 2 ? 4 : 8) * P; }
 // LDS byte offset, inside the slice's B block, of read r of lane `lane` for the fragment whose
 // columns start at chunk `c0` (even)
 constexpr int b_read_offset(int lane, int r, int c0, int P, int elem) {

@@ -234,6 +234,7 @@ extern "C" int agg_check_ag_args(int world, int rank, int64_t m_shard, int64_t n
   const int eb = elem_bytes(dtype);
   if ((k * eb) % 16) return fail(AGG_E_ARG, "k * %d bytes = %lld is not a multiple of 16", eb, (long long)(k * eb));
   if ((n * 2) % 16) return fail(AGG_E_ARG, "n * 2 bytes = %lld is not a multiple of 16", (long long)(n * 2));
+  if ((n * eb) % 16) return fail(AGG_E_ARG, "a row of b, n * %d bytes = %lld, is not a multiple of 16", eb, (long long)(n * eb));
   if (k > (int64_t(1) << 30) || n > (int64_t(1) << 30) || world * m_shard > (int64_t(1) << 30))
     return fail(AGG_E_UNSUPPORTED, "dimension beyond 2^30");
   if (world * m_shard * k * eb >= (int64_t(1) << 31) || n * k * eb >= (int64_t(1) << 31))
@@ -288,7 +289,7 @@ extern "C" int agg_check_rs_args(int world, int rank, int64_t m, int64_t n, int6
   const int64_t cpb = mb / chunk_rows;
   if (world * cpb > AGG_MAX_CHUNKS) return fail(AGG_E_UNSUPPORTED, "%lld chunks exceed %d", (long long)(world * cpb), AGG_MAX_CHUNKS);
   if ((k * 2) % 16) return fail(AGG_E_ARG, "k * 2 bytes = %lld is not a multiple of 16", (long long)(k * 2));
-  if ((n * 4) % 16) return fail(AGG_E_ARG, "n * 4 bytes = %lld is not a multiple of 16", (long long)(n * 4));
+  if ((n * 2) % 16) return fail(AGG_E_ARG, "a row of b, n * 2 bytes = %lld, is not a multiple of 16", (long long)(n * 2));
   if (k > (int64_t(1) << 30) || n > (int64_t(1) << 30) || m > (int64_t(1) << 30))
     return fail(AGG_E_UNSUPPORTED, "dimension beyond 2^30");
   if (m * k * 2 >= (int64_t(1) << 31) || n * k * 2 >= (int64_t(1) << 31))

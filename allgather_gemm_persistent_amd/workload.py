@@ -16,8 +16,8 @@ from . import binding as B
 class AgWorkload:
     """One rank's share of AllGather+GEMM with W-1 emulated peers on one GPU.
 
-    shards: W CPU tensors (Ms x K, bf16 or float8_e4m3fn); b_kn: CPU tensor (K x N), the logical
-    weight, stored on the device as N x K (K contiguous).
+    shards: W CPU tensors (Ms x K, bf16 or float8_e4m3fn); b_kn: CPU tensor (K x N), the weight,
+    passed to the library as it is (N contiguous).
     """
 
     def __init__(self, world, rank, shards, b_kn, chunk_rows, dtype="bf16", scale_a=1.0,
@@ -48,7 +48,7 @@ class AgWorkload:
 
     def device_weight(self, b_kn):
         """The weight as the library takes it, on the device."""
-        return b_kn.t().contiguous().to(self.device)
+        return b_kn.contiguous().to(self.device)
 
     def reset_local(self):
         """Place the local shard in its slot of the gather buffer (the caller's job)."""
@@ -89,7 +89,7 @@ class RsWorkload:
         self.mb = self.m // world
         self.device = torch.device(device)
         self.a = a.to(self.device)
-        self.b = b_kn.t().contiguous().to(self.device)
+        self.b = b_kn.contiguous().to(self.device)
         self.peers = [peers[p].to(self.device) if p != rank else None for p in range(world)]
         self.recv = torch.zeros(world, self.mb, self.n, dtype=torch.float32, device=self.device)
         cpb = self.mb // chunk_rows if chunk_rows else 0

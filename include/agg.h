@@ -35,9 +35,9 @@
  *    respect to the host, except that a non-NULL delay_us makes the calling thread wait between
  *    chunk enqueues (a test device: it emulates late peers).
  *  - A ctx serialises its calls: use one ctx from one host thread with one main stream.
- *  - Matrix layouts are row-major. The weight operand B is stored N x K (K contiguous): row n
- *    holds column n of the logical K x N matrix, the layout of a torch.nn.Linear weight.
- *    agg_transpose_kn_to_nk converts a K x N (N contiguous) matrix once.
+ *  - Matrix layouts are row-major: A and the gather buffer M x K (K contiguous), the weight B
+ *    K x N (N contiguous), C M x N. The kernel turns B's rows into K-packed MFMA fragments with
+ *    gfx950's transposing LDS reads, so no layout change is needed on either side.
  */
 #ifndef AGG_H
 #define AGG_H
@@ -229,7 +229,7 @@ int agg_put_signal(void* dst, const void* src, size_t bytes, uint32_t* flag, uin
  *                    AGG_E_STATE until agg_ctx_reset). Every flag ends at the call's epoch: the
  *                    local shard's chunks are raised first (their rows are in place at the call),
  *                    each remote chunk's once its rows have landed
- *   b                device (n x k), K contiguous, same dtype
+ *   b                device (k x n), N contiguous, same dtype
  *   c                device (M x n) bfloat16, row-major, rows in gathered (rank) order
  *   order, n_order   HOST: the remote chunk ids in arrival order, a permutation of all
  *                    (world-1)*m_shard/cr of them; NULL with n_order 0 = ring order (peers
@@ -245,7 +245,8 @@ int agg_put_signal(void* dst, const void* src, size_t bytes, uint32_t* flag, uin
  *                    earlier work on it, and later work on it starts after the copies. The
  *                    copies themselves run on the ctx's own streams (agg_ctx_set_copy_streams)
  *                    or inside the kernel (AGG_PRODUCER_CU)
- * Alignment: k * elem and n * 2 bytes multiples of 16, device pointers 16-byte aligned. */
+ * Alignment: k * elem, n * elem and n * 2 bytes multiples of 16 (rows of A, B and C), device
+ * pointers 16-byte aligned. */
 int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64_t k,
             int chunk_rows, int dtype, float scale_a, float scale_b,
             const void* const* peer_src, void* gather, uint32_t* flags, const void* b, void* c,
@@ -255,7 +256,7 @@ int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64
 /* ---- GEMM + ReduceScatter -------------------------------------------------------------- */
 
 /* P = A @ B in fp32 (bf16 operands); rows split into `world` blocks of Mb = m/world rows.
- *   a                device (m x k) bf16; b: device (n x k) bf16, K contiguous
+ *   a                device (m x k) bf16; b: device (k x n) bf16, N contiguous
  *   send             device fp32 (world-1) x Mb x n: the non-local blocks j != rank of P,
  *                    ascending j (what this rank would push to rank j)
  *   send_flags       device uint32[world * Mb/cr]: entry j*Mb/cr + q is set to the epoch
@@ -270,19 +271,12 @@ int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64
  *   order/n_order, delay_us, mode, streams: as for ag_gemm, over the (world-1)*Mb/cr incoming
  *   chunks. flags and send_flags are bound to the ctx like ag_gemm's flags; both end at the
  *   epoch everywhere, the local block's entries included (nothing arrives or leaves for them).
- * Alignment: k*2 and n*4 bytes multiples of 16; m a multiple of world; cr divides Mb. */
+ * Alignment: k*2 and n*2 bytes multiples of 16; m a multiple of world; cr divides Mb. */
 int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, int64_t k, int chunk_rows,
             const void* a, const void* b, float* send, uint32_t* send_flags,
             const float* const* peer_src, float* recv, uint32_t* flags, float* out,
             const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
             agg_stream stream, agg_stream copy_stream);
-
-/* ---- layout helper ---------------------------------------------------------------------- */
-
-/* dst (n x k) = transpose of src (k x n), elements of `elem_bytes` (1 or 2), on `stream`.
- * For callers holding the weight N-contiguous: done once, outside the per-call path. */
-int agg_transpose_kn_to_nk(const void* src, void* dst, int64_t k, int64_t n, int elem_bytes,
-                           agg_stream stream);
 
 /* ---- host-only planning (no device needed; used by the calls above) --------------------- */
 

@@ -117,7 +117,6 @@ def test_ctx_calls_reject_null(lib):
     assert lib.agg_ctx_destroy(None) == B.AGG_OK
     e = ctypes.c_uint32()
     assert lib.agg_ctx_epoch(None, ctypes.byref(e)) == B.AGG_E_ARG
-    assert lib.agg_transpose_kn_to_nk(None, None, -1, 2, 2, None) == B.AGG_E_ARG
 
 
 def _ag_call_args(**kw):
