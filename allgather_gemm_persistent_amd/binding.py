@@ -56,6 +56,8 @@ _SIGNATURES = {
     "agg_ctx_set_reserved_cus": [_vp, _c_int],
     "ag_gemm": [_vp, _c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_f32, _c_f32,
                 ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _i32p, _c_int, _u32p, _c_int, _vp, _vp],
+    "ag_gemm_noalloc": [_vp, _c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_f32, _c_f32,
+                        ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _i32p, _c_int, _u32p, _c_int, _vp, _vp],
     "gemm_rs": [_vp, _c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp, _vp, _vp,
                 ctypes.POINTER(_vp), _vp, _vp, _vp, _i32p, _c_int, _u32p, _c_int, _vp, _vp],
     "agg_tile_shape": [_c_int, _c_int, _c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_int),
@@ -299,6 +301,17 @@ def ag_gemm(ctx, world, rank, m_shard, n, k, chunk_rows, dtype, scale_a, scale_b
     _call("ag_gemm", ctx, world, rank, m_shard, n, k, chunk_rows, _dtype(dtype), scale_a, scale_b,
           peers, g, f, bp, cp, ordr, n_order, _u32_array(delay_us), _mode(mode), _stream(stream),
           _stream(copy_stream))
+
+
+def ag_gemm_noalloc(ctx, world, rank, m_shard, n, k, chunk_rows, dtype, scale_a, scale_b, peer_src,
+                    gather, flags, b, c, order=None, delay_us=None, mode="overlap", stream=None,
+                    copy_stream=None) -> None:
+    ordr, n_order = _i32_array(order)
+    peers, g, f, bp, cp = _ag_ptrs(world, rank, m_shard, n, k, chunk_rows, dtype, peer_src,
+                                   gather, flags, b, c)
+    _call("ag_gemm_noalloc", ctx, world, rank, m_shard, n, k, chunk_rows, _dtype(dtype), scale_a,
+          scale_b, peers, g, f, bp, cp, ordr, n_order, _u32_array(delay_us), _mode(mode),
+          _stream(stream), _stream(copy_stream))
 
 
 def _rs_ptrs(world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_src, recv, flags, out):

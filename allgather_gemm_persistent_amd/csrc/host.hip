@@ -47,6 +47,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -65,6 +66,30 @@ constexpr int64_t kPullMaxBytes = int64_t(4) << 20;
 constexpr int kTimingRing = 256;          // launches whose kernel duration is kept
 
 enum FlagSlot { kFlagsAg = 0, kFlagsRsRecv = 1, kFlagsRsSend = 2, kFlagSlots = 3 };
+
+// The no-allocation entry point's scratch: the kernel's counters, status and tables
+// (kScrWords words, rounded up to 256 bytes) followed by room for split-K partials.
+constexpr size_t kStaticWords = (size_t(kScrWords) + 63) / 64 * 64;
+constexpr size_t kStaticWsBytes = size_t(8) << 20;
+constexpr size_t kStaticBytes = kStaticWords * 4 + kStaticWsBytes;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+// One copy per GPU, held until the process ends. Host code never passes this name to a kernel
+// or a copy (on the host it is only a stand-in for the symbol): it uses the device address
+// hipGetSymbolAddress returned for the current device at set-up (static_scratch_setup).
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kStaticBytes];
+
+namespace {
+
+// Per device: the address of `scratch` on that device, and the tables it holds as last uploaded.
+struct StaticScratch {
+  uint32_t* words = nullptr;
+  std::vector<uint32_t> up[3];
+};
+std::mutex g_static_mu;
+StaticScratch g_static[kMaxDevices];
 
 }  // namespace
 
@@ -102,6 +127,8 @@ struct agg_ctx {
   // order, cumulative delays (kScrRowOrder / kScrOrder / kScrDelay)
   std::vector<uint32_t> up[3];
   uint32_t* up_host = nullptr;               // pinned staging for the three tables
+  bool used_static = false;                  // ag_gemm_noalloc ran on this ctx (its status and
+                                             //   counters are in the device's static scratch)
   hipEvent_t ev_upload = nullptr;
   bool upload_pending = false;
 };
@@ -282,6 +309,17 @@ int timed_launch(agg_ctx* ctx, F launch, hipStream_t ls = nullptr) {
   return AGG_OK;
 }
 
+// The scratch a call's kernels use: the ctx's own (counters and tables allocated at creation,
+// split-K partials grown on demand) or, for ag_gemm_noalloc, the device's static array (fixed
+// room for partials, nothing allocated).
+struct Scratch {
+  uint32_t* words;              // kScrWords counters, status and tables
+  std::vector<uint32_t>* up;    // the three tables the words hold, as last uploaded
+  bool fixed;                   // true: partials only in the static array's fixed room
+};
+
+Scratch own_scratch(agg_ctx* ctx) { return Scratch{ctx->scratch, ctx->up, false}; }
+
 // The split-K partial buffer, grown to `bytes` when needed (a synchronising reallocation: the
 // previous buffer may still be read by enqueued work).
 int ensure_ws(agg_ctx* ctx, size_t bytes) {
@@ -316,7 +354,6 @@ KSplit ksplit_for(agg_ctx* ctx, TileShape ts, int dtype, int64_t tiles, int64_t 
 }
 
 void fill_common(agg_ctx* ctx, GemmArgs& g, TileShape ts, int grid) {
-  g.scratch = ctx->scratch;
   g.n_lists = std::min(ctx->lists, kMaxLists);
   g.list_cols = ctx->list_cols > 0 && g.n_lists % ctx->list_cols == 0
                     ? ctx->list_cols
@@ -334,31 +371,30 @@ constexpr int kTabHostWords = AGG_MAX_ROW_TILES + 2 * AGG_MAX_CHUNKS;
 
 // Copy table `t` into scratch on stream `s`, unless scratch already holds exactly `v`. The
 // pinned staging area is reused only after the previous upload has been consumed.
-int upload_table(agg_ctx* ctx, hipStream_t s, int t, const std::vector<uint32_t>& v) {
-  if (v.empty() || v == ctx->up[t]) return AGG_OK;
+int upload_table(agg_ctx* ctx, const Scratch& sp, hipStream_t s, int t, const std::vector<uint32_t>& v) {
+  if (v.empty() || v == sp.up[t]) return AGG_OK;
   if (v.size() > size_t(kTabWords[t])) return fail(AGG_E_UNSUPPORTED, "table %d: %zu entries exceed %d", t, v.size(), kTabWords[t]);
-  if (!ctx->up_host) HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&ctx->up_host), kTabHostWords * sizeof(uint32_t)));
   if (ctx->upload_pending) {
     HIP_TRY(hipEventSynchronize(ctx->ev_upload));
     ctx->upload_pending = false;
   }
   std::memcpy(ctx->up_host + kTabHost[t], v.data(), v.size() * sizeof(uint32_t));
-  HIP_TRY(hipMemcpyAsync(ctx->scratch + kTabScratch[t], ctx->up_host + kTabHost[t],
+  HIP_TRY(hipMemcpyAsync(sp.words + kTabScratch[t], ctx->up_host + kTabHost[t],
                          v.size() * sizeof(uint32_t), hipMemcpyHostToDevice, s));
   HIP_TRY(hipEventRecord(ctx->ev_upload, s));
   ctx->upload_pending = true;
-  ctx->up[t] = v;
+  sp.up[t] = v;
   return AGG_OK;
 }
 
-int upload_rows(agg_ctx* ctx, hipStream_t s, const std::vector<int32_t>& rows) {
-  return upload_table(ctx, s, 0, std::vector<uint32_t>(rows.begin(), rows.end()));
+int upload_rows(agg_ctx* ctx, const Scratch& sp, hipStream_t s, const std::vector<int32_t>& rows) {
+  return upload_table(ctx, sp, s, 0, std::vector<uint32_t>(rows.begin(), rows.end()));
 }
 
 // Arrival order and cumulative delays (wall-clock ticks) for the CU producer.
-int upload_schedule(agg_ctx* ctx, hipStream_t s, const std::vector<int32_t>& ord,
+int upload_schedule(agg_ctx* ctx, const Scratch& sp, hipStream_t s, const std::vector<int32_t>& ord,
                     const uint32_t* delay_us) {
-  if (int rc = upload_table(ctx, s, 1, std::vector<uint32_t>(ord.begin(), ord.end()))) return rc;
+  if (int rc = upload_table(ctx, sp, s, 1, std::vector<uint32_t>(ord.begin(), ord.end()))) return rc;
   if (!delay_us) return AGG_OK;
   std::vector<uint32_t> d(ord.size());
   double sum = 0;
@@ -366,7 +402,7 @@ int upload_schedule(agg_ctx* ctx, hipStream_t s, const std::vector<int32_t>& ord
     sum += double(delay_us[i]) * ctx->ticks_per_us;
     d[i] = uint32_t(std::min(sum, 4.0e9));
   }
-  return upload_table(ctx, s, 2, d);
+  return upload_table(ctx, sp, s, 2, d);
 }
 
 // Copy-job fields of the kernel arguments for the CU producer.
@@ -438,7 +474,6 @@ int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int
     h.n_col_tiles = 0;
     h.trace = nullptr;
     h.trace_tiles = 0;
-    h.scratch = ctx->scratch;
     h.n_lists = 1;
     h.list_cols = 1;
     h.ksplit = 1;
@@ -492,6 +527,28 @@ int schedule_cu(agg_ctx* ctx, int mode, hipStream_t s, hipStream_t us, bool kern
 
 }  // namespace
 
+namespace {
+
+// Find the device address of `scratch` on `device` (current) once, and clear its counters; the
+// failed-flag word starts at "none". The partials need no initial value.
+int static_scratch_setup(int device) {
+  if (device < 0 || device >= kMaxDevices) return fail(AGG_E_UNSUPPORTED, "device %d beyond %d", device, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (g_static[device].words) return AGG_OK;
+  void* p = nullptr;
+  HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+  uint32_t* w = static_cast<uint32_t*>(p);
+  HIP_TRY(launch_fill_u32(w, kScrWords, 0u, nullptr));
+  HIP_TRY(launch_fill_u32(w + kScrFailed, 1, 0xFFFFFFFFu, nullptr));
+  HIP_TRY(hipStreamSynchronize(nullptr));
+  g_static[device].words = w;
+  return AGG_OK;
+}
+
+Scratch static_scratch(int device) { return Scratch{g_static[device].words, g_static[device].up, true}; }
+
+}  // namespace
+
 // ------------------------------------------------------------------------------------------
 // ctx
 // ------------------------------------------------------------------------------------------
@@ -534,6 +591,9 @@ extern "C" int agg_ctx_create(int device, agg_ctx** out) {
   for (int j = 0; j < kMaxCopyStreams; ++j)
     step(hipEventCreateWithFlags(&ctx->ev_copy[j], hipEventDisableTiming), "hipEventCreate");
   if (rc == AGG_OK) step(make_own_queue_stream(ctx, &ctx->ks), "hipExtStreamCreateWithCUMask");
+  step(hipHostMalloc(reinterpret_cast<void**>(&ctx->up_host), kTabHostWords * sizeof(uint32_t)),
+       "hipHostMalloc(tables)");
+  if (rc == AGG_OK) rc = static_scratch_setup(device);
   step(hipSetDevice(prev), "hipSetDevice");
   if (rc != AGG_OK) {
     agg_ctx_destroy(ctx);
@@ -586,6 +646,15 @@ extern "C" int agg_ctx_reset(agg_ctx* ctx, agg_stream stream) {
   }
   HIP_TRY(launch_fill_u32(ctx->scratch, kScrWords, 0u, S(stream)));
   HIP_TRY(launch_fill_u32(ctx->scratch + kScrFailed, 1, 0xFFFFFFFFu, S(stream)));
+  if (ctx->used_static) {
+    // the device's static scratch too (shared by every ctx on the device)
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    StaticScratch& st = g_static[ctx->device];
+    HIP_TRY(launch_fill_u32(st.words, kScrWords, 0u, S(stream)));
+    HIP_TRY(launch_fill_u32(st.words + kScrFailed, 1, 0xFFFFFFFFu, S(stream)));
+    for (auto& t : st.up) t.clear();
+    ctx->used_static = false;
+  }
   HIP_TRY(hipStreamSynchronize(S(stream)));
   ctx->epoch = 0;
   for (auto& t : ctx->up) t.clear();   // the scratch copies of the tables are gone too
@@ -599,6 +668,12 @@ extern "C" int agg_ctx_status(agg_ctx* ctx, agg_stream stream, uint32_t* status,
   HIP_TRY(hipStreamSynchronize(S(stream)));
   uint32_t words[2] = {0, 0};
   HIP_TRY(hipMemcpy(words, ctx->scratch + kScrStatus, sizeof words, hipMemcpyDeviceToHost));
+  if (ctx->used_static) {
+    uint32_t st[2] = {0, 0};
+    HIP_TRY(hipMemcpy(st, g_static[ctx->device].words + kScrStatus, sizeof st, hipMemcpyDeviceToHost));
+    if (!words[0]) words[1] = st[1];
+    words[0] |= st[0];
+  }
   if (status) *status = words[0];
   if (failed_chunk) *failed_chunk = words[1] == 0xFFFFFFFFu ? -1 : int32_t(words[1]);
   if (words[0]) return fail(AGG_E_TIMEOUT, "a chunk wait gave up (flag %d)", words[1] == 0xFFFFFFFFu ? -1 : int(words[1]));
@@ -752,15 +827,23 @@ extern "C" int agg_put_signal(void* dst, const void* src, size_t bytes, uint32_t
 // AllGather + GEMM
 // ------------------------------------------------------------------------------------------
 
-extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64_t k,
-                       int chunk_rows, int dtype, float scale_a, float scale_b,
-                       const void* const* peer_src, void* gather, uint32_t* flags, const void* b, void* c,
-                       const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
-                       agg_stream stream, agg_stream copy_stream) {
+namespace {
+
+// ag_gemm and ag_gemm_noalloc: the same call on the ctx's own scratch (noalloc false) or on the
+// device's static array, without any allocation (noalloc true).
+int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64_t k,
+                 int chunk_rows, int dtype, float scale_a, float scale_b,
+                 const void* const* peer_src, void* gather, uint32_t* flags, const void* b, void* c,
+                 const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
+                 agg_stream stream, agg_stream copy_stream, bool noalloc) {
   if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
   if (int rc = agg_check_ag_args(world, rank, m_shard, n, k, chunk_rows, dtype, scale_a, scale_b,
                                  peer_src, gather, flags, b, c, order, n_order, mode, stream, copy_stream))
     return rc;
+  if (noalloc && ctx->producer != AGG_PRODUCER_CU)
+    return fail(AGG_E_STATE, "ag_gemm_noalloc runs the in-kernel producer only (agg_ctx_set_producer)");
+  const Scratch sp = noalloc ? static_scratch(ctx->device) : own_scratch(ctx);
+  if (!sp.words) return fail(AGG_E_STATE, "no static scratch on device %d", ctx->device);
   const int64_t m = int64_t(world) * m_shard;
   if (m == 0) return AGG_OK;
   const TileShape ts = tile_for(ctx, 0, dtype, m, n, k);
@@ -792,11 +875,12 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
 
   GemmArgs g;
   std::memset(&g, 0, sizeof g);
+  g.scratch = sp.words;
   int64_t tiles = 0;
   int grid = 1;
   if (kernel) {
     const std::vector<int32_t> rows = ag_row_tile_order(world, rank, m_shard, chunk_rows, ord, ts.bm);
-    if (int rc = upload_rows(ctx, s, rows)) return rc;
+    if (int rc = upload_rows(ctx, sp, s, rows)) return rc;
     g.a = static_cast<const uint8_t*>(gather);
     g.b = static_cast<const uint8_t*>(b);
     g.c = static_cast<uint16_t*>(c);
@@ -818,8 +902,15 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
         return fail(AGG_E_UNSUPPORTED, "split-K over more than %d tiles", kMaxSplitTiles);
       const size_t ws_bytes = size_t(ks.ksplit) * size_t(m) * size_t(n) * sizeof(float);
       if (ws_bytes >= (size_t(1) << 31)) return fail(AGG_E_UNSUPPORTED, "split-K partials exceed 2 GiB");
-      if (int rc = ensure_ws(ctx, ws_bytes)) return rc;
-      g.ws = ctx->ws;
+      if (sp.fixed) {
+        if (ws_bytes > kStaticWsBytes)
+          return fail(AGG_E_UNSUPPORTED, "ag_gemm_noalloc: split-K partials of %zu bytes exceed its %zu-byte scratch",
+                      ws_bytes, kStaticWsBytes);
+        g.ws = reinterpret_cast<float*>(sp.words + kStaticWords);
+      } else {
+        if (int rc = ensure_ws(ctx, ws_bytes)) return rc;
+        g.ws = ctx->ws;
+      }
     }
     g.ksplit = ks.ksplit;
     g.kps = ks.kps;
@@ -838,9 +929,10 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
     fill_common(ctx, g, ts, grid);
     attach_trace(ctx, g, tiles);
   }
+  if (noalloc) ctx->used_static = true;
   if (cu) {
     if (chunks)
-      if (int rc = upload_schedule(ctx, s, ord, delay_us)) return rc;
+      if (int rc = upload_schedule(ctx, sp, s, ord, delay_us)) return rc;
     // pull: an overlapped call whose row tiles each lie inside one shard, with compute units to
     // spare for the copiers, reads the remote rows straight from the peers' blocks (automatic
     // for small gathers, where the chunk copy's latency would otherwise be exposed)
@@ -871,6 +963,26 @@ extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64
   };
   return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
                   [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams, rank); });
+}
+
+}  // namespace
+
+extern "C" int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64_t k,
+                       int chunk_rows, int dtype, float scale_a, float scale_b,
+                       const void* const* peer_src, void* gather, uint32_t* flags, const void* b, void* c,
+                       const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
+                       agg_stream stream, agg_stream copy_stream) {
+  return ag_gemm_impl(ctx, world, rank, m_shard, n, k, chunk_rows, dtype, scale_a, scale_b, peer_src,
+                      gather, flags, b, c, order, n_order, delay_us, mode, stream, copy_stream, false);
+}
+
+extern "C" int ag_gemm_noalloc(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64_t k,
+                               int chunk_rows, int dtype, float scale_a, float scale_b,
+                               const void* const* peer_src, void* gather, uint32_t* flags, const void* b,
+                               void* c, const int32_t* order, int n_order, const uint32_t* delay_us,
+                               int mode, agg_stream stream, agg_stream copy_stream) {
+  return ag_gemm_impl(ctx, world, rank, m_shard, n, k, chunk_rows, dtype, scale_a, scale_b, peer_src,
+                      gather, flags, b, c, order, n_order, delay_us, mode, stream, copy_stream, true);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -917,13 +1029,15 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
   cc.row_bytes = n * 4;
   cc.cps = cpb;
 
+  const Scratch sp = own_scratch(ctx);
   GemmArgs g;
   std::memset(&g, 0, sizeof g);
+  g.scratch = sp.words;
   int64_t tiles = 0;
   int grid = 1;
   if (kernel) {
     const std::vector<int32_t> rows = rs_row_tile_order(world, rank, m, chunk_rows, ord, ts.bm);
-    if (int rc = upload_rows(ctx, s, rows)) return rc;
+    if (int rc = upload_rows(ctx, sp, s, rows)) return rc;
     g.a = static_cast<const uint8_t*>(a);
     g.b = static_cast<const uint8_t*>(b);
     g.send = send;
@@ -958,7 +1072,7 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
   }
   if (cu) {
     if (chunks)
-      if (int rc = upload_schedule(ctx, s, ord, delay_us)) return rc;
+      if (int rc = upload_schedule(ctx, sp, s, ord, delay_us)) return rc;
     Marks marks;
     if (world > 1) {
       marks.copy_flags = flags + size_t(rank) * cpb;

@@ -253,6 +253,28 @@ int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64
             const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
             agg_stream stream, agg_stream copy_stream);
 
+/* ---- AllGather + GEMM without allocation ------------------------------------------------ */
+
+/* For callers that cannot allocate device memory while they run (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): ag_gemm, with the same arguments,
+ * results and errors, except that it allocates nothing. Its kernels keep their counters, status,
+ * tables and split-K partials in a static device array of 8 MiB + 78 KiB that the library holds
+ * on each GPU until the process ends (its address is looked up, and its counters cleared, once
+ * per device when the first ctx on that device is created), instead of in the ctx's scratch and
+ * the partial buffer ag_gemm grows on demand.
+ *  - AGG_E_UNSUPPORTED when the call's split-K partials (parts x M x N x 4 bytes) exceed 8 MiB.
+ *  - AGG_E_STATE unless the ctx's producer is AGG_PRODUCER_CU (the copy engines' streams are
+ *    created on demand).
+ *  - Every ctx on a GPU shares that GPU's array and the array keeps the last call's contents:
+ *    calls that overlap in time on one GPU (two streams, two threads, two ctxs) race. After
+ *    AGG_E_TIMEOUT, agg_ctx_reset clears the array's counters too; agg_ctx_status reports its
+ *    status together with the ctx's own. */
+int ag_gemm_noalloc(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64_t k,
+                    int chunk_rows, int dtype, float scale_a, float scale_b,
+                    const void* const* peer_src, void* gather, uint32_t* flags, const void* b, void* c,
+                    const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
+                    agg_stream stream, agg_stream copy_stream);
+
 /* ---- GEMM + ReduceScatter -------------------------------------------------------------- */
 
 /* P = A @ B in fp32 (bf16 operands); rows split into `world` blocks of Mb = m/world rows.
