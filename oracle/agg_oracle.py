@@ -18,6 +18,12 @@ What it computes, and where that is stated:
   p; the owner's block is the sum of all W partial blocks. One rank's share: its own product
   P = A @ B, the W-1 non-local row blocks of P (what it sends), and its reduced block
   P[block r] + sum of the W-1 incoming partial blocks.
+* GEMM+AllReduce (section "DITRON adds three levels of tiling" names AllReduce among the
+  chunked collectives): every rank's partial of the same output, summed on every rank; one
+  rank's share sends its partial and adds the W-1 incoming ones.
+* The FFN chain (same section's task-level tiles in one persistent kernel; section "The
+  performance case has a narrow, useful boundary" measures an FFN module on AMD GPUs):
+  AllGather+GEMM, an elementwise activation (SiLU), then GEMM+ReduceScatter.
 * The chunk / tile bookkeeping (section "DITRON adds three levels of tiling": collectives are
   broken into chunks that are paired with computation tiles, with synchronization inserted):
   which chunks a row tile needs, and the order in which row tiles become computable when the
@@ -43,6 +49,9 @@ __all__ = [
     "gather_ref",
     "ag_gemm_ref",
     "gemm_rs_ref",
+    "gemm_ar_ref",
+    "silu",
+    "ffn_chain_ref",
     "covering_chunks",
     "ag_mtile_order",
     "rs_mtile_order",
@@ -188,6 +197,78 @@ def gemm_rs_ref(a_mk, b_kn, peers, world: int, rank: int, dtype: str = "bf16"):
         if q != rank:
             out = out + peers64[q]
     return send, out
+
+
+# ----------------------------------------------------------------------------------------------
+# GEMM + AllReduce
+# ----------------------------------------------------------------------------------------------
+
+def gemm_ar_ref(a_mk, b_kn, peers, world: int, rank: int, dtype: str = "bf16"):
+    """One rank's share of GEMM+AllReduce, float64.
+
+    The same page ("DITRON adds three levels of tiling") names AllReduce among the collectives
+    the middle end cuts into chunks paired with compute tiles. Every rank holds a partial
+    product of the same M x N output (the rows of its K shard times its weight rows); the
+    AllReduce leaves the sum of all W partials on every rank. One rank's share in the one-shot
+    form, where each rank sends its whole partial to every peer and reduces all of them itself:
+      send: P = A @ B (M x N), what this rank sends to every peer;
+      out:  P + the W-1 incoming partials, added in ascending rank order.
+    a_mk: raw (M, K); b_kn: raw (K, N); peers: float array (W, M, N), slot `rank` ignored.
+    """
+    a = _decode(np.asarray(a_mk), dtype)
+    b = _decode(np.asarray(b_kn), dtype)
+    p = a @ b
+    out = p.copy()
+    peers64 = np.asarray(peers, dtype=np.float64)
+    for q in range(world):
+        if q != rank:
+            out = out + peers64[q]
+    return p, out
+
+
+# ----------------------------------------------------------------------------------------------
+# The FFN chain: AllGather+GEMM -> activation -> GEMM+ReduceScatter
+# ----------------------------------------------------------------------------------------------
+
+def silu(x) -> np.ndarray:
+    """x * sigmoid(x) = x / (1 + e^-x) in float64 (the activation of the Qwen3 MLP whose
+    tensor-parallel FFN the pages measure on AMD GPUs). Large negative x gives -0."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def ffn_chain_ref(shards, w1_kn, w2_kn, peers, world: int, rank: int, dtype: str = "bf16"):
+    """One rank's share of a tensor-parallel FFN built from the two overlapped operations, float64.
+
+    Page "Triton-distributed is turning communication into compiler territory", section "DITRON
+    adds three levels of tiling" (task-level tiles scheduled as one persistent kernel) and
+    section "The performance case has a narrow, useful boundary" (the FFN module on AMD GPUs):
+    the column-parallel first layer gathers the activations (AllGather+GEMM), the activation is
+    applied elementwise, and the row-parallel second layer's partial product is reduce-scattered.
+      h    = silu(concat(shards) @ W1)                 (M x N1)
+      y    = h @ W2                                     (M x N2, this rank's partial)
+      send = the W-1 non-local row blocks of y, ascending block index (M/W rows each)
+      out  = y[block rank] + the W-1 incoming partial blocks, ascending rank order
+    shards: W raw arrays (Ms, K1); w1_kn: raw (K1, N1); w2_kn: raw (N1, N2); peers: float array
+    (W, M/W, N2), slot `rank` ignored. Returns (h, send, out).
+    """
+    g = _decode(gather_ref(shards), dtype)
+    h = silu(g @ _decode(np.asarray(w1_kn), dtype))
+    y = h @ _decode(np.asarray(w2_kn), dtype)
+    m = y.shape[0]
+    if m % world:
+        raise ValueError("M must be a multiple of world")
+    mb = m // world
+    blocks = [y[j * mb:(j + 1) * mb] for j in range(world)]
+    send = np.stack([blocks[j] for j in range(world) if j != rank]) if world > 1 else \
+        np.zeros((0, mb, y.shape[1]))
+    out = blocks[rank].copy()
+    peers64 = np.asarray(peers, dtype=np.float64)
+    for q in range(world):
+        if q != rank:
+            out = out + peers64[q]
+    return h, send, out
 
 
 # ----------------------------------------------------------------------------------------------

@@ -349,3 +349,142 @@ def test_planted_schedule_mistake_fails_the_pin():
     order = inputs.ring_order(world, rank, ms // cr)[::-1]
     naive = list(range(world * ms // bm))
     assert naive != _simulate_ag(world, rank, ms, cr, order, bm)
+
+
+# ------------------------------------------------------------------ GEMM + AllReduce
+
+@pytest.mark.parametrize("world,rank", [(1, 0), (2, 1), (4, 3), (8, 0)])
+def test_gemm_ar_vs_exact_rational(world, rank):
+    rng = np.random.default_rng(700 + world * 10 + rank)
+    m, k, n = 3, 16, 4
+    a = _random_raw((m, k), "bf16", rng)
+    b = _random_raw((k, n), "bf16", rng)
+    peers = rng.standard_normal((world, m, n)).astype(np.float32)
+    send, out = O.gemm_ar_ref(a, b, peers, world, rank)
+    p = _exact_matmul(_frac_matrix(a, "bf16"), _frac_matrix(b, "bf16"))
+    for i in range(m):
+        for c in range(n):
+            e = p[i][c]
+            assert abs(Fraction(float(send[i, c])) - e) <= abs(e) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 30)
+            e = e + sum(Fraction(float(peers[q, i, c])) for q in range(world) if q != rank)
+            assert abs(Fraction(float(out[i, c])) - e) <= abs(e) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 30)
+
+
+@pytest.mark.parametrize("case", _golden()["ar"], ids=lambda c: c["name"])
+def test_ar_worked_examples(case):
+    send, out = O.gemm_ar_ref(_bf16_bits(case["a"]), _bf16_bits(case["b"]),
+                              np.array(case["peers"], dtype=np.float32), case["world"], case["rank"])
+    assert np.array_equal(send, np.array(case["send"], dtype=np.float64))
+    assert np.array_equal(out, np.array(case["out"], dtype=np.float64))
+
+
+def test_planted_ar_mistake_fails_the_pin():
+    """Adding the rank's own peer slot (instead of skipping it) fails the worked example."""
+    case = _golden()["ar"][0]
+    peers = np.array(case["peers"], dtype=np.float64)
+    send, _ = O.gemm_ar_ref(_bf16_bits(case["a"]), _bf16_bits(case["b"]), peers, case["world"], case["rank"])
+    wrong = send + peers.sum(axis=0)
+    assert not np.array_equal(wrong, np.array(case["out"], dtype=np.float64))
+
+
+# ------------------------------------------------------------------ the activation (SiLU)
+
+def _silu_decimal(x) -> Fraction:
+    """x / (1 + e^-x) with decimal's own 60-digit exp: an implementation independent of numpy's."""
+    import decimal
+    with decimal.localcontext() as ctx:
+        ctx.prec = 60
+        d = decimal.Decimal(Fraction(x).numerator) / decimal.Decimal(Fraction(x).denominator)
+        return Fraction(d / (1 + (-d).exp()))
+
+
+@pytest.mark.parametrize("x", [0.0, 1e-8, -1e-8, 0.5, -0.5, 1.0, -1.0, 2.0, -3.25, 7.5, -12.0,
+                               20.0, -40.0, 88.0, -700.0])
+def test_silu_vs_high_precision(x):
+    got = Fraction(float(O.silu(np.float64(x))))
+    want = _silu_decimal(x)
+    assert abs(got - want) <= abs(want) * Fraction(1, 10 ** 15) + Fraction(1, 10 ** 300)
+
+
+def test_silu_closed_forms():
+    assert O.silu(0.0) == 0.0
+    # sigmoid(ln 3) = 3/4
+    assert abs(float(O.silu(np.log(3.0))) - 0.75 * np.log(3.0)) <= 1e-15
+    # x sigmoid(x) - (-x) sigmoid(-x) = x
+    xs = np.linspace(-20, 20, 81)
+    assert np.allclose(O.silu(xs) - O.silu(-xs), xs, rtol=0, atol=1e-13)
+    # the large-|x| limits: silu(x) -> x, silu(-x) -> -0
+    assert O.silu(800.0) == 800.0 and O.silu(-800.0) == 0.0
+
+
+# ------------------------------------------------------------------ the FFN chain
+
+def _ffn_exact(shards, w1, w2, peers, world, rank):
+    """Exact rationals for both products, 60-digit SiLU in between."""
+    g = sum((_frac_matrix(s, "bf16") for s in shards), [])
+    pre = _exact_matmul(g, _frac_matrix(w1, "bf16"))
+    h = [[_silu_decimal(v) for v in row] for row in pre]
+    y = _exact_matmul(h, _frac_matrix(w2, "bf16"))
+    mb = len(y) // world
+    send = [[y[j * mb + i] for i in range(mb)] for j in range(world) if j != rank]
+    out = [[y[rank * mb + i][c] + sum(Fraction(float(peers[q][i][c])) for q in range(world) if q != rank)
+            for c in range(len(y[0]))] for i in range(mb)]
+    return h, send, out
+
+
+def _close(got, want):
+    return abs(Fraction(float(got)) - want) <= abs(want) * Fraction(1, 10 ** 12) + Fraction(1, 10 ** 30)
+
+
+@pytest.mark.parametrize("world,rank", [(1, 0), (2, 1), (4, 2)])
+def test_ffn_chain_vs_exact(world, rank):
+    rng = np.random.default_rng(800 + world * 10 + rank)
+    ms, k1, n1, n2 = 2, 8, 6, 3
+    shards = [_random_raw((ms, k1), "bf16", rng) for _ in range(world)]
+    w1 = _random_raw((k1, n1), "bf16", rng)
+    w2 = _random_raw((n1, n2), "bf16", rng)
+    peers = rng.standard_normal((world, ms, n2)).astype(np.float32)
+    h, send, out = O.ffn_chain_ref(shards, w1, w2, peers, world, rank)
+    eh, es, eo = _ffn_exact(shards, w1, w2, peers, world, rank)
+    assert all(_close(h[i, j], eh[i][j]) for i in range(len(eh)) for j in range(n1))
+    assert send.shape == (world - 1, ms, n2)
+    assert all(_close(send[b, i, c], es[b][i][c]) for b in range(world - 1) for i in range(ms) for c in range(n2))
+    assert all(_close(out[i, c], eo[i][c]) for i in range(ms) for c in range(n2))
+
+
+@pytest.mark.parametrize("case", _golden()["ffn"], ids=lambda c: c["name"])
+def test_ffn_worked_examples(case):
+    s = 2.0 / (1.0 + np.exp(-2.0))          # silu(2) from its definition
+    h, send, out = O.ffn_chain_ref([_bf16_bits(x) for x in case["shards"]], _bf16_bits(case["w1"]),
+                                   _bf16_bits(case["w2"]), np.array(case["peers"], dtype=np.float32),
+                                   case["world"], case["rank"])
+    assert np.allclose(h, [[0.0, s], [s - 2.0, 0.0]], rtol=0, atol=1e-15)
+    assert np.allclose(send, [[[s - 2.0]]], rtol=0, atol=1e-15)
+    assert np.allclose(out, [[s + 0.5]], rtol=0, atol=1e-15)
+
+
+def _ffn_no_activation(shards, w1, w2, peers, world, rank):
+    g = O.decode_bf16(O.gather_ref(shards))
+    y = (g @ O.decode_bf16(w1)) @ O.decode_bf16(w2)
+    mb = y.shape[0] // world
+    return y[rank * mb:(rank + 1) * mb] + sum(np.asarray(peers, np.float64)[q] for q in range(world) if q != rank)
+
+
+def _ffn_activation_last(shards, w1, w2, peers, world, rank):
+    g = O.decode_bf16(O.gather_ref(shards))
+    y = O.silu((g @ O.decode_bf16(w1)) @ O.decode_bf16(w2))
+    mb = y.shape[0] // world
+    return y[rank * mb:(rank + 1) * mb] + sum(np.asarray(peers, np.float64)[q] for q in range(world) if q != rank)
+
+
+@pytest.mark.parametrize("mutant", [_ffn_no_activation, _ffn_activation_last])
+def test_planted_ffn_mistakes_fail_the_pins(mutant):
+    rng = np.random.default_rng(811)
+    world, rank, ms, k1, n1, n2 = 2, 1, 2, 8, 6, 3
+    shards = [_random_raw((ms, k1), "bf16", rng) for _ in range(world)]
+    w1 = _random_raw((k1, n1), "bf16", rng)
+    w2 = _random_raw((n1, n2), "bf16", rng)
+    peers = rng.standard_normal((world, ms, n2)).astype(np.float32)
+    _, _, eo = _ffn_exact(shards, w1, w2, peers, world, rank)
+    bad = mutant(shards, w1, w2, peers, world, rank)
+    assert not all(_close(bad[i, c], eo[i][c]) for i in range(ms) for c in range(n2))
