@@ -60,6 +60,10 @@ _SIGNATURES = {
                         ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _i32p, _c_int, _u32p, _c_int, _vp, _vp],
     "gemm_rs": [_vp, _c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp, _vp, _vp,
                 ctypes.POINTER(_vp), _vp, _vp, _vp, _i32p, _c_int, _u32p, _c_int, _vp, _vp],
+    "gemm_ar": [_vp, _c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp, _vp, _vp,
+                ctypes.POINTER(_vp), _vp, _vp, _vp, _i32p, _c_int, _u32p, _c_int, _vp, _vp],
+    "agg_check_ar_args": [_c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp, _vp, _vp,
+                          ctypes.POINTER(_vp), _vp, _vp, _vp, _i32p, _c_int, _c_int, _vp, _vp],
     "agg_tile_shape": [_c_int, _c_int, _c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_int),
                        ctypes.POINTER(_c_int)],
     "agg_ag_row_tile_order": [_c_int, _c_int, _c_i64, _c_int, _i32p, _c_int, _c_int, _i32p,
@@ -337,6 +341,28 @@ def gemm_rs(ctx, world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_
           _u32_array(delay_us), _mode(mode), _stream(stream), _stream(copy_stream))
 
 
+def _ar_ptrs(world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_src, recv, flags, out):
+    """Checked device pointers of a gemm_ar call, in its argument order."""
+    cpb = m // chunk_rows if chunk_rows > 0 else 0
+    items = [(a, m * k * 2, "a"), (b, k * n * 2, "b"), (send, m * n * 4, "send"),
+             (send_flags, cpb * 4, "send_flags"), (recv, world * m * n * 4, "recv"),
+             (flags, world * cpb * 4, "flags"), (out, m * n * 4, "out")]
+    if peer_src is not None:
+        items += [(p, m * n * 4 if i != rank else 0, f"peer_src[{i}]") for i, p in enumerate(peer_src)]
+    ptrs = _checked(items)
+    peers = (_vp * len(peer_src))(*ptrs[7:]) if peer_src is not None else None
+    return (*ptrs[:4], peers, *ptrs[4:7])
+
+
+def gemm_ar(ctx, world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_src, recv, flags,
+            out, order=None, delay_us=None, mode="overlap", stream=None, copy_stream=None) -> None:
+    ordr, n_order = _i32_array(order)
+    ptrs = _ar_ptrs(world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_src, recv,
+                    flags, out)
+    _call("gemm_ar", ctx, world, rank, m, n, k, chunk_rows, *ptrs, ordr, n_order,
+          _u32_array(delay_us), _mode(mode), _stream(stream), _stream(copy_stream))
+
+
 def agg_tile_shape(op: int, dtype, m: int, n: int, k: int):
     bm, bn = _c_int(), _c_int()
     _call("agg_tile_shape", op, _dtype(dtype), m, n, k, ctypes.byref(bm), ctypes.byref(bn))
@@ -382,3 +408,12 @@ def agg_check_rs_args(world, rank, m, n, k, chunk_rows, a, b, send, send_flags, 
 
 def last_error() -> str:
     return load().agg_last_error().decode()
+
+
+def agg_check_ar_args(world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_src, recv,
+                      flags, out, order=None, mode="overlap", stream=None, copy_stream=None) -> int:
+    ordr, n_order = _i32_array(order)
+    return load().agg_check_ar_args(world, rank, m, n, k, chunk_rows, _ptr(a), _ptr(b), _ptr(send),
+                                    _ptr(send_flags), _ptr_array(peer_src), _ptr(recv), _ptr(flags),
+                                    _ptr(out), ordr, n_order, _mode(mode), _stream(stream),
+                                    _stream(copy_stream))

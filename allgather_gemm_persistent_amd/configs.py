@@ -90,6 +90,38 @@ class RsConfig:
         return inputs.seeded_order(self.world, self.rank, self.chunks_per_block, self.seed + 1)
 
 
+@dataclass(frozen=True)
+class ArConfig:
+    """GEMM+AllReduce: P = A (M x K) @ B (K x N) in fp32, summed with W-1 peers' partials."""
+    name: str
+    world: int
+    rank: int
+    m: int
+    k: int
+    n: int
+    chunk_rows: int
+    a_dist: dict
+    b_dist: dict
+    peer_dist: dict
+    order_kind: str
+    seed: int
+    dtype: str = "bf16"
+    op: str = field(default="ar")
+
+    @property
+    def chunks_per_peer(self) -> int:
+        return self.m // self.chunk_rows
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.m * self.n * self.k
+
+    def order(self) -> list:
+        if self.order_kind == "ring":
+            return inputs.ring_order(self.world, self.rank, self.chunks_per_peer)
+        return inputs.seeded_order(self.world, self.rank, self.chunks_per_peer, self.seed + 1)
+
+
 U11 = {"kind": "uniform", "lo": -1.0, "hi": 1.0}
 N1 = {"kind": "normal", "std": 1.0}
 N002 = {"kind": "normal", "std": 0.02}
@@ -115,6 +147,12 @@ CONFIGS = {
     "ag_w8_8192x7168x8192_fp8": AgConfig(
         "ag_w8_8192x7168x8192_fp8", world=8, rank=0, m_shard=1024, k=8192, n=7168, dtype="fp8",
         chunk_rows=256, a_dist=N1, b_dist=N002, order_kind="seeded", seed=1050),
+    # decode-shaped GEMM+AllReduce: the row-parallel layer after the decode AllGather+GEMM (its
+    # 3584-wide per-rank activations times this rank's 3584 x 8192 weight rows), partials of the
+    # whole 128 x 8192 output summed over 8 ranks
+    "ar_w8_128x8192x3584_bf16_decode": ArConfig(
+        "ar_w8_128x8192x3584_bf16_decode", world=8, rank=0, m=128, k=3584, n=8192, chunk_rows=16,
+        a_dist=N1, b_dist=N002, peer_dist=N1, order_kind="seeded", seed=1060),
 }
 
 HEADLINE = "ag_w8_4096x3584x8192_bf16"
@@ -139,5 +177,15 @@ def make_rs_data(cfg: RsConfig):
     a, _ = inputs.draw(cfg.a_dist, (cfg.m, cfg.k), cfg.dtype, cfg.seed)
     b, _ = inputs.draw(cfg.b_dist, (cfg.k, cfg.n), cfg.dtype, cfg.seed + 3)
     peers, _ = inputs.draw(cfg.peer_dist, (cfg.world, cfg.m_block, cfg.n), "f32", cfg.seed + 4)
+    peers[cfg.rank].zero_()
+    return {"a": a, "b": b, "peers": peers}
+
+
+def make_ar_data(cfg: ArConfig):
+    """Host tensors for a GEMM+AllReduce workload: a (M x K), b (K x N) bf16, and peers
+    (W x M x N fp32) where slot ``rank`` is zero and unused."""
+    a, _ = inputs.draw(cfg.a_dist, (cfg.m, cfg.k), cfg.dtype, cfg.seed)
+    b, _ = inputs.draw(cfg.b_dist, (cfg.k, cfg.n), cfg.dtype, cfg.seed + 3)
+    peers, _ = inputs.draw(cfg.peer_dist, (cfg.world, cfg.m, cfg.n), "f32", cfg.seed + 4)
     peers[cfg.rank].zero_()
     return {"a": a, "b": b, "peers": peers}

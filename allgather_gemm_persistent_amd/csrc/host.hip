@@ -65,7 +65,7 @@ constexpr int kDefaultReservedCus = 32;
 constexpr int64_t kPullMaxBytes = int64_t(4) << 20;
 constexpr int kTimingRing = 256;          // launches whose kernel duration is kept
 
-enum FlagSlot { kFlagsAg = 0, kFlagsRsRecv = 1, kFlagsRsSend = 2, kFlagSlots = 3 };
+enum FlagSlot { kFlagsAg = 0, kFlagsRsRecv = 1, kFlagsRsSend = 2, kFlagsArRecv = 3, kFlagsArSend = 4, kFlagSlots = 5 };
 
 // The no-allocation entry point's scratch: the kernel's counters, status and tables
 // (kScrWords words, rounded up to 256 bytes) followed by room for split-K partials.
@@ -114,8 +114,8 @@ struct agg_ctx {
   bool timing = false;                      // record a timing event pair around each launch
   hipEvent_t ev_t0[kTimingRing] = {}, ev_t1[kTimingRing] = {};
   uint64_t launches = 0;                    // launches recorded since timing was switched on
-  uint32_t* bound[kFlagSlots] = {nullptr, nullptr, nullptr};
-  size_t bound_words[kFlagSlots] = {0, 0, 0};
+  uint32_t* bound[kFlagSlots] = {};
+  size_t bound_words[kFlagSlots] = {};
   int force_split = 0;                       // 0: split-K chosen per call
   float* ws = nullptr;                       // split-K partials (grown on demand)
   size_t ws_bytes = 0;
@@ -1090,6 +1090,107 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
     return timed_launch(ctx, [&]() {
       return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiReduceScatter, grid, ctx->ks);
     });
+  };
+  return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
+                  [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams, rank); });
+}
+
+// ------------------------------------------------------------------------------------------
+// GEMM + AllReduce
+// ------------------------------------------------------------------------------------------
+
+extern "C" int gemm_ar(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, int64_t k, int chunk_rows,
+                       const void* a, const void* b, float* send, uint32_t* send_flags,
+                       const float* const* peer_src, float* recv, uint32_t* flags, float* out,
+                       const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
+                       agg_stream stream, agg_stream copy_stream) {
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (int rc = agg_check_ar_args(world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_src,
+                                 recv, flags, out, order, n_order, mode, stream, copy_stream))
+    return rc;
+  if (m == 0 || n == 0) return AGG_OK;
+  const TileShape ts = tile_for(ctx, 2, AGG_BF16, m, n, k);
+  if ((m + ts.bm - 1) / ts.bm > AGG_MAX_ROW_TILES) return fail(AGG_E_UNSUPPORTED, "row tiles exceed %d", AGG_MAX_ROW_TILES);
+  HIP_TRY(hipSetDevice(ctx->device));
+  const int cpb = int(m / chunk_rows);
+  if (world > 1) {
+    if (int rc = bind_flags(ctx, kFlagsArRecv, flags, size_t(world) * cpb)) return rc;
+    if (int rc = bind_flags(ctx, kFlagsArSend, send_flags, size_t(cpb))) return rc;
+  }
+  const std::vector<int32_t> ord = order ? std::vector<int32_t>(order, order + n_order) : ring_order(world, rank, cpb);
+  hipStream_t s = S(stream);
+  const bool kernel = mode != AGG_COPY_ONLY;
+  const bool chunks = (mode != AGG_GEMM_ONLY) && world > 1;
+  const bool cu = ctx->producer == AGG_PRODUCER_CU;
+  std::vector<hipStream_t> cstreams;
+  if (chunks && !cu)
+    if (int rc = copy_streams(ctx, ord.size(), cstreams)) return rc;
+  uint32_t epoch = ctx->epoch;
+  if (chunks)
+    if (int rc = next_epoch(ctx, s, &epoch)) return rc;
+
+  // chunk q of peer p: rows [q*cr, (q+1)*cr) of its M x N partial, into receive slot p
+  ChunkCopy cc;
+  cc.src = reinterpret_cast<const uint8_t* const*>(peer_src);
+  cc.dst = reinterpret_cast<uint8_t*>(recv);
+  cc.slot_rows = m;
+  cc.cr = chunk_rows;
+  cc.row_bytes = n * 4;
+  cc.cps = cpb;
+
+  const Scratch sp = own_scratch(ctx);
+  GemmArgs g;
+  std::memset(&g, 0, sizeof g);
+  g.scratch = sp.words;
+  int grid = 1;
+  if (kernel) {
+    // every tile reduces every peer's rows: plain ascending row tiles
+    std::vector<int32_t> rows(size_t((m + ts.bm - 1) / ts.bm));
+    for (size_t i = 0; i < rows.size(); ++i) rows[i] = int32_t(i);
+    if (int rc = upload_rows(ctx, sp, s, rows)) return rc;
+    g.a = static_cast<const uint8_t*>(a);
+    g.b = static_cast<const uint8_t*>(b);
+    g.send = send;
+    g.out = out;
+    g.recv = recv;
+    g.flags = flags;
+    g.send_flags = send_flags;
+    g.M = m;
+    g.N = n;
+    g.K = k;
+    g.m_block = m;
+    g.world = world;
+    g.rank = rank;
+    g.chunk_rows = chunk_rows;
+    g.cps = cpb;
+    g.n_row_tiles = int(rows.size());
+    g.n_col_tiles = int((n + ts.bn - 1) / ts.bn);
+    g.ksplit = 1;
+    g.kps = int(std::max<int64_t>(1, (k * 2 + slice_bytes(AGG_BF16) - 1) / slice_bytes(AGG_BF16)));
+    g.epoch = world > 1 ? epoch : 0;
+    g.scale = 1.0f;
+    const int64_t tiles = int64_t(g.n_row_tiles) * g.n_col_tiles;
+    grid = grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks && !cu);
+    fill_common(ctx, g, ts, grid);
+    attach_trace(ctx, g, tiles);
+  }
+  if (cu) {
+    if (chunks)
+      if (int rc = upload_schedule(ctx, sp, s, ord, delay_us)) return rc;
+    Marks marks;
+    if (world > 1) {
+      marks.copy_flags = flags + size_t(rank) * cpb;   // nothing arrives for this rank's own slot
+      marks.count = cpb;
+    }
+    return schedule_cu(ctx, mode, s, S(copy_stream), kernel, chunks,
+                       [&](bool copies, bool tiles_on, bool timed) {
+                         return launch_cu(ctx, s, g, ts, AGG_BF16, kEpiAllReduce, grid, cc, flags,
+                                          ord.size(), delay_us != nullptr, world, epoch, copies,
+                                          tiles_on, timed, marks);
+                       });
+  }
+  auto launch = [&]() -> int {
+    return timed_launch(ctx, [&]() { return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiAllReduce, grid, ctx->ks); });
   };
   return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
                   [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams, rank); });

@@ -27,17 +27,17 @@ constexpr int kScrLocal = kScrSplit + 1024;  // RS: local tiles stored, per row 
 constexpr int kScrWords = kScrLocal + AGG_MAX_ROW_TILES;
 constexpr int kMaxLists = 16;
 
-enum Epilogue { kEpiAllGather = 0, kEpiReduceScatter = 1 };
+enum Epilogue { kEpiAllGather = 0, kEpiReduceScatter = 1, kEpiAllReduce = 2 };
 
 struct GemmArgs {
   const uint8_t* a;         // AG: gather buffer M x K; RS: A, M x K
   const uint8_t* b;         // K x N (N contiguous)
   uint16_t* c;              // AG output, M x N bfloat16
-  float* send;              // RS: (world-1) x Mb x N
-  float* out;               // RS: Mb x N
-  const float* recv;        // RS: world x Mb x N
-  const uint32_t* flags;    // flags the tiles wait on (AG gather flags / RS receive flags)
-  uint32_t* send_flags;     // RS
+  float* send;              // RS: (world-1) x Mb x N; AR: M x N (the partial every peer gets)
+  float* out;               // RS: Mb x N; AR: M x N
+  const float* recv;        // RS: world x Mb x N; AR: world x M x N
+  const uint32_t* flags;    // flags the tiles wait on (AG gather flags / RS, AR receive flags)
+  uint32_t* send_flags;     // RS: world x Mb/cr; AR: M/cr
   uint32_t* scratch;        // ctx scratch (kScr*)
   uint32_t* trace;          // optional per-tile trace, 8 words per tile
   int64_t M, N, K;          // K in elements

@@ -415,7 +415,7 @@ __device__ inline bool claim(const GemmArgs& a, int home, int nstat, Tile& t) {
 template <int BM, int EPI>
 __device__ inline void tile_rows(const GemmArgs& a, int row_tile, int64_t& lo, int64_t& hi,
                                  int& block, int& tile_in_block) {
-  if (EPI == kEpiAllGather) {
+  if (EPI != kEpiReduceScatter) {
     lo = (int64_t)row_tile * BM;
     hi = lo + BM < a.M ? lo + BM : a.M;
     block = 0;
@@ -441,6 +441,11 @@ __device__ bool wait_chunks(const GemmArgs& a, int64_t lo, int64_t hi, int block
     q_lo = (int)(lo / a.chunk_rows);
     nq = (int)((hi - 1) / a.chunk_rows) - q_lo + 1;
     count = nq;
+  } else if (EPI == kEpiAllReduce) {
+    // every peer's chunks of these rows (chunk q of peer p is flag p*cps + q)
+    q_lo = (int)(lo / a.chunk_rows);
+    nq = (int)((hi - 1) / a.chunk_rows) - q_lo + 1;
+    count = (a.world - 1) * nq;
   } else {
     if (block != a.rank) return true;
     const int64_t base = (int64_t)block * a.m_block;
@@ -764,8 +769,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     // ---- wait for the chunks this tile's rows need
     if (wave == 0) {
       uint32_t seen = 0xFFFFFFFFu;
-      // (ReduceScatter tiles need no chunk: the received partials are added by reduce_local)
-      const bool ok = pull || EPI == kEpiReduceScatter || wait_chunks<EPI>(a, lo, hi, block, seen);
+      // (ReduceScatter tiles need no chunk: the received partials are added by reduce_local;
+      // AllReduce tiles wait for theirs in the epilogue, after the main loop)
+      const bool ok = pull || EPI != kEpiAllGather || wait_chunks<EPI>(a, lo, hi, block, seen);
       if (lane == 0) {
         s_ok = ok;
         if (trec) { trec[3] = seen; trec[6] = wall_ticks(); }
@@ -1334,6 +1340,79 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
           }
         }
       }
+    } else if (EPI == kEpiAllReduce) {
+      // One-shot AllReduce, fused: this tile's partial goes to `send` (what every peer receives;
+      // write-through, so it is visible everywhere once the stores complete) and the tile that
+      // completes a chunk of `send` raises its send flag; then, once every peer's chunks of these
+      // rows have arrived, out = partial + the peers' partials in ascending rank order (a fixed
+      // order: `out` does not depend on arrival order).
+      const int64_t MN = a.M * a.N;
+      const __amdgpu_buffer_rsrc_t rsend = __builtin_amdgcn_make_buffer_rsrc(a.send, 0, (int)(MN * 4), kBufferFlags);
+      const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, (int)(MN * 4), kBufferFlags);
+      const __amdgpu_buffer_rsrc_t rrecv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(a.recv), 0, (int)(a.world * MN * 4), kBufferFlags);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int64_t m = lo + qrow(i);
+        if (m >= hi) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t n = n0 + qcol(j);
+          if (n >= a.N) continue;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rsend,
+                                                 (int)((m * a.N + n) * 4), 0, kStoreSystemCoherent);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0) {
+        const int q_lo = (int)(lo / a.chunk_rows), q_hi = (int)((hi - 1) / a.chunk_rows);
+        for (int q = q_lo; q <= q_hi; ++q) {
+          const int64_t clo = (int64_t)q * a.chunk_rows;
+          const int64_t chi = clo + a.chunk_rows;
+          const int t_first = (int)(clo / BM), t_last = (int)((chi - 1) / BM);
+          const uint32_t expect = (uint32_t)(t_last - t_first + 1) * (uint32_t)a.n_col_tiles;
+          const uint32_t prev = __hip_atomic_fetch_add(a.scratch + kScrRsCount + q, 1u, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+          if (prev + 1 == expect)
+            __hip_atomic_store(a.send_flags + q, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+      }
+      if (wave == 0) {
+        uint32_t seen = 0xFFFFFFFFu;
+        const bool ok = wait_chunks<kEpiAllReduce>(a, lo, hi, 0, seen);
+        if (lane == 0) {
+          s_ok = ok;
+          if (trec) { trec[3] = seen; trec[6] = wall_ticks(); }
+        }
+      }
+      __syncthreads();
+      if (__builtin_amdgcn_readfirstlane(s_ok)) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+        const int world = __builtin_amdgcn_readfirstlane(a.world), rank = __builtin_amdgcn_readfirstlane(a.rank);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int64_t m = lo + qrow(i);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + qcol(j);
+            if (m >= hi || n >= a.N) continue;
+            // every peer's quad in flight, then added in rank order
+            f32x4 in[AGG_MAX_WORLD - 1];
+#pragma unroll
+            for (int q = 0; q < AGG_MAX_WORLD - 1; ++q) {
+              const int p = q < rank ? q : q + 1;
+              const int off = p < world ? (int)(((int64_t)p * MN + m * a.N + n) * 4) : (int)kOutOfRange;
+              in[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrecv, off, 0, 0));
+            }
+            f32x4 v = acc[i][j];
+#pragma unroll
+            for (int q = 0; q < AGG_MAX_WORLD - 1; ++q)
+              if (q + 1 < world) v += in[q];
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rout, (int)((m * a.N + n) * 4), 0, 0);
+          }
+        }
+      }
     } else {
       const int64_t base = (int64_t)block * a.m_block;
       const bool local = (block == a.rank);
@@ -1434,6 +1513,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         __hip_atomic_store(a.scratch + kScrPieces + a.scratch[kScrOrder + i], 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (EPI == kEpiAllReduce) {
+      for (int i = tid; i < a.cps; i += NT)
+        __hip_atomic_store(a.scratch + kScrRsCount + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (EPI == kEpiReduceScatter) {
       for (int i = tid; i < a.world * a.cps; i += NT)
         __hip_atomic_store(a.scratch + kScrRsCount + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1481,6 +1564,8 @@ int max_blocks_per_cu(int bm, int bn, int dtype, int epilogue) {
     if (dtype == AGG_FP8_E4M3) return occupancy_shape<AGG_FP8_E4M3, kEpiAllGather>(bm, bn);
   } else if (epilogue == kEpiReduceScatter && dtype == AGG_BF16) {
     return occupancy_shape<AGG_BF16, kEpiReduceScatter>(bm, bn);
+  } else if (epilogue == kEpiAllReduce && dtype == AGG_BF16) {
+    return occupancy_shape<AGG_BF16, kEpiAllReduce>(bm, bn);
   }
   return 0;
 }
@@ -1502,6 +1587,8 @@ hipError_t launch_gemm(const GemmArgs& args, int bm, int bn, int dtype, int epil
     if (dtype == AGG_FP8_E4M3) return launch_shape<AGG_FP8_E4M3, kEpiAllGather>(args, bm, bn, grid, stream);
   } else if (epilogue == kEpiReduceScatter && dtype == AGG_BF16) {
     return launch_shape<AGG_BF16, kEpiReduceScatter>(args, bm, bn, grid, stream);
+  } else if (epilogue == kEpiAllReduce && dtype == AGG_BF16) {
+    return launch_shape<AGG_BF16, kEpiAllReduce>(args, bm, bn, grid, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -375,3 +375,59 @@ extern "C" int agg_rs_row_tile_order(int world, int rank, int64_t m, int chunk_r
   std::copy(t.begin(), t.end(), out_tiles);
   return AGG_OK;
 }
+
+extern "C" int agg_check_ar_args(int world, int rank, int64_t m, int64_t n, int64_t k, int chunk_rows,
+                                 const void* a, const void* b, const void* send, const void* send_flags,
+                                 const float* const* peer_src, const void* recv, const void* flags,
+                                 const void* out, const int32_t* order, int n_order, int mode,
+                                 agg_stream stream, agg_stream copy_stream) {
+  using namespace agg;
+  clear_error();
+  if (world < 1 || world > AGG_MAX_WORLD) return fail(AGG_E_ARG, "world %d not in [1, %d]", world, AGG_MAX_WORLD);
+  if (rank < 0 || rank >= world) return fail(AGG_E_ARG, "rank %d not in [0, %d)", rank, world);
+  if (m < 0 || n < 0 || k < 0) return fail(AGG_E_ARG, "negative size");
+  if (mode < AGG_OVERLAP || mode > AGG_COPY_ONLY) return fail(AGG_E_ARG, "unknown mode %d", mode);
+  if (chunk_rows < 1) return fail(AGG_E_ARG, "chunk_rows %d < 1", chunk_rows);
+  if (m % chunk_rows) return fail(AGG_E_ARG, "chunk_rows %d does not divide m %lld", chunk_rows, (long long)m);
+  const int64_t cpb = m / chunk_rows;
+  if (world * cpb > AGG_MAX_CHUNKS) return fail(AGG_E_UNSUPPORTED, "%lld chunks exceed %d", (long long)(world * cpb), AGG_MAX_CHUNKS);
+  if ((k * 2) % 16) return fail(AGG_E_ARG, "k * 2 bytes = %lld is not a multiple of 16", (long long)(k * 2));
+  if ((n * 2) % 16) return fail(AGG_E_ARG, "a row of b, n * 2 bytes = %lld, is not a multiple of 16", (long long)(n * 2));
+  if (k > (int64_t(1) << 30) || n > (int64_t(1) << 30) || m > (int64_t(1) << 30))
+    return fail(AGG_E_UNSUPPORTED, "dimension beyond 2^30");
+  if (m * k * 2 >= (int64_t(1) << 31) || n * k * 2 >= (int64_t(1) << 31))
+    return fail(AGG_E_UNSUPPORTED, "an operand reaches 2 GiB (the kernel addresses operands with 31-bit offsets)");
+  if (world * m * n * 4 >= (int64_t(1) << 31))
+    return fail(AGG_E_UNSUPPORTED, "the receive buffer reaches 2 GiB (31-bit offsets)");
+  if (uses_copy_stream(mode) && copy_stream && stream == copy_stream)
+    return fail(AGG_E_ARG, "stream and copy_stream must differ");
+  if (m > 0 && n > 0) {
+    if (mode != AGG_COPY_ONLY) {
+      if (k > 0 && (!a || misaligned(a))) return fail(AGG_E_ARG, "a is NULL or not 16-byte aligned");
+      if (k > 0 && (!b || misaligned(b))) return fail(AGG_E_ARG, "b is NULL or not 16-byte aligned");
+      if (!send || misaligned(send)) return fail(AGG_E_ARG, "send is NULL or not 16-byte aligned");
+      if (world > 1 && (!send_flags || (reinterpret_cast<uintptr_t>(send_flags) & 3u))) return fail(AGG_E_ARG, "send_flags is NULL or not 4-byte aligned");
+      if (!out || misaligned(out)) return fail(AGG_E_ARG, "out is NULL or not 16-byte aligned");
+    }
+    if (world > 1) {
+      if (!recv || misaligned(recv)) return fail(AGG_E_ARG, "recv is NULL or not 16-byte aligned");
+      if (!flags || (reinterpret_cast<uintptr_t>(flags) & 3u)) return fail(AGG_E_ARG, "flags is NULL or not 4-byte aligned");
+      if (mode != AGG_GEMM_ONLY) {
+        if (!peer_src) return fail(AGG_E_ARG, "peer_src is NULL");
+        for (int p = 0; p < world; ++p)
+          if (p != rank && (!peer_src[p] || misaligned(peer_src[p])))
+            return fail(AGG_E_ARG, "peer_src[%d] is NULL or not 16-byte aligned", p);
+      }
+    }
+  }
+  if (order == nullptr) {
+    if (n_order != 0) return fail(AGG_E_ARG, "order is NULL but n_order = %d", n_order);
+  } else if (int rc = check_order(world, rank, int(cpb), order, n_order)) {
+    return rc;
+  }
+  if (m > 0) {
+    TileShape s = choose_tile(2, AGG_BF16, m, n, k);
+    if ((m + s.bm - 1) / s.bm > AGG_MAX_ROW_TILES) return fail(AGG_E_UNSUPPORTED, "row tiles exceed %d", AGG_MAX_ROW_TILES);
+  }
+  return AGG_OK;
+}

@@ -121,3 +121,50 @@ class RsWorkload:
         if self.ctx is not None:
             B.agg_ctx_destroy(self.ctx)
             self.ctx = None
+
+
+class ArWorkload:
+    """One rank's share of GEMM+AllReduce with W-1 emulated peers on one GPU.
+
+    a: CPU (M x K) bf16; b_kn: CPU (K x N) bf16; peers: CPU (W x M x N) float32 (slot rank
+    unused): the partial each peer sends.
+    """
+
+    def __init__(self, world, rank, a, b_kn, peers, chunk_rows, device="cuda", tile=None,
+                 producer="cu"):
+        self.world, self.rank, self.chunk_rows = world, rank, chunk_rows
+        self.m, self.k = a.shape
+        self.n = b_kn.shape[1]
+        self.device = torch.device(device)
+        self.a = a.to(self.device)
+        self.b = b_kn.contiguous().to(self.device)
+        self.peers = [peers[p].to(self.device) if p != rank else None for p in range(world)]
+        self.recv = torch.zeros(world, self.m, self.n, dtype=torch.float32, device=self.device)
+        cpb = self.m // chunk_rows if chunk_rows else 0
+        self.flags = torch.zeros(max(world * cpb, 1), dtype=torch.int32, device=self.device)
+        self.send_flags = torch.zeros(max(cpb, 1), dtype=torch.int32, device=self.device)
+        self.send = torch.zeros(self.m, self.n, dtype=torch.float32, device=self.device)
+        self.out = torch.zeros(self.m, self.n, dtype=torch.float32, device=self.device)
+        self.copy_stream = None
+        self.ctx = B.agg_ctx_create(self.device.index or 0)
+        B.agg_ctx_set_producer(self.ctx, producer)
+        if tile:
+            B.agg_ctx_set_tile(self.ctx, *tile)
+
+    def peer_ptrs(self):
+        return [p if p is not None else 0 for p in self.peers]
+
+    def run(self, mode="overlap", order=None, delay_us=None, stream=None):
+        stream = stream or torch.cuda.current_stream(self.device)
+        B.gemm_ar(self.ctx, self.world, self.rank, self.m, self.n, self.k, self.chunk_rows,
+                  self.a, self.b, self.send, self.send_flags, self.peer_ptrs(), self.recv,
+                  self.flags, self.out, order=order, delay_us=delay_us, mode=mode, stream=stream,
+                  copy_stream=self.copy_stream)
+
+    def status(self):
+        return B.agg_ctx_status(self.ctx, torch.cuda.current_stream(self.device))
+
+    def close(self):
+        if self.ctx is not None:
+            B.agg_ctx_destroy(self.ctx)
+            self.ctx = None

@@ -300,10 +300,41 @@ int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, int64_t k, 
             const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
             agg_stream stream, agg_stream copy_stream);
 
+/* ---- GEMM + AllReduce -------------------------------------------------------------------- */
+
+/* One rank's share of GEMM+AllReduce (page "Triton-distributed is turning communication into
+ * compiler territory", section "DITRON adds three levels of tiling": AllReduce is one of the
+ * collectives cut into chunks paired with compute tiles). Every rank holds a partial P_q of the
+ * same M x N output (its K shard of the activations times its rows of the weight); AllReduce
+ * leaves their sum on every rank. One-shot form: each rank sends its whole partial to every
+ * peer and adds the W-1 it receives. Each output tile computes its part of P = A @ B (fp32),
+ * stores it to `send`, waits for every peer's chunks of its rows and writes
+ * out = P + recv[p] for p != rank in ascending rank order, all in one kernel.
+ *   a                device (m x k) bf16; b: device (k x n) bf16, N contiguous
+ *   send             device fp32 m x n: this rank's partial P, what every peer receives
+ *   send_flags       device uint32[m/cr]: entry q is set to the epoch once rows [q*cr, (q+1)*cr)
+ *                    of `send` are complete
+ *   peer_src         HOST array of `world` device pointers to fp32 m x n partials: what peer p
+ *                    sends; entry `rank` ignored
+ *   recv             device fp32 world x m x n: symmetric receive buffer; the producer copies
+ *                    peer p's partial into slot p chunk by chunk (cr rows each; slot `rank` unused)
+ *   flags            device uint32[world * m/cr]: receive flag of chunk q of peer p is
+ *                    p*(m/cr) + q; every entry ends at the epoch (the rank's own slot included)
+ *   out              device fp32 m x n: P + sum over p != rank, ascending p, of recv[p]; a fixed
+ *                    summation order, so the result does not depend on arrival order
+ *   order/n_order, delay_us, mode, streams: as for gemm_rs, over the (world-1)*m/cr incoming
+ *   chunks (NULL order = ring order). flags and send_flags are bound to the ctx like ag_gemm's.
+ * Alignment: k*2 and n*2 bytes multiples of 16; cr divides m. */
+int gemm_ar(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, int64_t k, int chunk_rows,
+            const void* a, const void* b, float* send, uint32_t* send_flags,
+            const float* const* peer_src, float* recv, uint32_t* flags, float* out,
+            const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
+            agg_stream stream, agg_stream copy_stream);
+
 /* ---- host-only planning (no device needed; used by the calls above) --------------------- */
 
-/* The tile shape the library uses for a call: *bm x *bn output tiles, *n_lists claim lists.
- * op: 0 = ag_gemm, 1 = gemm_rs. m is M (ag: world*m_shard). */
+/* The tile shape the library uses for a call: *bm x *bn output tiles.
+ * op: 0 = ag_gemm, 1 = gemm_rs, 2 = gemm_ar. m is M (ag: world*m_shard). */
 int agg_tile_shape(int op, int dtype, int64_t m, int64_t n, int64_t k, int* bm, int* bn);
 
 /* Row-tile order of ag_gemm: tiles of `bm` rows of C sorted by the arrival position of the
@@ -328,6 +359,11 @@ int agg_check_ag_args(int world, int rank, int64_t m_shard, int64_t n, int64_t k
                       const int32_t* order, int n_order, int mode, agg_stream stream,
                       agg_stream copy_stream);
 int agg_check_rs_args(int world, int rank, int64_t m, int64_t n, int64_t k, int chunk_rows,
+                      const void* a, const void* b, const void* send, const void* send_flags,
+                      const float* const* peer_src, const void* recv, const void* flags,
+                      const void* out, const int32_t* order, int n_order, int mode,
+                      agg_stream stream, agg_stream copy_stream);
+int agg_check_ar_args(int world, int rank, int64_t m, int64_t n, int64_t k, int chunk_rows,
                       const void* a, const void* b, const void* send, const void* send_flags,
                       const float* const* peer_src, const void* recv, const void* flags,
                       const void* out, const int32_t* order, int n_order, int mode,

@@ -77,6 +77,24 @@ def test_rs_args(lib):
         assert _rs(**kw) == B.AGG_E_ARG, kw
 
 
+def _ar(**kw):
+    args = dict(world=2, rank=1, m=128, n=256, k=512, chunk_rows=16, a=FAKE, b=FAKE, send=FAKE,
+                send_flags=FAKE, peer_src=[FAKE, FAKE], recv=FAKE, flags=FAKE, out=FAKE, order=None,
+                mode="overlap", stream=1, copy_stream=2)
+    args.update(kw)
+    return B.agg_check_ar_args(**args)
+
+
+def test_ar_args(lib):
+    assert _ar() == B.AGG_OK
+    assert _ar(order=list(range(8))) == B.AGG_OK            # peer 0's 8 chunks
+    assert _ar(world=1, rank=0, peer_src=None, send_flags=None) == B.AGG_OK
+    for kw in (dict(m=120), dict(chunk_rows=0), dict(n=252), dict(k=4), dict(out=None),
+               dict(send=FAKE + 4), dict(recv=None), dict(order=[8]), dict(order=list(range(8, 16))),
+               dict(copy_stream=1), dict(world=0), dict(rank=2), dict(send_flags=FAKE + 2)):
+        assert _ar(**kw) == B.AGG_E_ARG, kw
+
+
 @pytest.mark.parametrize("world,rank,ms,cr,bm,seed", [
     (2, 0, 128, 64, 64, 1), (8, 0, 512, 128, 256, 0), (8, 3, 16, 16, 64, 2), (3, 2, 10, 5, 64, 3),
     (8, 0, 1024, 256, 256, 4), (5, 1, 60, 12, 128, 5), (1, 0, 100, 10, 64, 0)])
@@ -104,11 +122,12 @@ def test_tile_shapes_for_the_workloads(lib):
     sizes allow)."""
     got = {}
     for name, cfg in configs.CONFIGS.items():
-        op = 1 if cfg.op == "rs" else 0
+        op = {"ag": 0, "rs": 1, "ar": 2}[cfg.op]
         got[name] = B.agg_tile_shape(op, cfg.dtype, cfg.m, cfg.n, cfg.k)
     assert got["ag_w8_4096x3584x8192_bf16"] == (256, 224)     # 16 x 16 = 256 tiles
     assert got["rs_w8_8192x8192x3584_bf16"] == (256, 256)     # 32 x 32 = 1024 tiles
     assert got["ag_w8_8192x7168x8192_fp8"] == (256, 224)      # 32 x 32 = 1024 tiles
+    assert got["ar_w8_128x8192x3584_bf16_decode"] == (64, 64)  # 2 x 128 = 256 tiles
 
 
 def test_ctx_calls_reject_null(lib):
