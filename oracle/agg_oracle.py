@@ -246,15 +246,18 @@ def ffn_chain_ref(shards, w1_kn, w2_kn, peers, world: int, rank: int, dtype: str
     section "The performance case has a narrow, useful boundary" (the FFN module on AMD GPUs):
     the column-parallel first layer gathers the activations (AllGather+GEMM), the activation is
     applied elementwise, and the row-parallel second layer's partial product is reduce-scattered.
-      h    = silu(concat(shards) @ W1)                 (M x N1)
+      h    = bf16(silu(concat(shards) @ W1))           (M x N1)
       y    = h @ W2                                     (M x N2, this rank's partial)
       send = the W-1 non-local row blocks of y, ascending block index (M/W rows each)
       out  = y[block rank] + the W-1 incoming partial blocks, ascending rank order
+    The activation is the second layer's operand, so it is a tensor of the operands' type: h is
+    silu of the exact product rounded to bf16 (nearest, ties to even), and the second product
+    uses those values.
     shards: W raw arrays (Ms, K1); w1_kn: raw (K1, N1); w2_kn: raw (N1, N2); peers: float array
-    (W, M/W, N2), slot `rank` ignored. Returns (h, send, out).
+    (W, M/W, N2), slot `rank` ignored. Returns (h, send, out), h as the exact values of the bf16.
     """
     g = _decode(gather_ref(shards), dtype)
-    h = silu(g @ _decode(np.asarray(w1_kn), dtype))
+    h = decode_bf16(encode_bf16_rne(silu(g @ _decode(np.asarray(w1_kn), dtype))))
     y = h @ _decode(np.asarray(w2_kn), dtype)
     m = y.shape[0]
     if m % world:

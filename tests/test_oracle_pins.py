@@ -419,11 +419,19 @@ def test_silu_closed_forms():
 
 # ------------------------------------------------------------------ the FFN chain
 
+def _bf16_round(x: Fraction) -> Fraction:
+    """Nearest bf16 (ties to even) of an exact value, through torch's float32 -> bfloat16 cast
+    (float32 first: a second rounding only on the rare values within 2^-24 of a bf16 midpoint)."""
+    v = torch.tensor(float(x), dtype=torch.float32).to(torch.bfloat16).to(torch.float64).item()
+    return Fraction(v)
+
+
 def _ffn_exact(shards, w1, w2, peers, world, rank):
-    """Exact rationals for both products, 60-digit SiLU in between."""
+    """Exact rationals for both products, 60-digit SiLU in between, the activation rounded to bf16
+    (the second layer's operand type)."""
     g = sum((_frac_matrix(s, "bf16") for s in shards), [])
     pre = _exact_matmul(g, _frac_matrix(w1, "bf16"))
-    h = [[_silu_decimal(v) for v in row] for row in pre]
+    h = [[_bf16_round(_silu_decimal(v)) for v in row] for row in pre]
     y = _exact_matmul(h, _frac_matrix(w2, "bf16"))
     mb = len(y) // world
     send = [[y[j * mb + i] for i in range(mb)] for j in range(world) if j != rank]
@@ -455,12 +463,17 @@ def test_ffn_chain_vs_exact(world, rank):
 @pytest.mark.parametrize("case", _golden()["ffn"], ids=lambda c: c["name"])
 def test_ffn_worked_examples(case):
     s = 2.0 / (1.0 + np.exp(-2.0))          # silu(2) from its definition
+    # h is rounded to bf16: s = 1.7616 lies between the bf16 values 225/128 and 226/128 (spacing
+    # 2^-7 in [1, 2)), nearer the first; s - 2 = -0.23841 lies between -244/1024 and -245/1024
+    # (spacing 2^-10 in [1/8, 1/4)), nearer the first
+    hs, hm = 225 / 128, -244 / 1024
+    assert abs(s - hs) < 2 ** -8 and abs((s - 2.0) - hm) < 2 ** -11
     h, send, out = O.ffn_chain_ref([_bf16_bits(x) for x in case["shards"]], _bf16_bits(case["w1"]),
                                    _bf16_bits(case["w2"]), np.array(case["peers"], dtype=np.float32),
                                    case["world"], case["rank"])
-    assert np.allclose(h, [[0.0, s], [s - 2.0, 0.0]], rtol=0, atol=1e-15)
-    assert np.allclose(send, [[[s - 2.0]]], rtol=0, atol=1e-15)
-    assert np.allclose(out, [[s + 0.5]], rtol=0, atol=1e-15)
+    assert np.array_equal(h, [[0.0, hs], [hm, 0.0]])
+    assert np.array_equal(send, [[[hm]]])
+    assert np.array_equal(out, [[hs + 0.5]])
 
 
 def _ffn_no_activation(shards, w1, w2, peers, world, rank):
