@@ -64,6 +64,10 @@ _SIGNATURES = {
                 ctypes.POINTER(_vp), _vp, _vp, _vp, _i32p, _c_int, _u32p, _c_int, _vp, _vp],
     "agg_check_ar_args": [_c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp, _vp, _vp,
                           ctypes.POINTER(_vp), _vp, _vp, _vp, _i32p, _c_int, _c_int, _vp, _vp],
+    "ffn_chain": [_vp, _c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_int,
+                  ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_vp), _vp,
+                  _vp, _vp, _i32p, _c_int, _i32p, _c_int, _c_int, _vp, _vp],
+    "agg_ctx_set_chain_fused": [_vp, _c_int],
     "agg_tile_shape": [_c_int, _c_int, _c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_int),
                        ctypes.POINTER(_c_int)],
     "agg_ag_row_tile_order": [_c_int, _c_int, _c_i64, _c_int, _i32p, _c_int, _c_int, _i32p,
@@ -361,6 +365,37 @@ def gemm_ar(ctx, world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_
                     flags, out)
     _call("gemm_ar", ctx, world, rank, m, n, k, chunk_rows, *ptrs, ordr, n_order,
           _u32_array(delay_us), _mode(mode), _stream(stream), _stream(copy_stream))
+
+
+def ffn_chain(ctx, world, rank, m_shard, k1, n1, n2, chunk_rows, rs_chunk_rows, peer_src, gather,
+              flags, w1, h, w2, send, send_flags, rs_peer_src, recv, rs_flags, out, order=None,
+              rs_order=None, mode="overlap", stream=None, copy_stream=None) -> None:
+    m = world * m_shard
+    cps = m_shard // chunk_rows if chunk_rows > 0 else 0
+    cpb = m_shard // rs_chunk_rows if rs_chunk_rows > 0 else 0
+    items = [(gather, m * k1 * 2, "gather"), (flags, world * cps * 4, "flags"), (w1, k1 * n1 * 2, "w1"),
+             (h, m * n1 * 2, "h"), (w2, n1 * n2 * 2, "w2"),
+             (send, max(world - 1, 0) * m_shard * n2 * 4, "send"), (send_flags, world * cpb * 4, "send_flags"),
+             (recv, world * m_shard * n2 * 4, "recv"), (rs_flags, world * cpb * 4, "rs_flags"),
+             (out, m_shard * n2 * 4, "out")]
+    for i, p in enumerate(peer_src or []):
+        items.append((p, m_shard * k1 * 2 if i != rank else 0, f"peer_src[{i}]"))
+    for i, p in enumerate(rs_peer_src or []):
+        items.append((p, m_shard * n2 * 4 if i != rank else 0, f"rs_peer_src[{i}]"))
+    ptrs = _checked(items)
+    nw = len(peer_src or [])
+    peers = (_vp * nw)(*ptrs[10:10 + nw]) if peer_src is not None else None
+    rs_peers = (_vp * len(rs_peer_src))(*ptrs[10 + nw:]) if rs_peer_src is not None else None
+    ordr, n_order = _i32_array(order)
+    rs_ordr, n_rs_order = _i32_array(rs_order)
+    _call("ffn_chain", ctx, world, rank, m_shard, k1, n1, n2, chunk_rows, rs_chunk_rows, peers,
+          ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], ptrs[5], ptrs[6], rs_peers, ptrs[7], ptrs[8],
+          ptrs[9], ordr, n_order, rs_ordr, n_rs_order, _mode(mode), _stream(stream),
+          _stream(copy_stream))
+
+
+def agg_ctx_set_chain_fused(ctx, on: bool = True) -> None:
+    _call("agg_ctx_set_chain_fused", ctx, 1 if on else 0)
 
 
 def agg_tile_shape(op: int, dtype, m: int, n: int, k: int):

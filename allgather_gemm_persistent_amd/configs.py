@@ -122,6 +122,42 @@ class ArConfig:
         return inputs.seeded_order(self.world, self.rank, self.chunks_per_peer, self.seed + 1)
 
 
+@dataclass(frozen=True)
+class FfnConfig:
+    """FFN chain: h = silu(concat(shards) @ W1) (M x N1 bf16); y = h @ W2 (M x N2 fp32),
+    reduce-scattered over W row blocks of Ms rows."""
+    name: str
+    world: int
+    rank: int
+    m_shard: int
+    k1: int
+    n1: int
+    n2: int
+    chunk_rows: int
+    rs_chunk_rows: int
+    a_dist: dict
+    w1_dist: dict
+    w2_dist: dict
+    peer_dist: dict
+    seed: int
+    dtype: str = "bf16"
+    op: str = field(default="ffn")
+
+    @property
+    def m(self) -> int:
+        return self.world * self.m_shard
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.m * self.k1 * self.n1 + 2 * self.m * self.n1 * self.n2
+
+    def order(self) -> list:
+        return inputs.ring_order(self.world, self.rank, self.m_shard // self.chunk_rows)
+
+    def rs_order(self) -> list:
+        return inputs.seeded_order(self.world, self.rank, self.m_shard // self.rs_chunk_rows, self.seed + 1)
+
+
 U11 = {"kind": "uniform", "lo": -1.0, "hi": 1.0}
 N1 = {"kind": "normal", "std": 1.0}
 N002 = {"kind": "normal", "std": 0.02}
@@ -153,6 +189,13 @@ CONFIGS = {
     "ar_w8_128x8192x3584_bf16_decode": ArConfig(
         "ar_w8_128x8192x3584_bf16_decode", world=8, rank=0, m=128, k=3584, n=8192, chunk_rows=16,
         a_dist=N1, b_dist=N002, peer_dist=N1, order_kind="seeded", seed=1060),
+    # the two bf16 operations as one tensor-parallel FFN: the W=8 AllGather+GEMM above
+    # (4096 x 8192 @ 8192 x 3584), SiLU, then GEMM+ReduceScatter with the ReduceScatter
+    # workload's weight shape (3584 x 8192) on its 4096 rows
+    "ffn_w8_4096x8192x3584_bf16": FfnConfig(
+        "ffn_w8_4096x8192x3584_bf16", world=8, rank=0, m_shard=512, k1=8192, n1=3584, n2=8192,
+        chunk_rows=128, rs_chunk_rows=128, a_dist=N1, w1_dist=N002, w2_dist=N002, peer_dist=N1,
+        seed=1070),
 }
 
 HEADLINE = "ag_w8_4096x3584x8192_bf16"
@@ -189,3 +232,15 @@ def make_ar_data(cfg: ArConfig):
     peers, _ = inputs.draw(cfg.peer_dist, (cfg.world, cfg.m, cfg.n), "f32", cfg.seed + 4)
     peers[cfg.rank].zero_()
     return {"a": a, "b": b, "peers": peers}
+
+
+def make_ffn_data(cfg: FfnConfig):
+    """Host tensors for the FFN chain: shards (W x Ms x K1 bf16), w1 (K1 x N1), w2 (N1 x N2) bf16,
+    peers (W x Ms x N2 fp32, slot ``rank`` zero and unused)."""
+    a, _ = inputs.draw(cfg.a_dist, (cfg.m, cfg.k1), cfg.dtype, cfg.seed)
+    w1, _ = inputs.draw(cfg.w1_dist, (cfg.k1, cfg.n1), cfg.dtype, cfg.seed + 3)
+    w2, _ = inputs.draw(cfg.w2_dist, (cfg.n1, cfg.n2), cfg.dtype, cfg.seed + 5)
+    peers, _ = inputs.draw(cfg.peer_dist, (cfg.world, cfg.m_shard, cfg.n2), "f32", cfg.seed + 4)
+    peers[cfg.rank].zero_()
+    shards = [a[p * cfg.m_shard:(p + 1) * cfg.m_shard].contiguous() for p in range(cfg.world)]
+    return {"shards": shards, "w1": w1, "w2": w2, "peers": peers}

@@ -117,6 +117,7 @@ struct agg_ctx {
   uint32_t* bound[kFlagSlots] = {};
   size_t bound_words[kFlagSlots] = {};
   int force_split = 0;                       // 0: split-K chosen per call
+  bool chain_fused = true;                   // ffn_chain: both layers in one launch
   float* ws = nullptr;                       // split-K partials (grown on demand)
   size_t ws_bytes = 0;
   int producer = AGG_PRODUCER_CU;
@@ -405,27 +406,50 @@ int upload_schedule(agg_ctx* ctx, const Scratch& sp, hipStream_t s, const std::v
   return upload_table(ctx, sp, s, 2, d);
 }
 
-// Copy-job fields of the kernel arguments for the CU producer.
-void fill_copies(agg_ctx* ctx, GemmArgs& g, const ChunkCopy& cc, uint32_t* flags, size_t n_order,
-                 bool delays, int world, int grid, int pull_copiers) {
-  for (int p = 0; p < world; ++p) g.peer[p] = cc.src[p];
-  g.sym = cc.dst;
-  g.put_flags = flags;
-  g.chunk_bytes = cc.cr * cc.row_bytes;
+// One set of copies of the producer: its chunk geometry, the flags it releases and how many
+// chunks arrive (in the order uploaded for it).
+struct CopyPlan {
+  ChunkCopy cc;
+  uint32_t* flags;
+  size_t n_order;
+};
+
+// Copy-job fields of the kernel arguments for the CU producer: set s's jobs follow set s-1's, its
+// arrival order follows theirs in the uploaded table, and its piece counters start at s * 2048.
+void fill_copies(agg_ctx* ctx, GemmArgs& g, const CopyPlan* sets, int nsets, bool delays, int world,
+                 int grid, int pull_copiers) {
   // automatic piece size: as many pieces per chunk as keep every job in one round of the
   // copying workgroups (so no workgroup copies twice while others idle), in whole 4 KiB pages,
   // at least 16 KiB
   const int copiers = pull_copiers > 0 ? pull_copiers
                       : ctx->copy_wgs > 0 ? std::min(ctx->copy_wgs, grid) : grid;
-  const int64_t per_chunk = std::max<int64_t>(1, int64_t(copiers) / std::max<int64_t>(int64_t(n_order), 1));
-  const int64_t autop =
-      std::max<int64_t>(((g.chunk_bytes + per_chunk - 1) / per_chunk + 4095) / 4096 * 4096, 16384);
-  const int64_t piece = std::max<int64_t>(16, (ctx->piece_bytes > 0 ? ctx->piece_bytes : autop) / 16 * 16);
-  g.piece_bytes = std::min<int64_t>(g.chunk_bytes, piece);
-  g.pieces = g.piece_bytes > 0 ? int((g.chunk_bytes + g.piece_bytes - 1) / g.piece_bytes) : 1;
-  if (g.piece_bytes == 0) g.piece_bytes = 16;   // empty chunks (k = 0): one empty piece each
-  g.copy_jobs = uint32_t(n_order) * uint32_t(g.pieces);
-  g.copy_cps = cc.cps;
+  size_t chunks = 0;
+  for (int s = 0; s < nsets; ++s) chunks += sets[s].n_order;
+  const int64_t per_chunk = std::max<int64_t>(1, int64_t(copiers) / std::max<int64_t>(int64_t(chunks), 1));
+  g.copy_jobs = 0;
+  int order_off = 0;
+  for (int s = 0; s < 2; ++s) {
+    CopySet& cs = g.cs[s];
+    std::memset(&cs, 0, sizeof cs);
+    if (s >= nsets) continue;
+    const CopyPlan& pl = sets[s];
+    for (int p = 0; p < world; ++p) cs.peer[p] = pl.cc.src[p];
+    cs.sym = pl.cc.dst;
+    cs.put_flags = pl.flags;
+    cs.chunk_bytes = pl.cc.cr * pl.cc.row_bytes;
+    const int64_t autop =
+        std::max<int64_t>(((cs.chunk_bytes + per_chunk - 1) / per_chunk + 4095) / 4096 * 4096, 16384);
+    const int64_t piece = std::max<int64_t>(16, (ctx->piece_bytes > 0 ? ctx->piece_bytes : autop) / 16 * 16);
+    cs.piece_bytes = std::min<int64_t>(cs.chunk_bytes, piece);
+    cs.pieces = cs.piece_bytes > 0 ? int((cs.chunk_bytes + cs.piece_bytes - 1) / cs.piece_bytes) : 1;
+    if (cs.piece_bytes == 0) cs.piece_bytes = 16;   // empty chunks (k = 0): one empty piece each
+    cs.jobs = uint32_t(pl.n_order) * uint32_t(cs.pieces);
+    cs.cps = pl.cc.cps;
+    cs.order_off = order_off;
+    cs.piece_off = s * (AGG_MAX_CHUNKS / 2);
+    order_off += int(pl.n_order);
+    g.copy_jobs += cs.jobs;
+  }
   // default: every workgroup copies first. A grid of one tile per workgroup finishes at the last
   // tile's start plus one tile time, and the copy ends soonest with every workgroup on it.
   g.copy_wgs = copiers;
@@ -439,30 +463,33 @@ void attach_trace(agg_ctx* ctx, GemmArgs& g, int64_t tiles) {
   }
 }
 
-// One launch of the persistent kernel under the CU producer: `copies` adds the copy jobs,
-// `tiles_on` keeps the GEMM tiles (without them: a copy-only grid of one workgroup per CU).
-// Flags a launch raises to the epoch at its start: the local slot of the flags the producer
+// Flags a launch raises to the epoch at its start: the local slot of the flags each producer set
 // releases (a launch with copy jobs) and, ReduceScatter, the local slot of the send flags (a
 // launch with tiles).
 struct Marks {
-  uint32_t* copy_flags = nullptr;
+  uint32_t* copy_flags[2] = {nullptr, nullptr};
+  int copy_count[2] = {0, 0};
   uint32_t* tile_flags = nullptr;
-  int count = 0;
+  int tile_count = 0;
 };
 
+// One launch of the persistent kernel under the CU producer: `copies` adds the copy jobs,
+// `tiles_on` keeps the GEMM tiles (without them: a copy-only grid of one workgroup per CU).
 int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int dtype, int epi,
-              int grid, const ChunkCopy& cc, uint32_t* flags, size_t n_order, bool delays,
-              int world, uint32_t epoch, bool copies, bool tiles_on, bool timed, const Marks& marks,
-              int pull_copiers = 0) {
+              int grid, const CopyPlan* sets, int nsets, bool delays, int world, uint32_t epoch,
+              bool copies, bool tiles_on, bool timed, const Marks& marks, int pull_copiers = 0) {
   GemmArgs h = g;
-  h.mark_count[0] = h.mark_count[1] = 0;
-  if (copies && marks.copy_flags) {
-    h.mark_flags[0] = marks.copy_flags;
-    h.mark_count[0] = marks.count;
+  h.mark_count[0] = h.mark_count[1] = h.mark_count[2] = 0;
+  if (copies) {
+    for (int s = 0; s < 2; ++s)
+      if (marks.copy_flags[s]) {
+        h.mark_flags[s] = marks.copy_flags[s];
+        h.mark_count[s] = marks.copy_count[s];
+      }
   }
   if (tiles_on && marks.tile_flags) {
-    h.mark_flags[1] = marks.tile_flags;
-    h.mark_count[1] = marks.count;
+    h.mark_flags[2] = marks.tile_flags;
+    h.mark_count[2] = marks.tile_count;
   }
   int gr = grid;
   // pull only where tiles and copies share the launch: the grid gains the copiers
@@ -472,6 +499,8 @@ int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int
   if (!tiles_on) {
     h.n_row_tiles = 0;
     h.n_col_tiles = 0;
+    h.n_row_tiles1 = 0;
+    h.n_col_tiles1 = 0;
     h.trace = nullptr;
     h.trace_tiles = 0;
     h.n_lists = 1;
@@ -482,9 +511,10 @@ int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int
   }
   if (copies) {
     h.epoch = epoch;
-    fill_copies(ctx, h, cc, flags, n_order, delays, world, gr, pull ? pull_copiers : 0);
+    fill_copies(ctx, h, sets, nsets, delays, world, gr, pull ? pull_copiers : 0);
   } else {
     h.copy_jobs = 0;
+    std::memset(h.cs, 0, sizeof h.cs);
   }
   auto go = [&]() { return launch_gemm(h, ts.bm, ts.bn, dtype, epi, gr, ls); };
   if (timed) return timed_launch(ctx, go, ls);
@@ -946,14 +976,15 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
     }
     Marks marks;
     if (world > 1) {
-      marks.copy_flags = flags + size_t(rank) * cps;
-      marks.count = cps;
+      marks.copy_flags[0] = flags + size_t(rank) * cps;
+      marks.copy_count[0] = cps;
     }
+    const CopyPlan plan{cc, flags, ord.size()};
     return schedule_cu(ctx, mode, s, S(copy_stream), kernel, chunks,
                        [&](bool copies, bool tiles_on, bool timed) {
-                         return launch_cu(ctx, s, g, ts, dtype, kEpiAllGather, grid, cc, flags,
-                                          ord.size(), delay_us != nullptr, world, epoch, copies,
-                                          tiles_on, timed, marks, pull_copiers);
+                         return launch_cu(ctx, s, g, ts, dtype, kEpiAllGather, grid, &plan, 1,
+                                          delay_us != nullptr, world, epoch, copies, tiles_on,
+                                          timed, marks, pull_copiers);
                        });
   }
   auto launch = [&]() -> int {
@@ -1066,8 +1097,8 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
     attach_trace(ctx, g, tiles);
     if (world > 1) {
       // nothing is sent for the local block: its send flags are raised with the others' epoch
-      g.mark_flags[1] = send_flags + size_t(rank) * cpb;
-      g.mark_count[1] = cpb;
+      g.mark_flags[2] = send_flags + size_t(rank) * cpb;
+      g.mark_count[2] = cpb;
     }
   }
   if (cu) {
@@ -1075,15 +1106,17 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
       if (int rc = upload_schedule(ctx, sp, s, ord, delay_us)) return rc;
     Marks marks;
     if (world > 1) {
-      marks.copy_flags = flags + size_t(rank) * cpb;
+      marks.copy_flags[0] = flags + size_t(rank) * cpb;
+      marks.copy_count[0] = cpb;
       marks.tile_flags = send_flags + size_t(rank) * cpb;
-      marks.count = cpb;
+      marks.tile_count = cpb;
     }
+    const CopyPlan plan{cc, flags, ord.size()};
     return schedule_cu(ctx, mode, s, S(copy_stream), kernel, chunks,
                        [&](bool copies, bool tiles_on, bool timed) {
-                         return launch_cu(ctx, s, g, ts, AGG_BF16, kEpiReduceScatter, grid, cc,
-                                          flags, ord.size(), delay_us != nullptr, world, epoch,
-                                          copies, tiles_on, timed, marks);
+                         return launch_cu(ctx, s, g, ts, AGG_BF16, kEpiReduceScatter, grid, &plan, 1,
+                                          delay_us != nullptr, world, epoch, copies, tiles_on, timed,
+                                          marks);
                        });
   }
   auto launch = [&]() -> int {
@@ -1179,14 +1212,15 @@ extern "C" int gemm_ar(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
       if (int rc = upload_schedule(ctx, sp, s, ord, delay_us)) return rc;
     Marks marks;
     if (world > 1) {
-      marks.copy_flags = flags + size_t(rank) * cpb;   // nothing arrives for this rank's own slot
-      marks.count = cpb;
+      marks.copy_flags[0] = flags + size_t(rank) * cpb;   // nothing arrives for this rank's own slot
+      marks.copy_count[0] = cpb;
     }
+    const CopyPlan plan{cc, flags, ord.size()};
     return schedule_cu(ctx, mode, s, S(copy_stream), kernel, chunks,
                        [&](bool copies, bool tiles_on, bool timed) {
-                         return launch_cu(ctx, s, g, ts, AGG_BF16, kEpiAllReduce, grid, cc, flags,
-                                          ord.size(), delay_us != nullptr, world, epoch, copies,
-                                          tiles_on, timed, marks);
+                         return launch_cu(ctx, s, g, ts, AGG_BF16, kEpiAllReduce, grid, &plan, 1,
+                                          delay_us != nullptr, world, epoch, copies, tiles_on, timed,
+                                          marks);
                        });
   }
   auto launch = [&]() -> int {
@@ -1194,4 +1228,173 @@ extern "C" int gemm_ar(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
   };
   return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
                   [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams, rank); });
+}
+
+// ------------------------------------------------------------------------------------------
+// The FFN chain: AllGather+GEMM -> SiLU -> GEMM+ReduceScatter
+// ------------------------------------------------------------------------------------------
+
+extern "C" int agg_ctx_set_chain_fused(agg_ctx* ctx, int on) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  ctx->chain_fused = on != 0;
+  return AGG_OK;
+}
+
+extern "C" int ffn_chain(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t k1, int64_t n1,
+                         int64_t n2, int chunk_rows, int rs_chunk_rows, const void* const* peer_src,
+                         void* gather, uint32_t* flags, const void* w1, void* h, const void* w2,
+                         float* send, uint32_t* send_flags, const float* const* rs_peer_src, float* recv,
+                         uint32_t* rs_flags, float* out, const int32_t* order, int n_order,
+                         const int32_t* rs_order, int n_rs_order, int mode, agg_stream stream,
+                         agg_stream copy_stream) {
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  const int64_t m = int64_t(world) * m_shard;
+  // the two layers' arguments, each checked as the operation it is
+  if (int rc = agg_check_ag_args(world, rank, m_shard, n1, k1, chunk_rows, AGG_BF16, 1.0f, 1.0f, peer_src,
+                                 gather, flags, w1, h, order, n_order, mode, stream, copy_stream))
+    return rc;
+  if (int rc = agg_check_rs_args(world, rank, m, n2, n1, rs_chunk_rows, h, w2, send, send_flags,
+                                 rs_peer_src, recv, rs_flags, out, rs_order, n_rs_order, mode, stream,
+                                 copy_stream))
+    return rc;
+  const int cps = int(m_shard / chunk_rows), cpb = int(m_shard / rs_chunk_rows);
+  if (world * cps > AGG_MAX_CHUNKS / 2 || world * cpb > AGG_MAX_CHUNKS / 2)
+    return fail(AGG_E_UNSUPPORTED, "each layer's chunks must stay within %d", AGG_MAX_CHUNKS / 2);
+  if (m == 0 || n1 == 0 || n2 == 0) return AGG_OK;
+  const TileShape ts{256, 256};
+  if ((m + ts.bm - 1) / ts.bm * 2 + world > AGG_MAX_ROW_TILES)
+    return fail(AGG_E_UNSUPPORTED, "row tiles exceed %d", AGG_MAX_ROW_TILES);
+  HIP_TRY(hipSetDevice(ctx->device));
+  if (world > 1) {
+    if (int rc = bind_flags(ctx, kFlagsAg, flags, size_t(world) * cps)) return rc;
+    if (int rc = bind_flags(ctx, kFlagsRsRecv, rs_flags, size_t(world) * cpb)) return rc;
+    if (int rc = bind_flags(ctx, kFlagsRsSend, send_flags, size_t(world) * cpb)) return rc;
+  }
+  const std::vector<int32_t> ord = order ? std::vector<int32_t>(order, order + n_order) : ring_order(world, rank, cps);
+  const std::vector<int32_t> ord2 =
+      rs_order ? std::vector<int32_t>(rs_order, rs_order + n_rs_order) : ring_order(world, rank, cpb);
+  hipStream_t s = S(stream);
+  const bool kernel = mode != AGG_COPY_ONLY;
+  const bool chunks = (mode != AGG_GEMM_ONLY) && world > 1;
+  const bool cu = ctx->producer == AGG_PRODUCER_CU;
+  std::vector<hipStream_t> cstreams;
+  if (chunks && !cu)
+    if (int rc = copy_streams(ctx, ord.size() + ord2.size(), cstreams)) return rc;
+  uint32_t epoch = ctx->epoch;
+  if (chunks)
+    if (int rc = next_epoch(ctx, s, &epoch)) return rc;
+
+  CopyPlan plans[2];
+  plans[0].cc = ChunkCopy{reinterpret_cast<const uint8_t* const*>(peer_src), static_cast<uint8_t*>(gather),
+                          m_shard, chunk_rows, k1 * 2, cps};
+  plans[0].flags = flags;
+  plans[0].n_order = ord.size();
+  plans[1].cc = ChunkCopy{reinterpret_cast<const uint8_t* const*>(rs_peer_src), reinterpret_cast<uint8_t*>(recv),
+                          m_shard, rs_chunk_rows, n2 * 4, cpb};
+  plans[1].flags = rs_flags;
+  plans[1].n_order = ord2.size();
+
+  const Scratch sp = own_scratch(ctx);
+  GemmArgs g;
+  std::memset(&g, 0, sizeof g);
+  g.scratch = sp.words;
+  int grid = 1;
+  if (kernel) {
+    // phase 1's row tiles in arrival order, then phase 2's in ReduceScatter order
+    const std::vector<int32_t> rows1 = ag_row_tile_order(world, rank, m_shard, chunk_rows, ord, ts.bm);
+    const std::vector<int32_t> rows2 = rs_row_tile_order(world, rank, m, rs_chunk_rows, ord2, ts.bm);
+    std::vector<int32_t> rows(rows1);
+    rows.insert(rows.end(), rows2.begin(), rows2.end());
+    if (int rc = upload_rows(ctx, sp, s, rows)) return rc;
+    // phase 2: GEMM+ReduceScatter of h
+    g.a = static_cast<const uint8_t*>(h);
+    g.b = static_cast<const uint8_t*>(w2);
+    g.send = send;
+    g.out = out;
+    g.recv = recv;
+    g.flags = rs_flags;
+    g.send_flags = send_flags;
+    g.M = m;
+    g.N = n2;
+    g.K = n1;
+    g.m_block = m_shard;
+    g.world = world;
+    g.rank = rank;
+    g.chunk_rows = rs_chunk_rows;
+    g.cps = cpb;
+    g.tpb = int((m_shard + ts.bm - 1) / ts.bm);
+    g.n_row_tiles = int(rows2.size());
+    g.n_col_tiles = int((n2 + ts.bn - 1) / ts.bn);
+    // phase 1: AllGather+GEMM into h
+    g.a1 = static_cast<const uint8_t*>(gather);
+    g.b1 = static_cast<const uint8_t*>(w1);
+    g.h = static_cast<uint16_t*>(h);
+    g.flags1 = flags;
+    g.K1 = k1;
+    g.N1 = n1;
+    g.chunk_rows1 = chunk_rows;
+    g.cps1 = cps;
+    g.n_row_tiles1 = int(rows1.size());
+    g.n_col_tiles1 = int((n1 + ts.bn - 1) / ts.bn);
+    g.ksplit = 1;
+    g.kps = 1 << 28;                       // no split: every tile covers its whole K
+    g.epoch = world > 1 ? epoch : 0;
+    g.scale = 1.0f;
+    g.n_lists = 1;
+    g.list_cols = 1;
+    g.timeout_ticks = uint64_t(double(ctx->timeout_us) * ctx->ticks_per_us);
+    const int64_t tasks = int64_t(g.n_row_tiles1) * g.n_col_tiles1 + int64_t(g.n_row_tiles) * g.n_col_tiles;
+    grid = grid_for(ctx, tasks, mode == AGG_OVERLAP && chunks && !cu);
+    if (world > 1) {
+      g.mark_flags[2] = send_flags + size_t(rank) * cpb;   // nothing is sent for the local block
+      g.mark_count[2] = cpb;
+    }
+  }
+  // The tiles as one launch (fused) or as two: phase 1 alone, then phase 2 alone.
+  auto tile_launches = [&](auto&& launch_one) -> int {
+    if (ctx->chain_fused) return launch_one(g, true);
+    GemmArgs g1 = g, g2 = g;
+    g1.n_row_tiles = 0;                    // phase 1 only
+    g2.n_row_tiles1 = 0;                   // phase 2 only: no phase-1 tile to wait for
+    g2.n_col_tiles1 = 0;
+    if (int rc = launch_one(g1, true)) return rc;
+    return launch_one(g2, false);
+  };
+  if (cu) {
+    if (chunks) {
+      std::vector<int32_t> both(ord);
+      both.insert(both.end(), ord2.begin(), ord2.end());
+      if (int rc = upload_schedule(ctx, sp, s, both, nullptr)) return rc;
+    }
+    Marks marks;
+    if (world > 1) {
+      marks.copy_flags[0] = flags + size_t(rank) * cps;
+      marks.copy_count[0] = cps;
+      marks.copy_flags[1] = rs_flags + size_t(rank) * cpb;
+      marks.copy_count[1] = cpb;
+      marks.tile_flags = send_flags + size_t(rank) * cpb;
+      marks.tile_count = cpb;
+    }
+    return schedule_cu(ctx, mode, s, S(copy_stream), kernel, chunks,
+                       [&](bool copies, bool tiles_on, bool timed) {
+                         if (!tiles_on)
+                           return launch_cu(ctx, s, g, ts, AGG_BF16, kEpiFfn, grid, plans, 2, false, world,
+                                            epoch, copies, false, timed, marks);
+                         return tile_launches([&](const GemmArgs& gg, bool first) {
+                           // the copies go with the first (or only) tile launch
+                           return launch_cu(ctx, s, gg, ts, AGG_BF16, kEpiFfn, grid, plans, 2, false, world,
+                                            epoch, copies && first, true, timed, marks);
+                         });
+                       });
+  }
+  auto launch = [&]() -> int {
+    return tile_launches([&](const GemmArgs& gg, bool) {
+      return timed_launch(ctx, [&]() { return launch_gemm(gg, ts.bm, ts.bn, AGG_BF16, kEpiFfn, grid, ctx->ks); });
+    });
+  };
+  return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks, [&]() -> int {
+    if (int rc = produce(plans[0].cc, flags, ord, nullptr, epoch, cstreams, rank)) return rc;
+    return produce(plans[1].cc, rs_flags, ord2, nullptr, epoch, cstreams, rank);
+  });
 }

@@ -27,7 +27,22 @@ constexpr int kScrLocal = kScrSplit + 1024;  // RS: local tiles stored, per row 
 constexpr int kScrWords = kScrLocal + AGG_MAX_ROW_TILES;
 constexpr int kMaxLists = 16;
 
-enum Epilogue { kEpiAllGather = 0, kEpiReduceScatter = 1, kEpiAllReduce = 2 };
+enum Epilogue { kEpiAllGather = 0, kEpiReduceScatter = 1, kEpiAllReduce = 2, kEpiFfn = 3 };
+
+// One set of copy jobs of the in-kernel producer: job i*pieces + q of the set moves piece q of the
+// i-th arriving chunk from its peer's block into the symmetric buffer; the job completing a chunk
+// releases its flag.
+struct CopySet {
+  const uint8_t* peer[AGG_MAX_WORLD];   // per-peer source blocks (emulated peers)
+  uint8_t* sym;                         // symmetric buffer (gather / receive)
+  uint32_t* put_flags;                  // flags the producer releases
+  int64_t chunk_bytes, piece_bytes;
+  uint32_t jobs;                        // chunks x pieces of this set
+  int pieces;                           // pieces per chunk
+  int cps;                              // chunks per peer block
+  int order_off;                        // its arrival order: scratch[kScrOrder + order_off + i]
+  int piece_off;                        // its piece counters: scratch[kScrPieces + piece_off + chunk]
+};
 
 struct GemmArgs {
   const uint8_t* a;         // AG: gather buffer M x K; RS: A, M x K
@@ -59,17 +74,11 @@ struct GemmArgs {
   uint64_t timeout_ticks;   // in wall-clock (s_memrealtime) ticks
   uint32_t trace_tiles;     // capacity of `trace` in tiles (0 = off)
   // (the row tiles in compute order are in scratch, kScrRowOrder)
-  // in-kernel producer: copy job i*pieces + q moves piece q of the i-th arriving chunk from its
-  // peer's block to the symmetric buffer; the job completing a chunk releases its flag
-  const uint8_t* peer[AGG_MAX_WORLD];   // per-peer source blocks (emulated peers)
-  uint8_t* sym;                         // symmetric buffer (AG gather / RS receive)
-  uint32_t* put_flags;                  // flags the producer releases
-  int64_t chunk_bytes, piece_bytes;
-  uint32_t copy_jobs;                   // 0: no copies in this launch
-  int pieces;                           // pieces per chunk
+  // in-kernel producer: the jobs of set 0, then those of set 1 (the FFN chain's receive chunks)
+  CopySet cs[2];
+  uint32_t copy_jobs;                   // 0: no copies in this launch; else cs[0].jobs + cs[1].jobs
   int copy_wgs;                         // workgroups that take copy jobs first (<= grid)
-  int copy_cps;                         // chunks per peer block
-  int copy_delays;                      // nonzero: honour the cumulative delays in scratch
+  int copy_delays;                      // nonzero: honour set 0's cumulative delays in scratch
   // AG pull: tiles read remote rows straight from the peers' blocks (no chunk wait); the copy
   // jobs (which still fill the gather buffer and release the flags) go to the last copy_wgs
   // workgroups, which claim tiles only after copying
@@ -77,8 +86,20 @@ struct GemmArgs {
   // flags this launch sets to the epoch at its start (workgroup 0): the local shard's chunks
   // (present from the call's start; a launch that carries the copy jobs marks them) and, for
   // ReduceScatter tile launches, the local block's send flags (nothing is sent for that block)
-  uint32_t* mark_flags[2];
-  int mark_count[2];
+  uint32_t* mark_flags[3];
+  int mark_count[3];
+  // FFN chain (kEpiFfn): the fields above describe phase 2, a GEMM+ReduceScatter whose A is h
+  // (K = the first layer's N); phase 1, AllGather+GEMM tiles whose epilogue writes
+  // silu(product) into h as bf16, uses these. Tasks: phase 1's tiles (row tiles in scratch
+  // kScrRowOrder[0 .. n_row_tiles1)) then phase 2's (kScrRowOrder[n_row_tiles1 ..]), claimed in
+  // that order from one counter.
+  const uint8_t* a1;                    // gather buffer M x K1
+  const uint8_t* b1;                    // K1 x N1
+  uint16_t* h;                          // M x N1 bfloat16
+  const uint32_t* flags1;               // gather flags
+  int64_t K1, N1;
+  int chunk_rows1, cps1;
+  int n_row_tiles1, n_col_tiles1;
 };
 
 // Launch the persistent kernel instantiated for (bm, bn, dtype, epilogue) with `grid`

@@ -261,7 +261,6 @@ __device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job, in
   // loop out so that the lanes of one wave run different iterations, which misaligns the
   // barriers between the waves
   const uint32_t jobs = __builtin_amdgcn_readfirstlane(a.copy_jobs);
-  const uint32_t pieces = __builtin_amdgcn_readfirstlane((uint32_t)a.pieces);
   // the next job comes from a shared counter; once it is past the last job a plain load says so
   // (one uncontended read per workgroup at the end of the copy instead of an atomic add)
   // (static_rank >= 0: this is copier static_rank of a.copy_wgs, which takes jobs static_rank,
@@ -290,29 +289,35 @@ __device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job, in
     const uint32_t prev = atomicCAS(a.scratch + kScrCopyT0, 0u, now);
     t0 = prev ? prev : now;
   }
+  const uint32_t jobs0 = __builtin_amdgcn_readfirstlane(a.cs[0].jobs);
   for (uint32_t job = next_job(); job < jobs; job = next_job()) {
-    const uint32_t j = job / pieces, q = job - j * pieces;
-    const int c = (int)__builtin_amdgcn_readfirstlane(order[j]);
-    const int p = c / a.copy_cps, jl = c - p * a.copy_cps;
-    if (a.copy_delays && tid == 0) {
+    // the set this job belongs to (uniform): set 0's jobs come first
+    const int set = job < jobs0 ? 0 : 1;
+    const CopySet& cs = a.cs[set];
+    const uint32_t pieces = __builtin_amdgcn_readfirstlane((uint32_t)cs.pieces);
+    const uint32_t jj = job - (set ? jobs0 : 0u);
+    const uint32_t j = jj / pieces, q = jj - j * pieces;
+    const int c = (int)__builtin_amdgcn_readfirstlane(order[cs.order_off + j]);
+    const int p = c / cs.cps, jl = c - p * cs.cps;
+    if (set == 0 && a.copy_delays && tid == 0) {
       const uint32_t due = a.scratch[kScrDelay + j];
       while (wall_ticks() - t0 < due) __builtin_amdgcn_s_sleep(2);
     }
     __syncthreads();
-    const int64_t lo = (int64_t)q * a.piece_bytes;
-    const int64_t hi = lo + a.piece_bytes < a.chunk_bytes ? lo + a.piece_bytes : a.chunk_bytes;
-    const int64_t base = (int64_t)jl * a.chunk_bytes;
-    copy_piece<NT>(a.sym + ((int64_t)p * a.copy_cps) * a.chunk_bytes + base + lo,
-               a.peer[p] + base + lo, hi - lo, tid);
+    const int64_t lo = (int64_t)q * cs.piece_bytes;
+    const int64_t hi = lo + cs.piece_bytes < cs.chunk_bytes ? lo + cs.piece_bytes : cs.chunk_bytes;
+    const int64_t base = (int64_t)jl * cs.chunk_bytes;
+    copy_piece<NT>(cs.sym + ((int64_t)p * cs.cps) * cs.chunk_bytes + base + lo,
+               cs.peer[p] + base + lo, hi - lo, tid);
     // every thread's write-through stores have completed in memory (copy_piece waited for
     // them), so the count and the flag need no cache maintenance: a relaxed count per piece,
     // and the piece that completes the chunk writes its flag (a system-coherent store)
     __syncthreads();
     if (tid == 0) {
-      const uint32_t prev = __hip_atomic_fetch_add(a.scratch + kScrPieces + c, 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t prev = __hip_atomic_fetch_add(a.scratch + kScrPieces + cs.piece_off + c, 1u,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (prev + 1 == pieces)
-        __hip_atomic_store(a.put_flags + c, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(cs.put_flags + c, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
 }
@@ -411,11 +416,44 @@ __device__ inline bool claim(const GemmArgs& a, int home, int nstat, Tile& t) {
   }
 }
 
-// Rows of a row tile: [lo, hi) in the A operand, and (RS) the block it belongs to.
-template <int BM, int EPI>
-__device__ inline void tile_rows(const GemmArgs& a, int row_tile, int64_t& lo, int64_t& hi,
+// FFN chain: task k of the launch is phase 1's tile k (k < tasks1: row tile k / N1-tiles of phase
+// 1's order, column k % N1-tiles) or phase 2's tile k - tasks1. Workgroup b takes task b first
+// (no atomic); later tasks come from one counter in increasing order, so a task is claimed only
+// after every task before it, and the phase-1 tiles a phase-2 tile waits for are held by running
+// workgroups that wait for nothing but chunk flags. Run by one wave; uniform result.
+__device__ inline bool claim_chain(const GemmArgs& a, bool first, Tile& t) {
+  const uint32_t t1 = (uint32_t)a.n_row_tiles1 * (uint32_t)a.n_col_tiles1;
+  const uint32_t total = t1 + (uint32_t)a.n_row_tiles * (uint32_t)a.n_col_tiles;
+  uint32_t k = blockIdx.x;
+  if (!first) {
+    uint32_t* ctr = a.scratch + kScrLists;
+    k = total;
+    if ((threadIdx.x & 63) == 0 &&
+        __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + gridDim.x < total)
+      k = atomicAdd(ctr, 1u) + gridDim.x;
+    k = (uint32_t)__shfl((int)k, 0);
+  }
+  if (k >= total) return false;
+  if (k < t1) {
+    t.row_tile = (int)a.scratch[kScrRowOrder + k / (uint32_t)a.n_col_tiles1];
+    t.col_tile = (int)(k % (uint32_t)a.n_col_tiles1);
+    t.list = 1;
+  } else {
+    const uint32_t k2 = k - t1;
+    t.row_tile = (int)a.scratch[kScrRowOrder + a.n_row_tiles1 + k2 / (uint32_t)a.n_col_tiles];
+    t.col_tile = (int)(k2 % (uint32_t)a.n_col_tiles);
+    t.list = 2;
+  }
+  t.pos = (int)k;
+  return true;
+}
+
+// Rows of a row tile: [lo, hi) in the A operand, and (RS) the block it belongs to. ReduceScatter
+// row tiles (rs) are numbered block * tpb + tile within the block; others count from row 0.
+template <int BM>
+__device__ inline void tile_rows(const GemmArgs& a, int row_tile, bool rs, int64_t& lo, int64_t& hi,
                                  int& block, int& tile_in_block) {
-  if (EPI != kEpiReduceScatter) {
+  if (!rs) {
     lo = (int64_t)row_tile * BM;
     hi = lo + BM < a.M ? lo + BM : a.M;
     block = 0;
@@ -430,48 +468,39 @@ __device__ inline void tile_rows(const GemmArgs& a, int row_tile, int64_t& lo, i
   }
 }
 
-// Wave 0 waits until every flag the tile needs holds >= epoch. Returns false if the wait gave
-// up (its own limit, or another workgroup's). Reports the smallest flag value seen: on success
-// over all the tile's flags, on giving up the last value read of a flag still short of epoch.
-template <int EPI>
-__device__ bool wait_chunks(const GemmArgs& a, int64_t lo, int64_t hi, int block, uint32_t& min_seen) {
+// Wave 0 waits until every flag the tile needs holds >= epoch: rows [lo, hi) of a buffer cut
+// into chunks of `cr` rows, `cps` chunks per peer, flag p*cps + q for chunk q of peer p. ALL_PEERS
+// false: the rows are gathered rows whose own chunks are needed (the local shard's need no wait);
+// true: the rows are rows of every peer's block (the chunks of every peer but this rank). Returns
+// false if the wait gave up (its own limit, or another workgroup's). Reports the smallest flag value
+// seen: on success over all the tile's flags, on giving up the last value read of a flag still
+// short of epoch.
+template <bool ALL_PEERS>
+__device__ bool wait_flags(const GemmArgs& a, const uint32_t* flags, int cr, int cps, int64_t lo,
+                           int64_t hi, uint32_t& min_seen) {
   const int lane = threadIdx.x & 63;
-  int count, q_lo, nq;
-  if (EPI == kEpiAllGather) {
-    q_lo = (int)(lo / a.chunk_rows);
-    nq = (int)((hi - 1) / a.chunk_rows) - q_lo + 1;
-    count = nq;
-  } else if (EPI == kEpiAllReduce) {
-    // every peer's chunks of these rows (chunk q of peer p is flag p*cps + q)
-    q_lo = (int)(lo / a.chunk_rows);
-    nq = (int)((hi - 1) / a.chunk_rows) - q_lo + 1;
-    count = (a.world - 1) * nq;
-  } else {
-    if (block != a.rank) return true;
-    const int64_t base = (int64_t)block * a.m_block;
-    q_lo = (int)((lo - base) / a.chunk_rows);
-    nq = (int)((hi - 1 - base) / a.chunk_rows) - q_lo + 1;
-    count = (a.world - 1) * nq;
-  }
+  const int q_lo = (int)(lo / cr);
+  const int nq = (int)((hi - 1) / cr) - q_lo + 1;
+  const int count = ALL_PEERS ? (a.world - 1) * nq : nq;
   uint32_t seen = 0xFFFFFFFFu;
   for (int base_i = 0; base_i < count; base_i += 64) {
     const int i = base_i + lane;
     int f = -1;
     if (i < count) {
-      if (EPI == kEpiAllGather) {
+      if (!ALL_PEERS) {
         const int c = q_lo + i;
-        if (c / a.cps != a.rank) f = c;
+        if (c / cps != a.rank) f = c;
       } else {
         int p = i / nq;
         if (p >= a.rank) ++p;
-        f = p * a.cps + q_lo + (i % nq);
+        f = p * cps + q_lo + (i % nq);
       }
     }
     const uint32_t t0 = wall_ticks();
     uint32_t polls = 0;
     for (;;) {
       uint32_t v = 0xFFFFFFFFu;
-      if (f >= 0) v = load_flag(a.flags + f);
+      if (f >= 0) v = load_flag(flags + f);
       const bool ok = v >= a.epoch;
       if (__all(ok)) {
         seen = v < seen ? v : seen;
@@ -504,6 +533,18 @@ __device__ bool wait_chunks(const GemmArgs& a, int64_t lo, int64_t hi, int block
   }
   min_seen = seen;
   return true;
+}
+
+// The chunk waits of the three operations' tiles (rows [lo, hi) of the output; `block` is the
+// ReduceScatter block): AllGather+GEMM waits for its gathered rows, the ReduceScatter local block
+// and the AllReduce tiles for every peer's chunks of their rows.
+template <int EPI>
+__device__ bool wait_chunks(const GemmArgs& a, int64_t lo, int64_t hi, int block, uint32_t& min_seen) {
+  if (EPI == kEpiAllGather) return wait_flags<false>(a, a.flags, a.chunk_rows, a.cps, lo, hi, min_seen);
+  if (EPI == kEpiAllReduce) return wait_flags<true>(a, a.flags, a.chunk_rows, a.cps, lo, hi, min_seen);
+  if (block != a.rank) return true;
+  const int64_t base = (int64_t)block * a.m_block;
+  return wait_flags<true>(a, a.flags, a.chunk_rows, a.cps, lo - base, hi - base, min_seen);
 }
 
 // Wave-uniform bounded wait until *ctr >= expect: relaxed agent-scope polls with s_sleep, giving
@@ -703,7 +744,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   const int wm = wave / WNW, wn = wave % WNW;
   if (blockIdx.x == 0) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < 3; ++f)
       for (int i = tid; i < a.mark_count[f]; i += NT)
         __hip_atomic_store(a.mark_flags[f] + i, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
@@ -711,14 +752,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   // workgroups of one list share an XCD (they are dealt to the XCDs round robin), so its
   // tiles' operand rows stay in that XCD's L2.
   const int home = (int)blockIdx.x % a.n_lists;
-  const int64_t kbytes = a.K * (FP8 ? 1 : 2);
 
   // workgroups whose first tile is taken statically (pull: all but the copiers at the end)
   const int nstat = (EPI == kEpiAllGather && a.pull) ? (int)gridDim.x - a.copy_wgs : (int)gridDim.x;
   auto claim_tile = [&](bool first) {
     if (wave == 0) {
       Tile t{};
-      const bool got = (first && (int)blockIdx.x < nstat && claim_static(a, t)) || claim(a, home, nstat, t);
+      bool got;
+      if constexpr (EPI == kEpiFfn) got = claim_chain(a, first, t);
+      else got = (first && (int)blockIdx.x < nstat && claim_static(a, t)) || claim(a, home, nstat, t);
       if (lane == 0) {
         s_tile[0] = got ? t.row_tile : -1;
         s_tile[1] = t.col_tile; s_tile[2] = t.list; s_tile[3] = t.pos;
@@ -742,756 +784,804 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   if (copier) produce_chunks<NT>(a, tid, &s_job, pull ? (int)blockIdx.x - first_copier : -1);
   if (pull && copier) claim_tile(false);
 
-  for (;; claim_tile(false)) {   // (an abandoned tile's `continue` claims the next one too)
+  for (;; claim_tile(false)) {   // (an abandoned tile returns early; the next claim follows)
     // uniform for the compiler too (see produce_chunks)
     const int row_tile = __builtin_amdgcn_readfirstlane(s_tile[0]);
     if (row_tile < 0) break;
-    const int vcol = __builtin_amdgcn_readfirstlane(s_tile[1]);
-    const int col_tile = vcol / a.ksplit, part = vcol - col_tile * a.ksplit;
-    int64_t lo, hi;
-    int block, tib;
-    tile_rows<BM, EPI>(a, row_tile, lo, hi, block, tib);
-    const int64_t n0 = (int64_t)col_tile * BN;
-    // this part's K slices [t_lo, t_hi) and the K byte where its loads stop (zeros past it)
-    constexpr int kSlice = kSliceBytes;
-    const int nk_all = (int)((kbytes + kSlice - 1) / kSlice);
-    const int t_lo = part * a.kps;
-    const int t_hi = t_lo + a.kps < nk_all ? t_lo + a.kps : nk_all;
-    const uint32_t kend = (uint32_t)((int64_t)t_hi * kSlice < kbytes ? (int64_t)t_hi * kSlice : kbytes);
-    uint32_t* trec = nullptr;
-    if (a.trace && (uint32_t)(row_tile * a.n_col_tiles + vcol) < a.trace_tiles)
-      trec = a.trace + 8 * ((int64_t)row_tile * a.n_col_tiles + vcol);
-    if (tid == 0 && trec) {
-      trec[0] = (uint32_t)s_tile[2]; trec[1] = (uint32_t)s_tile[3]; trec[2] = (uint32_t)xcc_id();
-      trec[5] = wall_ticks();
-    }
+    // the tile: one copy per FFN phase (compile-time), so that each keeps the registers of a
+    // single-operation kernel
+    auto tile_body = [&](auto ph1_) {
+      const int vcol = __builtin_amdgcn_readfirstlane(s_tile[1]);
+      const int col_tile = vcol / a.ksplit, part = vcol - col_tile * a.ksplit;
+      // FFN chain: phase 1 (AllGather+GEMM into h) or phase 2 (GEMM+ReduceScatter of h); the
+      // operands of this tile
+      constexpr bool ph1 = EPI == kEpiFfn && decltype(ph1_)::value;
+      const uint8_t* const opA = ph1 ? a.a1 : a.a;
+      const uint8_t* const opB = ph1 ? a.b1 : a.b;
+      const int64_t opN = ph1 ? a.N1 : a.N;
+      const int64_t kbytes = (ph1 ? a.K1 : a.K) * (FP8 ? 1 : 2);
+      int64_t lo, hi;
+      int block, tib;
+      tile_rows<BM>(a, row_tile, (EPI == kEpiReduceScatter || EPI == kEpiFfn) && !ph1, lo, hi, block, tib);
+      const int64_t n0 = (int64_t)col_tile * BN;
+      // this part's K slices [t_lo, t_hi) and the K byte where its loads stop (zeros past it)
+      constexpr int kSlice = kSliceBytes;
+      const int nk_all = (int)((kbytes + kSlice - 1) / kSlice);
+      const int t_lo = part * a.kps;
+      const int t_hi = t_lo + a.kps < nk_all ? t_lo + a.kps : nk_all;
+      const uint32_t kend = (uint32_t)((int64_t)t_hi * kSlice < kbytes ? (int64_t)t_hi * kSlice : kbytes);
+      uint32_t* trec = nullptr;
+      if (a.trace && (uint32_t)(row_tile * a.n_col_tiles + vcol) < a.trace_tiles)
+        trec = a.trace + 8 * ((int64_t)row_tile * a.n_col_tiles + vcol);
+      if (tid == 0 && trec) {
+        trec[0] = (uint32_t)s_tile[2]; trec[1] = (uint32_t)s_tile[3]; trec[2] = (uint32_t)xcc_id();
+        trec[5] = wall_ticks();
+      }
 
-    // ---- wait for the chunks this tile's rows need
-    if (wave == 0) {
-      uint32_t seen = 0xFFFFFFFFu;
-      // (ReduceScatter tiles need no chunk: the received partials are added by reduce_local;
-      // AllReduce tiles wait for theirs in the epilogue, after the main loop)
-      const bool ok = pull || EPI != kEpiAllGather || wait_chunks<EPI>(a, lo, hi, block, seen);
-      if (lane == 0) {
-        s_ok = ok;
-        if (trec) { trec[3] = seen; trec[6] = wall_ticks(); }
-      }
-    }
-    __syncthreads();
-    if (!__builtin_amdgcn_readfirstlane(s_ok)) {
-      __syncthreads();
-      continue;  // abandoned (timeout): the tile's output is left as it was
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
-
-    // ---- K loop: 64-byte K slices in LDS stages or pair regions, filled by direct-to-LDS loads
-    // (out-of-range rows and the K tail read zeros through the buffer descriptor's range check)
-    f32x4 acc[FM][FN];
-    constexpr int NI = (BM + BNP) / (16 * NW);   // load instructions per wave per stage
-    constexpr int NA = BM / (16 * NW);           // the first NA of them fetch A rows
-    static_assert(BM % (16 * NW) == 0 && BNP % (16 * NW) == 0, "whole 16-row groups per wave");
-    // pairs: NL load instructions per wave per slice pair, 8 rows x 128 bytes each, the first NAL
-    // of them fetching A rows
-    // mixed: NLA A loads per wave per pair (8 rows x 128 bytes), then NIB B loads per wave per
-    // slice (16 rows x 64 bytes)
-    constexpr int NLA = BM / (8 * NW), NIB = BNP / (16 * NW), NHB = NIB / 2;
-    constexpr int NL = kMixed ? NLA + NIB : kPairs ? 2 * NI : NI;
-    constexpr int NAL = kMixed ? NLA : kPairs ? 2 * NA : NA;
-    constexpr int EL = FP8 ? 1 : 2;
-    constexpr int kRowsB = kSliceBytes / EL;              // K rows of B per slice
-    constexpr int kChunksB = BNP * EL / 16;               // 16-byte chunks per B row
-    constexpr int NBS = BNP / (16 * NW);                  // B loads per wave per slice
-    static_assert(NL - NAL == (kPairs ? 2 : 1) * NBS, "B loads per slice");
-    static_assert(!kPairs || (kRegions - 1) * NL < 64, "loads in flight within the vmcnt range");
-    // lane's chunk: rows of a 16-row group are lane/4, chunk position lane%4 (pairs: rows of an
-    // 8-row group are lane/8, chunk position lane%8)
-    const uint32_t gk = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) << 4);
-    auto pair_row = [&](int j) { return (j * NW + wave) * 8 + (lane >> 3); };
-    auto pair_gk = [&](int r) { return (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) << 4); };
-    // B (K x N, N contiguous): a slice's B block holds kRowsB K rows of kChunksB 16-byte chunks;
-    // B load jb of a slice (NBS per wave) fills chunk positions (jb*NW + wave)*64 + lane, i.e. K row
-    // b_load_row and column chunk b_load_chunk of the slice (whole rows per instruction, 2..16 of
-    // them, so each request is a whole line for rows of 128 bytes and more). Pair tiles load two
-    // slices of B per pair: B loads jb and jb + NBS fill the same positions of consecutive slices.
-    auto b_pos = [&](int j) { return (((j - NAL) % NBS) * NW + wave) * 64 + lane; };
-    uint32_t base[NL];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      if (j < NAL) {
-        const int r = (kPairs || kMixed) ? pair_row(j) : (j * NW + wave) * 16 + (lane >> 2);  // tile row
-        const uint32_t g = (kPairs || kMixed) ? pair_gk(r) : gk;
-        const int64_t gr = lo + r;
-        base[j] = gr < a.M ? (uint32_t)gr * (uint32_t)kbytes + g : kOutOfRange;
-      } else {
-        const int q = b_pos(j);
-        const int ncol = b_load_chunk(q, kChunksB, EL) * (16 / EL);
-        const int64_t gn = n0 + ncol;
-        base[j] = (ncol < BN && gn < a.N)
-                      ? (uint32_t)b_load_row(q, kChunksB) * (uint32_t)(a.N * EL) + (uint32_t)gn * EL
-                      : kOutOfRange;
-      }
-    }
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    // A operand: one descriptor for the tile, or (pull, tiles of up to 128 rows) one per A load,
-    // whose 16-row group lies in one shard when shards are multiples of 16 rows
-    constexpr bool kGroupPull = BM <= 128;
-    u32x4 da = buffer_desc(a.a, (uint32_t)(a.M * kbytes));
-    u32x4 dag[kGroupPull ? NAL : 1];
-#pragma unroll
-    for (int j = 0; j < (kGroupPull ? NAL : 1); ++j) dag[j] = da;
-    if (pull) {
-      // remote rows are read from the peer's block: rebase those A offsets from gather-buffer
-      // rows to block rows
-      const int64_t ms = (int64_t)a.chunk_rows * a.cps;
-      if constexpr (kGroupPull) {
-#pragma unroll
-        for (int j = 0; j < NAL; ++j) {
-          const int64_t g0 = lo + (int64_t)(j * NW + wave_u) * (kPairs ? 8 : 16);  // first row of the group
-          const int p = (int)(g0 / ms);
-          if (g0 < a.M && p != a.rank) {
-            dag[j] = buffer_desc(a.peer[p], (uint32_t)(ms * kbytes));
-            if (base[j] != kOutOfRange) base[j] -= (uint32_t)((int64_t)p * ms * kbytes);
-          }
-        }
-      } else {
-        // (a tile of more than 128 rows is pulled only when it lies inside one shard)
-        const int p = (int)(lo / ms);
-        if (p != a.rank) {
-          da = buffer_desc(a.peer[p], (uint32_t)(ms * kbytes));
-          const uint32_t shift = (uint32_t)((int64_t)p * ms * kbytes);
-#pragma unroll
-          for (int j = 0; j < NAL; ++j)
-            if (base[j] != kOutOfRange) base[j] -= shift;
-        }
-      }
-    }
-    const u32x4 db = buffer_desc(a.b, (uint32_t)(a.N * kbytes));
-    const uint32_t lds0 = lds_addr(stages) + (uint32_t)wave_u * 1024u;
-    // Load j of a slice (j < NI; pairs: of a slice pair, j < NL): A rows for j < NA (NAL), else B
-    // rows. The LDS stage of slice t is (t - t_lo) % 4 (pairs: region ((t - t_lo) / 2) % R); the
-    // main loop runs four (pairs: 2R) slices per trip, so every stage and region is a constant.
-    auto desc_of = [&](int j) -> const u32x4& {
-      return j < NAL ? (kGroupPull ? dag[j < NAL ? j : 0] : da) : db;
-    };
-    auto m0_of = [&](int sg, int j) { return lds0 + (uint32_t)sg * DSTAGE + (uint32_t)j * (NW * 1024u); };
-    // pairs: LDS address of load j into pair region rg
-    auto m0p = [&](int rg, int j) { return lds0 + (uint32_t)rg * (2 * DSTAGE) + (uint32_t)j * (NW * 1024u); };
-    // K byte offset of load j of slice t. Slices below t_safe lie wholly inside the part's K
-    // range: a plain offset. Otherwise (`masked`) the offset's top bit is set past the K end
-    // (out of range: reads zero), lane by lane, since a slice may straddle the end.
-    const int t_safe = (int)(kend / kSlice);
-    // B load j of slice t: row b_load_row of the slice's K rows, which start at K row t*kRowsB
-    // (64 * N bytes per slice); masked: rows at or past the part's K end read zeros
-    const uint32_t kend_rows = kend / EL;
-    auto voff_b = [&](auto masked, int t, int j) -> uint32_t {
-      const uint32_t tb = (uint32_t)t * (uint32_t)(kSliceBytes * a.N);
-      if constexpr (decltype(masked)::value) {
-        const uint32_t row = (uint32_t)(t * kRowsB + b_load_row(b_pos(j), kChunksB));
-        return (base[j] + tb) | (row >= kend_rows ? kOutOfRange : 0u);
-      } else {
-        return base[j] + tb;
-      }
-    };
-    auto voff_of = [&](auto masked, int t, int j) -> uint32_t {
-      if (j >= NAL) return voff_b(masked, t, j);
-      const uint32_t tk = (uint32_t)t * kSliceBytes;
-      if constexpr (decltype(masked)::value) {
-        const uint32_t oob = (uint32_t)((int)(tk + gk - kend) >> 31) ^ 0xFFFFFFFFu;
-        return (base[j] + tk) | (oob & kOutOfRange);
-      } else {
-        return base[j] + tk;
-      }
-    };
-    // pairs: K byte offset of load j of slice pair pr (slices 2pr and 2pr+1), masked as above
-    auto voffp = [&](auto masked, int pr, int j) -> uint32_t {
-      if (j >= NAL) return voff_b(masked, 2 * pr + (j - NAL) / NBS, j);
-      const uint32_t pk = (uint32_t)pr * (2 * kSliceBytes);
-      if constexpr (decltype(masked)::value) {
-        const uint32_t oob = (uint32_t)((int)(pk + pair_gk(pair_row(j)) - kend) >> 31) ^ 0xFFFFFFFFu;
-        return (base[j] + pk) | (oob & kOutOfRange);
-      } else {
-        return base[j] + pk;
-      }
-    };
-    // mixed: A load j into A region rg; B load j (>= NLA) into B stage sg
-    auto m0ma = [&](int rg, int j) { return lds0 + (uint32_t)rg * AREG + (uint32_t)j * (NW * 1024u); };
-    auto m0mb = [&](int sg, int j) {
-      return lds0 + (uint32_t)(2 * AREG + sg * BSTAGE) + (uint32_t)(j - NLA) * (NW * 1024u);
-    };
-    auto issue_one = [&](auto masked, int t, int sg, int j) {
-      lds_dma_load(desc_of(j), m0_of(sg, j), voff_of(masked, t, j));
-    };
-    // The loads a slice issues, as (load index, LDS address, offset). Four stages: in the first
-    // half of slice t, loads NH.. of slice t+3 into stage (t+3)%4; in the second half, loads
-    // 0..NH-1 of slice t+4 into stage t%4. Pairs: an even slice t issues, in its first half, the
-    // second half of the loads of pair t/2+1 into the other region; an odd slice t, in its second
-    // half, the first half of the loads of pair (t+1)/2+1 into its own region (whose pair every
-    // wave has finished at the odd slice's barrier).
-    struct Ld { int j; uint32_t m0, vo; };
-    auto ld_first = [&](auto masked, auto u_, int t, int e) -> Ld {
-      constexpr int U = decltype(u_)::value;
-      if constexpr (kMixed) {
-        // even slices: the second part of A pair t/2+1, then (all slices) the second part of B
-        // slice t+3
-        constexpr int EA = (U & 1) ? 0 : NLA - NLA / 2;
-        if (e < EA) {
-          const int j = NLA / 2 + e;
-          return Ld{j, m0ma(((U >> 1) + 1) & 1, j), voffp(masked, t / 2 + 1, j)};
-        }
-        const int j = NLA + NHB + (e - EA);
-        return Ld{j, m0mb((U + 3) & 3, j), voff_of(masked, t + 3, j)};
-      } else if constexpr (kPairs) {
-        const int j = NL / 2 + e;
-        return Ld{j, m0p(((U >> 1) + kRegions - 1) % kRegions, j), voffp(masked, t / 2 + kRegions - 1, j)};
-      } else {
-        const int j = NI / 2 + e;
-        return Ld{j, m0_of((U + 3) & 3, j), voff_of(masked, t + 3, j)};
-      }
-    };
-    auto ld_second = [&](auto masked, auto u_, int t, int k) -> Ld {
-      constexpr int U = decltype(u_)::value;
-      if constexpr (kMixed) {
-        // odd slices: the first part of A pair (t+1)/2+1, then (all slices) the first part of B
-        // slice t+4
-        constexpr int KA = (U & 1) ? NLA / 2 : 0;
-        if (k < KA) return Ld{k, m0ma(U >> 1, k), voffp(masked, (t + 1) / 2 + 1, k)};
-        const int j = NLA + (k - KA);
-        return Ld{j, m0mb(U, j), voff_of(masked, t + 4, j)};
-      }
-      if constexpr (kPairs) return Ld{k, m0p(U >> 1, k), voffp(masked, (t + 1) / 2 + kRegions - 1, k)};
-      else return Ld{k, m0_of(U, k), voff_of(masked, t + 4, k)};
-    };
-    constexpr int NH = NI / 2;                 // loads of a slice issued in the earlier half
-    // The slice schedule, for both dtypes: RM x CN MFMA blocks per wave and slice, operand
-    // fragments of type F read from LDS by lda(stage, block row) / ldb(stage, block column).
-    // One K slice t in stage U, its B fragments in fbc and its first A fragment in fa (requested
-    // during the previous slice). Stage U is refilled with slice t+4 by NI direct-to-LDS loads,
-    // the first NH of them in the second half of slice t and the rest in the first half of slice
-    // t+1, so that every half slice carries about NI/2 loads between its MFMAs and the load path
-    // never takes a burst. First half of slice t: the remaining A fragments of slice t are
-    // requested row by row, and the loads NH..NI-1 of slice t+3 go between the MFMAs. Then the
-    // waves meet (slice t+1 has landed everywhere; every wave has read all of slice t), and the
-    // second half spreads slice t+1's B fragments and first A fragment, then the loads 0..NH-1
-    // of slice t+4, between its MFMAs. (Pairs: the same two halves carry the pair loads that
-    // ld_first / ld_second describe.) A load that follows an MFMA shares its asm statement
-    // (mma_dma), so the MFMA is the wait state between the M0 write and the load.
-    auto run_slices = [&](auto& accs, auto fa, auto lda, auto ldb, auto mma, auto mma_dma,
-                          auto rm_, auto cn_, auto lone_) {
-      constexpr int RM = decltype(rm_)::value, CN = decltype(cn_)::value;
-      constexpr bool kLone = decltype(lone_)::value;
-      using F = decltype(fa);
-      constexpr int RB = RM / 2;                 // block rows before the barrier
-      constexpr int S1 = RB * CN, S2 = (RM - RB) * CN;
-      static_assert(RM - RB - 1 <= RB, "the A fragments after the barrier are loaded before it");
-      auto slice = [&](auto u_, auto masked, F (&fbc)[CN], F (&fbn)[CN], int t) {
-        constexpr int U = decltype(u_)::value;
-        constexpr int U1 = (U + 1) % (kPairs ? 2 * kRegions : 4);
-        // loads issued in the first half (E1) and in the second half (ND) of this slice
-        constexpr int E1 = kMixed ? ((U & 1) ? 0 : NLA - NLA / 2) + (NIB - NHB)
-                           : kPairs ? ((U & 1) ? 0 : NL / 2) : NI - NH;
-        constexpr int ND = kMixed ? ((U & 1) ? NLA / 2 : 0) + NHB : kPairs ? ((U & 1) ? NL / 2 : 0) : NH;
-        constexpr int E2 = CN + 1 + ND;
-        F far[RM];
-        far[0] = fa;
-        if (S1 == 0) {                            // no MFMA before the barrier: issue plainly
-#pragma unroll
-          for (int e = 0; e < E1; ++e) {
-            const Ld l = ld_first(masked, u_, t, e);
-            lds_dma_load(desc_of(l.j), l.m0, l.vo);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          far[i + 1] = lda(U, i + 1);
-          if (RB + 1 + i < RM) far[RB + 1 + i] = lda(U, RB + 1 + i);
-#pragma unroll
-          for (int j = 0; j < CN; ++j) {
-            const int q = i * CN + j;
-            bool fused = false;
-#pragma unroll
-            for (int e = 0; e < E1; ++e) {
-              if (S1 == 0 || e * S1 / (E1 > 0 ? E1 : 1) != q) continue;
-              const Ld l = ld_first(masked, u_, t, e);
-              if (!fused) {
-                mma_dma(accs[i][j], fbc[j], far[i], desc_of(l.j), l.m0, l.vo);
-                fused = true;
-              } else {
-                lds_dma_load(desc_of(l.j), l.m0, l.vo);
-              }
-            }
-            if (!fused) mma(accs[i][j], fbc[j], far[i]);
-          }
-        }
-        // slice t+1 has landed (four stages: all but the 2*NI loads issued since; pairs, odd t:
-        // all of pair (t+1)/2, the last loads issued; even t: all but the NL of pair t/2+1)
-        stage_barrier<kMixed ? mixed_barrier_count(U, NLA, NIB, NHB)
-                      : kPairs ? pair_barrier_count(U, kRegions, NL) : stage_barrier_count(NI)>();
-#pragma unroll
-        for (int i = RB; i < RM; ++i) {
-#pragma unroll
-          for (int j = 0; j < CN; ++j) {
-            const int q = (i - RB) * CN + j;
-            if (kLone) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-            // the first second-half load scheduled after this MFMA is fused with it
-            int fuse_e = -1;
-#pragma unroll
-            for (int e = CN + 1; e < E2; ++e)
-              if (fuse_e < 0 && e * S2 / E2 == q) fuse_e = e;
-            if (fuse_e >= 0) {
-              const Ld l = ld_second(masked, u_, t, fuse_e - CN - 1);
-              mma_dma(accs[i][j], fbc[j], far[i], desc_of(l.j), l.m0, l.vo);
-            } else {
-              mma(accs[i][j], fbc[j], far[i]);
-            }
-#pragma unroll
-            for (int e = 0; e < E2; ++e) {
-              if (e * S2 / E2 != q || e == fuse_e) continue;   // request e goes after MFMA slot e*S2/E2
-              if (e < CN) fbn[e] = ldb(U1, e);
-              else if (e == CN) fa = lda(U1, 0);
-              else {
-                const Ld l = ld_second(masked, u_, t, e - CN - 1);
-                lds_dma_load(desc_of(l.j), l.m0, l.vo);
-              }
-            }
-          }
-        }
-      };
-      if (t_hi > t_lo) {
-        F fb0[CN], fb1[CN];
-        acc_settle(accs);
-        constexpr auto kPlain = std::integral_constant<bool, false>{};
-        constexpr auto kMasked = std::integral_constant<bool, true>{};
-        if constexpr (kMixed) {
-          // A pair 0 whole and the first part of A pair 1; B slices 0..2 whole and the first part
-          // of B slice 3 (the first slices issue the rest)
-#pragma unroll
-          for (int j = 0; j < NLA; ++j) lds_dma_load(desc_of(j), m0ma(0, j), voffp(kMasked, t_lo / 2, j));
-#pragma unroll
-          for (int j = 0; j < NLA / 2; ++j) lds_dma_load(desc_of(j), m0ma(1, j), voffp(kMasked, t_lo / 2 + 1, j));
-#pragma unroll
-          for (int q = 0; q < 3; ++q)
-#pragma unroll
-            for (int j = NLA; j < NLA + NIB; ++j) lds_dma_load(desc_of(j), m0mb(q, j), voff_of(kMasked, t_lo + q, j));
-#pragma unroll
-          for (int j = NLA; j < NLA + NHB; ++j) lds_dma_load(desc_of(j), m0mb(3, j), voff_of(kMasked, t_lo + 3, j));
-          stage_barrier<mixed_prologue_count(NLA, NIB, NHB)>();
-        } else if constexpr (kPairs) {
-          // pairs 0 .. R-2 whole and the first half of pair R-1 (the first slice issues the rest)
-#pragma unroll
-          for (int q = 0; q + 1 < kRegions; ++q)
-#pragma unroll
-            for (int j = 0; j < NL; ++j) lds_dma_load(desc_of(j), m0p(q, j), voffp(kMasked, t_lo / 2 + q, j));
-#pragma unroll
-          for (int j = 0; j < NL / 2; ++j)
-            lds_dma_load(desc_of(j), m0p(kRegions - 1, j), voffp(kMasked, t_lo / 2 + kRegions - 1, j));
-          stage_barrier<pair_prologue_count(kRegions, NL)>();
-        } else {
-#pragma unroll
-          for (int s = 0; s < 3; ++s)
-#pragma unroll
-            for (int j = 0; j < NI; ++j) issue_one(kMasked, t_lo + s, s, j);
-#pragma unroll
-          for (int j = 0; j < NH; ++j) issue_one(kMasked, t_lo + 3, 3, j);   // the first slice issues the rest
-          stage_barrier<stage_prologue_count(NI)>();
-        }
-#pragma unroll
-        for (int j = 0; j < CN; ++j) fb0[j] = ldb(0, j);
-        fa = lda(0, 0);
-        // four slices per trip (slices past the part's end read zeros); a trip whose loads
-        // (up to slice t+7) stay below t_safe needs no K-end masks
-        // (pairs: 2R slices per trip, whose loads reach slice t + 4R - 1)
-        constexpr int TRIP = kPairs ? 2 * kRegions : 4;
-        auto trip = [&](auto masked, int t) {
-          slice(std::integral_constant<int, 0>{}, masked, fb0, fb1, t);
-          slice(std::integral_constant<int, 1>{}, masked, fb1, fb0, t + 1);
-          slice(std::integral_constant<int, 2>{}, masked, fb0, fb1, t + 2);
-          slice(std::integral_constant<int, 3>{}, masked, fb1, fb0, t + 3);
-          if constexpr (TRIP == 8) {
-            slice(std::integral_constant<int, 4>{}, masked, fb0, fb1, t + 4);
-            slice(std::integral_constant<int, 5>{}, masked, fb1, fb0, t + 5);
-            slice(std::integral_constant<int, 6>{}, masked, fb0, fb1, t + 6);
-            slice(std::integral_constant<int, 7>{}, masked, fb1, fb0, t + 7);
-          }
-        };
-        int t = t_lo;
-        for (; t + (kPairs ? 4 * kRegions : 8) - 1 < t_safe; t += TRIP) trip(kPlain, t);
-        for (; t < t_hi; t += TRIP) trip(kMasked, t);
-        acc_settle(accs);
-        // loads issued past the end land (as zeros) and every wave is done with LDS before the
-        // next tile refills it
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      }
-    };
-    // LDS byte offset of 16-byte chunk g (0..3) of A row `row` of slice stage sg
-    auto frag_off = [&](int sg, int row, int g) -> uint32_t {
-      if constexpr (kMixed) {
-        // A rows: pair region (sg/2) % 2, half sg % 2
-        return (uint32_t)(((sg >> 1) & 1) * AREG) + lds128_off(row, (sg & 1) * 4 + g);
-      } else if constexpr (kPairs) {
-        return (uint32_t)((sg >> 1) * (2 * DSTAGE)) + lds128_off(row, (sg & 1) * 4 + g);
-      } else {
-        return (uint32_t)(sg * DSTAGE) + lds64_off(row, g);
-      }
-    };
-    // LDS byte offset of the B block of slice stage sg (after the A rows of its stage or pair
-    // region; mixed: the B stages after the two A regions)
-    auto bblk = [&](int sg) -> uint32_t {
-      if constexpr (kMixed) return (uint32_t)(2 * AREG + sg * BSTAGE);
-      else if constexpr (kPairs)
-        return (uint32_t)((sg >> 1) * (2 * DSTAGE) + BM * 2 * kSliceBytes + (sg & 1) * (BNP * kSliceBytes));
-      else return (uint32_t)(sg * DSTAGE + BM * kSliceBytes);
-    };
-    // this lane's transposing B reads: byte offset of read 0 inside a B block for the fragment
-    // whose first chunk is 0, and its rows' swizzle (read r adds r times 4 rows (bf16) or 8 rows
-    // (fp8); the fragment's first chunk c0 (even) enters as (c0 ^ swizzle))
-    const uint32_t boff0 = (uint32_t)b_read_base(lane, kChunksB, EL);
-    const uint32_t bswz = (uint32_t)b_read_swizzle(lane, kChunksB, EL);
-    constexpr uint32_t kReadRowStep = (uint32_t)b_read_step(kChunksB, EL);
-    if constexpr (!FP8) {
-      // ---- bf16: 16x16x32 MFMA blocks, one 16-byte fragment per lane
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // B fragment: 16 columns starting at chunk c0, K rows 8*(lane/16) .. +7 from two
-      // transposing reads (rows +0..3 and +4..7)
-      auto ldb = [&](int sg, int j) {
-        const uint32_t c0 = (uint32_t)((wn * WTN + j * 16) >> 3);
-        const uint32_t off = bblk(sg) + boff0 + 16u * (c0 ^ bswz);
-        const u32x2 r0 = lds_read_tr16(stages, off);
-        const u32x2 r1 = lds_read_tr16(stages, off + kReadRowStep);
-        return u32x4{r0[0], r0[1], r1[0], r1[1]};
-      };
-      auto lda = [&](int sg, int i) {
-        return *reinterpret_cast<const u32x4*>(stages + frag_off(sg, wm * WTM + i * 16 + (lane & 15), lane >> 4));
-      };
-      run_slices(acc, u32x4{}, lda, ldb,
-                 [](f32x4& c, const u32x4& b, const u32x4& x) { mfma_bf16(c, b, x); },
-                 [](f32x4& c, const u32x4& b, const u32x4& x, const u32x4& d, uint32_t m0v, uint32_t vo) {
-                   mfma_bf16_dma(c, b, x, d, m0v, vo);
-                 },
-                 std::integral_constant<int, FM>{}, std::integral_constant<int, FN>{},
-                 std::integral_constant<bool, false>{});
-    } else {
-      // ---- fp8 (e4m3): 32x32x64 MFMA blocks with unit block scales, one 32-byte fragment per
-      // lane; the per-tensor scales are applied in the epilogue
-      f32x16 acc8[F8M][F8N];
-#pragma unroll
-      for (int i = 0; i < F8M; ++i)
-#pragma unroll
-        for (int j = 0; j < F8N; ++j) acc8[i][j] = f32x16{};
-      // a 32-row fp8 A fragment: row r + (lane & 31), K bytes 32*(lane/32) .. +31 of the slice
-      auto lda = [&](int sg, int i) {
-        const int row = wm * WTM + i * 32 + (lane & 31), g = (lane >> 5) * 2;
-        const u32x4 lo4 = *reinterpret_cast<const u32x4*>(stages + frag_off(sg, row, g));
-        const u32x4 hi4 = *reinterpret_cast<const u32x4*>(stages + frag_off(sg, row, g + 1));
-        return i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
-                     (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
-      };
-      // B fragment: 32 columns starting at chunk c0, K rows 32*(lane/32) .. +31 from four
-      // transposing reads of 8 rows each
-      auto ldb = [&](int sg, int j) {
-        const uint32_t c0 = (uint32_t)((wn * WTN + j * 32) >> 4);
-        const uint32_t off = bblk(sg) + boff0 + 16u * (c0 ^ bswz);
-        const u32x2 r0 = lds_read_tr8(stages, off);
-        const u32x2 r1 = lds_read_tr8(stages, off + kReadRowStep);
-        const u32x2 r2 = lds_read_tr8(stages, off + 2 * kReadRowStep);
-        const u32x2 r3 = lds_read_tr8(stages, off + 3 * kReadRowStep);
-        return i32x8{(int)r0[0], (int)r0[1], (int)r1[0], (int)r1[1],
-                     (int)r2[0], (int)r2[1], (int)r3[0], (int)r3[1]};
-      };
-      // a wave with a single 32x32 block reuses its accumulator in the next slice's first
-      // MFMA: give the previous one time to write it back
-      run_slices(acc8, i32x8{}, lda, ldb,
-                 [](f32x16& c, const i32x8& b, const i32x8& x) { mfma_fp8(c, b, x); },
-                 [](f32x16& c, const i32x8& b, const i32x8& x, const u32x4& d, uint32_t m0v, uint32_t vo) {
-                   mfma_fp8_dma(c, b, x, d, m0v, vo);
-                 },
-                 std::integral_constant<int, F8M>{}, std::integral_constant<int, F8N>{},
-                 std::integral_constant<bool, (F8M * F8N < 3)>{});
-      // the epilogue's view: quad q of block (i, j) is acc[i][4j + q]
-#pragma unroll
-      for (int i = 0; i < F8M; ++i)
-#pragma unroll
-        for (int j = 0; j < F8N; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            acc[i][4 * j + q] = f32x4{acc8[i][j][4 * q], acc8[i][j][4 * q + 1], acc8[i][j][4 * q + 2],
-                                      acc8[i][j][4 * q + 3]};
-    }
-
-    // ---- epilogue
-    // quad (i, j) of this lane: row qrow(i), columns qcol(j) .. qcol(j)+3 of the tile
-    auto qrow = [&](int i) {
-      return FP8 ? wm * WTM + i * 32 + (lane & 31) : wm * WTM + i * 16 + (lane & 15);
-    };
-    auto qcol = [&](int j) {
-      return FP8 ? wn * WTN + (j >> 2) * 32 + (j & 3) * 8 + (lane >> 5) * 4
-                 : wn * WTN + j * 16 + (lane >> 4) * 4;
-    };
-    if (EPI == kEpiAllGather) {
-      bool finish = true;
-      // split-K exists for tiles up to 128 x 128 only (the host never splits a larger one): the
-      // partial and reduction code would cost the big tiles registers in their main loop
-      if (kSplitTiles && a.ksplit > 1) {
-        // split-K: every part writes its fp32 partial (write-through) and counts itself in; the
-        // parts are summed in part order (so the sum does not depend on which part is last),
-        // by all parts together or by the part that arrives last, then converted and stored.
-        // The partial loads are system-coherent: a stale line of an earlier launch must not be
-        // read.
-        const int64_t plane = a.M * a.N;
-        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-            a.ws, 0, (int)(a.ksplit * plane * 4), kBufferFlags);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int64_t m = lo + qrow(i);
-          if (m >= hi) continue;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + qcol(j);
-            if (n >= a.N) continue;
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rw,
-                                                   (int)(((int64_t)part * plane + m * a.N + n) * 4),
-                                                   0, kStoreSystemCoherent);
-          }
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        const int tile_id = row_tile * (a.n_col_tiles / a.ksplit) + col_tile;
-        uint32_t* split_ctr = a.scratch + kScrSplit + tile_id;
-        if (a.split_together) {
-          // every part has its own workgroup in this launch: once all parts have stored, each
-          // sums a row range of the tile; the counter counts every part in twice (stored, then
-          // summed) and the last arrival resets it
-          const uint32_t ks = (uint32_t)a.ksplit;
-          if (tid == 0) __hip_atomic_fetch_add(split_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (wave == 0) {
-            const bool ok = wait_count(a, split_ctr, ks);
-            if (lane == 0) s_ok = ok;
-          }
-          __syncthreads();
-          if (__builtin_amdgcn_readfirstlane(s_ok)) sum_split_rows<BM, BN, FP8>(a, tid, lo, hi, n0, part);
-          __syncthreads();
-          if (tid == 0 && __hip_atomic_fetch_add(split_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 2 * ks - 1)
-            __hip_atomic_store(split_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          finish = false;
-        } else {
-          if (tid == 0)
-            s_ok = (__hip_atomic_fetch_add(split_ctr, 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)a.ksplit - 1);
-          __syncthreads();
-          finish = __builtin_amdgcn_readfirstlane(s_ok) != 0;
-          if (finish) {
-            // parts in order, G at a time: the loads of G parts are in flight together (one round
-            // trip per group instead of per part), then they are added one after another in part
-            // order, so the sum does not depend on the grouping
-            auto load_part = [&](f32x4 (&v)[FM][FN], int q) {
-#pragma unroll
-              for (int i = 0; i < FM; ++i) {
-                const int64_t m = lo + qrow(i);
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                  const int64_t n = n0 + qcol(j);
-                  // rows / columns past the end, and parts past the last, read zeros (offset past
-                  // the buffer)
-                  const int off = (q < a.ksplit && m < hi && n < a.N)
-                                      ? (int)(((int64_t)q * plane + m * a.N + n) * 4)
-                                      : (int)kOutOfRange;
-                  v[i][j] = __builtin_bit_cast(
-                      f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kStoreSystemCoherent));
-                }
-              }
-            };
-            constexpr int G = FM * FN >= 32 ? 1 : (32 / (FM * FN) > 8 ? 8 : 32 / (FM * FN));
-            const int ks = __builtin_amdgcn_readfirstlane(a.ksplit);
-            for (int q0 = 0; q0 < ks; q0 += G) {
-              f32x4 v[G][FM][FN];
-#pragma unroll
-              for (int g = 0; g < G; ++g) load_part(v[g], q0 + g);
-              __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-              for (int g = 0; g < G; ++g) {
-                if (q0 + g >= ks) break;
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                  for (int j = 0; j < FN; ++j) acc[i][j] = (q0 + g == 0) ? v[g][i][j] : acc[i][j] + v[g][i][j];
-              }
-            }
-            if (tid == 0) __hip_atomic_store(split_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-      }
-      if (finish) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int64_t m = lo + qrow(i);
-          if (m >= hi) continue;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + qcol(j);
-            if (n >= a.N) continue;
-            f32x4 v = acc[i][j];
-            if (FP8) v *= a.scale;
-            u32x2 packed;
-            packed[0] = bf16x2_rne(v[0], v[1]);
-            packed[1] = bf16x2_rne(v[2], v[3]);
-            *reinterpret_cast<u32x2*>(a.c + m * a.N + n) = packed;
-          }
-        }
-      }
-    } else if (EPI == kEpiAllReduce) {
-      // One-shot AllReduce, fused: this tile's partial goes to `send` (what every peer receives;
-      // write-through, so it is visible everywhere once the stores complete) and the tile that
-      // completes a chunk of `send` raises its send flag; then, once every peer's chunks of these
-      // rows have arrived, out = partial + the peers' partials in ascending rank order (a fixed
-      // order: `out` does not depend on arrival order).
-      const int64_t MN = a.M * a.N;
-      const __amdgpu_buffer_rsrc_t rsend = __builtin_amdgcn_make_buffer_rsrc(a.send, 0, (int)(MN * 4), kBufferFlags);
-      const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, (int)(MN * 4), kBufferFlags);
-      const __amdgpu_buffer_rsrc_t rrecv = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(a.recv), 0, (int)(a.world * MN * 4), kBufferFlags);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int64_t m = lo + qrow(i);
-        if (m >= hi) continue;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int64_t n = n0 + qcol(j);
-          if (n >= a.N) continue;
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rsend,
-                                                 (int)((m * a.N + n) * 4), 0, kStoreSystemCoherent);
-        }
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (tid == 0) {
-        const int q_lo = (int)(lo / a.chunk_rows), q_hi = (int)((hi - 1) / a.chunk_rows);
-        for (int q = q_lo; q <= q_hi; ++q) {
-          const int64_t clo = (int64_t)q * a.chunk_rows;
-          const int64_t chi = clo + a.chunk_rows;
-          const int t_first = (int)(clo / BM), t_last = (int)((chi - 1) / BM);
-          const uint32_t expect = (uint32_t)(t_last - t_first + 1) * (uint32_t)a.n_col_tiles;
-          const uint32_t prev = __hip_atomic_fetch_add(a.scratch + kScrRsCount + q, 1u, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-          if (prev + 1 == expect)
-            __hip_atomic_store(a.send_flags + q, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        }
-      }
+      // ---- wait for the chunks this tile's rows need
       if (wave == 0) {
         uint32_t seen = 0xFFFFFFFFu;
-        const bool ok = wait_chunks<kEpiAllReduce>(a, lo, hi, 0, seen);
+        // (ReduceScatter tiles need no chunk: the received partials are added by reduce_local;
+        // AllReduce tiles wait for theirs in the epilogue, after the main loop)
+        bool ok = true;
+        if (EPI == kEpiAllGather && !pull) {
+          ok = wait_chunks<EPI>(a, lo, hi, block, seen);
+        } else if (EPI == kEpiFfn && ph1) {
+          ok = wait_flags<false>(a, a.flags1, a.chunk_rows1, a.cps1, lo, hi, seen);
+        } else if (EPI == kEpiFfn) {
+          // phase 2: every phase-1 tile of these rows has stored its part of h
+          for (int64_t r = lo / BM; ok && r <= (hi - 1) / BM; ++r)
+            ok = wait_count(a, a.scratch + kScrSplit + (int)r, (uint32_t)a.n_col_tiles1);
+        }
         if (lane == 0) {
           s_ok = ok;
           if (trec) { trec[3] = seen; trec[6] = wall_ticks(); }
         }
       }
       __syncthreads();
-      if (__builtin_amdgcn_readfirstlane(s_ok)) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
-        const int world = __builtin_amdgcn_readfirstlane(a.world), rank = __builtin_amdgcn_readfirstlane(a.rank);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int64_t m = lo + qrow(i);
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + qcol(j);
-            if (m >= hi || n >= a.N) continue;
-            // every peer's quad in flight, then added in rank order
-            f32x4 in[AGG_MAX_WORLD - 1];
-#pragma unroll
-            for (int q = 0; q < AGG_MAX_WORLD - 1; ++q) {
-              const int p = q < rank ? q : q + 1;
-              const int off = p < world ? (int)(((int64_t)p * MN + m * a.N + n) * 4) : (int)kOutOfRange;
-              in[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrecv, off, 0, 0));
+      if (!__builtin_amdgcn_readfirstlane(s_ok)) {
+        __syncthreads();
+        return;  // abandoned (timeout): the tile's output is left as it was
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+
+      // ---- K loop: 64-byte K slices in LDS stages or pair regions, filled by direct-to-LDS loads
+      // (out-of-range rows and the K tail read zeros through the buffer descriptor's range check)
+      f32x4 acc[FM][FN];
+      constexpr int NI = (BM + BNP) / (16 * NW);   // load instructions per wave per stage
+      constexpr int NA = BM / (16 * NW);           // the first NA of them fetch A rows
+      static_assert(BM % (16 * NW) == 0 && BNP % (16 * NW) == 0, "whole 16-row groups per wave");
+      // pairs: NL load instructions per wave per slice pair, 8 rows x 128 bytes each, the first NAL
+      // of them fetching A rows
+      // mixed: NLA A loads per wave per pair (8 rows x 128 bytes), then NIB B loads per wave per
+      // slice (16 rows x 64 bytes)
+      constexpr int NLA = BM / (8 * NW), NIB = BNP / (16 * NW), NHB = NIB / 2;
+      constexpr int NL = kMixed ? NLA + NIB : kPairs ? 2 * NI : NI;
+      constexpr int NAL = kMixed ? NLA : kPairs ? 2 * NA : NA;
+      constexpr int EL = FP8 ? 1 : 2;
+      constexpr int kRowsB = kSliceBytes / EL;              // K rows of B per slice
+      constexpr int kChunksB = BNP * EL / 16;               // 16-byte chunks per B row
+      constexpr int NBS = BNP / (16 * NW);                  // B loads per wave per slice
+      static_assert(NL - NAL == (kPairs ? 2 : 1) * NBS, "B loads per slice");
+      static_assert(!kPairs || (kRegions - 1) * NL < 64, "loads in flight within the vmcnt range");
+      // lane's chunk: rows of a 16-row group are lane/4, chunk position lane%4 (pairs: rows of an
+      // 8-row group are lane/8, chunk position lane%8)
+      const uint32_t gk = (uint32_t)(((lane & 3) ^ ((lane >> 3) & 3)) << 4);
+      auto pair_row = [&](int j) { return (j * NW + wave) * 8 + (lane >> 3); };
+      auto pair_gk = [&](int r) { return (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) << 4); };
+      // B (K x N, N contiguous): a slice's B block holds kRowsB K rows of kChunksB 16-byte chunks;
+      // B load jb of a slice (NBS per wave) fills chunk positions (jb*NW + wave)*64 + lane, i.e. K row
+      // b_load_row and column chunk b_load_chunk of the slice (whole rows per instruction, 2..16 of
+      // them, so each request is a whole line for rows of 128 bytes and more). Pair tiles load two
+      // slices of B per pair: B loads jb and jb + NBS fill the same positions of consecutive slices.
+      auto b_pos = [&](int j) { return (((j - NAL) % NBS) * NW + wave) * 64 + lane; };
+      uint32_t base[NL];
+  #pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        if (j < NAL) {
+          const int r = (kPairs || kMixed) ? pair_row(j) : (j * NW + wave) * 16 + (lane >> 2);  // tile row
+          const uint32_t g = (kPairs || kMixed) ? pair_gk(r) : gk;
+          const int64_t gr = lo + r;
+          base[j] = gr < a.M ? (uint32_t)gr * (uint32_t)kbytes + g : kOutOfRange;
+        } else {
+          const int q = b_pos(j);
+          const int ncol = b_load_chunk(q, kChunksB, EL) * (16 / EL);
+          const int64_t gn = n0 + ncol;
+          base[j] = (ncol < BN && gn < opN)
+                        ? (uint32_t)b_load_row(q, kChunksB) * (uint32_t)(opN * EL) + (uint32_t)gn * EL
+                        : kOutOfRange;
+        }
+      }
+      const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+      // A operand: one descriptor for the tile, or (pull, tiles of up to 128 rows) one per A load,
+      // whose 16-row group lies in one shard when shards are multiples of 16 rows
+      constexpr bool kGroupPull = BM <= 128;
+      u32x4 da = buffer_desc(opA, (uint32_t)(a.M * kbytes));
+      u32x4 dag[kGroupPull ? NAL : 1];
+  #pragma unroll
+      for (int j = 0; j < (kGroupPull ? NAL : 1); ++j) dag[j] = da;
+      if (pull) {
+        // remote rows are read from the peer's block: rebase those A offsets from gather-buffer
+        // rows to block rows
+        const int64_t ms = (int64_t)a.chunk_rows * a.cps;
+        if constexpr (kGroupPull) {
+  #pragma unroll
+          for (int j = 0; j < NAL; ++j) {
+            const int64_t g0 = lo + (int64_t)(j * NW + wave_u) * (kPairs ? 8 : 16);  // first row of the group
+            const int p = (int)(g0 / ms);
+            if (g0 < a.M && p != a.rank) {
+              dag[j] = buffer_desc(a.cs[0].peer[p], (uint32_t)(ms * kbytes));
+              if (base[j] != kOutOfRange) base[j] -= (uint32_t)((int64_t)p * ms * kbytes);
             }
-            f32x4 v = acc[i][j];
-#pragma unroll
-            for (int q = 0; q < AGG_MAX_WORLD - 1; ++q)
-              if (q + 1 < world) v += in[q];
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rout, (int)((m * a.N + n) * 4), 0, 0);
+          }
+        } else {
+          // (a tile of more than 128 rows is pulled only when it lies inside one shard)
+          const int p = (int)(lo / ms);
+          if (p != a.rank) {
+            da = buffer_desc(a.cs[0].peer[p], (uint32_t)(ms * kbytes));
+            const uint32_t shift = (uint32_t)((int64_t)p * ms * kbytes);
+  #pragma unroll
+            for (int j = 0; j < NAL; ++j)
+              if (base[j] != kOutOfRange) base[j] -= shift;
           }
         }
       }
-    } else {
-      const int64_t base = (int64_t)block * a.m_block;
-      const bool local = (block == a.rank);
-      const int slot = block < a.rank ? block : block - 1;
-      const int64_t blk = a.m_block * a.N;    // floats per block
-      if (!local) {
-        // a non-local block's partial goes to `send` with write-through stores, so it is visible
-        // everywhere once they complete (no L2 writeback before the flag)
-        const __amdgpu_buffer_rsrc_t rsend = __builtin_amdgcn_make_buffer_rsrc(
-            a.send, 0, (int)((a.world - 1) * blk * 4), kBufferFlags);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int64_t m = lo + qrow(i);
-          if (m >= hi) continue;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + qcol(j);
-            if (n >= a.N) continue;
-            __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(u32x4, acc[i][j]), rsend,
-                (int)(((int64_t)slot * blk + (m - base) * a.N + n) * 4), 0, kStoreSystemCoherent);
-          }
+      const u32x4 db = buffer_desc(opB, (uint32_t)(opN * kbytes));
+      const uint32_t lds0 = lds_addr(stages) + (uint32_t)wave_u * 1024u;
+      // Load j of a slice (j < NI; pairs: of a slice pair, j < NL): A rows for j < NA (NAL), else B
+      // rows. The LDS stage of slice t is (t - t_lo) % 4 (pairs: region ((t - t_lo) / 2) % R); the
+      // main loop runs four (pairs: 2R) slices per trip, so every stage and region is a constant.
+      auto desc_of = [&](int j) -> const u32x4& {
+        return j < NAL ? (kGroupPull ? dag[j < NAL ? j : 0] : da) : db;
+      };
+      auto m0_of = [&](int sg, int j) { return lds0 + (uint32_t)sg * DSTAGE + (uint32_t)j * (NW * 1024u); };
+      // pairs: LDS address of load j into pair region rg
+      auto m0p = [&](int rg, int j) { return lds0 + (uint32_t)rg * (2 * DSTAGE) + (uint32_t)j * (NW * 1024u); };
+      // K byte offset of load j of slice t. Slices below t_safe lie wholly inside the part's K
+      // range: a plain offset. Otherwise (`masked`) the offset's top bit is set past the K end
+      // (out of range: reads zero), lane by lane, since a slice may straddle the end.
+      const int t_safe = (int)(kend / kSlice);
+      // B load j of slice t: row b_load_row of the slice's K rows, which start at K row t*kRowsB
+      // (64 * N bytes per slice); masked: rows at or past the part's K end read zeros
+      const uint32_t kend_rows = kend / EL;
+      auto voff_b = [&](auto masked, int t, int j) -> uint32_t {
+        const uint32_t tb = (uint32_t)t * (uint32_t)(kSliceBytes * opN);
+        if constexpr (decltype(masked)::value) {
+          const uint32_t row = (uint32_t)(t * kRowsB + b_load_row(b_pos(j), kChunksB));
+          return (base[j] + tb) | (row >= kend_rows ? kOutOfRange : 0u);
+        } else {
+          return base[j] + tb;
         }
+      };
+      auto voff_of = [&](auto masked, int t, int j) -> uint32_t {
+        if (j >= NAL) return voff_b(masked, t, j);
+        const uint32_t tk = (uint32_t)t * kSliceBytes;
+        if constexpr (decltype(masked)::value) {
+          const uint32_t oob = (uint32_t)((int)(tk + gk - kend) >> 31) ^ 0xFFFFFFFFu;
+          return (base[j] + tk) | (oob & kOutOfRange);
+        } else {
+          return base[j] + tk;
+        }
+      };
+      // pairs: K byte offset of load j of slice pair pr (slices 2pr and 2pr+1), masked as above
+      auto voffp = [&](auto masked, int pr, int j) -> uint32_t {
+        if (j >= NAL) return voff_b(masked, 2 * pr + (j - NAL) / NBS, j);
+        const uint32_t pk = (uint32_t)pr * (2 * kSliceBytes);
+        if constexpr (decltype(masked)::value) {
+          const uint32_t oob = (uint32_t)((int)(pk + pair_gk(pair_row(j)) - kend) >> 31) ^ 0xFFFFFFFFu;
+          return (base[j] + pk) | (oob & kOutOfRange);
+        } else {
+          return base[j] + pk;
+        }
+      };
+      // mixed: A load j into A region rg; B load j (>= NLA) into B stage sg
+      auto m0ma = [&](int rg, int j) { return lds0 + (uint32_t)rg * AREG + (uint32_t)j * (NW * 1024u); };
+      auto m0mb = [&](int sg, int j) {
+        return lds0 + (uint32_t)(2 * AREG + sg * BSTAGE) + (uint32_t)(j - NLA) * (NW * 1024u);
+      };
+      auto issue_one = [&](auto masked, int t, int sg, int j) {
+        lds_dma_load(desc_of(j), m0_of(sg, j), voff_of(masked, t, j));
+      };
+      // The loads a slice issues, as (load index, LDS address, offset). Four stages: in the first
+      // half of slice t, loads NH.. of slice t+3 into stage (t+3)%4; in the second half, loads
+      // 0..NH-1 of slice t+4 into stage t%4. Pairs: an even slice t issues, in its first half, the
+      // second half of the loads of pair t/2+1 into the other region; an odd slice t, in its second
+      // half, the first half of the loads of pair (t+1)/2+1 into its own region (whose pair every
+      // wave has finished at the odd slice's barrier).
+      struct Ld { int j; uint32_t m0, vo; };
+      auto ld_first = [&](auto masked, auto u_, int t, int e) -> Ld {
+        constexpr int U = decltype(u_)::value;
+        if constexpr (kMixed) {
+          // even slices: the second part of A pair t/2+1, then (all slices) the second part of B
+          // slice t+3
+          constexpr int EA = (U & 1) ? 0 : NLA - NLA / 2;
+          if (e < EA) {
+            const int j = NLA / 2 + e;
+            return Ld{j, m0ma(((U >> 1) + 1) & 1, j), voffp(masked, t / 2 + 1, j)};
+          }
+          const int j = NLA + NHB + (e - EA);
+          return Ld{j, m0mb((U + 3) & 3, j), voff_of(masked, t + 3, j)};
+        } else if constexpr (kPairs) {
+          const int j = NL / 2 + e;
+          return Ld{j, m0p(((U >> 1) + kRegions - 1) % kRegions, j), voffp(masked, t / 2 + kRegions - 1, j)};
+        } else {
+          const int j = NI / 2 + e;
+          return Ld{j, m0_of((U + 3) & 3, j), voff_of(masked, t + 3, j)};
+        }
+      };
+      auto ld_second = [&](auto masked, auto u_, int t, int k) -> Ld {
+        constexpr int U = decltype(u_)::value;
+        if constexpr (kMixed) {
+          // odd slices: the first part of A pair (t+1)/2+1, then (all slices) the first part of B
+          // slice t+4
+          constexpr int KA = (U & 1) ? NLA / 2 : 0;
+          if (k < KA) return Ld{k, m0ma(U >> 1, k), voffp(masked, (t + 1) / 2 + 1, k)};
+          const int j = NLA + (k - KA);
+          return Ld{j, m0mb(U, j), voff_of(masked, t + 4, j)};
+        }
+        if constexpr (kPairs) return Ld{k, m0p(U >> 1, k), voffp(masked, (t + 1) / 2 + kRegions - 1, k)};
+        else return Ld{k, m0_of(U, k), voff_of(masked, t + 4, k)};
+      };
+      constexpr int NH = NI / 2;                 // loads of a slice issued in the earlier half
+      // The slice schedule, for both dtypes: RM x CN MFMA blocks per wave and slice, operand
+      // fragments of type F read from LDS by lda(stage, block row) / ldb(stage, block column).
+      // One K slice t in stage U, its B fragments in fbc and its first A fragment in fa (requested
+      // during the previous slice). Stage U is refilled with slice t+4 by NI direct-to-LDS loads,
+      // the first NH of them in the second half of slice t and the rest in the first half of slice
+      // t+1, so that every half slice carries about NI/2 loads between its MFMAs and the load path
+      // never takes a burst. First half of slice t: the remaining A fragments of slice t are
+      // requested row by row, and the loads NH..NI-1 of slice t+3 go between the MFMAs. Then the
+      // waves meet (slice t+1 has landed everywhere; every wave has read all of slice t), and the
+      // second half spreads slice t+1's B fragments and first A fragment, then the loads 0..NH-1
+      // of slice t+4, between its MFMAs. (Pairs: the same two halves carry the pair loads that
+      // ld_first / ld_second describe.) A load that follows an MFMA shares its asm statement
+      // (mma_dma), so the MFMA is the wait state between the M0 write and the load.
+      auto run_slices = [&](auto& accs, auto fa, auto lda, auto ldb, auto mma, auto mma_dma,
+                            auto rm_, auto cn_, auto lone_) {
+        constexpr int RM = decltype(rm_)::value, CN = decltype(cn_)::value;
+        constexpr bool kLone = decltype(lone_)::value;
+        using F = decltype(fa);
+        constexpr int RB = RM / 2;                 // block rows before the barrier
+        constexpr int S1 = RB * CN, S2 = (RM - RB) * CN;
+        static_assert(RM - RB - 1 <= RB, "the A fragments after the barrier are loaded before it");
+        auto slice = [&](auto u_, auto masked, F (&fbc)[CN], F (&fbn)[CN], int t) {
+          constexpr int U = decltype(u_)::value;
+          constexpr int U1 = (U + 1) % (kPairs ? 2 * kRegions : 4);
+          // loads issued in the first half (E1) and in the second half (ND) of this slice
+          constexpr int E1 = kMixed ? ((U & 1) ? 0 : NLA - NLA / 2) + (NIB - NHB)
+                             : kPairs ? ((U & 1) ? 0 : NL / 2) : NI - NH;
+          constexpr int ND = kMixed ? ((U & 1) ? NLA / 2 : 0) + NHB : kPairs ? ((U & 1) ? NL / 2 : 0) : NH;
+          constexpr int E2 = CN + 1 + ND;
+          F far[RM];
+          far[0] = fa;
+          if (S1 == 0) {                            // no MFMA before the barrier: issue plainly
+  #pragma unroll
+            for (int e = 0; e < E1; ++e) {
+              const Ld l = ld_first(masked, u_, t, e);
+              lds_dma_load(desc_of(l.j), l.m0, l.vo);
+            }
+          }
+  #pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            far[i + 1] = lda(U, i + 1);
+            if (RB + 1 + i < RM) far[RB + 1 + i] = lda(U, RB + 1 + i);
+  #pragma unroll
+            for (int j = 0; j < CN; ++j) {
+              const int q = i * CN + j;
+              bool fused = false;
+  #pragma unroll
+              for (int e = 0; e < E1; ++e) {
+                if (S1 == 0 || e * S1 / (E1 > 0 ? E1 : 1) != q) continue;
+                const Ld l = ld_first(masked, u_, t, e);
+                if (!fused) {
+                  mma_dma(accs[i][j], fbc[j], far[i], desc_of(l.j), l.m0, l.vo);
+                  fused = true;
+                } else {
+                  lds_dma_load(desc_of(l.j), l.m0, l.vo);
+                }
+              }
+              if (!fused) mma(accs[i][j], fbc[j], far[i]);
+            }
+          }
+          // slice t+1 has landed (four stages: all but the 2*NI loads issued since; pairs, odd t:
+          // all of pair (t+1)/2, the last loads issued; even t: all but the NL of pair t/2+1)
+          stage_barrier<kMixed ? mixed_barrier_count(U, NLA, NIB, NHB)
+                        : kPairs ? pair_barrier_count(U, kRegions, NL) : stage_barrier_count(NI)>();
+  #pragma unroll
+          for (int i = RB; i < RM; ++i) {
+  #pragma unroll
+            for (int j = 0; j < CN; ++j) {
+              const int q = (i - RB) * CN + j;
+              if (kLone) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+              // the first second-half load scheduled after this MFMA is fused with it
+              int fuse_e = -1;
+  #pragma unroll
+              for (int e = CN + 1; e < E2; ++e)
+                if (fuse_e < 0 && e * S2 / E2 == q) fuse_e = e;
+              if (fuse_e >= 0) {
+                const Ld l = ld_second(masked, u_, t, fuse_e - CN - 1);
+                mma_dma(accs[i][j], fbc[j], far[i], desc_of(l.j), l.m0, l.vo);
+              } else {
+                mma(accs[i][j], fbc[j], far[i]);
+              }
+  #pragma unroll
+              for (int e = 0; e < E2; ++e) {
+                if (e * S2 / E2 != q || e == fuse_e) continue;   // request e goes after MFMA slot e*S2/E2
+                if (e < CN) fbn[e] = ldb(U1, e);
+                else if (e == CN) fa = lda(U1, 0);
+                else {
+                  const Ld l = ld_second(masked, u_, t, e - CN - 1);
+                  lds_dma_load(desc_of(l.j), l.m0, l.vo);
+                }
+              }
+            }
+          }
+        };
+        if (t_hi > t_lo) {
+          F fb0[CN], fb1[CN];
+          acc_settle(accs);
+          constexpr auto kPlain = std::integral_constant<bool, false>{};
+          constexpr auto kMasked = std::integral_constant<bool, true>{};
+          if constexpr (kMixed) {
+            // A pair 0 whole and the first part of A pair 1; B slices 0..2 whole and the first part
+            // of B slice 3 (the first slices issue the rest)
+  #pragma unroll
+            for (int j = 0; j < NLA; ++j) lds_dma_load(desc_of(j), m0ma(0, j), voffp(kMasked, t_lo / 2, j));
+  #pragma unroll
+            for (int j = 0; j < NLA / 2; ++j) lds_dma_load(desc_of(j), m0ma(1, j), voffp(kMasked, t_lo / 2 + 1, j));
+  #pragma unroll
+            for (int q = 0; q < 3; ++q)
+  #pragma unroll
+              for (int j = NLA; j < NLA + NIB; ++j) lds_dma_load(desc_of(j), m0mb(q, j), voff_of(kMasked, t_lo + q, j));
+  #pragma unroll
+            for (int j = NLA; j < NLA + NHB; ++j) lds_dma_load(desc_of(j), m0mb(3, j), voff_of(kMasked, t_lo + 3, j));
+            stage_barrier<mixed_prologue_count(NLA, NIB, NHB)>();
+          } else if constexpr (kPairs) {
+            // pairs 0 .. R-2 whole and the first half of pair R-1 (the first slice issues the rest)
+  #pragma unroll
+            for (int q = 0; q + 1 < kRegions; ++q)
+  #pragma unroll
+              for (int j = 0; j < NL; ++j) lds_dma_load(desc_of(j), m0p(q, j), voffp(kMasked, t_lo / 2 + q, j));
+  #pragma unroll
+            for (int j = 0; j < NL / 2; ++j)
+              lds_dma_load(desc_of(j), m0p(kRegions - 1, j), voffp(kMasked, t_lo / 2 + kRegions - 1, j));
+            stage_barrier<pair_prologue_count(kRegions, NL)>();
+          } else {
+  #pragma unroll
+            for (int s = 0; s < 3; ++s)
+  #pragma unroll
+              for (int j = 0; j < NI; ++j) issue_one(kMasked, t_lo + s, s, j);
+  #pragma unroll
+            for (int j = 0; j < NH; ++j) issue_one(kMasked, t_lo + 3, 3, j);   // the first slice issues the rest
+            stage_barrier<stage_prologue_count(NI)>();
+          }
+  #pragma unroll
+          for (int j = 0; j < CN; ++j) fb0[j] = ldb(0, j);
+          fa = lda(0, 0);
+          // four slices per trip (slices past the part's end read zeros); a trip whose loads
+          // (up to slice t+7) stay below t_safe needs no K-end masks
+          // (pairs: 2R slices per trip, whose loads reach slice t + 4R - 1)
+          constexpr int TRIP = kPairs ? 2 * kRegions : 4;
+          auto trip = [&](auto masked, int t) {
+            slice(std::integral_constant<int, 0>{}, masked, fb0, fb1, t);
+            slice(std::integral_constant<int, 1>{}, masked, fb1, fb0, t + 1);
+            slice(std::integral_constant<int, 2>{}, masked, fb0, fb1, t + 2);
+            slice(std::integral_constant<int, 3>{}, masked, fb1, fb0, t + 3);
+            if constexpr (TRIP == 8) {
+              slice(std::integral_constant<int, 4>{}, masked, fb0, fb1, t + 4);
+              slice(std::integral_constant<int, 5>{}, masked, fb1, fb0, t + 5);
+              slice(std::integral_constant<int, 6>{}, masked, fb0, fb1, t + 6);
+              slice(std::integral_constant<int, 7>{}, masked, fb1, fb0, t + 7);
+            }
+          };
+          int t = t_lo;
+          for (; t + (kPairs ? 4 * kRegions : 8) - 1 < t_safe; t += TRIP) trip(kPlain, t);
+          for (; t < t_hi; t += TRIP) trip(kMasked, t);
+          acc_settle(accs);
+          // loads issued past the end land (as zeros) and every wave is done with LDS before the
+          // next tile refills it
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+      };
+      // LDS byte offset of 16-byte chunk g (0..3) of A row `row` of slice stage sg
+      auto frag_off = [&](int sg, int row, int g) -> uint32_t {
+        if constexpr (kMixed) {
+          // A rows: pair region (sg/2) % 2, half sg % 2
+          return (uint32_t)(((sg >> 1) & 1) * AREG) + lds128_off(row, (sg & 1) * 4 + g);
+        } else if constexpr (kPairs) {
+          return (uint32_t)((sg >> 1) * (2 * DSTAGE)) + lds128_off(row, (sg & 1) * 4 + g);
+        } else {
+          return (uint32_t)(sg * DSTAGE) + lds64_off(row, g);
+        }
+      };
+      // LDS byte offset of the B block of slice stage sg (after the A rows of its stage or pair
+      // region; mixed: the B stages after the two A regions)
+      auto bblk = [&](int sg) -> uint32_t {
+        if constexpr (kMixed) return (uint32_t)(2 * AREG + sg * BSTAGE);
+        else if constexpr (kPairs)
+          return (uint32_t)((sg >> 1) * (2 * DSTAGE) + BM * 2 * kSliceBytes + (sg & 1) * (BNP * kSliceBytes));
+        else return (uint32_t)(sg * DSTAGE + BM * kSliceBytes);
+      };
+      // this lane's transposing B reads: byte offset of read 0 inside a B block for the fragment
+      // whose first chunk is 0, and its rows' swizzle (read r adds r times 4 rows (bf16) or 8 rows
+      // (fp8); the fragment's first chunk c0 (even) enters as (c0 ^ swizzle))
+      const uint32_t boff0 = (uint32_t)b_read_base(lane, kChunksB, EL);
+      const uint32_t bswz = (uint32_t)b_read_swizzle(lane, kChunksB, EL);
+      constexpr uint32_t kReadRowStep = (uint32_t)b_read_step(kChunksB, EL);
+      if constexpr (!FP8) {
+        // ---- bf16: 16x16x32 MFMA blocks, one 16-byte fragment per lane
+  #pragma unroll
+        for (int i = 0; i < FM; ++i)
+  #pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // B fragment: 16 columns starting at chunk c0, K rows 8*(lane/16) .. +7 from two
+        // transposing reads (rows +0..3 and +4..7)
+        auto ldb = [&](int sg, int j) {
+          const uint32_t c0 = (uint32_t)((wn * WTN + j * 16) >> 3);
+          const uint32_t off = bblk(sg) + boff0 + 16u * (c0 ^ bswz);
+          const u32x2 r0 = lds_read_tr16(stages, off);
+          const u32x2 r1 = lds_read_tr16(stages, off + kReadRowStep);
+          return u32x4{r0[0], r0[1], r1[0], r1[1]};
+        };
+        auto lda = [&](int sg, int i) {
+          return *reinterpret_cast<const u32x4*>(stages + frag_off(sg, wm * WTM + i * 16 + (lane & 15), lane >> 4));
+        };
+        run_slices(acc, u32x4{}, lda, ldb,
+                   [](f32x4& c, const u32x4& b, const u32x4& x) { mfma_bf16(c, b, x); },
+                   [](f32x4& c, const u32x4& b, const u32x4& x, const u32x4& d, uint32_t m0v, uint32_t vo) {
+                     mfma_bf16_dma(c, b, x, d, m0v, vo);
+                   },
+                   std::integral_constant<int, FM>{}, std::integral_constant<int, FN>{},
+                   std::integral_constant<bool, false>{});
       } else {
-        // the local block: the tile's partial goes to `out` (write-through, like `send`); the
-        // peers' partials are added after the last tile by reduce_local
-        const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(
-            a.out, 0, (int)(blk * 4), kBufferFlags);
-#pragma unroll
+        // ---- fp8 (e4m3): 32x32x64 MFMA blocks with unit block scales, one 32-byte fragment per
+        // lane; the per-tensor scales are applied in the epilogue
+        f32x16 acc8[F8M][F8N];
+  #pragma unroll
+        for (int i = 0; i < F8M; ++i)
+  #pragma unroll
+          for (int j = 0; j < F8N; ++j) acc8[i][j] = f32x16{};
+        // a 32-row fp8 A fragment: row r + (lane & 31), K bytes 32*(lane/32) .. +31 of the slice
+        auto lda = [&](int sg, int i) {
+          const int row = wm * WTM + i * 32 + (lane & 31), g = (lane >> 5) * 2;
+          const u32x4 lo4 = *reinterpret_cast<const u32x4*>(stages + frag_off(sg, row, g));
+          const u32x4 hi4 = *reinterpret_cast<const u32x4*>(stages + frag_off(sg, row, g + 1));
+          return i32x8{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3],
+                       (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+        };
+        // B fragment: 32 columns starting at chunk c0, K rows 32*(lane/32) .. +31 from four
+        // transposing reads of 8 rows each
+        auto ldb = [&](int sg, int j) {
+          const uint32_t c0 = (uint32_t)((wn * WTN + j * 32) >> 4);
+          const uint32_t off = bblk(sg) + boff0 + 16u * (c0 ^ bswz);
+          const u32x2 r0 = lds_read_tr8(stages, off);
+          const u32x2 r1 = lds_read_tr8(stages, off + kReadRowStep);
+          const u32x2 r2 = lds_read_tr8(stages, off + 2 * kReadRowStep);
+          const u32x2 r3 = lds_read_tr8(stages, off + 3 * kReadRowStep);
+          return i32x8{(int)r0[0], (int)r0[1], (int)r1[0], (int)r1[1],
+                       (int)r2[0], (int)r2[1], (int)r3[0], (int)r3[1]};
+        };
+        // a wave with a single 32x32 block reuses its accumulator in the next slice's first
+        // MFMA: give the previous one time to write it back
+        run_slices(acc8, i32x8{}, lda, ldb,
+                   [](f32x16& c, const i32x8& b, const i32x8& x) { mfma_fp8(c, b, x); },
+                   [](f32x16& c, const i32x8& b, const i32x8& x, const u32x4& d, uint32_t m0v, uint32_t vo) {
+                     mfma_fp8_dma(c, b, x, d, m0v, vo);
+                   },
+                   std::integral_constant<int, F8M>{}, std::integral_constant<int, F8N>{},
+                   std::integral_constant<bool, (F8M * F8N < 3)>{});
+        // the epilogue's view: quad q of block (i, j) is acc[i][4j + q]
+  #pragma unroll
+        for (int i = 0; i < F8M; ++i)
+  #pragma unroll
+          for (int j = 0; j < F8N; ++j)
+  #pragma unroll
+            for (int q = 0; q < 4; ++q)
+              acc[i][4 * j + q] = f32x4{acc8[i][j][4 * q], acc8[i][j][4 * q + 1], acc8[i][j][4 * q + 2],
+                                        acc8[i][j][4 * q + 3]};
+      }
+
+      // ---- epilogue
+      // quad (i, j) of this lane: row qrow(i), columns qcol(j) .. qcol(j)+3 of the tile
+      auto qrow = [&](int i) {
+        return FP8 ? wm * WTM + i * 32 + (lane & 31) : wm * WTM + i * 16 + (lane & 15);
+      };
+      auto qcol = [&](int j) {
+        return FP8 ? wn * WTN + (j >> 2) * 32 + (j & 3) * 8 + (lane >> 5) * 4
+                   : wn * WTN + j * 16 + (lane >> 4) * 4;
+      };
+      if (EPI == kEpiFfn && ph1) {
+        // phase 1: h = silu(acc) as bf16, written through (phase-2 tiles on any XCD read it), then
+        // the tile counts itself in its row tile once its stores have completed
+        const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(a.h, 0, (int)(a.M * a.N1 * 2), kBufferFlags);
+  #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const int64_t m = lo + qrow(i);
           if (m >= hi) continue;
-#pragma unroll
+  #pragma unroll
           for (int j = 0; j < FN; ++j) {
             const int64_t n = n0 + qcol(j);
-            if (n >= a.N) continue;
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rout,
-                                                   (int)(((m - base) * a.N + n) * 4), 0, kStoreSystemCoherent);
+            if (n >= a.N1) continue;
+            f32x4 v = acc[i][j];
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = v[e] / (1.0f + __expf(-v[e]));
+            u32x2 packed;
+            packed[0] = bf16x2_rne(v[0], v[1]);
+            packed[1] = bf16x2_rne(v[2], v[3]);
+            __builtin_amdgcn_raw_buffer_store_b64(packed, rh, (int)((m * a.N1 + n) * 2), 0, kStoreSystemCoherent);
           }
         }
-        // once the stores have completed, count the tile in its row tile
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tid == 0)
-          __hip_atomic_fetch_add(a.scratch + kScrLocal + tib, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if (!local) {
-        // publish: once every thread's write-through stores have completed, this tile's rows of
-        // `send` are final for its column range; the tile that completes a send chunk raises
-        // its flag (a system-coherent store)
+          __hip_atomic_fetch_add(a.scratch + kScrSplit + row_tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else if (EPI == kEpiAllGather) {
+        bool finish = true;
+        // split-K exists for tiles up to 128 x 128 only (the host never splits a larger one): the
+        // partial and reduction code would cost the big tiles registers in their main loop
+        if (kSplitTiles && a.ksplit > 1) {
+          // split-K: every part writes its fp32 partial (write-through) and counts itself in; the
+          // parts are summed in part order (so the sum does not depend on which part is last),
+          // by all parts together or by the part that arrives last, then converted and stored.
+          // The partial loads are system-coherent: a stale line of an earlier launch must not be
+          // read.
+          const int64_t plane = a.M * a.N;
+          const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+              a.ws, 0, (int)(a.ksplit * plane * 4), kBufferFlags);
+  #pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int64_t m = lo + qrow(i);
+            if (m >= hi) continue;
+  #pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int64_t n = n0 + qcol(j);
+              if (n >= a.N) continue;
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rw,
+                                                     (int)(((int64_t)part * plane + m * a.N + n) * 4),
+                                                     0, kStoreSystemCoherent);
+            }
+          }
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          const int tile_id = row_tile * (a.n_col_tiles / a.ksplit) + col_tile;
+          uint32_t* split_ctr = a.scratch + kScrSplit + tile_id;
+          if (a.split_together) {
+            // every part has its own workgroup in this launch: once all parts have stored, each
+            // sums a row range of the tile; the counter counts every part in twice (stored, then
+            // summed) and the last arrival resets it
+            const uint32_t ks = (uint32_t)a.ksplit;
+            if (tid == 0) __hip_atomic_fetch_add(split_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (wave == 0) {
+              const bool ok = wait_count(a, split_ctr, ks);
+              if (lane == 0) s_ok = ok;
+            }
+            __syncthreads();
+            if (__builtin_amdgcn_readfirstlane(s_ok)) sum_split_rows<BM, BN, FP8>(a, tid, lo, hi, n0, part);
+            __syncthreads();
+            if (tid == 0 && __hip_atomic_fetch_add(split_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 2 * ks - 1)
+              __hip_atomic_store(split_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            finish = false;
+          } else {
+            if (tid == 0)
+              s_ok = (__hip_atomic_fetch_add(split_ctr, 1u, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)a.ksplit - 1);
+            __syncthreads();
+            finish = __builtin_amdgcn_readfirstlane(s_ok) != 0;
+            if (finish) {
+              // parts in order, G at a time: the loads of G parts are in flight together (one round
+              // trip per group instead of per part), then they are added one after another in part
+              // order, so the sum does not depend on the grouping
+              auto load_part = [&](f32x4 (&v)[FM][FN], int q) {
+  #pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                  const int64_t m = lo + qrow(i);
+  #pragma unroll
+                  for (int j = 0; j < FN; ++j) {
+                    const int64_t n = n0 + qcol(j);
+                    // rows / columns past the end, and parts past the last, read zeros (offset past
+                    // the buffer)
+                    const int off = (q < a.ksplit && m < hi && n < a.N)
+                                        ? (int)(((int64_t)q * plane + m * a.N + n) * 4)
+                                        : (int)kOutOfRange;
+                    v[i][j] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kStoreSystemCoherent));
+                  }
+                }
+              };
+              constexpr int G = FM * FN >= 32 ? 1 : (32 / (FM * FN) > 8 ? 8 : 32 / (FM * FN));
+              const int ks = __builtin_amdgcn_readfirstlane(a.ksplit);
+              for (int q0 = 0; q0 < ks; q0 += G) {
+                f32x4 v[G][FM][FN];
+  #pragma unroll
+                for (int g = 0; g < G; ++g) load_part(v[g], q0 + g);
+                __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+                for (int g = 0; g < G; ++g) {
+                  if (q0 + g >= ks) break;
+  #pragma unroll
+                  for (int i = 0; i < FM; ++i)
+  #pragma unroll
+                    for (int j = 0; j < FN; ++j) acc[i][j] = (q0 + g == 0) ? v[g][i][j] : acc[i][j] + v[g][i][j];
+                }
+              }
+              if (tid == 0) __hip_atomic_store(split_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        }
+        if (finish) {
+  #pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int64_t m = lo + qrow(i);
+            if (m >= hi) continue;
+  #pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int64_t n = n0 + qcol(j);
+              if (n >= a.N) continue;
+              f32x4 v = acc[i][j];
+              if (FP8) v *= a.scale;
+              u32x2 packed;
+              packed[0] = bf16x2_rne(v[0], v[1]);
+              packed[1] = bf16x2_rne(v[2], v[3]);
+              *reinterpret_cast<u32x2*>(a.c + m * a.N + n) = packed;
+            }
+          }
+        }
+      } else if (EPI == kEpiAllReduce) {
+        // One-shot AllReduce, fused: this tile's partial goes to `send` (what every peer receives;
+        // write-through, so it is visible everywhere once the stores complete) and the tile that
+        // completes a chunk of `send` raises its send flag; then, once every peer's chunks of these
+        // rows have arrived, out = partial + the peers' partials in ascending rank order (a fixed
+        // order: `out` does not depend on arrival order).
+        const int64_t MN = a.M * a.N;
+        const __amdgpu_buffer_rsrc_t rsend = __builtin_amdgcn_make_buffer_rsrc(a.send, 0, (int)(MN * 4), kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(a.out, 0, (int)(MN * 4), kBufferFlags);
+        const __amdgpu_buffer_rsrc_t rrecv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(a.recv), 0, (int)(a.world * MN * 4), kBufferFlags);
+  #pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int64_t m = lo + qrow(i);
+          if (m >= hi) continue;
+  #pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + qcol(j);
+            if (n >= a.N) continue;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rsend,
+                                                   (int)((m * a.N + n) * 4), 0, kStoreSystemCoherent);
+          }
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tid == 0) {
-          const int64_t rlo = lo - base, rhi = hi - base;
-          const int q_lo = (int)(rlo / a.chunk_rows), q_hi = (int)((rhi - 1) / a.chunk_rows);
+          const int q_lo = (int)(lo / a.chunk_rows), q_hi = (int)((hi - 1) / a.chunk_rows);
           for (int q = q_lo; q <= q_hi; ++q) {
-            // tiles overlapping chunk q of this block, times the column tiles
             const int64_t clo = (int64_t)q * a.chunk_rows;
             const int64_t chi = clo + a.chunk_rows;
             const int t_first = (int)(clo / BM), t_last = (int)((chi - 1) / BM);
             const uint32_t expect = (uint32_t)(t_last - t_first + 1) * (uint32_t)a.n_col_tiles;
-            const int c = block * a.cps + q;
-            const uint32_t prev = __hip_atomic_fetch_add(a.scratch + kScrRsCount + c, 1u, __ATOMIC_RELAXED,
+            const uint32_t prev = __hip_atomic_fetch_add(a.scratch + kScrRsCount + q, 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);
             if (prev + 1 == expect)
-              __hip_atomic_store(a.send_flags + c, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+              __hip_atomic_store(a.send_flags + q, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          }
+        }
+        if (wave == 0) {
+          uint32_t seen = 0xFFFFFFFFu;
+          const bool ok = wait_chunks<kEpiAllReduce>(a, lo, hi, 0, seen);
+          if (lane == 0) {
+            s_ok = ok;
+            if (trec) { trec[3] = seen; trec[6] = wall_ticks(); }
+          }
+        }
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(s_ok)) {
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+          const int world = __builtin_amdgcn_readfirstlane(a.world), rank = __builtin_amdgcn_readfirstlane(a.rank);
+  #pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int64_t m = lo + qrow(i);
+  #pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int64_t n = n0 + qcol(j);
+              if (m >= hi || n >= a.N) continue;
+              // every peer's quad in flight, then added in rank order
+              f32x4 in[AGG_MAX_WORLD - 1];
+  #pragma unroll
+              for (int q = 0; q < AGG_MAX_WORLD - 1; ++q) {
+                const int p = q < rank ? q : q + 1;
+                const int off = p < world ? (int)(((int64_t)p * MN + m * a.N + n) * 4) : (int)kOutOfRange;
+                in[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrecv, off, 0, 0));
+              }
+              f32x4 v = acc[i][j];
+  #pragma unroll
+              for (int q = 0; q < AGG_MAX_WORLD - 1; ++q)
+                if (q + 1 < world) v += in[q];
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rout, (int)((m * a.N + n) * 4), 0, 0);
+            }
+          }
+        }
+      } else {
+        const int64_t base = (int64_t)block * a.m_block;
+        const bool local = (block == a.rank);
+        const int slot = block < a.rank ? block : block - 1;
+        const int64_t blk = a.m_block * a.N;    // floats per block
+        if (!local) {
+          // a non-local block's partial goes to `send` with write-through stores, so it is visible
+          // everywhere once they complete (no L2 writeback before the flag)
+          const __amdgpu_buffer_rsrc_t rsend = __builtin_amdgcn_make_buffer_rsrc(
+              a.send, 0, (int)((a.world - 1) * blk * 4), kBufferFlags);
+  #pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int64_t m = lo + qrow(i);
+            if (m >= hi) continue;
+  #pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int64_t n = n0 + qcol(j);
+              if (n >= a.N) continue;
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  __builtin_bit_cast(u32x4, acc[i][j]), rsend,
+                  (int)(((int64_t)slot * blk + (m - base) * a.N + n) * 4), 0, kStoreSystemCoherent);
+            }
+          }
+        } else {
+          // the local block: the tile's partial goes to `out` (write-through, like `send`); the
+          // peers' partials are added after the last tile by reduce_local
+          const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(
+              a.out, 0, (int)(blk * 4), kBufferFlags);
+  #pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int64_t m = lo + qrow(i);
+            if (m >= hi) continue;
+  #pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int64_t n = n0 + qcol(j);
+              if (n >= a.N) continue;
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rout,
+                                                     (int)(((m - base) * a.N + n) * 4), 0, kStoreSystemCoherent);
+            }
+          }
+          // once the stores have completed, count the tile in its row tile
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          if (tid == 0)
+            __hip_atomic_fetch_add(a.scratch + kScrLocal + tib, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (!local) {
+          // publish: once every thread's write-through stores have completed, this tile's rows of
+          // `send` are final for its column range; the tile that completes a send chunk raises
+          // its flag (a system-coherent store)
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          if (tid == 0) {
+            const int64_t rlo = lo - base, rhi = hi - base;
+            const int q_lo = (int)(rlo / a.chunk_rows), q_hi = (int)((rhi - 1) / a.chunk_rows);
+            for (int q = q_lo; q <= q_hi; ++q) {
+              // tiles overlapping chunk q of this block, times the column tiles
+              const int64_t clo = (int64_t)q * a.chunk_rows;
+              const int64_t chi = clo + a.chunk_rows;
+              const int t_first = (int)(clo / BM), t_last = (int)((chi - 1) / BM);
+              const uint32_t expect = (uint32_t)(t_last - t_first + 1) * (uint32_t)a.n_col_tiles;
+              const int c = block * a.cps + q;
+              const uint32_t prev = __hip_atomic_fetch_add(a.scratch + kScrRsCount + c, 1u, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+              if (prev + 1 == expect)
+                __hip_atomic_store(a.send_flags + c, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
           }
         }
       }
-    }
-    if (tid == 0 && trec) {
-      trec[7] = wall_ticks();
-      atomicAdd(trec + 4, 1u);
-    }
-    // s_tile / s_ok are rewritten by the next claim only after every thread passed here
-    __syncthreads();
+      if (tid == 0 && trec) {
+        trec[7] = wall_ticks();
+        atomicAdd(trec + 4, 1u);
+      }
+      // s_tile / s_ok are rewritten by the next claim only after every thread passed here
+      __syncthreads();
+    };
+    if (EPI == kEpiFfn && __builtin_amdgcn_readfirstlane(s_tile[2]) == 1) tile_body(std::true_type{});
+    else tile_body(std::false_type{});
   }
 
-  if (EPI == kEpiReduceScatter) reduce_local<BM>(a, tid, &s_job, &s_ok);
+  // (only a launch that computes the tiles reduces: a copy-only launch leaves `out` alone)
+  if ((EPI == kEpiReduceScatter || EPI == kEpiFfn) && a.n_row_tiles > 0) reduce_local<BM>(a, tid, &s_job, &s_ok);
 
   // ---- the last workgroup resets the counters for the next launch. No fence: every counter
   // reset here was last touched by the other workgroups through atomics whose returned values
@@ -1509,15 +1599,23 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         __hip_atomic_store(a.scratch + kScrCopyNext, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(a.scratch + kScrCopyT0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      for (uint32_t i = tid; i * (uint32_t)a.pieces < a.copy_jobs; i += NT)
-        __hip_atomic_store(a.scratch + kScrPieces + a.scratch[kScrOrder + i], 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int set = 0; set < 2; ++set) {
+        const CopySet& cs = a.cs[set];
+        for (uint32_t i = tid; i * (uint32_t)cs.pieces < cs.jobs; i += NT)
+          __hip_atomic_store(a.scratch + kScrPieces + cs.piece_off + a.scratch[kScrOrder + cs.order_off + i], 0u,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     if (EPI == kEpiAllReduce) {
       for (int i = tid; i < a.cps; i += NT)
         __hip_atomic_store(a.scratch + kScrRsCount + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (EPI == kEpiReduceScatter) {
+    if (EPI == kEpiFfn) {
+      for (int i = tid; i < a.n_row_tiles1; i += NT)
+        __hip_atomic_store(a.scratch + kScrSplit + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (EPI == kEpiReduceScatter || EPI == kEpiFfn) {
       for (int i = tid; i < a.world * a.cps; i += NT)
         __hip_atomic_store(a.scratch + kScrRsCount + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (int i = tid; i < a.tpb; i += NT)
@@ -1566,6 +1664,8 @@ int max_blocks_per_cu(int bm, int bn, int dtype, int epilogue) {
     return occupancy_shape<AGG_BF16, kEpiReduceScatter>(bm, bn);
   } else if (epilogue == kEpiAllReduce && dtype == AGG_BF16) {
     return occupancy_shape<AGG_BF16, kEpiAllReduce>(bm, bn);
+  } else if (epilogue == kEpiFfn && dtype == AGG_BF16 && bm == 256 && bn == 256) {
+    return occupancy_one<256, 256, AGG_BF16, kEpiFfn>();
   }
   return 0;
 }
@@ -1589,6 +1689,8 @@ hipError_t launch_gemm(const GemmArgs& args, int bm, int bn, int dtype, int epil
     return launch_shape<AGG_BF16, kEpiReduceScatter>(args, bm, bn, grid, stream);
   } else if (epilogue == kEpiAllReduce && dtype == AGG_BF16) {
     return launch_shape<AGG_BF16, kEpiAllReduce>(args, bm, bn, grid, stream);
+  } else if (epilogue == kEpiFfn && dtype == AGG_BF16 && bm == 256 && bn == 256) {
+    return launch_one<256, 256, AGG_BF16, kEpiFfn>(args, grid, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -168,3 +168,63 @@ class ArWorkload:
         if self.ctx is not None:
             B.agg_ctx_destroy(self.ctx)
             self.ctx = None
+
+
+class FfnWorkload:
+    """One rank's share of the FFN chain (AllGather+GEMM, SiLU, GEMM+ReduceScatter) with W-1
+    emulated peers on one GPU.
+
+    shards: W CPU tensors (Ms x K1 bf16); w1: CPU (K1 x N1) bf16; w2: CPU (N1 x N2) bf16; peers:
+    CPU (W x Ms x N2) float32 (slot rank unused): what each peer contributes to this rank's block.
+    """
+
+    def __init__(self, world, rank, shards, w1, w2, peers, chunk_rows, rs_chunk_rows,
+                 device="cuda", producer="cu"):
+        self.world, self.rank = world, rank
+        self.chunk_rows, self.rs_chunk_rows = chunk_rows, rs_chunk_rows
+        self.m_shard, self.k1 = shards[0].shape
+        self.n1, self.n2 = w1.shape[1], w2.shape[1]
+        self.m = world * self.m_shard
+        self.device = torch.device(device)
+        dev = self.device
+        self.peers = [s.to(dev) if p != rank else None for p, s in enumerate(shards)]
+        self.local = shards[rank].to(dev)
+        self.gather = torch.zeros(self.m, self.k1, dtype=torch.bfloat16, device=dev)
+        self.reset_local()
+        cps = self.m_shard // chunk_rows
+        cpb = self.m_shard // rs_chunk_rows
+        self.flags = torch.zeros(max(world * cps, 1), dtype=torch.int32, device=dev)
+        self.w1 = w1.contiguous().to(dev)
+        self.w2 = w2.contiguous().to(dev)
+        self.h = torch.zeros(self.m, self.n1, dtype=torch.bfloat16, device=dev)
+        self.rs_peers = [peers[p].to(dev) if p != rank else None for p in range(world)]
+        self.recv = torch.zeros(world, self.m_shard, self.n2, dtype=torch.float32, device=dev)
+        self.rs_flags = torch.zeros(max(world * cpb, 1), dtype=torch.int32, device=dev)
+        self.send_flags = torch.zeros(max(world * cpb, 1), dtype=torch.int32, device=dev)
+        self.send = torch.zeros(max(world - 1, 1), self.m_shard, self.n2, dtype=torch.float32, device=dev)
+        self.out = torch.zeros(self.m_shard, self.n2, dtype=torch.float32, device=dev)
+        self.copy_stream = None
+        self.ctx = B.agg_ctx_create(dev.index or 0)
+        B.agg_ctx_set_producer(self.ctx, producer)
+
+    def reset_local(self):
+        ms = self.m_shard
+        self.gather[self.rank * ms:(self.rank + 1) * ms].copy_(self.local)
+
+    def run(self, mode="overlap", order=None, rs_order=None, stream=None):
+        stream = stream or torch.cuda.current_stream(self.device)
+        peers = [p if p is not None else 0 for p in self.peers]
+        rs_peers = [p if p is not None else 0 for p in self.rs_peers]
+        B.ffn_chain(self.ctx, self.world, self.rank, self.m_shard, self.k1, self.n1, self.n2,
+                    self.chunk_rows, self.rs_chunk_rows, peers, self.gather, self.flags, self.w1,
+                    self.h, self.w2, self.send, self.send_flags, rs_peers, self.recv,
+                    self.rs_flags, self.out, order=order, rs_order=rs_order, mode=mode,
+                    stream=stream, copy_stream=self.copy_stream)
+
+    def status(self):
+        return B.agg_ctx_status(self.ctx, torch.cuda.current_stream(self.device))
+
+    def close(self):
+        if self.ctx is not None:
+            B.agg_ctx_destroy(self.ctx)
+            self.ctx = None

@@ -331,6 +331,38 @@ int gemm_ar(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, int64_t k, 
             const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
             agg_stream stream, agg_stream copy_stream);
 
+/* ---- The FFN chain: AllGather+GEMM -> SiLU -> GEMM+ReduceScatter ------------------------- */
+
+/* One rank's share of a tensor-parallel FFN built from the two overlapped operations, run as one
+ * persistent kernel over a task graph (page "Triton-distributed is turning communication into
+ * compiler territory", section "DITRON adds three levels of tiling": task-level tiles scheduled
+ * in one persistent kernel; section "The performance case has a narrow, useful boundary": the
+ * FFN module on AMD GPUs). M = world * m_shard.
+ *   phase 1  h = silu(concat(shards) @ W1): AllGather+GEMM tiles (as ag_gemm: chunk flags, arrival
+ *            order) whose epilogue applies x * sigmoid(x) in fp32 and stores bf16
+ *   phase 2  y = h @ W2 in fp32, reduce-scattered over row blocks of m_shard rows (as gemm_rs)
+ * A phase-2 tile starts once every phase-1 tile of its rows has stored its part of h; both phases'
+ * tiles are claimed from one ordered list, so a tile only ever waits for tiles claimed before it.
+ *   k1, n1, n2       W1 is k1 x n1, W2 is n1 x n2 (bf16, N contiguous)
+ *   chunk_rows       rows per gather chunk (divides m_shard); order/n_order: gather arrival order
+ *   rs_chunk_rows    rows per receive chunk (divides m_shard); rs_order/n_rs_order: their order
+ *   peer_src, gather, flags       as ag_gemm's (the activations' shards)
+ *   h                device (M x n1) bf16: phase 1's output, phase 2's input
+ *   send, send_flags, rs_peer_src, recv, rs_flags, out   as gemm_rs's (m = M, n = n2, k = n1)
+ *   mode, streams    as ag_gemm; the producer copies both layers' chunks (gather chunks first)
+ * Errors: those of ag_gemm and gemm_rs on their halves; AGG_E_UNSUPPORTED beyond 2048 chunks per
+ * layer. agg_ctx_set_chain_fused(ctx, 0) runs the same tiles as two launches, all of phase 1 then
+ * all of phase 2 (the unfused baseline; results identical). */
+int ffn_chain(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t k1, int64_t n1, int64_t n2,
+              int chunk_rows, int rs_chunk_rows, const void* const* peer_src, void* gather,
+              uint32_t* flags, const void* w1, void* h, const void* w2, float* send,
+              uint32_t* send_flags, const float* const* rs_peer_src, float* recv, uint32_t* rs_flags,
+              float* out, const int32_t* order, int n_order, const int32_t* rs_order, int n_rs_order,
+              int mode, agg_stream stream, agg_stream copy_stream);
+
+/* Whether later ffn_chain calls run both phases in one launch (on, the default) or in two. */
+int agg_ctx_set_chain_fused(agg_ctx* ctx, int on);
+
 /* ---- host-only planning (no device needed; used by the calls above) --------------------- */
 
 /* The tile shape the library uses for a call: *bm x *bn output tiles.

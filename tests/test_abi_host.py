@@ -122,6 +122,8 @@ def test_tile_shapes_for_the_workloads(lib):
     sizes allow)."""
     got = {}
     for name, cfg in configs.CONFIGS.items():
+        if cfg.op == "ffn":
+            continue                       # the chain's kernel is instantiated for 256 x 256 only
         op = {"ag": 0, "rs": 1, "ar": 2}[cfg.op]
         got[name] = B.agg_tile_shape(op, cfg.dtype, cfg.m, cfg.n, cfg.k)
     assert got["ag_w8_4096x3584x8192_bf16"] == (256, 224)     # 16 x 16 = 256 tiles
