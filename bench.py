@@ -14,6 +14,12 @@ t_*_us fields are the modes timed one after another, which the board's clock dri
 dominant kernel's roofline (its own duration from timing events on the stream it runs on), and
 the CPU oracle's rate on the same workload as a baseline.
 
+`configs` holds one block per workload (the two AllGather+GEMM sizes, ReduceScatter, decode, fp8,
+decode GEMM+AllReduce, the FFN chain): the same four modes interleaved call by call, each call
+preceded (outside its timed span) by a 512 MiB write that evicts the caches, so every byte comes
+from HBM; R, eta and the roofline of the bare and the overlapped kernel against the bound that
+applies (MFMA bf16 or fp8, HBM bytes, or launch latency).
+
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 
@@ -35,6 +41,15 @@ PEAK_FP8_TFLOPS = 5033.2
 PEAK_HBM_GBS = 8000.0
 # counter records (profiles/traffic_<record>.txt) of each workload's overlapped launch
 TRAFFIC_RECORDS = {"ag_w8_4096x3584x8192_bf16": "gemm_kernel_256x224_bf16_ag_w8_4096x3584x8192_overlap"}
+# what bounds each workload's kernel: MFMA (flops against the dtype's peak), HBM (bytes against
+# 8 TB/s) or launch latency (a handful of tiles on 256 CUs)
+BOUND = {"ag_w2_256x256x512_bf16": "latency", "ag_w8_4096x3584x8192_bf16": "mfma",
+         "rs_w8_8192x8192x3584_bf16": "mfma", "ag_w8_128x3584x8192_bf16_decode": "hbm",
+         "ag_w8_8192x7168x8192_fp8": "mfma", "ar_w8_128x8192x3584_bf16_decode": "hbm",
+         "ffn_w8_4096x8192x3584_bf16": "mfma"}
+# workloads where pulling remote rows is possible: also timed with pull off (flag-gated push)
+PULL_VARIANTS = {"ag_w2_256x256x512_bf16", "ag_w8_128x3584x8192_bf16_decode"}
+FLUSH_BYTES = 512 << 20
 
 
 def parse():
@@ -48,6 +63,14 @@ def parse():
                     help="modes to time; the overlapped steps always run (profiling runs use"
                          " 'overlap' alone so that every consumer-kernel launch is a timed step);"
                          " 'sdma' also times the overlap with the copy-engine producer")
+    ap.add_argument("--configs", default="all",
+                    help="per-workload blocks to measure: 'all', 'none', or a comma list of names")
+    ap.add_argument("--config-reps", type=int, default=20, help="interleaved calls per mode per block")
+    ap.add_argument("--block-modes", default="all",
+                    help="profiling: the variants a block times ('all' or a comma list such as"
+                         " 'gemm_only,overlap')")
+    ap.add_argument("--skip-headline", action="store_true",
+                    help="profiling: time only the blocks and print them (not a benchmark line)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before the timed steps, run one plain device copy of this many MiB (a"
                          " known-size kernel that HBM byte counters are scaled against)")
@@ -108,6 +131,171 @@ def cpu_baseline(cfg, data):
                       f" exact decode + float64 matmul, {dt:.2f} s"}
 
 
+def rnd(x, d=1):
+    return None if x is None else round(x, d)
+
+
+# ------------------------------------------------------------------------ per-workload blocks
+
+def make_workload(name):
+    """(cfg, workload object, algorithmic bytes of the bare kernel, bytes the copy moves)."""
+    from allgather_gemm_persistent_amd import configs
+    from allgather_gemm_persistent_amd.workload import AgWorkload, ArWorkload, FfnWorkload, RsWorkload
+    cfg = configs.CONFIGS[name]
+    if cfg.op == "ag":
+        d = configs.make_ag_data(cfg)
+        w = AgWorkload(cfg.world, cfg.rank, d["shards"], d["b"], cfg.chunk_rows, cfg.dtype,
+                       d["scale_a"], d["scale_b"])
+        el = 1 if cfg.dtype == "fp8" else 2
+        bare = cfg.m * cfg.k * el + cfg.k * cfg.n * el + cfg.m * cfg.n * 2
+        copy = (cfg.world - 1) * cfg.m_shard * cfg.k * el
+    elif cfg.op == "rs":
+        d = configs.make_rs_data(cfg)
+        w = RsWorkload(cfg.world, cfg.rank, d["a"], d["b"], d["peers"], cfg.chunk_rows)
+        mb = cfg.m_block
+        # A, B, the sent partial blocks, the incoming blocks read, the reduced block written
+        bare = cfg.m * cfg.k * 2 + cfg.k * cfg.n * 2 + (cfg.world - 1) * mb * cfg.n * 4 * 2 + mb * cfg.n * 4
+        copy = (cfg.world - 1) * mb * cfg.n * 4
+    elif cfg.op == "ar":
+        d = configs.make_ar_data(cfg)
+        w = ArWorkload(cfg.world, cfg.rank, d["a"], d["b"], d["peers"], cfg.chunk_rows)
+        # A, B, the partial sent, the incoming partials read, the reduced output written
+        bare = cfg.m * cfg.k * 2 + cfg.k * cfg.n * 2 + cfg.m * cfg.n * 4 * (cfg.world - 1 + 2)
+        copy = (cfg.world - 1) * cfg.m * cfg.n * 4
+    elif cfg.op == "ffn":
+        d = configs.make_ffn_data(cfg)
+        w = FfnWorkload(cfg.world, cfg.rank, d["shards"], d["w1"], d["w2"], d["peers"], cfg.chunk_rows,
+                        cfg.rs_chunk_rows)
+        m, mb = cfg.m, cfg.m_shard
+        # X, W1, h written and read, W2, the sent blocks, the incoming blocks read, the reduced block
+        bare = (m * cfg.k1 * 2 + cfg.k1 * cfg.n1 * 2 + 2 * m * cfg.n1 * 2 + cfg.n1 * cfg.n2 * 2
+                + (cfg.world - 1) * mb * cfg.n2 * 4 * 2 + mb * cfg.n2 * 4)
+        copy = (cfg.world - 1) * mb * (cfg.k1 * 2 + cfg.n2 * 4)
+    else:
+        raise ValueError(cfg.op)
+    return cfg, w, bare, copy
+
+
+def measure_block(name, reps, flush, only="all"):
+    """Interleaved, cache-flushed timing of one workload's modes; returns the JSON block."""
+    import torch
+
+    from allgather_gemm_persistent_amd import binding as B
+    cfg, w, bare_bytes, copy_bytes = make_workload(name)
+    ffn = cfg.op == "ffn"
+    # (label, mode, pull setting or chain fusion, timed kernel launches per call)
+    variants = [("overlap", "overlap", "auto", 1), ("gemm_only", "gemm_only", "auto", 1),
+                ("copy_only", "copy_only", "auto", 1), ("serial", "serial", "auto", 1)]
+    if name in PULL_VARIANTS:
+        variants.append(("overlap_push", "overlap", "off", 1))
+    if ffn:
+        variants.append(("overlap_unfused", "overlap", "unfused", 2))
+        variants.append(("gemm_only_unfused", "gemm_only", "unfused", 2))
+    if only != "all":
+        variants = [v for v in variants if v[0] in only.split(",")]
+    has_pull = cfg.op == "ag"
+
+    def setup(setting):
+        if has_pull:
+            B.agg_ctx_set_pull(w.ctx, setting)
+        if ffn:
+            B.agg_ctx_set_chain_fused(w.ctx, setting != "unfused")
+
+    def run(mode):
+        if ffn:
+            w.run(mode, order=cfg.order(), rs_order=cfg.rs_order())
+        else:
+            w.run(mode, order=cfg.order())
+    stream = torch.cuda.current_stream()
+    try:
+        for _ in range(3):                               # warm-up of every variant
+            for _, mode, setting, _ in variants:
+                setup(setting)
+                run(mode)
+        torch.cuda.synchronize()
+        B.agg_ctx_set_timing(w.ctx, True)
+        ev, seq = [], []
+        for i in range(reps):
+            for label, mode, setting, launches in variants:
+                setup(setting)
+                flush(i)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                run(mode)
+                e1.record(stream)
+                ev.append((label, e0, e1))
+                seq.extend([label] * launches)           # the timed kernel launches of the call
+        torch.cuda.synchronize()
+        st = w.status()
+        if st[0]:
+            raise RuntimeError(f"{name}: a chunk wait gave up (flag {st[1]})")
+        ks = B.agg_ctx_kernel_times(w.ctx, 256)
+        ks = ks[len(ks) - len(seq):] if len(seq) <= 256 else None
+        if ffn:
+            bm, bn = 256, 256
+        else:
+            bm, bn = B.agg_tile_shape({"ag": 0, "rs": 1, "ar": 2}[cfg.op], cfg.dtype, cfg.m, cfg.n, cfg.k)
+    finally:
+        B.agg_ctx_set_timing(w.ctx, False)
+        w.close()
+    labels = [v[0] for v in variants]
+    call = {lb: statistics.median([a.elapsed_time(b) * 1e3 for q, a, b in ev if q == lb]) for lb in labels}
+    if only != "all":
+        return {"call_us": call, "kernel_us": None}
+    # kernel time per call: the sum of its launches (the ring keeps the last 256 launches)
+    kern = {}
+    if ks is not None:
+        per_call, i = [], 0
+        for label, _, _, launches in [v for _ in range(reps) for v in variants]:
+            per_call.append((label, sum(ks[i:i + launches])))
+            i += launches
+        kern = {lb: statistics.median([k * 1e3 for q, k in per_call if q == lb]) for lb in labels}
+    R = call["overlap"] / call["gemm_only"]
+    eta = (call["serial"] - call["overlap"]) / min(call["copy_only"], call["gemm_only"])
+    bound = BOUND[name]
+    flops = cfg.flops
+
+    def roof(kernel_us, bytes_):
+        if bound == "mfma":
+            peak = PEAK_FP8_TFLOPS if cfg.dtype == "fp8" else PEAK_BF16_TFLOPS
+            a = flops / (kernel_us * 1e-6) / 1e12
+            return {"bound": "mfma", "achieved": rnd(a), "peak": peak, "unit": "TFLOP/s", "frac": rnd(a / peak, 4)}
+        if bound == "hbm":
+            a = bytes_ / (kernel_us * 1e-6) / 1e9
+            return {"bound": "hbm", "achieved": rnd(a), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": rnd(a / PEAK_HBM_GBS, 4), "bytes": bytes_}
+        return {"bound": "latency", "achieved": rnd(kernel_us, 2), "peak": None, "unit": "us", "frac": None}
+
+    block = {
+        "op": cfg.op, "dtype": cfg.dtype, "m": cfg.m,
+        **({"k1": cfg.k1, "n1": cfg.n1, "n2": cfg.n2} if ffn else {"n": cfg.n, "k": cfg.k}),
+        "world": cfg.world, "chunk_rows": cfg.chunk_rows, "tile": [bm, bn], "reps": reps,
+        "cache_flushed": True,
+        "call_us": {lb: rnd(v, 2) for lb, v in call.items()},
+        "kernel_us": {lb: rnd(v, 2) for lb, v in kern.items()},
+        "R": rnd(R, 3), "eta": rnd(eta, 3),
+        "tflops_overlap": rnd(flops / (call["overlap"] * 1e-6) / 1e12, 2),
+        "roofline_bare": roof(kern["gemm_only"], bare_bytes) if kern else None,
+        # the overlapped launch also reads every remote chunk from its peer and writes it into
+        # the symmetric buffer (CU producer)
+        "roofline_overlap": roof(kern["overlap"], bare_bytes + 2 * copy_bytes) if kern else None,
+    }
+    if ffn:
+        block["fusion_speedup"] = rnd(call["overlap_unfused"] / call["overlap"], 3)
+        block["fusion_speedup_bare"] = rnd(call["gemm_only_unfused"] / call["gemm_only"], 3)
+        block["note"] = ("overlap / gemm_only: both layers in one launch over the tile dependency graph;"
+                         " *_unfused: the same tiles as two launches (all of layer 1, then all of"
+                         " layer 2); fusion_speedup = unfused / fused call time")
+    if "overlap_push" in call:
+        block["R_push"] = rnd(call["overlap_push"] / call["gemm_only"], 3)
+        block["roofline_overlap_push"] = roof(kern["overlap_push"], bare_bytes + 2 * copy_bytes)
+        block["note"] = ("overlap = the automatic choice (pulled: tiles read remote rows from the peers'"
+                         " blocks, which on one GPU cost nothing like a link); overlap_push = every"
+                         " remote tile waits for its chunks' flags")
+    return block
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -120,9 +308,16 @@ def main():
     from allgather_gemm_persistent_amd import configs
     from allgather_gemm_persistent_amd.workload import AgWorkload
 
+    if args.skip_headline:
+        torch.cuda.set_stream(torch.cuda.Stream())
+        flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        out = {n: measure_block(n, args.config_reps, lambda i: flush_buf.fill_(i & 0xFF), args.block_modes)
+               for n in args.configs.split(",")}
+        print(json.dumps(out), flush=True)
+        return
     name = args.workload or configs.HEADLINE
     cfg = configs.CONFIGS[name]
-    assert cfg.op == "ag", "the benchmark measures AllGather+GEMM workloads"
+    assert cfg.op == "ag", "the headline measures AllGather+GEMM workloads"
     data = configs.make_ag_data(cfg)
     w = AgWorkload(cfg.world, cfg.rank, data["shards"], data["b"], cfg.chunk_rows, cfg.dtype,
                    data["scale_a"], data["scale_b"])
@@ -202,12 +397,24 @@ def main():
         B.agg_ctx_set_timing(w.ctx, False)
         w.close()
 
+    # per-workload blocks, each call after a cache-evicting write
+    blocks = {}
+    if args.configs != "none":
+        names = list(BOUND) if args.configs == "all" else args.configs.split(",")
+        names = [n for n in names if n in configs.CONFIGS]
+        flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+
+        def flush(i):
+            flush_buf.fill_(i & 0xFF)
+        for n in names:
+            blocks[n] = measure_block(n, args.config_reps, flush, args.block_modes)
+            print(f"block {n}: R {blocks[n]['R']} bare {blocks[n]['kernel_us']['gemm_only']} us",
+                  file=sys.stderr, flush=True)
+        del flush_buf
+
     flops = cfg.flops
     value = flops / (t_ovl * 1e-6) / 1e12
     achieved = flops / (k_ovl_us * 1e-6) / 1e12
-
-    def rnd(x, d=1):
-        return None if x is None else round(x, d)
     # R and eta from the interleaved per-call times (same clock for every mode)
     R = eta = None
     if s_int and "gemm_only" in s_int:
@@ -248,14 +455,16 @@ def main():
                     f"t_ovl_{other}_producer_us": rnd(t_ovl_other),
                     f"R_{other}_producer": rnd(t_ovl_other / t_gemm, 3)
                     if (t_ovl_other and t_gemm) else None},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+        "roofline": {"bound": BOUND.get(name, "mfma"), "achieved": round(achieved, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(TRAFFIC_RECORDS.get(name, "")),
                      "traffic_unit": "bytes per launch",
                      "kernel": "agg::gemm_kernel (overlap launch)",
                      "kernel_us": round(k_ovl_us, 1),
+                     "warm_caches": True,
                      "gemm_only_frac": rnd(flops / (k_gemm_us * 1e-6) / 1e12 / peak, 4)
                      if k_gemm_us else None},
+        "configs": blocks,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, data)
