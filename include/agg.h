@@ -23,6 +23,9 @@
  *    chunk on side streams; while chunks are in flight the kernel leaves a few CUs free for the
  *    runtime's own helper kernels (agg_ctx_set_reserved_cus).
  *
+ * Each declaration below names the passage it implements: "section ..." refers to a section of the
+ * page "Triton-distributed is turning communication into compiler territory" (cronfeed.work).
+ *
  * Conventions (every entry point):
  *  - Returns AGG_OK (0) or an AGG_E_* code; agg_last_error() then holds a text for the
  *    calling thread. No C++ exception crosses this boundary.
@@ -82,39 +85,63 @@ enum agg_mode {
 
 /* ---- context -------------------------------------------------------------------------- */
 
-/* Create a ctx on HIP device `device`. Allocates the ctx's device scratch (tile counters,
- * status word, ReduceScatter completion counters, 16.6 KiB) and creates its kernel stream.
- * AGG_E_UNSUPPORTED unless the device's architecture is gfx950. */
+/* Create a ctx on HIP device `device`. Allocates the ctx's device scratch (claim counters, status
+ * word, completion counters and the tables the kernel reads, 78 KiB) and pinned host staging for
+ * those tables, creates its kernel stream, and, for the first ctx on a device, finds and clears
+ * that device's static scratch (ag_gemm_noalloc). AGG_E_UNSUPPORTED unless the device's
+ * architecture is gfx950.
+ * Passage: section "The first move was to expose the overlap": symmetric memory and signaling as
+ *  the building blocks; the ctx holds the signaling state (epoch, counters) of the calls.
+ */
 int agg_ctx_create(int device, agg_ctx** out);
 
-/* Free the ctx (synchronises the device first). NULL is accepted. */
+/* Free the ctx (synchronises the device first). NULL is accepted.
+ * Passage: section "The first move was to expose the overlap" (the ctx's signaling state).
+ */
 int agg_ctx_destroy(agg_ctx* ctx);
 
 /* After AGG_E_TIMEOUT, or before passing different flags buffers: synchronises the device,
  * zero-fills the flags buffers bound to the ctx (they must still be allocated), unbinds them,
- * clears counters and status, and restarts the epoch at 0. */
+ * clears counters and status, and restarts the epoch at 0.
+ * Passage: section "The first move was to expose the overlap" (signaling); recovery after an
+ *  abandoned wait is this library's own, the pages describe none.
+ */
 int agg_ctx_reset(agg_ctx* ctx, agg_stream stream);
 
 /* Synchronise `stream` and read the ctx's device status: *status = 0 when no wait gave up,
  * else bit 0 set; *failed_chunk = the first flag index whose wait gave up, or -1.
- * Returns AGG_E_TIMEOUT when status != 0. Either output pointer may be NULL. */
+ * Returns AGG_E_TIMEOUT when status != 0. Either output pointer may be NULL.
+ * Passage: section "DITRON adds three levels of tiling" (synchronization inserted between chunks
+ *  and tiles: the status of those waits).
+ */
 int agg_ctx_status(agg_ctx* ctx, agg_stream stream, uint32_t* status, int32_t* failed_chunk);
 
-/* Current epoch: the value the last producing call wrote into its flags (0 before any). */
+/* Current epoch: the value the last producing call wrote into its flags (0 before any).
+ * Passage: section "The first move was to expose the overlap" (signaling: a flag carries the epoch
+ *  of the call that delivered its chunk).
+ */
 int agg_ctx_epoch(agg_ctx* ctx, uint32_t* epoch);
 
 /* Move the epoch (tests of the wrap-around): the next producing call uses epoch+1. Epochs run
  * 1 .. 0xFFFFFFFE; past the end the ctx zero-fills its bound flags and restarts at 1.
- * Requires no bound flags buffer (fresh ctx or after agg_ctx_reset); AGG_E_STATE otherwise. */
+ * Requires no bound flags buffer (fresh ctx or after agg_ctx_reset); AGG_E_STATE otherwise.
+ * Passage: section "The first move was to expose the overlap" (signaling: epoch-tagged flags).
+ */
 int agg_ctx_set_epoch(agg_ctx* ctx, uint32_t epoch);
 
 /* Device-side wait limit in microseconds (default 2,000,000). A wait that runs past it sets
- * the status word and abandons its tile; later waits of the same call give up at once. */
+ * the status word and abandons its tile; later waits of the same call give up at once.
+ * Passage: section "DITRON adds three levels of tiling" (synchronization inserted); the bound on a
+ *  wait is this library's own.
+ */
 int agg_ctx_set_timeout_us(agg_ctx* ctx, uint64_t timeout_us);
 
 /* Number of copy streams the producer spreads chunks over (1..8, default 4), all created by
  * the ctx with hardware queues of their own. Chunk i of the arrival order goes to stream i mod n,
- * so every stream keeps the arrival order and the SDMA engines work in parallel. */
+ * so every stream keeps the arrival order and the SDMA engines work in parallel.
+ * Passage: section "DITRON adds three levels of tiling" (device-level tiles are data movements on
+ *  DMA engines).
+ */
 int agg_ctx_set_copy_streams(agg_ctx* ctx, int n);
 
 /* Producer kinds. */
@@ -130,7 +157,10 @@ enum {
  * copying workgroups; a chunk is cut into ceil(chunk bytes / piece) pieces), in arrival order, and only then
  * claim tiles; the workgroup that completes a chunk's last piece releases its flag. The other
  * arguments are ignored for AGG_PRODUCER_SDMA. AGG_E_ARG for an unknown kind or a negative
- * count. */
+ * count.
+ * Passage: section "The first move was to expose the overlap" (remote data access and signaling)
+ *  and section "DITRON adds three levels of tiling" (device-level tiles on DMA engines).
+ */
 int agg_ctx_set_producer(agg_ctx* ctx, int kind, int copy_wgs, int piece_kib);
 
 /* Pull modes of ag_gemm (AGG_OVERLAP calls under AGG_PRODUCER_CU without delays). */
@@ -149,16 +179,25 @@ enum {
  * than compute units leave room for the copiers;
  * otherwise the call pushes. Results are identical either way. The pages' overlap puts a
  * chunk's transfer before its tiles; pulling takes that transfer off the tiles' path for small
- * gathers, whose cost is latency rather than bandwidth. AGG_E_ARG for an unknown mode. */
+ * gathers, whose cost is latency rather than bandwidth. AGG_E_ARG for an unknown mode.
+ * Passage: section "The first move was to expose the overlap" (remote data access; compute on
+ *  arrived data while the rest moves).
+ */
 int agg_ctx_set_pull(agg_ctx* ctx, int pull);
 
 /* CUs the persistent grid leaves free in AGG_OVERLAP mode (default 32, four per XCD), where
  * the producer's copies and flag writes must run beside it: in the HIP runtime shipped with
- * torch several of them execute as runtime kernels and need a CU. 0..CUs-1. */
+ * torch several of them execute as runtime kernels and need a CU. 0..CUs-1.
+ * Passage: section "DITRON adds three levels of tiling" (data movements on DMA engines beside the
+ *  compute tiles).
+ */
 int agg_ctx_set_reserved_cus(agg_ctx* ctx, int n);
 
 /* Force the output tile shape (bm x bn) of later calls; 0, 0 restores the automatic choice.
- * Shapes: 256x256, 256x224, 128x128, 128x64, 64x64; anything else is AGG_E_ARG. */
+ * Shapes: 256x256, 256x224, 128x128, 128x64, 64x64; anything else is AGG_E_ARG.
+ * Passage: section "DITRON adds three levels of tiling" (core-level tiles in registers, shared
+ *  memory and matrix units).
+ */
 int agg_ctx_set_tile(agg_ctx* ctx, int bm, int bn);
 
 /* Split-K of later AllGather+GEMM calls. With few output tiles (fewer than half the CUs) and a
@@ -170,7 +209,9 @@ int agg_ctx_set_tile(agg_ctx* ctx, int bm, int bn);
  * tiles of up to 128 x 128 (larger tiles are never split); parts span a whole number of 64-byte
  * K slice pairs, so fewer parts may result (at most one per pair). 0 restores the automatic
  * choice. A chunk wait that times out leaves split-K tile counters behind: call agg_ctx_reset
- * before the next call. */
+ * before the next call.
+ * Passage: section "DITRON adds three levels of tiling" (core-level tiles).
+ */
 int agg_ctx_set_split(agg_ctx* ctx, int ksplit);
 
 /* Tile-claim lists of later calls. The persistent workgroups claim tiles from `lists` lists
@@ -178,13 +219,19 @@ int agg_ctx_set_split(agg_ctx* ctx, int ksplit);
  * stealing from the others when that is empty). The lists form a (lists / list_cols) x list_cols
  * grid over the output: row tiles dealt round-robin in compute order to the grid rows, column
  * tiles in list_cols contiguous blocks, so the tiles in flight on one XCD share A rows and B
- * columns in its L2. list_cols must divide lists; 0 picks it per call from the tile counts. */
+ * columns in its L2. list_cols must divide lists; 0 picks it per call from the tile counts.
+ * Passage: section "DITRON adds three levels of tiling" (collectives cut into chunks paired with
+ *  computation tiles: the order tiles are taken in).
+ */
 int agg_ctx_set_lists(agg_ctx* ctx, int lists, int list_cols);
 
 /* Kernel timing: with timing on, each call brackets its consumer kernel with a pair of timing
  * events on the kernel's own stream (a ring of the last 256 launches; switching it on clears
  * the ring). agg_ctx_kernel_times waits for and returns the durations in milliseconds of the
- * last min(max, recorded) launches, oldest first, in ms[0..*n). */
+ * last min(max, recorded) launches, oldest first, in ms[0..*n).
+ * Passage: section "What would prove the compiler layer is portable" (measurements disclosed with
+ *  the numerical checks).
+ */
 int agg_ctx_set_timing(agg_ctx* ctx, int on);
 int agg_ctx_kernel_times(agg_ctx* ctx, float* ms, int max, int* n);
 
@@ -192,21 +239,30 @@ int agg_ctx_kernel_times(agg_ctx* ctx, float* ms, int max, int* n);
  * `bytes` >= 32 * tiles bytes; each computed tile (m-tile i, n-tile j) writes the 8 words
  * agg_trace_rec at index i * n_tiles + j: claim list, position in that list, XCD id of the
  * claiming workgroup, minimum flag value it observed (0xFFFFFFFF if it needed none), visit
- * count (atomic increment), and the three 100 MHz timestamps: claimed, flags seen, done. */
+ * count (atomic increment), and the three 100 MHz timestamps: claimed, flags seen, done.
+ * Passage: section "DITRON adds three levels of tiling" (synchronization inserted: each tile's
+ *  claim and flag observation).
+ */
 int agg_set_trace(agg_ctx* ctx, void* dev_buf, size_t bytes);
 
 typedef struct agg_trace_rec {
   uint32_t list, pos, xcd, min_flag, visits, t_claim, t_ready, t_done;
 } agg_trace_rec;
 
-/* Thread-local text describing the last non-OK return of this thread. */
+/* Thread-local text describing the last non-OK return of this thread.
+ * Passage: none (the library's error convention).
+ */
 const char* agg_last_error(void);
 
 /* ---- primitive: put with signal -------------------------------------------------------- */
 
 /* Enqueue on copy_stream: copy `bytes` from src to dst (hipMemcpyDeviceToDeviceNoCU), then
  * write `value` into *flag (4-byte aligned) with a stream write, so that stream order places the
- * flag after the data. This is the one-GPU form of the remote data access + signaling pair. */
+ * flag after the data. This is the one-GPU form of the remote data access + signaling pair.
+ * Passage: section "The first move was to expose the overlap" (remote data access followed by a
+ *  signal); the project page "Triton-distributed" (sourcepulse.org), "How It Works" (low-level
+ *  communication primitives).
+ */
 int agg_put_signal(void* dst, const void* src, size_t bytes, uint32_t* flag, uint32_t value,
                    agg_stream copy_stream);
 
@@ -246,7 +302,12 @@ int agg_put_signal(void* dst, const void* src, size_t bytes, uint32_t* flag, uin
  *                    copies themselves run on the ctx's own streams (agg_ctx_set_copy_streams)
  *                    or inside the kernel (AGG_PRODUCER_CU)
  * Alignment: k * elem, n * elem and n * 2 bytes multiples of 16 (rows of A, B and C), device
- * pointers 16-byte aligned. */
+ * pointers 16-byte aligned.
+ * Passage: section "The first move was to expose the overlap" (an AllGather moves shards into
+ *  place, a GEMM consumes them; cut into chunks, computation proceeds on arrived chunks) and
+ *  section "DITRON adds three levels of tiling" (chunks paired with computation tiles,
+ *  synchronization inserted).
+ */
 int ag_gemm(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64_t k,
             int chunk_rows, int dtype, float scale_a, float scale_b,
             const void* const* peer_src, void* gather, uint32_t* flags, const void* b, void* c,
@@ -293,7 +354,11 @@ int ag_gemm_noalloc(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t 
  *   order/n_order, delay_us, mode, streams: as for ag_gemm, over the (world-1)*Mb/cr incoming
  *   chunks. flags and send_flags are bound to the ctx like ag_gemm's flags; both end at the
  *   epoch everywhere, the local block's entries included (nothing arrives or leaves for them).
- * Alignment: k*2 and n*2 bytes multiples of 16; m a multiple of world; cr divides Mb. */
+ * Alignment: k*2 and n*2 bytes multiples of 16; m a multiple of world; cr divides Mb.
+ * Passage: section "The first move was to expose the overlap" (GEMM+ReduceScatter, reducing partial
+ *  results) and section "DITRON adds three levels of tiling" (ReduceScatter cut into chunks paired
+ *  with tiles).
+ */
 int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, int64_t k, int chunk_rows,
             const void* a, const void* b, float* send, uint32_t* send_flags,
             const float* const* peer_src, float* recv, uint32_t* flags, float* out,
@@ -360,18 +425,27 @@ int ffn_chain(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t k1, in
               float* out, const int32_t* order, int n_order, const int32_t* rs_order, int n_rs_order,
               int mode, agg_stream stream, agg_stream copy_stream);
 
-/* Whether later ffn_chain calls run both phases in one launch (on, the default) or in two. */
+/* Whether later ffn_chain calls run both phases in one launch (on, the default) or in two.
+ * Passage: section "DITRON adds three levels of tiling" (task-level tiles in one persistent kernel)
+ *  and section "The performance case has a narrow, useful boundary" (the FFN module).
+ */
 int agg_ctx_set_chain_fused(agg_ctx* ctx, int on);
 
 /* ---- host-only planning (no device needed; used by the calls above) --------------------- */
 
 /* The tile shape the library uses for a call: *bm x *bn output tiles.
- * op: 0 = ag_gemm, 1 = gemm_rs, 2 = gemm_ar. m is M (ag: world*m_shard). */
+ * op: 0 = ag_gemm, 1 = gemm_rs, 2 = gemm_ar. m is M (ag: world*m_shard).
+ * Passage: section "DITRON adds three levels of tiling" (core-level tiles).
+ */
 int agg_tile_shape(int op, int dtype, int64_t m, int64_t n, int64_t k, int* bm, int* bn);
 
 /* Row-tile order of ag_gemm: tiles of `bm` rows of C sorted by the arrival position of the
  * latest remote chunk they overlap (-1 when none), ties by tile index. Writes
- * ceil(world*m_shard/bm) entries to out_tiles (capacity max_tiles); *n_tiles = that count. */
+ * ceil(world*m_shard/bm) entries to out_tiles (capacity max_tiles); *n_tiles = that count.
+ * Passage: section "DITRON adds three levels of tiling" (chunks paired with computation tiles) and
+ *  section "The first move was to expose the overlap" (computation on the chunks that have
+ *  arrived).
+ */
 int agg_ag_row_tile_order(int world, int rank, int64_t m_shard, int chunk_rows,
                           const int32_t* order, int n_order, int bm, int32_t* out_tiles,
                           int max_tiles, int* n_tiles);
@@ -379,12 +453,17 @@ int agg_ag_row_tile_order(int world, int rank, int64_t m_shard, int chunk_rows,
 /* Row-tile order of gemm_rs as (block, tile-in-block) pairs flattened to block*tpb + tile,
  * tpb = ceil(Mb/bm): non-local blocks in send order rank+1, ..., rank+world-1 (mod world), each
  * ascending; then the local block's tiles by the arrival position of the latest incoming
- * chunk they need, ties by index. */
+ * chunk they need, ties by index.
+ * Passage: section "DITRON adds three levels of tiling" (chunks paired with computation tiles).
+ */
 int agg_rs_row_tile_order(int world, int rank, int64_t m, int chunk_rows, const int32_t* order,
                           int n_order, int bm, int32_t* out_tiles, int max_tiles, int* n_tiles);
 
 /* The argument checks ag_gemm / gemm_rs run first (pointers are checked for NULL and 16-byte
- * alignment only). AGG_OK or AGG_E_ARG / AGG_E_UNSUPPORTED with agg_last_error set. */
+ * alignment only). AGG_OK or AGG_E_ARG / AGG_E_UNSUPPORTED with agg_last_error set.
+ * Passage: the passages of ag_gemm, gemm_rs and gemm_ar, whose argument contracts these checks
+ *  enforce.
+ */
 int agg_check_ag_args(int world, int rank, int64_t m_shard, int64_t n, int64_t k, int chunk_rows,
                       int dtype, float scale_a, float scale_b, const void* const* peer_src,
                       const void* gather, const void* flags, const void* b, const void* c,
