@@ -48,6 +48,7 @@ _SIGNATURES = {
     "agg_ctx_set_split": [_vp, _c_int],
     "agg_ctx_set_pull": [_vp, _c_int],
     "agg_ctx_set_producer": [_vp, _c_int, _c_int, _c_int],
+    "agg_ctx_last_producer": [_vp, _i32p],
     "agg_set_trace": [_vp, _vp, _sz],
     "agg_ctx_set_timing": [_vp, _c_int],
     "agg_ctx_kernel_times": [_vp, ctypes.POINTER(ctypes.c_float), _c_int, ctypes.POINTER(_c_int)],
@@ -68,6 +69,7 @@ _SIGNATURES = {
                   ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_vp), _vp,
                   _vp, _vp, _i32p, _c_int, _i32p, _c_int, _c_int, _vp, _vp],
     "agg_ctx_set_chain_fused": [_vp, _c_int],
+    "agg_kernel_regs": [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)],
     "agg_tile_shape": [_c_int, _c_int, _c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_int),
                        ctypes.POINTER(_c_int)],
     "agg_ag_row_tile_order": [_c_int, _c_int, _c_i64, _c_int, _i32p, _c_int, _c_int, _i32p,
@@ -257,13 +259,22 @@ def agg_ctx_set_copy_streams(ctx, n: int) -> None:
     _call("agg_ctx_set_copy_streams", ctx, n)
 
 
-PRODUCERS = {"cu": 0, "sdma": 1}
+PRODUCERS = {"cu": 0, "sdma": 1, "kernel": 2}
 
 
 def agg_ctx_set_producer(ctx, kind="cu", copy_wgs: int = 0, piece_kib: int = 0) -> None:
-    """Producer of later calls: "cu" (copy jobs inside the persistent kernel) or "sdma"."""
+    """Producer of later calls: "cu" (copy jobs inside the persistent kernel), "sdma" (copy
+    engines) or "kernel" (a copy kernel beside the persistent kernel)."""
     _call("agg_ctx_set_producer", ctx, PRODUCERS[kind] if isinstance(kind, str) else int(kind),
           copy_wgs, piece_kib)
+
+
+def agg_ctx_last_producer(ctx):
+    """The producer the last call on `ctx` ran ("cu", "sdma", "kernel"), None before the first."""
+    v = _c_int(0)
+    _call("agg_ctx_last_producer", ctx, ctypes.byref(v))
+    names = {i: k for k, i in PRODUCERS.items()}
+    return names.get(v.value)
 
 
 PULL_MODES = {"auto": 0, "off": 1, "on": 2}
@@ -452,3 +463,10 @@ def agg_check_ar_args(world, rank, m, n, k, chunk_rows, a, b, send, send_flags, 
                                     _ptr(send_flags), _ptr_array(peer_src), _ptr(recv), _ptr(flags),
                                     _ptr(out), ordr, n_order, _mode(mode), _stream(stream),
                                     _stream(copy_stream))
+
+
+def agg_kernel_regs(op: int, dtype, bm: int, bn: int):
+    """(GEMM kernel registers per lane, copy kernel registers per lane) as the runtime reports them."""
+    g, c = _c_int(), _c_int()
+    _call("agg_kernel_regs", op, _dtype(dtype), bm, bn, ctypes.byref(g), ctypes.byref(c))
+    return g.value, c.value

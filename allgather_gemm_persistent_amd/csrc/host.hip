@@ -1,5 +1,5 @@
-// libagg host runtime: the ctx, the producer (put + signal without compute units) and the C entry
-// points ag_gemm / gemm_rs / agg_put_signal.
+// libagg host runtime: the ctx, the producers (put + signal) and the C entry points ag_gemm,
+// ag_gemm_noalloc, gemm_rs, gemm_ar, ffn_chain and agg_put_signal.
 //
 // Method: page "Triton-distributed is turning communication into compiler territory", section
 // "The first move was to expose the overlap": chunked transfers and computation proceed together
@@ -13,19 +13,21 @@
 // epoch into the chunk's flag word on the same stream, so stream order puts the flag after the
 // data.
 //
-// The producer needs a few free compute units. Measured under a grid that holds every wave slot
-// of every CU: in the HIP runtime that ships with torch, the stream write, memsets,
-// host-to-device copies and device-to-device copies below 64 KiB or from 1 MiB up all run as
-// runtime kernels and never start, so the consumer would wait for them forever (until its
-// timeout). In overlap mode the persistent grid therefore leaves `reserved_cus` CUs to the
-// producer (default 32, four per XCD: workgroups are dealt round-robin over the XCDs and one
-// fills a CU; 8 and 16 free CUs were measured to still starve it); every other mode uses all
-// CUs.
+// This producer needs a few free compute units. A kernel trace of it shows the chunk copies
+// (2 MiB each) on the copy engines, at about 51 GB/s per copy, but every stream write as a
+// runtime kernel (__amd_rocclr_streamOpsWrite), and memsets and host-to-device copies are
+// runtime kernels too. Under a grid that holds every CU those kernels never start, so the
+// consumer would wait for them until its timeout. In overlap mode the persistent grid therefore
+// leaves `reserved_cus` CUs to the producer (default 32, four per XCD: workgroups are dealt
+// round-robin over the XCDs and one fills a CU; 8 and 16 free CUs were measured to still starve
+// it); every other mode uses all CUs.
 //
 // The CU producer needs none of that: copy workgroups inside the persistent kernel take the chunk
 // copies as jobs (arrival order, a chunk cut into pieces), the workgroup that completes a chunk
 // releases its flag, and copy workgroups turn to tiles when the jobs run out. Its arrival order
-// and delays sit in the ctx scratch, uploaded only when they change.
+// and delays sit in the ctx scratch, uploaded only when they change. The kernel producer runs the
+// same jobs in a kernel of its own (one-wave workgroups) on one copy stream, resident beside the
+// persistent kernel where the registers allow it.
 //
 // Chunks are spread over several copy streams (chunk i of the arrival order on stream i mod S),
 // each stream feeding its own SDMA engine the way W-1 peers feed separate links; every stream
@@ -121,6 +123,7 @@ struct agg_ctx {
   float* ws = nullptr;                       // split-K partials (grown on demand)
   size_t ws_bytes = 0;
   int producer = AGG_PRODUCER_CU;
+  int last_producer = -1;        // the producer the last call ran (AGG_PRODUCER_*)
   int copy_wgs = 0;                          // 0: every workgroup takes copy jobs first
   int pull = AGG_PULL_AUTO;                  // AllGather+GEMM pull mode (overlapped CU calls)
   int64_t piece_bytes = 0;                   // 0: chosen per call
@@ -522,6 +525,36 @@ int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int
   return AGG_OK;
 }
 
+// The producer a call runs: the ctx's choice, except that the copy kernel (AGG_PRODUCER_KERNEL)
+// gives way to copy jobs inside the GEMM kernel where it cannot run beside it (the GEMM kernel
+// leaves it too few registers on a SIMD) or where delays are asked for.
+constexpr int kCopyGrid = 1024;           // copy-kernel workgroups (one wave each): one per SIMD
+int effective_producer(agg_ctx* ctx, TileShape ts, int dtype, int epi, bool delays) {
+  if (ctx->producer != AGG_PRODUCER_KERNEL) return ctx->producer;
+  if (delays) return AGG_PRODUCER_CU;
+  auto alloc = [](int r) { return (r + 7) / 8 * 8; };
+  const int g = kernel_regs(ts.bm, ts.bn, dtype, epi), c = copy_kernel_regs();
+  if (g < 0 || c < 0 || alloc(g) + alloc(c) > 512) return AGG_PRODUCER_CU;
+  return AGG_PRODUCER_KERNEL;
+}
+
+// Enqueue the copy kernel for `plans` on `cs` (the producer as a kernel of its own).
+int launch_copy_producer(agg_ctx* ctx, uint32_t* scratch, const CopyPlan* plans, int nsets, int world,
+                         uint32_t epoch, const Marks& marks, hipStream_t cs) {
+  GemmArgs gc;
+  std::memset(&gc, 0, sizeof gc);
+  gc.scratch = scratch;
+  gc.epoch = epoch;
+  // pieces sized for every copy-kernel workgroup (the CU producer's copy_wgs does not apply)
+  fill_copies(ctx, gc, plans, nsets, false, world, kCopyGrid, kCopyGrid);
+  for (int s = 0; s < 2; ++s) {
+    gc.mark_flags[s] = marks.copy_flags[s];
+    gc.mark_count[s] = marks.copy_flags[s] ? marks.copy_count[s] : 0;
+  }
+  HIP_TRY(launch_copy(gc, kCopyGrid, cs));
+  return AGG_OK;
+}
+
 // Stream choreography under the CU producer. Nothing runs beside the kernel, so it goes on the
 // caller's stream itself (no fork, no join, no second hardware queue):
 //   OVERLAP:   one launch (copy jobs, then tiles)
@@ -754,11 +787,19 @@ extern "C" int agg_ctx_set_tile(agg_ctx* ctx, int bm, int bn) {
 extern "C" int agg_ctx_set_producer(agg_ctx* ctx, int kind, int copy_wgs, int piece_kib) {
   clear_error();
   if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
-  if (kind != AGG_PRODUCER_CU && kind != AGG_PRODUCER_SDMA) return fail(AGG_E_ARG, "unknown producer kind %d", kind);
+  if (kind != AGG_PRODUCER_CU && kind != AGG_PRODUCER_SDMA && kind != AGG_PRODUCER_KERNEL)
+    return fail(AGG_E_ARG, "unknown producer kind %d", kind);
   if (copy_wgs < 0 || piece_kib < 0) return fail(AGG_E_ARG, "negative copy_wgs or piece_kib");
   ctx->producer = kind;
   ctx->copy_wgs = copy_wgs;
   ctx->piece_bytes = piece_kib > 0 ? int64_t(piece_kib) << 10 : 0;
+  return AGG_OK;
+}
+
+extern "C" int agg_ctx_last_producer(const agg_ctx* ctx, int* kind) {
+  clear_error();
+  if (!ctx || !kind) return fail(AGG_E_ARG, "ctx or kind is NULL");
+  *kind = ctx->last_producer;
   return AGG_OK;
 }
 
@@ -887,10 +928,12 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
   hipStream_t s = S(stream);
   const bool kernel = (mode != AGG_COPY_ONLY) && n > 0;
   const bool chunks = (mode != AGG_GEMM_ONLY) && world > 1;
-  const bool cu = ctx->producer == AGG_PRODUCER_CU;
+  const int prod = effective_producer(ctx, ts, dtype, kEpiAllGather, delay_us != nullptr);
+  ctx->last_producer = prod;
+  const bool cu = prod == AGG_PRODUCER_CU;
   std::vector<hipStream_t> cstreams;
   if (chunks && !cu)
-    if (int rc = copy_streams(ctx, ord.size(), cstreams)) return rc;
+    if (int rc = copy_streams(ctx, prod == AGG_PRODUCER_SDMA ? ord.size() : 1, cstreams)) return rc;
   uint32_t epoch = ctx->epoch;
   if (chunks)
     if (int rc = next_epoch(ctx, s, &epoch)) return rc;
@@ -948,7 +991,7 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
     g.epoch = world > 1 ? epoch : 0;
     g.scale = dtype == AGG_FP8_E4M3 ? scale_a * scale_b : 1.0f;
     tiles = int64_t(g.n_row_tiles) * g.n_col_tiles;
-    grid = grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks && !cu);
+    grid = grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks && prod == AGG_PRODUCER_SDMA);
     // every split part claims its workgroup at launch (no more parts than workgroups): the parts
     // of a tile can wait for each other and sum the tile together
     // (and only when the whole grid fits on the GPU at once, so that no part waits for a sibling
@@ -992,8 +1035,19 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
       return launch_gemm(g, ts.bm, ts.bn, dtype, kEpiAllGather, grid, ctx->ks);
     });
   };
-  return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
-                  [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams, rank); });
+  const CopyPlan kplan{cc, flags, ord.size()};
+  Marks kmarks;
+  if (world > 1) {
+    kmarks.copy_flags[0] = flags + size_t(rank) * cps;
+    kmarks.copy_count[0] = cps;
+  }
+  if (prod == AGG_PRODUCER_KERNEL && chunks)
+    if (int rc = upload_schedule(ctx, sp, s, ord, nullptr)) return rc;
+  return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks, [&]() -> int {
+    if (prod == AGG_PRODUCER_KERNEL)
+      return launch_copy_producer(ctx, sp.words, &kplan, 1, world, epoch, kmarks, cstreams[0]);
+    return produce(cc, flags, ord, delay_us, epoch, cstreams, rank);
+  });
 }
 
 }  // namespace
@@ -1044,10 +1098,12 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
   hipStream_t s = S(stream);
   const bool kernel = mode != AGG_COPY_ONLY;
   const bool chunks = (mode != AGG_GEMM_ONLY) && world > 1;
-  const bool cu = ctx->producer == AGG_PRODUCER_CU;
+  const int prod = effective_producer(ctx, ts, AGG_BF16, kEpiReduceScatter, delay_us != nullptr);
+  ctx->last_producer = prod;
+  const bool cu = prod == AGG_PRODUCER_CU;
   std::vector<hipStream_t> cstreams;
   if (chunks && !cu)
-    if (int rc = copy_streams(ctx, ord.size(), cstreams)) return rc;
+    if (int rc = copy_streams(ctx, prod == AGG_PRODUCER_SDMA ? ord.size() : 1, cstreams)) return rc;
   uint32_t epoch = ctx->epoch;
   if (chunks)
     if (int rc = next_epoch(ctx, s, &epoch)) return rc;
@@ -1092,7 +1148,7 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
     g.epoch = world > 1 ? epoch : 0;
     g.scale = 1.0f;
     tiles = int64_t(g.n_row_tiles) * g.n_col_tiles;
-    grid = grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks && !cu);
+    grid = grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks && prod == AGG_PRODUCER_SDMA);
     fill_common(ctx, g, ts, grid);
     attach_trace(ctx, g, tiles);
     if (world > 1) {
@@ -1124,8 +1180,19 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
       return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiReduceScatter, grid, ctx->ks);
     });
   };
-  return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
-                  [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams, rank); });
+  const CopyPlan kplan{cc, flags, ord.size()};
+  Marks kmarks;
+  if (world > 1) {
+    kmarks.copy_flags[0] = flags + size_t(rank) * cpb;
+    kmarks.copy_count[0] = cpb;
+  }
+  if (prod == AGG_PRODUCER_KERNEL && chunks)
+    if (int rc = upload_schedule(ctx, sp, s, ord, nullptr)) return rc;
+  return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks, [&]() -> int {
+    if (prod == AGG_PRODUCER_KERNEL)
+      return launch_copy_producer(ctx, sp.words, &kplan, 1, world, epoch, kmarks, cstreams[0]);
+    return produce(cc, flags, ord, delay_us, epoch, cstreams, rank);
+  });
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1154,10 +1221,12 @@ extern "C" int gemm_ar(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
   hipStream_t s = S(stream);
   const bool kernel = mode != AGG_COPY_ONLY;
   const bool chunks = (mode != AGG_GEMM_ONLY) && world > 1;
-  const bool cu = ctx->producer == AGG_PRODUCER_CU;
+  const int prod = effective_producer(ctx, ts, AGG_BF16, kEpiAllReduce, delay_us != nullptr);
+  ctx->last_producer = prod;
+  const bool cu = prod == AGG_PRODUCER_CU;
   std::vector<hipStream_t> cstreams;
   if (chunks && !cu)
-    if (int rc = copy_streams(ctx, ord.size(), cstreams)) return rc;
+    if (int rc = copy_streams(ctx, prod == AGG_PRODUCER_SDMA ? ord.size() : 1, cstreams)) return rc;
   uint32_t epoch = ctx->epoch;
   if (chunks)
     if (int rc = next_epoch(ctx, s, &epoch)) return rc;
@@ -1203,7 +1272,7 @@ extern "C" int gemm_ar(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
     g.epoch = world > 1 ? epoch : 0;
     g.scale = 1.0f;
     const int64_t tiles = int64_t(g.n_row_tiles) * g.n_col_tiles;
-    grid = grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks && !cu);
+    grid = grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks && prod == AGG_PRODUCER_SDMA);
     fill_common(ctx, g, ts, grid);
     attach_trace(ctx, g, tiles);
   }
@@ -1226,8 +1295,19 @@ extern "C" int gemm_ar(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
   auto launch = [&]() -> int {
     return timed_launch(ctx, [&]() { return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiAllReduce, grid, ctx->ks); });
   };
-  return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks,
-                  [&]() { return produce(cc, flags, ord, delay_us, epoch, cstreams, rank); });
+  const CopyPlan kplan{cc, flags, ord.size()};
+  Marks kmarks;
+  if (world > 1) {
+    kmarks.copy_flags[0] = flags + size_t(rank) * cpb;
+    kmarks.copy_count[0] = cpb;
+  }
+  if (prod == AGG_PRODUCER_KERNEL && chunks)
+    if (int rc = upload_schedule(ctx, sp, s, ord, nullptr)) return rc;
+  return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks, [&]() -> int {
+    if (prod == AGG_PRODUCER_KERNEL)
+      return launch_copy_producer(ctx, sp.words, &kplan, 1, world, epoch, kmarks, cstreams[0]);
+    return produce(cc, flags, ord, delay_us, epoch, cstreams, rank);
+  });
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1277,10 +1357,12 @@ extern "C" int ffn_chain(agg_ctx* ctx, int world, int rank, int64_t m_shard, int
   hipStream_t s = S(stream);
   const bool kernel = mode != AGG_COPY_ONLY;
   const bool chunks = (mode != AGG_GEMM_ONLY) && world > 1;
-  const bool cu = ctx->producer == AGG_PRODUCER_CU;
+  const int prod = effective_producer(ctx, ts, AGG_BF16, kEpiFfn, false);
+  ctx->last_producer = prod;
+  const bool cu = prod == AGG_PRODUCER_CU;
   std::vector<hipStream_t> cstreams;
   if (chunks && !cu)
-    if (int rc = copy_streams(ctx, ord.size() + ord2.size(), cstreams)) return rc;
+    if (int rc = copy_streams(ctx, prod == AGG_PRODUCER_SDMA ? ord.size() + ord2.size() : 1, cstreams)) return rc;
   uint32_t epoch = ctx->epoch;
   if (chunks)
     if (int rc = next_epoch(ctx, s, &epoch)) return rc;
@@ -1345,7 +1427,7 @@ extern "C" int ffn_chain(agg_ctx* ctx, int world, int rank, int64_t m_shard, int
     g.list_cols = 1;
     g.timeout_ticks = uint64_t(double(ctx->timeout_us) * ctx->ticks_per_us);
     const int64_t tasks = int64_t(g.n_row_tiles1) * g.n_col_tiles1 + int64_t(g.n_row_tiles) * g.n_col_tiles;
-    grid = grid_for(ctx, tasks, mode == AGG_OVERLAP && chunks && !cu);
+    grid = grid_for(ctx, tasks, mode == AGG_OVERLAP && chunks && prod == AGG_PRODUCER_SDMA);
     if (world > 1) {
       g.mark_flags[2] = send_flags + size_t(rank) * cpb;   // nothing is sent for the local block
       g.mark_count[2] = cpb;
@@ -1393,8 +1475,37 @@ extern "C" int ffn_chain(agg_ctx* ctx, int world, int rank, int64_t m_shard, int
       return timed_launch(ctx, [&]() { return launch_gemm(gg, ts.bm, ts.bn, AGG_BF16, kEpiFfn, grid, ctx->ks); });
     });
   };
+  Marks kmarks;
+  if (world > 1) {
+    kmarks.copy_flags[0] = flags + size_t(rank) * cps;
+    kmarks.copy_count[0] = cps;
+    kmarks.copy_flags[1] = rs_flags + size_t(rank) * cpb;
+    kmarks.copy_count[1] = cpb;
+  }
+  if (prod == AGG_PRODUCER_KERNEL && chunks) {
+    std::vector<int32_t> both(ord);
+    both.insert(both.end(), ord2.begin(), ord2.end());
+    if (int rc = upload_schedule(ctx, sp, s, both, nullptr)) return rc;
+  }
   return schedule(ctx, mode, s, S(copy_stream), cstreams, kernel, launch, chunks, [&]() -> int {
+    if (prod == AGG_PRODUCER_KERNEL)
+      return launch_copy_producer(ctx, sp.words, plans, 2, world, epoch, kmarks, cstreams[0]);
     if (int rc = produce(plans[0].cc, flags, ord, nullptr, epoch, cstreams, rank)) return rc;
     return produce(plans[1].cc, rs_flags, ord2, nullptr, epoch, cstreams, rank);
   });
+}
+
+// ------------------------------------------------------------------------------------------
+// diagnostics
+// ------------------------------------------------------------------------------------------
+
+extern "C" int agg_kernel_regs(int op, int dtype, int bm, int bn, int* gemm_regs, int* copy_regs) {
+  clear_error();
+  if (!gemm_regs || !copy_regs) return fail(AGG_E_ARG, "NULL output");
+  static const int epi[4] = {kEpiAllGather, kEpiReduceScatter, kEpiAllReduce, kEpiFfn};
+  if (op < 0 || op > 3) return fail(AGG_E_ARG, "unknown op %d", op);
+  *gemm_regs = kernel_regs(bm, bn, dtype, epi[op]);
+  *copy_regs = copy_kernel_regs();
+  if (*gemm_regs < 0) return fail(AGG_E_ARG, "no kernel for op %d dtype %d tile %dx%d", op, dtype, bm, bn);
+  return AGG_OK;
 }

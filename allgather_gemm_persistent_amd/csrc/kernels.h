@@ -17,6 +17,7 @@ constexpr int kScrFailed = 18;     // first flag index that timed out (0xFFFFFFF
 constexpr int kScrCopyNext = 19;   // in-kernel producer: next copy job
 constexpr int kScrCopyT0 = 20;     // in-kernel producer: wall clock of the first job (delays)
 constexpr int kScrRedNext = 21;    // ReduceScatter: next row group of the local block to reduce
+constexpr int kScrCopyDone = 22;   // copy kernel: workgroups that finished the current launch
 constexpr int kScrRsCount = 64;    // ReduceScatter per-send-chunk completion counters
 constexpr int kScrPieces = kScrRsCount + AGG_MAX_CHUNKS;   // per-chunk copied-piece counters
 constexpr int kScrOrder = kScrPieces + AGG_MAX_CHUNKS;     // arrival order (chunk ids)
@@ -111,6 +112,16 @@ hipError_t launch_gemm(const GemmArgs& args, int bm, int bn, int dtype, int epil
 // Workgroups of the (bm, bn, dtype, epilogue) kernel that fit on one CU at once (0 for a shape
 // without an instantiation).
 int max_blocks_per_cu(int bm, int bn, int dtype, int epilogue);
+
+// The producer as a kernel of its own (one wave per workgroup, `grid` workgroups, few registers),
+// run beside the GEMM kernel in the register and wave slots it leaves free: args.cs / copy_jobs /
+// epoch / scratch / mark_flags[0..1] as for the in-kernel producer.
+hipError_t launch_copy(const GemmArgs& args, int grid, hipStream_t stream);
+
+// Registers per lane of a GEMM kernel instance and of the copy kernel as the runtime reports
+// them (hipFuncGetAttributes), or -1.
+int kernel_regs(int bm, int bn, int dtype, int epilogue);
+int copy_kernel_regs();
 
 // Fill `words` uint32 at `dst` with `value` (a kernel, not a memset node).
 hipError_t launch_fill_u32(uint32_t* dst, size_t words, uint32_t value, hipStream_t stream);

@@ -200,10 +200,9 @@ constexpr int kStoreSystemCoherent = 1 | 16;
 // stores in issue order, so a load wait never waits for the stores issued after it). The
 // source (a peer's block) is read once: non-temporal loads; the stores write through. On return
 // every store of the calling thread has completed.
-template <int NT>
+template <int NT, int U = 16>
 __device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __restrict__ src,
                                   int64_t bytes, int tid) {
-  constexpr int U = 16;
   constexpr int64_t kStep = (int64_t)U * NT;
   const int64_t n16 = bytes >> 4;
   const u32x4* s = reinterpret_cast<const u32x4*>(src);
@@ -1627,6 +1626,76 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   }
 }
 
+// The producer as a kernel of its own: every workgroup is one wave that takes copy jobs (set 0's,
+// then set 1's, in arrival order) from the shared counter until none is left, copying each piece
+// with a few vectors per lane in flight (so that it fits in the registers the GEMM kernel leaves
+// free on each SIMD); the wave that completes a chunk releases its flag. Workgroup 0 first raises
+// the local slots' flags. The last workgroup to finish clears the counters for the next launch.
+__global__ void __launch_bounds__(64) copy_kernel(const GemmArgs a) {
+  const int lane = threadIdx.x;
+  if (blockIdx.x == 0) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      for (int i = lane; i < a.mark_count[f]; i += 64)
+        __hip_atomic_store(a.mark_flags[f] + i, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  const uint32_t* order = a.scratch + kScrOrder;
+  const uint32_t jobs = __builtin_amdgcn_readfirstlane(a.copy_jobs);
+  const uint32_t jobs0 = __builtin_amdgcn_readfirstlane(a.cs[0].jobs);
+  // The next job, taken with no lane-dependent branch: every lane joins the add (lane 0 adds 1,
+  // the others 0) and lane 0's result, the count before its own 1, is the job. (A fetch under
+  // `if (lane == 0)` followed by a cross-lane read lets the compiler lay the loop out as two
+  // nested loops, lane 0 in the outer one, and the cross-lane read then misses lane 0.)
+  auto next_job = [&]() -> uint32_t {
+    const uint32_t cur = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(a.scratch + kScrCopyNext, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (cur >= jobs) return jobs;
+    return __builtin_amdgcn_readfirstlane(atomicAdd(a.scratch + kScrCopyNext, lane == 0 ? 1u : 0u));
+  };
+  for (uint32_t job = next_job(); job < jobs; job = next_job()) {
+    const int set = job < jobs0 ? 0 : 1;
+    const CopySet& cs = a.cs[set];
+    const uint32_t pieces = __builtin_amdgcn_readfirstlane((uint32_t)cs.pieces);
+    const uint32_t jj = job - (set ? jobs0 : 0u);
+    const uint32_t j = jj / pieces, q = jj - j * pieces;
+    const int c = (int)__builtin_amdgcn_readfirstlane(order[cs.order_off + j]);
+    const int p = c / cs.cps, jl = c - p * cs.cps;
+    const int64_t lo = (int64_t)q * cs.piece_bytes;
+    const int64_t hi = lo + cs.piece_bytes < cs.chunk_bytes ? lo + cs.piece_bytes : cs.chunk_bytes;
+    const int64_t base = (int64_t)jl * cs.chunk_bytes;
+    copy_piece<64, 2>(cs.sym + ((int64_t)p * cs.cps) * cs.chunk_bytes + base + lo, cs.peer[p] + base + lo,
+                      hi - lo, lane);
+    // the wave's write-through stores have completed (copy_piece waited for them)
+    if (lane == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(a.scratch + kScrPieces + cs.piece_off + c, 1u,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev + 1 == pieces)
+        __hip_atomic_store(cs.put_flags + c, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+  }
+  // the last wave out clears the job counter and every chunk's piece count (the same
+  // branch-free count as the job fetch)
+  const uint32_t done = __builtin_amdgcn_readfirstlane(atomicAdd(a.scratch + kScrCopyDone, lane == 0 ? 1u : 0u));
+  if (done == gridDim.x - 1) {
+#pragma unroll
+    for (int set = 0; set < 2; ++set) {
+      const CopySet& cs = a.cs[set];
+      for (uint32_t i = lane; i * (uint32_t)cs.pieces < cs.jobs; i += 64)
+        __hip_atomic_store(a.scratch + kScrPieces + cs.piece_off + a.scratch[kScrOrder + cs.order_off + i], 0u,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (lane == 0) {
+      __hip_atomic_store(a.scratch + kScrCopyNext, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.scratch + kScrCopyDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+hipError_t launch_copy(const GemmArgs& args, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(64), 0, stream, args);
+  return hipGetLastError();
+}
+
 __global__ void fill_u32_kernel(uint32_t* dst, size_t words, uint32_t value) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x)
     dst[i] = value;
@@ -1636,6 +1705,46 @@ template <int BM, int BN, int DT, int EPI>
 static hipError_t launch_one(const GemmArgs& args, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_kernel<BM, BN, DT, EPI>), dim3(grid), dim3(kThreads), 0, stream, args);
   return hipGetLastError();
+}
+
+__global__ void copy_kernel(const GemmArgs a);
+
+template <int BM, int BN, int DT, int EPI>
+static int regs_one() {
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(gemm_kernel<BM, BN, DT, EPI>)) != hipSuccess)
+    return -1;
+  return attr.numRegs;
+}
+
+template <int DT, int EPI>
+static int regs_shape(int bm, int bn) {
+  if (bm == 256 && bn == 256) return regs_one<256, 256, DT, EPI>();
+  if (bm == 256 && bn == 224) return regs_one<256, 224, DT, EPI>();
+  if (bm == 128 && bn == 128) return regs_one<128, 128, DT, EPI>();
+  if (bm == 128 && bn == 64) return regs_one<128, 64, DT, EPI>();
+  if (bm == 64 && bn == 64) return regs_one<64, 64, DT, EPI>();
+  return -1;
+}
+
+int kernel_regs(int bm, int bn, int dtype, int epilogue) {
+  if (epilogue == kEpiAllGather) {
+    if (dtype == AGG_BF16) return regs_shape<AGG_BF16, kEpiAllGather>(bm, bn);
+    if (dtype == AGG_FP8_E4M3) return regs_shape<AGG_FP8_E4M3, kEpiAllGather>(bm, bn);
+  } else if (epilogue == kEpiReduceScatter && dtype == AGG_BF16) {
+    return regs_shape<AGG_BF16, kEpiReduceScatter>(bm, bn);
+  } else if (epilogue == kEpiAllReduce && dtype == AGG_BF16) {
+    return regs_shape<AGG_BF16, kEpiAllReduce>(bm, bn);
+  } else if (epilogue == kEpiFfn && dtype == AGG_BF16 && bm == 256 && bn == 256) {
+    return regs_one<256, 256, AGG_BF16, kEpiFfn>();
+  }
+  return -1;
+}
+
+int copy_kernel_regs() {
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(copy_kernel)) != hipSuccess) return -1;
+  return attr.numRegs;
 }
 
 template <int BM, int BN, int DT, int EPI>

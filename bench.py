@@ -74,7 +74,7 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before the timed steps, run one plain device copy of this many MiB (a"
                          " known-size kernel that HBM byte counters are scaled against)")
-    ap.add_argument("--producer", default="cu", choices=["cu", "sdma"],
+    ap.add_argument("--producer", default="cu", choices=["cu", "sdma", "kernel"],
                     help="producer of the timed steps: copy jobs inside the kernel (cu) or the"
                          " copy engines (sdma)")
     return ap.parse_args()
@@ -191,13 +191,18 @@ def measure_block(name, reps, flush, only="all"):
     if ffn:
         variants.append(("overlap_unfused", "overlap", "unfused", 2))
         variants.append(("gemm_only_unfused", "gemm_only", "unfused", 2))
+    # the copy kernel beside the GEMM kernel (AGG_PRODUCER_KERNEL; the call falls back to copy
+    # jobs inside the kernel where the GEMM kernel leaves it too few registers)
+    variants.append(("overlap_copy_kernel", "overlap", "kernel", 1))
     if only != "all":
         variants = [v for v in variants if v[0] in only.split(",")]
     has_pull = cfg.op == "ag"
+    ran = {}
 
     def setup(setting):
+        B.agg_ctx_set_producer(w.ctx, "kernel" if setting == "kernel" else "cu")
         if has_pull:
-            B.agg_ctx_set_pull(w.ctx, setting)
+            B.agg_ctx_set_pull(w.ctx, "off" if setting == "off" else "auto")
         if ffn:
             B.agg_ctx_set_chain_fused(w.ctx, setting != "unfused")
 
@@ -209,9 +214,10 @@ def measure_block(name, reps, flush, only="all"):
     stream = torch.cuda.current_stream()
     try:
         for _ in range(3):                               # warm-up of every variant
-            for _, mode, setting, _ in variants:
+            for label, mode, setting, _ in variants:
                 setup(setting)
                 run(mode)
+                ran[label] = B.agg_ctx_last_producer(w.ctx)
         torch.cuda.synchronize()
         B.agg_ctx_set_timing(w.ctx, True)
         ev, seq = [], []
@@ -287,6 +293,9 @@ def measure_block(name, reps, flush, only="all"):
         block["note"] = ("overlap / gemm_only: both layers in one launch over the tile dependency graph;"
                          " *_unfused: the same tiles as two launches (all of layer 1, then all of"
                          " layer 2); fusion_speedup = unfused / fused call time")
+    if "overlap_copy_kernel" in call:
+        block["R_copy_kernel"] = rnd(call["overlap_copy_kernel"] / call["gemm_only"], 3)
+        block["copy_kernel_producer_ran"] = ran.get("overlap_copy_kernel")
     if "overlap_push" in call:
         block["R_push"] = rnd(call["overlap_push"] / call["gemm_only"], 3)
         block["roofline_overlap_push"] = roof(kern["overlap_push"], bare_bytes + 2 * copy_bytes)
@@ -387,7 +396,7 @@ def main():
                      for m in ("overlap", "gemm_only")}
             s_int = {m: statistics.median([a.elapsed_time(b) * 1e3 for q, a, b in ev if q == m])
                      for m in inter}
-        other = {"cu": "sdma", "sdma": "cu"}[args.producer]
+        other = {"cu": "sdma", "sdma": "cu", "kernel": "cu"}[args.producer]
         t_ovl_other = None
         if other in modes:
             B.agg_ctx_set_producer(w.ctx, other)

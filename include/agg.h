@@ -21,7 +21,10 @@
  *    (thread blocks dedicated to data movement) of the same overlap;
  *  - AGG_PRODUCER_SDMA: the copy engines, one hipMemcpyAsync (no CU) plus one stream write per
  *    chunk on side streams; while chunks are in flight the kernel leaves a few CUs free for the
- *    runtime's own helper kernels (agg_ctx_set_reserved_cus).
+ *    runtime's own helper kernels (agg_ctx_set_reserved_cus);
+ *  - AGG_PRODUCER_KERNEL: a kernel of its own on one ctx stream, beside the persistent kernel:
+ *    one-wave workgroups, each taking chunk pieces in arrival order, that fit in the registers
+ *    the persistent kernel leaves free on every SIMD, so both run at once on every CU.
  *
  * Each declaration below names the passage it implements: "section ..." refers to a section of the
  * page "Triton-distributed is turning communication into compiler territory" (cronfeed.work).
@@ -147,7 +150,11 @@ int agg_ctx_set_copy_streams(agg_ctx* ctx, int n);
 /* Producer kinds. */
 enum {
   AGG_PRODUCER_CU = 0,    /* copy jobs inside the persistent kernel (default) */
-  AGG_PRODUCER_SDMA = 1   /* hipMemcpyAsync (copy engines) + stream write per chunk */
+  AGG_PRODUCER_SDMA = 1,  /* hipMemcpyAsync (copy engines) + stream write per chunk */
+  AGG_PRODUCER_KERNEL = 2 /* a copy kernel of one-wave workgroups on a ctx stream, beside the GEMM
+                             kernel in the registers it leaves free on each SIMD; where the GEMM
+                             kernel leaves too few (agg_kernel_regs), or with delays, the call
+                             uses AGG_PRODUCER_CU instead */
 };
 
 /* Select the producer of later calls. For AGG_PRODUCER_CU, `copy_wgs` workgroups of the
@@ -156,12 +163,21 @@ enum {
  * rounded up to whole 4 KiB and at least 16 KiB, so that every job fits in one round of the
  * copying workgroups; a chunk is cut into ceil(chunk bytes / piece) pieces), in arrival order, and only then
  * claim tiles; the workgroup that completes a chunk's last piece releases its flag. The other
- * arguments are ignored for AGG_PRODUCER_SDMA. AGG_E_ARG for an unknown kind or a negative
- * count.
+ * arguments are ignored for AGG_PRODUCER_SDMA. AGG_PRODUCER_KERNEL cuts chunks into `piece_kib`
+ * KiB pieces the same way (its grid is 1024 one-wave workgroups; `copy_wgs` is ignored); a call
+ * whose persistent kernel leaves the copy kernel too few registers (agg_kernel_regs), or that is
+ * given delays, runs AGG_PRODUCER_CU instead (agg_ctx_last_producer says which ran). AGG_E_ARG
+ * for an unknown kind or a negative count.
  * Passage: section "The first move was to expose the overlap" (remote data access and signaling)
  *  and section "DITRON adds three levels of tiling" (device-level tiles on DMA engines).
  */
 int agg_ctx_set_producer(agg_ctx* ctx, int kind, int copy_wgs, int piece_kib);
+
+/* Store in *kind the producer (AGG_PRODUCER_*) the last ag_gemm, gemm_rs, gemm_ar or ffn_chain
+ * call on `ctx` ran, -1 before the first. AGG_E_ARG for a NULL ctx or kind.
+ * Passage: section "The first move was to expose the overlap" (the producer side of a call).
+ */
+int agg_ctx_last_producer(const agg_ctx* ctx, int* kind);
 
 /* Pull modes of ag_gemm (AGG_OVERLAP calls under AGG_PRODUCER_CU without delays). */
 enum {
@@ -479,6 +495,14 @@ int agg_check_ar_args(int world, int rank, int64_t m, int64_t n, int64_t k, int 
                       const float* const* peer_src, const void* recv, const void* flags,
                       const void* out, const int32_t* order, int n_order, int mode,
                       agg_stream stream, agg_stream copy_stream);
+
+/* ---- diagnostics ---------------------------------------------------------------------- */
+
+/* Registers per lane that the runtime reports for the GEMM kernel instance of (op, dtype, bm x bn)
+ * (op: 0 = ag_gemm, 1 = gemm_rs, 2 = gemm_ar, 3 = ffn_chain) and for the copy kernel of
+ * AGG_PRODUCER_KERNEL. AGG_E_ARG for a combination without a kernel.
+ * Passage: section "DITRON adds three levels of tiling" (core-level tiles in registers). */
+int agg_kernel_regs(int op, int dtype, int bm, int bn, int* gemm_regs, int* copy_regs);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,7 @@ from helpers import BF16_TOL, FP8_TOL, assert_close, bits_equal, raw, small_ag_d
 pytestmark = pytest.mark.gpu
 
 TILES = [(256, 256), (256, 224), (128, 128), (128, 64), (64, 64)]
-PRODUCERS = ["cu", "sdma"]
+PRODUCERS = ["cu", "sdma", "kernel"]
 
 
 def _oracle_c(shards, b, dtype, sa, sb):
@@ -28,6 +28,38 @@ def _oracle_c(shards, b, dtype, sa, sb):
 
 def _tol(dtype):
     return FP8_TOL if dtype == "fp8" else BF16_TOL
+
+
+def _alloc(regs):
+    return (regs + 7) // 8 * 8
+
+
+def test_register_counts_and_kernel_producer_choice(gpu):
+    """The copy-kernel producer runs beside the GEMM kernel only if both fit in one SIMD's 512
+    registers per lane. The counts the runtime reports must include the accumulation registers
+    (the 256x256 kernels hold a 256-register accumulator per lane), else the choice would put
+    the copy kernel where it cannot be resident; the copy kernel itself must be small. A call
+    runs the copy kernel exactly where the counts fit, and the CU producer otherwise."""
+    g, c = B.agg_kernel_regs(0, "bf16", 256, 256)
+    assert 256 < g <= 512 and 0 < c <= 64, (g, c)
+    g, _ = B.agg_kernel_regs(1, "bf16", 256, 256)
+    assert 256 < g <= 512, g
+    world, ms, k, n = 2, 128, 256, 256
+    shards, b, _, _ = small_ag_data(world, ms, k, n, "bf16", seed=3)
+    for tile in [(256, 256), (256, 224), (64, 64)]:
+        w = AgWorkload(world, 0, shards, b, chunk_rows=32, tile=tile, producer="kernel")
+        try:
+            assert B.agg_ctx_last_producer(w.ctx) is None
+            w.run("overlap")
+            assert w.status() == (0, -1)
+            g, c = B.agg_kernel_regs(0, "bf16", *tile)
+            want = "kernel" if _alloc(g) + _alloc(c) <= 512 else "cu"
+            assert B.agg_ctx_last_producer(w.ctx) == want, (tile, g, c)
+            w.run("overlap", delay_us=inputs.delays_us((world - 1) * ms // 32, 5, 20))
+            assert w.status() == (0, -1)
+            assert B.agg_ctx_last_producer(w.ctx) == "cu"          # delays: copy jobs in-kernel
+        finally:
+            w.close()
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
@@ -505,7 +537,7 @@ def test_config_vs_oracle(gpu, name):
         assert_close(to_f64(c_ovl), _config_ref(name, d), _tol(cfg.dtype), name)
         _check_gather_and_flags(w, d, "overlap")
         runs = [("cu", "auto", "serial"), ("cu", "auto", "gemm_only"), ("cu", "off", "overlap"),
-                ("sdma", "auto", "overlap"), ("sdma", "auto", "serial")]
+                ("sdma", "auto", "overlap"), ("sdma", "auto", "serial"), ("kernel", "auto", "overlap")]
         for producer, pull, mode in runs:
             print(f"config {name}: {producer} pull={pull} {mode}", flush=True)
             B.agg_ctx_set_producer(w.ctx, producer)

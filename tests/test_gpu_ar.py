@@ -21,7 +21,7 @@ from helpers import BF16_TOL, assert_close, raw, to_f64
 pytestmark = pytest.mark.gpu
 
 TILES = [(256, 256), (256, 224), (128, 128), (128, 64), (64, 64)]
-PRODUCERS = ["cu", "sdma"]
+PRODUCERS = ["cu", "sdma", "kernel"]
 
 
 def _data(world, m, k, n, seed, kind="normal"):
@@ -149,7 +149,7 @@ def test_config_decode_vs_oracle(gpu):
         assert_close(to_f64(w.out), out, BF16_TOL, "out")
         _bookkeeping(w, d["peers"], "overlap")
         o1, s1 = w.out.clone(), w.send.clone()
-        for producer, mode in (("cu", "serial"), ("cu", "gemm_only"), ("sdma", "overlap")):
+        for producer, mode in (("cu", "serial"), ("cu", "gemm_only"), ("sdma", "overlap"), ("kernel", "overlap")):
             print(f"config ar decode: {producer} {mode}", flush=True)
             B.agg_ctx_set_producer(w.ctx, producer)
             w.out.zero_()

@@ -62,7 +62,7 @@ def _compare(w, ref, what):
 
 
 @pytest.mark.parametrize("mode", ["overlap", "serial"])
-@pytest.mark.parametrize("producer", ["cu", "sdma"])
+@pytest.mark.parametrize("producer", ["cu", "sdma", "kernel"])
 @pytest.mark.parametrize("fused", [True, False])
 def test_ragged_vs_oracle(gpu, mode, producer, fused):
     """Shard rows, both layers' columns and K not multiples of the 256 x 256 tile."""
@@ -96,7 +96,7 @@ def test_zero_first_layer_bitexact(gpu):
         w.close()
 
 
-@pytest.mark.parametrize("producer", ["cu", "sdma"])
+@pytest.mark.parametrize("producer", ["cu", "sdma", "kernel"])
 def test_orders_modes_fusion_bit_identical(gpu, producer):
     world, rank, ms, k1, n1, n2 = 8, 3, 128, 512, 512, 512
     shards, w1, w2, peers = _data(world, ms, k1, n1, n2, seed=421)

@@ -19,7 +19,7 @@ from helpers import BF16_TOL, assert_close, raw, to_f64
 pytestmark = pytest.mark.gpu
 
 TILES = [(256, 256), (256, 224), (128, 128), (128, 64), (64, 64)]
-PRODUCERS = ["cu", "sdma"]
+PRODUCERS = ["cu", "sdma", "kernel"]
 
 
 def _data(world, m, k, n, seed, kind="normal"):
@@ -152,7 +152,7 @@ def test_config_c3_vs_oracle(gpu):
         assert_close(to_f64(w.out), out, BF16_TOL, "out")
         bookkeeping("overlap")
         o1, s1 = w.out.clone(), w.send.clone()
-        for producer, mode in (("cu", "serial"), ("sdma", "overlap")):
+        for producer, mode in (("cu", "serial"), ("sdma", "overlap"), ("kernel", "overlap")):
             print(f"config c3: {producer} {mode}", flush=True)
             B.agg_ctx_set_producer(w.ctx, producer)
             w.out.zero_()
