@@ -564,7 +564,9 @@ __device__ bool wait_count(const GemmArgs& a, const uint32_t* ctr, uint32_t expe
   }
 }
 
-// The local block of a ReduceScatter ("reduce partial results"): out = out + the incoming
+// The local block of a ReduceScatter (the owner sums the partial blocks; page "Triton-distributed
+// is turning communication into compiler territory", section "The first move was to expose the
+// overlap"): out = out + the incoming
 // partial of every peer in ascending rank order, where `out` already holds this rank's own
 // partial (stored by the local tiles). Run by every workgroup once no tile is left, over groups
 // of kRedRows rows claimed from a shared counter, so the reduction is spread over the whole grid

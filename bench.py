@@ -194,6 +194,7 @@ def measure_block(name, reps, flush, only="all"):
     # the copy kernel beside the GEMM kernel (AGG_PRODUCER_KERNEL; the call falls back to copy
     # jobs inside the kernel where the GEMM kernel leaves it too few registers)
     variants.append(("overlap_copy_kernel", "overlap", "kernel", 1))
+    variants.append(("copy_only_copy_kernel", "copy_only", "kernel", 0))
     if only != "all":
         variants = [v for v in variants if v[0] in only.split(",")]
     has_pull = cfg.op == "ag"

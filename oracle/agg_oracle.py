@@ -13,9 +13,10 @@ What it computes, and where that is stated:
   chunked schedule changes when rows arrive, never the arithmetic, so the result is the plain
   definition  C = concat(A_shard_0, ..., A_shard_{W-1}) @ B  with every element of the
   inputs decoded exactly and accumulated in fp64.
-* GEMM+ReduceScatter (same section, and the lede's "reduce partial results"): every rank
-  produces a full partial product; the rows are split into W blocks; block p belongs to rank
-  p; the owner's block is the sum of all W partial blocks. One rank's share: its own product
+* GEMM+ReduceScatter (same section, and the page's opening, where partial products are
+  summed by their owners): every rank produces a full partial product; the rows are split
+  into W blocks; block p belongs to rank p; the owner's block is the sum of all W partial
+  blocks. One rank's share: its own product
   P = A @ B, the W-1 non-local row blocks of P (what it sends), and its reduced block
   P[block r] + sum of the W-1 incoming partial blocks.
 * GEMM+AllReduce (section "DITRON adds three levels of tiling" names AllReduce among the

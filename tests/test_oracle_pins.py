@@ -6,8 +6,11 @@
   exact C is computable with fractions.Fraction) and hand-derived worked examples;
 * the chunk/tile bookkeeping: an event simulation of chunk arrivals, independent of the
   oracle's "latest arrival position" formulation;
-* planted mistakes: plausible bugs (transposed operand, dropped peer, wrong sign, ignored
-  arrival order) planted in copies of the oracle must fail these pins.
+* planted mistakes: plausible bugs planted in copies of the oracle must fail these pins: a
+  transposed weight, shards concatenated in arrival order instead of rank order, a dropped
+  peer in the ReduceScatter sum, an e4m3 decoder off by a factor of 2, a tile order blind to the
+  arrival order, the AllReduce adding the rank's own slot, and the FFN chain without its
+  activation or with the activation after the second product.
 """
 
 import json
