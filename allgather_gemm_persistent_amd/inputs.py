@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the AllGather+GEMM and GEMM+ReduceScatter workloads.
+"""Seeded synthetic inputs for the workloads (gathers, reductions, token routings).
 
 This module holds no arithmetic of the method itself (no product, no reduction, no schedule):
 it only draws input tensors, arrival orders and delays from seeds, so that the HIP library and
@@ -7,7 +7,7 @@ the CPU oracle can be fed the very same bytes. It imports nothing else from the 
 * Tensor values come from a CPU ``torch.Generator`` (normal or uniform in float32), rounded to
   bfloat16 by torch, or quantised to float8 e4m3fn with one per-tensor scale
   ``s = amax|x| / 448`` and ``q = clamp(x / s, -448, 448)`` rounded by torch's cast.
-* Permutations and delays come from SplitMix64 (Steele, Lea and Flood, "Fast splittable
+* Permutations, delays and token routings come from SplitMix64 (Steele, Lea and Flood, "Fast splittable
   pseudorandom number generators", OOPSLA 2014; the constants of Vigna's public-domain
   reference version), which is stable across library versions; a Fisher-Yates shuffle draws
   ``next() % (i + 1)`` for i = n-1 down to 1.
@@ -34,6 +34,27 @@ class SplitMix64:
         z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & MASK64
         z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & MASK64
         return z ^ (z >> 31)
+
+
+def routing(n_tokens: int, weights, seed: int) -> list:
+    """The rank each of ``n_tokens`` tokens is routed to: a categorical draw over the ranks with
+    integer ``weights``, token by token from SplitMix64(seed): r = next() % sum(weights), and the
+    token goes to the first rank whose cumulative weight exceeds r."""
+    w = [int(x) for x in weights]
+    if not w or min(w) < 0 or sum(w) == 0:
+        raise ValueError("weights must be non-negative integers with a positive sum")
+    total = sum(w)
+    g = SplitMix64(seed)
+    out = []
+    for _ in range(n_tokens):
+        r = g.next() % total
+        acc = 0
+        for e, we in enumerate(w):
+            acc += we
+            if r < acc:
+                out.append(e)
+                break
+    return out
 
 
 def permutation(items, seed: int) -> list:

@@ -25,6 +25,11 @@ What it computes, and where that is stated:
 * The FFN chain (same section's task-level tiles in one persistent kernel; section "The
   performance case has a narrow, useful boundary" measures an FFN module on AMD GPUs):
   AllGather+GEMM, an elementwise activation (SiLU), then GEMM+ReduceScatter.
+* AllToAll + GEMM (section "DITRON adds three levels of tiling" names AllToAll among the
+  chunked collectives): every rank routes each of its tokens to one rank; the AllToAll delivers
+  to a rank, from every source, the tokens routed to it (in token order, at most `cap` per
+  source, the rest dropped), into one slot of `cap` rows per source; the rank's GEMM multiplies
+  every delivered row by its local weight.
 * The chunk / tile bookkeeping (section "DITRON adds three levels of tiling": collectives are
   broken into chunks that are paired with computation tiles, with synchronization inserted):
   which chunks a row tile needs, and the order in which row tiles become computable when the
@@ -53,9 +58,12 @@ __all__ = [
     "gemm_ar_ref",
     "silu",
     "ffn_chain_ref",
+    "a2a_dispatch_ref",
+    "a2a_gemm_ref",
     "covering_chunks",
     "ag_mtile_order",
     "rs_mtile_order",
+    "a2a_mtile_order",
 ]
 
 
@@ -279,6 +287,46 @@ def ffn_chain_ref(shards, w1_kn, w2_kn, peers, world: int, rank: int, dtype: str
 # Chunk / tile bookkeeping
 # ----------------------------------------------------------------------------------------------
 
+# ----------------------------------------------------------------------------------------------
+# AllToAll (dispatch) + GEMM
+# ----------------------------------------------------------------------------------------------
+
+def a2a_dispatch_ref(tokens, dests, rank: int, cap: int):
+    """The rows an AllToAll delivers to `rank`: one block per source rank.
+
+    tokens: W raw arrays (T_p, K), the token rows source p holds; dests: W integer sequences
+    (T_p,), the rank each of those tokens is routed to. Source p's block is its tokens whose
+    destination is `rank`, in token order, the first `cap` of them (tokens past the capacity are
+    dropped). Written token by token. Returns a list of W raw arrays (count_p, K).
+    """
+    out = []
+    for t, d in zip(tokens, dests):
+        t = np.asarray(t)
+        rows = []
+        for i in range(len(d)):
+            if int(d[i]) == rank and len(rows) < cap:
+                rows.append(i)
+        out.append(t[rows] if rows else np.zeros((0, t.shape[1]), dtype=t.dtype))
+    return out
+
+
+def a2a_gemm_ref(blocks, b_kn, dtype: str = "bf16", scale_a: float = 1.0, scale_b: float = 1.0):
+    """The GEMM on the delivered rows: every source's block times the local weight, float64.
+
+    blocks: W raw arrays (count_p, K) (a2a_dispatch_ref); b_kn: raw (K, N). fp8 inputs are
+    dequantised by their per-tensor scales as in ag_gemm_ref. Returns W arrays (count_p, N): the
+    rows of C in slot p that hold a delivered row; the slot's rows past count_p hold none.
+    """
+    b = _decode(np.asarray(b_kn), dtype)
+    out = []
+    for blk in blocks:
+        c = _decode(np.asarray(blk), dtype) @ b if len(blk) else np.zeros((0, b.shape[1]))
+        if dtype == "fp8":
+            c = c * (float(scale_a) * float(scale_b))
+        out.append(c)
+    return out
+
+
 def covering_chunks(row_lo: int, row_hi: int, chunk_rows: int) -> list[int]:
     """Chunk indices whose rows [c*cr, (c+1)*cr) meet the half-open row range [row_lo, row_hi).
 
@@ -345,3 +393,31 @@ def rs_mtile_order(world: int, rank: int, m_block: int, chunk_rows: int, order, 
         ready.append(max(need) if need else -1)
     seq.extend((rank, i) for i in sorted(range(tpb), key=lambda i: (ready[i], i)))
     return seq
+
+
+def a2a_mtile_order(world: int, rank: int, cap: int, chunk_rows: int, counts, order, bm: int):
+    """Order in which the row tiles of C become computable in AllToAll+GEMM.
+
+    The receive buffer has W slots of `cap` rows; slot p holds rows [p*cap, p*cap + counts[p]).
+    Chunk c = p*(cap/cr) + j covers rows [c*cr, (c+1)*cr) and holds rows when j*cr < counts[p].
+    The local slot's chunks and the chunks that hold no row are present from the start; the
+    others arrive at their position in `order` (every remote chunk listed). A row tile of `bm`
+    rows that holds no row is not computed at all; the others are computable at the arrival
+    position of the latest chunk they cover that holds rows (-1 if none), and are taken in
+    increasing position, ties by tile index. Returns the tile order as a list.
+    """
+    cps = cap // chunk_rows
+    m = world * cap
+    pos = {c: i for i, c in enumerate(order)}
+
+    def holds(c):
+        return (c % cps) * chunk_rows < counts[c // cps]
+    ready = {}
+    for t in range(-(-m // bm)):
+        lo, hi = t * bm, min((t + 1) * bm, m)
+        if not any((x - (x // cap) * cap) < counts[x // cap] for x in range(lo, hi)):
+            continue
+        need = [pos[c] for c in covering_chunks(lo, hi, chunk_rows) if c // cps != rank and holds(c)]
+        ready[t] = max(need) if need else -1
+    return sorted(ready, key=lambda t: (ready[t], t))
+

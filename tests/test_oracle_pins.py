@@ -504,3 +504,153 @@ def test_planted_ffn_mistakes_fail_the_pins(mutant):
     _, _, eo = _ffn_exact(shards, w1, w2, peers, world, rank)
     bad = mutant(shards, w1, w2, peers, world, rank)
     assert not all(_close(bad[i, c], eo[i][c]) for i in range(ms) for c in range(n2))
+
+
+# ------------------------------------------------------------------ AllToAll (dispatch) + GEMM
+
+def _a2a_case(world, t, k, rng, dtype="bf16"):
+    tokens = [_random_raw((t, k), dtype, rng) for _ in range(world)]
+    dests = [list(rng.integers(0, world, size=t)) for _ in range(world)]
+    return tokens, dests
+
+
+@pytest.mark.parametrize("world,rank,t,cap", [(1, 0, 5, 5), (2, 1, 6, 2), (3, 0, 7, 3), (4, 2, 9, 9)])
+def test_a2a_dispatch_token_by_token(world, rank, t, cap):
+    """Every source's block for a rank is its tokens routed there, in token order, the first cap.
+    Checked against row ids written into the tokens themselves (token i of source p holds the
+    value 16*p + i in every column), so a dropped, reordered or misrouted row shows up."""
+    rng = np.random.default_rng(900 + world * 10 + rank)
+    dests = [list(rng.integers(0, world, size=t)) for _ in range(world)]
+    tokens = [_bf16_bits([[16 * p + i] * 2 for i in range(t)]) for p in range(world)]
+    blocks = O.a2a_dispatch_ref(tokens, dests, rank, cap)
+    for p in range(world):
+        ids = [int(v) for v in O.decode_bf16(blocks[p])[:, 0] - 16 * p] if len(blocks[p]) else []
+        routed = [i for i in range(t) if dests[p][i] == rank]
+        assert ids == routed[:cap]
+        assert np.array_equal(O.decode_bf16(blocks[p])[:, 1], O.decode_bf16(blocks[p])[:, 0])
+
+
+def test_a2a_dispatch_delivers_every_token_once():
+    """With a capacity no source exceeds, the blocks all ranks receive from one source are a
+    partition of that source's tokens (each token delivered once, to its destination)."""
+    rng = np.random.default_rng(931)
+    world, t, k = 4, 11, 3
+    tokens, dests = _a2a_case(world, t, k, rng)
+    for p in range(world):
+        got = np.concatenate([O.a2a_dispatch_ref(tokens, dests, r, t)[p] for r in range(world)])
+        assert sorted(map(tuple, got.tolist())) == sorted(map(tuple, np.asarray(tokens[p]).tolist()))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_a2a_gemm_vs_exact_rational(dtype):
+    rng = np.random.default_rng(941)
+    world, rank, t, k, n, cap = 3, 1, 5, 16, 3, 2
+    tokens, dests = _a2a_case(world, t, k, rng, dtype)
+    blocks = O.a2a_dispatch_ref(tokens, dests, rank, cap)
+    b = _random_raw((k, n), dtype, rng)
+    sa, sb = (0.5, 0.25) if dtype == "fp8" else (1.0, 1.0)
+    c = O.a2a_gemm_ref(blocks, b, dtype, sa, sb)
+    scale = Fraction(sa) * Fraction(sb) if dtype == "fp8" else Fraction(1)
+    for p in range(world):
+        assert c[p].shape == (len(blocks[p]), n)
+        if not len(blocks[p]):
+            continue
+        exact = _exact_matmul(_frac_matrix(blocks[p], dtype), _frac_matrix(b, dtype))
+        for i in range(len(blocks[p])):
+            for j in range(n):
+                assert Fraction(float(c[p][i, j])) == exact[i][j] * scale
+
+
+@pytest.mark.parametrize("case", _golden()["a2a"], ids=lambda c: c["name"])
+def test_a2a_worked_examples(case):
+    tokens = [_bf16_bits(x) if x else np.zeros((0, 2), np.uint16) for x in case["tokens"]]
+    blocks = O.a2a_dispatch_ref(tokens, case["dests"], case["rank"], case["cap"])
+    for p, want in enumerate(case["blocks"]):
+        assert np.array_equal(O.decode_bf16(blocks[p]).reshape(-1, 2), np.array(want, np.float64).reshape(-1, 2))
+    c = O.a2a_gemm_ref(blocks, _bf16_bits(case["b"]))
+    for p, want in enumerate(case["c"]):
+        assert np.array_equal(c[p].reshape(-1, 2), np.array(want, np.float64).reshape(-1, 2))
+
+
+def _simulate_a2a(world, rank, cap, cr, counts, order, bm):
+    """Deliver chunks one at a time (a chunk's rows, token rows or not, arrive together; rows of
+    chunks without a token are there from the start); after each delivery, emit (ascending)
+    every row tile that holds a token and whose rows are all present."""
+    m = world * cap
+    token = np.array([(x % cap) < counts[x // cap] for x in range(m)])
+    present = np.zeros(m, dtype=bool)
+    present[rank * cap:(rank + 1) * cap] = True
+    for c in range(world * (cap // cr)):
+        if not token[c * cr:(c + 1) * cr].any():
+            present[c * cr:(c + 1) * cr] = True
+    n_tiles = -(-m // bm)
+    done, seq = set(), []
+
+    def sweep():
+        for t in range(n_tiles):
+            rows = slice(t * bm, min((t + 1) * bm, m))
+            if t not in done and token[rows].any() and present[rows].all():
+                done.add(t)
+                seq.append(t)
+    sweep()
+    for c in order:
+        present[c * cr:(c + 1) * cr] = True
+        sweep()
+    return seq
+
+
+@pytest.mark.parametrize("world,rank,cap,cr,bm,counts", [
+    (2, 0, 8, 4, 4, [3, 5]), (3, 1, 12, 4, 8, [12, 0, 7]), (4, 3, 6, 2, 4, [1, 6, 0, 2]),
+    (8, 0, 640, 128, 256, [626, 603, 606, 617, 629, 614, 640, 616]), (8, 5, 16, 4, 64, [0] * 8),
+    (5, 2, 10, 5, 3, [10, 4, 5, 0, 9]), (3, 0, 9, 3, 5, [2, 9, 4])])
+@pytest.mark.parametrize("order_seed", [0, 1, 2])
+def test_a2a_mtile_order_vs_simulation(world, rank, cap, cr, bm, counts, order_seed):
+    cps = cap // cr
+    order = inputs.seeded_order(world, rank, cps, 7 + order_seed) if order_seed else \
+        inputs.ring_order(world, rank, cps)
+    got = O.a2a_mtile_order(world, rank, cap, cr, counts, order, bm)
+    assert got == _simulate_a2a(world, rank, cap, cr, counts, order, bm)
+
+
+def _a2a_ignore_cap(tokens, dests, rank, cap):
+    return O.a2a_dispatch_ref(tokens, dests, rank, 10 ** 9)
+
+
+def _a2a_last_cap(tokens, dests, rank, cap):
+    out = []
+    for t, d in zip(tokens, dests):
+        rows = [i for i in range(len(d)) if int(d[i]) == rank][-cap:] if cap else []
+        out.append(np.asarray(t)[rows])
+    return out
+
+
+def _a2a_wrong_rank(tokens, dests, rank, cap):
+    return O.a2a_dispatch_ref(tokens, dests, (rank + 1) % len(tokens), cap)
+
+
+@pytest.mark.parametrize("mutant", [_a2a_ignore_cap, _a2a_last_cap, _a2a_wrong_rank])
+def test_planted_a2a_mistakes_fail_the_pins(mutant):
+    case = _golden()["a2a"][0]
+    tokens = [_bf16_bits(x) if x else np.zeros((0, 2), np.uint16) for x in case["tokens"]]
+    blocks = mutant(tokens, case["dests"], case["rank"], case["cap"])
+    same = all(np.array_equal(O.decode_bf16(np.asarray(blk)).reshape(-1, 2), np.array(w, np.float64).reshape(-1, 2))
+               for blk, w in zip(blocks, case["blocks"]))
+    assert not same
+
+
+def test_planted_a2a_schedule_mistake_fails_the_pin():
+    """A tile order that waits for chunks holding no token at their place in the arrival order
+    (instead of counting them present) differs from the simulation."""
+    world, rank, cap, cr, bm, counts = 3, 0, 8, 4, 8, [8, 8, 3]
+    order = [4, 2, 3, 5]              # slot 2's empty chunk 5 comes last: it must not delay tile 2
+    cps = cap // cr
+    pos = {c: i for i, c in enumerate(order)}
+    ready = {}
+    for t in range(world * cap // bm):
+        lo, hi = t * bm, (t + 1) * bm
+        if any((x % cap) < counts[x // cap] for x in range(lo, hi)):
+            need = [pos[c] for c in O.covering_chunks(lo, hi, cr) if c // cps != rank]
+            ready[t] = max(need) if need else -1
+    wrong = sorted(ready, key=lambda t: (ready[t], t))
+    assert wrong != _simulate_a2a(world, rank, cap, cr, counts, order, bm)
+
