@@ -76,6 +76,12 @@ _SIGNATURES = {
                               _c_int, ctypes.POINTER(_c_int)],
     "agg_rs_row_tile_order": [_c_int, _c_int, _c_i64, _c_int, _i32p, _c_int, _c_int, _i32p,
                               _c_int, ctypes.POINTER(_c_int)],
+    "a2a_gemm": [_vp, _c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_f32, _c_f32, _i32p,
+                 ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _i32p, _c_int, _u32p, _c_int, _vp, _vp],
+    "agg_check_a2a_args": [_c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_f32, _c_f32, _i32p,
+                           ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _i32p, _c_int, _c_int, _vp, _vp],
+    "agg_a2a_row_tile_order": [_c_int, _c_int, _c_i64, _c_int, _i32p, _i32p, _c_int, _c_int, _i32p,
+                               _c_int, ctypes.POINTER(_c_int)],
     "agg_check_ag_args": [_c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _c_f32, _c_f32,
                           ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _i32p, _c_int, _c_int, _vp, _vp],
     "agg_check_rs_args": [_c_int, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp, _vp, _vp,
@@ -333,6 +339,20 @@ def ag_gemm_noalloc(ctx, world, rank, m_shard, n, k, chunk_rows, dtype, scale_a,
           _stream(stream), _stream(copy_stream))
 
 
+def a2a_gemm(ctx, world, rank, cap, n, k, chunk_rows, dtype, scale_a, scale_b, counts, peer_src,
+             recv, flags, b, c, order=None, delay_us=None, mode="overlap", stream=None,
+             copy_stream=None) -> None:
+    """AllToAll (dispatch) + GEMM: slot p of `recv` receives counts[p] rows from source p."""
+    if counts is None or len(counts) != world:
+        raise AggError(AGG_E_ARG, "a2a_gemm", f"counts must hold {world} entries")
+    cnt, _ = _i32_array(counts)
+    ordr, n_order = _i32_array(order)
+    peers, g, f, bp, cp = _ag_ptrs(world, rank, cap, n, k, chunk_rows, dtype, peer_src, recv, flags, b, c)
+    _call("a2a_gemm", ctx, world, rank, cap, n, k, chunk_rows, _dtype(dtype), scale_a, scale_b, cnt,
+          peers, g, f, bp, cp, ordr, n_order, _u32_array(delay_us), _mode(mode), _stream(stream),
+          _stream(copy_stream))
+
+
 def _rs_ptrs(world, rank, m, n, k, chunk_rows, a, b, send, send_flags, peer_src, recv, flags, out):
     """Checked device pointers of a gemm_rs call, in its argument order."""
     mb = m // world if world > 0 else 0
@@ -430,6 +450,29 @@ def agg_ag_row_tile_order(world, rank, m_shard, chunk_rows, order, bm) -> list:
 
 def agg_rs_row_tile_order(world, rank, m, chunk_rows, order, bm) -> list:
     return _tile_order("agg_rs_row_tile_order", world, rank, m, chunk_rows, order, bm)
+
+
+def agg_a2a_row_tile_order(world, rank, cap, chunk_rows, counts, order, bm) -> list:
+    cnt, _ = _i32_array(counts)
+    ordr, n_order = _i32_array(order)
+    room = MAX_ROW_TILES * 64
+    out = (ctypes.c_int32 * room)()
+    n = _c_int()
+    _call("agg_a2a_row_tile_order", world, rank, cap, chunk_rows, cnt, ordr, n_order, bm, out, room,
+          ctypes.byref(n))
+    return list(out[:n.value])
+
+
+def agg_check_a2a_args(world, rank, cap, n, k, chunk_rows, dtype, scale_a, scale_b, counts, peer_src,
+                       recv, flags, b, c, order=None, mode="overlap", stream=None,
+                       copy_stream=None) -> int:
+    """Returns the status code (does not raise) so tests can check each error code."""
+    cnt, _ = _i32_array(counts)
+    ordr, n_order = _i32_array(order)
+    return load().agg_check_a2a_args(world, rank, cap, n, k, chunk_rows, _dtype(dtype), scale_a,
+                                     scale_b, cnt, _ptr_array(peer_src), _ptr(recv), _ptr(flags),
+                                     _ptr(b), _ptr(c), ordr, n_order, _mode(mode), _stream(stream),
+                                     _stream(copy_stream))
 
 
 def agg_check_ag_args(world, rank, m_shard, n, k, chunk_rows, dtype, scale_a, scale_b, peer_src,

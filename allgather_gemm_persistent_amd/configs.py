@@ -9,6 +9,8 @@ from __future__ import annotations
 
 from dataclasses import dataclass, field
 
+import torch
+
 from . import inputs
 
 
@@ -162,6 +164,46 @@ U11 = {"kind": "uniform", "lo": -1.0, "hi": 1.0}
 N1 = {"kind": "normal", "std": 1.0}
 N002 = {"kind": "normal", "std": 0.02}
 
+@dataclass(frozen=True)
+class A2aConfig:
+    """AllToAll (dispatch) + GEMM: each of W source ranks holds `tokens` token rows (of K) and
+    routes each to one rank (a seeded categorical draw with integer `weights`); this rank
+    receives, from each source, the tokens routed to it (the first `cap`, the rest dropped) into
+    slot p of a W*cap x K buffer, and multiplies every received row by B (K x N)."""
+    name: str
+    world: int
+    rank: int
+    tokens: int
+    cap: int
+    k: int
+    n: int
+    chunk_rows: int
+    dtype: str
+    a_dist: dict
+    b_dist: dict
+    weights: tuple
+    order_kind: str
+    seed: int
+    op: str = field(default="a2a")
+
+    @property
+    def m(self) -> int:
+        return self.world * self.cap
+
+    @property
+    def chunks_per_slot(self) -> int:
+        return self.cap // self.chunk_rows
+
+    def order(self) -> list:
+        if self.order_kind == "ring":
+            return inputs.ring_order(self.world, self.rank, self.chunks_per_slot)
+        return inputs.seeded_order(self.world, self.rank, self.chunks_per_slot, self.seed + 1)
+
+    def dests(self, p: int) -> list:
+        """The rank each token of source p is routed to."""
+        return inputs.routing(self.tokens, self.weights, self.seed + 100 + p)
+
+
 CONFIGS = {
     # tiny, latency-bound; the oracle takes milliseconds
     "ag_w2_256x256x512_bf16": AgConfig(
@@ -196,6 +238,13 @@ CONFIGS = {
         "ffn_w8_4096x8192x3584_bf16", world=8, rank=0, m_shard=512, k1=8192, n1=3584, n2=8192,
         chunk_rows=128, rs_chunk_rows=128, a_dist=N1, w1_dist=N002, w2_dist=N002, peer_dist=N1,
         seed=1070),
+    # AllToAll dispatch + the expert GEMM: 8 sources x 4096 tokens, top-1 routing with this
+    # rank's expert drawn 10/66 of the time (~620 tokens per source against a capacity of 640,
+    # so some sources fill their slot and drop the rest), hidden 8192, expert width 3584
+    "a2a_w8_5120x3584x8192_bf16": A2aConfig(
+        "a2a_w8_5120x3584x8192_bf16", world=8, rank=0, tokens=4096, cap=640, k=8192, n=3584,
+        chunk_rows=128, dtype="bf16", a_dist=N1, b_dist=N002, weights=(10, 8, 8, 8, 8, 8, 8, 8),
+        order_kind="seeded", seed=1080),
 }
 
 HEADLINE = "ag_w8_4096x3584x8192_bf16"
@@ -244,3 +293,30 @@ def make_ffn_data(cfg: FfnConfig):
     peers[cfg.rank].zero_()
     shards = [a[p * cfg.m_shard:(p + 1) * cfg.m_shard].contiguous() for p in range(cfg.world)]
     return {"shards": shards, "w1": w1, "w2": w2, "peers": peers}
+
+
+def make_a2a_data(cfg: A2aConfig):
+    """Host tensors for an AllToAll+GEMM workload.
+
+    Returns dict: tokens (W CPU tensors T x K, each source's token rows), dests (W lists, each
+    token's destination rank), blocks (W CPU tensors cap x K: what source p sends this rank, its
+    tokens routed here in token order, the first cap of them, zero rows after), counts (rows in
+    each block), b (K x N), scale_a, scale_b. All W sources' tokens are drawn as one tensor so
+    that fp8 has one per-tensor scale.
+    """
+    a, sa = inputs.draw(cfg.a_dist, (cfg.world * cfg.tokens, cfg.k), cfg.dtype, cfg.seed)
+    b, sb = inputs.draw(cfg.b_dist, (cfg.k, cfg.n), cfg.dtype, cfg.seed + 3)
+    tokens = [a[p * cfg.tokens:(p + 1) * cfg.tokens].contiguous() for p in range(cfg.world)]
+    dests = [cfg.dests(p) for p in range(cfg.world)]
+    blocks, counts = [], []
+    for p in range(cfg.world):
+        d = torch.tensor(dests[p], dtype=torch.int64)
+        idx = torch.nonzero(d == cfg.rank).flatten()[:cfg.cap]
+        blk = torch.zeros(cfg.cap, cfg.k, dtype=torch.uint8 if cfg.dtype == "fp8" else torch.int16)
+        blk = blk.view(tokens[p].dtype)
+        blk[:len(idx)] = tokens[p][idx]
+        blocks.append(blk)
+        counts.append(int(len(idx)))
+    return {"tokens": tokens, "dests": dests, "blocks": blocks, "counts": counts, "b": b,
+            "scale_a": sa, "scale_b": sb}
+

@@ -195,7 +195,16 @@ struct ChunkCopy {
   uint8_t* dst;                // symmetric buffer base
   int64_t slot_rows, cr, row_bytes;
   int cps;
+  const int32_t* valid_rows = nullptr;   // AllToAll: rows of each peer's slot that hold data
 };
+
+// Bytes of chunk q of peer p that hold rows: the whole chunk, or (AllToAll) the part of it
+// below the peer's count.
+int64_t held_bytes(const ChunkCopy& cc, int p, int q) {
+  const int64_t rows = cc.valid_rows ? std::min<int64_t>(std::max<int64_t>(cc.valid_rows[p] - q * cc.cr, 0), cc.cr)
+                                     : cc.cr;
+  return rows * cc.row_bytes;
+}
 
 hipError_t make_own_queue_stream(agg_ctx* ctx, hipStream_t* out) {
   std::vector<uint32_t> mask(size_t((ctx->cus + 31) / 32), 0xFFFFFFFFu);
@@ -226,7 +235,8 @@ int produce(const ChunkCopy& cc, uint32_t* flags, const std::vector<int32_t>& or
     if (delay_us) busy_wait_us(delay_us[i]);
     const uint8_t* src = cc.src[p] + size_t(q) * bytes;
     uint8_t* dst = cc.dst + size_t(p * cc.slot_rows + q * cc.cr) * size_t(cc.row_bytes);
-    if (int rc = put_signal(dst, src, bytes, flags + c, epoch, streams[i % streams.size()])) return rc;
+    if (int rc = put_signal(dst, src, size_t(held_bytes(cc, p, q)), flags + c, epoch, streams[i % streams.size()]))
+      return rc;
   }
   return AGG_OK;
 }
@@ -436,7 +446,10 @@ void fill_copies(agg_ctx* ctx, GemmArgs& g, const CopyPlan* sets, int nsets, boo
     std::memset(&cs, 0, sizeof cs);
     if (s >= nsets) continue;
     const CopyPlan& pl = sets[s];
-    for (int p = 0; p < world; ++p) cs.peer[p] = pl.cc.src[p];
+    for (int p = 0; p < world; ++p) {
+      cs.peer[p] = pl.cc.src[p];
+      cs.valid_bytes[p] = (pl.cc.valid_rows ? pl.cc.valid_rows[p] : pl.cc.slot_rows) * pl.cc.row_bytes;
+    }
     cs.sym = pl.cc.dst;
     cs.put_flags = pl.flags;
     cs.chunk_bytes = pl.cc.cr * pl.cc.row_bytes;
@@ -902,15 +915,23 @@ namespace {
 
 // ag_gemm and ag_gemm_noalloc: the same call on the ctx's own scratch (noalloc false) or on the
 // device's static array, without any allocation (noalloc true).
+// AllGather+GEMM, and (with `counts`) AllToAll+GEMM: the same path over slots that hold only
+// their first counts[p] rows.
 int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, int64_t k,
                  int chunk_rows, int dtype, float scale_a, float scale_b,
                  const void* const* peer_src, void* gather, uint32_t* flags, const void* b, void* c,
                  const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
-                 agg_stream stream, agg_stream copy_stream, bool noalloc) {
+                 agg_stream stream, agg_stream copy_stream, bool noalloc, const int32_t* counts = nullptr) {
   if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
-  if (int rc = agg_check_ag_args(world, rank, m_shard, n, k, chunk_rows, dtype, scale_a, scale_b,
-                                 peer_src, gather, flags, b, c, order, n_order, mode, stream, copy_stream))
+  if (counts) {
+    if (int rc = agg_check_a2a_args(world, rank, m_shard, n, k, chunk_rows, dtype, scale_a, scale_b, counts,
+                                    peer_src, gather, flags, b, c, order, n_order, mode, stream, copy_stream))
+      return rc;
+  } else if (int rc = agg_check_ag_args(world, rank, m_shard, n, k, chunk_rows, dtype, scale_a, scale_b,
+                                        peer_src, gather, flags, b, c, order, n_order, mode, stream,
+                                        copy_stream)) {
     return rc;
+  }
   if (noalloc && ctx->producer != AGG_PRODUCER_CU)
     return fail(AGG_E_STATE, "ag_gemm_noalloc runs the in-kernel producer only (agg_ctx_set_producer)");
   const Scratch sp = noalloc ? static_scratch(ctx->device) : own_scratch(ctx);
@@ -924,9 +945,32 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
   const int cps = int(m_shard / chunk_rows);
   if (world > 1)
     if (int rc = bind_flags(ctx, kFlagsAg, flags, size_t(world) * cps)) return rc;
-  const std::vector<int32_t> ord = order ? std::vector<int32_t>(order, order + n_order) : ring_order(world, rank, cps);
+  std::vector<int32_t> ord = order ? std::vector<int32_t>(order, order + n_order) : ring_order(world, rank, cps);
+  std::vector<uint32_t> delays_held;
+  if (counts) {
+    // chunks that hold no row go first (their copies are empty: only the flag is raised), the
+    // others keep their order; delays stay with their chunks
+    std::vector<int32_t> first, rest;
+    std::vector<uint32_t> dfirst, drest;
+    for (size_t i = 0; i < ord.size(); ++i) {
+      const int32_t ch = ord[i];
+      const bool holds = int64_t(ch % cps) * chunk_rows < counts[ch / cps];
+      (holds ? rest : first).push_back(ch);
+      if (delay_us) (holds ? drest : dfirst).push_back(delay_us[i]);
+    }
+    first.insert(first.end(), rest.begin(), rest.end());
+    ord.swap(first);
+    if (delay_us) {
+      dfirst.insert(dfirst.end(), drest.begin(), drest.end());
+      delays_held.swap(dfirst);
+      delay_us = delays_held.data();
+    }
+  }
   hipStream_t s = S(stream);
-  const bool kernel = (mode != AGG_COPY_ONLY) && n > 0;
+  const std::vector<int32_t> rows =
+      (mode != AGG_COPY_ONLY && n > 0) ? ag_row_tile_order(world, rank, m_shard, chunk_rows, ord, ts.bm, counts)
+                                       : std::vector<int32_t>();
+  const bool kernel = !rows.empty();
   const bool chunks = (mode != AGG_GEMM_ONLY) && world > 1;
   const int prod = effective_producer(ctx, ts, dtype, kEpiAllGather, delay_us != nullptr);
   ctx->last_producer = prod;
@@ -945,6 +989,7 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
   cc.cr = chunk_rows;
   cc.row_bytes = k * elem_bytes(dtype);
   cc.cps = cps;
+  cc.valid_rows = counts;
 
   GemmArgs g;
   std::memset(&g, 0, sizeof g);
@@ -952,7 +997,6 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
   int64_t tiles = 0;
   int grid = 1;
   if (kernel) {
-    const std::vector<int32_t> rows = ag_row_tile_order(world, rank, m_shard, chunk_rows, ord, ts.bm);
     if (int rc = upload_rows(ctx, sp, s, rows)) return rc;
     g.a = static_cast<const uint8_t*>(gather);
     g.b = static_cast<const uint8_t*>(b);
@@ -1010,7 +1054,7 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
     // spare for the copiers, reads the remote rows straight from the peers' blocks (automatic
     // for small gathers, where the chunk copy's latency would otherwise be exposed)
     int pull_copiers = 0;
-    if (kernel && chunks && mode == AGG_OVERLAP && ctx->pull != AGG_PULL_OFF && delay_us == nullptr &&
+    if (kernel && chunks && mode == AGG_OVERLAP && ctx->pull != AGG_PULL_OFF && delay_us == nullptr && !counts &&
         (m_shard % ts.bm == 0 || (ts.bm <= 128 && m_shard % 16 == 0))) {
       const int64_t remote = int64_t(world - 1) * m_shard * cc.row_bytes;
       const int64_t spare = int64_t(ctx->cus) - grid;
@@ -1068,6 +1112,16 @@ extern "C" int ag_gemm_noalloc(agg_ctx* ctx, int world, int rank, int64_t m_shar
                                int mode, agg_stream stream, agg_stream copy_stream) {
   return ag_gemm_impl(ctx, world, rank, m_shard, n, k, chunk_rows, dtype, scale_a, scale_b, peer_src,
                       gather, flags, b, c, order, n_order, delay_us, mode, stream, copy_stream, true);
+}
+
+extern "C" int a2a_gemm(agg_ctx* ctx, int world, int rank, int64_t cap, int64_t n, int64_t k, int chunk_rows,
+                        int dtype, float scale_a, float scale_b, const int32_t* counts,
+                        const void* const* peer_src, void* recv, uint32_t* flags, const void* b, void* c,
+                        const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
+                        agg_stream stream, agg_stream copy_stream) {
+  if (!counts) return fail(AGG_E_ARG, "counts is NULL");
+  return ag_gemm_impl(ctx, world, rank, cap, n, k, chunk_rows, dtype, scale_a, scale_b, peer_src, recv,
+                      flags, b, c, order, n_order, delay_us, mode, stream, copy_stream, false, counts);
 }
 
 // ------------------------------------------------------------------------------------------

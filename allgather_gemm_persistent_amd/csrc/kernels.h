@@ -38,6 +38,8 @@ struct CopySet {
   uint8_t* sym;                         // symmetric buffer (gather / receive)
   uint32_t* put_flags;                  // flags the producer releases
   int64_t chunk_bytes, piece_bytes;
+  int64_t valid_bytes[AGG_MAX_WORLD];   // bytes of each peer's slot that hold rows (AllToAll:
+                                        // counts[p] rows; otherwise the whole slot)
   uint32_t jobs;                        // chunks x pieces of this set
   int pieces;                           // pieces per chunk
   int cps;                              // chunks per peer block

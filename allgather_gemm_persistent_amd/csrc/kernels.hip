@@ -246,6 +246,10 @@ __device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __re
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+__device__ inline int64_t min_i64(int64_t x, int64_t y) { return x < y ? x : y; }
+// x clamped to [0, hi]
+__device__ inline int64_t clamp_bytes(int64_t x, int64_t hi) { return x < 0 ? 0 : (x > hi ? hi : x); }
+
 // The in-kernel producer. Job j*pieces + q copies piece q of the chunk at arrival position j;
 // the job that completes a chunk (all its pieces copied and released) stores the epoch into the
 // chunk's flag. Jobs are taken from a shared counter in arrival order, so chunks complete
@@ -303,9 +307,11 @@ __device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job, in
       while (wall_ticks() - t0 < due) __builtin_amdgcn_s_sleep(2);
     }
     __syncthreads();
-    const int64_t lo = (int64_t)q * cs.piece_bytes;
-    const int64_t hi = lo + cs.piece_bytes < cs.chunk_bytes ? lo + cs.piece_bytes : cs.chunk_bytes;
     const int64_t base = (int64_t)jl * cs.chunk_bytes;
+    // the chunk's bytes that hold rows (all of them, except in an AllToAll's partly filled slots)
+    const int64_t held = clamp_bytes(cs.valid_bytes[p] - base, cs.chunk_bytes);
+    const int64_t lo = min_i64((int64_t)q * cs.piece_bytes, held);
+    const int64_t hi = min_i64(lo + cs.piece_bytes, held);
     copy_piece<NT>(cs.sym + ((int64_t)p * cs.cps) * cs.chunk_bytes + base + lo,
                cs.peer[p] + base + lo, hi - lo, tid);
     // every thread's write-through stores have completed in memory (copy_piece waited for
@@ -1662,9 +1668,10 @@ __global__ void __launch_bounds__(64) copy_kernel(const GemmArgs a) {
     const uint32_t j = jj / pieces, q = jj - j * pieces;
     const int c = (int)__builtin_amdgcn_readfirstlane(order[cs.order_off + j]);
     const int p = c / cs.cps, jl = c - p * cs.cps;
-    const int64_t lo = (int64_t)q * cs.piece_bytes;
-    const int64_t hi = lo + cs.piece_bytes < cs.chunk_bytes ? lo + cs.piece_bytes : cs.chunk_bytes;
     const int64_t base = (int64_t)jl * cs.chunk_bytes;
+    const int64_t held = clamp_bytes(cs.valid_bytes[p] - base, cs.chunk_bytes);
+    const int64_t lo = min_i64((int64_t)q * cs.piece_bytes, held);
+    const int64_t hi = min_i64(lo + cs.piece_bytes, held);
     copy_piece<64, 2>(cs.sym + ((int64_t)p * cs.cps) * cs.chunk_bytes + base + lo, cs.peer[p] + base + lo,
                       hi - lo, lane);
     // the wave's write-through stores have completed (copy_piece waited for them)

@@ -138,21 +138,32 @@ int check_order(int world, int rank, int chunks_per_shard, const int32_t* order,
 }
 
 std::vector<int32_t> ag_row_tile_order(int world, int rank, int64_t m_shard, int chunk_rows,
-                                       const std::vector<int32_t>& order, int bm) {
+                                       const std::vector<int32_t>& order, int bm, const int32_t* counts) {
   const int64_t m = int64_t(world) * m_shard;
   const int64_t cps = m_shard / chunk_rows;
   const int64_t n_chunks = int64_t(world) * cps;
   std::vector<int64_t> pos(size_t(n_chunks), -1);
   for (size_t i = 0; i < order.size(); ++i) pos[size_t(order[i])] = int64_t(i);
+  // with counts: chunk c holds rows when its first row lies below its slot's count
+  auto holds = [&](int64_t c) { return !counts || (c % cps) * chunk_rows < counts[c / cps]; };
+  // with counts: rows [lo, hi) hold a row when some slot they meet has rows there
+  auto has_rows = [&](int64_t lo, int64_t hi) {
+    if (!counts) return true;
+    for (int64_t p = lo / m_shard; p <= (hi - 1) / m_shard; ++p)
+      if (std::max(lo, p * m_shard) < p * m_shard + counts[p]) return true;
+    return false;
+  };
   const int64_t tiles = (m + bm - 1) / bm;
   std::vector<int64_t> ready(size_t(tiles), -1);
+  std::vector<int32_t> idx;
+  idx.reserve(size_t(tiles));
   for (int64_t t = 0; t < tiles; ++t) {
     int64_t lo = t * bm, hi = std::min(m, lo + bm);
+    if (!has_rows(lo, hi)) continue;
+    idx.push_back(int32_t(t));
     for (int64_t c = lo / chunk_rows; c <= (hi - 1) / chunk_rows; ++c)
-      if (c / cps != rank) ready[size_t(t)] = std::max(ready[size_t(t)], pos[size_t(c)]);
+      if (c / cps != rank && holds(c)) ready[size_t(t)] = std::max(ready[size_t(t)], pos[size_t(c)]);
   }
-  std::vector<int32_t> idx(static_cast<size_t>(tiles));
-  std::iota(idx.begin(), idx.end(), 0);
   std::stable_sort(idx.begin(), idx.end(),
                    [&](int32_t a, int32_t b) { return ready[size_t(a)] < ready[size_t(b)]; });
   return idx;
@@ -272,6 +283,21 @@ extern "C" int agg_check_ag_args(int world, int rank, int64_t m_shard, int64_t n
   return AGG_OK;
 }
 
+extern "C" int agg_check_a2a_args(int world, int rank, int64_t cap, int64_t n, int64_t k,
+                                  int chunk_rows, int dtype, float scale_a, float scale_b,
+                                  const int32_t* counts, const void* const* peer_src, const void* recv,
+                                  const void* flags, const void* b, const void* c, const int32_t* order,
+                                  int n_order, int mode, agg_stream stream, agg_stream copy_stream) {
+  if (int rc = agg_check_ag_args(world, rank, cap, n, k, chunk_rows, dtype, scale_a, scale_b, peer_src,
+                                 recv, flags, b, c, order, n_order, mode, stream, copy_stream))
+    return rc;
+  if (!counts) return fail(AGG_E_ARG, "counts is NULL");
+  for (int p = 0; p < world; ++p)
+    if (counts[p] < 0 || counts[p] > cap)
+      return fail(AGG_E_ARG, "counts[%d] = %d not in [0, cap = %lld]", p, counts[p], (long long)cap);
+  return AGG_OK;
+}
+
 extern "C" int agg_check_rs_args(int world, int rank, int64_t m, int64_t n, int64_t k, int chunk_rows,
                                  const void* a, const void* b, const void* send, const void* send_flags,
                                  const float* const* peer_src, const void* recv, const void* flags,
@@ -349,6 +375,31 @@ extern "C" int agg_ag_row_tile_order(int world, int rank, int64_t m_shard, int c
   *n_tiles = int(t.size());
   if (int(t.size()) > max_tiles || (!out_tiles && !t.empty()))
     return fail(AGG_E_ARG, "agg_ag_row_tile_order: needs %d entries", int(t.size()));
+  std::copy(t.begin(), t.end(), out_tiles);
+  return AGG_OK;
+}
+
+extern "C" int agg_a2a_row_tile_order(int world, int rank, int64_t cap, int chunk_rows,
+                                      const int32_t* counts, const int32_t* order, int n_order, int bm,
+                                      int32_t* out_tiles, int max_tiles, int* n_tiles) {
+  clear_error();
+  if (world < 1 || world > AGG_MAX_WORLD || rank < 0 || rank >= world || cap < 0 ||
+      chunk_rows < 1 || cap % chunk_rows || bm < 1 || !n_tiles || !counts)
+    return fail(AGG_E_ARG, "agg_a2a_row_tile_order: invalid geometry");
+  for (int p = 0; p < world; ++p)
+    if (counts[p] < 0 || counts[p] > cap) return fail(AGG_E_ARG, "counts[%d] = %d not in [0, cap]", p, counts[p]);
+  const int cps = int(cap / chunk_rows);
+  std::vector<int32_t> ord;
+  if (order) {
+    if (int rc = check_order(world, rank, cps, order, n_order)) return rc;
+    ord.assign(order, order + n_order);
+  } else {
+    ord = ring_order(world, rank, cps);
+  }
+  std::vector<int32_t> t = ag_row_tile_order(world, rank, cap, chunk_rows, ord, bm, counts);
+  *n_tiles = int(t.size());
+  if (int(t.size()) > max_tiles || (!out_tiles && !t.empty()))
+    return fail(AGG_E_ARG, "agg_a2a_row_tile_order: needs %d entries", int(t.size()));
   std::copy(t.begin(), t.end(), out_tiles);
   return AGG_OK;
 }

@@ -44,9 +44,12 @@ int choose_list_cols(int lists, int n_row_tiles, int n_col_tiles, int bm, int bn
 // Every candidate tile shape the kernels are instantiated for.
 const std::vector<TileShape>& tile_shapes();
 
-// Row tiles of the AllGather+GEMM output in computable order (see agg.h).
+// Row tiles of the AllGather+GEMM output in computable order (see agg.h). With `counts`
+// (AllToAll: slot p holds only its first counts[p] rows), chunks that hold no row count as
+// present from the start and row tiles that hold no row are left out.
 std::vector<int32_t> ag_row_tile_order(int world, int rank, int64_t m_shard, int chunk_rows,
-                                       const std::vector<int32_t>& order, int bm);
+                                       const std::vector<int32_t>& order, int bm,
+                                       const int32_t* counts = nullptr);
 
 // Row tiles (block * tiles_per_block + tile) of GEMM+ReduceScatter in compute order.
 std::vector<int32_t> rs_row_tile_order(int world, int rank, int64_t m, int chunk_rows,

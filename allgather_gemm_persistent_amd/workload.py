@@ -1,5 +1,6 @@
-"""Device buffers for one AllGather+GEMM or GEMM+ReduceScatter workload, and calls through the
-binding. PyTorch provides device memory and streams only; every step runs in libagg.
+"""Device buffers for one workload (AllGather, AllToAll, ReduceScatter, AllReduce, the FFN
+chain) and calls through the binding. PyTorch provides device memory and streams only; every
+step runs in libagg.
 
 The emulated peers are ordinary device allocations holding each remote rank's shard (or, for
 ReduceScatter, the partial block it contributes); the symmetric buffers (gather / receive) and
@@ -72,6 +73,38 @@ class AgWorkload:
         if self.ctx is not None:
             B.agg_ctx_destroy(self.ctx)
             self.ctx = None
+
+
+class A2aWorkload(AgWorkload):
+    """One rank's share of AllToAll (dispatch) + GEMM with W-1 emulated sources on one GPU.
+
+    blocks: W CPU tensors (cap x K, bf16 or float8_e4m3fn), what each source sends this rank (its
+    first counts[p] rows hold tokens); counts: W ints; b_kn: CPU tensor (K x N). The receive
+    buffer is the gather buffer of the base class, slot p of `cap` rows per source.
+    """
+
+    def __init__(self, world, rank, blocks, counts, b_kn, chunk_rows, dtype="bf16", scale_a=1.0,
+                 scale_b=1.0, device="cuda", tile=None, producer="cu"):
+        self.counts = [int(x) for x in counts]
+        super().__init__(world, rank, blocks, b_kn, chunk_rows, dtype, scale_a, scale_b, device,
+                         tile, producer)
+        self.cap = self.m_shard
+
+    def reset_local(self):
+        """Place the rank's own routed rows in its slot of the receive buffer."""
+        ms, cnt = self.m_shard, self.counts[self.rank]
+        self.gather[self.rank * ms:self.rank * ms + cnt].copy_(self.local[:cnt])
+
+    def run(self, mode="overlap", order=None, delay_us=None, stream=None):
+        stream = stream or torch.cuda.current_stream(self.device)
+        B.a2a_gemm(self.ctx, self.world, self.rank, self.m_shard, self.n, self.k, self.chunk_rows,
+                   self.dtype, self.scale_a, self.scale_b, self.counts, self.peer_ptrs(), self.gather,
+                   self.flags, self.b, self.c, order=order, delay_us=delay_us, mode=mode,
+                   stream=stream, copy_stream=self.copy_stream)
+
+    def held_rows(self):
+        """Row indices of the receive buffer (and of C) that hold tokens."""
+        return [p * self.m_shard + i for p in range(self.world) for i in range(self.counts[p])]
 
 
 class RsWorkload:

@@ -219,6 +219,10 @@ def measure_block(name, reps, flush, only="all"):
                 setup(setting)
                 run(mode)
                 ran[label] = B.agg_ctx_last_producer(w.ctx)
+        # a copy-only call times no launch under the copy kernel, one where the call fell back to
+        # the in-kernel producer (its copy-only launch of the persistent kernel)
+        variants = [(lb, md, st, (1 if ran.get(lb) == "cu" else 0) if lb == "copy_only_copy_kernel" else n)
+                    for lb, md, st, n in variants]
         torch.cuda.synchronize()
         B.agg_ctx_set_timing(w.ctx, True)
         ev, seq = [], []

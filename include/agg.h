@@ -352,6 +352,44 @@ int ag_gemm_noalloc(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t 
                     const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
                     agg_stream stream, agg_stream copy_stream);
 
+/* ---- AllToAll + GEMM -------------------------------------------------------------------- */
+
+/* One rank's share of an AllToAll (dispatch) and the GEMM on what it delivers: every source
+ * rank p sends this rank the tokens it routed here, counts[p] rows of k (at most `cap`), which
+ * land in slot p of the receive buffer; then C = recv @ B over the rows that hold tokens. The
+ * path is ag_gemm's over slots of `cap` rows that hold only their first counts[p] rows:
+ *   cap              rows per slot (>= 0, a multiple of chunk_rows); M = world * cap
+ *   counts           HOST int32[world], 0 <= counts[p] <= cap: rows source p sends this rank
+ *                    (counts[rank]: the rank's own tokens routed to itself, already in place)
+ *   peer_src         HOST array of `world` device pointers: source p's block for this rank
+ *                    (cap x k, its first counts[p] rows are the tokens); entry `rank` ignored
+ *   recv             device (M x k): the symmetric receive buffer; slot `rank` must already
+ *                    hold the local rows; the producer copies rows [0, counts[p]) of each
+ *                    other slot and leaves the rest of the slot alone
+ *   flags            as ag_gemm's (one per chunk of cr rows of a slot); every flag ends at the
+ *                    call's epoch. A chunk that holds no row (its first row at or past
+ *                    counts[p]) is raised at the start without a copy; a partly filled chunk
+ *                    copies its rows below the count
+ *   b, c             device (k x n) weight, N contiguous; device (M x n) bf16 output. Rows of
+ *                    slot p below counts[p] hold the product; a row tile that holds no token
+ *                    is not computed (its rows of c are left alone); the other rows at or past
+ *                    a count are computed from whatever the receive buffer holds there
+ *   order, n_order   HOST: every remote chunk id in arrival order (as ag_gemm's, empty chunks
+ *                    included; they are raised first whatever their position), NULL = ring
+ *   other arguments  as ag_gemm's (dtype, scales, delay_us, mode, streams); tiles never read
+ *                    the sources' blocks directly (no pull)
+ * Errors: those of ag_gemm with m_shard = cap, AGG_E_ARG for NULL counts or a count outside
+ * [0, cap].
+ * Passage: section "DITRON adds three levels of tiling" (AllToAll among the collectives cut
+ *  into chunks and paired with computation tiles) and section "The first move was to expose
+ *  the overlap" (computation proceeds on the chunks that have arrived).
+ */
+int a2a_gemm(agg_ctx* ctx, int world, int rank, int64_t cap, int64_t n, int64_t k, int chunk_rows,
+             int dtype, float scale_a, float scale_b, const int32_t* counts,
+             const void* const* peer_src, void* recv, uint32_t* flags, const void* b, void* c,
+             const int32_t* order, int n_order, const uint32_t* delay_us, int mode,
+             agg_stream stream, agg_stream copy_stream);
+
 /* ---- GEMM + ReduceScatter -------------------------------------------------------------- */
 
 /* P = A @ B in fp32 (bf16 operands); rows split into `world` blocks of Mb = m/world rows.
@@ -450,7 +488,8 @@ int agg_ctx_set_chain_fused(agg_ctx* ctx, int on);
 /* ---- host-only planning (no device needed; used by the calls above) --------------------- */
 
 /* The tile shape the library uses for a call: *bm x *bn output tiles.
- * op: 0 = ag_gemm, 1 = gemm_rs, 2 = gemm_ar. m is M (ag: world*m_shard).
+ * op: 0 = ag_gemm (and a2a_gemm), 1 = gemm_rs, 2 = gemm_ar. m is M (ag: world*m_shard; a2a:
+ * world*cap).
  * Passage: section "DITRON adds three levels of tiling" (core-level tiles).
  */
 int agg_tile_shape(int op, int dtype, int64_t m, int64_t n, int64_t k, int* bm, int* bn);
@@ -465,6 +504,17 @@ int agg_tile_shape(int op, int dtype, int64_t m, int64_t n, int64_t k, int* bm, 
 int agg_ag_row_tile_order(int world, int rank, int64_t m_shard, int chunk_rows,
                           const int32_t* order, int n_order, int bm, int32_t* out_tiles,
                           int max_tiles, int* n_tiles);
+
+/* The row tiles (of bm rows over the world*cap receive rows) a2a_gemm computes, in the order it
+ * takes them: tiles that hold no token are left out; the others by the arrival position of the
+ * latest chunk they cover that holds rows (local chunks and empty ones count as present from
+ * the start), ties by tile index. Writes *n_tiles entries to out_tiles (max_tiles room);
+ * AGG_E_ARG for bad geometry, counts or order, or too little room.
+ * Passage: section "DITRON adds three levels of tiling" (chunks paired with tiles).
+ */
+int agg_a2a_row_tile_order(int world, int rank, int64_t cap, int chunk_rows, const int32_t* counts,
+                           const int32_t* order, int n_order, int bm, int32_t* out_tiles,
+                           int max_tiles, int* n_tiles);
 
 /* Row-tile order of gemm_rs as (block, tile-in-block) pairs flattened to block*tpb + tile,
  * tpb = ceil(Mb/bm): non-local blocks in send order rank+1, ..., rank+world-1 (mod world), each
@@ -485,6 +535,16 @@ int agg_check_ag_args(int world, int rank, int64_t m_shard, int64_t n, int64_t k
                       const void* gather, const void* flags, const void* b, const void* c,
                       const int32_t* order, int n_order, int mode, agg_stream stream,
                       agg_stream copy_stream);
+
+/* a2a_gemm's argument checks alone (no ctx, no GPU work): agg_check_ag_args with m_shard = cap,
+ * then counts. Returns AGG_OK or the code a2a_gemm would return.
+ * Passage: section "DITRON adds three levels of tiling" (AllToAll chunks).
+ */
+int agg_check_a2a_args(int world, int rank, int64_t cap, int64_t n, int64_t k, int chunk_rows,
+                       int dtype, float scale_a, float scale_b, const int32_t* counts,
+                       const void* const* peer_src, const void* recv, const void* flags,
+                       const void* b, const void* c, const int32_t* order, int n_order, int mode,
+                       agg_stream stream, agg_stream copy_stream);
 int agg_check_rs_args(int world, int rank, int64_t m, int64_t n, int64_t k, int chunk_rows,
                       const void* a, const void* b, const void* send, const void* send_flags,
                       const float* const* peer_src, const void* recv, const void* flags,

@@ -124,12 +124,48 @@ def test_tile_shapes_for_the_workloads(lib):
     for name, cfg in configs.CONFIGS.items():
         if cfg.op == "ffn":
             continue                       # the chain's kernel is instantiated for 256 x 256 only
-        op = {"ag": 0, "rs": 1, "ar": 2}[cfg.op]
+        op = {"ag": 0, "a2a": 0, "rs": 1, "ar": 2}[cfg.op]
         got[name] = B.agg_tile_shape(op, cfg.dtype, cfg.m, cfg.n, cfg.k)
     assert got["ag_w8_4096x3584x8192_bf16"] == (256, 224)     # 16 x 16 = 256 tiles
     assert got["rs_w8_8192x8192x3584_bf16"] == (256, 256)     # 32 x 32 = 1024 tiles
     assert got["ag_w8_8192x7168x8192_fp8"] == (256, 224)      # 32 x 32 = 1024 tiles
     assert got["ar_w8_128x8192x3584_bf16_decode"] == (64, 64)  # 2 x 128 = 256 tiles
+    assert got["a2a_w8_5120x3584x8192_bf16"] == (128, 128)    # 40 x 28 = 1120 tiles of capacity
+
+
+def _a2a(**kw):
+    args = dict(world=3, rank=1, cap=64, n=256, k=512, chunk_rows=16, dtype="bf16", scale_a=1.0,
+                scale_b=1.0, counts=[10, 64, 0], peer_src=[FAKE, FAKE, FAKE], recv=FAKE, flags=FAKE,
+                b=FAKE, c=FAKE, order=None, mode="overlap", stream=1, copy_stream=2)
+    args.update(kw)
+    return B.agg_check_a2a_args(**args)
+
+
+def test_a2a_args(lib):
+    assert _a2a() == B.AGG_OK
+    assert _a2a(counts=[0, 0, 0]) == B.AGG_OK
+    assert _a2a(counts=[64, 64, 64], order=[11, 0, 10, 1, 2, 3, 8, 9]) == B.AGG_OK
+    for kw in (dict(counts=None), dict(counts=[65, 0, 0]), dict(counts=[0, -1, 0]),
+               dict(cap=60), dict(order=[0, 1]), dict(peer_src=[FAKE, FAKE, None]),
+               dict(recv=FAKE + 4), dict(world=9)):
+        assert _a2a(**kw) == B.AGG_E_ARG, kw
+        assert B.last_error()
+
+
+@pytest.mark.parametrize("world,rank,cap,cr,bm,seed", [
+    (2, 0, 128, 64, 64, 1), (8, 0, 640, 128, 256, 0), (3, 2, 12, 4, 8, 3), (5, 1, 60, 12, 128, 5),
+    (1, 0, 100, 10, 64, 0), (4, 3, 32, 8, 16, 2)])
+def test_a2a_row_tile_order_matches_oracle(lib, world, rank, cap, cr, bm, seed):
+    cps = cap // cr
+    gen = inputs.SplitMix64(1234 + seed)
+    for trial in range(6):
+        counts = [[0, cap, int(gen.next() % (cap + 1))][int(gen.next() % 3)] for _ in range(world)]
+        order = inputs.ring_order(world, rank, cps) if seed == 0 else \
+            inputs.seeded_order(world, rank, cps, seed + trial)
+        want = O.a2a_mtile_order(world, rank, cap, cr, counts, order, bm)
+        assert B.agg_a2a_row_tile_order(world, rank, cap, cr, counts, order, bm) == want, counts
+    with pytest.raises(B.AggError):
+        B.agg_a2a_row_tile_order(world, rank, cap, cr, [cap + 1] * world, None, bm)
 
 
 def test_ctx_calls_reject_null(lib):

@@ -1,0 +1,221 @@
+"""AllToAll (dispatch) + GEMM on the GPU through the C ABI, compared with the CPU oracle.
+
+Bar: bf16 |C - ref| <= 1e-2 + 1e-2 |ref|, fp8 <= 2e-2 + 2e-2 |ref| on the rows that hold
+tokens; bit-exact for the receive buffer's token rows, for the rows the call must leave alone
+(receive rows past a source's count, C rows of tiles that hold no token), for the flags, and for
+integer-valued inputs.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from allgather_gemm_persistent_amd import binding as B
+from allgather_gemm_persistent_amd import configs, inputs
+from allgather_gemm_persistent_amd.workload import A2aWorkload
+from oracle import agg_oracle as O
+
+from helpers import BF16_TOL, FP8_TOL, assert_close, bits_equal, raw, to_f64
+
+pytestmark = pytest.mark.gpu
+
+TILES = [(256, 256), (256, 224), (128, 128), (128, 64), (64, 64)]
+PRODUCERS = ["cu", "sdma", "kernel"]
+SENTINEL_BF16 = 0x7FC1      # a NaN pattern no product yields: marks rows a call must not write
+
+
+def _blocks(world, cap, k, n, dtype, seed, kind="normal"):
+    if kind == "int":
+        da = db = {"kind": "int", "lo": -2, "hi": 2}
+    else:
+        da, db = {"kind": "normal", "std": 1.0}, {"kind": "normal", "std": 0.05}
+    a, sa = inputs.draw(da, (world * cap, k), dtype, seed)
+    b, sb = inputs.draw(db, (k, n), dtype, seed + 7)
+    return [a[p * cap:(p + 1) * cap].contiguous() for p in range(world)], b, sa, sb
+
+
+def _fill_sentinel(w):
+    """Receive rows past every count and all of C hold a sentinel before the call."""
+    byte = 0x5A
+    for p in range(w.world):
+        lo = p * w.cap + w.counts[p]
+        w.gather[lo:(p + 1) * w.cap].view(torch.uint8).fill_(byte)
+    w.c.view(torch.int16).fill_(SENTINEL_BF16)
+    w.reset_local()
+
+
+def _check(w, blocks, b, dtype, sa, sb, what, untouched_recv=True):
+    """Token rows of the receive buffer equal the sources' rows; C's token rows match the oracle;
+    rows past the counts of the receive buffer are untouched; C rows of tiles that hold no token
+    keep the sentinel; every flag holds the epoch."""
+    cap = w.cap
+    g = w.gather.cpu()
+    for p in range(w.world):
+        cnt = w.counts[p]
+        assert bits_equal(g[p * cap:p * cap + cnt], blocks[p][:cnt]), (what, p)
+        if untouched_recv:
+            rest = g[p * cap + cnt:(p + 1) * cap].contiguous().view(torch.uint8)
+            assert bool((rest == 0x5A).all()), (what, "receive rows past the count were written", p)
+    ref = O.a2a_gemm_ref([raw(blocks[p][:w.counts[p]]) for p in range(w.world)], raw(b), dtype, sa, sb)
+    c = to_f64(w.c)
+    tol = FP8_TOL if dtype == "fp8" else BF16_TOL
+    for p in range(w.world):
+        if w.counts[p]:
+            assert_close(c[p * cap:p * cap + w.counts[p]], ref[p], tol, f"{what} C slot {p}")
+    e = B.agg_ctx_epoch(w.ctx)
+    assert (w.flags.cpu().numpy() == e).all(), (what, w.flags.cpu().numpy(), e)
+
+
+def _untouched_tiles(w, bm):
+    """C rows of row tiles that hold no token still hold the sentinel."""
+    craw = w.c.cpu().view(torch.int16)
+    for t in range(-(-w.world * w.cap // bm)):
+        lo, hi = t * bm, min((t + 1) * bm, w.world * w.cap)
+        if not any((x % w.cap) < w.counts[x // w.cap] for x in range(lo, hi)):
+            assert bool((craw[lo:hi] == SENTINEL_BF16).all()), ("tile without tokens written", t)
+
+
+CASES = [  # world, rank, cap, k, n, cr, counts
+    (3, 1, 96, 264, 200, 32, [70, 96, 0]),
+    (4, 0, 128, 256, 256, 32, [128, 5, 0, 100]),
+    (2, 1, 160, 320, 136, 40, [0, 33]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("mode", ["overlap", "serial"])
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_ragged_counts_vs_oracle(gpu, case, tile, mode, producer):
+    world, rank, cap, k, n, cr, counts = CASES[case]
+    blocks, b, sa, sb = _blocks(world, cap, k, n, "bf16", seed=100 + case)
+    w = A2aWorkload(world, rank, blocks, counts, b, cr, tile=tile, producer=producer)
+    try:
+        _fill_sentinel(w)
+        w.run(mode, order=inputs.seeded_order(world, rank, cap // cr, 3 + case))
+        assert w.status() == (0, -1)
+        _check(w, blocks, b, "bf16", sa, sb, (case, tile, mode, producer))
+        _untouched_tiles(w, tile[0])
+    finally:
+        w.close()
+
+
+@pytest.mark.parametrize("tile", [(256, 224), (128, 64), (64, 64)])
+def test_fp8_and_integer_inputs(gpu, tile):
+    """fp8 within its bar; integer-valued bf16 inputs bit-exact (every fp32 sum exact)."""
+    world, rank, cap, k, n, cr, counts = 4, 2, 64, 512, 208, 16, [64, 17, 0, 50]
+    blocks, b, sa, sb = _blocks(world, cap, k, n, "fp8", seed=151)
+    w = A2aWorkload(world, rank, blocks, counts, b, cr, dtype="fp8", scale_a=sa, scale_b=sb, tile=tile)
+    try:
+        _fill_sentinel(w)
+        w.run("overlap")
+        assert w.status() == (0, -1)
+        _check(w, blocks, b, "fp8", sa, sb, ("fp8", tile))
+    finally:
+        w.close()
+    blocks, b, _, _ = _blocks(world, cap, k, n, "bf16", seed=161, kind="int")
+    w = A2aWorkload(world, rank, blocks, counts, b, cr, tile=tile)
+    try:
+        _fill_sentinel(w)
+        w.run("overlap")
+        assert w.status() == (0, -1)
+        ref = O.a2a_gemm_ref([raw(blocks[p][:counts[p]]) for p in range(world)], raw(b))
+        craw = raw(w.c)
+        for p in range(world):
+            assert np.array_equal(craw[p * cap:p * cap + counts[p]], O.encode_bf16_rne(ref[p])), p
+    finally:
+        w.close()
+
+
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_orders_and_modes_bit_identical(gpu, producer):
+    world, rank, cap, k, n, cr, counts = 8, 3, 64, 256, 256, 16, [64, 0, 33, 16, 1, 64, 47, 8]
+    blocks, b, sa, sb = _blocks(world, cap, k, n, "bf16", seed=171)
+    w = A2aWorkload(world, rank, blocks, counts, b, cr, tile=(64, 64), producer=producer)
+    try:
+        outs = []
+        for s in (None, 1, 2):
+            order = None if s is None else inputs.seeded_order(world, rank, cap // cr, s)
+            for mode in ("overlap", "serial", "gemm_only"):
+                if mode != "gemm_only":
+                    _fill_sentinel(w)
+                w.run(mode, order=order)
+                assert w.status() == (0, -1)
+                outs.append(w.c.clone())
+        rows = w.held_rows()
+        for o in outs[1:]:
+            assert bits_equal(o[rows], outs[0][rows])
+        _check(w, blocks, b, "bf16", sa, sb, producer)
+    finally:
+        w.close()
+
+
+def test_no_tokens_anywhere(gpu):
+    """Every count zero: no tile is computed (C untouched) and every flag still ends at the
+    epoch; the call with host delays keeps the empty chunks first."""
+    world, rank, cap, k, n, cr = 4, 1, 32, 128, 64, 16
+    blocks, b, _, _ = _blocks(world, cap, k, n, "bf16", seed=181)
+    for producer in PRODUCERS:
+        w = A2aWorkload(world, rank, blocks, [0] * world, b, cr, producer=producer)
+        try:
+            _fill_sentinel(w)
+            w.run("overlap", delay_us=inputs.delays_us((world - 1) * cap // cr, 5, 20))
+            assert w.status() == (0, -1)
+            assert bool((w.c.cpu().view(torch.int16) == SENTINEL_BF16).all()), producer
+            assert (w.flags.cpu().numpy() == B.agg_ctx_epoch(w.ctx)).all(), producer
+        finally:
+            w.close()
+
+
+def test_config_vs_oracle(gpu):
+    """The W=8 AllToAll workload at full size: the harness's blocks equal the oracle's dispatch
+    of the routed tokens; the overlapped call matches the oracle on every token row; serialized,
+    copy-engine and copy-kernel runs give the same bits; every flag holds the epoch."""
+    cfg = configs.CONFIGS["a2a_w8_5120x3584x8192_bf16"]
+    d = configs.make_a2a_data(cfg)
+    want = O.a2a_dispatch_ref([raw(t) for t in d["tokens"]], d["dests"], cfg.rank, cfg.cap)
+    for p in range(cfg.world):
+        assert np.array_equal(raw(d["blocks"][p][:d["counts"][p]]), want[p]), p
+    w = A2aWorkload(cfg.world, cfg.rank, d["blocks"], d["counts"], d["b"], cfg.chunk_rows)
+    try:
+        print("config a2a: overlap", flush=True)
+        _fill_sentinel(w)
+        w.run("overlap", order=cfg.order())
+        assert w.status() == (0, -1)
+        _check(w, d["blocks"], d["b"], "bf16", 1.0, 1.0, "overlap")
+        rows = w.held_rows()
+        c1 = w.c[rows].clone()
+        for producer, mode in (("cu", "serial"), ("sdma", "overlap"), ("kernel", "overlap")):
+            print(f"config a2a: {producer} {mode}", flush=True)
+            B.agg_ctx_set_producer(w.ctx, producer)
+            _fill_sentinel(w)
+            w.run(mode, order=cfg.order())
+            assert w.status() == (0, -1), (producer, mode)
+            assert bits_equal(w.c[rows], c1), (producer, mode)
+            g = w.gather.cpu()
+            for p in range(cfg.world):
+                cnt = d["counts"][p]
+                assert bits_equal(g[p * cfg.cap:p * cfg.cap + cnt], d["blocks"][p][:cnt]), (producer, p)
+            assert (w.flags.cpu().numpy() == B.agg_ctx_epoch(w.ctx)).all(), (producer, mode)
+    finally:
+        w.close()
+
+
+def test_small_config_dispatch(gpu):
+    """A test-sized copy of the workload (same routing, fewer tokens): routing, capacity drops
+    and the whole call against the oracle."""
+    cfg = dataclasses.replace(configs.CONFIGS["a2a_w8_5120x3584x8192_bf16"], tokens=512, cap=80,
+                              k=256, n=192, chunk_rows=16)
+    d = configs.make_a2a_data(cfg)
+    want = O.a2a_dispatch_ref([raw(t) for t in d["tokens"]], d["dests"], cfg.rank, cfg.cap)
+    assert [len(x) for x in want] == d["counts"]
+    w = A2aWorkload(cfg.world, cfg.rank, d["blocks"], d["counts"], d["b"], cfg.chunk_rows)
+    try:
+        _fill_sentinel(w)
+        w.run("overlap", order=cfg.order())
+        assert w.status() == (0, -1)
+        _check(w, d["blocks"], d["b"], "bf16", 1.0, 1.0, "small")
+    finally:
+        w.close()
