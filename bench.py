@@ -15,10 +15,11 @@ dominant kernel's roofline (its own duration from timing events on the stream it
 the CPU oracle's rate on the same workload as a baseline.
 
 `configs` holds one block per workload (the two AllGather+GEMM sizes, ReduceScatter, decode, fp8,
-decode GEMM+AllReduce, the FFN chain): the same four modes interleaved call by call, each call
-preceded (outside its timed span) by a 512 MiB write that evicts the caches, so every byte comes
-from HBM; R, eta and the roofline of the bare and the overlapped kernel against the bound that
-applies (MFMA bf16 or fp8, HBM bytes, or launch latency).
+decode GEMM+AllReduce, the FFN chain, AllToAll+GEMM): the same four modes interleaved call by
+call, each call preceded (outside its timed span) by a 512 MiB write that evicts the caches, so
+every byte comes from HBM; R, eta and the roofline of the bare and the overlapped kernel against
+the bound that applies (MFMA bf16 or fp8, HBM bytes, or launch latency); the overlap with the
+copy kernel as producer (R_copy_kernel), and with pull off where pulling applies.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -46,7 +47,7 @@ TRAFFIC_RECORDS = {"ag_w8_4096x3584x8192_bf16": "gemm_kernel_256x224_bf16_ag_w8_
 BOUND = {"ag_w2_256x256x512_bf16": "latency", "ag_w8_4096x3584x8192_bf16": "mfma",
          "rs_w8_8192x8192x3584_bf16": "mfma", "ag_w8_128x3584x8192_bf16_decode": "hbm",
          "ag_w8_8192x7168x8192_fp8": "mfma", "ar_w8_128x8192x3584_bf16_decode": "hbm",
-         "ffn_w8_4096x8192x3584_bf16": "mfma"}
+         "ffn_w8_4096x8192x3584_bf16": "mfma", "a2a_w8_5120x3584x8192_bf16": "mfma"}
 # workloads where pulling remote rows is possible: also timed with pull off (flag-gated push)
 PULL_VARIANTS = {"ag_w2_256x256x512_bf16", "ag_w8_128x3584x8192_bf16_decode"}
 FLUSH_BYTES = 512 << 20
@@ -138,10 +139,21 @@ def rnd(x, d=1):
 # ------------------------------------------------------------------------ per-workload blocks
 
 def make_workload(name):
-    """(cfg, workload object, algorithmic bytes of the bare kernel, bytes the copy moves)."""
+    """(cfg, workload object, algorithmic bytes of the bare kernel, bytes the copy moves, flops)."""
     from allgather_gemm_persistent_amd import configs
-    from allgather_gemm_persistent_amd.workload import AgWorkload, ArWorkload, FfnWorkload, RsWorkload
+    from allgather_gemm_persistent_amd.workload import (A2aWorkload, AgWorkload, ArWorkload, FfnWorkload,
+                                                        RsWorkload)
     cfg = configs.CONFIGS[name]
+    if cfg.op == "a2a":
+        d = configs.make_a2a_data(cfg)
+        w = A2aWorkload(cfg.world, cfg.rank, d["blocks"], d["counts"], d["b"], cfg.chunk_rows, cfg.dtype,
+                        d["scale_a"], d["scale_b"])
+        el = 1 if cfg.dtype == "fp8" else 2
+        rows = sum(d["counts"])
+        # the rows that hold tokens: read once, their products written; the weight read once
+        bare = rows * cfg.k * el + cfg.k * cfg.n * el + rows * cfg.n * 2
+        copy = (rows - d["counts"][cfg.rank]) * cfg.k * el
+        return cfg, w, bare, copy, 2 * rows * cfg.k * cfg.n
     if cfg.op == "ag":
         d = configs.make_ag_data(cfg)
         w = AgWorkload(cfg.world, cfg.rank, d["shards"], d["b"], cfg.chunk_rows, cfg.dtype,
@@ -173,7 +185,7 @@ def make_workload(name):
         copy = (cfg.world - 1) * mb * (cfg.k1 * 2 + cfg.n2 * 4)
     else:
         raise ValueError(cfg.op)
-    return cfg, w, bare, copy
+    return cfg, w, bare, copy, cfg.flops
 
 
 def measure_block(name, reps, flush, only="all"):
@@ -181,7 +193,7 @@ def measure_block(name, reps, flush, only="all"):
     import torch
 
     from allgather_gemm_persistent_amd import binding as B
-    cfg, w, bare_bytes, copy_bytes = make_workload(name)
+    cfg, w, bare_bytes, copy_bytes, flops = make_workload(name)
     ffn = cfg.op == "ffn"
     # (label, mode, pull setting or chain fusion, timed kernel launches per call)
     variants = [("overlap", "overlap", "auto", 1), ("gemm_only", "gemm_only", "auto", 1),
@@ -246,7 +258,8 @@ def measure_block(name, reps, flush, only="all"):
         if ffn:
             bm, bn = 256, 256
         else:
-            bm, bn = B.agg_tile_shape({"ag": 0, "rs": 1, "ar": 2}[cfg.op], cfg.dtype, cfg.m, cfg.n, cfg.k)
+            bm, bn = B.agg_tile_shape({"ag": 0, "a2a": 0, "rs": 1, "ar": 2}[cfg.op], cfg.dtype, cfg.m, cfg.n,
+                                      cfg.k)
     finally:
         B.agg_ctx_set_timing(w.ctx, False)
         w.close()
@@ -265,7 +278,6 @@ def measure_block(name, reps, flush, only="all"):
     R = call["overlap"] / call["gemm_only"]
     eta = (call["serial"] - call["overlap"]) / min(call["copy_only"], call["gemm_only"])
     bound = BOUND[name]
-    flops = cfg.flops
 
     def roof(kernel_us, bytes_):
         if bound == "mfma":
@@ -292,6 +304,10 @@ def measure_block(name, reps, flush, only="all"):
         # the symmetric buffer (CU producer)
         "roofline_overlap": roof(kern["overlap"], bare_bytes + 2 * copy_bytes) if kern else None,
     }
+    if cfg.op == "a2a":
+        block["token_rows"] = flops // (2 * cfg.k * cfg.n)
+        block["note_a2a"] = ("flops and bytes count the rows that hold tokens; tiles that straddle a"
+                             " slot's count also compute the rows past it")
     if ffn:
         block["fusion_speedup"] = rnd(call["overlap_unfused"] / call["overlap"], 3)
         block["fusion_speedup_bare"] = rnd(call["gemm_only_unfused"] / call["gemm_only"], 3)

@@ -130,7 +130,7 @@ def test_tile_shapes_for_the_workloads(lib):
     assert got["rs_w8_8192x8192x3584_bf16"] == (256, 256)     # 32 x 32 = 1024 tiles
     assert got["ag_w8_8192x7168x8192_fp8"] == (256, 224)      # 32 x 32 = 1024 tiles
     assert got["ar_w8_128x8192x3584_bf16_decode"] == (64, 64)  # 2 x 128 = 256 tiles
-    assert got["a2a_w8_5120x3584x8192_bf16"] == (128, 128)    # 40 x 28 = 1120 tiles of capacity
+    assert got["a2a_w8_5120x3584x8192_bf16"] == (256, 224)    # 20 x 16 = 320 tiles of capacity
 
 
 def _a2a(**kw):
