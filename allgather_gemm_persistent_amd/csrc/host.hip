@@ -265,7 +265,7 @@ int grid_for(agg_ctx* ctx, int64_t tiles, bool overlapped) {
 template <typename Launch, typename Put>
 int schedule(agg_ctx* ctx, int mode, hipStream_t s, hipStream_t us,
              const std::vector<hipStream_t>& cstreams, bool kernel, Launch launch, bool chunks,
-             Put put_all) {
+             Put put_all, hipStream_t ks) {
   HIP_TRY(hipEventRecord(ctx->ev_fork, s));
   if (chunks) {
     if (us) HIP_TRY(hipEventRecord(ctx->ev_user, us));
@@ -283,26 +283,31 @@ int schedule(agg_ctx* ctx, int mode, hipStream_t s, hipStream_t us,
     return AGG_OK;
   };
   if (mode == AGG_OVERLAP) {
+    // the kernel on the caller's stream: the copies go first, so that nothing enqueued later
+    // can hold them behind the kernel that waits for them
+    if (chunks && ks == s)
+      if (int rc = put_all()) return rc;
     if (kernel) {
-      HIP_TRY(hipStreamWaitEvent(ctx->ks, ctx->ev_fork, 0));
+      if (ks != s) HIP_TRY(hipStreamWaitEvent(ks, ctx->ev_fork, 0));
       if (int rc = launch()) return rc;
     }
     if (chunks) {
-      if (int rc = put_all()) return rc;
+      if (ks != s)
+        if (int rc = put_all()) return rc;
       if (int rc = join_copies(s)) return rc;
     }
   } else {
     if (chunks) {
       if (int rc = put_all()) return rc;
-      if (int rc = join_copies(kernel ? ctx->ks : s)) return rc;
+      if (int rc = join_copies(kernel ? ks : s)) return rc;
     }
     if (kernel) {
-      HIP_TRY(hipStreamWaitEvent(ctx->ks, ctx->ev_fork, 0));
+      if (ks != s) HIP_TRY(hipStreamWaitEvent(ks, ctx->ev_fork, 0));
       if (int rc = launch()) return rc;
     }
   }
-  if (kernel) {
-    HIP_TRY(hipEventRecord(ctx->ev_kernel, ctx->ks));
+  if (kernel && ks != s) {
+    HIP_TRY(hipEventRecord(ctx->ev_kernel, ks));
     HIP_TRY(hipStreamWaitEvent(s, ctx->ev_kernel, 0));
   }
   return AGG_OK;
@@ -537,6 +542,11 @@ int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int
   HIP_TRY(go());
   return AGG_OK;
 }
+
+// Whether the consumer kernel may run on the caller's stream beside the copy kernel: not on the
+// legacy default stream (or the per-thread one), whose implicit synchronisation would hold the
+// copy kernel's stream behind the consumer that waits for it.
+bool own_queue_free(hipStream_t s) { return s != nullptr && s != hipStreamPerThread; }
 
 // The producer a call runs: the ctx's choice, except that the copy kernel (AGG_PRODUCER_KERNEL)
 // gives way to copy jobs inside the GEMM kernel where it cannot run beside it (the GEMM kernel
@@ -1074,10 +1084,14 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
                                           timed, marks, pull_copiers);
                        });
   }
+  // the copy engines' producer keeps the kernel on a queue of its own (see the top of this
+  // file); beside the copy kernel it runs on the caller's stream where that stream allows it
+  // (no fork and join of the kernel's queue)
+  hipStream_t ls = prod == AGG_PRODUCER_KERNEL && own_queue_free(s) ? s : ctx->ks;
   auto launch = [&]() -> int {
     return timed_launch(ctx, [&]() {
-      return launch_gemm(g, ts.bm, ts.bn, dtype, kEpiAllGather, grid, ctx->ks);
-    });
+      return launch_gemm(g, ts.bm, ts.bn, dtype, kEpiAllGather, grid, ls);
+    }, ls);
   };
   const CopyPlan kplan{cc, flags, ord.size()};
   Marks kmarks;
@@ -1091,7 +1105,7 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
     if (prod == AGG_PRODUCER_KERNEL)
       return launch_copy_producer(ctx, sp.words, &kplan, 1, world, epoch, kmarks, cstreams[0]);
     return produce(cc, flags, ord, delay_us, epoch, cstreams, rank);
-  });
+  }, ls);
 }
 
 }  // namespace
@@ -1229,10 +1243,11 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
                                           marks);
                        });
   }
+  hipStream_t ls = prod == AGG_PRODUCER_KERNEL && own_queue_free(s) ? s : ctx->ks;
   auto launch = [&]() -> int {
     return timed_launch(ctx, [&]() {
-      return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiReduceScatter, grid, ctx->ks);
-    });
+      return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiReduceScatter, grid, ls);
+    }, ls);
   };
   const CopyPlan kplan{cc, flags, ord.size()};
   Marks kmarks;
@@ -1246,7 +1261,7 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
     if (prod == AGG_PRODUCER_KERNEL)
       return launch_copy_producer(ctx, sp.words, &kplan, 1, world, epoch, kmarks, cstreams[0]);
     return produce(cc, flags, ord, delay_us, epoch, cstreams, rank);
-  });
+  }, ls);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1346,8 +1361,9 @@ extern "C" int gemm_ar(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
                                           marks);
                        });
   }
+  hipStream_t ls = prod == AGG_PRODUCER_KERNEL && own_queue_free(s) ? s : ctx->ks;
   auto launch = [&]() -> int {
-    return timed_launch(ctx, [&]() { return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiAllReduce, grid, ctx->ks); });
+    return timed_launch(ctx, [&]() { return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiAllReduce, grid, ls); }, ls);
   };
   const CopyPlan kplan{cc, flags, ord.size()};
   Marks kmarks;
@@ -1361,7 +1377,7 @@ extern "C" int gemm_ar(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
     if (prod == AGG_PRODUCER_KERNEL)
       return launch_copy_producer(ctx, sp.words, &kplan, 1, world, epoch, kmarks, cstreams[0]);
     return produce(cc, flags, ord, delay_us, epoch, cstreams, rank);
-  });
+  }, ls);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1524,9 +1540,10 @@ extern "C" int ffn_chain(agg_ctx* ctx, int world, int rank, int64_t m_shard, int
                          });
                        });
   }
+  hipStream_t ls = prod == AGG_PRODUCER_KERNEL && own_queue_free(s) ? s : ctx->ks;
   auto launch = [&]() -> int {
     return tile_launches([&](const GemmArgs& gg, bool) {
-      return timed_launch(ctx, [&]() { return launch_gemm(gg, ts.bm, ts.bn, AGG_BF16, kEpiFfn, grid, ctx->ks); });
+      return timed_launch(ctx, [&]() { return launch_gemm(gg, ts.bm, ts.bn, AGG_BF16, kEpiFfn, grid, ls); }, ls);
     });
   };
   Marks kmarks;
@@ -1546,7 +1563,7 @@ extern "C" int ffn_chain(agg_ctx* ctx, int world, int rank, int64_t m_shard, int
       return launch_copy_producer(ctx, sp.words, plans, 2, world, epoch, kmarks, cstreams[0]);
     if (int rc = produce(plans[0].cc, flags, ord, nullptr, epoch, cstreams, rank)) return rc;
     return produce(plans[1].cc, rs_flags, ord2, nullptr, epoch, cstreams, rank);
-  });
+  }, ls);
 }
 
 // ------------------------------------------------------------------------------------------

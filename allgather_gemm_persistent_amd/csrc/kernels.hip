@@ -195,9 +195,10 @@ __device__ inline uint32_t bf16x2_rne(float lo, float hi) {
 constexpr int kStoreSystemCoherent = 1 | 16;
 
 // Copy `bytes` (a multiple of 16, < 2 GiB) from src to dst with the whole workgroup: 16-byte
-// vectors in groups of sixteen per thread, software-pipelined over two register sets so that
-// the loads of group g+1 are issued before the stores of group g (one counter tracks loads and
-// stores in issue order, so a load wait never waits for the stores issued after it). The
+// vectors in groups of U per thread, software-pipelined over two register sets so that the
+// loads of group g+1 are issued before the stores of group g (one counter tracks loads and
+// stores in issue order, so a load wait never waits for the stores issued after it), then the
+// partial last group with all its loads ahead of its stores. The
 // source (a peer's block) is read once: non-temporal loads; the stores write through. On return
 // every store of the calling thread has completed.
 template <int NT, int U = 16>
@@ -242,7 +243,15 @@ __device__ inline void copy_piece(uint8_t* __restrict__ dst, const uint8_t* __re
       i += kStep;
     }
   }
-  for (; i < n16; i += NT) put(i, __builtin_nontemporal_load(s + i));
+  // the tail: fewer than U vectors per thread are left; all their loads go out before the first
+  // store (one load-to-store round trip, not one per vector)
+  u32x4 vt[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (i + (int64_t)u * NT < n16) vt[u] = __builtin_nontemporal_load(s + i + (int64_t)u * NT);
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (i + (int64_t)u * NT < n16) put(i + (int64_t)u * NT, vt[u]);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 

@@ -62,6 +62,46 @@ def test_register_counts_and_kernel_producer_choice(gpu):
             w.close()
 
 
+@pytest.mark.parametrize("mode", ["overlap", "serial", "gemm_only"])
+def test_kernel_producer_on_a_side_stream(gpu, mode):
+    """On a stream of the caller's own (not the legacy default one) the consumer kernel runs on
+    that stream beside the copy kernel; every op gives the bits the in-kernel producer gives."""
+    from allgather_gemm_persistent_amd.workload import A2aWorkload, ArWorkload, RsWorkload
+    side = torch.cuda.Stream()
+    rng = 211
+    shards, b, _, _ = small_ag_data(4, 96, 256, 224, "bf16", seed=rng)
+    a, _ = inputs.draw({"kind": "normal", "std": 1.0}, (384, 256), "bf16", rng + 1)
+    peers_rs, _ = inputs.draw({"kind": "normal", "std": 1.0}, (4, 96, 224), "f32", rng + 2)
+    peers_ar, _ = inputs.draw({"kind": "normal", "std": 1.0}, (4, 384, 224), "f32", rng + 3)
+    makers = {
+        "ag": lambda prod: AgWorkload(4, 1, shards, b, 32, tile=(256, 224), producer=prod),
+        "rs": lambda prod: RsWorkload(4, 1, a, b, peers_rs, 32, tile=(64, 64), producer=prod),
+        "ar": lambda prod: ArWorkload(4, 1, a, b, peers_ar, 32, tile=(64, 64), producer=prod),
+        "a2a": lambda prod: A2aWorkload(4, 1, shards, [96, 40, 0, 77], b, 32, tile=(256, 224), producer=prod),
+    }
+    for op, make in makers.items():
+        outs = {}
+        for prod in ("cu", "kernel"):
+            w = make(prod)
+            try:
+                if mode == "gemm_only":
+                    w.run("overlap")                  # gather first; then time the bare kernel
+                with torch.cuda.stream(side):
+                    w.run(mode, stream=side)
+                torch.cuda.synchronize()
+                assert w.status() == (0, -1), (op, prod, mode)
+                assert B.agg_ctx_last_producer(w.ctx) == prod, (op, prod)
+                res = w.c if op in ("ag", "a2a") else w.out
+                outs[prod] = res.clone()
+            finally:
+                w.close()
+        if op == "a2a":
+            rows = [p * 96 + i for p, cnt in enumerate([96, 40, 0, 77]) for i in range(cnt)]
+            assert bits_equal(outs["cu"][rows], outs["kernel"][rows]), (op, mode)
+        else:
+            assert bits_equal(outs["cu"], outs["kernel"]), (op, mode)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("tile", TILES)
 def test_identity_weight_gives_gather_bitexact(gpu, dtype, tile):
