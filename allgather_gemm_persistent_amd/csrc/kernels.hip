@@ -7,22 +7,31 @@
 // tiles, with synchronization inserted).
 //
 // Design, per workgroup (256 threads = 4 wave64s, 2 x 2 over the tile; 4 x 1 for fp8 tiles
-// whose half width is not a multiple of 32):
+// whose half width is not a multiple of 32; one workgroup per CU):
+//   copy jobs first (the in-kernel producer): pieces of the remote chunks in arrival order,
+//     the workgroup completing a chunk raising its flag; block 0 raises the local chunks' flags
 //   loop:
 //     claim a tile from this XCD's list (atomic counter), stealing from other XCDs' lists when
 //       its own is exhausted; lists hold row tiles in arrival order, so early chunks are
-//       computed first; a workgroup never waits on another workgroup, only on chunk flags
-//     wave 0 polls the flags of the chunks the tile's rows overlap (relaxed system-scope
-//       loads, s_sleep back-off, bounded by a wall-clock limit), then an acquire fence
-//     K loop: 64-byte-wide K slices (32 bf16 or 64 fp8) of the A and B tiles go straight from
-//       global memory to LDS (direct-to-LDS buffer loads, swizzled 16-byte chunks, four
-//       stages, one barrier per slice); MFMA 16x16x32 bf16 or 32x32x64 f8f6f4 blocks
-//       accumulate in fp32
-//     epilogue: AllGather -> bf16 (round to nearest even) rows of C; ReduceScatter -> fp32
-//       partial rows to `send` (non-local blocks, then a per-chunk completion counter and a
-//       release store of the send flag) or, for the local block, the accumulator plus the
-//       incoming partials of every peer in ascending rank order.
-//   the last workgroup to finish resets the claim counters for the next launch.
+//       computed first
+//     wave 0 polls the flags of the chunks the tile's rows need (relaxed system-scope loads,
+//       s_sleep back-off, bounded by a wall-clock limit), then an acquire fence
+//     K loop: 64-byte-wide K slices (32 bf16 or 64 fp8) of the A rows (K contiguous) and of the
+//       B rows (K x N, N contiguous) go straight from global memory to LDS (direct-to-LDS buffer
+//       loads into swizzled stages or slice-pair regions below 128 KiB, one barrier per slice);
+//       A fragments come from plain LDS reads, B fragments from gfx950's transposing LDS reads;
+//       MFMA 16x16x32 bf16 or 32x32x64 f8f6f4 blocks accumulate in fp32
+//     epilogue, by operation: AllGather -> bf16 (round to nearest even) rows of C; ReduceScatter
+//       -> fp32 partial rows to `send` (non-local blocks; a per-chunk completion counter
+//       releases the send flag) or to `out` (the local block); AllReduce -> the partial to
+//       `send` with its send flag, then, once the peers' chunks of its rows have arrived, the
+//       sum over ranks in ascending order to `out`; FFN chain -> SiLU and bf16 rows of h for
+//       the first layer's tiles (which release the second layer's rows), the ReduceScatter
+//       epilogue for the second layer's
+//   ReduceScatter and the FFN chain then reduce the local block over the whole grid
+//   the last workgroup to finish resets the counters for the next launch.
+// A workgroup waits only on chunk flags or on tiles claimed before its own (split-K parts of a
+// tile that all hold a workgroup; the FFN chain's second layer), so the grid never deadlocks.
 //
 // MFMA operand roles are swapped (the B tile feeds the instruction's first operand), so each
 // lane ends with quads of 4 consecutive output columns of one row: 8-byte bf16 or 16-byte fp32
