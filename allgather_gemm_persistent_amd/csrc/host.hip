@@ -1043,6 +1043,7 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
     g.kps = ks.kps;
     g.n_col_tiles *= ks.ksplit;
     g.epoch = world > 1 ? epoch : 0;
+    g.concurrent_producer = (mode == AGG_OVERLAP && chunks) ? 1 : 0;
     g.scale = dtype == AGG_FP8_E4M3 ? scale_a * scale_b : 1.0f;
     tiles = int64_t(g.n_row_tiles) * g.n_col_tiles;
     grid = grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks && prod == AGG_PRODUCER_SDMA);
@@ -1492,6 +1493,7 @@ extern "C" int ffn_chain(agg_ctx* ctx, int world, int rank, int64_t m_shard, int
     g.ksplit = 1;
     g.kps = 1 << 28;                       // no split: every tile covers its whole K
     g.epoch = world > 1 ? epoch : 0;
+    g.concurrent_producer = (mode == AGG_OVERLAP && chunks) ? 1 : 0;
     g.scale = 1.0f;
     g.n_lists = 1;
     g.list_cols = 1;

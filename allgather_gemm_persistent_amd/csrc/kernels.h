@@ -86,6 +86,10 @@ struct GemmArgs {
   // jobs (which still fill the gather buffer and release the flags) go to the last copy_wgs
   // workgroups, which claim tiles only after copying
   int pull;
+  // nonzero: remote chunks may land while this launch runs (an overlapped call); a tile that
+  // reads remote rows then acquires after its chunk waits. Otherwise every row a tile reads was
+  // written before the launch began, which the launch's own start makes visible.
+  int concurrent_producer;
   // flags this launch sets to the epoch at its start (workgroup 0): the local shard's chunks
   // (present from the call's start; a launch that carries the copy jobs marks them) and, for
   // ReduceScatter tile launches, the local block's send flags (nothing is sent for that block)

@@ -756,6 +756,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     int tile[4];
     int ok;
     int job;
+    int acq;
   };
   static_assert(kStageBytes <= kLdsDmaLimit, "direct-to-LDS destinations must stay below 128 KiB");
   static_assert(__builtin_offsetof(Smem, stages) == 0, "the operand stages start the LDS block");
@@ -763,6 +764,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   auto& stages = sm.stages;
   auto& s_tile = sm.tile;
   auto& s_ok = sm.ok;
+  auto& s_acq = sm.acq;
   auto& s_job = sm.job;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -858,8 +860,23 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
           for (int64_t r = lo / BM; ok && r <= (hi - 1) / BM; ++r)
             ok = wait_count(a, a.scratch + kScrSplit + (int)r, (uint32_t)a.n_col_tiles1);
         }
+        // acquire only where this launch may have written what the tile reads: rows of a remote
+        // chunk that can land during an overlapped call (not pulled: those come from the peers'
+        // blocks), and the FFN chain's h, which its first layer writes in this very launch. An
+        // acquire invalidates the XCD's L2, which costs the decode-sized launches ~10%.
+        bool acq = false;
+        if (EPI == kEpiAllGather && !pull && a.concurrent_producer) {
+          const int64_t ms = (int64_t)a.cps * a.chunk_rows;
+          acq = !(lo >= (int64_t)a.rank * ms && hi <= (int64_t)(a.rank + 1) * ms);
+        } else if (EPI == kEpiFfn && ph1) {
+          const int64_t ms = (int64_t)a.cps1 * a.chunk_rows1;
+          acq = a.concurrent_producer && !(lo >= (int64_t)a.rank * ms && hi <= (int64_t)(a.rank + 1) * ms);
+        } else if (EPI == kEpiFfn) {
+          acq = true;
+        }
         if (lane == 0) {
           s_ok = ok;
+          s_acq = acq;
           if (trec) { trec[3] = seen; trec[6] = wall_ticks(); }
         }
       }
@@ -868,7 +885,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         __syncthreads();
         return;  // abandoned (timeout): the tile's output is left as it was
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+      if (__builtin_amdgcn_readfirstlane(s_acq)) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
 
       // ---- K loop: 64-byte K slices in LDS stages or pair regions, filled by direct-to-LDS loads
       // (out-of-range rows and the K tail read zeros through the buffer descriptor's range check)
