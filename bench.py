@@ -57,7 +57,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first (the board needs some tens of ms of load to reach"
+                         " its operating clock)")
     ap.add_argument("--workload", default=None, help="workload name (default: the W=8 bf16 one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--modes", default="overlap,gemm_only,copy_only,serial,sdma",
