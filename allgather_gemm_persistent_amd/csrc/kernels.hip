@@ -673,41 +673,59 @@ __device__ void reduce_local(const GemmArgs& a, int tid, int* s_item, int* s_ok)
 // Split-K, every part of the tile running at once: part `part` of `ks` sums rows
 // [part*BM/ks, (part+1)*BM/ks) of the tile over all parts' fp32 partials, in part order (the
 // same sum, bit for bit, as one workgroup adding every part), scales (fp8), and stores bf16.
-// Coalesced: consecutive threads take consecutive 16-byte column quads of a row. The partial
-// loads are system-coherent, like the partial stores.
+// Coalesced: consecutive threads take consecutive 16-byte column quads of a row; each thread's
+// loads for E quads and G parts are in flight together (one round trip for E quads when ks <= G).
+// The partial loads are system-coherent, like the partial stores.
 template <int BM, int BN, bool FP8>
 __device__ void sum_split_rows(const GemmArgs& a, int tid, int64_t lo, int64_t hi, int64_t n0, int part) {
   constexpr int Q = BN / 4;                       // column quads per tile row
-  constexpr int G = 8;                            // partial loads in flight per quad
+  constexpr int G = 8;                            // parts whose loads are in flight together
+  constexpr int E = 2;                            // quads per thread in flight together
   const int ks = __builtin_amdgcn_readfirstlane(a.ksplit);
   const int r0 = part * BM / ks, r1 = (part + 1) * BM / ks;
+  const int n_el = (r1 - r0) * Q;
   const int64_t plane = a.M * a.N;
   const __amdgpu_buffer_rsrc_t rw =
       __builtin_amdgcn_make_buffer_rsrc(a.ws, 0, (int)(ks * plane * 4), kBufferFlags);
-  for (int e = tid; e < (r1 - r0) * Q; e += kThreads) {
-    const int64_t m = lo + r0 + e / Q;
-    const int64_t n = n0 + 4 * (e % Q);
-    if (m >= hi || n >= a.N) continue;
-    const int64_t off = (m * a.N + n) * 4;
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int q0 = 0; q0 < ks; q0 += G) {
-      f32x4 v[G];
+  for (int e0 = tid; e0 < n_el; e0 += E * kThreads) {
+    int64_t idx[E];                               // m * N + n of each quad
+    bool live[E];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const int o = q0 + g < ks ? (int)((q0 + g) * plane * 4 + off) : (int)kOutOfRange;
-        v[g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, o, 0, kStoreSystemCoherent));
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        if (q0 + g >= ks) break;
-        sum = (q0 + g == 0) ? v[g] : sum + v[g];
-      }
+    for (int u = 0; u < E; ++u) {
+      const int e = e0 + u * kThreads;
+      const int64_t m = lo + r0 + e / Q;
+      const int64_t n = n0 + 4 * (e % Q);
+      live[u] = e < n_el && m < hi && n < a.N;
+      idx[u] = m * a.N + n;
     }
-    if (FP8) sum *= a.scale;
-    u32x2 packed;
-    packed[0] = bf16x2_rne(sum[0], sum[1]);
-    packed[1] = bf16x2_rne(sum[2], sum[3]);
-    *reinterpret_cast<u32x2*>(a.c + m * a.N + n) = packed;
+    f32x4 sum[E] = {};
+    for (int q0 = 0; q0 < ks; q0 += G) {
+      f32x4 v[E][G];
+#pragma unroll
+      for (int u = 0; u < E; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const int o = (live[u] && q0 + g < ks) ? (int)(((q0 + g) * plane + idx[u]) * 4) : (int)kOutOfRange;
+          v[u][g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, o, 0, kStoreSystemCoherent));
+        }
+#pragma unroll
+      for (int u = 0; u < E; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          if (q0 + g >= ks) break;
+          sum[u] = (q0 + g == 0) ? v[u][g] : sum[u] + v[u][g];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      if (!live[u]) continue;
+      f32x4 r = sum[u];
+      if (FP8) r *= a.scale;
+      u32x2 packed;
+      packed[0] = bf16x2_rne(r[0], r[1]);
+      packed[1] = bf16x2_rne(r[2], r[3]);
+      *reinterpret_cast<u32x2*>(a.c + idx[u]) = packed;
+    }
   }
 }
 

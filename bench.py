@@ -16,8 +16,9 @@ the CPU oracle's rate on the same workload as a baseline.
 
 `configs` holds one block per workload (the two AllGather+GEMM sizes, ReduceScatter, decode, fp8,
 decode GEMM+AllReduce, the FFN chain, AllToAll+GEMM): the same four modes interleaved call by
-call, each call preceded (outside its timed span) by a 512 MiB write that evicts the caches, so
-every byte comes from HBM; R, eta and the roofline of the bare and the overlapped kernel against
+call, each call preceded (outside its timed span) by a 512 MiB write and a read of the same
+512 MiB, which evict the caches (every operand byte then comes from HBM) and leave them holding
+clean lines, so that the timed call is not charged for writing back the flush's own data; R, eta and the roofline of the bare and the overlapped kernel against
 the bound that applies (MFMA bf16 or fp8, HBM bytes, or launch latency); the overlap with the
 copy kernel as producer (R_copy_kernel), and with pull off where pulling applies.
 
@@ -51,6 +52,21 @@ BOUND = {"ag_w2_256x256x512_bf16": "latency", "ag_w8_4096x3584x8192_bf16": "mfma
 # workloads where pulling remote rows is possible: also timed with pull off (flag-gated push)
 PULL_VARIANTS = {"ag_w2_256x256x512_bf16", "ag_w8_128x3584x8192_bf16_decode"}
 FLUSH_BYTES = 512 << 20
+
+
+def cache_flush():
+    """The flush before each timed call of a block: a 512 MiB write, which evicts every operand
+    from the L2s and the 256 MB MALL, then a read of the same bytes, which evicts the write's
+    dirty lines in turn (their write-back happens here, not in the timed call) and leaves clean
+    ones. Returns flush(i)."""
+    import torch
+    buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    words = buf.view(torch.int32)
+
+    def flush(i):
+        buf.fill_(i & 0xFF)
+        words.sum(dtype=torch.int64)
+    return flush
 
 
 def parse():
@@ -342,9 +358,8 @@ def main():
 
     if args.skip_headline:
         torch.cuda.set_stream(torch.cuda.Stream())
-        flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
-        out = {n: measure_block(n, args.config_reps, lambda i: flush_buf.fill_(i & 0xFF), args.block_modes)
-               for n in args.configs.split(",")}
+        flush = cache_flush()
+        out = {n: measure_block(n, args.config_reps, flush, args.block_modes) for n in args.configs.split(",")}
         print(json.dumps(out), flush=True)
         return
     name = args.workload or configs.HEADLINE
@@ -429,20 +444,17 @@ def main():
         B.agg_ctx_set_timing(w.ctx, False)
         w.close()
 
-    # per-workload blocks, each call after a cache-evicting write
+    # per-workload blocks, each call after a cache-evicting write and read
     blocks = {}
     if args.configs != "none":
         names = list(BOUND) if args.configs == "all" else args.configs.split(",")
         names = [n for n in names if n in configs.CONFIGS]
-        flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
-
-        def flush(i):
-            flush_buf.fill_(i & 0xFF)
+        flush = cache_flush()
         for n in names:
             blocks[n] = measure_block(n, args.config_reps, flush, args.block_modes)
             print(f"block {n}: R {blocks[n]['R']} bare {blocks[n]['kernel_us']['gemm_only']} us",
                   file=sys.stderr, flush=True)
-        del flush_buf
+        del flush
 
     flops = cfg.flops
     value = flops / (t_ovl * 1e-6) / 1e12
