@@ -16,7 +16,8 @@ the CPU oracle's rate on the same workload as a baseline.
 
 `configs` holds one block per workload (the two AllGather+GEMM sizes, ReduceScatter, decode, fp8,
 decode GEMM+AllReduce, the FFN chain, AllToAll+GEMM): the same four modes interleaved call by
-call, each call preceded (outside its timed span) by a 512 MiB write and a read of the same
+call (50 calls per mode for the MFMA-bound workloads, 1000 for the latency- and HBM-bound ones;
+medians, with p10 / p90), each call preceded (outside its timed span) by a 512 MiB write and a read of the same
 512 MiB, which evict the caches (every operand byte then comes from HBM) and leave them holding
 clean lines, so that the timed call is not charged for writing back the flush's own data; R, eta and the roofline of the bare and the overlapped kernel against
 the bound that applies (MFMA bf16 or fp8, HBM bytes, or launch latency); the overlap with the
@@ -84,7 +85,9 @@ def parse():
                          " 'sdma' also times the overlap with the copy-engine producer")
     ap.add_argument("--configs", default="all",
                     help="per-workload blocks to measure: 'all', 'none', or a comma list of names")
-    ap.add_argument("--config-reps", type=int, default=20, help="interleaved calls per mode per block")
+    ap.add_argument("--config-reps", type=int, default=None,
+                    help="interleaved calls per mode per block (default: 50 for MFMA-bound workloads,"
+                         " 1000 for latency- and HBM-bound ones)")
     ap.add_argument("--block-modes", default="all",
                     help="profiling: the variants a block times ('all' or a comma list such as"
                          " 'gemm_only,overlap')")
@@ -206,6 +209,14 @@ def make_workload(name):
     return cfg, w, bare, copy, cfg.flops
 
 
+def block_reps(name, reps=None):
+    """Calls per mode in a workload's block: as given, else 50 for an MFMA-bound workload (long
+    calls, small spread) and 1000 for a latency- or HBM-bound one (calls of tens of us)."""
+    if reps is not None:
+        return reps
+    return 50 if BOUND[name] == "mfma" else 1000
+
+
 def measure_block(name, reps, flush, only="all"):
     """Interleaved, cache-flushed timing of one workload's modes; returns the JSON block."""
     import torch
@@ -254,25 +265,35 @@ def measure_block(name, reps, flush, only="all"):
         variants = [(lb, md, st, (1 if ran.get(lb) == "cu" else 0) if lb == "copy_only_copy_kernel" else n)
                     for lb, md, st, n in variants]
         torch.cuda.synchronize()
-        B.agg_ctx_set_timing(w.ctx, True)
-        ev, seq = [], []
-        for i in range(reps):
-            for label, mode, setting, launches in variants:
-                setup(setting)
-                flush(i)
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                run(mode)
-                e1.record(stream)
-                ev.append((label, e0, e1))
-                seq.extend([label] * launches)           # the timed kernel launches of the call
-        torch.cuda.synchronize()
+        # the ctx keeps the durations of its last 256 launches: time the reps in batches that fit
+        per_rep = sum(n for *_, n in variants)
+        batch = max(1, 256 // max(per_rep, 1))
+        ev, per_call = [], []                            # per call: (label, kernel ms)
+        for b0 in range(0, reps, batch):
+            B.agg_ctx_set_timing(w.ctx, True)            # clears the ring
+            seq = []
+            for i in range(b0, min(reps, b0 + batch)):
+                for label, mode, setting, launches in variants:
+                    setup(setting)
+                    flush(i)
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    run(mode)
+                    e1.record(stream)
+                    ev.append((label, e0, e1))
+                    seq.append((label, launches))        # the timed kernel launches of the call
+            torch.cuda.synchronize()
+            n_launch = sum(n for _, n in seq)
+            ks = B.agg_ctx_kernel_times(w.ctx, 256)
+            ks = ks[len(ks) - n_launch:]
+            j = 0
+            for label, n in seq:                         # a call's kernel time: its launches' sum
+                per_call.append((label, sum(ks[j:j + n])))
+                j += n
         st = w.status()
         if st[0]:
             raise RuntimeError(f"{name}: a chunk wait gave up (flag {st[1]})")
-        ks = B.agg_ctx_kernel_times(w.ctx, 256)
-        ks = ks[len(ks) - len(seq):] if len(seq) <= 256 else None
         if ffn:
             bm, bn = 256, 256
         else:
@@ -282,17 +303,19 @@ def measure_block(name, reps, flush, only="all"):
         B.agg_ctx_set_timing(w.ctx, False)
         w.close()
     labels = [v[0] for v in variants]
-    call = {lb: statistics.median([a.elapsed_time(b) * 1e3 for q, a, b in ev if q == lb]) for lb in labels}
+    call_all = {lb: [a.elapsed_time(b) * 1e3 for q, a, b in ev if q == lb] for lb in labels}
+    call = {lb: statistics.median(v) for lb, v in call_all.items()}
     if only != "all":
         return {"call_us": call, "kernel_us": None}
-    # kernel time per call: the sum of its launches (the ring keeps the last 256 launches)
-    kern = {}
-    if ks is not None:
-        per_call, i = [], 0
-        for label, _, _, launches in [v for _ in range(reps) for v in variants]:
-            per_call.append((label, sum(ks[i:i + launches])))
-            i += launches
-        kern = {lb: statistics.median([k * 1e3 for q, k in per_call if q == lb]) for lb in labels}
+    kern_all = {lb: [k * 1e3 for q, k in per_call if q == lb] for lb in labels}
+    kern = {lb: statistics.median(v) for lb, v in kern_all.items()}
+
+    def spread(v):
+        """[p10, p90] of a list of times"""
+        if len(v) < 2:
+            return [rnd(v[0], 2)] * 2 if v else None
+        q = statistics.quantiles(v, n=10, method="inclusive")
+        return [rnd(q[0], 2), rnd(q[8], 2)]
     R = call["overlap"] / call["gemm_only"]
     eta = (call["serial"] - call["overlap"]) / min(call["copy_only"], call["gemm_only"])
     bound = BOUND[name]
@@ -315,12 +338,14 @@ def measure_block(name, reps, flush, only="all"):
         "cache_flushed": True,
         "call_us": {lb: rnd(v, 2) for lb, v in call.items()},
         "kernel_us": {lb: rnd(v, 2) for lb, v in kern.items()},
+        "call_us_p10_p90": {lb: spread(v) for lb, v in call_all.items()},
+        "kernel_us_p10_p90": {lb: spread(v) for lb, v in kern_all.items()},
         "R": rnd(R, 3), "eta": rnd(eta, 3),
         "tflops_overlap": rnd(flops / (call["overlap"] * 1e-6) / 1e12, 2),
-        "roofline_bare": roof(kern["gemm_only"], bare_bytes) if kern else None,
+        "roofline_bare": roof(kern["gemm_only"], bare_bytes),
         # the overlapped launch also reads every remote chunk from its peer and writes it into
         # the symmetric buffer (CU producer)
-        "roofline_overlap": roof(kern["overlap"], bare_bytes + 2 * copy_bytes) if kern else None,
+        "roofline_overlap": roof(kern["overlap"], bare_bytes + 2 * copy_bytes),
     }
     if cfg.op == "a2a":
         block["token_rows"] = flops // (2 * cfg.k * cfg.n)
@@ -359,7 +384,8 @@ def main():
     if args.skip_headline:
         torch.cuda.set_stream(torch.cuda.Stream())
         flush = cache_flush()
-        out = {n: measure_block(n, args.config_reps, flush, args.block_modes) for n in args.configs.split(",")}
+        out = {n: measure_block(n, block_reps(n, args.config_reps), flush, args.block_modes)
+               for n in args.configs.split(",")}
         print(json.dumps(out), flush=True)
         return
     name = args.workload or configs.HEADLINE
@@ -451,7 +477,7 @@ def main():
         names = [n for n in names if n in configs.CONFIGS]
         flush = cache_flush()
         for n in names:
-            blocks[n] = measure_block(n, args.config_reps, flush, args.block_modes)
+            blocks[n] = measure_block(n, block_reps(n, args.config_reps), flush, args.block_modes)
             print(f"block {n}: R {blocks[n]['R']} bare {blocks[n]['kernel_us']['gemm_only']} us",
                   file=sys.stderr, flush=True)
         del flush
