@@ -753,15 +753,16 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   // slices of a tile row, so that each load instruction fetches whole 128-byte lines (8 lanes per
   // row) and the L1 sends half as many requests for the same bytes. kRegions pair regions of
   // 2 x DSTAGE bytes each replace the four stages; slice stage sg lies in region sg / 2, half
-  // sg % 2. The split-K tiles take four regions (a longer lead for their latency-bound loads;
-  // split parts start on whole pairs); the big fp8 tiles two. The big bf16 tiles (kMixed) load
-  // only their A rows in pairs (two regions) and keep their B rows in the four 64-byte stages,
-  // whose longer lead the B rows need (the XCD's L2 reuses them less); more regions do not fit
-  // the 128 KiB that direct-to-LDS loads were seen to fill correctly. 64 x 64 tiles, whose short
-  // K loops measured faster with the four 64-byte stages, keep those.
-  constexpr bool kMixed = !kSplitTiles && !FP8;
+  // sg % 2. The split-K tiles (128 x 64, 128 x 128) take four regions (a longer lead for their
+  // latency-bound loads; split parts start on whole pairs). The big tiles (kMixed, both dtypes)
+  // load only their A rows in pairs (two regions) and keep their B rows in the four 64-byte
+  // stages, whose longer lead the B rows need (the XCD's L2 reuses them less; for fp8 this beat
+  // two pair regions by ~5%); more regions do not fit the 128 KiB that direct-to-LDS loads were
+  // seen to fill correctly. 64 x 64 tiles, whose short K loops measured faster with the four
+  // 64-byte stages, keep those.
+  constexpr bool kMixed = !kSplitTiles;
   constexpr bool kPairs = BM * BN >= 128 * 64 && !kMixed;
-  constexpr int kRegions = kSplitTiles ? 4 : 2;
+  constexpr int kRegions = 4;
   constexpr int AREG = BM * 2 * kSliceBytes;                 // mixed: one A pair region
   constexpr int BSTAGE = BNP * kSliceBytes;                  // mixed: one B slice stage
   constexpr int kStageBytes = kMixed ? 2 * AREG + 4 * BSTAGE : kPairs ? kRegions * 2 * DSTAGE : kStages * DSTAGE;

@@ -24,7 +24,7 @@ constexpr int stage_prologue_count(int NI) { return 2 * NI + NI / 2; }
 constexpr int pair_barrier_count(int u, int R, int NL) { return (u & 1) ? (R - 2) * NL : (R - 1) * NL; }
 constexpr int pair_prologue_count(int R, int NL) { return (R - 2) * NL + NL / 2; }
 
-// Mixed (big bf16 tiles): A rows in two regions of slice pairs (NLA loads per pair), B rows in four
+// Mixed (the big tiles, bf16 and fp8): A rows in two regions of slice pairs (NLA loads per pair), B rows in four
 // 64-byte stages (NIB loads per slice, NHB of them after the barrier). Issue order per wave: the
 // prologue's A pair 0, first half of A pair 1, B slices 0..2, first NHB loads of B slice 3; then
 // slice s issues before its barrier the second half of A pair s/2+1 (even s) and the last NIB-NHB

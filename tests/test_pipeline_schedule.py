@@ -15,7 +15,8 @@ HEADER = os.path.join(ROOT, "allgather_gemm_persistent_amd", "csrc", "pipeline.h
 
 # (NI) of the four-stage tiles; (R, NL) of the pair tiles; (NLA, NIB, NHB) of the mixed tiles, as
 # the kernel instantiates them (4 waves): 64x64 -> NI 2; 128x64 / 128x128 split tiles -> R 4,
-# NL 6 / 8; fp8 256x224 / 256x256 -> R 2, NL 16; bf16 256x224 / 256x256 -> NLA 8, NIB 4, NHB 2
+# NL 6 / 8; 256x224 / 256x256, bf16 and fp8 -> NLA 8, NIB 4, NHB 2 (the other values exercise the
+# same arithmetic)
 STAGE_NI = [2, 3, 4, 8]
 PAIRS = [(2, 16), (4, 6), (4, 8), (2, 8)]
 MIXED = [(8, 4, 2)]
