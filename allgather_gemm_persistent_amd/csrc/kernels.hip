@@ -40,6 +40,7 @@
 #include "pipeline.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace agg {
 
@@ -729,6 +730,16 @@ __device__ void sum_split_rows(const GemmArgs& a, int tid, int64_t lo, int64_t h
   }
 }
 
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N-1>{}), in order
+template <typename F, int... I>
+__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int BM, int BN, int DT, int EPI>
 __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   constexpr int NW = kThreads / kWaveLanes, NT = kThreads;   // one wave per SIMD
@@ -1219,21 +1230,20 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   #pragma unroll
           for (int j = 0; j < CN; ++j) fb0[j] = ldb(0, j);
           fa = lda(0, 0);
-          // four slices per trip (slices past the part's end read zeros); a trip whose loads
-          // (up to slice t+7) stay below t_safe needs no K-end masks
-          // (pairs: 2R slices per trip, whose loads reach slice t + 4R - 1)
+          // four slices per trip (pairs: 2R), slice U of a trip in stage U (pairs: region U / 2).
+          // A trip whose loads (up to slice t+7; pairs: t + 4R - 1) stay below t_safe needs no
+          // K-end masks. The masked trips stop after the part's last slice (a uniform branch):
+          // the loads already issued for later slices read zeros and are drained below.
           constexpr int TRIP = kPairs ? 2 * kRegions : 4;
           auto trip = [&](auto masked, int t) {
-            slice(std::integral_constant<int, 0>{}, masked, fb0, fb1, t);
-            slice(std::integral_constant<int, 1>{}, masked, fb1, fb0, t + 1);
-            slice(std::integral_constant<int, 2>{}, masked, fb0, fb1, t + 2);
-            slice(std::integral_constant<int, 3>{}, masked, fb1, fb0, t + 3);
-            if constexpr (TRIP == 8) {
-              slice(std::integral_constant<int, 4>{}, masked, fb0, fb1, t + 4);
-              slice(std::integral_constant<int, 5>{}, masked, fb1, fb0, t + 5);
-              slice(std::integral_constant<int, 6>{}, masked, fb0, fb1, t + 6);
-              slice(std::integral_constant<int, 7>{}, masked, fb1, fb0, t + 7);
-            }
+            bool live = true;
+            static_for<TRIP>([&](auto u_) {
+              constexpr int U = decltype(u_)::value;
+              if (!live) return;
+              if constexpr (U % 2 == 0) slice(u_, masked, fb0, fb1, t + U);
+              else slice(u_, masked, fb1, fb0, t + U);
+              if constexpr (decltype(masked)::value) live = t + U + 1 < t_hi;
+            });
           };
           int t = t_lo;
           for (; t + (kPairs ? 4 * kRegions : 8) - 1 < t_safe; t += TRIP) trip(kPlain, t);
