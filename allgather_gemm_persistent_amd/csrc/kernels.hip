@@ -15,7 +15,8 @@
 //       its own is exhausted; lists hold row tiles in arrival order, so early chunks are
 //       computed first
 //     wave 0 polls the flags of the chunks the tile's rows need (relaxed system-scope loads,
-//       s_sleep back-off, bounded by a wall-clock limit), then an acquire fence
+//       s_sleep back-off, bounded by a wall-clock limit), then an acquire fence where the
+//       launch may have written the rows read
 //     K loop: 64-byte-wide K slices (32 bf16 or 64 fp8) of the A rows (K contiguous) and of the
 //       B rows (K x N, N contiguous) go straight from global memory to LDS (direct-to-LDS buffer
 //       loads into swizzled stages or slice-pair regions below 128 KiB, one barrier per slice);
@@ -199,9 +200,10 @@ __device__ inline uint32_t bf16x2_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// Cache-policy bits of a buffer store on gfx950: sc0 | sc1 = system coherent, i.e. the store
-// writes through to memory and is visible to every XCD once it completes, without writing back
-// this XCD's whole L2 afterwards.
+// Cache-policy bits of a buffer access on gfx950: sc0 | sc1 = system coherent. A store writes
+// through to memory and is visible to every XCD once it completes, without writing back this
+// XCD's whole L2 afterwards; a load bypasses the caches and returns what memory holds, so data
+// read once after a flag needs no acquire fence (an L2 invalidate) before it.
 constexpr int kStoreSystemCoherent = 1 | 16;
 
 // Copy `bytes` (a multiple of 16, < 2 GiB) from src to dst with the whole workgroup: 16-byte
@@ -598,9 +600,10 @@ __device__ bool wait_count(const GemmArgs& a, const uint32_t* ctr, uint32_t expe
 // instead of the few workgroups holding local tiles. A group waits (wave 0, bounded) until the
 // local tiles of its row tile have all stored their partials and until every peer's chunk of
 // its rows has arrived; an abandoned group leaves its rows at the local partial. The sums are
-// elementwise over 16-byte vectors, consecutive threads on consecutive addresses; `out` is read
-// system-coherent (written through by other workgroups of this launch), the received blocks after
-// an acquire fence, as the tiles read the gather buffer.
+// elementwise over 16-byte vectors, consecutive threads on consecutive addresses; `out` (written
+// through by other workgroups of this launch) and the received blocks (written by the producer)
+// are read with system-coherent loads, which bypass the caches: no acquire fence, whose L2
+// invalidate costs more than these once-read lines.
 template <int BM>
 __device__ void reduce_local(const GemmArgs& a, int tid, int* s_item, int* s_ok) {
   constexpr int kRedRows = 4;              // divides every tile height: a group is in one row tile
@@ -639,7 +642,6 @@ __device__ void reduce_local(const GemmArgs& a, int tid, int* s_item, int* s_ok)
       __syncthreads();
       continue;
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
     const int64_t v0 = r0 * N / 4, nv = (r1 - r0) * N / 4;   // the group's 16-byte vectors
     for (int64_t e0 = tid; e0 < nv; e0 += (int64_t)kThreads * U) {
       f32x4 v[U], in[U][AGG_MAX_WORLD - 1];
@@ -653,7 +655,7 @@ __device__ void reduce_local(const GemmArgs& a, int tid, int* s_item, int* s_ok)
         for (int q = 0; q < AGG_MAX_WORLD - 1; ++q) {
           const int p = q < rank ? q : q + 1;     // peers in ascending rank order
           const int off = (live && p < world) ? (int)((int64_t)p * blk * 4 + (v0 + e) * 16) : (int)kOutOfRange;
-          in[u][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrecv, off, 0, 0));
+          in[u][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrecv, off, 0, kStoreSystemCoherent));
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1545,7 +1547,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         }
         __syncthreads();
         if (__builtin_amdgcn_readfirstlane(s_ok)) {
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+          // the peers' partials: system-coherent loads (read once; no L2 invalidate)
           const int world = __builtin_amdgcn_readfirstlane(a.world), rank = __builtin_amdgcn_readfirstlane(a.rank);
   #pragma unroll
           for (int i = 0; i < FM; ++i) {
@@ -1560,7 +1562,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
               for (int q = 0; q < AGG_MAX_WORLD - 1; ++q) {
                 const int p = q < rank ? q : q + 1;
                 const int off = p < world ? (int)(((int64_t)p * MN + m * a.N + n) * 4) : (int)kOutOfRange;
-                in[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrecv, off, 0, 0));
+                in[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrecv, off, 0, kStoreSystemCoherent));
               }
               f32x4 v = acc[i][j];
   #pragma unroll
