@@ -15,11 +15,11 @@ HEADER = os.path.join(ROOT, "allgather_gemm_persistent_amd", "csrc", "pipeline.h
 
 # (NI) of the four-stage tiles; (R, NL) of the pair tiles; (NLA, NIB, NHB) of the mixed tiles, as
 # the kernel instantiates them (4 waves): 64x64 -> NI 2; 128x64 / 128x128 split tiles -> R 4,
-# NL 6 / 8; 256x224 / 256x256, bf16 and fp8 -> NLA 8, NIB 4, NHB 2 (the other values exercise the
-# same arithmetic)
-STAGE_NI = [2, 3, 4, 8]
-PAIRS = [(2, 16), (4, 6), (4, 8), (2, 8)]
-MIXED = [(8, 4, 2)]
+# NL 6 / 8, NLP 0; 256x224 / 256x256, bf16 and fp8 -> NLA 8, NIB 4, NHB 0, NLAP 4 (the other values
+# exercise the same arithmetic)
+STAGE = [(2, 1), (2, 0), (3, 1), (4, 2), (4, 0), (8, 4)]                     # (NI, NH)
+PAIRS = [(2, 16, 8), (4, 6, 3), (4, 6, 0), (4, 8, 4), (4, 8, 0), (2, 8, 4)]   # (R, NL, NLP)
+MIXED = [(8, 4, 0, 4), (8, 4, 0, 0), (8, 4, 1, 4), (8, 4, 2, 4), (8, 4, 0, 2)]   # (NLA, NIB, NHB, NLAP)
 
 
 @pytest.fixture(scope="module")
@@ -31,15 +31,16 @@ def counts(tmp_path_factory):
     d = tmp_path_factory.mktemp("pipeline")
     src = d / "counts.cpp"
     lines = ['#include <cstdio>', f'#include "{HEADER}"', "int main() {", "  using namespace agg;"]
-    for ni in STAGE_NI:
-        lines.append(f'  std::printf("stage {ni} %d %d\\n", stage_barrier_count({ni}), stage_prologue_count({ni}));')
-    for r, nl in PAIRS:
-        lines.append(f'  std::printf("pair {r} {nl} %d %d %d\\n", pair_barrier_count(0, {r}, {nl}), '
-                     f'pair_barrier_count(1, {r}, {nl}), pair_prologue_count({r}, {nl}));')
-    for nla, nib, nhb in MIXED:
-        lines.append(f'  std::printf("mixed {nla} {nib} {nhb} %d %d %d %d %d\\n", '
-                     + ", ".join(f"mixed_barrier_count({u}, {nla}, {nib}, {nhb})" for u in range(4))
-                     + f", mixed_prologue_count({nla}, {nib}, {nhb}));")
+    for ni, nh in STAGE:
+        lines.append(f'  std::printf("stage {ni} {nh} %d %d\\n", stage_barrier_count({ni}), '
+                     f'stage_prologue_count({ni}, {nh}));')
+    for r, nl, nlp in PAIRS:
+        lines.append(f'  std::printf("pair {r} {nl} {nlp} %d %d %d\\n", pair_barrier_count(0, {r}, {nl}), '
+                     f'pair_barrier_count(1, {r}, {nl}), pair_prologue_count({r}, {nl}, {nlp}));')
+    for nla, nib, nhb, nlap in MIXED:
+        lines.append(f'  std::printf("mixed {nla} {nib} {nhb} {nlap} %d %d %d %d %d\\n", '
+                     + ", ".join(f"mixed_barrier_count({u}, {nla}, {nib}, {nhb}, {nlap})" for u in range(4))
+                     + f", mixed_prologue_count({nla}, {nib}, {nhb}, {nlap}));")
     lines += ["  return 0;", "}"]
     src.write_text("\n".join(lines) + "\n")
     exe = d / "counts"
@@ -49,11 +50,11 @@ def counts(tmp_path_factory):
     for line in out.splitlines():
         f = line.split()
         if f[0] == "stage":
-            table[("stage", int(f[1]))] = (int(f[2]), int(f[3]))
+            table[("stage", int(f[1]), int(f[2]))] = (int(f[3]), int(f[4]))
         elif f[0] == "pair":
-            table[("pair", int(f[1]), int(f[2]))] = tuple(int(x) for x in f[3:])
+            table[("pair", int(f[1]), int(f[2]), int(f[3]))] = tuple(int(x) for x in f[4:])
         else:
-            table[("mixed", int(f[1]), int(f[2]), int(f[3]))] = tuple(int(x) for x in f[4:])
+            table[("mixed", int(f[1]), int(f[2]), int(f[3]), int(f[4]))] = tuple(int(x) for x in f[5:])
     return table
 
 
@@ -77,8 +78,7 @@ class Replay:
         return len(idx) == n and max(idx) < self.done
 
 
-def replay_stages(ni, bar, pro, slices=64):
-    nh = ni // 2
+def replay_stages(ni, nh, bar, pro, slices=64):
     r = Replay()
     for q in range(3):
         r.issue(("B", q), ni)
@@ -99,31 +99,31 @@ def replay_stages(ni, bar, pro, slices=64):
     return r.errors
 
 
-def replay_pairs(R, nl, bar_even, bar_odd, pro, slices=96):
+def replay_pairs(R, nl, nlp, bar_even, bar_odd, pro, slices=96):
     r = Replay()
     for q in range(R - 1):
         r.issue(("P", q), nl)
-    r.issue(("P", R - 1), nl // 2)
+    r.issue(("P", R - 1), nlp)
     r.barrier(pro)
     if not r.landed(("P", 0), nl):
         r.errors.append("prologue")
     for t in range(slices):
         if t % 2 == 0:
             # into the region pair t/2-1 left: its last read was before the barrier of slice t-1
-            r.issue(("P", t // 2 + R - 1), nl - nl // 2)
+            r.issue(("P", t // 2 + R - 1), nl - nlp)
         r.barrier(bar_odd if t % 2 else bar_even)
         if not r.landed(("P", (t + 1) // 2), nl):
             r.errors.append(("pair", (t + 1) // 2, t))
         if t % 2 == 1:
             # into slice t's own region: every wave has read pair (t-1)/2 before this barrier
-            r.issue(("P", (t + 1) // 2 + R - 1), nl // 2)
+            r.issue(("P", (t + 1) // 2 + R - 1), nlp)
     return r.errors
 
 
-def replay_mixed(nla, nib, nhb, bars, pro, slices=96):
+def replay_mixed(nla, nib, nhb, nlap, bars, pro, slices=96):
     r = Replay()
     r.issue(("A", 0), nla)
-    r.issue(("A", 1), nla // 2)
+    r.issue(("A", 1), nlap)
     for q in range(3):
         r.issue(("B", q), nib)
     r.issue(("B", 3), nhb)
@@ -132,7 +132,7 @@ def replay_mixed(nla, nib, nhb, bars, pro, slices=96):
         r.errors.append("prologue")
     for t in range(slices):
         if t % 2 == 0:
-            r.issue(("A", t // 2 + 1), nla - nla // 2)
+            r.issue(("A", t // 2 + 1), nla - nlap)
         r.issue(("B", t + 3), nib - nhb)
         r.barrier(bars[t % 4])
         if not r.landed(("A", (t + 1) // 2), nla):
@@ -140,38 +140,38 @@ def replay_mixed(nla, nib, nhb, bars, pro, slices=96):
         if not r.landed(("B", t + 1), nib):
             r.errors.append(("B", t + 1, t))
         if t % 2 == 1:
-            r.issue(("A", (t + 1) // 2 + 1), nla // 2)
+            r.issue(("A", (t + 1) // 2 + 1), nlap)
         r.issue(("B", t + 4), nhb)
     return r.errors
 
 
-@pytest.mark.parametrize("ni", STAGE_NI)
-def test_stage_counts(counts, ni):
-    bar, pro = counts[("stage", ni)]
-    assert replay_stages(ni, bar, pro) == []
+@pytest.mark.parametrize("ni,nh", STAGE)
+def test_stage_counts(counts, ni, nh):
+    bar, pro = counts[("stage", ni, nh)]
+    assert replay_stages(ni, nh, bar, pro) == []
     # one more load in flight would be a race
-    assert replay_stages(ni, bar + 1, pro) != [] or replay_stages(ni, bar, pro + 1) != []
+    assert replay_stages(ni, nh, bar + 1, pro) != [] or replay_stages(ni, nh, bar, pro + 1) != []
 
 
-@pytest.mark.parametrize("R,nl", PAIRS)
-def test_pair_counts(counts, R, nl):
-    even, odd, pro = counts[("pair", R, nl)]
-    assert replay_pairs(R, nl, even, odd, pro) == []
+@pytest.mark.parametrize("R,nl,nlp", PAIRS)
+def test_pair_counts(counts, R, nl, nlp):
+    even, odd, pro = counts[("pair", R, nl, nlp)]
+    assert replay_pairs(R, nl, nlp, even, odd, pro) == []
     # the odd barriers and the prologue's wait for the last loads they may: one more in flight
     # would be a race (an even barrier needs the pair its odd predecessor already waited for)
-    assert replay_pairs(R, nl, even, odd + 1, pro) != []
-    assert replay_pairs(R, nl, even, odd, pro + 1) != []
+    assert replay_pairs(R, nl, nlp, even, odd + 1, pro) != []
+    assert replay_pairs(R, nl, nlp, even, odd, pro + 1) != []
 
 
-@pytest.mark.parametrize("nla,nib,nhb", MIXED)
-def test_mixed_counts(counts, nla, nib, nhb):
-    *bars, pro = counts[("mixed", nla, nib, nhb)]
-    assert replay_mixed(nla, nib, nhb, bars, pro) == []
+@pytest.mark.parametrize("nla,nib,nhb,nlap", MIXED)
+def test_mixed_counts(counts, nla, nib, nhb, nlap):
+    *bars, pro = counts[("mixed", nla, nib, nhb, nlap)]
+    assert replay_mixed(nla, nib, nhb, nlap, bars, pro) == []
     for u in range(4):
         worse = list(bars)
         worse[u] += 1
-        assert replay_mixed(nla, nib, nhb, worse, pro) != [], u
-    assert replay_mixed(nla, nib, nhb, bars, pro + 1) != []
+        assert replay_mixed(nla, nib, nhb, nlap, worse, pro) != [], u
+    assert replay_mixed(nla, nib, nhb, nlap, bars, pro + 1) != []
 
 
 def test_refills_follow_last_reads():
