@@ -1125,7 +1125,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         constexpr int RM = decltype(rm_)::value, CN = decltype(cn_)::value;
         constexpr bool kLone = decltype(lone_)::value;
         using F = decltype(fa);
-        constexpr int RB = RM / 2;                 // block rows before the barrier
+        // block rows before the barrier: one more than half (when that leaves one after it), which
+        // measured 1-3% faster than half
+        constexpr int RB = (RM / 2 + 1 < RM) ? RM / 2 + 1 : RM / 2;
         constexpr int S1 = RB * CN, S2 = (RM - RB) * CN;
         static_assert(RM - RB - 1 <= RB, "the A fragments after the barrier are loaded before it");
         auto slice = [&](auto u_, auto masked, F (&fbc)[CN], F (&fbn)[CN], int t) {
