@@ -930,8 +930,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       // mixed: NLA A loads per wave per pair (8 rows x 128 bytes), then NIB B loads per wave per
       // slice (16 rows x 64 bytes). NHB of a B slice's loads may go after the barrier of the slice
       // four before it, the rest before the barrier of the slice three before it: all of them
-      // before (NHB = 0) measured 9% (bf16) and 12% (fp8) faster than half and half, with the same
-      // bits out.
+      // before (NHB = 0) measured 3% (bf16) and 6% (fp8) faster than half and half on the
+      // workloads' data (9% and 12% with zero-valued remote rows, which draw less power), with the
+      // same bits out.
       constexpr int NLA = BM / (8 * NW), NIB = BNP / (16 * NW), NHB = 0;
       // mixed: NLAP of an A pair's loads go after the barrier of an odd slice, the rest before the
       // barrier of the next even slice
