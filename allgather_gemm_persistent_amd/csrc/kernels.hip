@@ -762,19 +762,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   // 64-byte K slices filled by direct-to-LDS loads, in four stages or in regions of slice pairs
   constexpr int BNP = (BN + 63) / 64 * 64;                   // B rows held in LDS
   constexpr int DSTAGE = (BM + BNP) * kSliceBytes;
-  // Tiles of 128 x 64 and larger load K slices in pairs: an LDS row holds two consecutive 64-byte
+  // Tiles of 64 x 64 and larger load K slices in pairs: an LDS row holds two consecutive 64-byte
   // slices of a tile row, so that each load instruction fetches whole 128-byte lines (8 lanes per
   // row) and the L1 sends half as many requests for the same bytes. kRegions pair regions of
   // 2 x DSTAGE bytes each replace the four stages; slice stage sg lies in region sg / 2, half
-  // sg % 2. The split-K tiles (128 x 64, 128 x 128) take four regions (a longer lead for their
-  // latency-bound loads; split parts start on whole pairs). The big tiles (kMixed, both dtypes)
+  // sg % 2. The tiles up to 128 x 128 take four regions (a longer lead for their latency-bound
+  // loads; split parts start on whole pairs). The big tiles (kMixed, both dtypes)
   // load only their A rows in pairs (two regions) and keep their B rows in the four 64-byte
   // stages, whose longer lead the B rows need (the XCD's L2 reuses them less; for fp8 this beat
   // two pair regions by ~5%); more regions do not fit the 128 KiB that direct-to-LDS loads were
-  // seen to fill correctly. 64 x 64 tiles, whose short K loops measured faster with the four
-  // 64-byte stages, keep those.
+  // seen to fill correctly. 64 x 64 tiles take pairs too (the decode AllReduce: 51.3 -> 45.8 us
+  // against four 64-byte stages); a tile smaller than that would keep the four stages.
   constexpr bool kMixed = !kSplitTiles;
-  constexpr bool kPairs = BM * BN >= 128 * 64 && !kMixed;
+  constexpr bool kPairs = BM * BN >= 64 * 64 && !kMixed;
   constexpr int kRegions = 4;
   constexpr int AREG = BM * 2 * kSliceBytes;                 // mixed: one A pair region
   constexpr int BSTAGE = BNP * kSliceBytes;                  // mixed: one B slice stage
