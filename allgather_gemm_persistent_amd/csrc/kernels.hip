@@ -943,7 +943,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
       // rest before the barrier of the slice three before it; pairs: NLP of a pair's loads go after
       // the barrier of an odd slice, the rest before the barrier of the next even slice
       constexpr int NH = NI / 2;
-      constexpr int NLP = 0;
+      constexpr int NLP = NL / 2;
       constexpr int EL = FP8 ? 1 : 2;
       constexpr int kRowsB = kSliceBytes / EL;              // K rows of B per slice
       constexpr int kChunksB = BNP * EL / 16;               // 16-byte chunks per B row

@@ -14,11 +14,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "allgather_gemm_persistent_amd", "csrc", "pipeline.h")
 
 # (NI) of the four-stage tiles; (R, NL) of the pair tiles; (NLA, NIB, NHB) of the mixed tiles, as
-# the kernel instantiates them (4 waves): 64x64 / 128x64 / 128x128 -> R 4, NL 4 / 6 / 8, NLP 0;
+# the kernel instantiates them (4 waves): 64x64 / 128x64 / 128x128 -> R 4, NL 4 / 6 / 8, NLP NL/2;
 # 256x224 / 256x256, bf16 and fp8 -> NLA 8, NIB 4, NHB 0, NLAP 4 (a tile below 64x64 would take the
 # four stages; the other values exercise the same arithmetic)
 STAGE = [(2, 1), (2, 0), (3, 1), (4, 2), (4, 0), (8, 4)]                     # (NI, NH)
-PAIRS = [(2, 16, 8), (4, 4, 0), (4, 6, 3), (4, 6, 0), (4, 8, 4), (4, 8, 0), (2, 8, 4)]   # (R, NL, NLP)
+PAIRS = [(2, 16, 8), (4, 4, 2), (4, 4, 0), (4, 6, 3), (4, 6, 0), (4, 8, 4), (4, 8, 0), (2, 8, 4)]   # (R, NL, NLP)
 MIXED = [(8, 4, 0, 4), (8, 4, 0, 0), (8, 4, 1, 4), (8, 4, 2, 4), (8, 4, 0, 2)]   # (NLA, NIB, NHB, NLAP)
 
 
