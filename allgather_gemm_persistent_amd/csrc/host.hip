@@ -313,18 +313,18 @@ int schedule(agg_ctx* ctx, int mode, hipStream_t s, hipStream_t us,
   return AGG_OK;
 }
 
-// Enqueue the consumer kernel (on `ls`, ctx->ks unless given), bracketed by a timing event
-// pair on the same stream when timing is on.
+// Enqueue the consumer kernel: launch(t0, t1) with the ring's next timing event pair when timing
+// is on (the launch itself records the kernel's start and end in them: no marker packets on the
+// stream), or with null events.
 template <typename F>
-int timed_launch(agg_ctx* ctx, F launch, hipStream_t ls = nullptr) {
-  if (!ls) ls = ctx->ks;
-  const int slot = int(ctx->launches % kTimingRing);
-  if (ctx->timing) HIP_TRY(hipEventRecord(ctx->ev_t0[slot], ls));
-  HIP_TRY(launch());
-  if (ctx->timing) {
-    HIP_TRY(hipEventRecord(ctx->ev_t1[slot], ls));
-    ++ctx->launches;
+int timed_launch(agg_ctx* ctx, F launch) {
+  if (!ctx->timing) {
+    HIP_TRY(launch(nullptr, nullptr));
+    return AGG_OK;
   }
+  const int slot = int(ctx->launches % kTimingRing);
+  HIP_TRY(launch(ctx->ev_t0[slot], ctx->ev_t1[slot]));
+  ++ctx->launches;
   return AGG_OK;
 }
 
@@ -537,9 +537,9 @@ int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int
     h.copy_jobs = 0;
     std::memset(h.cs, 0, sizeof h.cs);
   }
-  auto go = [&]() { return launch_gemm(h, ts.bm, ts.bn, dtype, epi, gr, ls); };
-  if (timed) return timed_launch(ctx, go, ls);
-  HIP_TRY(go());
+  auto go = [&](hipEvent_t t0, hipEvent_t t1) { return launch_gemm(h, ts.bm, ts.bn, dtype, epi, gr, ls, t0, t1); };
+  if (timed) return timed_launch(ctx, go);
+  HIP_TRY(go(nullptr, nullptr));
   return AGG_OK;
 }
 
@@ -1090,9 +1090,9 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
   // (no fork and join of the kernel's queue)
   hipStream_t ls = prod == AGG_PRODUCER_KERNEL && own_queue_free(s) ? s : ctx->ks;
   auto launch = [&]() -> int {
-    return timed_launch(ctx, [&]() {
-      return launch_gemm(g, ts.bm, ts.bn, dtype, kEpiAllGather, grid, ls);
-    }, ls);
+    return timed_launch(ctx, [&](hipEvent_t t0, hipEvent_t t1) {
+      return launch_gemm(g, ts.bm, ts.bn, dtype, kEpiAllGather, grid, ls, t0, t1);
+    });
   };
   const CopyPlan kplan{cc, flags, ord.size()};
   Marks kmarks;
@@ -1246,9 +1246,9 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
   }
   hipStream_t ls = prod == AGG_PRODUCER_KERNEL && own_queue_free(s) ? s : ctx->ks;
   auto launch = [&]() -> int {
-    return timed_launch(ctx, [&]() {
-      return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiReduceScatter, grid, ls);
-    }, ls);
+    return timed_launch(ctx, [&](hipEvent_t t0, hipEvent_t t1) {
+      return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiReduceScatter, grid, ls, t0, t1);
+    });
   };
   const CopyPlan kplan{cc, flags, ord.size()};
   Marks kmarks;
@@ -1364,7 +1364,9 @@ extern "C" int gemm_ar(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
   }
   hipStream_t ls = prod == AGG_PRODUCER_KERNEL && own_queue_free(s) ? s : ctx->ks;
   auto launch = [&]() -> int {
-    return timed_launch(ctx, [&]() { return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiAllReduce, grid, ls); }, ls);
+    return timed_launch(ctx, [&](hipEvent_t t0, hipEvent_t t1) {
+      return launch_gemm(g, ts.bm, ts.bn, AGG_BF16, kEpiAllReduce, grid, ls, t0, t1);
+    });
   };
   const CopyPlan kplan{cc, flags, ord.size()};
   Marks kmarks;
@@ -1545,7 +1547,9 @@ extern "C" int ffn_chain(agg_ctx* ctx, int world, int rank, int64_t m_shard, int
   hipStream_t ls = prod == AGG_PRODUCER_KERNEL && own_queue_free(s) ? s : ctx->ks;
   auto launch = [&]() -> int {
     return tile_launches([&](const GemmArgs& gg, bool) {
-      return timed_launch(ctx, [&]() { return launch_gemm(gg, ts.bm, ts.bn, AGG_BF16, kEpiFfn, grid, ls); }, ls);
+      return timed_launch(ctx, [&](hipEvent_t t0, hipEvent_t t1) {
+        return launch_gemm(gg, ts.bm, ts.bn, AGG_BF16, kEpiFfn, grid, ls, t0, t1);
+      });
     });
   };
   Marks kmarks;

@@ -110,10 +110,10 @@ struct GemmArgs {
 };
 
 // Launch the persistent kernel instantiated for (bm, bn, dtype, epilogue) with `grid`
-// workgroups of 256 threads on `stream`. Returns hipErrorInvalidValue for a shape that has no
-// instantiation.
+// workgroups of 256 threads on `stream`; non-null events t0 / t1 receive the launch's start and
+// end. Returns hipErrorInvalidValue for a shape that has no instantiation.
 hipError_t launch_gemm(const GemmArgs& args, int bm, int bn, int dtype, int epilogue, int grid,
-                       hipStream_t stream);
+                       hipStream_t stream, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 // Workgroups of the (bm, bn, dtype, epilogue) kernel that fit on one CU at once (0 for a shape
 // without an instantiation).

@@ -40,6 +40,8 @@
 #include "kernels.h"
 #include "pipeline.h"
 
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 #include <utility>
 
@@ -1789,9 +1791,14 @@ __global__ void fill_u32_kernel(uint32_t* dst, size_t words, uint32_t value) {
     dst[i] = value;
 }
 
+// With timing events, the launch carries them (the dispatch's own start and end timestamps), so
+// timing adds no packets to the stream between launches.
 template <int BM, int BN, int DT, int EPI>
-static hipError_t launch_one(const GemmArgs& args, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, DT, EPI>), dim3(grid), dim3(kThreads), 0, stream, args);
+static hipError_t launch_one(const GemmArgs& args, int grid, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  if (t0 || t1)
+    hipExtLaunchKernelGGL((gemm_kernel<BM, BN, DT, EPI>), dim3(grid), dim3(kThreads), 0, stream, t0, t1, 0, args);
+  else
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, DT, EPI>), dim3(grid), dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 
@@ -1868,26 +1875,28 @@ int max_blocks_per_cu(int bm, int bn, int dtype, int epilogue) {
 }
 
 template <int DT, int EPI>
-static hipError_t launch_shape(const GemmArgs& args, int bm, int bn, int grid, hipStream_t s) {
-  if (bm == 256 && bn == 256) return launch_one<256, 256, DT, EPI>(args, grid, s);
-  if (bm == 256 && bn == 224) return launch_one<256, 224, DT, EPI>(args, grid, s);
-  if (bm == 128 && bn == 128) return launch_one<128, 128, DT, EPI>(args, grid, s);
-  if (bm == 128 && bn == 64) return launch_one<128, 64, DT, EPI>(args, grid, s);
-  if (bm == 64 && bn == 64) return launch_one<64, 64, DT, EPI>(args, grid, s);
+static hipError_t launch_shape(const GemmArgs& args, int bm, int bn, int grid, hipStream_t s, hipEvent_t t0,
+                               hipEvent_t t1) {
+  if (bm == 256 && bn == 256) return launch_one<256, 256, DT, EPI>(args, grid, s, t0, t1);
+  if (bm == 256 && bn == 224) return launch_one<256, 224, DT, EPI>(args, grid, s, t0, t1);
+  if (bm == 128 && bn == 128) return launch_one<128, 128, DT, EPI>(args, grid, s, t0, t1);
+  if (bm == 128 && bn == 64) return launch_one<128, 64, DT, EPI>(args, grid, s, t0, t1);
+  if (bm == 64 && bn == 64) return launch_one<64, 64, DT, EPI>(args, grid, s, t0, t1);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(const GemmArgs& args, int bm, int bn, int dtype, int epilogue, int grid,
-                       hipStream_t stream) {
+                       hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   if (epilogue == kEpiAllGather) {
-    if (dtype == AGG_BF16) return launch_shape<AGG_BF16, kEpiAllGather>(args, bm, bn, grid, stream);
-    if (dtype == AGG_FP8_E4M3) return launch_shape<AGG_FP8_E4M3, kEpiAllGather>(args, bm, bn, grid, stream);
+    if (dtype == AGG_BF16) return launch_shape<AGG_BF16, kEpiAllGather>(args, bm, bn, grid, stream, t0, t1);
+    if (dtype == AGG_FP8_E4M3)
+      return launch_shape<AGG_FP8_E4M3, kEpiAllGather>(args, bm, bn, grid, stream, t0, t1);
   } else if (epilogue == kEpiReduceScatter && dtype == AGG_BF16) {
-    return launch_shape<AGG_BF16, kEpiReduceScatter>(args, bm, bn, grid, stream);
+    return launch_shape<AGG_BF16, kEpiReduceScatter>(args, bm, bn, grid, stream, t0, t1);
   } else if (epilogue == kEpiAllReduce && dtype == AGG_BF16) {
-    return launch_shape<AGG_BF16, kEpiAllReduce>(args, bm, bn, grid, stream);
+    return launch_shape<AGG_BF16, kEpiAllReduce>(args, bm, bn, grid, stream, t0, t1);
   } else if (epilogue == kEpiFfn && dtype == AGG_BF16 && bm == 256 && bn == 256) {
-    return launch_one<256, 256, AGG_BF16, kEpiFfn>(args, grid, stream);
+    return launch_one<256, 256, AGG_BF16, kEpiFfn>(args, grid, stream, t0, t1);
   }
   return hipErrorInvalidValue;
 }
