@@ -241,8 +241,9 @@ def agg_ctx_set_tile(ctx, bm: int = 0, bn: int = 0) -> None:
     _call("agg_ctx_set_tile", ctx, bm, bn)
 
 
-def agg_ctx_set_timing(ctx, on: bool = True) -> None:
-    _call("agg_ctx_set_timing", ctx, 1 if on else 0)
+def agg_ctx_set_timing(ctx, on=True) -> None:
+    """on: False/0 off, True/1 every launch timed, n > 1 every n-th launch timed."""
+    _call("agg_ctx_set_timing", ctx, int(on))
 
 
 def agg_ctx_kernel_times(ctx, max_n: int = 256) -> list:

@@ -113,8 +113,10 @@ struct agg_ctx {
   hipEvent_t ev_copy[kMaxCopyStreams] = {};
   uint32_t* trace = nullptr;
   size_t trace_bytes = 0;
-  bool timing = false;                      // record a timing event pair around each launch
+  int timing_every = 0;                     // record a timing event pair around every n-th
+                                            // launch (0: none)
   hipEvent_t ev_t0[kTimingRing] = {}, ev_t1[kTimingRing] = {};
+  uint64_t calls = 0;                       // launches since timing was switched on
   uint64_t launches = 0;                    // launches recorded since timing was switched on
   uint32_t* bound[kFlagSlots] = {};
   size_t bound_words[kFlagSlots] = {};
@@ -314,11 +316,11 @@ int schedule(agg_ctx* ctx, int mode, hipStream_t s, hipStream_t us,
 }
 
 // Enqueue the consumer kernel: launch(t0, t1) with the ring's next timing event pair when timing
-// is on (the launch itself records the kernel's start and end in them: no marker packets on the
-// stream), or with null events.
+// is on and this launch is one of the sampled ones (the launch itself records the kernel's start
+// and end in them: no marker packets on the stream), or with null events.
 template <typename F>
 int timed_launch(agg_ctx* ctx, F launch) {
-  if (!ctx->timing) {
+  if (!ctx->timing_every || ctx->calls++ % uint64_t(ctx->timing_every) != 0) {
     HIP_TRY(launch(nullptr, nullptr));
     return AGG_OK;
   }
@@ -869,17 +871,19 @@ extern "C" int agg_ctx_set_copy_streams(agg_ctx* ctx, int n) {
   return AGG_OK;
 }
 
-extern "C" int agg_ctx_set_timing(agg_ctx* ctx, int on) {
+extern "C" int agg_ctx_set_timing(agg_ctx* ctx, int every) {
   clear_error();
   if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
-  if (on && !ctx->ev_t0[0]) {
+  if (every < 0) return fail(AGG_E_ARG, "timing interval %d is negative", every);
+  if (every && !ctx->ev_t0[0]) {
     HIP_TRY(hipSetDevice(ctx->device));
     for (int j = 0; j < kTimingRing; ++j) {
       HIP_TRY(hipEventCreate(&ctx->ev_t0[j]));
       HIP_TRY(hipEventCreate(&ctx->ev_t1[j]));
     }
   }
-  ctx->timing = on != 0;
+  ctx->timing_every = every;
+  ctx->calls = 0;
   ctx->launches = 0;
   return AGG_OK;
 }
@@ -887,7 +891,7 @@ extern "C" int agg_ctx_set_timing(agg_ctx* ctx, int on) {
 extern "C" int agg_ctx_kernel_times(agg_ctx* ctx, float* ms, int max, int* n) {
   clear_error();
   if (!ctx || !n || (max > 0 && !ms)) return fail(AGG_E_ARG, "NULL argument");
-  if (!ctx->timing) return fail(AGG_E_STATE, "timing is off (agg_ctx_set_timing)");
+  if (!ctx->timing_every) return fail(AGG_E_STATE, "timing is off (agg_ctx_set_timing)");
   HIP_TRY(hipSetDevice(ctx->device));
   const uint64_t have = std::min<uint64_t>(ctx->launches, kTimingRing);
   const int count = int(std::min<uint64_t>(have, uint64_t(std::max(max, 0))));

@@ -11,8 +11,10 @@ Printed (one JSON line): overlapped TFLOP/s (value), % of the bf16 MFMA peak, th
 figures R = T_ovl / T_gemm and eta = (T_serial - T_ovl) / min(T_copy, T_gemm) from the same
 kernels in the other modes (per-call stream times with the modes interleaved call by call; the
 t_*_us fields are the modes timed one after another, which the board's clock drift skews), the
-dominant kernel's roofline (its own duration from timing events on the stream it runs on), and
-the CPU oracle's rate on the same workload as a baseline.
+dominant kernel's roofline (its own duration from timing events that every n-th timed launch
+carries on the stream it runs on, n = min(8, K // 8) or 1: the events cost each launch that
+carries them some microseconds, so the timed steps sample), and the CPU oracle's rate on the same
+workload as a baseline.
 
 `configs` holds one block per workload (the two AllGather+GEMM sizes, ReduceScatter, decode, fp8,
 decode GEMM+AllReduce, the FFN chain, AllToAll+GEMM): the same four modes interleaved call by
@@ -73,7 +75,7 @@ def cache_flush():
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed steps first (the board needs some tens of ms of load to reach"
                          " its operating clock)")
@@ -81,7 +83,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--modes", default="overlap,gemm_only,copy_only,serial,sdma",
                     help="modes to time; the overlapped steps always run (profiling runs use"
-                         " 'overlap' alone so that every consumer-kernel launch is a timed step);"
+                         " 'overlap' alone so that every consumer-kernel launch is an overlapped step);"
                          " 'sdma' also times the overlap with the copy-engine producer")
     ap.add_argument("--configs", default="all",
                     help="per-workload blocks to measure: 'all', 'none', or a comma list of names")
@@ -420,7 +422,10 @@ def main():
         for _ in range(args.warmup):
             w.run("overlap", order=order)
         torch.cuda.synchronize()
-        B.agg_ctx_set_timing(w.ctx, True)          # clears the ring: only timed launches count
+        # clears the ring: only timed launches count; launches 0, every, 2 * every, ... carry
+        # the timing events
+        every = max(1, min(8, args.steps // 8))
+        B.agg_ctx_set_timing(w.ctx, every)
         t0 = time.perf_counter()
         for _ in range(args.steps):
             w.run("overlap", order=order)
@@ -430,6 +435,7 @@ def main():
         if st[0]:
             raise RuntimeError(f"overlap: a chunk wait gave up (flag {st[1]})")
         kms = B.agg_ctx_kernel_times(w.ctx, args.steps)
+        assert len(kms) == (args.steps + every - 1) // every, (len(kms), args.steps, every)
         k_ovl_us = statistics.mean(kms) * 1e3
         # context: the same steps without the per-launch timing events (the timed steps above
         # carry them, which costs each step some microseconds)
@@ -548,6 +554,8 @@ def main():
                      "traffic_unit": "bytes per launch",
                      "kernel": "agg::gemm_kernel (overlap launch)",
                      "kernel_us": round(k_ovl_us, 1),
+                     "kernel_us_timed_launches": f"every {every}th of the {args.steps} timed steps"
+                     if every > 1 else f"all {args.steps} timed steps",
                      "warm_caches": True,
                      "gemm_only_frac": rnd(flops / (k_gemm_us * 1e-6) / 1e12 / peak, 4)
                      if k_gemm_us else None},

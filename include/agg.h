@@ -241,14 +241,18 @@ int agg_ctx_set_split(agg_ctx* ctx, int ksplit);
  */
 int agg_ctx_set_lists(agg_ctx* ctx, int lists, int list_cols);
 
-/* Kernel timing: with timing on, each call brackets its consumer kernel with a pair of timing
- * events on the kernel's own stream (a ring of the last 256 launches; switching it on clears
- * the ring). agg_ctx_kernel_times waits for and returns the durations in milliseconds of the
- * last min(max, recorded) launches, oldest first, in ms[0..*n).
+/* Kernel timing: with every = n >= 1, the 1st, (n+1)-th, (2n+1)-th, ... consumer-kernel launch
+ * after this call carries a start and an end timing event on the kernel's own stream (n = 1:
+ * every launch); the recorded durations go to a ring of the last 256 (switching timing on, or
+ * changing n, clears it); every = 0 switches timing off. The events cost a launch some
+ * microseconds of its own and of the gap to the next one, so a long run samples. A negative n
+ * is AGG_E_ARG. agg_ctx_kernel_times waits for and returns the durations in milliseconds of
+ * the last min(max, recorded) timed launches, oldest first, in ms[0..*n); with timing off it
+ * is AGG_E_STATE.
  * Passage: section "What would prove the compiler layer is portable" (measurements disclosed with
  *  the numerical checks).
  */
-int agg_ctx_set_timing(agg_ctx* ctx, int on);
+int agg_ctx_set_timing(agg_ctx* ctx, int every);
 int agg_ctx_kernel_times(agg_ctx* ctx, float* ms, int max, int* n);
 
 /* Optional per-tile trace (NULL or 0 bytes disables). The buffer is device memory of

@@ -641,9 +641,9 @@ def test_stale_data_reuse_full_size(gpu, producer):
 
 @pytest.mark.parametrize("mode", ["overlap", "gemm_only"])
 def test_kernel_times_ring(gpu, mode):
-    """With timing on, every consumer-kernel launch leaves one duration in the ctx's ring (the
-    launch carries its own start and end events), oldest first, and the results are those of the
-    untimed calls; with timing off, reading the ring is a state error."""
+    """With timing on, every consumer-kernel launch (or every n-th) leaves one duration in the
+    ctx's ring (the launch carries its own start and end events), oldest first, and the results
+    are those of the untimed calls; with timing off, reading the ring is a state error."""
     world, rank, ms, cr, k, n = 4, 1, 64, 32, 256, 128
     shards, b, sa, sb = small_ag_data(world, ms, k, n, "bf16", seed=501)
     w = AgWorkload(world, rank, shards, b, cr)
@@ -652,6 +652,14 @@ def test_kernel_times_ring(gpu, mode):
         ref = w.c.clone()
         B.agg_ctx_set_timing(w.ctx, True)
         for _ in range(3):
+            w.run(mode)
+        torch.cuda.synchronize()
+        times = B.agg_ctx_kernel_times(w.ctx, 8)
+        assert len(times) == 3 and all(0.0 < t < 1000.0 for t in times), times
+        assert bits_equal(w.c, ref)
+        # every third launch: launches 1, 4 and 7 of seven
+        B.agg_ctx_set_timing(w.ctx, 3)
+        for _ in range(7):
             w.run(mode)
         torch.cuda.synchronize()
         times = B.agg_ctx_kernel_times(w.ctx, 8)
