@@ -437,8 +437,8 @@ def main():
         kms = B.agg_ctx_kernel_times(w.ctx, args.steps)
         assert len(kms) == (args.steps + every - 1) // every, (len(kms), args.steps, every)
         k_ovl_us = statistics.mean(kms) * 1e3
-        # context: the same steps without the per-launch timing events (the timed steps above
-        # carry them, which costs each step some microseconds)
+        # context: the same steps with no timing events at all (the sampled launches above
+        # carry them, which costs each of those launches some microseconds)
         B.agg_ctx_set_timing(w.ctx, False)
         t_ovl_untimed = time_mode(w, "overlap", order, args.steps, 0)
         # the same kernels in the other modes
