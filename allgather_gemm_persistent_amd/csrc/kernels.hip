@@ -73,8 +73,9 @@ __device__ inline uint32_t load_flag(const uint32_t* p) {
 }
 
 // ---- operand pipeline: 64-byte K slices (32 bf16 or 64 fp8 elements) in LDS, filled by
-// direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): four 64-byte stages, or (tiles of
-// 128 x 64 and up) regions of slice pairs with 128-byte rows. One wave instruction writes 1 KiB of
+// direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): four 64-byte stages (tiles below
+// 64 x 64), regions of slice pairs with 128-byte rows (64 x 64 up to 128 x 128), or, for the
+// 256-row tiles, A in slice-pair regions and B in four 64-byte stages. One wave instruction writes 1 KiB of
 // LDS: 16 tile rows of 64 bytes, lane i landing at byte 16*i. Lane i therefore fetches row i/4
 // of its 16-row group and the 16-byte chunk that the swizzle below puts at position i%4.
 constexpr int kSliceBytes = 64;
