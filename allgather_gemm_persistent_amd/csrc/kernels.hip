@@ -1540,9 +1540,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (tid == 0) {
+        // one lane per chunk of the tile's rows, so the counts are one round trip (the chunks'
+        // counters are shared by every column tile, and one after another they cost the tile
+        // several microseconds)
+        if (wave == 0) {
           const int q_lo = (int)(lo / a.chunk_rows), q_hi = (int)((hi - 1) / a.chunk_rows);
-          for (int q = q_lo; q <= q_hi; ++q) {
+          for (int q = q_lo + lane; q <= q_hi; q += kWaveLanes) {
             const int64_t clo = (int64_t)q * a.chunk_rows;
             const int64_t chi = clo + a.chunk_rows;
             const int t_first = (int)(clo / BM), t_last = (int)((chi - 1) / BM);
@@ -1640,10 +1643,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
           // its flag (a system-coherent store)
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           __syncthreads();
-          if (tid == 0) {
+          if (wave == 0) {
+            // one lane per send chunk of the tile's rows: the counts in one round trip
             const int64_t rlo = lo - base, rhi = hi - base;
             const int q_lo = (int)(rlo / a.chunk_rows), q_hi = (int)((rhi - 1) / a.chunk_rows);
-            for (int q = q_lo; q <= q_hi; ++q) {
+            for (int q = q_lo + lane; q <= q_hi; q += kWaveLanes) {
               // tiles overlapping chunk q of this block, times the column tiles
               const int64_t clo = (int64_t)q * a.chunk_rows;
               const int64_t chi = clo + a.chunk_rows;
