@@ -1436,8 +1436,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
           uint32_t* split_ctr = a.scratch + kScrSplit + tile_id;
           if (a.split_together) {
             // every part has its own workgroup in this launch: once all parts have stored, each
-            // sums a row range of the tile; the counter counts every part in twice (stored, then
-            // summed) and the last arrival resets it
+            // sums a row range of the tile. The counter is cleared by the launch's last
+            // workgroup (not by the last part to finish its sum, which would cost every part
+            // another atomic round trip before it is done)
             const uint32_t ks = (uint32_t)a.ksplit;
             if (tid == 0) __hip_atomic_fetch_add(split_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (wave == 0) {
@@ -1446,9 +1447,6 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
             }
             __syncthreads();
             if (__builtin_amdgcn_readfirstlane(s_ok)) sum_split_rows<BM, BN, FP8>(a, tid, lo, hi, n0, part);
-            __syncthreads();
-            if (tid == 0 && __hip_atomic_fetch_add(split_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 2 * ks - 1)
-              __hip_atomic_store(split_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             finish = false;
           } else {
             if (tid == 0)
@@ -1679,7 +1677,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   // ---- the last workgroup resets the counters for the next launch. No fence: every counter
   // reset here was last touched by the other workgroups through atomics whose returned values
   // they used, i.e. that had completed, before they counted themselves done (the local row-tile
-  // counts were read to their final values by the reduction's waits).
+  // counts were read to their final values by the reduction's waits, the split-K counts by every
+  // part's wait).
   if (tid == 0) {
     const uint32_t prev = atomicAdd(a.scratch + kScrDone, 1u);
     s_ok = (prev == gridDim.x - 1);
@@ -1706,6 +1705,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
     }
     if (EPI == kEpiFfn) {
       for (int i = tid; i < a.n_row_tiles1; i += NT)
+        __hip_atomic_store(a.scratch + kScrSplit + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (EPI == kEpiAllGather && kSplitTiles && a.ksplit > 1) {
+      // split-K tile counters (a launch whose parts all ran together leaves them at ksplit)
+      for (int i = tid; i < a.n_row_tiles * (a.n_col_tiles / a.ksplit); i += NT)
         __hip_atomic_store(a.scratch + kScrSplit + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (EPI == kEpiReduceScatter || EPI == kEpiFfn) {
