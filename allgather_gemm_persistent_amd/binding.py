@@ -46,6 +46,7 @@ _SIGNATURES = {
     "agg_ctx_set_tile": [_vp, _c_int, _c_int],
     "agg_ctx_set_lists": [_vp, _c_int, _c_int],
     "agg_ctx_set_split": [_vp, _c_int],
+    "agg_ctx_set_tail": [_vp, _c_int],
     "agg_ctx_set_pull": [_vp, _c_int],
     "agg_ctx_set_producer": [_vp, _c_int, _c_int, _c_int],
     "agg_ctx_last_producer": [_vp, _i32p],
@@ -72,6 +73,8 @@ _SIGNATURES = {
     "agg_kernel_regs": [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)],
     "agg_tile_shape": [_c_int, _c_int, _c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_int),
                        ctypes.POINTER(_c_int)],
+    "agg_tail_split": [_c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int, _c_int, ctypes.POINTER(_c_int),
+                       ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)],
     "agg_ag_row_tile_order": [_c_int, _c_int, _c_i64, _c_int, _i32p, _c_int, _c_int, _i32p,
                               _c_int, ctypes.POINTER(_c_int)],
     "agg_rs_row_tile_order": [_c_int, _c_int, _c_i64, _c_int, _i32p, _c_int, _c_int, _i32p,
@@ -295,6 +298,14 @@ def agg_ctx_set_split(ctx, ksplit: int = 0) -> None:
     _call("agg_ctx_set_split", ctx, ksplit)
 
 
+_TAIL_MODES = {"auto": 0, "off": 1, "on": 2}
+
+
+def agg_ctx_set_tail(ctx, mode: str = "auto") -> None:
+    """Tail split of later ag_gemm / a2a_gemm calls: "auto", "off" or "on"."""
+    _call("agg_ctx_set_tail", ctx, _TAIL_MODES[mode] if isinstance(mode, str) else int(mode))
+
+
 def agg_ctx_set_lists(ctx, lists: int = 8, list_cols: int = 0) -> None:
     _call("agg_ctx_set_lists", ctx, lists, list_cols)
 
@@ -434,6 +445,15 @@ def agg_tile_shape(op: int, dtype, m: int, n: int, k: int):
     bm, bn = _c_int(), _c_int()
     _call("agg_tile_shape", op, _dtype(dtype), m, n, k, ctypes.byref(bm), ctypes.byref(bn))
     return bm.value, bn.value
+
+
+def agg_tail_split(bm: int, bn: int, m: int, n: int, n_row_tiles: int, units: int = 256, mode="auto"):
+    """(head row tiles, tail tile shape) of the tail split; head 0 = no split."""
+    head, tbm, tbn = _c_int(), _c_int(), _c_int()
+    _call("agg_tail_split", bm, bn, m, n, n_row_tiles, units,
+          _TAIL_MODES[mode] if isinstance(mode, str) else int(mode),
+          ctypes.byref(head), ctypes.byref(tbm), ctypes.byref(tbn))
+    return head.value, (tbm.value, tbn.value)
 
 
 def _tile_order(name, world, rank, size, chunk_rows, order, bm):

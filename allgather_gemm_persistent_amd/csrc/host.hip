@@ -122,6 +122,7 @@ struct agg_ctx {
   size_t bound_words[kFlagSlots] = {};
   int force_split = 0;                       // 0: split-K chosen per call
   bool chain_fused = true;                   // ffn_chain: both layers in one launch
+  int tail = AGG_TAIL_AUTO;                  // ag_gemm / a2a_gemm: tail split of the last wave
   float* ws = nullptr;                       // split-K partials (grown on demand)
   size_t ws_bytes = 0;
   int producer = AGG_PRODUCER_CU;
@@ -498,9 +499,18 @@ struct Marks {
 
 // One launch of the persistent kernel under the CU producer: `copies` adds the copy jobs,
 // `tiles_on` keeps the GEMM tiles (without them: a copy-only grid of one workgroup per CU).
+// A tail launch (ag_gemm's tail split): the second launch of a call's tiles, with its own
+// arguments, shape and grid; it carries no copies and marks no flags.
+struct TailLaunch {
+  const GemmArgs* g = nullptr;
+  TileShape ts{0, 0};
+  int grid = 0;
+};
+
 int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int dtype, int epi,
               int grid, const CopyPlan* sets, int nsets, bool delays, int world, uint32_t epoch,
-              bool copies, bool tiles_on, bool timed, const Marks& marks, int pull_copiers = 0) {
+              bool copies, bool tiles_on, bool timed, const Marks& marks, int pull_copiers = 0,
+              const TailLaunch& tail = TailLaunch{}) {
   GemmArgs h = g;
   h.mark_count[0] = h.mark_count[1] = h.mark_count[2] = 0;
   if (copies) {
@@ -539,7 +549,15 @@ int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int
     h.copy_jobs = 0;
     std::memset(h.cs, 0, sizeof h.cs);
   }
-  auto go = [&](hipEvent_t t0, hipEvent_t t1) { return launch_gemm(h, ts.bm, ts.bn, dtype, epi, gr, ls, t0, t1); };
+  // with a tail launch (tiles only), the timing events span both: the start of the first and
+  // the end of the second
+  const bool two = tiles_on && tail.g;
+  auto go = [&](hipEvent_t t0, hipEvent_t t1) -> hipError_t {
+    if (!two) return launch_gemm(h, ts.bm, ts.bn, dtype, epi, gr, ls, t0, t1);
+    const hipError_t e = launch_gemm(h, ts.bm, ts.bn, dtype, epi, gr, ls, t0, nullptr);
+    if (e != hipSuccess) return e;
+    return launch_gemm(*tail.g, tail.ts.bm, tail.ts.bn, dtype, epi, tail.grid, ls, nullptr, t1);
+  };
   if (timed) return timed_launch(ctx, go);
   HIP_TRY(go(nullptr, nullptr));
   return AGG_OK;
@@ -844,6 +862,15 @@ extern "C" int agg_ctx_set_split(agg_ctx* ctx, int ksplit) {
   return AGG_OK;
 }
 
+extern "C" int agg_ctx_set_tail(agg_ctx* ctx, int mode) {
+  clear_error();
+  if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
+  if (mode != AGG_TAIL_AUTO && mode != AGG_TAIL_OFF && mode != AGG_TAIL_ON)
+    return fail(AGG_E_ARG, "unknown tail mode %d", mode);
+  ctx->tail = mode;
+  return AGG_OK;
+}
+
 extern "C" int agg_ctx_set_lists(agg_ctx* ctx, int lists, int list_cols) {
   clear_error();
   if (!ctx) return fail(AGG_E_ARG, "ctx is NULL");
@@ -1011,7 +1038,6 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
   int64_t tiles = 0;
   int grid = 1;
   if (kernel) {
-    if (int rc = upload_rows(ctx, sp, s, rows)) return rc;
     g.a = static_cast<const uint8_t*>(gather);
     g.b = static_cast<const uint8_t*>(b);
     g.c = static_cast<uint16_t*>(c);
@@ -1062,6 +1088,8 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
     attach_trace(ctx, g, tiles);
   }
   if (noalloc) ctx->used_static = true;
+  if (!cu && kernel)
+    if (int rc = upload_rows(ctx, sp, s, rows)) return rc;
   if (cu) {
     if (chunks)
       if (int rc = upload_schedule(ctx, sp, s, ord, delay_us)) return rc;
@@ -1076,6 +1104,47 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
       if (spare >= 1 && (ctx->pull == AGG_PULL_ON || remote <= kPullMaxBytes))
         pull_copiers = int(std::min<int64_t>(spare, std::max<int64_t>(1, (remote + 16383) / 16384)));
     }
+    // tail split: the row tiles of the whole waves in this launch, the rest cut into the next
+    // smaller shape in a second launch right after it (after the copy jobs, which the first
+    // launch carries, have all completed). Both launches' row tiles share one order table.
+    std::vector<int32_t> table = rows;
+    GemmArgs g2;
+    TailLaunch tl;
+    if (kernel && pull_copiers == 0 && g.ksplit == 1 && !ctx->trace && ctx->tail != AGG_TAIL_OFF) {
+      const TailSplit plan2 = tail_split(ts, m, n, int(rows.size()), ctx->cus, ctx->tail);
+      if (plan2.head_rows > 0) {
+        const TileShape ts2 = plan2.tail;
+        const int sub = ts.bm / ts2.bm;
+        const int64_t row_tiles2 = (m + ts2.bm - 1) / ts2.bm;
+        std::vector<int32_t> rows2;
+        for (size_t i = size_t(plan2.head_rows); i < rows.size(); ++i)
+          for (int j = 0; j < sub; ++j) {
+            const int64_t r2 = int64_t(rows[i]) * sub + j;
+            if (r2 < row_tiles2) rows2.push_back(int32_t(r2));
+          }
+        if (!rows2.empty() && size_t(plan2.head_rows) + rows2.size() <= size_t(AGG_MAX_ROW_TILES)) {
+          g2 = g;
+          g2.n_row_tiles = int(rows2.size());
+          g2.row_base = plan2.head_rows;
+          g2.n_col_tiles = int((n + ts2.bn - 1) / ts2.bn);
+          g2.concurrent_producer = 0;
+          g2.trace = nullptr;
+          g2.trace_tiles = 0;
+          const int grid2 = grid_for(ctx, int64_t(g2.n_row_tiles) * g2.n_col_tiles, false);
+          fill_common(ctx, g2, ts2, grid2);
+          g.n_row_tiles = plan2.head_rows;
+          grid = grid_for(ctx, int64_t(g.n_row_tiles) * g.n_col_tiles, false);
+          fill_common(ctx, g, ts, grid);
+          table.resize(size_t(plan2.head_rows));
+          table.insert(table.end(), rows2.begin(), rows2.end());
+          tl.g = &g2;
+          tl.ts = ts2;
+          tl.grid = grid2;
+        }
+      }
+    }
+    if (kernel)
+      if (int rc = upload_rows(ctx, sp, s, table)) return rc;
     Marks marks;
     if (world > 1) {
       marks.copy_flags[0] = flags + size_t(rank) * cps;
@@ -1086,7 +1155,7 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
                        [&](bool copies, bool tiles_on, bool timed) {
                          return launch_cu(ctx, s, g, ts, dtype, kEpiAllGather, grid, &plan, 1,
                                           delay_us != nullptr, world, epoch, copies, tiles_on,
-                                          timed, marks, pull_copiers);
+                                          timed, marks, pull_copiers, tl);
                        });
   }
   // the copy engines' producer keeps the kernel on a queue of its own (see the top of this

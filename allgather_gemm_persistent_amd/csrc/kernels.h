@@ -62,7 +62,10 @@ struct GemmArgs {
   int64_t m_block;          // RS: rows per block (Mb)
   int world, rank;
   int chunk_rows, cps;      // rows per chunk, chunks per shard (AG) / per block (RS)
-  int n_row_tiles;          // AG: ceil(M/BM); RS: world * tiles_per_block
+  int n_row_tiles;          // row tiles this launch computes (AG: up to ceil(M/BM); RS: world *
+                            //   tiles_per_block), listed from scratch[kScrRowOrder + row_base]
+  int row_base;             // AG: where this launch's row-tile order starts (a tail launch's
+                            //   rows follow the head launch's in the same table)
   int n_col_tiles;          // ceil(N/BN) * ksplit: claimable columns (each tile's K parts)
   int ksplit;               // K parts per tile (1: no split); part p covers K slices
   int kps;                  //   [p*kps, min((p+1)*kps, slices)) of the main loop's slices
@@ -76,7 +79,7 @@ struct GemmArgs {
   float scale;              // fp8: scale_a * scale_b; bf16: 1
   uint64_t timeout_ticks;   // in wall-clock (s_memrealtime) ticks
   uint32_t trace_tiles;     // capacity of `trace` in tiles (0 = off)
-  // (the row tiles in compute order are in scratch, kScrRowOrder)
+  // (the row tiles in compute order are in scratch, kScrRowOrder + row_base)
   // in-kernel producer: the jobs of set 0, then those of set 1 (the FFN chain's receive chunks)
   CopySet cs[2];
   uint32_t copy_jobs;                   // 0: no copies in this launch; else cs[0].jobs + cs[1].jobs

@@ -390,7 +390,7 @@ __device__ inline uint32_t static_taken(const GemmArgs& a, int x, int nstat, uin
 
 __device__ inline void list_tile(const GemmArgs& a, int x, const ListGeom& g, uint32_t k, Tile& t) {
   const int Lr = a.n_lists / a.list_cols;
-  t.row_tile = (int)a.scratch[kScrRowOrder + g.xr + (int)(k / (uint32_t)g.nx) * Lr];
+  t.row_tile = (int)a.scratch[kScrRowOrder + a.row_base + g.xr + (int)(k / (uint32_t)g.nx) * Lr];
   t.col_tile = g.c_lo + (int)(k % (uint32_t)g.nx);
   t.list = x;
   t.pos = (int)k;

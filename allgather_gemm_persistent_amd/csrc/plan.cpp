@@ -79,17 +79,53 @@ KSplit choose_ksplit(int op, int dtype, int64_t tiles, int64_t k, int units) {
   return r;
 }
 
+// Relative MFMA efficiency of each shape (operand bytes per flop fall as the tile grows; the
+// 128 x 128 weight from bare launches of the 5120-row AllToAll workload, where its 4.4 waves
+// ran 14% slower than two waves of 256 x 256 tiles).
+static double tile_eff(const TileShape& s) {
+  if (s.bm == 256 && s.bn == 256) return 1.0;
+  if (s.bm == 256) return 0.98;
+  if (s.bm == 128 && s.bn == 128) return 0.6;
+  if (s.bm == 128) return 0.5;
+  return 0.35;
+}
+
+static_assert(kTailAuto == AGG_TAIL_AUTO && kTailOff == AGG_TAIL_OFF && kTailOn == AGG_TAIL_ON, "tail modes");
+
+TailSplit tail_split(TileShape ts, int64_t m, int64_t n, int n_rows, int units, int mode) {
+  TailSplit r{0, {0, 0}};
+  if (mode == kTailOff || n_rows < 2 || n <= 0 || m <= 0 || units < 1) return r;
+  // the next smaller shape whose rows divide the big tile's
+  TileShape t2{0, 0};
+  if (ts.bm == 256) t2 = {128, 128};
+  else if (ts.bm == 128 && ts.bn == 128) t2 = {128, 64};
+  else if (ts.bm == 128 && ts.bn == 64) t2 = {64, 64};
+  if (t2.bm == 0) return r;
+  const int64_t nct = (n + ts.bn - 1) / ts.bn;
+  const int64_t tiles = int64_t(n_rows) * nct;
+  // the head: whole row tiles that fill whole waves
+  int64_t head = (tiles / units) * units / nct;
+  if (mode == kTailOn) head = std::min<int64_t>(std::max<int64_t>(head, 1), n_rows - 1);
+  if (head < 1 || head >= n_rows) return r;
+  // the tail's rows at the smaller shape (every sub-tile of a tail row tile, clipped at m)
+  const int64_t sub = ts.bm / t2.bm;
+  const int64_t tail_rows = std::min<int64_t>((n_rows - head) * sub, (m + t2.bm - 1) / t2.bm);
+  const int64_t tiles2 = tail_rows * ((n + t2.bn - 1) / t2.bn);
+  if (mode == kTailAuto) {
+    // in waves of big tiles: the split pays when its second launch (plus ~5% for the launch
+    // itself) takes less than the big tiles' last wave
+    const double ratio = (double(t2.bm) * t2.bn / tile_eff(t2)) / (double(ts.bm) * ts.bn / tile_eff(ts));
+    const double unsplit = double((tiles + units - 1) / units);
+    const double split = double((head * nct + units - 1) / units) + double((tiles2 + units - 1) / units) * ratio + 0.05;
+    if (split >= unsplit) return r;
+  }
+  r.head_rows = int(head);
+  r.tail = t2;
+  return r;
+}
+
 TileShape choose_tile(int op, int dtype, int64_t m, int64_t n, int64_t k) {
-  // Relative MFMA efficiency of each shape (operand bytes per flop fall as the tile grows; the
-  // 128 x 128 weight from bare launches of the 5120-row AllToAll workload, where its 4.4 waves
-  // ran 14% slower than two waves of 256 x 256 tiles).
-  auto eff = [](const TileShape& s) {
-    if (s.bm == 256 && s.bn == 256) return 1.0;
-    if (s.bm == 256) return 0.98;
-    if (s.bm == 128 && s.bn == 128) return 0.6;
-    if (s.bm == 128) return 0.5;
-    return 0.35;
-  };
+  auto eff = tile_eff;
   const int64_t kUnits = 256;  // compute units of one MI355X, one workgroup each
   TileShape best = tile_shapes().back();
   double best_cost = 1e300;
@@ -226,6 +262,18 @@ extern "C" int agg_tile_shape(int op, int dtype, int64_t m, int64_t n, int64_t k
   TileShape s = choose_tile(op, dtype, m, n, k);
   *bm = s.bm;
   *bn = s.bn;
+  return AGG_OK;
+}
+
+extern "C" int agg_tail_split(int bm, int bn, int64_t m, int64_t n, int n_row_tiles, int units, int mode,
+                              int* head_rows, int* tail_bm, int* tail_bn) {
+  clear_error();
+  if (!head_rows || !tail_bm || !tail_bn) return fail(AGG_E_ARG, "agg_tail_split: NULL output");
+  if (mode != kTailAuto && mode != kTailOff && mode != kTailOn) return fail(AGG_E_ARG, "unknown tail mode %d", mode);
+  const TailSplit t = tail_split(TileShape{bm, bn}, m, n, n_row_tiles, units, mode);
+  *head_rows = t.head_rows;
+  *tail_bm = t.tail.bm;
+  *tail_bn = t.tail.bn;
   return AGG_OK;
 }
 

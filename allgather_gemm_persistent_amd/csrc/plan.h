@@ -41,6 +41,19 @@ constexpr int kMaxSplitTiles = 1024;   // tiles of a split-K call (one arrival c
 // flight) touches the fewest distinct A and B rows per K step, so the XCD's L2 holds them.
 int choose_list_cols(int lists, int n_row_tiles, int n_col_tiles, int bm, int bn, int workers);
 
+// Tail split of an AllGather+GEMM call whose tiles spill into a last, partly filled wave: the
+// first `head_rows` row tiles of the compute order (whole waves of `ts` tiles) run in one launch,
+// the remaining row tiles, cut into the smaller shape `tail`, in a second launch right after
+// it. head_rows == 0: no split. mode: kTailAuto (split when a tile-time model says the second
+// launch beats the last wave), kTailOff, kTailOn (split whenever a smaller shape exists and
+// there are two row tiles or more).
+constexpr int kTailAuto = 0, kTailOff = 1, kTailOn = 2;
+struct TailSplit {
+  int head_rows;
+  TileShape tail;
+};
+TailSplit tail_split(TileShape ts, int64_t m, int64_t n, int n_rows, int units, int mode);
+
 // Every candidate tile shape the kernels are instantiated for.
 const std::vector<TileShape>& tile_shapes();
 

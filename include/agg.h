@@ -241,6 +241,27 @@ int agg_ctx_set_split(agg_ctx* ctx, int ksplit);
  */
 int agg_ctx_set_lists(agg_ctx* ctx, int lists, int list_cols);
 
+/* Tail split of ag_gemm / a2a_gemm calls under the in-kernel producer (AGG_PRODUCER_CU, no
+ * pull, no split-K, no per-tile trace attached). A call whose output tiles fill some waves of
+ * the grid and spill a partly filled last wave runs its compute in two launches on the same
+ * stream: the first (with the copy jobs) takes the row tiles of the whole waves, in compute
+ * order; the second, right after it, takes the remaining row tiles, each cut into tiles of the
+ * next smaller shape (256-row tiles into 128 x 128, 128 x 128 into 128 x 64, 128 x 64 into
+ * 64 x 64), so the last wave's work is spread over more compute units. The same rows are
+ * computed with the same per-element K order, so C is bit-identical either way. With kernel
+ * timing on, one duration spans both launches.
+ *   AGG_TAIL_AUTO (default): split when a tile-time model says the second launch takes less
+ *                 than the last wave of big tiles; AGG_TAIL_OFF: never; AGG_TAIL_ON: whenever a
+ *                 smaller shape exists and the call has two row tiles or more (at least one
+ *                 row tile in each launch).
+ * AGG_E_ARG for an unknown mode.
+ * Passage: section "DITRON adds three levels of tiling" (core-level tiles; tiles paired with
+ *  the chunks) and section "The performance case has a narrow, useful boundary" (wave
+ *  quantisation of small and ragged shapes).
+ */
+enum { AGG_TAIL_AUTO = 0, AGG_TAIL_OFF = 1, AGG_TAIL_ON = 2 };
+int agg_ctx_set_tail(agg_ctx* ctx, int mode);
+
 /* Kernel timing: with every = n >= 1, the 1st, (n+1)-th, (2n+1)-th, ... consumer-kernel launch
  * after this call carries a start and an end timing event on the kernel's own stream (n = 1:
  * every launch); the recorded durations go to a ring of the last 256 (switching timing on, or
@@ -497,6 +518,15 @@ int agg_ctx_set_chain_fused(agg_ctx* ctx, int on);
  * Passage: section "DITRON adds three levels of tiling" (core-level tiles).
  */
 int agg_tile_shape(int op, int dtype, int64_t m, int64_t n, int64_t k, int* bm, int* bn);
+
+/* The tail split (agg_ctx_set_tail) of a call computing n_row_tiles row tiles of bm x bn over an
+ * m x n output on `units` compute units: *head_rows row tiles in the first launch (0: no split)
+ * and the second launch's tile shape *tail_bm x *tail_bn. AGG_E_ARG for an unknown mode or
+ * NULL outputs.
+ * Passage: section "DITRON adds three levels of tiling" (core-level tiles).
+ */
+int agg_tail_split(int bm, int bn, int64_t m, int64_t n, int n_row_tiles, int units, int mode,
+                   int* head_rows, int* tail_bm, int* tail_bn);
 
 /* Row-tile order of ag_gemm: tiles of `bm` rows of C sorted by the arrival position of the
  * latest remote chunk they overlap (-1 when none), ties by tile index. Writes

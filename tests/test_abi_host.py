@@ -133,6 +133,43 @@ def test_tile_shapes_for_the_workloads(lib):
     assert got["a2a_w8_5120x3584x8192_bf16"] == (256, 224)    # 20 x 16 = 320 tiles of capacity
 
 
+def test_tail_split_decisions(lib):
+    """The tail split: the AllToAll workload's 320 tiles (one whole wave of 16 row tiles plus 4
+    row tiles of a second) split into 16 row tiles and 8 tail row tiles of 128 x 128; whole waves
+    (c2: 256 tiles, c5: 1024) and the smallest shape never split; forced on, any call with two
+    row tiles does; off never; an unknown mode is an argument error."""
+    assert B.agg_tail_split(256, 224, 5120, 3584, 20) == (16, (128, 128))
+    assert B.agg_tail_split(256, 224, 4096, 3584, 16) == (0, (0, 0))
+    assert B.agg_tail_split(256, 224, 8192, 7168, 32) == (0, (0, 0))
+    assert B.agg_tail_split(256, 256, 8192, 8192, 32) == (0, (0, 0))
+    assert B.agg_tail_split(256, 224, 5120, 3584, 20, mode="off") == (0, (0, 0))
+    assert B.agg_tail_split(64, 64, 5120, 3584, 80, mode="on") == (0, (0, 0))
+    assert B.agg_tail_split(256, 224, 512, 448, 2, mode="on") == (1, (128, 128))
+    assert B.agg_tail_split(128, 128, 512, 448, 4, mode="on") == (1, (128, 64))
+    assert B.agg_tail_split(128, 64, 512, 448, 4, mode="on") == (1, (64, 64))
+    assert B.agg_tail_split(256, 224, 512, 448, 1, mode="on") == (0, (0, 0))
+    # a last wave that is nearly full does not pay for a second launch
+    assert B.agg_tail_split(256, 224, 256 * 31, 3584, 31) == (0, (0, 0))
+    # the head always ends on whole waves of the big tile
+    for rows in range(17, 32):
+        head, t2 = B.agg_tail_split(256, 224, 256 * rows, 3584, rows)
+        assert head in (0, 16), (rows, head)
+    with pytest.raises(B.AggError):
+        B.agg_tail_split(256, 224, 5120, 3584, 20, mode=3)
+
+
+def test_tail_split_cases_of_the_gpu_tests_split(lib):
+    """The AllToAll cases the GPU tail test runs split at every tile shape it uses (so the
+    test runs a second launch)."""
+    from test_gpu_a2a import CASES
+    for tile in [(256, 224), (128, 128), (128, 64)]:
+        heads = []
+        for world, rank, cap, k, n, cr, counts in CASES:
+            rows = B.agg_a2a_row_tile_order(world, rank, cap, cr, counts, None, tile[0])
+            heads.append(B.agg_tail_split(tile[0], tile[1], world * cap, n, len(rows), 256, "on")[0])
+        assert any(h > 0 for h in heads), (tile, heads)
+
+
 def _a2a(**kw):
     args = dict(world=3, rank=1, cap=64, n=256, k=512, chunk_rows=16, dtype="bf16", scale_a=1.0,
                 scale_b=1.0, counts=[10, 64, 0], peer_src=[FAKE, FAKE, FAKE], recv=FAKE, flags=FAKE,

@@ -219,3 +219,30 @@ def test_small_config_dispatch(gpu):
         _check(w, d["blocks"], d["b"], "bf16", 1.0, 1.0, "small")
     finally:
         w.close()
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("tile", [(256, 224), (128, 128), (128, 64)])
+@pytest.mark.parametrize("mode", ["overlap", "serial"])
+def test_tail_split_keeps_rows_and_bits(gpu, case, tile, mode):
+    """The tail split forced on: C bit-identical to the single launch, within the bar against
+    the oracle, C rows of (big) tiles that hold no token untouched, receive rows past the counts
+    untouched, every flag at the epoch."""
+    world, rank, cap, k, n, cr, counts = CASES[case]
+    blocks, b, sa, sb = _blocks(world, cap, k, n, "bf16", seed=200 + case)
+    order = inputs.seeded_order(world, rank, cap // cr, 11 + case)
+    outs = []
+    for tail in ("off", "on"):
+        w = A2aWorkload(world, rank, blocks, counts, b, cr, tile=tile)
+        try:
+            B.agg_ctx_set_tail(w.ctx, tail)
+            _fill_sentinel(w)
+            w.run(mode, order=order)
+            assert w.status() == (0, -1)
+            _check(w, blocks, b, "bf16", sa, sb, (case, tile, mode, tail))
+            _untouched_tiles(w, tile[0])
+            outs.append(w.c.clone())
+        finally:
+            w.close()
+    assert bits_equal(outs[0], outs[1]), (case, tile, mode)
+

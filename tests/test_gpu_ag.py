@@ -674,3 +674,66 @@ def test_kernel_times_ring(gpu, mode):
     finally:
         B.agg_ctx_set_timing(w.ctx, False)
         w.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("tile", [(256, 224), (256, 256), (128, 128), (128, 64)])
+@pytest.mark.parametrize("mode", ["overlap", "serial", "gemm_only"])
+def test_tail_split_bit_identical(gpu, dtype, tile, mode):
+    """The tail split forced on (the last row tiles of the compute order in a second launch of
+    the next smaller tile shape): C within the bar against the oracle and bit-identical to the
+    single launch (same rows, same per-element K order), every flag at the epoch, and, with
+    timing on, one duration for the call's two launches."""
+    world, rank, ms, cr, k, n = 4, 1, 128, 32, 320, 448
+    if dtype == "fp8":
+        k = 384
+    m = world * ms
+    head, tail_ts = B.agg_tail_split(tile[0], tile[1], m, n, -(-m // tile[0]), 256, "on")
+    assert head >= 1 and tail_ts[0] > 0, (tile, head, tail_ts)
+    shards, b, sa, sb = small_ag_data(world, ms, k, n, dtype, seed=41)
+    order = inputs.seeded_order(world, rank, ms // cr, 5)
+    outs = []
+    for tail in ("off", "on"):
+        w = AgWorkload(world, rank, shards, b, chunk_rows=cr, dtype=dtype, scale_a=sa, scale_b=sb,
+                       tile=tile)
+        try:
+            B.agg_ctx_set_tail(w.ctx, tail)
+            if mode == "gemm_only":
+                w.run("copy_only", order=order)
+            B.agg_ctx_set_timing(w.ctx, True)
+            w.run(mode, order=order)
+            torch.cuda.synchronize()
+            times = B.agg_ctx_kernel_times(w.ctx, 8)
+            assert len(times) == 1 and 0.0 < times[0] < 1000.0, times
+            assert w.status() == (0, -1)
+            assert_close(to_f64(w.c), _oracle_c(shards, b, dtype, sa, sb), _tol(dtype), ("C", tail))
+            assert (w.flags.cpu().numpy() == B.agg_ctx_epoch(w.ctx)).all(), tail
+            outs.append(w.c.clone())
+        finally:
+            w.close()
+    assert bits_equal(outs[0], outs[1]), (dtype, tile, mode)
+
+
+def test_tail_split_full_size_auto(gpu):
+    """The 5120-row AllToAll workload's 320 tiles of 256 x 224 split automatically (16 row tiles in
+    the first launch, 8 tail row tiles of 128 x 128 in the second); its C is bit-identical to the
+    single launch."""
+    cfg = configs.CONFIGS["a2a_w8_5120x3584x8192_bf16"]
+    d = configs.make_a2a_data(cfg)
+    from allgather_gemm_persistent_amd.workload import A2aWorkload
+    rows = B.agg_a2a_row_tile_order(cfg.world, cfg.rank, cfg.cap, cfg.chunk_rows, d["counts"], cfg.order(), 256)
+    head, tail_ts = B.agg_tail_split(256, 224, cfg.world * cfg.cap, cfg.n, len(rows), 256, "auto")
+    assert (head, tail_ts) == (16, (128, 128)), (len(rows), head, tail_ts)
+    outs = []
+    for tail in ("off", "auto"):
+        w = A2aWorkload(cfg.world, cfg.rank, d["blocks"], d["counts"], d["b"], cfg.chunk_rows, cfg.dtype,
+                        d["scale_a"], d["scale_b"])
+        try:
+            B.agg_ctx_set_tail(w.ctx, tail)
+            w.run("overlap", order=cfg.order())
+            torch.cuda.synchronize()
+            assert w.status() == (0, -1)
+            outs.append(w.c.clone())
+        finally:
+            w.close()
+    assert bits_equal(outs[0], outs[1])
