@@ -408,9 +408,12 @@ __device__ inline bool claim_static(const GemmArgs& a, Tile& t) {
 }
 
 // Claim the next tile: this XCD's list first, then the others in turn. Run by all lanes of one
-// wave: lane d reads the counter of the d-th list in search order, so one round trip finds the
-// first list with tiles left (and, at the end, that none has any); the lane owning that list
-// takes a tile with an atomic add, retrying if another workgroup emptied the list in between.
+// wave: an atomic add on the home list takes a tile while it has one; after that, lane d reads
+// the counter of the d-th list in search order, so one round trip finds the first list with
+// tiles left (and, at the end, that none has any); the lane owning that list takes a tile with
+// an atomic add, retrying if another workgroup emptied the list in between. (Four tiles per
+// workgroup, the 8192 x 7168 x 8192 fp8 AllGather+GEMM: 0.9% faster than reading the counters
+// before every add.)
 // Returns, on every lane, whether a tile was claimed (then in t).
 __device__ inline bool claim(const GemmArgs& a, int home, int nstat, Tile& t) {
   const int L = a.n_lists;
@@ -426,6 +429,25 @@ __device__ inline bool claim(const GemmArgs& a, int home, int nstat, Tile& t) {
   // no list has tiles past its static positions: nothing to claim, no counter to read
   if (__ballot(len > 0) == 0) return false;
   uint32_t* ctr = a.scratch + kScrLists + x;
+  // the home list first, with the atomic add alone (one round trip instead of a read and then
+  // the add while the home list has tiles; a failed add leaves its counter past the list's
+  // length, which every later read and add takes as empty)
+  {
+    const uint32_t len_home = (uint32_t)__shfl((int)len, 0);
+    if (len_home > 0) {
+      uint32_t k = 0;
+      if (lane == 0) k = atomicAdd(ctr, 1u);
+      k = (uint32_t)__shfl((int)k, 0);
+      if (k < len_home) {
+        if (lane == 0) list_tile(a, x, g, skip + k, t);
+        t.row_tile = __shfl(t.row_tile, 0);
+        t.col_tile = __shfl(t.col_tile, 0);
+        t.list = __shfl(t.list, 0);
+        t.pos = __shfl(t.pos, 0);
+        return true;
+      }
+    }
+  }
   for (;;) {
     const bool open = len > 0 && __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < len;
     const uint64_t m = __ballot(open);
