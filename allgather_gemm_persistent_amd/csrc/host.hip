@@ -1291,6 +1291,10 @@ extern "C" int gemm_rs(agg_ctx* ctx, int world, int rank, int64_t m, int64_t n, 
     g.scale = 1.0f;
     tiles = int64_t(g.n_row_tiles) * g.n_col_tiles;
     grid = grid_for(ctx, tiles, mode == AGG_OVERLAP && chunks && prod == AGG_PRODUCER_SDMA);
+    // the local block's tiles reduce it themselves (no round trip of its partial through `out`)
+    // when they are at least half the grid: fewer of them would leave the HBM-bound reduction to
+    // a few compute units, where the grid-wide reduction after the tiles spreads it over all
+    g.fuse_local = (world > 1 && int64_t(g.tpb) * g.n_col_tiles * 2 >= grid) ? 1 : 0;
     fill_common(ctx, g, ts, grid);
     attach_trace(ctx, g, tiles);
     if (world > 1) {

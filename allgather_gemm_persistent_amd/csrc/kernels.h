@@ -73,6 +73,8 @@ struct GemmArgs {
   int split_together;       // split-K with every part of every tile in its own workgroup at
                             //   once: the parts sum the tile together, a row range each
   int tpb;                  // RS: row tiles per block
+  int fuse_local;           // RS: the local block's tiles add the peers' partials themselves
+                            //   (else every workgroup reduces the local block after the tiles)
   int n_lists;              // claim lists (one per XCD)
   int list_cols;            // lists split as (n_lists / list_cols) row groups x list_cols column blocks
   uint32_t epoch;           // flags >= epoch mean "arrived"

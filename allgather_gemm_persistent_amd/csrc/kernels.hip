@@ -1635,27 +1635,93 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
             }
           }
         } else {
-          // the local block: the tile's partial goes to `out` (write-through, like `send`); the
-          // peers' partials are added after the last tile by reduce_local
-          const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(
-              a.out, 0, (int)(blk * 4), kBufferFlags);
-  #pragma unroll
-          for (int i = 0; i < FM; ++i) {
-            const int64_t m = lo + qrow(i);
-            if (m >= hi) continue;
-  #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-              const int64_t n = n0 + qcol(j);
-              if (n >= a.N) continue;
-              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rout,
-                                                     (int)(((m - base) * a.N + n) * 4), 0, kStoreSystemCoherent);
+          if (EPI == kEpiReduceScatter && a.fuse_local) {
+            // the local block: once every peer's chunks of these rows have arrived, out = partial +
+            // the peers' partials in ascending rank order. The partial goes through LDS (the operand
+            // stages, free after the K loop) in passes of RP rows, so that all threads then read
+            // whole rows of the peers' blocks (coalesced) while no accumulator is held beside them
+            if (wave == 0) {
+              uint32_t seen = 0xFFFFFFFFu;
+              const bool ok = wait_chunks<EPI>(a, lo, hi, block, seen);
+              if (lane == 0) s_ok = ok;
             }
+            __syncthreads();
+            const bool all_in = __builtin_amdgcn_readfirstlane(s_ok) != 0;
+            constexpr int RP0 = (kStageBytes / (BN * 4)) / WTM * WTM;
+            constexpr int RP = RP0 < BM ? RP0 : BM;
+            static_assert(RP >= WTM && RP % WTM == 0 && RP * BN * 4 <= kStageBytes, "LDS passes");
+            constexpr int Q4 = BN / 4, NE = RP * Q4, U = 2;
+            float* const tl = reinterpret_cast<float*>(stages);
+            const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(
+                a.out, 0, (int)(blk * 4), kBufferFlags);
+            const __amdgpu_buffer_rsrc_t rrecv = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float*>(a.recv), 0, (int)(a.world * blk * 4), kBufferFlags);
+            const int world = __builtin_amdgcn_readfirstlane(a.world), rank = __builtin_amdgcn_readfirstlane(a.rank);
+            for (int p0 = 0; p0 < BM; p0 += RP) {
+              if (wm * WTM >= p0 && wm * WTM < p0 + RP) {
+    #pragma unroll
+                for (int i = 0; i < FM; ++i)
+    #pragma unroll
+                  for (int j = 0; j < FN; ++j)
+                    *reinterpret_cast<f32x4*>(tl + (qrow(i) - p0) * BN + qcol(j)) = acc[i][j];
+              }
+              __syncthreads();
+              for (int e0 = tid; e0 < NE; e0 += NT * U) {
+                f32x4 v[U], in[U][AGG_MAX_WORLD - 1];
+                int64_t mo[U];
+                bool ok[U];
+    #pragma unroll
+                for (int u = 0; u < U; ++u) {
+                  const int e = e0 + u * NT;
+                  const int r = e / Q4, c4 = e - (e / Q4) * Q4;
+                  const int64_t m = lo + p0 + r, n = n0 + 4 * c4;
+                  ok[u] = e < NE && m < hi && n < a.N;
+                  mo[u] = (m - base) * a.N + n;
+                  v[u] = ok[u] ? *reinterpret_cast<const f32x4*>(tl + r * BN + 4 * c4) : f32x4{};
+    #pragma unroll
+                  for (int q = 0; q < AGG_MAX_WORLD - 1; ++q) {
+                    const int p = q < rank ? q : q + 1;
+                    const int off = (ok[u] && all_in && p < world) ? (int)(((int64_t)p * blk + mo[u]) * 4) : (int)kOutOfRange;
+                    in[u][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rrecv, off, 0, kStoreSystemCoherent));
+                  }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int u = 0; u < U; ++u) {
+                  if (!ok[u]) continue;
+                  if (all_in) {
+    #pragma unroll
+                    for (int q = 0; q < AGG_MAX_WORLD - 1; ++q)
+                      if (q + 1 < world) v[u] += in[u][q];
+                  }
+                  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[u]), rout, (int)(mo[u] * 4), 0, 0);
+                }
+              }
+              __syncthreads();
+            }
+          } else {
+            // the local block: the tile's partial goes to `out` (write-through, like `send`); the
+            // peers' partials are added after the last tile by reduce_local
+            const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(
+                a.out, 0, (int)(blk * 4), kBufferFlags);
+    #pragma unroll
+            for (int i = 0; i < FM; ++i) {
+              const int64_t m = lo + qrow(i);
+              if (m >= hi) continue;
+    #pragma unroll
+              for (int j = 0; j < FN; ++j) {
+                const int64_t n = n0 + qcol(j);
+                if (n >= a.N) continue;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), rout,
+                                                       (int)(((m - base) * a.N + n) * 4), 0, kStoreSystemCoherent);
+              }
+            }
+            // once the stores have completed, count the tile in its row tile
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid == 0)
+              __hip_atomic_fetch_add(a.scratch + kScrLocal + tib, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
-          // once the stores have completed, count the tile in its row tile
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          __syncthreads();
-          if (tid == 0)
-            __hip_atomic_fetch_add(a.scratch + kScrLocal + tib, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (!local) {
           // publish: once every thread's write-through stores have completed, this tile's rows of
@@ -1694,7 +1760,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   }
 
   // (only a launch that computes the tiles reduces: a copy-only launch leaves `out` alone)
-  if ((EPI == kEpiReduceScatter || EPI == kEpiFfn) && a.n_row_tiles > 0) reduce_local<BM>(a, tid, &s_job, &s_ok);
+  if (((EPI == kEpiReduceScatter && !a.fuse_local) || EPI == kEpiFfn) && a.n_row_tiles > 0)
+    reduce_local<BM>(a, tid, &s_job, &s_ok);
 
   // ---- the last workgroup resets the counters for the next launch. No fence: every counter
   // reset here was last touched by the other workgroups through atomics whose returned values

@@ -164,3 +164,34 @@ def test_config_c3_vs_oracle(gpu):
             bookkeeping((producer, mode))
     finally:
         w.close()
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("mode", ["overlap", "serial", "gemm_only"])
+def test_two_ranks_fused_local_block_vs_oracle(gpu, tile, mode):
+    """W = 2: the local block's tiles are half the grid, so they add the peer's partial in their
+    own epilogue (through LDS) instead of leaving it to the grid-wide reduction; ragged rows,
+    columns and K tail within the bar, integer inputs bit-exact."""
+    world, rank, m, k, n, cr = 2, 1, 2 * 328, 328, 264, 41
+    a, b, peers = _data(world, m, k, n, seed=27)
+    w = RsWorkload(world, rank, a, b, peers, cr, tile=tile)
+    try:
+        if mode == "gemm_only":
+            w.run("copy_only", order=None)
+        w.run(mode)
+        assert w.status() == (0, -1)
+        send, out = _ref(w, a, b, peers)
+        assert_close(to_f64(w.send[:world - 1]), send, BF16_TOL, "send")
+        assert_close(to_f64(w.out), out, BF16_TOL, "out")
+    finally:
+        w.close()
+    a, b, peers = _data(world, m, k, n, seed=29, kind="int")
+    w = RsWorkload(world, rank, a, b, peers, cr, tile=tile)
+    try:
+        w.run(mode if mode != "gemm_only" else "overlap")
+        assert w.status() == (0, -1)
+        send, out = _ref(w, a, b, peers)
+        assert np.array_equal(to_f64(w.send[:world - 1]), send)
+        assert np.array_equal(to_f64(w.out), out)
+    finally:
+        w.close()
