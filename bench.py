@@ -12,7 +12,7 @@ figures R = T_ovl / T_gemm and eta = (T_serial - T_ovl) / min(T_copy, T_gemm) fr
 kernels in the other modes (per-call stream times with the modes interleaved call by call; the
 t_*_us fields are the modes timed one after another, which the board's clock drift skews), the
 dominant kernel's roofline (its own duration from timing events that every n-th timed launch
-carries on the stream it runs on, n = min(8, K // 8) or 1: the events cost each launch that
+carries on the stream it runs on, n = min(8, K // 8) or 1 (at least K / 256): the events cost each launch that
 carries them some microseconds, so the timed steps sample), and the CPU oracle's rate on the same
 workload as a baseline.
 
@@ -424,7 +424,8 @@ def main():
         torch.cuda.synchronize()
         # clears the ring: only timed launches count; launches 0, every, 2 * every, ... carry
         # the timing events
-        every = max(1, min(8, args.steps // 8))
+        # (at most 256 timed launches: the ring holds the last 256)
+        every = max(1, min(8, args.steps // 8), -(-args.steps // 256))
         B.agg_ctx_set_timing(w.ctx, every)
         t0 = time.perf_counter()
         for _ in range(args.steps):
@@ -435,7 +436,7 @@ def main():
         if st[0]:
             raise RuntimeError(f"overlap: a chunk wait gave up (flag {st[1]})")
         kms = B.agg_ctx_kernel_times(w.ctx, args.steps)
-        assert len(kms) == (args.steps + every - 1) // every, (len(kms), args.steps, every)
+        assert len(kms) == min(256, (args.steps + every - 1) // every), (len(kms), args.steps, every)
         k_ovl_us = statistics.mean(kms) * 1e3
         # context: the same steps with no timing events at all (the sampled launches above
         # carry them, which costs each of those launches some microseconds)
