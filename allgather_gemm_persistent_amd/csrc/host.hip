@@ -438,10 +438,14 @@ struct CopyPlan {
 // Copy-job fields of the kernel arguments for the CU producer: set s's jobs follow set s-1's, its
 // arrival order follows theirs in the uploaded table, and its piece counters start at s * 2048.
 void fill_copies(agg_ctx* ctx, GemmArgs& g, const CopyPlan* sets, int nsets, bool delays, int world,
-                 int grid, int pull_copiers) {
+                 int grid, int pull_copiers, int64_t min_piece = 65536) {
   // automatic piece size: as many pieces per chunk as keep every job in one round of the
   // copying workgroups (so no workgroup copies twice while others idle), in whole 4 KiB pages,
-  // at least 16 KiB
+  // at least min_piece: for the persistent kernel's 256-thread copiers, when tiles wait for the
+  // chunks, 64 KiB, one round of their copy loop (256 threads x 16 vectors of 16 bytes), so a
+  // smaller piece saves no time and adds a counted piece to its chunk (pushed small gathers:
+  // 64 KiB pieces took the 256-row call's launch from 13.4 to 12.7 us and the decode gather's
+  // from 46.2 to 45.5 against 16 KiB); 16 KiB for pulled calls and the copy kernel
   const int copiers = pull_copiers > 0 ? pull_copiers
                       : ctx->copy_wgs > 0 ? std::min(ctx->copy_wgs, grid) : grid;
   size_t chunks = 0;
@@ -462,7 +466,7 @@ void fill_copies(agg_ctx* ctx, GemmArgs& g, const CopyPlan* sets, int nsets, boo
     cs.put_flags = pl.flags;
     cs.chunk_bytes = pl.cc.cr * pl.cc.row_bytes;
     const int64_t autop =
-        std::max<int64_t>(((cs.chunk_bytes + per_chunk - 1) / per_chunk + 4095) / 4096 * 4096, 16384);
+        std::max<int64_t>(((cs.chunk_bytes + per_chunk - 1) / per_chunk + 4095) / 4096 * 4096, min_piece);
     const int64_t piece = std::max<int64_t>(16, (ctx->piece_bytes > 0 ? ctx->piece_bytes : autop) / 16 * 16);
     cs.piece_bytes = std::min<int64_t>(cs.chunk_bytes, piece);
     cs.pieces = cs.piece_bytes > 0 ? int((cs.chunk_bytes + cs.piece_bytes - 1) / cs.piece_bytes) : 1;
@@ -544,7 +548,8 @@ int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int
   }
   if (copies) {
     h.epoch = epoch;
-    fill_copies(ctx, h, sets, nsets, delays, world, gr, pull ? pull_copiers : 0);
+    // (pulled: the copies gate no tile; 16 KiB pieces over more copiers end them sooner)
+    fill_copies(ctx, h, sets, nsets, delays, world, gr, pull ? pull_copiers : 0, pull ? 16384 : 65536);
   } else {
     h.copy_jobs = 0;
     std::memset(h.cs, 0, sizeof h.cs);
@@ -589,7 +594,7 @@ int launch_copy_producer(agg_ctx* ctx, uint32_t* scratch, const CopyPlan* plans,
   gc.scratch = scratch;
   gc.epoch = epoch;
   // pieces sized for every copy-kernel workgroup (the CU producer's copy_wgs does not apply)
-  fill_copies(ctx, gc, plans, nsets, false, world, kCopyGrid, kCopyGrid);
+  fill_copies(ctx, gc, plans, nsets, false, world, kCopyGrid, kCopyGrid, 16384);
   for (int s = 0; s < 2; ++s) {
     gc.mark_flags[s] = marks.copy_flags[s];
     gc.mark_count[s] = marks.copy_flags[s] ? marks.copy_count[s] : 0;

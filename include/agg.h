@@ -160,7 +160,7 @@ enum {
 /* Select the producer of later calls. For AGG_PRODUCER_CU, `copy_wgs` workgroups of the
  * persistent grid (0: all of them) first take copy jobs, each moving `piece_kib` KiB of one chunk
  * (0: a chunk is cut into floor(copying workgroups / remote chunks) pieces, at least one, each
- * rounded up to whole 4 KiB and at least 16 KiB, so that every job fits in one round of the
+ * rounded up to whole 4 KiB and at least 64 KiB (16 KiB when pulled and for AGG_PRODUCER_KERNEL), so that every job fits in one round of the
  * copying workgroups; a chunk is cut into ceil(chunk bytes / piece) pieces), in arrival order, and only then
  * claim tiles; the workgroup that completes a chunk's last piece releases its flag. The other
  * arguments are ignored for AGG_PRODUCER_SDMA. AGG_PRODUCER_KERNEL cuts chunks into `piece_kib`
