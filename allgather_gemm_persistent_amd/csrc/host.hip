@@ -514,7 +514,7 @@ struct TailLaunch {
 int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int dtype, int epi,
               int grid, const CopyPlan* sets, int nsets, bool delays, int world, uint32_t epoch,
               bool copies, bool tiles_on, bool timed, const Marks& marks, int pull_copiers = 0,
-              const TailLaunch& tail = TailLaunch{}) {
+              const TailLaunch& tail = TailLaunch{}, int last_copiers = 0) {
   GemmArgs h = g;
   h.mark_count[0] = h.mark_count[1] = h.mark_count[2] = 0;
   if (copies) {
@@ -533,6 +533,10 @@ int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int
   const bool pull = pull_copiers > 0 && copies && tiles_on;
   h.pull = pull ? 1 : 0;
   if (pull) gr = grid + pull_copiers;
+  // small pushed gathers: the copiers after the tile workgroups
+  const bool last = !pull && last_copiers > 0 && copies && tiles_on;
+  h.copiers_last = last ? 1 : 0;
+  if (last) gr = grid + last_copiers;
   if (!tiles_on) {
     h.n_row_tiles = 0;
     h.n_col_tiles = 0;
@@ -549,7 +553,8 @@ int launch_cu(agg_ctx* ctx, hipStream_t ls, const GemmArgs& g, TileShape ts, int
   if (copies) {
     h.epoch = epoch;
     // (pulled: the copies gate no tile; 16 KiB pieces over more copiers end them sooner)
-    fill_copies(ctx, h, sets, nsets, delays, world, gr, pull ? pull_copiers : 0, pull ? 16384 : 65536);
+    fill_copies(ctx, h, sets, nsets, delays, world, gr, pull ? pull_copiers : last ? last_copiers : 0,
+                pull ? 16384 : 65536);
   } else {
     h.copy_jobs = 0;
     std::memset(h.cs, 0, sizeof h.cs);
@@ -1148,6 +1153,15 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
         }
       }
     }
+    // small pushed gathers with compute units to spare: the copies on workgroups of their own
+    // after the tile workgroups (which then start their tiles, local chunks first, at once)
+    int last_copiers = 0;
+    if (kernel && chunks && mode == AGG_OVERLAP && pull_copiers == 0 && !tl.g && delay_us == nullptr) {
+      const int64_t remote = int64_t(world - 1) * m_shard * cc.row_bytes;
+      const int64_t spare = int64_t(ctx->cus) - grid;
+      if (spare >= 1 && remote <= kPullMaxBytes && ctx->copy_wgs == 0)
+        last_copiers = int(std::min<int64_t>(spare, std::max<int64_t>(1, (remote + 65535) / 65536)));
+    }
     if (kernel)
       if (int rc = upload_rows(ctx, sp, s, table)) return rc;
     Marks marks;
@@ -1160,7 +1174,7 @@ int ag_gemm_impl(agg_ctx* ctx, int world, int rank, int64_t m_shard, int64_t n, 
                        [&](bool copies, bool tiles_on, bool timed) {
                          return launch_cu(ctx, s, g, ts, dtype, kEpiAllGather, grid, &plan, 1,
                                           delay_us != nullptr, world, epoch, copies, tiles_on,
-                                          timed, marks, pull_copiers, tl);
+                                          timed, marks, pull_copiers, tl, last_copiers);
                        });
   }
   // the copy engines' producer keeps the kernel on a queue of its own (see the top of this

@@ -91,6 +91,10 @@ struct GemmArgs {
   // jobs (which still fill the gather buffer and release the flags) go to the last copy_wgs
   // workgroups, which claim tiles only after copying
   int pull;
+  // AG push with copiers to spare (small gathers): the copy jobs go to the last copy_wgs
+  // workgroups, which take no tile before copying, so no tile's start waits behind a copy of
+  // its own workgroup; the tiles still wait for their chunks' flags
+  int copiers_last;
   // nonzero: remote chunks may land while this launch runs (an overlapped call); a tile that
   // reads remote rows then acquires after its chunk waits. Otherwise every row a tile reads was
   // written before the launch began, which the launch's own start makes visible.

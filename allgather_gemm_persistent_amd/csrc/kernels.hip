@@ -838,7 +838,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   const int home = (int)blockIdx.x % a.n_lists;
 
   // workgroups whose first tile is taken statically (pull: all but the copiers at the end)
-  const int nstat = (EPI == kEpiAllGather && a.pull) ? (int)gridDim.x - a.copy_wgs : (int)gridDim.x;
+  const int nstat = (EPI == kEpiAllGather && (a.pull || a.copiers_last)) ? (int)gridDim.x - a.copy_wgs
+                                                                        : (int)gridDim.x;
   auto claim_tile = [&](bool first) {
     if (wave == 0) {
       Tile t{};
@@ -857,16 +858,18 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(const GemmArgs a) {
   // copy_wgs workgroups move the remote chunks (so the claim is off the path from the end of
   // the copy to the first tile), and every workgroup computes tiles, claiming the next one after
   // each
-  // (pull: the copiers are the last copy_wgs workgroups and take no tile before copying, so the
-  // tiles start at once on the others)
+  // (pull, and small pushed gathers: the copiers are the last copy_wgs workgroups and take no
+  // tile before copying, so the tiles start at once on the others)
   const bool pull = EPI == kEpiAllGather && a.pull;
-  const int first_copier = pull ? (int)gridDim.x - a.copy_wgs : 0;
+  const bool last = EPI == kEpiAllGather && (a.pull || a.copiers_last);
+  const int first_copier = last ? (int)gridDim.x - a.copy_wgs : 0;
   const bool copier = a.copy_jobs && (int)blockIdx.x >= first_copier &&
                       (int)blockIdx.x < first_copier + a.copy_wgs;
-  if (!(pull && copier)) claim_tile(true);
-  // (pulled: no tile waits for a copy, so the copiers may deal the jobs among themselves)
+  if (!(last && copier)) claim_tile(true);
+  // (pulled: no tile waits for a copy, so the copiers may deal the jobs among themselves;
+  // pushed, tiles wait for the copies, so any running copier takes the next job)
   if (copier) produce_chunks<NT>(a, tid, &s_job, pull ? (int)blockIdx.x - first_copier : -1);
-  if (pull && copier) claim_tile(false);
+  if (last && copier) claim_tile(false);
 
   for (;; claim_tile(false)) {   // (an abandoned tile returns early; the next claim follows)
     // uniform for the compiler too (see produce_chunks)
