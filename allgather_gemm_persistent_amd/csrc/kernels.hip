@@ -343,8 +343,10 @@ __device__ inline void produce_chunks(const GemmArgs& a, int tid, int* s_job, in
     // and the piece that completes the chunk writes its flag (a system-coherent store)
     __syncthreads();
     if (tid == 0) {
-      const uint32_t prev = __hip_atomic_fetch_add(a.scratch + kScrPieces + cs.piece_off + c, 1u,
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // (a chunk in one piece needs no count: its only job raises the flag, a round trip sooner)
+      const uint32_t prev = pieces == 1 ? 0u
+                                        : __hip_atomic_fetch_add(a.scratch + kScrPieces + cs.piece_off + c, 1u,
+                                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (prev + 1 == pieces)
         __hip_atomic_store(cs.put_flags + c, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
